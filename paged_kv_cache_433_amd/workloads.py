@@ -1,0 +1,469 @@
+"""Seeded synthetic decode batches and a small CPU block manager.
+
+This module makes inputs; it holds none of the attention arithmetic. Tests,
+``bench.py`` and the smoke check feed the same arrays to the GPU library and
+to the float64 oracle.
+
+bfloat16 data is carried as raw 16-bit patterns (``numpy.uint16``).
+
+Block management follows the pages' description:
+
+* "vLLM: Anatomy and Mechanisms of High-Throughput LLM Inference", section
+  "Block-Level Management": a request's logical blocks map to physical blocks
+  through a block table; a new physical block comes from a free block pool
+  when the last logical block is full; the default block holds 16 tokens.
+* the same page, section "Memory Sharing via Copy-on-Write (CoW)": beams
+  share physical blocks, and only the block where they diverge is copied.
+* "vLLM Internals", section "The Block Manager": the worked example of three
+  requests with tables [B0,B1,B2], [B3,B4] and [B5..B8].
+* "Inside vLLM: Anatomy of a High-Throughput LLM Inference System", section
+  "Generate function": a finished request's blocks go back to the free queue.
+
+The page's example says that R1 holds 48 tokens and that it is "at token 47".
+This module reads "48 tokens cached" as positions 0..47, which fill three
+blocks. So the token at position 48 opens logical block 3. The rule used is:
+a token at position ``pos`` needs a fresh block iff ``pos % block_size == 0``.
+"""
+
+from __future__ import annotations
+
+import collections
+import dataclasses
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+BLOCK_SIZE = 16
+BF16_QNAN = np.uint16(0x7FC0)          # poison for slots no table references
+TABLE_PAD_OFFSET = 12345               # padded table entries hold num_blocks + this
+
+# ----------------------------------------------------------------------------
+# bfloat16 bit helpers (input preparation only)
+# ----------------------------------------------------------------------------
+
+
+def f32_to_bf16_bits(x) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); return bits.
+
+    Only finite inputs are expected (generated data); NaN maps to a quiet NaN.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    rounded = (u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) >> np.uint32(16)
+    out = rounded.astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        out[nan] = BF16_QNAN
+    return out
+
+
+def normal_bf16(rng: np.random.Generator, shape) -> np.ndarray:
+    """``N(0, 1)`` float32 draws rounded to bfloat16 bits."""
+    return f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
+
+
+def bytes_per_block(block_size: int, num_kv_heads: int, head_size: int, dtype_bytes: int = 2) -> int:
+    """Bytes of one physical KV block of one layer, K and V together.
+
+    The figure the page gives for sizing the cache ("Inside vLLM", section
+    "LLM Engine constructor"): 2 (key and value) x block_size x num_kv_heads x
+    head_size x bytes per element.
+    """
+    return 2 * block_size * num_kv_heads * head_size * dtype_bytes
+
+
+def _rng(seed: int, *stream: int) -> np.random.Generator:
+    """Independent generator for one named stream of one seed."""
+    return np.random.default_rng([seed, *stream])
+
+
+def _workers() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+# ----------------------------------------------------------------------------
+# the block manager
+# ----------------------------------------------------------------------------
+
+
+class BlockPool:
+    """Free-block pool with reference counts.
+
+    Blocks are handed out in the order of ``order`` (a shuffled pool when the
+    caller passes a permutation) and come back to the tail of the queue when
+    their count drops to zero.
+    """
+
+    def __init__(self, num_blocks: int, order=None):
+        self.num_blocks = int(num_blocks)
+        order = np.arange(num_blocks) if order is None else np.asarray(order)
+        assert sorted(order.tolist()) == list(range(num_blocks))
+        self.free = collections.deque(int(b) for b in order)
+        self.ref = np.zeros(num_blocks, dtype=np.int64)
+
+    def alloc(self) -> int:
+        if not self.free:
+            raise MemoryError("block pool exhausted")
+        b = self.free.popleft()
+        assert self.ref[b] == 0
+        self.ref[b] = 1
+        return b
+
+    def incref(self, b: int) -> None:
+        assert self.ref[b] > 0
+        self.ref[b] += 1
+
+    def decref(self, b: int) -> None:
+        assert self.ref[b] > 0
+        self.ref[b] -= 1
+        if self.ref[b] == 0:
+            self.free.append(int(b))
+
+    @property
+    def num_free(self) -> int:
+        return len(self.free)
+
+
+@dataclasses.dataclass
+class SeqBlocks:
+    """A sequence's block table and number of cached tokens."""
+
+    table: list
+    length: int = 0
+
+    def fork(self, pool: BlockPool) -> "SeqBlocks":
+        for b in self.table:
+            pool.incref(b)
+        return SeqBlocks(list(self.table), self.length)
+
+    def release(self, pool: BlockPool) -> None:
+        for b in self.table:
+            pool.decref(b)
+        self.table = []
+        self.length = 0
+
+
+def append_token(pool: BlockPool, seq: SeqBlocks, block_size: int = BLOCK_SIZE):
+    """Give the sequence's next token a slot; return ``(slot, cow_pair)``.
+
+    A token at position ``pos`` opens a new block iff ``pos % block_size == 0``.
+    Otherwise it goes into the last block. If that block is shared, it is
+    first replaced by a private copy: ``cow_pair = (old, new)``.
+    """
+    pos = seq.length
+    cow = None
+    if pos % block_size == 0:
+        seq.table.append(pool.alloc())
+    else:
+        last = seq.table[-1]
+        if pool.ref[last] > 1:
+            fresh = pool.alloc()
+            pool.decref(last)
+            seq.table[-1] = fresh
+            cow = (last, fresh)
+    seq.length += 1
+    slot = seq.table[-1] * block_size + pos % block_size
+    return slot, cow
+
+
+def allocate_prefix(pool: BlockPool, n_tokens: int, block_size: int = BLOCK_SIZE) -> SeqBlocks:
+    """Blocks for a sequence's first ``n_tokens`` tokens, in one go."""
+    seq = SeqBlocks([])
+    for _ in range((n_tokens + block_size - 1) // block_size):
+        seq.table.append(pool.alloc())
+    seq.length = n_tokens
+    return seq
+
+
+# ----------------------------------------------------------------------------
+# decode batches
+# ----------------------------------------------------------------------------
+
+
+@dataclasses.dataclass
+class DecodeBatch:
+    """One decode step's inputs, all as host arrays.
+
+    The caches hold every token before the newest one. The newest token of
+    each sequence (position ``context_lens[s] - 1``) is in ``new_k``/``new_v``
+    and goes to ``slot_mapping[s]``, so the step is a scatter followed by a
+    decode over ``context_lens``. Slots no table references, including the
+    newest token's slot before the scatter, hold bfloat16 NaN. Table entries
+    past a sequence's last block hold ``num_blocks + 12345``.
+    """
+
+    name: str
+    seed: int
+    num_blocks: int
+    block_size: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_size: int
+    scale: np.float32
+    block_tables: np.ndarray   # int32 [S, MB]
+    context_lens: np.ndarray   # int32 [S]
+    q: np.ndarray              # uint16 [S, Hq, D]
+    k_cache: np.ndarray        # uint16 [NB, bs, Hkv, D]
+    v_cache: np.ndarray
+    new_k: np.ndarray          # uint16 [T, Hkv, D]
+    new_v: np.ndarray
+    slot_mapping: np.ndarray   # int64 [T]
+    cow_pairs: np.ndarray      # int64 [P, 2]
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return int(self.block_tables.shape[1])
+
+
+def _fill_sequence(k_cache, v_cache, table, k_bits, v_bits, block_size):
+    """Put per-logical-position data ``[m, Hkv, D]`` into its physical slots."""
+    m = k_bits.shape[0]
+    for j in range((m + block_size - 1) // block_size):
+        lo, hi = j * block_size, min(m, (j + 1) * block_size)
+        k_cache[table[j], : hi - lo] = k_bits[lo:hi]
+        v_cache[table[j], : hi - lo] = v_bits[lo:hi]
+
+
+def make_batch(name, seed, lens, num_q_heads, num_kv_heads, head_size, num_blocks,
+               max_blocks_per_seq=None, scale=None, block_size=BLOCK_SIZE) -> DecodeBatch:
+    """A decode batch with the given context lengths (newest token included).
+
+    Draw order for ``seed``:
+    * stream (seed, 0) shuffles the free pool;
+    * stream (seed, 2) draws q;
+    * stream (seed, 1, s) draws sequence s's K then V, per logical position.
+
+    Blocks are popped from the shuffled pool in (sequence, logical block)
+    order. Data therefore depends only on (seed, s, position), not on where a
+    block lands.
+    """
+    lens = np.asarray(lens, dtype=np.int64)
+    assert np.all(lens >= 1)
+    S = len(lens)
+    nblk = (lens + block_size - 1) // block_size
+    MB = int(max_blocks_per_seq or nblk.max())
+    assert nblk.max() <= MB
+    pool = BlockPool(num_blocks, _rng(seed, 0).permutation(num_blocks))
+    seqs = [allocate_prefix(pool, int(n), block_size) for n in lens]
+    tables = np.full((S, MB), num_blocks + TABLE_PAD_OFFSET, dtype=np.int32)
+    for s, sq in enumerate(seqs):
+        tables[s, : len(sq.table)] = sq.table
+    shape = (num_blocks, block_size, num_kv_heads, head_size)
+    k_cache = np.full(shape, BF16_QNAN, dtype=np.uint16)
+    v_cache = np.full(shape, BF16_QNAN, dtype=np.uint16)
+    new_k = np.empty((S, num_kv_heads, head_size), dtype=np.uint16)
+    new_v = np.empty_like(new_k)
+    slots = np.empty(S, dtype=np.int64)
+
+    def one(s):
+        n = int(lens[s])
+        r = _rng(seed, 1, s)
+        kb = normal_bf16(r, (n, num_kv_heads, head_size))
+        vb = normal_bf16(r, (n, num_kv_heads, head_size))
+        _fill_sequence(k_cache, v_cache, seqs[s].table, kb[: n - 1], vb[: n - 1], block_size)
+        new_k[s], new_v[s] = kb[n - 1], vb[n - 1]
+        slots[s] = seqs[s].table[(n - 1) // block_size] * block_size + (n - 1) % block_size
+
+    with ThreadPoolExecutor(_workers()) as ex:
+        list(ex.map(one, range(S)))
+    q = normal_bf16(_rng(seed, 2), (S, num_q_heads, head_size))
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_size)
+    return DecodeBatch(name, seed, num_blocks, block_size, num_q_heads, num_kv_heads,
+                       head_size, np.float32(scale), tables, lens.astype(np.int32), q,
+                       k_cache, v_cache, new_k, new_v, slots,
+                       np.zeros((0, 2), dtype=np.int64))
+
+
+def sequence_kv(batch: DecodeBatch, s: int):
+    """Regenerate sequence ``s``'s logical K/V bits ``[n, Hkv, D]``.
+
+    The draws are the same ones ``make_batch`` made. Tests use this to build
+    the dense, contiguous K/V without reading the paged cache.
+    """
+    n = int(batch.context_lens[s])
+    r = _rng(batch.seed, 1, s)
+    kb = normal_bf16(r, (n, batch.num_kv_heads, batch.head_size))
+    vb = normal_bf16(r, (n, batch.num_kv_heads, batch.head_size))
+    return kb, vb
+
+
+# ----------------------------------------------------------------------------
+# the five named workloads
+# ----------------------------------------------------------------------------
+
+CONFIG_NAMES = ("tiny_mha", "llama2_7b", "llama3_8b_gqa", "long_splitk", "beam_cow")
+
+
+def lognormal_lens(rng, count, median, sigma, lo, hi):
+    """``clip(round(exp(N(ln median, sigma))), lo, hi)``."""
+    x = np.exp(rng.normal(math.log(median), sigma, size=count))
+    return np.clip(np.rint(x), lo, hi).astype(np.int64)
+
+
+def config_lens(name: str, seed: int):
+    """Context lengths of a named config (stream (seed, 3))."""
+    r = _rng(seed, 3)
+    if name == "tiny_mha":
+        return np.array([1, 17, 33, 100])
+    if name == "llama2_7b":
+        return r.integers(128, 2048, size=64, endpoint=True)
+    if name == "llama3_8b_gqa":
+        return lognormal_lens(r, 256, 1024, 0.5, 16, 4096)
+    if name == "long_splitk":
+        return np.tile(np.array([32768, 65536, 98304, 131072]), 2)
+    if name == "long_splitk_max":
+        return np.full(8, 131072)
+    raise KeyError(name)
+
+
+CONFIG_SHAPES = {
+    # name: (num_q_heads, num_kv_heads, head_size, num_blocks, max_blocks_per_seq, seed)
+    "tiny_mha": (8, 8, 64, 64, 8, 1),
+    "llama2_7b": (32, 32, 128, 16384, 128, 2),
+    "llama3_8b_gqa": (32, 8, 128, 65536, 256, 3),
+    "long_splitk": (64, 8, 128, 65536, 8192, 4),
+    "long_splitk_max": (64, 8, 128, 65536, 8192, 4),
+}
+
+
+def make_config(name: str, seed: int | None = None) -> DecodeBatch:
+    """Build one of the named decode configs (the CoW config has its own class)."""
+    hq, hkv, d, nb, mb, default_seed = CONFIG_SHAPES[name]
+    seed = default_seed if seed is None else seed
+    return make_batch(name, seed, config_lens(name, seed), hq, hkv, d, nb, mb)
+
+
+def algorithmic_bytes(context_lens, num_q_heads, num_kv_heads, head_size,
+                      block_size=BLOCK_SIZE, dtype_bytes=2) -> int:
+    """Bytes a decode step must move: K and V of every cached token, q in,
+    out back, the used block-table entries and the context lengths."""
+    n = np.asarray(context_lens, dtype=np.int64)
+    kv = int(n.sum()) * 2 * num_kv_heads * head_size * dtype_bytes
+    qo = len(n) * 2 * num_q_heads * head_size * dtype_bytes
+    tables = int(((n + block_size - 1) // block_size).sum()) * 4
+    return kv + qo + tables + 4 * len(n)
+
+
+def scatter_bytes(num_tokens, num_kv_heads, head_size, dtype_bytes=2) -> int:
+    """Bytes of the slot scatter: read new K/V, write them, read the slots."""
+    return num_tokens * (2 * num_kv_heads * head_size * dtype_bytes * 2 + 8)
+
+
+def copy_bytes(num_pairs, block_size, num_kv_heads, head_size, dtype_bytes=2) -> int:
+    """Bytes of the copy-on-write: read and write K and V of every pair."""
+    return num_pairs * (bytes_per_block(block_size, num_kv_heads, head_size, dtype_bytes) * 2 + 16)
+
+
+# ----------------------------------------------------------------------------
+# beam search with copy-on-write
+# ----------------------------------------------------------------------------
+
+
+class BeamSearchWorkload:
+    """Prompts shared by beams, then fork / copy-on-write / append steps.
+
+    ``num_prompts`` prompts of ``prompt_len`` tokens each, each shared by
+    ``beams`` beams (refcount = beams), plus ``U{0..max_private}`` private
+    tokens per beam. A step does the following:
+
+    1. every new beam picks a parent uniformly among its prompt's beams and
+       inherits its table (refcounts go up), then the old beams let go of
+       theirs;
+    2. beams append one token each, in ascending index. A partial last block
+       that is still shared is copied first (copy-on-write), so the
+       highest-index sharer keeps the original;
+    3. the batch is the pairs to copy, the new tokens' slots and K/V, and the
+       tables and lengths to decode over.
+
+    ``k_cache``/``v_cache`` hold the state before the first step. Callers
+    apply each step's copy and scatter themselves (GPU library or oracle).
+    """
+
+    def __init__(self, seed=5, num_prompts=64, beams=4, prompt_len=1024, max_private=200,
+                 num_q_heads=32, num_kv_heads=8, head_size=128, num_blocks=16384,
+                 block_size=BLOCK_SIZE):
+        self.seed, self.beams, self.bs = seed, beams, block_size
+        self.num_q_heads, self.num_kv_heads, self.head_size = num_q_heads, num_kv_heads, head_size
+        self.num_blocks = num_blocks
+        self.scale = np.float32(1.0 / math.sqrt(head_size))
+        self.num_seqs = num_prompts * beams
+        self.pool = BlockPool(num_blocks, _rng(seed, 0).permutation(num_blocks))
+        shape = (num_blocks, block_size, num_kv_heads, head_size)
+        self.k_cache = np.full(shape, BF16_QNAN, dtype=np.uint16)
+        self.v_cache = np.full(shape, BF16_QNAN, dtype=np.uint16)
+        priv = _rng(seed, 3).integers(0, max_private, size=self.num_seqs, endpoint=True)
+        self.seqs = []
+        for p in range(num_prompts):
+            prompt = allocate_prefix(self.pool, prompt_len, block_size)
+            r = _rng(seed, 1, p)
+            kb = normal_bf16(r, (prompt_len, num_kv_heads, head_size))
+            vb = normal_bf16(r, (prompt_len, num_kv_heads, head_size))
+            _fill_sequence(self.k_cache, self.v_cache, prompt.table, kb, vb, block_size)
+            for b in range(beams):
+                sq = prompt.fork(self.pool) if b < beams - 1 else prompt
+                self.seqs.append(sq)
+        for i, sq in enumerate(self.seqs):
+            m = int(priv[i])
+            if m == 0:
+                continue
+            r = _rng(seed, 4, i)
+            kb = normal_bf16(r, (m, num_kv_heads, head_size))
+            vb = normal_bf16(r, (m, num_kv_heads, head_size))
+            for t in range(m):
+                slot, cow = append_token(self.pool, sq, block_size)
+                if cow is not None:
+                    src, dst = cow
+                    self.k_cache[dst] = self.k_cache[src]
+                    self.v_cache[dst] = self.v_cache[src]
+                blk, off = divmod(slot, block_size)
+                self.k_cache[blk, off] = kb[t]
+                self.v_cache[blk, off] = vb[t]
+        self.q_rng = _rng(seed, 2)
+        self.step_index = 0
+
+    def step(self) -> DecodeBatch:
+        i = self.step_index
+        self.step_index += 1
+        r = _rng(self.seed, 5, i)
+        parents = r.integers(0, self.beams, size=self.num_seqs)
+        new = []
+        for s in range(self.num_seqs):
+            base = (s // self.beams) * self.beams
+            new.append(self.seqs[base + int(parents[s])].fork(self.pool))
+        for sq in self.seqs:
+            sq.release(self.pool)
+        self.seqs = new
+        slots = np.empty(self.num_seqs, dtype=np.int64)
+        pairs = []
+        for s, sq in enumerate(self.seqs):
+            slot, cow = append_token(self.pool, sq, self.bs)
+            slots[s] = slot
+            if cow is not None:
+                pairs.append(cow)
+        lens = np.array([sq.length for sq in self.seqs], dtype=np.int32)
+        MB = max(len(sq.table) for sq in self.seqs)
+        tables = np.full((self.num_seqs, MB), self.num_blocks + TABLE_PAD_OFFSET, dtype=np.int32)
+        for s, sq in enumerate(self.seqs):
+            tables[s, : len(sq.table)] = sq.table
+        kv_shape = (self.num_seqs, self.num_kv_heads, self.head_size)
+        new_k = normal_bf16(r, kv_shape)
+        new_v = normal_bf16(r, kv_shape)
+        q = normal_bf16(self.q_rng, (self.num_seqs, self.num_q_heads, self.head_size))
+        return DecodeBatch("beam_cow", self.seed, self.num_blocks, self.bs, self.num_q_heads,
+                           self.num_kv_heads, self.head_size, self.scale, tables, lens, q,
+                           self.k_cache, self.v_cache, new_k, new_v, slots,
+                           np.array(pairs, dtype=np.int64).reshape(-1, 2))
+
+    def unique_blocks(self) -> int:
+        return int(np.count_nonzero(self.pool.ref))

@@ -1,0 +1,51 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and check
+that the pins catch every one of them."""
+
+import pathlib
+import types
+
+import pytest
+
+from oracle_pins import ALL_PINS
+
+SRC = (pathlib.Path(__file__).resolve().parents[1] / "oracle" / "paged_attention.py").read_text()
+
+MUTANTS = {
+    "kv head h % Hkv instead of h // G": ("range(kv_head * group, (kv_head + 1) * group)",
+                                          "range(kv_head, num_q_heads, num_kv_heads)"),
+    "block index from offset": ("[positions // block_size]", "[positions % block_size]"),
+    "offset from block index": ("offsets = positions % block_size", "offsets = positions // block_size"),
+    "scale dropped": ("z = scale64 * (keys @ qf[h])", "z = (keys @ qf[h])"),
+    "scale applied twice": ("z = scale64 * (keys @ qf[h])", "z = scale64 * scale64 * (keys @ qf[h])"),
+    "weights applied to keys": ("out[h] = p @ values", "out[h] = p @ keys"),
+    "normalised by max": ("p = w / w.sum()", "p = w / w.max()"),
+    "wrong sign in exponent": ("w = np.exp(z - z.max())", "w = np.exp(z.max() - z)"),
+    "last token dropped": ("positions = np.arange(n)", "positions = np.arange(n - 1)"),
+    "K and V swapped in scatter": ("k_cache[blk, off] = k[t]", "k_cache[blk, off] = v[t]"),
+    "scatter off by one": ("blk, off = divmod(int(slot), block_size)",
+                           "blk, off = divmod(int(slot) + 1, block_size)"),
+    "negative slot not skipped": ("if slot < 0:\n            continue", "if False:\n            continue"),
+    "copy reads V into K": ("k_cache[d] = k_src[i]", "k_cache[d] = v_src[i]"),
+    "copy direction reversed": ("k_src = k_cache[src].copy()", "k_src = k_cache[dst].copy()"),
+    "widening shift wrong": ("<< np.uint32(16)", "<< np.uint32(15)"),
+    "query heads transposed": ("qf = bf16_bits_to_f64(q_s)", "qf = bf16_bits_to_f64(q_s)[::-1]"),
+}
+
+
+def mutant_module(old, new):
+    assert SRC.count(old) >= 1, f"mutation anchor not found: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(SRC.replace(old, new), "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name):
+    mod = mutant_module(*MUTANTS[name])
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(mod)
+        except Exception as e:  # AssertionError or a crash both count as caught
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"no pin caught the mutant '{name}'"
