@@ -1,0 +1,224 @@
+"""Benchmark: paged decode steps on one MI355X.
+
+A step is one pass of the whole hot path over one synthetic batch:
+copy-on-write of diverging blocks (when the workload has any), the
+new tokens' slot scatter, then paged decode attention. The default workload
+is the Llama-3-8B-shaped grouped-query decode layer: 256 sequences, 32 query
+and 8 KV heads, head size 128, 16-token blocks, context lengths lognormal
+(median 1024, sigma 0.5, clipped to [16, 4096]), a shuffled pool of 65536
+blocks.
+
+Prints one JSON line. ``value`` is algorithmic bytes per step / time per
+step (GB/s). ``roofline`` covers the decode kernel: its algorithmic bytes
+per launch / its mean launch time from HIP events on the launch stream,
+against 8 TB/s. ``cpu_baseline`` times the float64 oracle on a bounded
+sample of the same workload on this host.
+
+    python bench.py [--gpus 1] [--steps 500] [--warmup 20] [--config NAME]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention: achieved KV HBM GB/s (% of peak) and seq-steps/sec"
+PEAK_HBM_GBS = 8000.0
+DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_433_amd", "csrc", "decode.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+
+
+def source_digest(path=DECODE_SRC) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """Per-launch HBM bytes of the decode kernel from committed rocprofv3
+    counter runs, if they were taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("decode_hip_sha256_16") != source_digest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(batch, seconds: float):
+    """Time the float64 oracle on whole sequences, in a seeded order (cycling
+    through the batch), until `seconds` of work; rate in the metric's unit
+    (algorithmic GB/s)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from paged_kv_cache_433_amd import workloads as W
+
+    kc, vc = batch.k_cache, batch.v_cache
+    oracle.reshape_and_cache(kc, vc, batch.new_k, batch.new_v, batch.slot_mapping)
+    order = np.random.default_rng(0).permutation(batch.num_seqs)
+    done = []
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            for s in order:
+                oracle.decode_sequence(batch.q[s], kc, vc, batch.block_tables[s],
+                                       batch.context_lens[s], batch.scale)
+                done.append(int(s))
+                if time.perf_counter() - t0 >= seconds:
+                    break
+        dt = time.perf_counter() - t0
+    lens = batch.context_lens[done]
+    nbytes = W.algorithmic_bytes(lens, batch.num_q_heads, batch.num_kv_heads, batch.head_size)
+    return {
+        "value": round(nbytes / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"{len(done)} sequence-steps of the {batch.num_seqs}-sequence batch, taken in a "
+                   f"seeded order ({int(lens.sum())} tokens), float64 numpy oracle, BLAS limited "
+                   f"to 1 thread, {dt:.1f} s"),
+        "seq_steps_per_s": round(len(done) / dt, 3),
+    }
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="llama3_8b_gqa")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_433_amd as pa
+    from paged_kv_cache_433_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    print(f"[bench] generating {args.config}", file=sys.stderr, flush=True)
+    b = W.make_config(args.config)
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    kc, vc = bf16(b.k_cache), bf16(b.v_cache)
+    q = bf16(b.q)
+    new_k, new_v = bf16(b.new_k), bf16(b.new_v)
+    tables = torch.from_numpy(b.block_tables).to(dev)
+    lens = torch.from_numpy(b.context_lens).to(dev)
+    slots = torch.from_numpy(b.slot_mapping).to(dev)
+    pairs = torch.from_numpy(b.cow_pairs).to(dev) if len(b.cow_pairs) else None
+    out = torch.empty_like(q)
+    scale = float(b.scale)
+
+    decode_bytes = W.algorithmic_bytes(b.context_lens, b.num_q_heads, b.num_kv_heads, b.head_size)
+    step_bytes = decode_bytes + W.scatter_bytes(b.num_seqs, b.num_kv_heads, b.head_size)
+    if pairs is not None:
+        step_bytes += W.copy_bytes(len(b.cow_pairs), b.block_size, b.num_kv_heads, b.head_size)
+
+    stream = torch.cuda.current_stream(dev)
+    n_ev = args.steps
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+
+    def step(i=None):
+        if pairs is not None:
+            pa.copy_blocks(kc, vc, pairs)
+        pa.reshape_and_cache(new_k, new_v, kc, vc, slots)
+        if i is not None:
+            ev_a[i].record(stream)
+        pa.decode(q, kc, vc, tables, lens, scale, out=out)
+        if i is not None:
+            ev_b[i].record(stream)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms = total_ms / args.steps
+    dec_ms = [a.elapsed_time(z) for a, z in zip(ev_a, ev_b)]
+    dec_mean = float(np.mean(dec_ms))
+    print(f"[bench] {args.steps} steps: {ms * 1e3:.1f} us/step, decode {dec_mean * 1e3:.1f} us "
+          f"(p10 {np.percentile(dec_ms, 10) * 1e3:.1f}, p90 {np.percentile(dec_ms, 90) * 1e3:.1f})",
+          file=sys.stderr, flush=True)
+
+    value = step_bytes / (ms * 1e-3) / 1e9
+    achieved = decode_bytes / (dec_mean * 1e-3) / 1e9
+    traffic = measured_traffic(args.config)
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": args.config,
+            "num_seqs": b.num_seqs,
+            "num_q_heads": b.num_q_heads,
+            "num_kv_heads": b.num_kv_heads,
+            "head_size": b.head_size,
+            "block_size": b.block_size,
+            "kv_pool_blocks": b.num_blocks,
+            "sum_context_tokens": int(b.context_lens.sum()),
+            "seed": b.seed,
+            "step": ("copy_blocks + " if pairs is not None else "")
+                    + "reshape_and_cache + decode",
+            "parallelism": "single GPU",
+        },
+        "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
+        "seq_steps_per_s": round(b.num_seqs / (ms * 1e-3), 1),
+        "bytes_per_step": int(step_bytes),
+        "roofline": {
+            "kernel": "decode",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": int(decode_bytes),
+            "mean_launch_us": round(dec_mean * 1e3, 2),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print(f"[bench] cpu baseline (~{args.cpu_seconds:.0f} s)", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(b, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,186 @@
+/*
+ * pa.h - C ABI of the MI355X (gfx950) paged KV-cache decode library (libpa.so).
+ *
+ * The library implements the data-parallel hot path of a decode step over a
+ * KV cache kept in fixed-size, non-contiguous physical blocks:
+ *
+ *   - "vLLM: Anatomy and Mechanisms of High-Throughput LLM Inference",
+ *     section "PagedAttention: The vLLM Innovation" / "Block-Level
+ *     Management": a request's KV cache is split into logical blocks that a
+ *     block table maps to physical blocks; 16 tokens per block by default.
+ *   - the same page, section "Memory Sharing via Copy-on-Write (CoW)":
+ *     sequences share physical blocks and only the block where they diverge
+ *     is copied.
+ *   - "Inside vLLM: Anatomy of a High-Throughput LLM Inference System",
+ *     section "Scheduler": a decode step is a forward pass over the most
+ *     recent token, with every earlier K/V vector already cached; section
+ *     "LLM Engine constructor": the cache is allocated, reshaped and bound
+ *     to the attention layers (here: a caller-owned pa_kv_cache descriptor).
+ *
+ * Conventions shared by every call:
+ *   - Every data pointer is a DEVICE pointer owned by the caller. The library
+ *     never frees caller memory and keeps no state between calls, except a
+ *     thread-local error string (pa_last_error) and a process-wide call
+ *     counter that tags split-K completion counters (see pa_decode).
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the null
+ *     stream). A return of PA_OK means the work was enqueued.
+ *   - bfloat16 tensors are passed as raw 16-bit storage.
+ *   - Errors that can be seen on the host are reported before anything is
+ *     enqueued: a NULL pointer, a negative count, an unsupported dtype, head
+ *     size, block size or head grouping, or a workspace that is too small.
+ *     PA_ERR_HIP reports a failed HIP call; its text is in pa_last_error().
+ *   - Device-side indices are clamped or skipped, never trusted: a block id
+ *     outside [0, num_blocks), a slot outside the pool or a CoW pair outside
+ *     the pool never causes an out-of-bounds access. Such input makes the
+ *     affected output unspecified; the kernels still finish normally.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,        /* a required pointer is NULL */
+  PA_ERR_SHAPE = -2,       /* a count or size is negative or inconsistent */
+  PA_ERR_UNSUPPORTED = -3, /* dtype, block size, head size or grouping not built */
+  PA_ERR_WORKSPACE = -4,   /* workspace given but smaller than required */
+  PA_ERR_HIP = -5          /* a HIP runtime call failed */
+} pa_status;
+
+enum { PA_DTYPE_BF16 = 0 };
+
+/*
+ * The KV cache bound to one attention layer ("Inside vLLM", section "LLM
+ * Engine constructor": allocate, reshape and bind). K and V are separate
+ * contiguous arrays of shape [num_blocks, block_size, num_kv_heads,
+ * head_size]: element (b, t, h, d) is at ((b*block_size + t)*num_kv_heads +
+ * h)*head_size + d. One block of one array holds block_size tokens of every
+ * KV head, so a block's K plus V is 2*block_size*num_kv_heads*head_size*2
+ * bytes, the per-block size the page gives.
+ *
+ * Supported: dtype PA_DTYPE_BF16, block_size 16, head_size 64 or 128,
+ * num_blocks >= 1, num_kv_heads >= 1. The descriptor is read on every call
+ * and not kept.
+ */
+typedef struct pa_kv_cache {
+  void *k_cache;
+  void *v_cache;
+  int64_t num_blocks;
+  int32_t block_size;
+  int32_t num_kv_heads;
+  int32_t head_size;
+  int32_t dtype;
+} pa_kv_cache;
+
+/*
+ * pa_decode - attention of one new query token per sequence over that
+ * sequence's paged K/V ("Inside vLLM", section "Scheduler"; block-table
+ * indexing from "vLLM: Anatomy and Mechanisms", section "Block-Level
+ * Management").
+ *
+ * For sequence s with n = context_lens[s] cached tokens (the newest one
+ * included, so pa_reshape_and_cache of this step runs first), logical token
+ * i lives in physical block block_tables[s*max_blocks_per_seq + i/16] at
+ * offset i%16. Query head h uses KV head h / (num_q_heads/num_kv_heads).
+ *   out[s,h,:] = sum_i softmax_i(scale * q[s,h,:].k_i) * v_i
+ * computed with fp32 accumulation and stored as bfloat16 (round to nearest
+ * even). n == 0 gives a zero row.
+ *
+ *   q             bf16 [num_seqs, num_q_heads, head_size], contiguous
+ *   block_tables  int32 [num_seqs, max_blocks_per_seq]; entries at index
+ *                 >= ceil(n/16) are never read
+ *   context_lens  int32 [num_seqs]; 0 <= n <= max_blocks_per_seq*16
+ *                 (larger values are treated as max_blocks_per_seq*16)
+ *   num_q_heads   multiple of num_kv_heads, with at most 16 query heads per
+ *                 KV head
+ *   out           bf16 [num_seqs, num_q_heads, head_size]; must not alias
+ *                 any input
+ *   workspace     device scratch of at least pa_decode_workspace_bytes(...)
+ *                 bytes, or NULL. Long contexts are split into partitions
+ *                 whose partial results (running max, sum, unnormalised
+ *                 output) are merged with log-sum-exp weights; the
+ *                 workspace holds those partials and one completion counter
+ *                 per (sequence, KV head). It needs no initialisation: each
+ *                 call tags its counters with its own epoch, so contents left
+ *                 by other calls or other shapes are ignored. Calls that
+ *                 share a workspace must not overlap in time (keep them on
+ *                 one stream, or order them). With NULL the library allocates
+ *                 scratch stream-ordered (hipMallocAsync) and frees it after
+ *                 the launch.
+ *
+ * Errors: PA_ERR_NULL (cache, cache->k_cache/v_cache, q, block_tables,
+ * context_lens or out NULL while num_seqs > 0), PA_ERR_SHAPE (negative
+ * counts, max_blocks_per_seq < 1, num_q_heads % num_kv_heads != 0),
+ * PA_ERR_UNSUPPORTED (see pa_kv_cache; group size > 16), PA_ERR_WORKSPACE,
+ * PA_ERR_HIP. num_seqs == 0 is a no-op.
+ */
+int pa_decode(const pa_kv_cache *cache, const void *q, const int32_t *block_tables,
+              const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+              int32_t max_blocks_per_seq, float scale, void *out, void *workspace,
+              size_t workspace_bytes, void *stream);
+
+/*
+ * Bytes of workspace pa_decode needs for these sizes (0 when no sequence can
+ * span more than one partition). Host-only; returns 0 for invalid sizes.
+ */
+size_t pa_decode_workspace_bytes(const pa_kv_cache *cache, int32_t num_seqs,
+                                 int32_t num_q_heads, int32_t max_blocks_per_seq);
+
+/*
+ * pa_reshape_and_cache - write each new token's K and V into its physical
+ * slot before attention runs (the slot the block manager assigned on demand:
+ * "vLLM: Anatomy and Mechanisms", section "Block-Level Management"; the
+ * decode step that follows sees every earlier token cached: "Inside vLLM",
+ * section "Scheduler").
+ *
+ *   k, v          bf16 [num_tokens, num_kv_heads, head_size], contiguous
+ *   slot_mapping  int64 [num_tokens]; slot = block*16 + offset. A negative
+ *                 slot (padding) or a slot >= num_blocks*16 is skipped.
+ *                 Slots must be distinct (otherwise which token wins is
+ *                 unspecified).
+ * The copy is bit-exact. num_tokens == 0 is a no-op.
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE (num_tokens < 0), PA_ERR_UNSUPPORTED,
+ * PA_ERR_HIP.
+ */
+int pa_reshape_and_cache(const pa_kv_cache *cache, const void *k, const void *v,
+                         const int64_t *slot_mapping, int32_t num_tokens, void *stream);
+
+/*
+ * pa_copy_blocks - copy-on-write of diverging blocks ("vLLM: Anatomy and
+ * Mechanisms", section "Memory Sharing via Copy-on-Write (CoW)": only the
+ * block where beams diverge is copied).
+ *
+ *   src_dst_pairs int64 [num_pairs][2], device memory: block dst becomes a
+ *                 bit copy of block src, for K and for V. Destinations must
+ *                 be distinct and never also a source (a CoW destination is
+ *                 a fresh block); otherwise the result is unspecified. A pair
+ *                 with an index outside [0, num_blocks) is skipped.
+ * num_pairs == 0 is a no-op.
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE (num_pairs < 0), PA_ERR_UNSUPPORTED,
+ * PA_ERR_HIP.
+ */
+int pa_copy_blocks(const pa_kv_cache *cache, const int64_t *src_dst_pairs, int32_t num_pairs,
+                   void *stream);
+
+/* Text of the last error on this thread ("" after a successful call). */
+const char *pa_last_error(void);
+
+/*
+ * Measurement helper, not part of the decode path: copy `bytes` bytes (a
+ * multiple of 16, both pointers 16-byte aligned) with plain 16-byte vector
+ * loads and stores. Used to calibrate hardware byte counters and to measure
+ * achievable HBM bandwidth.
+ */
+int pa_probe_copy(void *dst, const void *src, size_t bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

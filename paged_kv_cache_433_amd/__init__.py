@@ -1,1 +1,15 @@
-"""MI355X (gfx950) paged KV-cache decode: HIP kernels behind a C ABI."""
+"""MI355X (gfx950) paged KV-cache decode: HIP kernels behind a C ABI.
+
+``decode``, ``reshape_and_cache`` and ``copy_blocks`` call libpa.so (built
+with ``python -m paged_kv_cache_433_amd.build``); the library is loaded on
+first use and a missing build raises. ``workloads`` makes seeded inputs.
+"""
+
+from .ops import (  # noqa: F401
+    PagedAttentionError,
+    copy_blocks,
+    decode,
+    decode_workspace_bytes,
+    probe_copy,
+    reshape_and_cache,
+)

@@ -1,0 +1,105 @@
+// Cache maintenance kernels for CDNA4 (gfx950): slot scatter, copy-on-write
+// block copy, and a plain 16-byte copy used for measurement.
+//
+// Both cache kernels are bit copies. They only move 16-byte vectors, and
+// every index taken from device memory is range-checked: a slot or block
+// outside the pool is skipped, never dereferenced.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// One workgroup per new token. The token's K row and V row (num_kv_heads *
+// head_size elements each) go to physical slot slot_mapping[t]: offset
+// slot % 16 of block slot / 16 ("vLLM: Anatomy and Mechanisms of
+// High-Throughput LLM Inference", section "Block-Level Management": a block
+// from the free pool receives the tokens of its logical block as they come).
+// In the [num_blocks, 16, Hkv, D] layout a slot's row is contiguous and
+// starts at element slot * row_elems.
+__global__ __launch_bounds__(256) void reshape_and_cache_kernel(
+    const uint16_t *__restrict__ k, const uint16_t *__restrict__ v, const int64_t *__restrict__ slots,
+    uint16_t *__restrict__ k_cache, uint16_t *__restrict__ v_cache, int32_t row_elems,
+    int64_t num_slots) {
+  const int t = blockIdx.x;
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= num_slots) return;
+  const int vecs = row_elems / 8;
+  const u32x4_t *ks = reinterpret_cast<const u32x4_t *>(k + (size_t)t * row_elems);
+  const u32x4_t *vs = reinterpret_cast<const u32x4_t *>(v + (size_t)t * row_elems);
+  u32x4_t *kd = reinterpret_cast<u32x4_t *>(k_cache + (size_t)slot * row_elems);
+  u32x4_t *vd = reinterpret_cast<u32x4_t *>(v_cache + (size_t)slot * row_elems);
+  for (int i = threadIdx.x; i < vecs; i += blockDim.x) {
+    kd[i] = ks[i];
+    vd[i] = vs[i];
+  }
+}
+
+// grid.x = pair, grid.y = 0 for K and 1 for V, grid.z = chunk of the block.
+// Block dst becomes a copy of block src ("vLLM: Anatomy and Mechanisms",
+// section "Memory Sharing via Copy-on-Write (CoW)": only the block where the
+// beams diverge is copied).
+__global__ __launch_bounds__(256) void copy_blocks_kernel(uint16_t *__restrict__ k_cache,
+                                                          uint16_t *__restrict__ v_cache,
+                                                          const int64_t *__restrict__ pairs,
+                                                          int64_t block_elems, int64_t num_blocks,
+                                                          int32_t chunk_vecs) {
+  const int64_t src = pairs[2 * (size_t)blockIdx.x];
+  const int64_t dst = pairs[2 * (size_t)blockIdx.x + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  uint16_t *cache = blockIdx.y ? v_cache : k_cache;
+  const u32x4_t *from = reinterpret_cast<const u32x4_t *>(cache + (size_t)src * block_elems);
+  u32x4_t *to = reinterpret_cast<u32x4_t *>(cache + (size_t)dst * block_elems);
+  const int64_t vecs = block_elems / 8;
+  const int64_t lo = (int64_t)blockIdx.z * chunk_vecs;
+  const int64_t hi = lo + chunk_vecs < vecs ? lo + chunk_vecs : vecs;
+  for (int64_t i = lo + threadIdx.x; i < hi; i += blockDim.x) to[i] = from[i];
+}
+
+// Grid-stride 16-byte copy (measurement helper).
+__global__ __launch_bounds__(256) void probe_copy_kernel(u32x4_t *__restrict__ dst,
+                                                         const u32x4_t *__restrict__ src,
+                                                         size_t vecs) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < vecs; i += stride) dst[i] = src[i];
+}
+
+}  // namespace
+
+hipError_t launch_reshape_and_cache(const uint16_t *k, const uint16_t *v, const int64_t *slots,
+                                    uint16_t *k_cache, uint16_t *v_cache, int32_t num_tokens,
+                                    int32_t row_elems, int64_t num_slots, hipStream_t stream) {
+  const int vecs = row_elems / 8;
+  const int threads = vecs >= 256 ? 256 : ((vecs + 63) / 64) * 64;
+  hipLaunchKernelGGL(reshape_and_cache_kernel, dim3((unsigned)num_tokens), dim3(threads), 0, stream,
+                     k, v, slots, k_cache, v_cache, row_elems, num_slots);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(uint16_t *k_cache, uint16_t *v_cache, const int64_t *pairs,
+                              int32_t num_pairs, int64_t block_elems, int64_t num_blocks,
+                              hipStream_t stream) {
+  const int64_t vecs = block_elems / 8;
+  const int32_t chunk = 2048;  // 32 KiB of a block per workgroup
+  const unsigned chunks = (unsigned)((vecs + chunk - 1) / chunk);
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)num_pairs, 2, chunks), dim3(256), 0, stream,
+                     k_cache, v_cache, pairs, block_elems, num_blocks, chunk);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_copy(void *dst, const void *src, size_t bytes, hipStream_t stream) {
+  const size_t vecs = bytes / 16;
+  size_t blocks = (vecs + 255) / 256;
+  if (blocks > 256 * 64) blocks = 256 * 64;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(probe_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     static_cast<u32x4_t *>(dst), static_cast<const u32x4_t *>(src), vecs);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,240 @@
+// C-ABI front end of libpa.so: argument checks, decode planning, workspace
+// handling and launches. Every check here runs on the host before any HIP
+// call, so argument errors are reported without a GPU.
+
+#include <stdlib.h>
+#include <string.h>
+
+#include <atomic>
+#include <string>
+
+#include "../../include/pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+int fail(int code, const std::string &msg) {
+  g_error = msg;
+  return code;
+}
+
+int ok() {
+  g_error.clear();
+  return PA_OK;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+  return fail(PA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// Blocks per split-K partition. Default: start at 64 blocks (1024 tokens)
+// and halve, down to 8 blocks, while a batch whose sequences all reached
+// max_blocks_per_seq would give fewer than 2048 (sequence, KV head,
+// partition) work items, so short batches still fill the GPU.
+// PA_PARTITION_TOKENS overrides (rounded to an even block count in [2, 64]).
+int32_t partition_blocks(int32_t num_seqs, int32_t num_kv_heads, int32_t max_blocks_per_seq) {
+  int32_t blocks = 64;
+  const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
+  while (blocks > 8 && pairs * ((max_blocks_per_seq + blocks - 1) / blocks) < 2048) blocks /= 2;
+  if (const char *env = getenv("PA_PARTITION_TOKENS")) {
+    const long tokens = strtol(env, nullptr, 10);
+    if (tokens > 0) blocks = (int32_t)((tokens + 15) / 16);
+  }
+  blocks = (blocks + 1) & ~1;
+  if (blocks < 2) blocks = 2;
+  if (blocks > 64) blocks = 64;
+  return blocks;
+}
+
+// Split calls are merged by a separate kernel by default. With
+// PA_FUSED_MERGE_MAX_PARTS=N (N > 1), calls with at most N partitions per
+// sequence instead let the last partition to finish merge. That saves a launch
+// but needs device-scope fences, which write back and invalidate L2 on every
+// split wave. On gfx950 that costs more than the launch for large batches.
+int32_t fused_merge_max_parts() {
+  int32_t v = 0;
+  if (const char *env = getenv("PA_FUSED_MERGE_MAX_PARTS")) v = (int32_t)strtol(env, nullptr, 10);
+  return v;
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Per-call tag of the split-K completion counters (never 0).
+std::atomic<uint32_t> g_epoch{0};
+
+uint32_t next_epoch() {
+  uint32_t e;
+  do {
+    e = g_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
+  } while (e == 0);
+  return e;
+}
+
+int check_cache(const pa_kv_cache *c, bool need_data) {
+  if (!c) return fail(PA_ERR_NULL, "cache descriptor is NULL");
+  if (need_data && (!c->k_cache || !c->v_cache)) return fail(PA_ERR_NULL, "k_cache or v_cache is NULL");
+  if (c->dtype != PA_DTYPE_BF16) return fail(PA_ERR_UNSUPPORTED, "only bf16 caches are supported");
+  if (c->block_size != 16) return fail(PA_ERR_UNSUPPORTED, "only block_size 16 is supported");
+  if (c->head_size != 64 && c->head_size != 128)
+    return fail(PA_ERR_UNSUPPORTED, "head_size must be 64 or 128");
+  if (c->num_blocks < 1) return fail(PA_ERR_SHAPE, "num_blocks must be >= 1");
+  if (c->num_kv_heads < 1) return fail(PA_ERR_SHAPE, "num_kv_heads must be >= 1");
+  return PA_OK;
+}
+
+int check_decode_shape(const pa_kv_cache *c, int32_t num_seqs, int32_t num_q_heads,
+                       int32_t max_blocks_per_seq) {
+  if (num_seqs < 0) return fail(PA_ERR_SHAPE, "num_seqs < 0");
+  if (max_blocks_per_seq < 1) return fail(PA_ERR_SHAPE, "max_blocks_per_seq must be >= 1");
+  if (num_q_heads < 1 || num_q_heads % c->num_kv_heads != 0)
+    return fail(PA_ERR_SHAPE, "num_q_heads must be a positive multiple of num_kv_heads");
+  if (num_q_heads / c->num_kv_heads > 16)
+    return fail(PA_ERR_UNSUPPORTED, "more than 16 query heads per KV head");
+  if ((int64_t)max_blocks_per_seq * 16 > 0x7fffffffLL)
+    return fail(PA_ERR_SHAPE, "max_blocks_per_seq too large");
+  if ((int64_t)num_seqs * c->num_kv_heads > 0x7fffffffLL)
+    return fail(PA_ERR_SHAPE, "num_seqs * num_kv_heads too large");
+  return PA_OK;
+}
+
+}  // namespace
+
+namespace pa {
+
+DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t head_size, int32_t max_blocks_per_seq) {
+  DecodePlan p{};
+  p.part_blocks = partition_blocks(num_seqs, num_kv_heads, max_blocks_per_seq);
+  p.max_parts = (max_blocks_per_seq + p.part_blocks - 1) / p.part_blocks;
+  p.fused_merge = (p.max_parts > 1 && p.max_parts <= fused_merge_max_parts()) ? 1 : 0;
+  if (p.max_parts <= 1) return p;
+  const size_t rows = (size_t)num_seqs * num_q_heads * p.max_parts;
+  p.counters_bytes = round_up((size_t)num_seqs * num_kv_heads * sizeof(unsigned long long), 256);
+  p.ml_bytes = round_up(rows * 2 * sizeof(float), 256);
+  p.o_bytes = round_up(rows * head_size * sizeof(float), 256);
+  p.total_bytes = p.counters_bytes + p.ml_bytes + p.o_bytes;
+  return p;
+}
+
+}  // namespace pa
+
+extern "C" {
+
+const char *pa_last_error(void) { return g_error.c_str(); }
+
+size_t pa_decode_workspace_bytes(const pa_kv_cache *cache, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t max_blocks_per_seq) {
+  if (check_cache(cache, false) != PA_OK) return 0;
+  if (check_decode_shape(cache, num_seqs, num_q_heads, max_blocks_per_seq) != PA_OK) return 0;
+  return pa::plan_decode(num_seqs, num_q_heads, cache->num_kv_heads, cache->head_size,
+                         max_blocks_per_seq)
+      .total_bytes;
+}
+
+int pa_decode(const pa_kv_cache *cache, const void *q, const int32_t *block_tables,
+              const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+              int32_t max_blocks_per_seq, float scale, void *out, void *workspace,
+              size_t workspace_bytes, void *stream) {
+  int rc = check_cache(cache, num_seqs > 0);
+  if (rc != PA_OK) return rc;
+  rc = check_decode_shape(cache, num_seqs, num_q_heads, max_blocks_per_seq);
+  if (rc != PA_OK) return rc;
+  if (num_seqs == 0) return ok();
+  if (!q || !block_tables || !context_lens || !out)
+    return fail(PA_ERR_NULL, "q, block_tables, context_lens or out is NULL");
+
+  const pa::DecodePlan plan = pa::plan_decode(num_seqs, num_q_heads, cache->num_kv_heads,
+                                              cache->head_size, max_blocks_per_seq);
+  if (plan.max_parts > 65535) return fail(PA_ERR_SHAPE, "too many partitions per sequence");
+  if (workspace && workspace_bytes < plan.total_bytes)
+    return fail(PA_ERR_WORKSPACE, "workspace smaller than pa_decode_workspace_bytes()");
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  void *ws = workspace;
+  bool owned = false;
+  if (plan.total_bytes && !ws) {
+    hipError_t e = hipMallocAsync(&ws, plan.total_bytes, hs);
+    if (e != hipSuccess) return hip_fail(e, "hipMallocAsync(workspace)");
+    owned = true;
+  }
+
+  pa::DecodeArgs a{};
+  a.q = static_cast<const uint16_t *>(q);
+  a.k_cache = static_cast<const uint16_t *>(cache->k_cache);
+  a.v_cache = static_cast<const uint16_t *>(cache->v_cache);
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.out = static_cast<uint16_t *>(out);
+  if (plan.total_bytes) {
+    char *base = static_cast<char *>(ws);
+    a.counters = reinterpret_cast<unsigned long long *>(base);
+    a.part_ml = reinterpret_cast<float *>(base + plan.counters_bytes);
+    a.part_o = reinterpret_cast<float *>(base + plan.counters_bytes + plan.ml_bytes);
+  }
+  a.num_blocks = cache->num_blocks;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.group = num_q_heads / cache->num_kv_heads;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.part_blocks = plan.part_blocks;
+  a.max_parts = plan.max_parts;
+  a.fused_merge = plan.fused_merge;
+  a.scale_log2 = scale * 1.44269504088896340736f;
+  a.epoch = next_epoch();
+
+  hipError_t e = pa::launch_decode(a, cache->head_size, hs);
+  if (owned) {
+    hipError_t fe = hipFreeAsync(ws, hs);
+    if (e == hipSuccess) e = fe;
+  }
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return ok();
+}
+
+int pa_reshape_and_cache(const pa_kv_cache *cache, const void *k, const void *v,
+                         const int64_t *slot_mapping, int32_t num_tokens, void *stream) {
+  int rc = check_cache(cache, num_tokens > 0);
+  if (rc != PA_OK) return rc;
+  if (num_tokens < 0) return fail(PA_ERR_SHAPE, "num_tokens < 0");
+  if (num_tokens == 0) return ok();
+  if (!k || !v || !slot_mapping) return fail(PA_ERR_NULL, "k, v or slot_mapping is NULL");
+  const int64_t row = (int64_t)cache->num_kv_heads * cache->head_size;
+  if (row > 0x7fffffffLL) return fail(PA_ERR_SHAPE, "num_kv_heads * head_size too large");
+  hipError_t e = pa::launch_reshape_and_cache(
+      static_cast<const uint16_t *>(k), static_cast<const uint16_t *>(v), slot_mapping,
+      static_cast<uint16_t *>(cache->k_cache), static_cast<uint16_t *>(cache->v_cache), num_tokens,
+      (int32_t)row, cache->num_blocks * cache->block_size, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "reshape_and_cache launch");
+  return ok();
+}
+
+int pa_copy_blocks(const pa_kv_cache *cache, const int64_t *src_dst_pairs, int32_t num_pairs,
+                   void *stream) {
+  int rc = check_cache(cache, num_pairs > 0);
+  if (rc != PA_OK) return rc;
+  if (num_pairs < 0) return fail(PA_ERR_SHAPE, "num_pairs < 0");
+  if (num_pairs == 0) return ok();
+  if (!src_dst_pairs) return fail(PA_ERR_NULL, "src_dst_pairs is NULL");
+  const int64_t block_elems = (int64_t)cache->block_size * cache->num_kv_heads * cache->head_size;
+  hipError_t e = pa::launch_copy_blocks(static_cast<uint16_t *>(cache->k_cache),
+                                        static_cast<uint16_t *>(cache->v_cache), src_dst_pairs,
+                                        num_pairs, block_elems, cache->num_blocks,
+                                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "copy_blocks launch");
+  return ok();
+}
+
+int pa_probe_copy(void *dst, const void *src, size_t bytes, void *stream) {
+  if (bytes == 0) return ok();
+  if (!dst || !src) return fail(PA_ERR_NULL, "dst or src is NULL");
+  if (bytes % 16 || (reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(src)) % 16)
+    return fail(PA_ERR_SHAPE, "probe copy needs 16-byte sizes and alignment");
+  hipError_t e = pa::launch_probe_copy(dst, src, bytes, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "probe copy launch");
+  return ok();
+}
+
+}  // extern "C"

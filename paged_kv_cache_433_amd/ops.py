@@ -1,0 +1,134 @@
+"""torch-facing calls of the paged decode library.
+
+Argument marshalling only: tensors are checked for dtype, device, shape and
+contiguity, then their pointers and the current HIP stream go to libpa.so.
+Every step of the computation runs in the library's HIP kernels; there is
+no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+
+_BF16 = torch.bfloat16
+
+
+class PagedAttentionError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"libpa error {code}: {message}")
+        self.code = code
+
+
+def _check(rc: int) -> None:
+    if rc != _lib.PA_OK:
+        raise PagedAttentionError(rc, _lib.last_error())
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _cache_desc(k_cache: torch.Tensor, v_cache: torch.Tensor) -> _lib.KVCacheDesc:
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if t.dtype != _BF16 or t.dim() != 4 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous bf16 CUDA tensor "
+                             "[num_blocks, block_size, num_kv_heads, head_size]")
+    if k_cache.shape != v_cache.shape or k_cache.device != v_cache.device:
+        raise ValueError("k_cache and v_cache must have the same shape and device")
+    nb, bs, hkv, d = k_cache.shape
+    return _lib.KVCacheDesc(k_cache.data_ptr(), v_cache.data_ptr(), nb, bs, hkv, d,
+                            _lib.PA_DTYPE_BF16)
+
+
+def _need(t, name, dtype, shape, device):
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous() or t.device != device:
+        raise ValueError(f"{name}: expected contiguous {dtype} {tuple(shape)} on {device}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+_workspaces: dict = {}
+
+
+def _workspace(device, nbytes: int) -> torch.Tensor:
+    """A scratch buffer per (device, stream), grown on demand.
+
+    One buffer per stream keeps calls that share it ordered; its contents
+    need no initialisation.
+    """
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def decode_workspace_bytes(k_cache, num_seqs, num_q_heads, max_blocks_per_seq) -> int:
+    desc = _cache_desc(k_cache, k_cache)
+    return int(_lib.lib().pa_decode_workspace_bytes(ctypes.byref(desc), num_seqs, num_q_heads,
+                                                   max_blocks_per_seq))
+
+
+def decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=None, workspace=None):
+    """Paged decode attention; returns ``out`` (bf16 ``[num_seqs, num_q_heads, head_size]``).
+
+    ``block_tables`` int32 ``[num_seqs, max_blocks_per_seq]``, ``context_lens``
+    int32 ``[num_seqs]`` (newest token included). Runs on the current stream.
+    """
+    desc = _cache_desc(k_cache, v_cache)
+    dev = k_cache.device
+    S, hq, d = q.shape
+    _need(q, "q", _BF16, (S, hq, k_cache.shape[3]), dev)
+    mb = block_tables.shape[1] if block_tables.dim() == 2 else -1
+    _need(block_tables, "block_tables", torch.int32, (S, mb), dev)
+    _need(context_lens, "context_lens", torch.int32, (S,), dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", _BF16, (S, hq, d), dev)
+    lib = _lib.lib()
+    nbytes = int(lib.pa_decode_workspace_bytes(ctypes.byref(desc), S, hq, mb))
+    if workspace is None and nbytes:
+        workspace = _workspace(dev, nbytes)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.pa_decode(ctypes.byref(desc), _ptr(q), _ptr(block_tables), _ptr(context_lens), S, hq,
+                         mb, float(scale), _ptr(out), _ptr(workspace), ws_bytes, _stream(dev)))
+    return out
+
+
+def reshape_and_cache(k, v, k_cache, v_cache, slot_mapping) -> None:
+    """Scatter new tokens' K/V (bf16 ``[T, num_kv_heads, head_size]``) into
+    their slots (int64 ``[T]``; negative = skip), in place, on the current stream."""
+    desc = _cache_desc(k_cache, v_cache)
+    dev = k_cache.device
+    T = k.shape[0]
+    _need(k, "k", _BF16, (T,) + tuple(k_cache.shape[2:]), dev)
+    _need(v, "v", _BF16, (T,) + tuple(k_cache.shape[2:]), dev)
+    _need(slot_mapping, "slot_mapping", torch.int64, (T,), dev)
+    _check(_lib.lib().pa_reshape_and_cache(ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(slot_mapping),
+                                           T, _stream(dev)))
+
+
+def copy_blocks(k_cache, v_cache, src_dst_pairs) -> None:
+    """Copy-on-write: block ``dst`` becomes a copy of block ``src`` for every
+    row of ``src_dst_pairs`` (int64 ``[P, 2]``, device), K and V, in place."""
+    desc = _cache_desc(k_cache, v_cache)
+    dev = k_cache.device
+    P = src_dst_pairs.shape[0]
+    _need(src_dst_pairs, "src_dst_pairs", torch.int64, (P, 2), dev)
+    _check(_lib.lib().pa_copy_blocks(ctypes.byref(desc), _ptr(src_dst_pairs), P, _stream(dev)))
+
+
+def probe_copy(dst: torch.Tensor, src: torch.Tensor) -> None:
+    """Plain 16-byte-vector copy of ``src`` into ``dst`` (measurement helper)."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst smaller than src")
+    _check(_lib.lib().pa_probe_copy(_ptr(dst), _ptr(src), nbytes, _stream(src.device)))
