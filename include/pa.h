@@ -20,8 +20,7 @@
  * Conventions shared by every call:
  *   - Every data pointer is a DEVICE pointer owned by the caller. The library
  *     never frees caller memory and keeps no state between calls, except a
- *     thread-local error string (pa_last_error) and a process-wide call
- *     counter that tags split-K completion counters (see pa_decode).
+ *     thread-local error string (pa_last_error).
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the null
  *     stream). A return of PA_OK means the work was enqueued.
  *   - bfloat16 tensors are passed as raw 16-bit storage.
@@ -102,23 +101,28 @@ typedef struct pa_kv_cache {
  *   out           bf16 [num_seqs, num_q_heads, head_size]; must not alias
  *                 any input
  *   workspace     device scratch of at least pa_decode_workspace_bytes(...)
- *                 bytes, or NULL. Long contexts are split into partitions
- *                 whose partial results (running max, sum, unnormalised
- *                 output) are merged with log-sum-exp weights; the
- *                 workspace holds those partials and one completion counter
- *                 per (sequence, KV head). It needs no initialisation: each
- *                 call tags its counters with its own epoch, so contents left
- *                 by other calls or other shapes are ignored. Calls that
- *                 share a workspace must not overlap in time (keep them on
- *                 one stream, or order them). With NULL the library allocates
- *                 scratch stream-ordered (hipMallocAsync) and frees it after
- *                 the launch.
+ *                 bytes, 16-byte aligned, or NULL. The call shares the K/V
+ *                 blocks of the whole batch evenly among its workgroups, so a
+ *                 sequence can be cut into pieces; each piece leaves partial
+ *                 results (running max, sum, unnormalised output) that a
+ *                 second kernel merges with log-sum-exp weights. The
+ *                 workspace holds those partials and one merge record per
+ *                 (sequence, group of up to 8 KV heads). It needs no
+ *                 initialisation: every call rewrites what it reads. Calls
+ *                 that share a workspace must not overlap in time (keep them
+ *                 on one stream, or order them). With NULL the library
+ *                 allocates scratch stream-ordered (hipMallocAsync) and frees
+ *                 it after the launch.
+ *
+ * The output does not depend on where blocks sit in the pool. It is
+ * reproducible bit for bit for the same sizes and context lengths (no
+ * atomics; the cut points depend only on those).
  *
  * Errors: PA_ERR_NULL (cache, cache->k_cache/v_cache, q, block_tables,
  * context_lens or out NULL while num_seqs > 0), PA_ERR_SHAPE (negative
  * counts, max_blocks_per_seq < 1, num_q_heads % num_kv_heads != 0),
- * PA_ERR_UNSUPPORTED (see pa_kv_cache; group size > 16), PA_ERR_WORKSPACE,
- * PA_ERR_HIP. num_seqs == 0 is a no-op.
+ * PA_ERR_UNSUPPORTED (see pa_kv_cache; group size > 16), PA_ERR_WORKSPACE
+ * (too small or misaligned), PA_ERR_HIP. num_seqs == 0 is a no-op.
  */
 int pa_decode(const pa_kv_cache *cache, const void *q, const int32_t *block_tables,
               const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
@@ -126,8 +130,9 @@ int pa_decode(const pa_kv_cache *cache, const void *q, const int32_t *block_tabl
               size_t workspace_bytes, void *stream);
 
 /*
- * Bytes of workspace pa_decode needs for these sizes (0 when no sequence can
- * span more than one partition). Host-only; returns 0 for invalid sizes.
+ * Bytes of workspace pa_decode needs for these sizes (0 when the call runs
+ * as a single workgroup and nothing is cut). Host-only; depends on the sizes
+ * alone, not on the device or the data; returns 0 for invalid sizes.
  */
 size_t pa_decode_workspace_bytes(const pa_kv_cache *cache, int32_t num_seqs,
                                  int32_t num_q_heads, int32_t max_blocks_per_seq);
@@ -178,6 +183,18 @@ const char *pa_last_error(void);
  * achievable HBM bandwidth.
  */
 int pa_probe_copy(void *dst, const void *src, size_t bytes, void *stream);
+
+/*
+ * Measurement helper, not part of the decode path: read `bytes` bytes of
+ * device memory at `src` (a multiple of 16, 16-byte aligned) with plain
+ * 16-byte vector loads and write one folded 32-bit word per thread to the
+ * device buffer `sink` (at least pa_probe_read_sink_bytes() bytes), so that
+ * the achievable HBM read bandwidth can be timed. Errors: PA_ERR_NULL,
+ * PA_ERR_SHAPE (size or alignment), PA_ERR_WORKSPACE (sink too small),
+ * PA_ERR_HIP.
+ */
+size_t pa_probe_read_sink_bytes(void);
+int pa_probe_read(const void *src, size_t bytes, void *sink, size_t sink_bytes, void *stream);
 
 #ifdef __cplusplus
 }

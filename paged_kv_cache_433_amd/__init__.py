@@ -11,5 +11,6 @@ from .ops import (  # noqa: F401
     decode,
     decode_workspace_bytes,
     probe_copy,
+    probe_read,
     reshape_and_cache,
 )

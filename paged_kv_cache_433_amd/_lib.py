@@ -19,7 +19,7 @@ PA_DTYPE_BF16 = 0
 
 # Every function include/pa.h declares.
 EXPORTS = ("pa_decode", "pa_decode_workspace_bytes", "pa_reshape_and_cache", "pa_copy_blocks",
-           "pa_last_error", "pa_probe_copy")
+           "pa_last_error", "pa_probe_copy", "pa_probe_read", "pa_probe_read_sink_bytes")
 
 
 class KVCacheDesc(ctypes.Structure):
@@ -56,6 +56,10 @@ def _declare(lib):
     lib.pa_last_error.restype = ctypes.c_char_p
     lib.pa_probe_copy.argtypes = [P, P, SZ, P]
     lib.pa_probe_copy.restype = ctypes.c_int
+    lib.pa_probe_read.argtypes = [P, SZ, P, SZ, P]
+    lib.pa_probe_read.restype = ctypes.c_int
+    lib.pa_probe_read_sink_bytes.argtypes = []
+    lib.pa_probe_read_sink_bytes.restype = SZ
     _ = I64
     return lib
 

@@ -69,6 +69,17 @@ __global__ __launch_bounds__(256) void probe_copy_kernel(u32x4_t *__restrict__ d
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < vecs; i += stride) dst[i] = src[i];
 }
 
+// Grid-stride 16-byte reads folded with xor; one word per thread goes to
+// `sink` so the loads cannot be dropped (measurement helper).
+__global__ __launch_bounds__(256) void probe_read_kernel(const u32x4_t *__restrict__ src,
+                                                         size_t vecs, uint32_t *__restrict__ sink) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  const size_t tid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  u32x4_t acc = {0, 0, 0, 0};
+  for (size_t i = tid; i < vecs; i += stride) acc ^= src[i];
+  sink[tid] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
 }  // namespace
 
 hipError_t launch_reshape_and_cache(const uint16_t *k, const uint16_t *v, const int64_t *slots,
@@ -99,6 +110,14 @@ hipError_t launch_probe_copy(void *dst, const void *src, size_t bytes, hipStream
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(probe_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                      static_cast<u32x4_t *>(dst), static_cast<const u32x4_t *>(src), vecs);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream) {
+  const size_t vecs = bytes / 16;
+  if (vecs == 0) return hipSuccess;
+  hipLaunchKernelGGL(probe_read_kernel, dim3(kProbeReadBlocks), dim3(256), 0, stream,
+                     static_cast<const u32x4_t *>(src), vecs, sink);
   return hipGetLastError();
 }
 

@@ -7,45 +7,50 @@
 // "Block-Level Management"; decode semantics from "Inside vLLM: Anatomy of a
 // High-Throughput LLM Inference System", section "Scheduler").
 //
-// Work split. One wavefront (64 lanes, one workgroup) owns one (sequence,
-// KV head, partition) item: a run of `part_blocks` blocks. It serves every
-// query head of the KV head's group (G <= 16), so each K/V byte is read
-// from HBM once for the whole group. A sequence that fits one partition
-// writes its bf16 output directly. Longer ones write fp32 partials (running
-// max, sum, unnormalised output) that are merged with log-sum-exp weights:
-// by the last partition to finish (an epoch-tagged counter per sequence and
-// KV head in the workspace), or by a separate merge kernel when there are
-// many partitions.
+// Work split (balanced). KV heads form groups of HG heads (HG = largest
+// divisor of num_kv_heads that is <= 8). A "unit" is one physical block of
+// one sequence for one head group; a "segment" is all units of one
+// (sequence, head group), in logical order. Segments are laid end to end in
+// (sequence, head group) order, and workgroup w takes units
+// [w*U/E, (w+1)*U/E) of the U in total, E = min(W, U) of the W workgroups
+// (the last W - E get nothing), whatever the context lengths are, so
+// every workgroup moves the same number of K/V bytes and the grid has no long
+// tail. A workgroup has one wavefront per KV head of the group; all of its
+// wavefronts walk the same blocks, so the 2 KiB token rows of a group are read
+// together. Each workgroup finds its start itself: it sums and scans the
+// clamped context lengths (cheap next to the K/V it streams).
 //
-// Inner loop, per pair of blocks (32 tokens), all on matrix cores:
-//   * QK^T on v_mfma_f32_16x16x32_bf16: rows are the 16 tokens of a block,
-//     columns the 16 query-head slots, and the reduction runs over head_size.
-//     Lane (c, grp) (c = lane % 16, grp = lane / 16) loads, for MFMA step
-//     j, the 16 bytes at head dims 32*j + 8*grp of token c's row, so each
-//     load instruction reads a contiguous 64-byte piece of 16 token rows. The
-//     sum over head_size is order-free, so q is loaded with the same mapping.
-//     The result gives lane (c, grp) the logits of query head c for tokens
-//     4*grp..4*grp+3.
-//   * V must be transposed (tokens along registers) before it can be a
-//     matrix operand of P*V. The transpose is itself an MFMA: multiplying the
-//     V rows by a one-hot 16x16 selector (v_mfma_f32_16x16x16_bf16) lands,
-//     in lane (c, grp), V[4*grp + r][d(c)] for r = 0..3. That is exactly the
-//     token set whose probabilities the same lane holds. The values are exact
-//     bf16, so their upper halves repack into an operand with v_perm.
-//   * P*V on v_mfma_f32_16x16x32_bf16, with P split into two bf16 terms
-//     (high part plus rounding residue) so the product keeps about 16
-//     significant bits of P. The accumulator layout leaves lane (c, grp)
-//     with output dims 32*j + 8*grp .. +7 of query head c for every j, so
-//     results leave as 16-byte stores.
+// A segment that lies inside one workgroup is finished there and written as
+// bf16. A segment cut by workgroup boundaries leaves fp32 partials (running
+// max in base 2, sum, unnormalised output) from each piece; the workgroup
+// that holds its last unit records which pieces exist, and merge_kernel
+// combines them with log-sum-exp weights after the decode kernel.
+//
+// Inner loop, per block (16 tokens), on matrix cores:
+//   * QK^T on v_mfma_f32_16x16x32_bf16: rows are the 16 tokens of the block,
+//     columns the 16 query-head slots, the reduction runs over head_size.
+//     Lane (c, grp) (c = lane % 16, grp = lane / 16) loads, for MFMA step j,
+//     the 16 bytes at head dims 32*j + 8*grp of token c's row; q is loaded
+//     with the same mapping (the sum over head_size is order-free). The
+//     result gives lane (c, grp) the logits of query head c for tokens
+//     4*grp .. 4*grp+3.
+//   * V is transposed (tokens along registers) by an MFMA with a one-hot
+//     16x16 selector (v_mfma_f32_16x16x16_bf16): lane (c, grp) receives
+//     V[4*grp + r][d(c)], r = 0..3, exactly the tokens whose probabilities it
+//     holds. The values are exact bf16, so their upper halves repack into an
+//     operand with v_perm.
+//   * P*V on v_mfma_f32_16x16x16_bf16 with P split into two bf16 terms (high
+//     part plus rounding residue), which keeps about 16 significant bits of
+//     P. The accumulators leave lane (c, grp) with output dims
+//     32*j + 8*grp .. +7 of query head c, stored as 16-byte vectors.
 // Online softmax works in base 2 (logits prescaled by scale*log2 e, hardware
 // exp2). Row maxima are shared by the four lanes of a head with two
-// cross-lane exchanges per pair of blocks; row sums stay lane-partial until
-// the end.
+// cross-lane exchanges per block; row sums stay lane-partial until the end.
 //
-// Tokens past the context length are masked by a select on the logit, and
-// their V rows are zeroed, so stale data in the tail of the last block
-// (even NaN) cannot reach the output. Block ids are clamped to the pool, and
-// no table entry past the last used block is read.
+// Tokens past the context length are masked by a select on the logit and
+// their V rows are zeroed, so stale data in the tail of the last block (even
+// NaN) cannot reach the output. Block ids are clamped to the pool, and no
+// table entry past a sequence's last used block is read.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -98,6 +103,19 @@ __device__ __forceinline__ u32x4_t load16(const uint16_t *p) {
   return *reinterpret_cast<const u32x4_t *>(p);
 }
 
+__device__ __forceinline__ int clamp_len(int n, int cap) { return n < 0 ? 0 : (n > cap ? cap : n); }
+
+// Workgroup w's first unit, w <= E: floor(w * U / E). With E <= U every
+// range is non-empty.
+__device__ __forceinline__ long long range_lo(long long w, long long U, long long E) {
+  return w * U / E;
+}
+
+// The workgroup whose range holds unit u: the w with lo(w) <= u < lo(w+1).
+__device__ __forceinline__ int owner_of(long long u, long long U, long long E) {
+  return (int)(((u + 1) * E - 1) / U);
+}
+
 // Store the lane's outputs as bf16: accumulator tiles 2j and 2j+1 hold head
 // dims 32*j + 8*grp + 0..3 and + 4..7; `dst` already points at 8*grp.
 template <int NJ>
@@ -112,266 +130,304 @@ __device__ __forceinline__ void store_out(uint16_t *dst, const f32x4_t (&acc)[2 
   }
 }
 
-// Count this partition as finished; return how many of this call's
-// partitions have finished, this one included. A counter word holds the
-// call's epoch in its upper half and the count in its lower half, so a word
-// left over from another call (or never initialised) reads as zero
-// arrivals: the first arrival of this call replaces it. Lock-free: every
-// failed compare-and-swap means another arrival succeeded, so at most one
-// retry per partition.
-__device__ __forceinline__ int arrive(unsigned long long *ctr, uint32_t epoch) {
-  unsigned long long old = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  while (true) {
-    const unsigned long long want = (uint32_t)(old >> 32) == epoch
-                                        ? old + 1ull
-                                        : (((unsigned long long)epoch << 32) | 1ull);
-    const unsigned long long seen = atomicCAS(ctr, old, want);
-    if (seen == old) return (int)(uint32_t)want;
-    old = seen;
-  }
+// Sum of `v` over the workgroup (every thread gets the result). `red` holds
+// one slot per wavefront; the call starts and ends with a barrier so it can
+// be called repeatedly.
+__device__ __forceinline__ long long wg_sum(long long v, long long *red, int wave, int lane,
+                                            int nwaves) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  long long t = 0;
+  for (int i = 0; i < nwaves; ++i) t += red[i];
+  return t;
 }
 
+// Attention of one wavefront's query heads over blocks [b_begin, b_end) of
+// sequence s, KV head g (n tokens cached). Returns, for query head c of the
+// group (lane (c, grp)), the running max m_run (base 2), this lane's share
+// of the sum of weights l_part, and the unnormalised output in acc.
 template <int D>
-__global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
-  constexpr int NJ = D / 32;  // MFMA steps over head_size; 16-byte loads per lane per row
-  static_assert(NJ >= 1 && D % 32 == 0, "head_size must be a multiple of 32");
-
-  const int lane = threadIdx.x;
+__device__ __forceinline__ void attend_blocks(const DecodeArgs &a, int s, int g, int b_begin,
+                                              int b_end, int n, const u32x4_t (&qv)[D / 32],
+                                              float &m_run, float &l_part,
+                                              f32x4_t (&acc)[2 * (D / 32)]) {
+  constexpr int NJ = D / 32;
+  const int lane = threadIdx.x & 63;
   const int c = lane & 15;
   const int grp = lane >> 4;
-  const int sg = blockIdx.x;
-  const int s = sg / a.num_kv_heads;
-  const int g = sg - s * a.num_kv_heads;
-  const int part = blockIdx.y;
-
-  int n = a.context_lens[s];
-  n = n < 0 ? 0 : (n > a.max_blocks_per_seq * kBlock ? a.max_blocks_per_seq * kBlock : n);
-  const int nblk = (n + kBlock - 1) / kBlock;
-  const int b_begin = part * a.part_blocks;
-  const bool head_ok = c < a.group;
-  const int head = g * a.group + (head_ok ? c : 0);
-  uint16_t *out_row = a.out + ((size_t)s * a.num_q_heads + head) * D + grp * 8;
-
-  if (n == 0) {  // nothing cached: zero output, written once
-    if (part == 0 && head_ok) {
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) *reinterpret_cast<u32x4_t *>(out_row + 32 * j) = u32x4_t{0, 0, 0, 0};
-    }
-    return;
-  }
-  if (b_begin >= nblk) return;
-  const int b_end = min(nblk, b_begin + a.part_blocks);
-  const int nparts = (nblk + a.part_blocks - 1) / a.part_blocks;
-
-  // q of query head c, with the head-dim mapping this lane uses for K rows.
-  u32x4_t qv[NJ];
-  {
-    const uint16_t *q_row = a.q + ((size_t)s * a.num_q_heads + head) * D + grp * 8;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) qv[j] = head_ok ? load16(q_row + 32 * j) : u32x4_t{0, 0, 0, 0};
-  }
-
-  // Physical ids of this partition's blocks, one per lane, clamped to the pool.
-  int my_blk = 0;
-  if (lane < b_end - b_begin) {
-    my_blk = a.block_tables[(size_t)s * a.max_blocks_per_seq + b_begin + lane];
-    if (my_blk < 0 || (int64_t)my_blk >= a.num_blocks) my_blk = 0;
-  }
 
   const size_t tok_stride = (size_t)a.num_kv_heads * D;  // elements between tokens
   const size_t blk_stride = tok_stride * kBlock;
   const size_t lane_off = (size_t)c * tok_stride + (size_t)g * D + grp * 8;
   const uint16_t *kbase = a.k_cache + lane_off;
   const uint16_t *vbase = a.v_cache + lane_off;
+  const int32_t *table = a.block_tables + (size_t)s * a.max_blocks_per_seq;
 
-  // One-hot selector: column n of the 16x16 selector picks operand slot
-  // (group n/4, element n%4), i.e. lane (c, grp) holds 1.0 in element c%4
-  // iff grp == c/4.
+  // One-hot selector: lane (c, grp) holds 1.0 in element c%4 iff grp == c/4.
   u32x2_t sel = {0u, 0u};
   if (grp == (c >> 2)) {
     const uint32_t word = (c & 1) ? (kBf16One << 16) : kBf16One;
     if (c & 2) sel.y = word; else sel.x = word;
   }
-
-  float m_run = -INFINITY;  // running max of base-2 logits, head c
-  float l_run = 0.f;        // this lane's share of the running sum
-  f32x4_t acc[2 * NJ];
-#pragma unroll
-  for (int t = 0; t < 2 * NJ; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
-  for (int b = b_begin; b < b_end; b += 2) {
-    const int i0 = b - b_begin;
-    const bool has1 = b + 1 < b_end;
-    const int blk0 = __builtin_amdgcn_readlane(my_blk, i0);
-    const int blk1 = __builtin_amdgcn_readlane(my_blk, i0 + 1);
-    const uint16_t *k0 = kbase + (size_t)blk0 * blk_stride;
-    const uint16_t *v0 = vbase + (size_t)blk0 * blk_stride;
-    const uint16_t *k1 = kbase + (size_t)blk1 * blk_stride;
-    const uint16_t *v1 = vbase + (size_t)blk1 * blk_stride;
 
-    u32x4_t K0[NJ], K1[NJ], V0[NJ], V1[NJ];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) K0[j] = load16(k0 + 32 * j);
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) V0[j] = load16(v0 + 32 * j);
-    if (has1) {
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) K1[j] = load16(k1 + 32 * j);
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) V1[j] = load16(v1 + 32 * j);
-    } else {
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) K1[j] = V1[j] = u32x4_t{0, 0, 0, 0};
+  for (int chunk = b_begin; chunk < b_end; chunk += 64) {
+    const int cnt = min(64, b_end - chunk);
+    // Physical ids of up to 64 blocks, one per lane, clamped to the pool.
+    int my_blk = 0;
+    if (lane < cnt) {
+      my_blk = table[chunk + lane];
+      if (my_blk < 0 || (int64_t)my_blk >= a.num_blocks) my_blk = 0;
     }
+    for (int i = 0; i < cnt; ++i) {
+      const int b = chunk + i;
+      const int blk = __builtin_amdgcn_readlane(my_blk, i);
+      const uint16_t *kp = kbase + (size_t)blk * blk_stride;
+      const uint16_t *vp = vbase + (size_t)blk * blk_stride;
+      u32x4_t K[NJ], V[NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) K[j] = load16(kp + 32 * j);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) V[j] = load16(vp + 32 * j);
 
-    // logits: lane holds tokens 4*grp + r of each block, query head c
-    f32x4_t s0 = zero4, s1 = zero4;
+      f32x4_t sc = zero4;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      s0 = mfma32(K0[j], qv[j], s0);
-      s1 = mfma32(K1[j], qv[j], s1);
-    }
-    const int pos0 = b * kBlock + grp * 4;
-    float z[8];
+      for (int j = 0; j < NJ; ++j) sc = mfma32(K[j], qv[j], sc);
+      const int pos0 = b * kBlock + grp * 4;
+      float z[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      z[r] = (pos0 + r < n) ? s0[r] * a.scale_log2 : -INFINITY;
-      z[4 + r] = (pos0 + kBlock + r < n) ? s1[r] * a.scale_log2 : -INFINITY;
-    }
-    float mx = z[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, z[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);  // finite: token b*16 is always < n
-    const float alpha = fast_exp2(m_run - m_new);
-    m_run = m_new;
+      for (int r = 0; r < 4; ++r) z[r] = (pos0 + r < n) ? sc[r] * a.scale_log2 : -INFINITY;
+      float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);  // finite: token b*16 is always < n
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
 
-    // P = P_hi + P_lo, both bf16: the pair carries ~16 significant bits, so
-    // rounding P does not get amplified when the V terms nearly cancel.
-    u32x4_t pb_hi, pb_lo;
-    float psum = 0.f;
+      // P = P_hi + P_lo, both bf16.
+      const float p0 = fast_exp2(z[0] - m_new), p1 = fast_exp2(z[1] - m_new);
+      const float p2 = fast_exp2(z[2] - m_new), p3 = fast_exp2(z[3] - m_new);
+      const uint32_t h01 = to_bf16x2(p0, p1), h23 = to_bf16x2(p2, p3);
+      const u32x2_t pb_hi = {h01, h23};
+      const u32x2_t pb_lo = {to_bf16x2(p0 - bf16_lo(h01), p1 - bf16_hi(h01)),
+                             to_bf16x2(p2 - bf16_lo(h23), p3 - bf16_hi(h23))};
+      l_part = l_part * alpha + ((p0 + p1) + (p2 + p3));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p0 = fast_exp2(z[2 * i] - m_new);
-      const float p1 = fast_exp2(z[2 * i + 1] - m_new);
-      const uint32_t hi = to_bf16x2(p0, p1);
-      pb_hi[i] = hi;
-      pb_lo[i] = to_bf16x2(p0 - bf16_lo(hi), p1 - bf16_hi(hi));
-      psum += p0 + p1;
-    }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int t = 0; t < 2 * NJ; ++t) acc[t] *= alpha;
+      for (int t = 0; t < 2 * NJ; ++t) acc[t] *= alpha;
 
-    // V rows of tokens at or past n must not reach the sum, even as NaN * 0.
-    if ((b + 2) * kBlock > n) {
+      // V rows of tokens at or past n must not reach the sum, even as NaN * 0.
       if (b * kBlock + c >= n) {
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) V0[j] = u32x4_t{0, 0, 0, 0};
+        for (int j = 0; j < NJ; ++j) V[j] = u32x4_t{0, 0, 0, 0};
       }
-      if ((b + 1) * kBlock + c >= n) {
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) V1[j] = u32x4_t{0, 0, 0, 0};
-      }
-    }
-
+      for (int j = 0; j < NJ; ++j) {
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const f32x4_t t0 = mfma16(u32x2_t{V0[j][2 * h], V0[j][2 * h + 1]}, sel, zero4);
-        const f32x4_t t1 = mfma16(u32x2_t{V1[j][2 * h], V1[j][2 * h + 1]}, sel, zero4);
-        const u32x4_t av = {pack_hi(t0[0], t0[1]), pack_hi(t0[2], t0[3]), pack_hi(t1[0], t1[1]),
-                            pack_hi(t1[2], t1[3])};
-        acc[2 * j + h] = mfma32(av, pb_hi, acc[2 * j + h]);
-        acc[2 * j + h] = mfma32(av, pb_lo, acc[2 * j + h]);
+        for (int h = 0; h < 2; ++h) {
+          const f32x4_t t = mfma16(u32x2_t{V[j][2 * h], V[j][2 * h + 1]}, sel, zero4);
+          const u32x2_t av = {pack_hi(t[0], t[1]), pack_hi(t[2], t[3])};
+          acc[2 * j + h] = mfma16(av, pb_hi, acc[2 * j + h]);
+          acc[2 * j + h] = mfma16(av, pb_lo, acc[2 * j + h]);
+        }
       }
     }
   }
-
-  float l = l_run + __shfl_xor(l_run, 16);
-  l += __shfl_xor(l, 32);
-
-  if (nparts == 1) {
-    if (head_ok) store_out<NJ>(out_row, acc, 1.f / l);
-    return;
-  }
-
-  // Partial result of this partition.
-  const size_t prow = ((size_t)s * a.num_q_heads + head) * a.max_parts + part;
-  if (head_ok) {
-    float *po = a.part_o + prow * D + grp * 8;
-#pragma unroll
-    for (int t = 0; t < 2 * NJ; ++t) *reinterpret_cast<f32x4_t *>(po + 32 * (t >> 1) + 4 * (t & 1)) = acc[t];
-    if (grp == 0) *reinterpret_cast<f32x2_t *>(a.part_ml + prow * 2) = f32x2_t{m_run, l};
-  }
-  if (!a.fused_merge) return;
-
-  // The last partition of this (sequence, KV head) to finish merges them all.
-  __threadfence();
-  int arrived = 0;
-  if (lane == 0) arrived = arrive(a.counters + sg, a.epoch);
-  arrived = __shfl(arrived, 0);
-  if (arrived != nparts) return;
-  __threadfence();
-  if (!head_ok) return;
-
-  const size_t base = ((size_t)s * a.num_q_heads + head) * a.max_parts;
-  float M = -INFINITY;
-  for (int p = 0; p < nparts; ++p) M = fmaxf(M, a.part_ml[(base + p) * 2]);
-  float L = 0.f;
-  f32x4_t o[2 * NJ];
-#pragma unroll
-  for (int t = 0; t < 2 * NJ; ++t) o[t] = zero4;
-  for (int p = 0; p < nparts; ++p) {
-    const f32x2_t ml = *reinterpret_cast<const f32x2_t *>(a.part_ml + (base + p) * 2);
-    const float w = fast_exp2(ml[0] - M);
-    L += w * ml[1];
-    const float *po = a.part_o + (base + p) * D + grp * 8;
-#pragma unroll
-    for (int t = 0; t < 2 * NJ; ++t)
-      o[t] += w * *reinterpret_cast<const f32x4_t *>(po + 32 * (t >> 1) + 4 * (t & 1));
-  }
-  store_out<NJ>(out_row, o, 1.f / L);
 }
 
-// Separate log-sum-exp merge for calls with many partitions per sequence:
-// one wavefront per (sequence, query head); lane i owns dims [i*D/64, ...).
 template <int D>
-__global__ __launch_bounds__(64) void merge_kernel(const DecodeArgs a) {
-  constexpr int PL = D / 64;  // dims per lane: 1 or 2
-  const int lane = threadIdx.x;
-  const int s = blockIdx.x / a.num_q_heads;
-  const int h = blockIdx.x - s * a.num_q_heads;
-  int n = a.context_lens[s];
-  n = n < 0 ? 0 : (n > a.max_blocks_per_seq * kBlock ? a.max_blocks_per_seq * kBlock : n);
-  const int nblk = (n + kBlock - 1) / kBlock;
-  const int nparts = (nblk + a.part_blocks - 1) / a.part_blocks;
-  if (nparts <= 1) return;  // written by the decode kernel itself
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4)))
+void decode_kernel(const DecodeArgs a) {
+  constexpr int NJ = D / 32;
+  static_assert(NJ >= 1 && D % 32 == 0, "head_size must be a multiple of 32");
+  __shared__ long long red[8];
+  __shared__ int found_seq;
+  __shared__ long long found_prefix;
 
-  const size_t base = ((size_t)s * a.num_q_heads + h) * a.max_parts;
-  float M = -INFINITY;
-  for (int p = lane; p < nparts; p += 64) M = fmaxf(M, a.part_ml[(base + p) * 2]);
+  const int tid = threadIdx.x;
+  const int nthr = blockDim.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int c = lane & 15;
+  const int grp = lane >> 4;
+  const int w = blockIdx.x;
+  const int S = a.num_seqs;
+  const int NG = a.num_head_groups;
+  const int HG = a.heads_per_wg;
+  const int cap = a.max_blocks_per_seq * kBlock;
+  const long long W = a.num_wgs;
+
+  // Pass 1: total units; zero rows (and "no merge" records) for empty sequences.
+  long long mine = 0;
+  for (int s = tid; s < S; s += nthr) {
+    const int n = clamp_len(a.context_lens[s], cap);
+    mine += (n + kBlock - 1) / kBlock;
+    if (n == 0 && s % a.num_wgs == w) {
+      u32x4_t *row = reinterpret_cast<u32x4_t *>(a.out + (size_t)s * a.num_q_heads * D);
+      for (int i = 0; i < a.num_q_heads * D / 8; ++i) row[i] = u32x4_t{0, 0, 0, 0};
+      if (a.merge_desc)
+        for (int hg = 0; hg < NG; ++hg) a.merge_desc[(size_t)s * NG + hg] = int2{-1, -1};
+    }
+  }
+  const long long U = wg_sum(mine, red, wave, lane, nthr >> 6) * NG;
+  const long long E = U < W ? U : W;  // workgroups that get units
+  if (w >= E) return;
+  const long long lo = range_lo(w, U, E);
+  const long long hi = range_lo(w + 1, U, E);
+
+  // Pass 2: the sequence whose units hold `lo` (block scan over the lengths).
+  if (tid == 0) found_seq = -1;
+  long long before = 0;  // blocks of all sequences preceding this chunk
+  for (int base = 0; base < S; base += nthr) {
+    const int s = base + tid;
+    const long long L = s < S ? (clamp_len(a.context_lens[s], cap) + kBlock - 1) / kBlock : 0;
+    long long incl = L;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    for (int off = 1; off < 64; off <<= 1) {
+      const long long o = __shfl_up(incl, off);
+      if (lane >= off) incl += o;
+    }
+    __syncthreads();
+    if (lane == 63) red[wave] = incl;
+    __syncthreads();
+    long long pre = before;
+    long long chunk_total = 0;
+    for (int i = 0; i < (nthr >> 6); ++i) {
+      if (i < wave) pre += red[i];
+      chunk_total += red[i];
+    }
+    const long long excl = pre + incl - L;
+    if (L > 0 && excl * NG <= lo && lo < (excl + L) * NG) {
+      found_seq = s;
+      found_prefix = excl;
+    }
+    __syncthreads();
+    if (found_seq >= 0) break;
+    before += chunk_total;
+  }
 
-  float L = 0.f;
+  if (found_seq < 0) return;  // only if the lengths changed during the call
+
+  // Walk the range, piece by piece; every wavefront takes KV head
+  // hg*HG + wave of each piece.
+  int s = found_seq;
+  long long seg_base = found_prefix * NG;  // first unit of sequence s
+  int n = clamp_len(a.context_lens[s], cap);
+  int L = (n + kBlock - 1) / kBlock;
+  int hg = (int)((lo - seg_base) / L);
+  int off = (int)((lo - seg_base) % L);
+  long long u = lo;
+  bool first = true;
+  const bool head_ok = c < a.group;
+
+  while (u < hi) {
+    const long long seg_start = seg_base + (long long)hg * L;
+    const int piece = (int)min((long long)(L - off), hi - u);
+    const int g = hg * HG + wave;
+    const int head = g * a.group + (head_ok ? c : 0);
+
+    u32x4_t qv[NJ];
+    {
+      const uint16_t *q_row = a.q + ((size_t)s * a.num_q_heads + head) * D + grp * 8;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) qv[j] = head_ok ? load16(q_row + 32 * j) : u32x4_t{0, 0, 0, 0};
+    }
+    float m_run = -INFINITY, l_part = 0.f;
+    f32x4_t acc[2 * NJ];
+#pragma unroll
+    for (int t = 0; t < 2 * NJ; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    attend_blocks<D>(a, s, g, off, off + piece, n, qv, m_run, l_part, acc);
+    float l = l_part + __shfl_xor(l_part, 16);
+    l += __shfl_xor(l, 32);
+
+    const bool whole = off == 0 && piece == L;
+    const bool ends_here = off + piece == L;
+    if (whole) {
+      if (head_ok) store_out<NJ>(a.out + ((size_t)s * a.num_q_heads + head) * D + grp * 8, acc, 1.f / l);
+    } else {
+      const int slot = first ? 0 : 1;
+      const size_t row = (((size_t)w * 2 + slot) * HG + wave) * a.group + c;
+      if (head_ok) {
+        float *po = a.part_o + row * D + grp * 8;
+#pragma unroll
+        for (int t = 0; t < 2 * NJ; ++t)
+          *reinterpret_cast<f32x4_t *>(po + 32 * (t >> 1) + 4 * (t & 1)) = acc[t];
+        if (grp == 0) *reinterpret_cast<f32x2_t *>(a.part_ml + row * 2) = f32x2_t{m_run, l};
+      }
+    }
+    if (ends_here && tid == 0 && a.merge_desc) {
+      int2 d = {-1, -1};
+      if (!whole) {  // the segment began in an earlier workgroup: record its pieces
+        const int w0 = owner_of(seg_start, U, E);
+        const int slot0 = range_lo(w0, U, E) < seg_start ? 1 : 0;
+        d = int2{w0 * 2 + slot0, w};
+      }
+      a.merge_desc[(size_t)s * NG + hg] = d;
+    }
+
+    first = false;
+    u += piece;
+    off += piece;
+    if (off == L) {
+      off = 0;
+      if (++hg == NG && u < hi) {
+        hg = 0;
+        seg_base += (long long)NG * L;
+        do {  // units remain, so a non-empty sequence follows
+          ++s;
+          n = s < S ? clamp_len(a.context_lens[s], cap) : 0;
+          L = (n + kBlock - 1) / kBlock;
+        } while (L == 0 && s < S);
+        if (s >= S) break;  // only if the lengths changed during the call
+      }
+    }
+  }
+}
+
+// Log-sum-exp merge of the pieces of segments cut by workgroup boundaries.
+// Grid: (num_seqs * num_head_groups, heads_per_wg); one wavefront per query
+// head of the group; lane i owns head dims [i*D/64, (i+1)*D/64).
+template <int D>
+__global__ __launch_bounds__(1024) void merge_kernel(const DecodeArgs a) {
+  constexpr int PL = D / 64;  // dims per lane: 1 or 2
+  const int seg = blockIdx.x;
+  const int2 d = a.merge_desc[seg];
+  if (d.x < 0) return;
+  const int lane = threadIdx.x & 63;
+  const int c = threadIdx.x >> 6;            // query head within the KV head's group
+  const int wave = blockIdx.y;               // KV head within the head group
+  const int s = seg / a.num_head_groups;
+  const int hg = seg - s * a.num_head_groups;
+  const int g = hg * a.heads_per_wg + wave;
+  const int w0 = d.x >> 1, w1 = d.y;
+  const int HG = a.heads_per_wg;
+
+  auto rec_row = [&](int w) -> size_t {
+    const int rec = w == w0 ? d.x : 2 * w;
+    return ((size_t)rec * HG + wave) * a.group + c;
+  };
+  // Pieces: slot d.x & 1 of workgroup w0, then the first slot of every
+  // workgroup up to w1 (whose ranges all lie inside the segment).
+  float M = -INFINITY;
+  for (int w = w0; w <= w1; ++w) M = fmaxf(M, a.part_ml[rec_row(w) * 2]);
+  float Lsum = 0.f;
   float o[PL];
 #pragma unroll
   for (int i = 0; i < PL; ++i) o[i] = 0.f;
 #pragma unroll 4
-  for (int p = 0; p < nparts; ++p) {
-    const f32x2_t ml = *reinterpret_cast<const f32x2_t *>(a.part_ml + (base + p) * 2);
-    const float w = fast_exp2(ml[0] - M);
-    L += w * ml[1];
-    const float *po = a.part_o + (base + p) * D + lane * PL;
+  for (int w = w0; w <= w1; ++w) {
+    const size_t r = rec_row(w);
+    const f32x2_t ml = *reinterpret_cast<const f32x2_t *>(a.part_ml + r * 2);
+    const float wt = fast_exp2(ml[0] - M);
+    Lsum += wt * ml[1];
+    const float *po = a.part_o + r * D + lane * PL;
 #pragma unroll
-    for (int i = 0; i < PL; ++i) o[i] += w * po[i];
+    for (int i = 0; i < PL; ++i) o[i] += wt * po[i];
   }
-  const float inv = 1.f / L;
-  uint16_t *dst = a.out + ((size_t)s * a.num_q_heads + h) * D + lane * PL;
+  const float inv = 1.f / Lsum;
+  uint16_t *dst = a.out + ((size_t)s * a.num_q_heads + (size_t)g * a.group + c) * D + lane * PL;
   if constexpr (PL == 2) {
     *reinterpret_cast<uint32_t *>(dst) = to_bf16x2(o[0] * inv, o[1] * inv);
   } else {
@@ -382,8 +438,8 @@ __global__ __launch_bounds__(64) void merge_kernel(const DecodeArgs a) {
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs &args, int32_t head_size, hipStream_t stream) {
-  const dim3 grid((unsigned)args.num_seqs * (unsigned)args.num_kv_heads, (unsigned)args.max_parts);
-  const dim3 block(64);
+  const dim3 grid((unsigned)args.num_wgs);
+  const dim3 block(64 * (unsigned)args.heads_per_wg);
   if (head_size == 128) {
     hipLaunchKernelGGL(decode_kernel<128>, grid, block, 0, stream, args);
   } else if (head_size == 64) {
@@ -392,12 +448,14 @@ hipError_t launch_decode(const DecodeArgs &args, int32_t head_size, hipStream_t 
     return hipErrorInvalidValue;
   }
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || args.max_parts <= 1 || args.fused_merge) return err;
-  const dim3 mgrid((unsigned)args.num_seqs * (unsigned)args.num_q_heads);
+  if (err != hipSuccess || args.num_wgs <= 1) return err;
+  const dim3 mgrid((unsigned)args.num_seqs * (unsigned)args.num_head_groups,
+                   (unsigned)args.heads_per_wg);
+  const dim3 mblock(64 * (unsigned)args.group);
   if (head_size == 128) {
-    hipLaunchKernelGGL(merge_kernel<128>, mgrid, block, 0, stream, args);
+    hipLaunchKernelGGL(merge_kernel<128>, mgrid, mblock, 0, stream, args);
   } else {
-    hipLaunchKernelGGL(merge_kernel<64>, mgrid, block, 0, stream, args);
+    hipLaunchKernelGGL(merge_kernel<64>, mgrid, mblock, 0, stream, args);
   }
   return hipGetLastError();
 }

@@ -5,7 +5,6 @@
 #include <stdlib.h>
 #include <string.h>
 
-#include <atomic>
 #include <string>
 
 #include "../../include/pa.h"
@@ -29,48 +28,40 @@ int hip_fail(hipError_t e, const char *what) {
   return fail(PA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-// Blocks per split-K partition. Default: start at 64 blocks (1024 tokens)
-// and halve, down to 8 blocks, while a batch whose sequences all reached
-// max_blocks_per_seq would give fewer than 2048 (sequence, KV head,
-// partition) work items, so short batches still fill the GPU.
-// PA_PARTITION_TOKENS overrides (rounded to an even block count in [2, 64]).
-int32_t partition_blocks(int32_t num_seqs, int32_t num_kv_heads, int32_t max_blocks_per_seq) {
-  int32_t blocks = 64;
-  const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
-  while (blocks > 8 && pairs * ((max_blocks_per_seq + blocks - 1) / blocks) < 2048) blocks /= 2;
-  if (const char *env = getenv("PA_PARTITION_TOKENS")) {
-    const long tokens = strtol(env, nullptr, 10);
-    if (tokens > 0) blocks = (int32_t)((tokens + 15) / 16);
+// Workgroups per decode call. The units (blocks x head groups) are shared
+// evenly by all workgroups, so the count only sets how much of the chip is
+// busy and how many segments get cut: 16 wavefronts per compute unit on a
+// 256-CU MI355X (4 per SIMD, which the kernel's register budget allows),
+// and at least 4 units per workgroup when every sequence has
+// max_blocks_per_seq blocks. The count depends on the sizes only (not on the
+// device or the data), so workspace sizes can be computed on the host and
+// results are reproducible. PA_DECODE_WGS overrides it (tests, tuning).
+constexpr int64_t kTargetCUs = 256;
+constexpr int64_t kWavesPerCU = 16;
+
+int32_t decode_wgs(int64_t num_seqs, int32_t num_head_groups, int32_t heads_per_wg,
+                   int32_t max_blocks_per_seq) {
+  int64_t w = kTargetCUs * (kWavesPerCU / heads_per_wg > 0 ? kWavesPerCU / heads_per_wg : 1);
+  const int64_t units_bound = num_seqs * num_head_groups * (int64_t)max_blocks_per_seq;
+  const int64_t by_work = (units_bound + 3) / 4;
+  if (by_work < w) w = by_work;
+  if (const char *env = getenv("PA_DECODE_WGS")) {
+    const long v = strtol(env, nullptr, 10);
+    if (v > 0) w = v;
   }
-  blocks = (blocks + 1) & ~1;
-  if (blocks < 2) blocks = 2;
-  if (blocks > 64) blocks = 64;
-  return blocks;
+  if (w < 1) w = 1;
+  if (w > (1 << 20)) w = 1 << 20;
+  return (int32_t)w;
 }
 
-// Split calls are merged by a separate kernel by default. With
-// PA_FUSED_MERGE_MAX_PARTS=N (N > 1), calls with at most N partitions per
-// sequence instead let the last partition to finish merge. That saves a launch
-// but needs device-scope fences, which write back and invalidate L2 on every
-// split wave. On gfx950 that costs more than the launch for large batches.
-int32_t fused_merge_max_parts() {
-  int32_t v = 0;
-  if (const char *env = getenv("PA_FUSED_MERGE_MAX_PARTS")) v = (int32_t)strtol(env, nullptr, 10);
-  return v;
+// KV heads per workgroup: the largest divisor of num_kv_heads that is <= 8.
+int32_t heads_per_workgroup(int32_t num_kv_heads) {
+  for (int32_t h = 8; h > 1; --h)
+    if (num_kv_heads % h == 0) return h;
+  return 1;
 }
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
-
-// Per-call tag of the split-K completion counters (never 0).
-std::atomic<uint32_t> g_epoch{0};
-
-uint32_t next_epoch() {
-  uint32_t e;
-  do {
-    e = g_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
-  } while (e == 0);
-  return e;
-}
 
 int check_cache(const pa_kv_cache *c, bool need_data) {
   if (!c) return fail(PA_ERR_NULL, "cache descriptor is NULL");
@@ -106,15 +97,16 @@ namespace pa {
 DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                        int32_t head_size, int32_t max_blocks_per_seq) {
   DecodePlan p{};
-  p.part_blocks = partition_blocks(num_seqs, num_kv_heads, max_blocks_per_seq);
-  p.max_parts = (max_blocks_per_seq + p.part_blocks - 1) / p.part_blocks;
-  p.fused_merge = (p.max_parts > 1 && p.max_parts <= fused_merge_max_parts()) ? 1 : 0;
-  if (p.max_parts <= 1) return p;
-  const size_t rows = (size_t)num_seqs * num_q_heads * p.max_parts;
-  p.counters_bytes = round_up((size_t)num_seqs * num_kv_heads * sizeof(unsigned long long), 256);
+  p.heads_per_wg = heads_per_workgroup(num_kv_heads);
+  p.num_head_groups = num_kv_heads / p.heads_per_wg;
+  p.num_wgs = decode_wgs(num_seqs, p.num_head_groups, p.heads_per_wg, max_blocks_per_seq);
+  if (p.num_wgs <= 1) return p;
+  const size_t group = (size_t)(num_q_heads / num_kv_heads);
+  const size_t rows = (size_t)p.num_wgs * 2 * p.heads_per_wg * group;
+  p.desc_bytes = round_up((size_t)num_seqs * p.num_head_groups * sizeof(int2), 256);
   p.ml_bytes = round_up(rows * 2 * sizeof(float), 256);
   p.o_bytes = round_up(rows * head_size * sizeof(float), 256);
-  p.total_bytes = p.counters_bytes + p.ml_bytes + p.o_bytes;
+  p.total_bytes = p.desc_bytes + p.ml_bytes + p.o_bytes;
   return p;
 }
 
@@ -147,9 +139,10 @@ int pa_decode(const pa_kv_cache *cache, const void *q, const int32_t *block_tabl
 
   const pa::DecodePlan plan = pa::plan_decode(num_seqs, num_q_heads, cache->num_kv_heads,
                                               cache->head_size, max_blocks_per_seq);
-  if (plan.max_parts > 65535) return fail(PA_ERR_SHAPE, "too many partitions per sequence");
   if (workspace && workspace_bytes < plan.total_bytes)
     return fail(PA_ERR_WORKSPACE, "workspace smaller than pa_decode_workspace_bytes()");
+  if (workspace && reinterpret_cast<uintptr_t>(workspace) % 16)
+    return fail(PA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
   void *ws = workspace;
@@ -169,9 +162,9 @@ int pa_decode(const pa_kv_cache *cache, const void *q, const int32_t *block_tabl
   a.out = static_cast<uint16_t *>(out);
   if (plan.total_bytes) {
     char *base = static_cast<char *>(ws);
-    a.counters = reinterpret_cast<unsigned long long *>(base);
-    a.part_ml = reinterpret_cast<float *>(base + plan.counters_bytes);
-    a.part_o = reinterpret_cast<float *>(base + plan.counters_bytes + plan.ml_bytes);
+    a.merge_desc = reinterpret_cast<int2 *>(base);
+    a.part_ml = reinterpret_cast<float *>(base + plan.desc_bytes);
+    a.part_o = reinterpret_cast<float *>(base + plan.desc_bytes + plan.ml_bytes);
   }
   a.num_blocks = cache->num_blocks;
   a.num_seqs = num_seqs;
@@ -179,11 +172,10 @@ int pa_decode(const pa_kv_cache *cache, const void *q, const int32_t *block_tabl
   a.num_kv_heads = cache->num_kv_heads;
   a.group = num_q_heads / cache->num_kv_heads;
   a.max_blocks_per_seq = max_blocks_per_seq;
-  a.part_blocks = plan.part_blocks;
-  a.max_parts = plan.max_parts;
-  a.fused_merge = plan.fused_merge;
+  a.heads_per_wg = plan.heads_per_wg;
+  a.num_head_groups = plan.num_head_groups;
+  a.num_wgs = plan.num_wgs;
   a.scale_log2 = scale * 1.44269504088896340736f;
-  a.epoch = next_epoch();
 
   hipError_t e = pa::launch_decode(a, cache->head_size, hs);
   if (owned) {
@@ -234,6 +226,21 @@ int pa_probe_copy(void *dst, const void *src, size_t bytes, void *stream) {
     return fail(PA_ERR_SHAPE, "probe copy needs 16-byte sizes and alignment");
   hipError_t e = pa::launch_probe_copy(dst, src, bytes, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "probe copy launch");
+  return ok();
+}
+
+size_t pa_probe_read_sink_bytes(void) { return (size_t)pa::kProbeReadBlocks * 256 * sizeof(uint32_t); }
+
+int pa_probe_read(const void *src, size_t bytes, void *sink, size_t sink_bytes, void *stream) {
+  if (bytes == 0) return ok();
+  if (!src || !sink) return fail(PA_ERR_NULL, "src or sink is NULL");
+  if (bytes % 16 || reinterpret_cast<uintptr_t>(src) % 16)
+    return fail(PA_ERR_SHAPE, "probe read needs 16-byte sizes and alignment");
+  if (sink_bytes < pa_probe_read_sink_bytes())
+    return fail(PA_ERR_WORKSPACE, "sink smaller than pa_probe_read_sink_bytes()");
+  hipError_t e = pa::launch_probe_read(src, bytes, static_cast<uint32_t *>(sink),
+                                       static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "probe read launch");
   return ok();
 }
 

@@ -16,31 +16,30 @@ struct DecodeArgs {
   const int32_t *block_tables;   // [S, MB]
   const int32_t *context_lens;   // [S]
   uint16_t *out;                 // bf16 [S, Hq, D]
-  unsigned long long *counters;  // [S * Hkv] epoch-tagged completion counters
-  float *part_ml;                // [S, Hq, max_parts, 2]: running max (base 2), sum
-  float *part_o;                 // [S, Hq, max_parts, D]: unnormalised output
+  int2 *merge_desc;              // [S * num_head_groups]: pieces of cut segments
+  float *part_ml;                // [2 * num_wgs, heads_per_wg, group, 2]: max (base 2), sum
+  float *part_o;                 // [2 * num_wgs, heads_per_wg, group, D]: unnormalised output
   int64_t num_blocks;
   int32_t num_seqs;
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t group;                 // Hq / Hkv, <= 16
   int32_t max_blocks_per_seq;
-  int32_t part_blocks;           // blocks per partition: even, 2..64
-  int32_t max_parts;             // ceil(max_blocks_per_seq / part_blocks)
-  int32_t fused_merge;           // 1: the last partition of a (seq, KV head) merges
+  int32_t heads_per_wg;          // KV heads per workgroup (one wavefront each), <= 8
+  int32_t num_head_groups;       // Hkv / heads_per_wg
+  int32_t num_wgs;               // workgroups sharing the units evenly
   float scale_log2;              // softmax scale times log2(e)
-  uint32_t epoch;                // nonzero, distinct for consecutive calls
 };
 
 // How a decode call is split and what scratch it needs (host only).
 struct DecodePlan {
-  int32_t part_blocks;
-  int32_t max_parts;
-  int32_t fused_merge;
-  size_t counters_bytes;         // 8 bytes per (sequence, KV head); offset of part_ml
+  int32_t heads_per_wg;
+  int32_t num_head_groups;
+  int32_t num_wgs;
+  size_t desc_bytes;             // offset of part_ml
   size_t ml_bytes;
   size_t o_bytes;
-  size_t total_bytes;            // 0 when max_parts == 1
+  size_t total_bytes;            // 0 when num_wgs == 1 (nothing is ever cut)
 };
 
 DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
@@ -57,5 +56,10 @@ hipError_t launch_copy_blocks(uint16_t *k_cache, uint16_t *v_cache, const int64_
                               hipStream_t stream);
 
 hipError_t launch_probe_copy(void *dst, const void *src, size_t bytes, hipStream_t stream);
+
+// Workgroups of the read probe (256 threads each); its sink holds one
+// 32-bit word per thread.
+constexpr unsigned kProbeReadBlocks = 256 * 32;
+hipError_t launch_probe_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream);
 
 }  // namespace pa

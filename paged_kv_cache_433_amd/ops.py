@@ -132,3 +132,16 @@ def probe_copy(dst: torch.Tensor, src: torch.Tensor) -> None:
     if dst.numel() * dst.element_size() < nbytes:
         raise ValueError("dst smaller than src")
     _check(_lib.lib().pa_probe_copy(_ptr(dst), _ptr(src), nbytes, _stream(src.device)))
+
+
+def probe_read(src: torch.Tensor, sink: torch.Tensor = None) -> torch.Tensor:
+    """Read all of ``src`` with 16-byte vector loads (measurement helper);
+    returns the sink buffer the probe folds its loads into."""
+    lib = _lib.lib()
+    need = int(lib.pa_probe_read_sink_bytes())
+    if sink is None:
+        sink = torch.empty(need, dtype=torch.uint8, device=src.device)
+    nbytes = src.numel() * src.element_size()
+    _check(lib.pa_probe_read(_ptr(src), nbytes, _ptr(sink), sink.numel() * sink.element_size(),
+                             _stream(src.device)))
+    return sink

@@ -75,17 +75,25 @@ def test_decode_no_op_and_errors_reset(L):
     assert L.pa_last_error().decode() == ""
 
 
-def test_workspace_size_and_check(L):
-    d = desc()
-    # at most 8 blocks per sequence: never split, no workspace needed
-    assert L.pa_decode_workspace_bytes(ctypes.byref(d), 4, 32, 8) == 0
-    # small batch with long sequences: split into 8-block partitions
-    assert L.pa_decode_workspace_bytes(ctypes.byref(d), 4, 32, 32) >= 4 * 32 * 4 * 130 * 4
+def test_workspace_size_and_check(L, monkeypatch):
+    d = desc()                        # 8 KV heads of 128: one workgroup per 8-head group
+    # one sequence of one block: a single workgroup, nothing is ever cut
+    assert L.pa_decode_workspace_bytes(ctypes.byref(d), 1, 32, 1) == 0
+    # otherwise: a merge record per (sequence, head group) and two partial
+    # records (max, sum, 128 floats) per workgroup, KV head and query head
+    wgs = (4 * 32 + 3) // 4           # at least 4 units per workgroup
+    need = L.pa_decode_workspace_bytes(ctypes.byref(d), 4, 32, 32)
+    assert need >= 4 * 8 + wgs * 2 * 8 * 4 * (128 + 2) * 4
     need = L.pa_decode_workspace_bytes(ctypes.byref(d), 256, 32, 256)
-    parts = 4          # 1024-token partitions once the grid is large enough
-    assert need >= 256 * 32 * parts * (128 + 2) * 4 + 256 * 8 * 8
+    wgs = 256 * 2                     # 16 wavefronts per CU on 256 CUs, 8 per workgroup
+    assert need >= 256 * 8 + wgs * 2 * 8 * 4 * (128 + 2) * 4
+    assert need < 2 * (256 * 8 + wgs * 2 * 8 * 4 * (128 + 2) * 4)
     assert decode(L, d, S=256, hq=32, mb=256, ws=P, wsb=need - 1) == _lib.PA_ERR_WORKSPACE
     assert L.pa_decode_workspace_bytes(None, 1, 1, 1) == 0
+    monkeypatch.setenv("PA_DECODE_WGS", "1")
+    assert L.pa_decode_workspace_bytes(ctypes.byref(d), 256, 32, 256) == 0
+    monkeypatch.setenv("PA_DECODE_WGS", "3")
+    assert L.pa_decode_workspace_bytes(ctypes.byref(d), 256, 32, 256) >= 3 * 2 * 8 * 4 * 130 * 4
 
 
 def test_cache_op_argument_errors(L):

@@ -1,10 +1,12 @@
 """GPU parity of pa_decode / pa_reshape_and_cache against the float64 oracle.
 
 Small and mid-size cases run the whole batch through the oracle, element by
-element. They cover: single pass and split-K (fused and separate merge),
-every supported head size and group size, lengths at and around block and
-partition boundaries, NaN-poisoned unreferenced slots, and out-of-range
-padding in the block tables.
+element. They cover: every supported head size and group size, lengths at
+and around block boundaries, the work split at many workgroup counts (one
+workgroup, so nothing is cut; odd counts; more workgroups than units, so
+some ranges are empty), empty sequences, batches longer than a workgroup's
+length scan, NaN-poisoned unreferenced slots, and out-of-range padding in
+the block tables.
 """
 
 import numpy as np
@@ -40,22 +42,55 @@ def test_tiny_mha_config():
 
 
 @pytest.mark.parametrize("hq,hkv,d", [(8, 8, 64), (8, 8, 128), (16, 2, 128), (32, 8, 128),
-                                      (16, 1, 64), (12, 4, 128), (7, 7, 64), (40, 8, 128)])
-def test_edge_lengths_single_pass_and_split(hq, hkv, d, monkeypatch):
+                                      (16, 1, 64), (12, 4, 128), (7, 7, 64), (40, 8, 128),
+                                      (96, 12, 128), (64, 32, 64)])
+def test_edge_lengths_across_work_splits(hq, hkv, d, monkeypatch):
     b = small_batch(300 + hq + d, EDGE_LENS, hq, hkv, d, spare=11)
-    for tokens, fused in [(512, "16"), (32, "64"), (64, "0"), (1024, "16")]:
-        monkeypatch.setenv("PA_PARTITION_TOKENS", str(tokens))
-        monkeypatch.setenv("PA_FUSED_MERGE_MAX_PARTS", fused)
-        run_and_check(b, f"edge hq={hq} hkv={hkv} d={d} part={tokens} fused<={fused}")
+    for wgs in ("1", "3", "64", "default", "5000"):
+        if wgs == "default":
+            monkeypatch.delenv("PA_DECODE_WGS", raising=False)
+        else:
+            monkeypatch.setenv("PA_DECODE_WGS", wgs)
+        run_and_check(b, f"edge hq={hq} hkv={hkv} d={d} wgs={wgs}")
 
 
-def test_split_matches_single_pass_closely(monkeypatch):
-    """Different partitionings of the same batch agree to bf16 rounding."""
+@pytest.mark.parametrize("hkv", [1, 8])
+def test_many_sequences_and_empty_ones(hkv, monkeypatch):
+    """More sequences than one workgroup scans at once, with empty ones at
+    the ends and in between (their rows must come out zero)."""
+    rng = np.random.default_rng(77 + hkv)
+    lens = rng.integers(1, 90, size=700)
+    b = small_batch(420 + hkv, lens, 4 * hkv, hkv, 128, spare=5)
+    ctx = b.context_lens.copy()
+    empty = [0, 1, 2, 64, 65, 300, 511, 512, 513, 697, 698, 699]
+    ctx[empty] = 0
+    kc, vc, _, _ = oracle_step(b)
+    ref = oracle.decode(b.q, kc, vc, b.block_tables, ctx, b.scale)
+    for wgs in ("default", "1", "37", "2000"):
+        if wgs == "default":
+            monkeypatch.delenv("PA_DECODE_WGS", raising=False)
+        else:
+            monkeypatch.setenv("PA_DECODE_WGS", wgs)
+        note(f"many sequences hkv={hkv} wgs={wgs}")
+        db = DevBatch(b)
+        db.scatter()
+        db.context_lens = to_dev(ctx)
+        out = bits_of(db.decode())
+        assert np.all(out[empty] == 0)
+        assert_attention_close(out, ref, f"many sequences hkv={hkv} wgs={wgs}")
+
+
+def test_work_splits_agree_closely(monkeypatch):
+    """Different workgroup counts cut the same batch differently; the
+    results agree to bf16 rounding."""
     b = small_batch(401, [700, 1500, 2049, 64], 32, 8, 128)
     outs = []
-    for tokens in (4096, 512, 128, 32):
-        monkeypatch.setenv("PA_PARTITION_TOKENS", str(tokens))
-        _, _, out = run_and_check(b, f"partition {tokens}")
+    for wgs in ("1", "2", "17", "default"):
+        if wgs == "default":
+            monkeypatch.delenv("PA_DECODE_WGS", raising=False)
+        else:
+            monkeypatch.setenv("PA_DECODE_WGS", wgs)
+        _, _, out = run_and_check(b, f"workgroups {wgs}")
         outs.append(oracle.bf16_bits_to_f64(bits_of(out)))
     for o in outs[1:]:
         assert np.abs(o - outs[0]).max() <= 2 ** -6 * np.abs(outs[0]).max()
@@ -133,23 +168,35 @@ def test_block_relabelling_is_bitwise_invariant():
     assert np.array_equal(out1, out2)
 
 
-def test_head_slice_equals_slice_of_full_output():
+def test_head_slice_equals_slice_of_full_output(monkeypatch):
     """Each tensor-parallel rank holds a share of the K/V heads ('vLLM
-    Internals', section 'Multi-GPU Execution'): decoding a share gives
-    exactly that share of the full output."""
+    Internals', section 'Multi-GPU Execution'): decoding a share gives that
+    share of the full output. With one workgroup no sequence is cut, every
+    (sequence, head) is reduced in the same order in both calls, and the
+    share is bit-identical; with the default split the cut points depend on
+    the number of heads, so the share agrees to rounding (and each matches
+    the oracle)."""
     import paged_kv_cache_433_amd as pa
     b = small_batch(406, [10, 45, 640, 1300], 32, 8, 128)
-    note("head slice full")
-    db = DevBatch(b)
-    db.scatter()
-    full = bits_of(db.decode())
-    for g0, g1 in [(0, 1), (2, 4), (4, 8)]:
-        note(f"head slice {g0}:{g1}")
-        kc = db.k_cache[:, :, g0:g1].contiguous()
-        vc = db.v_cache[:, :, g0:g1].contiguous()
-        part = bits_of(pa.decode(db.q[:, g0 * 4:g1 * 4].contiguous(), kc, vc, db.block_tables,
-                                 db.context_lens, float(b.scale)))
-        assert np.array_equal(part, full[:, g0 * 4:g1 * 4]), (g0, g1)
+    kc, vc, ref, _ = oracle_step(b)
+    for wgs in ("1", "default"):
+        if wgs == "default":
+            monkeypatch.delenv("PA_DECODE_WGS", raising=False)
+        else:
+            monkeypatch.setenv("PA_DECODE_WGS", wgs)
+        note(f"head slice full wgs={wgs}")
+        db = DevBatch(b)
+        db.scatter()
+        full = bits_of(db.decode())
+        for g0, g1 in [(0, 1), (2, 4), (4, 8)]:
+            note(f"head slice {g0}:{g1} wgs={wgs}")
+            kcs = db.k_cache[:, :, g0:g1].contiguous()
+            vcs = db.v_cache[:, :, g0:g1].contiguous()
+            part = bits_of(pa.decode(db.q[:, g0 * 4:g1 * 4].contiguous(), kcs, vcs, db.block_tables,
+                                     db.context_lens, float(b.scale)))
+            if wgs == "1":
+                assert np.array_equal(part, full[:, g0 * 4:g1 * 4]), (g0, g1)
+            assert_attention_close(part, ref[:, g0 * 4:g1 * 4], f"slice {g0}:{g1} wgs={wgs}")
 
 
 def test_run_to_run_bitwise_deterministic():
@@ -164,14 +211,18 @@ def test_run_to_run_bitwise_deterministic():
 
 def test_workspace_reuse_across_shapes(monkeypatch):
     """One workspace serves calls of different shapes in turn: partials of
-    one call may sit where the next call keeps its counters."""
+    one call may sit where the next call keeps its merge records."""
     import torch
 
     import paged_kv_cache_433_amd as pa
     cases = [small_batch(410, [3000, 600, 2200], 16, 2, 128),
              small_batch(411, [700, 1100, 40, 513, 1600, 900, 2048, 5], 32, 8, 128),
              small_batch(412, [2500], 8, 8, 64)]
-    ws = torch.randint(0, 256, (8 << 20,), dtype=torch.uint8, device="cuda:0")
+    need = max(pa.decode_workspace_bytes(torch.empty((1, 16, b.num_kv_heads, b.head_size),
+                                                     dtype=torch.bfloat16, device="cuda:0"),
+                                         b.num_seqs, b.num_q_heads, b.max_blocks_per_seq)
+               for b in cases)
+    ws = torch.randint(0, 256, (need,), dtype=torch.uint8, device="cuda:0")
     for round_ in range(2):
         for i, b in enumerate(cases):
             note(f"workspace reuse round {round_} case {i}")
