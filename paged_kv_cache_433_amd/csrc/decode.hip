@@ -145,102 +145,304 @@ __device__ __forceinline__ long long wg_sum(long long v, long long *red, int wav
   return t;
 }
 
-// Attention of one wavefront's query heads over blocks [b_begin, b_end) of
-// sequence s, KV head g (n tokens cached). Returns, for query head c of the
-// group (lane (c, grp)), the running max m_run (base 2), this lane's share
-// of the sum of weights l_part, and the unnormalised output in acc.
-template <int D>
-__device__ __forceinline__ void attend_blocks(const DecodeArgs &a, int s, int g, int b_begin,
-                                              int b_end, int n, const u32x4_t (&qv)[D / 32],
-                                              float &m_run, float &l_part,
-                                              f32x4_t (&acc)[2 * (D / 32)]) {
-  constexpr int NJ = D / 32;
-  const int lane = threadIdx.x & 63;
-  const int c = lane & 15;
-  const int grp = lane >> 4;
+// A piece is the run of blocks of one (sequence, head group) that lies in
+// this workgroup's range of units; the walk hands it out in chunks of at
+// most 64 blocks, so that one register per lane holds a chunk's table
+// entries.
+struct Piece {
+  long long seg_start;  // first unit of the segment the piece belongs to
+  int s;                // sequence
+  int hg;               // head group
+  int off;              // first logical block of the chunk
+  int cnt;              // blocks in the chunk, 1..64
+  int piece_off;        // first logical block of the piece
+  int n;                // context length of s (clamped)
+  int L;                // blocks of s
+  bool first;           // the piece is the workgroup's first piece
+  bool starts_piece;    // the chunk is the piece's first
+  bool ends_piece;      // the chunk is the piece's last
+};
 
-  const size_t tok_stride = (size_t)a.num_kv_heads * D;  // elements between tokens
-  const size_t blk_stride = tok_stride * kBlock;
-  const size_t lane_off = (size_t)c * tok_stride + (size_t)g * D + grp * 8;
-  const uint16_t *kbase = a.k_cache + lane_off;
-  const uint16_t *vbase = a.v_cache + lane_off;
-  const int32_t *table = a.block_tables + (size_t)s * a.max_blocks_per_seq;
+// Produces the workgroup's pieces in order. Every thread of the workgroup
+// runs the same walk (the state is uniform). Context lengths come from a
+// window of 64 consecutive sequences held one per lane (read with
+// readlane), so the walk issues no memory load, and so no wait, while K/V
+// loads are in flight; the window moves only after 64 sequences.
+struct Walker {
+  const int32_t *lens;
+  int S, NG, cap, lane;
+  long long u, hi, seg_base;
+  int s, hg, off, L, n;
+  int win, win_base;  // clamped lens[win_base + lane]
+  int piece_off;      // first block of the current piece
+  bool first;         // the current piece is the workgroup's first
+};
 
-  // One-hot selector: lane (c, grp) holds 1.0 in element c%4 iff grp == c/4.
-  u32x2_t sel = {0u, 0u};
-  if (grp == (c >> 2)) {
-    const uint32_t word = (c & 1) ? (kBf16One << 16) : kBf16One;
-    if (c & 2) sel.y = word; else sel.x = word;
+__device__ __forceinline__ void load_window(Walker &wk, int base) {
+  wk.win_base = base;
+  wk.win = clamp_len(wk.lens[min(base + wk.lane, wk.S - 1)], wk.cap);
+}
+
+__device__ __forceinline__ int len_of(Walker &wk, int t) {
+  if (t - wk.win_base >= 64) load_window(wk, t);
+  return __builtin_amdgcn_readlane(wk.win, t - wk.win_base);
+}
+
+__device__ __forceinline__ bool next_chunk(Walker &wk, Piece &p) {
+  if (wk.u >= wk.hi) return false;
+  const int piece_left = (int)min((long long)(wk.L - wk.off), wk.hi - wk.u);
+  p.s = wk.s;
+  p.hg = wk.hg;
+  p.off = wk.off;
+  p.n = wk.n;
+  p.L = wk.L;
+  p.cnt = min(64, piece_left);
+  p.piece_off = wk.piece_off;
+  p.seg_start = wk.seg_base + (long long)wk.hg * wk.L;
+  p.first = wk.first;
+  p.starts_piece = wk.off == wk.piece_off;
+  p.ends_piece = p.cnt == piece_left;
+  wk.u += p.cnt;
+  wk.off += p.cnt;
+  if (p.ends_piece) wk.first = false;
+  if (wk.off == wk.L) {
+    wk.off = 0;
+    if (++wk.hg == wk.NG && wk.u < wk.hi) {
+      wk.hg = 0;
+      wk.seg_base += (long long)wk.NG * wk.L;
+      do {  // units remain, so a non-empty sequence follows
+        ++wk.s;
+        wk.n = wk.s < wk.S ? len_of(wk, wk.s) : 0;
+        wk.L = (wk.n + kBlock - 1) / kBlock;
+      } while (wk.L == 0 && wk.s < wk.S);
+      if (wk.s >= wk.S) wk.u = wk.hi;  // only if the lengths changed during the call
+    }
   }
-  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+  if (p.ends_piece) wk.piece_off = wk.off;
+  return true;
+}
 
-  for (int chunk = b_begin; chunk < b_end; chunk += 64) {
-    const int cnt = min(64, b_end - chunk);
-    // Physical ids of up to 64 blocks, one per lane, clamped to the pool.
-    int my_blk = 0;
-    if (lane < cnt) {
-      my_blk = table[chunk + lane];
-      if (my_blk < 0 || (int64_t)my_blk >= a.num_blocks) my_blk = 0;
-    }
-    for (int i = 0; i < cnt; ++i) {
-      const int b = chunk + i;
-      const int blk = __builtin_amdgcn_readlane(my_blk, i);
-      const uint16_t *kp = kbase + (size_t)blk * blk_stride;
-      const uint16_t *vp = vbase + (size_t)blk * blk_stride;
-      u32x4_t K[NJ], V[NJ];
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) K[j] = load16(kp + 32 * j);
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) V[j] = load16(vp + 32 * j);
+// Per-thread constants of the decode kernel.
+struct Lane {
+  int tid, wave, lane, c, grp, w;
+  int HG, NG;
+  bool head_ok;  // lane column c is a query head of the group
+  int crow;      // query head the lane loads (c, or the group's last head)
+  size_t blk_stride;  // elements per block of one cache array
+  uint32_t lane_off;  // byte offset of the lane's 16 bytes inside (block, head): token c, dims 8*grp..
+  long long U, E;
+  u32x2_t sel;
+};
 
-      f32x4_t sc = zero4;
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) sc = mfma32(K[j], qv[j], sc);
-      const int pos0 = b * kBlock + grp * 4;
-      float z[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) z[r] = (pos0 + r < n) ? sc[r] * a.scale_log2 : -INFINITY;
-      float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);  // finite: token b*16 is always < n
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
+// One wavefront's pass over its workgroup's stream of blocks.
+template <int NJ>
+struct Stream {
+  Piece P, Q;         // the chunk being computed and the next one
+  bool has_q;
+  int i;              // block of P being computed
+  int ids;            // table entries of P's blocks, one per lane
+  int ids_q;          // table entries of Q's blocks
+  size_t hoff, hoff_q;
+  u32x4_t qv[NJ], qn[NJ];
+  float m_run;        // running max of base-2 logits, query head c
+  float l_part;       // this lane's share of the running sum
+  f32x4_t acc[2 * NJ];
+};
 
-      // P = P_hi + P_lo, both bf16.
-      const float p0 = fast_exp2(z[0] - m_new), p1 = fast_exp2(z[1] - m_new);
-      const float p2 = fast_exp2(z[2] - m_new), p3 = fast_exp2(z[3] - m_new);
-      const uint32_t h01 = to_bf16x2(p0, p1), h23 = to_bf16x2(p2, p3);
-      const u32x2_t pb_hi = {h01, h23};
-      const u32x2_t pb_lo = {to_bf16x2(p0 - bf16_lo(h01), p1 - bf16_hi(h01)),
-                             to_bf16x2(p2 - bf16_lo(h23), p3 - bf16_hi(h23))};
-      l_part = l_part * alpha + ((p0 + p1) + (p2 + p3));
+template <int NJ>
+__device__ __forceinline__ void load_q(const DecodeArgs &a, const Lane &ln, const Piece &p, u32x4_t (&qv)[NJ]) {
+  constexpr int D = NJ * 32;
+  const uint16_t *qr = a.q +
+                       ((size_t)p.s * a.num_q_heads + (size_t)(p.hg * ln.HG + ln.wave) * a.group + ln.crow) * D +
+                       ln.grp * 8;
 #pragma unroll
-      for (int t = 0; t < 2 * NJ; ++t) acc[t] *= alpha;
+  for (int j = 0; j < NJ; ++j) qv[j] = load16(qr + 32 * j);
+}
 
-      // V rows of tokens at or past n must not reach the sum, even as NaN * 0.
-      if (b * kBlock + c >= n) {
+// Table entries [b0, b0 + 64) of the piece's sequence, one per lane; lanes
+// past `left` repeat the last entry. The load is unconditional and the
+// value is checked only where it is used, so no wait is forced here.
+__device__ __forceinline__ int table_ids(const DecodeArgs &a, const Lane &ln, const Piece &p, int b0, int left) {
+  return a.block_tables[(size_t)p.s * a.max_blocks_per_seq + b0 + (ln.lane < left ? ln.lane : left - 1)];
+}
+
+// Physical block held by lane k of `ids`, clamped to the pool.
+__device__ __forceinline__ int block_at(const DecodeArgs &a, int ids, int k) {
+  const int b = __builtin_amdgcn_readlane(ids, k);
+  return (b < 0 || (int64_t)b >= a.num_blocks) ? 0 : b;
+}
+
+// Element offset of the wavefront's KV head inside a token row (uniform).
+template <int NJ>
+__device__ __forceinline__ size_t head_off(const Lane &ln, const Piece &p) {
+  return (size_t)(p.hg * ln.HG + ln.wave) * (NJ * 32);
+}
+
+// Buffer-resource word 3 for gfx9-family raw (untyped) buffer loads.
+constexpr int kRawBufferWord3 = 0x00020000;
+
+// Starts the loads of one block's K and V rows for this wavefront's head.
+// Each array is read through a buffer resource whose base is the (block,
+// head) start (scalar registers) and whose size ends at the block's end;
+// the lane adds its fixed offset. So no vector address arithmetic happens
+// per block, and an offset past the block would read zeros, not another
+// block.
+template <int NJ>
+__device__ __forceinline__ void issue(const DecodeArgs &a, const Lane &ln, int blk, size_t hoff, u32x4_t (&K)[NJ],
+                                      u32x4_t (&V)[NJ]) {
+  const size_t base = ((size_t)blk * ln.blk_stride + hoff) * sizeof(uint16_t);
+  const int span = (int)((ln.blk_stride - hoff) * sizeof(uint16_t));
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char *>(reinterpret_cast<const char *>(a.k_cache) + base), 0, span, kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char *>(reinterpret_cast<const char *>(a.v_cache) + base), 0, span, kRawBufferWord3);
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) V[j] = u32x4_t{0, 0, 0, 0};
-      }
+  for (int j = 0; j < NJ; ++j)
+    K[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, ln.lane_off + 64 * j, 0, 0));
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
+  for (int j = 0; j < NJ; ++j)
+    V[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, ln.lane_off + 64 * j, 0, 0));
+}
+
+// Makes Q the current chunk (its first block is already loading) and looks
+// one chunk further ahead. A new piece starts from fresh softmax state and
+// the q loaded for it.
+template <int NJ>
+__device__ __forceinline__ void advance(const DecodeArgs &a, const Lane &ln, Walker &wk, Stream<NJ> &st) {
+  st.P = st.Q;
+  if (st.P.starts_piece) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const f32x4_t t = mfma16(u32x2_t{V[j][2 * h], V[j][2 * h + 1]}, sel, zero4);
-          const u32x2_t av = {pack_hi(t[0], t[1]), pack_hi(t[2], t[3])};
-          acc[2 * j + h] = mfma16(av, pb_hi, acc[2 * j + h]);
-          acc[2 * j + h] = mfma16(av, pb_lo, acc[2 * j + h]);
-        }
-      }
-    }
+    for (int j = 0; j < NJ; ++j) st.qv[j] = st.qn[j];
+    st.m_run = -INFINITY;
+    st.l_part = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2 * NJ; ++t) st.acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  st.ids = st.ids_q;
+  st.hoff = st.hoff_q;
+  st.i = 0;
+  st.has_q = next_chunk(wk, st.Q);
+  if (st.has_q) {
+    if (st.Q.starts_piece) load_q<NJ>(a, ln, st.Q, st.qn);
+    st.ids_q = table_ids(a, ln, st.Q, st.Q.off, st.Q.cnt);
+    st.hoff_q = head_off<NJ>(ln, st.Q);
   }
 }
 
+// Writes P's result: bf16 output when P is a whole segment, otherwise its
+// partial record; the workgroup holding a segment's last unit records the
+// segment's pieces for the merge.
+template <int NJ>
+__device__ __forceinline__ void finish_piece(const DecodeArgs &a, const Lane &ln, Stream<NJ> &st) {
+  constexpr int D = NJ * 32;
+  const Piece &P = st.P;
+  float l = st.l_part + __shfl_xor(st.l_part, 16);
+  l += __shfl_xor(l, 32);
+  const int head = (P.hg * ln.HG + ln.wave) * a.group + ln.c;
+  const bool whole = P.piece_off == 0 && P.off + P.cnt == P.L;
+  if (whole) {
+    if (ln.head_ok)
+      store_out<NJ>(a.out + ((size_t)P.s * a.num_q_heads + head) * D + ln.grp * 8, st.acc, 1.f / l);
+  } else {
+    const int slot = P.first ? 0 : 1;
+    const size_t row = (((size_t)ln.w * 2 + slot) * ln.HG + ln.wave) * a.group + ln.c;
+    if (ln.head_ok) {
+      float *po = a.part_o + row * D + ln.grp * 8;
+#pragma unroll
+      for (int t = 0; t < 2 * NJ; ++t) *reinterpret_cast<f32x4_t *>(po + 32 * (t >> 1) + 4 * (t & 1)) = st.acc[t];
+      if (ln.grp == 0) *reinterpret_cast<f32x2_t *>(a.part_ml + row * 2) = f32x2_t{st.m_run, l};
+    }
+  }
+  if (P.off + P.cnt == P.L && ln.tid == 0 && a.merge_desc) {
+    int2 d = {-1, -1};
+    if (!whole) {  // the segment began in an earlier workgroup: record its pieces
+      const int w0 = owner_of(P.seg_start, ln.U, ln.E);
+      const int slot0 = range_lo(w0, ln.U, ln.E) < P.seg_start ? 1 : 0;
+      d = int2{w0 * 2 + slot0, ln.w};
+    }
+    a.merge_desc[(size_t)P.s * ln.NG + P.hg] = d;
+  }
+}
+
+// Computes block i of P from (K, V) after starting the next block of the
+// stream loading into (Kn, Vn); finishes P at its end and moves to Q.
+// Returns false once the stream is done.
+template <int NJ>
+__device__ __forceinline__ bool step(const DecodeArgs &a, const Lane &ln, Walker &wk, Stream<NJ> &st,
+                                     u32x4_t (&K)[NJ], u32x4_t (&V)[NJ], u32x4_t (&Kn)[NJ], u32x4_t (&Vn)[NJ]) {
+  const Piece &P = st.P;
+  // The next block of the stream: P's next, else Q's first. The loads are
+  // issued on every path (past the end of the stream they reload the
+  // current block), so the compiler can count them when it places the wait
+  // for the current block: it waits for that block only, not for the next.
+  const int nx = st.i + 1;
+  int next_blk;
+  size_t next_hoff = st.hoff;
+  if (nx < P.cnt) {
+    next_blk = block_at(a, st.ids, nx);
+  } else if (st.has_q) {
+    next_blk = block_at(a, st.ids_q, 0);
+    next_hoff = st.hoff_q;
+  } else {
+    next_blk = block_at(a, st.ids, st.i);
+  }
+  issue<NJ>(a, ln, next_blk, next_hoff, Kn, Vn);
+  // Keep the scheduler from sinking those loads below the compute.
+  __builtin_amdgcn_sched_barrier(0);
+
+  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+  const int b = P.off + st.i;
+  f32x4_t sc = zero4;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) sc = mfma32(K[j], st.qv[j], sc);
+  const int pos0 = b * kBlock + ln.grp * 4;
+  float z[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) z[r] = (pos0 + r < P.n) ? sc[r] * a.scale_log2 : -INFINITY;
+  float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(st.m_run, mx);  // finite: token b*16 is always < n
+  const float alpha = fast_exp2(st.m_run - m_new);
+  st.m_run = m_new;
+
+  // P = P_hi + P_lo, both bf16.
+  const float p0 = fast_exp2(z[0] - m_new), p1 = fast_exp2(z[1] - m_new);
+  const float p2 = fast_exp2(z[2] - m_new), p3 = fast_exp2(z[3] - m_new);
+  const uint32_t h01 = to_bf16x2(p0, p1), h23 = to_bf16x2(p2, p3);
+  const u32x2_t pb_hi = {h01, h23};
+  const u32x2_t pb_lo = {to_bf16x2(p0 - bf16_lo(h01), p1 - bf16_hi(h01)),
+                         to_bf16x2(p2 - bf16_lo(h23), p3 - bf16_hi(h23))};
+  st.l_part = st.l_part * alpha + ((p0 + p1) + (p2 + p3));
+#pragma unroll
+  for (int t = 0; t < 2 * NJ; ++t) st.acc[t] *= alpha;
+
+  // V rows of tokens at or past n must not reach the sum, even as NaN * 0.
+  const bool v_live = b * kBlock + ln.c < P.n;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const u32x2_t vin = v_live ? u32x2_t{V[j][2 * h], V[j][2 * h + 1]} : u32x2_t{0u, 0u};
+      const f32x4_t t = mfma16(vin, ln.sel, zero4);
+      const u32x2_t av = {pack_hi(t[0], t[1]), pack_hi(t[2], t[3])};
+      st.acc[2 * j + h] = mfma16(av, pb_hi, st.acc[2 * j + h]);
+      st.acc[2 * j + h] = mfma16(av, pb_lo, st.acc[2 * j + h]);
+    }
+  }
+
+  st.i = nx;
+  if (nx < P.cnt) return true;
+  if (P.ends_piece) finish_piece<NJ>(a, ln, st);
+  if (!st.has_q) return false;
+  advance<NJ>(a, ln, wk, st);
+  return true;
+}
+
 template <int D>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_kernel(const DecodeArgs a) {
-  constexpr int NJ = D / 32;
+  constexpr int NJ = D / 32;  // MFMA steps over head_size; 16-byte loads per lane per row
   static_assert(NJ >= 1 && D % 32 == 0, "head_size must be a multiple of 32");
   __shared__ long long red[8];
   __shared__ int found_seq;
@@ -248,14 +450,11 @@ void decode_kernel(const DecodeArgs a) {
 
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wavefront
   const int lane = tid & 63;
-  const int c = lane & 15;
-  const int grp = lane >> 4;
   const int w = blockIdx.x;
   const int S = a.num_seqs;
   const int NG = a.num_head_groups;
-  const int HG = a.heads_per_wg;
   const int cap = a.max_blocks_per_seq * kBlock;
   const long long W = a.num_wgs;
 
@@ -307,82 +506,78 @@ void decode_kernel(const DecodeArgs a) {
     if (found_seq >= 0) break;
     before += chunk_total;
   }
-
   if (found_seq < 0) return;  // only if the lengths changed during the call
 
-  // Walk the range, piece by piece; every wavefront takes KV head
-  // hg*HG + wave of each piece.
-  int s = found_seq;
-  long long seg_base = found_prefix * NG;  // first unit of sequence s
-  int n = clamp_len(a.context_lens[s], cap);
-  int L = (n + kBlock - 1) / kBlock;
-  int hg = (int)((lo - seg_base) / L);
-  int off = (int)((lo - seg_base) % L);
-  long long u = lo;
-  bool first = true;
-  const bool head_ok = c < a.group;
+  Walker wk;
+  wk.lens = a.context_lens;
+  wk.S = S;
+  wk.NG = NG;
+  wk.cap = cap;
+  wk.lane = lane;
+  wk.u = lo;
+  wk.hi = hi;
+  wk.seg_base = found_prefix * NG;
+  wk.s = found_seq;
+  load_window(wk, found_seq);
+  wk.n = len_of(wk, found_seq);
+  wk.L = (wk.n + kBlock - 1) / kBlock;
+  wk.hg = (int)((lo - wk.seg_base) / wk.L);
+  wk.off = (int)((lo - wk.seg_base) % wk.L);
+  wk.piece_off = wk.off;
+  wk.first = true;
 
-  while (u < hi) {
-    const long long seg_start = seg_base + (long long)hg * L;
-    const int piece = (int)min((long long)(L - off), hi - u);
-    const int g = hg * HG + wave;
-    const int head = g * a.group + (head_ok ? c : 0);
+  // The wavefront serves KV head hg*HG + wave of every piece: its query heads
+  // are that head's group, one per lane column c. Lanes with c >= group
+  // repeat the group's last head; their results are never stored.
+  Lane ln;
+  ln.tid = tid;
+  ln.wave = wave;
+  ln.lane = lane;
+  ln.c = lane & 15;
+  ln.grp = lane >> 4;
+  ln.w = w;
+  ln.HG = a.heads_per_wg;
+  ln.NG = NG;
+  ln.head_ok = ln.c < a.group;
+  ln.crow = ln.head_ok ? ln.c : a.group - 1;
+  ln.blk_stride = (size_t)a.num_kv_heads * D * kBlock;
+  ln.lane_off = (uint32_t)(((size_t)ln.c * a.num_kv_heads * D + ln.grp * 8) * sizeof(uint16_t));
+  ln.U = U;
+  ln.E = E;
+  // One-hot selector: lane (c, grp) holds 1.0 in element c%4 iff grp == c/4.
+  ln.sel = u32x2_t{0u, 0u};
+  if (ln.grp == (ln.c >> 2)) {
+    const uint32_t word = (ln.c & 1) ? (kBf16One << 16) : kBf16One;
+    if (ln.c & 2) ln.sel.y = word; else ln.sel.x = word;
+  }
 
-    u32x4_t qv[NJ];
-    {
-      const uint16_t *q_row = a.q + ((size_t)s * a.num_q_heads + head) * D + grp * 8;
+  // Software pipeline over the workgroup's stream of blocks. Two register
+  // buffers take turns: while one block is computed, the next block of the
+  // stream (possibly the first block of the next piece) loads into the
+  // other. The next piece's q and table entries load one piece ahead.
+  Stream<NJ> st;
+  next_chunk(wk, st.P);
+  load_q<NJ>(a, ln, st.P, st.qv);
+  st.ids = table_ids(a, ln, st.P, st.P.off, st.P.cnt);
+  st.hoff = head_off<NJ>(ln, st.P);
+  st.has_q = next_chunk(wk, st.Q);
+  st.ids_q = 0;
+  st.hoff_q = 0;
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) qv[j] = head_ok ? load16(q_row + 32 * j) : u32x4_t{0, 0, 0, 0};
-    }
-    float m_run = -INFINITY, l_part = 0.f;
-    f32x4_t acc[2 * NJ];
+  for (int j = 0; j < NJ; ++j) st.qn[j] = st.qv[j];
+  if (st.has_q) {
+    if (st.Q.starts_piece) load_q<NJ>(a, ln, st.Q, st.qn);
+    st.ids_q = table_ids(a, ln, st.Q, st.Q.off, st.Q.cnt);
+    st.hoff_q = head_off<NJ>(ln, st.Q);
+  }
+  st.i = 0;
+  st.m_run = -INFINITY;
+  st.l_part = 0.f;
 #pragma unroll
-    for (int t = 0; t < 2 * NJ; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    attend_blocks<D>(a, s, g, off, off + piece, n, qv, m_run, l_part, acc);
-    float l = l_part + __shfl_xor(l_part, 16);
-    l += __shfl_xor(l, 32);
-
-    const bool whole = off == 0 && piece == L;
-    const bool ends_here = off + piece == L;
-    if (whole) {
-      if (head_ok) store_out<NJ>(a.out + ((size_t)s * a.num_q_heads + head) * D + grp * 8, acc, 1.f / l);
-    } else {
-      const int slot = first ? 0 : 1;
-      const size_t row = (((size_t)w * 2 + slot) * HG + wave) * a.group + c;
-      if (head_ok) {
-        float *po = a.part_o + row * D + grp * 8;
-#pragma unroll
-        for (int t = 0; t < 2 * NJ; ++t)
-          *reinterpret_cast<f32x4_t *>(po + 32 * (t >> 1) + 4 * (t & 1)) = acc[t];
-        if (grp == 0) *reinterpret_cast<f32x2_t *>(a.part_ml + row * 2) = f32x2_t{m_run, l};
-      }
-    }
-    if (ends_here && tid == 0 && a.merge_desc) {
-      int2 d = {-1, -1};
-      if (!whole) {  // the segment began in an earlier workgroup: record its pieces
-        const int w0 = owner_of(seg_start, U, E);
-        const int slot0 = range_lo(w0, U, E) < seg_start ? 1 : 0;
-        d = int2{w0 * 2 + slot0, w};
-      }
-      a.merge_desc[(size_t)s * NG + hg] = d;
-    }
-
-    first = false;
-    u += piece;
-    off += piece;
-    if (off == L) {
-      off = 0;
-      if (++hg == NG && u < hi) {
-        hg = 0;
-        seg_base += (long long)NG * L;
-        do {  // units remain, so a non-empty sequence follows
-          ++s;
-          n = s < S ? clamp_len(a.context_lens[s], cap) : 0;
-          L = (n + kBlock - 1) / kBlock;
-        } while (L == 0 && s < S);
-        if (s >= S) break;  // only if the lengths changed during the call
-      }
-    }
+  for (int t = 0; t < 2 * NJ; ++t) st.acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  u32x4_t KA[NJ], VA[NJ], KB[NJ], VB[NJ];
+  issue<NJ>(a, ln, block_at(a, st.ids, 0), st.hoff, KA, VA);
+  while (step<NJ>(a, ln, wk, st, KA, VA, KB, VB) && step<NJ>(a, ln, wk, st, KB, VB, KA, VA)) {
   }
 }
 

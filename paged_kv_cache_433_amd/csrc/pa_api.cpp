@@ -30,14 +30,16 @@ int hip_fail(hipError_t e, const char *what) {
 
 // Workgroups per decode call. The units (blocks x head groups) are shared
 // evenly by all workgroups, so the count only sets how much of the chip is
-// busy and how many segments get cut: 16 wavefronts per compute unit on a
-// 256-CU MI355X (4 per SIMD, which the kernel's register budget allows),
-// and at least 4 units per workgroup when every sequence has
-// max_blocks_per_seq blocks. The count depends on the sizes only (not on the
-// device or the data), so workspace sizes can be computed on the host and
+// busy and how many segments get cut. The kernel keeps two blocks per
+// wavefront in flight and fits 2 wavefronts per SIMD, so 8 wavefronts per
+// compute unit on a 256-CU MI355X: floor(8 / heads_per_wg) workgroups per CU,
+// all resident at once (a second round of workgroups would undo the
+// balance). Fewer when every sequence at max_blocks_per_seq would still give
+// a workgroup fewer than 4 units. The count depends on the sizes only (not on
+// the device or the data), so workspace sizes are a host function and
 // results are reproducible. PA_DECODE_WGS overrides it (tests, tuning).
 constexpr int64_t kTargetCUs = 256;
-constexpr int64_t kWavesPerCU = 16;
+constexpr int64_t kWavesPerCU = 8;
 
 int32_t decode_wgs(int64_t num_seqs, int32_t num_head_groups, int32_t heads_per_wg,
                    int32_t max_blocks_per_seq) {

@@ -85,7 +85,7 @@ def test_workspace_size_and_check(L, monkeypatch):
     need = L.pa_decode_workspace_bytes(ctypes.byref(d), 4, 32, 32)
     assert need >= 4 * 8 + wgs * 2 * 8 * 4 * (128 + 2) * 4
     need = L.pa_decode_workspace_bytes(ctypes.byref(d), 256, 32, 256)
-    wgs = 256 * 2                     # 16 wavefronts per CU on 256 CUs, 8 per workgroup
+    wgs = 256                         # 8 wavefronts per CU on 256 CUs, 8 per workgroup
     assert need >= 256 * 8 + wgs * 2 * 8 * 4 * (128 + 2) * 4
     assert need < 2 * (256 * 8 + wgs * 2 * 8 * 4 * (128 + 2) * 4)
     assert decode(L, d, S=256, hq=32, mb=256, ws=P, wsb=need - 1) == _lib.PA_ERR_WORKSPACE
