@@ -91,6 +91,32 @@ def cpu_baseline(batch, seconds: float):
     }
 
 
+def probe_copy(nbytes: int, steps: int, warmup: int, dev) -> int:
+    """Time pa_probe_copy over `nbytes` bytes (read once, written once)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_433_amd as pa
+
+    nbytes = (nbytes + 15) // 16 * 16
+    src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(warmup):
+        pa.probe_copy(dst, src)
+    stream = torch.cuda.current_stream(dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record(stream)
+        pa.probe_copy(dst, src)
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = float(np.median([a.elapsed_time(b) for a, b in evs]) * 1e3)
+    print(json.dumps({"probe": "copy", "bytes_read": nbytes, "bytes_written": nbytes, "launches": warmup + steps,
+                      "median_us": round(us, 2), "read_plus_write_GBps": round(2 * nbytes / us / 1e3, 1)}),
+          flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -99,6 +125,9 @@ def main(argv=None) -> int:
     ap.add_argument("--config", default="llama3_8b_gqa")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--probe-copy", type=int, default=0, metavar="BYTES",
+                    help="instead of the decode step: time a plain 16-byte copy of BYTES bytes "
+                         "(the reference kernel that calibrates rocprofv3 byte counters)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -113,6 +142,8 @@ def main(argv=None) -> int:
     from paged_kv_cache_433_amd import workloads as W
 
     dev = torch.device("cuda:0")
+    if args.probe_copy:
+        return probe_copy(args.probe_copy, args.steps, args.warmup, dev)
     print(f"[bench] generating {args.config}", file=sys.stderr, flush=True)
     b = W.make_config(args.config)
 

@@ -146,65 +146,42 @@ __device__ __forceinline__ long long wg_sum(long long v, long long *red, int wav
 }
 
 // A piece is the run of blocks of one (sequence, head group) that lies in
-// this workgroup's range of units; the walk hands it out in chunks of at
-// most 64 blocks, so that one register per lane holds a chunk's table
-// entries.
+// this workgroup's range of units.
 struct Piece {
   long long seg_start;  // first unit of the segment the piece belongs to
   int s;                // sequence
   int hg;               // head group
-  int off;              // first logical block of the chunk
-  int cnt;              // blocks in the chunk, 1..64
-  int piece_off;        // first logical block of the piece
+  int off;              // first logical block of the piece
+  int cnt;              // blocks in the piece (>= 1)
   int n;                // context length of s (clamped)
   int L;                // blocks of s
-  bool first;           // the piece is the workgroup's first piece
-  bool starts_piece;    // the chunk is the piece's first
-  bool ends_piece;      // the chunk is the piece's last
+  bool first;           // the workgroup's first piece
 };
 
 // Produces the workgroup's pieces in order. Every thread of the workgroup
-// runs the same walk (the state is uniform). Context lengths come from a
-// window of 64 consecutive sequences held one per lane (read with
-// readlane), so the walk issues no memory load, and so no wait, while K/V
-// loads are in flight; the window moves only after 64 sequences.
+// runs the same walk; the state is uniform, and so are the addresses of the
+// context lengths it reads (scalar loads).
 struct Walker {
   const int32_t *lens;
-  int S, NG, cap, lane;
+  int S, NG, cap;
   long long u, hi, seg_base;
   int s, hg, off, L, n;
-  int win, win_base;  // clamped lens[win_base + lane]
-  int piece_off;      // first block of the current piece
-  bool first;         // the current piece is the workgroup's first
+  bool first;
 };
 
-__device__ __forceinline__ void load_window(Walker &wk, int base) {
-  wk.win_base = base;
-  wk.win = clamp_len(wk.lens[min(base + wk.lane, wk.S - 1)], wk.cap);
-}
-
-__device__ __forceinline__ int len_of(Walker &wk, int t) {
-  if (t - wk.win_base >= 64) load_window(wk, t);
-  return __builtin_amdgcn_readlane(wk.win, t - wk.win_base);
-}
-
-__device__ __forceinline__ bool next_chunk(Walker &wk, Piece &p) {
+__device__ __forceinline__ bool next_piece(Walker &wk, Piece &p) {
   if (wk.u >= wk.hi) return false;
-  const int piece_left = (int)min((long long)(wk.L - wk.off), wk.hi - wk.u);
   p.s = wk.s;
   p.hg = wk.hg;
   p.off = wk.off;
   p.n = wk.n;
   p.L = wk.L;
-  p.cnt = min(64, piece_left);
-  p.piece_off = wk.piece_off;
+  p.cnt = (int)min((long long)(wk.L - wk.off), wk.hi - wk.u);
   p.seg_start = wk.seg_base + (long long)wk.hg * wk.L;
   p.first = wk.first;
-  p.starts_piece = wk.off == wk.piece_off;
-  p.ends_piece = p.cnt == piece_left;
+  wk.first = false;
   wk.u += p.cnt;
   wk.off += p.cnt;
-  if (p.ends_piece) wk.first = false;
   if (wk.off == wk.L) {
     wk.off = 0;
     if (++wk.hg == wk.NG && wk.u < wk.hi) {
@@ -212,13 +189,12 @@ __device__ __forceinline__ bool next_chunk(Walker &wk, Piece &p) {
       wk.seg_base += (long long)wk.NG * wk.L;
       do {  // units remain, so a non-empty sequence follows
         ++wk.s;
-        wk.n = wk.s < wk.S ? len_of(wk, wk.s) : 0;
+        wk.n = wk.s < wk.S ? clamp_len(wk.lens[wk.s], wk.cap) : 0;
         wk.L = (wk.n + kBlock - 1) / kBlock;
       } while (wk.L == 0 && wk.s < wk.S);
       if (wk.s >= wk.S) wk.u = wk.hi;  // only if the lengths changed during the call
     }
   }
-  if (p.ends_piece) wk.piece_off = wk.off;
   return true;
 }
 
@@ -226,50 +202,65 @@ __device__ __forceinline__ bool next_chunk(Walker &wk, Piece &p) {
 struct Lane {
   int tid, wave, lane, c, grp, w;
   int HG, NG;
-  bool head_ok;  // lane column c is a query head of the group
-  int crow;      // query head the lane loads (c, or the group's last head)
+  bool head_ok;       // lane column c is a query head of the group
+  int crow;           // query head the lane loads (c, or the group's last head)
   size_t blk_stride;  // elements per block of one cache array
-  uint32_t lane_off;  // byte offset of the lane's 16 bytes inside (block, head): token c, dims 8*grp..
+  uint32_t lane_off;  // byte offset of the lane's 16 bytes in (block, head): token c, dims 8*grp..
+  uint32_t q_off;     // byte offset of the lane's 16 bytes in a group's q rows: row crow, dims 8*grp..
   long long U, E;
+  uint32_t pool32;    // min(num_blocks, INT32_MAX)
   u32x2_t sel;
 };
 
 // One wavefront's pass over its workgroup's stream of blocks.
 template <int NJ>
 struct Stream {
-  Piece P, Q;         // the chunk being computed and the next one
+  Piece P, Q;         // the piece being computed and the next one
   bool has_q;
   int i;              // block of P being computed
-  int ids;            // table entries of P's blocks, one per lane
-  int ids_q;          // table entries of Q's blocks
+  int ord;            // P's position among the workgroup's pieces
   size_t hoff, hoff_q;
-  u32x4_t qv[NJ], qn[NJ];
+  u32x4_t qv[NJ];     // q of P, in the MFMA operand layout
   float m_run;        // running max of base-2 logits, query head c
   float l_part;       // this lane's share of the running sum
   f32x4_t acc[2 * NJ];
 };
 
+// Buffer-resource word 3 for gfx9-family raw (untyped) buffer loads.
+constexpr int kRawBufferWord3 = 0x00020000;
+
+// q rows of the piece's query-head group for this wavefront, in the MFMA
+// operand layout. Read through a buffer resource (scalar base, fixed lane
+// offset) so that no vector address is computed here.
 template <int NJ>
 __device__ __forceinline__ void load_q(const DecodeArgs &a, const Lane &ln, const Piece &p, u32x4_t (&qv)[NJ]) {
   constexpr int D = NJ * 32;
-  const uint16_t *qr = a.q +
-                       ((size_t)p.s * a.num_q_heads + (size_t)(p.hg * ln.HG + ln.wave) * a.group + ln.crow) * D +
-                       ln.grp * 8;
+  const size_t base =
+      ((size_t)p.s * a.num_q_heads + (size_t)(p.hg * ln.HG + ln.wave) * a.group) * D * sizeof(uint16_t);
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char *>(reinterpret_cast<const char *>(a.q) + base), 0, a.group * D * (int)sizeof(uint16_t),
+      kRawBufferWord3);
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) qv[j] = load16(qr + 32 * j);
+  for (int j = 0; j < NJ; ++j)
+    qv[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, ln.q_off + 64 * j, 0, 0));
 }
 
-// Table entries [b0, b0 + 64) of the piece's sequence, one per lane; lanes
-// past `left` repeat the last entry. The load is unconditional and the
-// value is checked only where it is used, so no wait is forced here.
-__device__ __forceinline__ int table_ids(const DecodeArgs &a, const Lane &ln, const Piece &p, int b0, int left) {
-  return a.block_tables[(size_t)p.s * a.max_blocks_per_seq + b0 + (ln.lane < left ? ln.lane : left - 1)];
+// q of the next piece travels through LDS: two slots per wavefront, each
+// holding the group's rows [group][D] as bf16; slot = piece position & 1.
+template <int NJ>
+__device__ __forceinline__ uint16_t *q_slot(uint16_t *lds, const DecodeArgs &a, const Lane &ln, int ord) {
+  return lds + ((size_t)ln.wave * 2 + (ord & 1)) * a.group * (NJ * 32);
 }
 
-// Physical block held by lane k of `ids`, clamped to the pool.
-__device__ __forceinline__ int block_at(const DecodeArgs &a, int ids, int k) {
-  const int b = __builtin_amdgcn_readlane(ids, k);
-  return (b < 0 || (int64_t)b >= a.num_blocks) ? 0 : b;
+// Physical block of logical block b of sequence s, clamped to the pool. The
+// address is uniform, so this is a scalar load: waiting for it never waits
+// for the K/V loads in flight.
+// pool32 = min(num_blocks, INT32_MAX): one unsigned compare, in scalar
+// registers, rejects negative ids and ids past the pool.
+__device__ __forceinline__ int block_id(const int32_t *__restrict__ tables, const DecodeArgs &a, uint32_t pool32,
+                                        int s, int b) {
+  const int id = tables[(size_t)s * a.max_blocks_per_seq + b];
+  return (uint32_t)id < pool32 ? id : 0;
 }
 
 // Element offset of the wavefront's KV head inside a token row (uniform).
@@ -277,9 +268,6 @@ template <int NJ>
 __device__ __forceinline__ size_t head_off(const Lane &ln, const Piece &p) {
   return (size_t)(p.hg * ln.HG + ln.wave) * (NJ * 32);
 }
-
-// Buffer-resource word 3 for gfx9-family raw (untyped) buffer loads.
-constexpr int kRawBufferWord3 = 0x00020000;
 
 // Starts the loads of one block's K and V rows for this wavefront's head.
 // Each array is read through a buffer resource whose base is the (block,
@@ -304,31 +292,6 @@ __device__ __forceinline__ void issue(const DecodeArgs &a, const Lane &ln, int b
     V[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, ln.lane_off + 64 * j, 0, 0));
 }
 
-// Makes Q the current chunk (its first block is already loading) and looks
-// one chunk further ahead. A new piece starts from fresh softmax state and
-// the q loaded for it.
-template <int NJ>
-__device__ __forceinline__ void advance(const DecodeArgs &a, const Lane &ln, Walker &wk, Stream<NJ> &st) {
-  st.P = st.Q;
-  if (st.P.starts_piece) {
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) st.qv[j] = st.qn[j];
-    st.m_run = -INFINITY;
-    st.l_part = 0.f;
-#pragma unroll
-    for (int t = 0; t < 2 * NJ; ++t) st.acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
-  st.ids = st.ids_q;
-  st.hoff = st.hoff_q;
-  st.i = 0;
-  st.has_q = next_chunk(wk, st.Q);
-  if (st.has_q) {
-    if (st.Q.starts_piece) load_q<NJ>(a, ln, st.Q, st.qn);
-    st.ids_q = table_ids(a, ln, st.Q, st.Q.off, st.Q.cnt);
-    st.hoff_q = head_off<NJ>(ln, st.Q);
-  }
-}
-
 // Writes P's result: bf16 output when P is a whole segment, otherwise its
 // partial record; the workgroup holding a segment's last unit records the
 // segment's pieces for the merge.
@@ -339,7 +302,7 @@ __device__ __forceinline__ void finish_piece(const DecodeArgs &a, const Lane &ln
   float l = st.l_part + __shfl_xor(st.l_part, 16);
   l += __shfl_xor(l, 32);
   const int head = (P.hg * ln.HG + ln.wave) * a.group + ln.c;
-  const bool whole = P.piece_off == 0 && P.off + P.cnt == P.L;
+  const bool whole = P.off == 0 && P.cnt == P.L;
   if (whole) {
     if (ln.head_ok)
       store_out<NJ>(a.out + ((size_t)P.s * a.num_q_heads + head) * D + ln.grp * 8, st.acc, 1.f / l);
@@ -364,29 +327,53 @@ __device__ __forceinline__ void finish_piece(const DecodeArgs &a, const Lane &ln
   }
 }
 
+// Makes Q the current piece (its first block is already loading, its q is
+// in LDS) and looks one piece further ahead.
+template <int NJ>
+__device__ __forceinline__ void advance(const DecodeArgs &a, const Lane &ln, Walker &wk, Stream<NJ> &st,
+                                        uint16_t *lds) {
+  st.P = st.Q;
+  ++st.ord;
+  const uint16_t *qs = q_slot<NJ>(lds, a, ln, st.ord) + ln.crow * (NJ * 32) + ln.grp * 8;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) st.qv[j] = *reinterpret_cast<const u32x4_t *>(qs + 32 * j);
+  st.hoff = st.hoff_q;
+  st.i = 0;
+  st.m_run = -INFINITY;
+  st.l_part = 0.f;
+#pragma unroll
+  for (int t = 0; t < 2 * NJ; ++t) st.acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  st.has_q = next_piece(wk, st.Q);
+  if (!st.has_q) st.Q = st.P;
+  st.hoff_q = head_off<NJ>(ln, st.Q);
+}
+
 // Computes block i of P from (K, V) after starting the next block of the
 // stream loading into (Kn, Vn); finishes P at its end and moves to Q.
 // Returns false once the stream is done.
 template <int NJ>
-__device__ __forceinline__ bool step(const DecodeArgs &a, const Lane &ln, Walker &wk, Stream<NJ> &st,
-                                     u32x4_t (&K)[NJ], u32x4_t (&V)[NJ], u32x4_t (&Kn)[NJ], u32x4_t (&Vn)[NJ]) {
+__device__ __forceinline__ bool step(const int32_t *__restrict__ tables, const DecodeArgs &a, const Lane &ln,
+                                     Walker &wk, Stream<NJ> &st, u32x4_t (&K)[NJ], u32x4_t (&V)[NJ],
+                                     u32x4_t (&Kn)[NJ], u32x4_t (&Vn)[NJ], uint16_t *lds) {
   const Piece &P = st.P;
+  // In P's first step, q of the next piece is loaded (before this step's K/V
+  // loads) and parked in LDS at the end of the step: the registers never
+  // cross a loop iteration, and the wait for them covers only the K/V loads
+  // issued after them.
+  const bool stage_q = st.i == 0 && st.has_q;
+  u32x4_t qt[NJ];
+  if (stage_q) load_q<NJ>(a, ln, st.Q, qt);
   // The next block of the stream: P's next, else Q's first. The loads are
   // issued on every path (past the end of the stream they reload the
-  // current block), so the compiler can count them when it places the wait
-  // for the current block: it waits for that block only, not for the next.
+  // current block, which is still in the cache), so the compiler can count
+  // them when it places the wait for the current block: it waits for that
+  // block only, not for the next.
   const int nx = st.i + 1;
-  int next_blk;
-  size_t next_hoff = st.hoff;
-  if (nx < P.cnt) {
-    next_blk = block_at(a, st.ids, nx);
-  } else if (st.has_q) {
-    next_blk = block_at(a, st.ids_q, 0);
-    next_hoff = st.hoff_q;
-  } else {
-    next_blk = block_at(a, st.ids, st.i);
-  }
-  issue<NJ>(a, ln, next_blk, next_hoff, Kn, Vn);
+  const bool in_p = nx < P.cnt;
+  const bool to_q = !in_p && st.has_q;
+  const int next_s = to_q ? st.Q.s : P.s;
+  const int next_b = in_p ? P.off + nx : (to_q ? st.Q.off : P.off + st.i);
+  issue<NJ>(a, ln, block_id(tables, a, ln.pool32, next_s, next_b), to_q ? st.hoff_q : st.hoff, Kn, Vn);
   // Keep the scheduler from sinking those loads below the compute.
   __builtin_amdgcn_sched_barrier(0);
 
@@ -431,19 +418,26 @@ __device__ __forceinline__ bool step(const DecodeArgs &a, const Lane &ln, Walker
     }
   }
 
+  if (stage_q && ln.head_ok) {
+    uint16_t *qs = q_slot<NJ>(lds, a, ln, st.ord + 1) + ln.c * (NJ * 32) + ln.grp * 8;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) *reinterpret_cast<u32x4_t *>(qs + 32 * j) = qt[j];
+  }
+
   st.i = nx;
-  if (nx < P.cnt) return true;
-  if (P.ends_piece) finish_piece<NJ>(a, ln, st);
+  if (in_p) return true;
+  finish_piece<NJ>(a, ln, st);
   if (!st.has_q) return false;
-  advance<NJ>(a, ln, wk, st);
+  advance<NJ>(a, ln, wk, st, lds);
   return true;
 }
 
 template <int D>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
-void decode_kernel(const DecodeArgs a) {
+void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const int32_t *__restrict__ lens) {
   constexpr int NJ = D / 32;  // MFMA steps over head_size; 16-byte loads per lane per row
   static_assert(NJ >= 1 && D % 32 == 0, "head_size must be a multiple of 32");
+  extern __shared__ __align__(16) uint16_t q_lds[];  // heads_per_wg * 2 * group * D
   __shared__ long long red[8];
   __shared__ int found_seq;
   __shared__ long long found_prefix;
@@ -461,7 +455,7 @@ void decode_kernel(const DecodeArgs a) {
   // Pass 1: total units; zero rows (and "no merge" records) for empty sequences.
   long long mine = 0;
   for (int s = tid; s < S; s += nthr) {
-    const int n = clamp_len(a.context_lens[s], cap);
+    const int n = clamp_len(lens[s], cap);
     mine += (n + kBlock - 1) / kBlock;
     if (n == 0 && s % a.num_wgs == w) {
       u32x4_t *row = reinterpret_cast<u32x4_t *>(a.out + (size_t)s * a.num_q_heads * D);
@@ -481,7 +475,7 @@ void decode_kernel(const DecodeArgs a) {
   long long before = 0;  // blocks of all sequences preceding this chunk
   for (int base = 0; base < S; base += nthr) {
     const int s = base + tid;
-    const long long L = s < S ? (clamp_len(a.context_lens[s], cap) + kBlock - 1) / kBlock : 0;
+    const long long L = s < S ? (clamp_len(lens[s], cap) + kBlock - 1) / kBlock : 0;
     long long incl = L;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -509,21 +503,18 @@ void decode_kernel(const DecodeArgs a) {
   if (found_seq < 0) return;  // only if the lengths changed during the call
 
   Walker wk;
-  wk.lens = a.context_lens;
+  wk.lens = lens;
   wk.S = S;
   wk.NG = NG;
   wk.cap = cap;
-  wk.lane = lane;
   wk.u = lo;
   wk.hi = hi;
   wk.seg_base = found_prefix * NG;
-  wk.s = found_seq;
-  load_window(wk, found_seq);
-  wk.n = len_of(wk, found_seq);
+  wk.s = __builtin_amdgcn_readfirstlane(found_seq);
+  wk.n = clamp_len(lens[wk.s], cap);
   wk.L = (wk.n + kBlock - 1) / kBlock;
   wk.hg = (int)((lo - wk.seg_base) / wk.L);
   wk.off = (int)((lo - wk.seg_base) % wk.L);
-  wk.piece_off = wk.off;
   wk.first = true;
 
   // The wavefront serves KV head hg*HG + wave of every piece: its query heads
@@ -542,8 +533,10 @@ void decode_kernel(const DecodeArgs a) {
   ln.crow = ln.head_ok ? ln.c : a.group - 1;
   ln.blk_stride = (size_t)a.num_kv_heads * D * kBlock;
   ln.lane_off = (uint32_t)(((size_t)ln.c * a.num_kv_heads * D + ln.grp * 8) * sizeof(uint16_t));
+  ln.q_off = (uint32_t)((ln.crow * D + ln.grp * 8) * sizeof(uint16_t));
   ln.U = U;
   ln.E = E;
+  ln.pool32 = (uint32_t)(a.num_blocks < 0x7fffffffLL ? a.num_blocks : 0x7fffffffLL);
   // One-hot selector: lane (c, grp) holds 1.0 in element c%4 iff grp == c/4.
   ln.sel = u32x2_t{0u, 0u};
   if (ln.grp == (ln.c >> 2)) {
@@ -554,30 +547,24 @@ void decode_kernel(const DecodeArgs a) {
   // Software pipeline over the workgroup's stream of blocks. Two register
   // buffers take turns: while one block is computed, the next block of the
   // stream (possibly the first block of the next piece) loads into the
-  // other. The next piece's q and table entries load one piece ahead.
+  // other. The next piece's q goes through LDS one piece ahead.
   Stream<NJ> st;
-  next_chunk(wk, st.P);
+  next_piece(wk, st.P);
   load_q<NJ>(a, ln, st.P, st.qv);
-  st.ids = table_ids(a, ln, st.P, st.P.off, st.P.cnt);
   st.hoff = head_off<NJ>(ln, st.P);
-  st.has_q = next_chunk(wk, st.Q);
-  st.ids_q = 0;
-  st.hoff_q = 0;
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) st.qn[j] = st.qv[j];
-  if (st.has_q) {
-    if (st.Q.starts_piece) load_q<NJ>(a, ln, st.Q, st.qn);
-    st.ids_q = table_ids(a, ln, st.Q, st.Q.off, st.Q.cnt);
-    st.hoff_q = head_off<NJ>(ln, st.Q);
-  }
+  st.has_q = next_piece(wk, st.Q);
+  if (!st.has_q) st.Q = st.P;
+  st.hoff_q = head_off<NJ>(ln, st.Q);
   st.i = 0;
+  st.ord = 0;
   st.m_run = -INFINITY;
   st.l_part = 0.f;
 #pragma unroll
   for (int t = 0; t < 2 * NJ; ++t) st.acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   u32x4_t KA[NJ], VA[NJ], KB[NJ], VB[NJ];
-  issue<NJ>(a, ln, block_at(a, st.ids, 0), st.hoff, KA, VA);
-  while (step<NJ>(a, ln, wk, st, KA, VA, KB, VB) && step<NJ>(a, ln, wk, st, KB, VB, KA, VA)) {
+  issue<NJ>(a, ln, block_id(tables, a, ln.pool32, st.P.s, st.P.off), st.hoff, KA, VA);
+  while (step<NJ>(tables, a, ln, wk, st, KA, VA, KB, VB, q_lds) &&
+         step<NJ>(tables, a, ln, wk, st, KB, VB, KA, VA, q_lds)) {
   }
 }
 
@@ -635,10 +622,11 @@ __global__ __launch_bounds__(1024) void merge_kernel(const DecodeArgs a) {
 hipError_t launch_decode(const DecodeArgs &args, int32_t head_size, hipStream_t stream) {
   const dim3 grid((unsigned)args.num_wgs);
   const dim3 block(64 * (unsigned)args.heads_per_wg);
+  const size_t lds = (size_t)args.heads_per_wg * 2 * args.group * head_size * sizeof(uint16_t);
   if (head_size == 128) {
-    hipLaunchKernelGGL(decode_kernel<128>, grid, block, 0, stream, args);
+    hipLaunchKernelGGL(decode_kernel<128>, grid, block, lds, stream, args, args.block_tables, args.context_lens);
   } else if (head_size == 64) {
-    hipLaunchKernelGGL(decode_kernel<64>, grid, block, 0, stream, args);
+    hipLaunchKernelGGL(decode_kernel<64>, grid, block, lds, stream, args, args.block_tables, args.context_lens);
   } else {
     return hipErrorInvalidValue;
   }

@@ -30,16 +30,17 @@ int hip_fail(hipError_t e, const char *what) {
 
 // Workgroups per decode call. The units (blocks x head groups) are shared
 // evenly by all workgroups, so the count only sets how much of the chip is
-// busy and how many segments get cut. The kernel keeps two blocks per
-// wavefront in flight and fits 2 wavefronts per SIMD, so 8 wavefronts per
-// compute unit on a 256-CU MI355X: floor(8 / heads_per_wg) workgroups per CU,
+// busy and how many segments get cut. One wavefront per SIMD, 4 per compute
+// unit on a 256-CU MI355X: two wavefronts on one SIMD compete for issue,
+// and the older one runs ahead while the younger one finishes alone with
+// half the loads in flight. So floor(4 / heads_per_wg) workgroups per CU,
 // all resident at once (a second round of workgroups would undo the
 // balance). Fewer when every sequence at max_blocks_per_seq would still give
 // a workgroup fewer than 4 units. The count depends on the sizes only (not on
 // the device or the data), so workspace sizes are a host function and
 // results are reproducible. PA_DECODE_WGS overrides it (tests, tuning).
 constexpr int64_t kTargetCUs = 256;
-constexpr int64_t kWavesPerCU = 8;
+constexpr int64_t kWavesPerCU = 4;
 
 int32_t decode_wgs(int64_t num_seqs, int32_t num_head_groups, int32_t heads_per_wg,
                    int32_t max_blocks_per_seq) {
@@ -56,9 +57,10 @@ int32_t decode_wgs(int64_t num_seqs, int32_t num_head_groups, int32_t heads_per_
   return (int32_t)w;
 }
 
-// KV heads per workgroup: the largest divisor of num_kv_heads that is <= 8.
+// KV heads per workgroup (one wavefront each): the largest divisor of
+// num_kv_heads that is <= 4.
 int32_t heads_per_workgroup(int32_t num_kv_heads) {
-  for (int32_t h = 8; h > 1; --h)
+  for (int32_t h = 4; h > 1; --h)
     if (num_kv_heads % h == 0) return h;
   return 1;
 }

@@ -76,24 +76,29 @@ def test_decode_no_op_and_errors_reset(L):
 
 
 def test_workspace_size_and_check(L, monkeypatch):
-    d = desc()                        # 8 KV heads of 128: one workgroup per 8-head group
-    # one sequence of one block: a single workgroup, nothing is ever cut
-    assert L.pa_decode_workspace_bytes(ctypes.byref(d), 1, 32, 1) == 0
-    # otherwise: a merge record per (sequence, head group) and two partial
-    # records (max, sum, 128 floats) per workgroup, KV head and query head
-    wgs = (4 * 32 + 3) // 4           # at least 4 units per workgroup
+    d = desc()                        # 8 KV heads of 128: groups of 4 heads, one wavefront each
+    hg, ng, grp = 4, 2, 4             # heads per workgroup, head groups, query heads per KV head
+
+    def need_at_least(S, wgs):
+        # a merge record per (sequence, head group); two partial records
+        # (max, sum, 128 floats) per workgroup, KV head of the group and query head
+        return S * ng * 8 + wgs * 2 * hg * grp * (128 + 2) * 4
+
+    # one sequence of one block: at most one unit per head group; two groups
+    # give two workgroups at most, so partials are still possible
+    assert L.pa_decode_workspace_bytes(ctypes.byref(desc(num_kv_heads=4)), 1, 16, 1) == 0
+    wgs = (4 * ng * 32 + 3) // 4      # at least 4 units per workgroup
     need = L.pa_decode_workspace_bytes(ctypes.byref(d), 4, 32, 32)
-    assert need >= 4 * 8 + wgs * 2 * 8 * 4 * (128 + 2) * 4
+    assert need >= need_at_least(4, wgs)
     need = L.pa_decode_workspace_bytes(ctypes.byref(d), 256, 32, 256)
-    wgs = 256                         # 8 wavefronts per CU on 256 CUs, 8 per workgroup
-    assert need >= 256 * 8 + wgs * 2 * 8 * 4 * (128 + 2) * 4
-    assert need < 2 * (256 * 8 + wgs * 2 * 8 * 4 * (128 + 2) * 4)
+    wgs = 256                         # 4 wavefronts per CU on 256 CUs, 4 per workgroup
+    assert need_at_least(256, wgs) <= need < 2 * need_at_least(256, wgs)
     assert decode(L, d, S=256, hq=32, mb=256, ws=P, wsb=need - 1) == _lib.PA_ERR_WORKSPACE
     assert L.pa_decode_workspace_bytes(None, 1, 1, 1) == 0
     monkeypatch.setenv("PA_DECODE_WGS", "1")
     assert L.pa_decode_workspace_bytes(ctypes.byref(d), 256, 32, 256) == 0
     monkeypatch.setenv("PA_DECODE_WGS", "3")
-    assert L.pa_decode_workspace_bytes(ctypes.byref(d), 256, 32, 256) >= 3 * 2 * 8 * 4 * 130 * 4
+    assert L.pa_decode_workspace_bytes(ctypes.byref(d), 256, 32, 256) >= 3 * 2 * hg * grp * 130 * 4
 
 
 def test_cache_op_argument_errors(L):
