@@ -63,7 +63,9 @@ def cpu_baseline(batch, seconds: float):
     import oracle
     from paged_kv_cache_433_amd import workloads as W
 
-    kc, vc = batch.k_cache, batch.v_cache
+    kc, vc = batch.k_cache, batch.v_cache  # updated in place; the device copies exist already
+    if len(batch.cow_pairs):
+        oracle.copy_blocks(kc, vc, batch.cow_pairs)
     oracle.reshape_and_cache(kc, vc, batch.new_k, batch.new_v, batch.slot_mapping)
     order = np.random.default_rng(0).permutation(batch.num_seqs)
     done = []
@@ -145,7 +147,9 @@ def main(argv=None) -> int:
     if args.probe_copy:
         return probe_copy(args.probe_copy, args.steps, args.warmup, dev)
     print(f"[bench] generating {args.config}", file=sys.stderr, flush=True)
-    b = W.make_config(args.config)
+    # The beam-search workload's first step: its copy-on-write pairs, its
+    # scatter and its decode are repeated every step (both are idempotent).
+    b = W.BeamSearchWorkload().step() if args.config == "beam_cow" else W.make_config(args.config)
 
     def bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)

@@ -8,7 +8,7 @@
 // High-Throughput LLM Inference System", section "Scheduler").
 //
 // Work split (balanced). KV heads form groups of HG heads (HG = largest
-// divisor of num_kv_heads that is <= 8). A "unit" is one physical block of
+// divisor of num_kv_heads that is <= 4). A "unit" is one physical block of
 // one sequence for one head group; a "segment" is all units of one
 // (sequence, head group), in logical order. Segments are laid end to end in
 // (sequence, head group) order, and workgroup w takes units
@@ -47,9 +47,10 @@
 // exp2). Row maxima are shared by the four lanes of a head with two
 // cross-lane exchanges per block; row sums stay lane-partial until the end.
 //
-// Tokens past the context length are masked by a select on the logit and
-// their V rows are zeroed, so stale data in the tail of the last block (even
-// NaN) cannot reach the output. Block ids are clamped to the pool, and no
+// Tokens past the context length are never fetched (the last block's buffer
+// range ends at the context length, so those rows read as zeros), their
+// logits are masked by a select and their V rows are zeroed again, so stale
+// data in the tail of the last block (even NaN) cannot reach the output. Block ids are clamped to the pool, and no
 // table entry past a sequence's last used block is read.
 
 #include <hip/hip_runtime.h>
@@ -145,6 +146,29 @@ __device__ __forceinline__ long long wg_sum(long long v, long long *red, int wav
   return t;
 }
 
+// Inclusive prefix sum of `v` over the workgroup's threads in thread order.
+// Also returns the sum over the lower-numbered wavefronts (`pre`, to add to
+// the result) and over the whole workgroup (`total`). Starts and ends with a
+// barrier so it can be called repeatedly.
+__device__ __forceinline__ long long wg_scan(long long v, long long *red, int wave, int lane, int nwaves,
+                                             long long &pre, long long &total) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const long long o = __shfl_up(v, off);
+    if (lane >= off) v += o;
+  }
+  __syncthreads();
+  if (lane == 63) red[wave] = v;
+  __syncthreads();
+  pre = 0;
+  total = 0;
+  for (int i = 0; i < nwaves; ++i) {
+    if (i < wave) pre += red[i];
+    total += red[i];
+  }
+  return v;
+}
+
 // A piece is the run of blocks of one (sequence, head group) that lies in
 // this workgroup's range of units.
 struct Piece {
@@ -205,6 +229,7 @@ struct Lane {
   bool head_ok;       // lane column c is a query head of the group
   int crow;           // query head the lane loads (c, or the group's last head)
   size_t blk_stride;  // elements per block of one cache array
+  int row_bytes;      // bytes per token row of one cache array (all KV heads)
   uint32_t lane_off;  // byte offset of the lane's 16 bytes in (block, head): token c, dims 8*grp..
   uint32_t q_off;     // byte offset of the lane's 16 bytes in a group's q rows: row crow, dims 8*grp..
   long long U, E;
@@ -271,15 +296,15 @@ __device__ __forceinline__ size_t head_off(const Lane &ln, const Piece &p) {
 
 // Starts the loads of one block's K and V rows for this wavefront's head.
 // Each array is read through a buffer resource whose base is the (block,
-// head) start (scalar registers) and whose size ends at the block's end;
-// the lane adds its fixed offset. So no vector address arithmetic happens
-// per block, and an offset past the block would read zeros, not another
-// block.
+// head) start (scalar registers) and whose size covers the block's first
+// `nrows` token rows; the lane adds its fixed offset. So no vector address
+// arithmetic happens per block, and the rows past the context length in a
+// sequence's last block are never fetched: they read as zeros.
 template <int NJ>
-__device__ __forceinline__ void issue(const DecodeArgs &a, const Lane &ln, int blk, size_t hoff, u32x4_t (&K)[NJ],
-                                      u32x4_t (&V)[NJ]) {
+__device__ __forceinline__ void issue(const DecodeArgs &a, const Lane &ln, int blk, size_t hoff, int nrows,
+                                      u32x4_t (&K)[NJ], u32x4_t (&V)[NJ]) {
   const size_t base = ((size_t)blk * ln.blk_stride + hoff) * sizeof(uint16_t);
-  const int span = (int)((ln.blk_stride - hoff) * sizeof(uint16_t));
+  const int span = nrows * ln.row_bytes;
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<char *>(reinterpret_cast<const char *>(a.k_cache) + base), 0, span, kRawBufferWord3);
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
@@ -290,6 +315,12 @@ __device__ __forceinline__ void issue(const DecodeArgs &a, const Lane &ln, int b
 #pragma unroll
   for (int j = 0; j < NJ; ++j)
     V[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, ln.lane_off + 64 * j, 0, 0));
+}
+
+// Token rows of logical block b that lie before the context length n.
+__device__ __forceinline__ int rows_in(int n, int b) {
+  const int r = n - b * kBlock;
+  return r < kBlock ? r : kBlock;
 }
 
 // Writes P's result: bf16 output when P is a whole segment, otherwise its
@@ -373,7 +404,8 @@ __device__ __forceinline__ bool step(const int32_t *__restrict__ tables, const D
   const bool to_q = !in_p && st.has_q;
   const int next_s = to_q ? st.Q.s : P.s;
   const int next_b = in_p ? P.off + nx : (to_q ? st.Q.off : P.off + st.i);
-  issue<NJ>(a, ln, block_id(tables, a, ln.pool32, next_s, next_b), to_q ? st.hoff_q : st.hoff, Kn, Vn);
+  issue<NJ>(a, ln, block_id(tables, a, ln.pool32, next_s, next_b), to_q ? st.hoff_q : st.hoff,
+            rows_in(to_q ? st.Q.n : P.n, next_b), Kn, Vn);
   // Keep the scheduler from sinking those loads below the compute.
   __builtin_amdgcn_sched_barrier(0);
 
@@ -432,6 +464,17 @@ __device__ __forceinline__ bool step(const int32_t *__restrict__ tables, const D
   return true;
 }
 
+// An empty sequence attends to nothing: its output rows are zero, and its
+// segments need no merge. Done by one workgroup per sequence.
+template <int D>
+__device__ __forceinline__ void zero_empty(const DecodeArgs &a, int s, int w) {
+  if (s % a.num_wgs != w) return;
+  u32x4_t *row = reinterpret_cast<u32x4_t *>(a.out + (size_t)s * a.num_q_heads * D);
+  for (int i = 0; i < a.num_q_heads * D / 8; ++i) row[i] = u32x4_t{0, 0, 0, 0};
+  if (a.merge_desc)
+    for (int hg = 0; hg < a.num_head_groups; ++hg) a.merge_desc[(size_t)s * a.num_head_groups + hg] = int2{-1, -1};
+}
+
 template <int D>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const int32_t *__restrict__ lens) {
@@ -439,7 +482,7 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
   static_assert(NJ >= 1 && D % 32 == 0, "head_size must be a multiple of 32");
   extern __shared__ __align__(16) uint16_t q_lds[];  // heads_per_wg * 2 * group * D
   __shared__ long long red[8];
-  __shared__ int found_seq;
+  __shared__ int found_seq, found_n;
   __shared__ long long found_prefix;
 
   const int tid = threadIdx.x;
@@ -452,55 +495,62 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
   const int cap = a.max_blocks_per_seq * kBlock;
   const long long W = a.num_wgs;
 
-  // Pass 1: total units; zero rows (and "no merge" records) for empty sequences.
-  long long mine = 0;
-  for (int s = tid; s < S; s += nthr) {
-    const int n = clamp_len(lens[s], cap);
-    mine += (n + kBlock - 1) / kBlock;
-    if (n == 0 && s % a.num_wgs == w) {
-      u32x4_t *row = reinterpret_cast<u32x4_t *>(a.out + (size_t)s * a.num_q_heads * D);
-      for (int i = 0; i < a.num_q_heads * D / 8; ++i) row[i] = u32x4_t{0, 0, 0, 0};
-      if (a.merge_desc)
-        for (int hg = 0; hg < NG; ++hg) a.merge_desc[(size_t)s * NG + hg] = int2{-1, -1};
-    }
-  }
-  const long long U = wg_sum(mine, red, wave, lane, nthr >> 6) * NG;
-  const long long E = U < W ? U : W;  // workgroups that get units
-  if (w >= E) return;
-  const long long lo = range_lo(w, U, E);
-  const long long hi = range_lo(w + 1, U, E);
-
-  // Pass 2: the sequence whose units hold `lo` (block scan over the lengths).
-  if (tid == 0) found_seq = -1;
-  long long before = 0;  // blocks of all sequences preceding this chunk
-  for (int base = 0; base < S; base += nthr) {
-    const int s = base + tid;
-    const long long L = s < S ? (clamp_len(lens[s], cap) + kBlock - 1) / kBlock : 0;
-    long long incl = L;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const long long o = __shfl_up(incl, off);
-      if (lane >= off) incl += o;
-    }
-    __syncthreads();
-    if (lane == 63) red[wave] = incl;
-    __syncthreads();
-    long long pre = before;
-    long long chunk_total = 0;
-    for (int i = 0; i < (nthr >> 6); ++i) {
-      if (i < wave) pre += red[i];
-      chunk_total += red[i];
-    }
+  long long U, lo, hi, E;
+  if (S <= nthr) {
+    // One pass: every thread holds one sequence's block count; a block scan
+    // gives the total and every sequence's first unit at once.
+    const int n = tid < S ? clamp_len(lens[tid], cap) : 0;
+    if (tid < S && n == 0) zero_empty<D>(a, tid, w);
+    const long long L = (n + kBlock - 1) / kBlock;
+    long long pre, total;
+    const long long incl = wg_scan(L, red, wave, lane, nthr >> 6, pre, total);
+    U = total * NG;
+    E = U < W ? U : W;  // workgroups that get units
+    if (w >= E) return;
+    lo = range_lo(w, U, E);
+    hi = range_lo(w + 1, U, E);
     const long long excl = pre + incl - L;
     if (L > 0 && excl * NG <= lo && lo < (excl + L) * NG) {
-      found_seq = s;
+      found_seq = tid;
       found_prefix = excl;
+      found_n = n;
     }
     __syncthreads();
-    if (found_seq >= 0) break;
-    before += chunk_total;
+  } else {
+    // Pass 1: total units; zero the rows of empty sequences.
+    long long mine = 0;
+    for (int s = tid; s < S; s += nthr) {
+      const int n = clamp_len(lens[s], cap);
+      mine += (n + kBlock - 1) / kBlock;
+      if (n == 0) zero_empty<D>(a, s, w);
+    }
+    U = wg_sum(mine, red, wave, lane, nthr >> 6) * NG;
+    E = U < W ? U : W;
+    if (w >= E) return;
+    lo = range_lo(w, U, E);
+    hi = range_lo(w + 1, U, E);
+
+    // Pass 2: the sequence whose units hold `lo` (block scan over the lengths).
+    if (tid == 0) found_seq = -1;
+    long long before = 0;  // blocks of all sequences preceding this chunk
+    for (int base = 0; base < S; base += nthr) {
+      const int s = base + tid;
+      const int n = s < S ? clamp_len(lens[s], cap) : 0;
+      const long long L = (n + kBlock - 1) / kBlock;
+      long long pre, chunk_total;
+      const long long incl = wg_scan(L, red, wave, lane, nthr >> 6, pre, chunk_total);
+      const long long excl = before + pre + incl - L;
+      if (L > 0 && excl * NG <= lo && lo < (excl + L) * NG) {
+        found_seq = s;
+        found_prefix = excl;
+        found_n = n;
+      }
+      __syncthreads();
+      if (found_seq >= 0) break;
+      before += chunk_total;
+    }
+    if (found_seq < 0) return;  // only if the lengths changed during the call
   }
-  if (found_seq < 0) return;  // only if the lengths changed during the call
 
   Walker wk;
   wk.lens = lens;
@@ -511,7 +561,7 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
   wk.hi = hi;
   wk.seg_base = found_prefix * NG;
   wk.s = __builtin_amdgcn_readfirstlane(found_seq);
-  wk.n = clamp_len(lens[wk.s], cap);
+  wk.n = __builtin_amdgcn_readfirstlane(found_n);
   wk.L = (wk.n + kBlock - 1) / kBlock;
   wk.hg = (int)((lo - wk.seg_base) / wk.L);
   wk.off = (int)((lo - wk.seg_base) % wk.L);
@@ -532,6 +582,7 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
   ln.head_ok = ln.c < a.group;
   ln.crow = ln.head_ok ? ln.c : a.group - 1;
   ln.blk_stride = (size_t)a.num_kv_heads * D * kBlock;
+  ln.row_bytes = a.num_kv_heads * D * (int)sizeof(uint16_t);
   ln.lane_off = (uint32_t)(((size_t)ln.c * a.num_kv_heads * D + ln.grp * 8) * sizeof(uint16_t));
   ln.q_off = (uint32_t)((ln.crow * D + ln.grp * 8) * sizeof(uint16_t));
   ln.U = U;
@@ -562,7 +613,7 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
 #pragma unroll
   for (int t = 0; t < 2 * NJ; ++t) st.acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   u32x4_t KA[NJ], VA[NJ], KB[NJ], VB[NJ];
-  issue<NJ>(a, ln, block_id(tables, a, ln.pool32, st.P.s, st.P.off), st.hoff, KA, VA);
+  issue<NJ>(a, ln, block_id(tables, a, ln.pool32, st.P.s, st.P.off), st.hoff, rows_in(st.P.n, st.P.off), KA, VA);
   while (step<NJ>(tables, a, ln, wk, st, KA, VA, KB, VB, q_lds) &&
          step<NJ>(tables, a, ln, wk, st, KB, VB, KA, VA, q_lds)) {
   }
