@@ -107,7 +107,7 @@ typedef struct pa_kv_cache {
  *                 results (running max, sum, unnormalised output) that a
  *                 second kernel merges with log-sum-exp weights. The
  *                 workspace holds those partials and one merge record per
- *                 (sequence, group of up to 8 KV heads). It needs no
+ *                 workgroup. It needs no
  *                 initialisation: every call rewrites what it reads. Calls
  *                 that share a workspace must not overlap in time (keep them
  *                 on one stream, or order them). With NULL the library

@@ -324,8 +324,10 @@ __device__ __forceinline__ int rows_in(int n, int b) {
 }
 
 // Writes P's result: bf16 output when P is a whole segment, otherwise its
-// partial record; the workgroup holding a segment's last unit records the
-// segment's pieces for the merge.
+// partial record. A workgroup's first piece is the only one that can end a
+// segment begun in an earlier workgroup, so each workgroup writes one merge
+// record, when its first piece ends: that segment and where its pieces are,
+// or none.
 template <int NJ>
 __device__ __forceinline__ void finish_piece(const DecodeArgs &a, const Lane &ln, Stream<NJ> &st) {
   constexpr int D = NJ * 32;
@@ -347,14 +349,14 @@ __device__ __forceinline__ void finish_piece(const DecodeArgs &a, const Lane &ln
       if (ln.grp == 0) *reinterpret_cast<f32x2_t *>(a.part_ml + row * 2) = f32x2_t{st.m_run, l};
     }
   }
-  if (P.off + P.cnt == P.L && ln.tid == 0 && a.merge_desc) {
+  if (P.first && ln.tid == 0 && a.merge_desc) {
     int2 d = {-1, -1};
-    if (!whole) {  // the segment began in an earlier workgroup: record its pieces
+    if (!whole && P.off + P.cnt == P.L) {  // ends a segment begun in an earlier workgroup
       const int w0 = owner_of(P.seg_start, ln.U, ln.E);
       const int slot0 = range_lo(w0, ln.U, ln.E) < P.seg_start ? 1 : 0;
-      d = int2{w0 * 2 + slot0, ln.w};
+      d = int2{P.s * ln.NG + P.hg, w0 * 2 + slot0};
     }
-    a.merge_desc[(size_t)P.s * ln.NG + P.hg] = d;
+    a.merge_desc[ln.w] = d;
   }
 }
 
@@ -464,15 +466,18 @@ __device__ __forceinline__ bool step(const int32_t *__restrict__ tables, const D
   return true;
 }
 
-// An empty sequence attends to nothing: its output rows are zero, and its
-// segments need no merge. Done by one workgroup per sequence.
+// An empty sequence attends to nothing: its output rows are zero. Done by one
+// workgroup per sequence.
 template <int D>
 __device__ __forceinline__ void zero_empty(const DecodeArgs &a, int s, int w) {
   if (s % a.num_wgs != w) return;
   u32x4_t *row = reinterpret_cast<u32x4_t *>(a.out + (size_t)s * a.num_q_heads * D);
   for (int i = 0; i < a.num_q_heads * D / 8; ++i) row[i] = u32x4_t{0, 0, 0, 0};
-  if (a.merge_desc)
-    for (int hg = 0; hg < a.num_head_groups; ++hg) a.merge_desc[(size_t)s * a.num_head_groups + hg] = int2{-1, -1};
+}
+
+// Workgroups past the ones that get units have no merge record to write.
+__device__ __forceinline__ void no_merge(const DecodeArgs &a, int w, int tid) {
+  if (tid == 0 && a.merge_desc) a.merge_desc[w] = int2{-1, -1};
 }
 
 template <int D>
@@ -506,7 +511,10 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
     const long long incl = wg_scan(L, red, wave, lane, nthr >> 6, pre, total);
     U = total * NG;
     E = U < W ? U : W;  // workgroups that get units
-    if (w >= E) return;
+    if (w >= E) {
+      no_merge(a, w, tid);
+      return;
+    }
     lo = range_lo(w, U, E);
     hi = range_lo(w + 1, U, E);
     const long long excl = pre + incl - L;
@@ -526,7 +534,10 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
     }
     U = wg_sum(mine, red, wave, lane, nthr >> 6) * NG;
     E = U < W ? U : W;
-    if (w >= E) return;
+    if (w >= E) {
+      no_merge(a, w, tid);
+      return;
+    }
     lo = range_lo(w, U, E);
     hi = range_lo(w + 1, U, E);
 
@@ -620,44 +631,45 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
 }
 
 // Log-sum-exp merge of the pieces of segments cut by workgroup boundaries.
-// Grid: (num_seqs * num_head_groups, heads_per_wg); one wavefront per query
-// head of the group; lane i owns head dims [i*D/64, (i+1)*D/64).
+// Grid: (num_wgs, heads_per_wg): block (w, k) merges KV head k of the
+// segment that workgroup w's first piece ended, if any. One wavefront per
+// query head of the group; lane i owns head dims [i*D/64, (i+1)*D/64). The
+// pieces are read in one pass with a running rescale, so their loads are
+// all in flight together.
 template <int D>
 __global__ __launch_bounds__(1024) void merge_kernel(const DecodeArgs a) {
   constexpr int PL = D / 64;  // dims per lane: 1 or 2
-  const int seg = blockIdx.x;
-  const int2 d = a.merge_desc[seg];
+  const int w1 = blockIdx.x;
+  const int2 d = a.merge_desc[w1];
   if (d.x < 0) return;
   const int lane = threadIdx.x & 63;
   const int c = threadIdx.x >> 6;            // query head within the KV head's group
   const int wave = blockIdx.y;               // KV head within the head group
-  const int s = seg / a.num_head_groups;
-  const int hg = seg - s * a.num_head_groups;
+  const int s = d.x / a.num_head_groups;
+  const int hg = d.x - s * a.num_head_groups;
   const int g = hg * a.heads_per_wg + wave;
-  const int w0 = d.x >> 1, w1 = d.y;
+  const int w0 = d.y >> 1;
   const int HG = a.heads_per_wg;
 
-  auto rec_row = [&](int w) -> size_t {
-    const int rec = w == w0 ? d.x : 2 * w;
-    return ((size_t)rec * HG + wave) * a.group + c;
-  };
-  // Pieces: slot d.x & 1 of workgroup w0, then the first slot of every
+  // Pieces: slot d.y & 1 of workgroup w0, then the first slot of every
   // workgroup up to w1 (whose ranges all lie inside the segment).
-  float M = -INFINITY;
-  for (int w = w0; w <= w1; ++w) M = fmaxf(M, a.part_ml[rec_row(w) * 2]);
-  float Lsum = 0.f;
+  float M = -INFINITY, Lsum = 0.f;
   float o[PL];
 #pragma unroll
   for (int i = 0; i < PL; ++i) o[i] = 0.f;
-#pragma unroll 4
   for (int w = w0; w <= w1; ++w) {
-    const size_t r = rec_row(w);
+    const int rec = w == w0 ? d.y : 2 * w;
+    const size_t r = ((size_t)rec * HG + wave) * a.group + c;
     const f32x2_t ml = *reinterpret_cast<const f32x2_t *>(a.part_ml + r * 2);
-    const float wt = fast_exp2(ml[0] - M);
-    Lsum += wt * ml[1];
-    const float *po = a.part_o + r * D + lane * PL;
+    float po[PL];
 #pragma unroll
-    for (int i = 0; i < PL; ++i) o[i] += wt * po[i];
+    for (int i = 0; i < PL; ++i) po[i] = a.part_o[r * D + lane * PL + i];
+    const float Mn = fmaxf(M, ml[0]);
+    const float so = fast_exp2(M - Mn), wt = fast_exp2(ml[0] - Mn);
+    Lsum = Lsum * so + wt * ml[1];
+#pragma unroll
+    for (int i = 0; i < PL; ++i) o[i] = o[i] * so + wt * po[i];
+    M = Mn;
   }
   const float inv = 1.f / Lsum;
   uint16_t *dst = a.out + ((size_t)s * a.num_q_heads + (size_t)g * a.group + c) * D + lane * PL;
@@ -683,8 +695,7 @@ hipError_t launch_decode(const DecodeArgs &args, int32_t head_size, hipStream_t 
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || args.num_wgs <= 1) return err;
-  const dim3 mgrid((unsigned)args.num_seqs * (unsigned)args.num_head_groups,
-                   (unsigned)args.heads_per_wg);
+  const dim3 mgrid((unsigned)args.num_wgs, (unsigned)args.heads_per_wg);
   const dim3 mblock(64 * (unsigned)args.group);
   if (head_size == 128) {
     hipLaunchKernelGGL(merge_kernel<128>, mgrid, mblock, 0, stream, args);

@@ -107,7 +107,7 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
   if (p.num_wgs <= 1) return p;
   const size_t group = (size_t)(num_q_heads / num_kv_heads);
   const size_t rows = (size_t)p.num_wgs * 2 * p.heads_per_wg * group;
-  p.desc_bytes = round_up((size_t)num_seqs * p.num_head_groups * sizeof(int2), 256);
+  p.desc_bytes = round_up((size_t)p.num_wgs * sizeof(int2), 256);
   p.ml_bytes = round_up(rows * 2 * sizeof(float), 256);
   p.o_bytes = round_up(rows * head_size * sizeof(float), 256);
   p.total_bytes = p.desc_bytes + p.ml_bytes + p.o_bytes;

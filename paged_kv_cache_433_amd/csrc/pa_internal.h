@@ -16,7 +16,7 @@ struct DecodeArgs {
   const int32_t *block_tables;   // [S, MB]
   const int32_t *context_lens;   // [S]
   uint16_t *out;                 // bf16 [S, Hq, D]
-  int2 *merge_desc;              // [S * num_head_groups]: pieces of cut segments
+  int2 *merge_desc;              // [num_wgs]: segment ended by the workgroup's first piece, or -1
   float *part_ml;                // [2 * num_wgs, heads_per_wg, group, 2]: max (base 2), sum
   float *part_o;                 // [2 * num_wgs, heads_per_wg, group, D]: unnormalised output
   int64_t num_blocks;

@@ -80,9 +80,9 @@ def test_workspace_size_and_check(L, monkeypatch):
     hg, ng, grp = 4, 2, 4             # heads per workgroup, head groups, query heads per KV head
 
     def need_at_least(S, wgs):
-        # a merge record per (sequence, head group); two partial records
-        # (max, sum, 128 floats) per workgroup, KV head of the group and query head
-        return S * ng * 8 + wgs * 2 * hg * grp * (128 + 2) * 4
+        # a merge record per workgroup; two partial records (max, sum, 128
+        # floats) per workgroup, KV head of the group and query head
+        return wgs * 8 + wgs * 2 * hg * grp * (128 + 2) * 4
 
     # one sequence of one block: at most one unit per head group; two groups
     # give two workgroups at most, so partials are still possible
