@@ -9,9 +9,11 @@ and 8 KV heads, head size 128, 16-token blocks, context lengths lognormal
 blocks.
 
 Prints one JSON line. ``value`` is algorithmic bytes per step / time per
-step (GB/s). ``roofline`` covers the decode kernel: its algorithmic bytes
-per launch / its mean launch time from HIP events on the launch stream,
-against 8 TB/s. ``cpu_baseline`` times the float64 oracle on a bounded
+step (GB/s). ``roofline`` covers the decode call (the decode kernel and the
+merge of cut pieces that follows it on the same stream): its algorithmic
+bytes / its mean time from HIP events around the call on the launch stream,
+against 8 TB/s; ``traffic`` is the call's HBM bytes from rocprofv3 counters
+(profiles/decode_traffic.json) when they were taken on the current kernel. ``cpu_baseline`` times the float64 oracle on a bounded
 sample of the same workload on this host.
 
     python bench.py [--gpus 1] [--steps 500] [--warmup 20] [--config NAME]
@@ -51,6 +53,67 @@ def measured_traffic(workload: str):
     if not rec or rec.get("decode_hip_sha256_16") != source_digest():
         return None
     return rec.get("bytes_per_launch")
+
+
+def _counter_means(path: str, counter: str) -> dict:
+    """Mean value of `counter` per kernel name in a rocprofv3 counter CSV."""
+    import csv
+
+    sums, counts = {}, {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] != counter:
+                continue
+            name = row["Kernel_Name"]
+            sums[name] = sums.get(name, 0.0) + float(row["Counter_Value"])
+            counts[name] = counts.get(name, 0) + 1
+    return {k: sums[k] / counts[k] for k in sums}
+
+
+def _one(means: dict, fragment: str) -> float:
+    hits = [v for k, v in means.items() if fragment in k]
+    if len(hits) != 1:
+        raise SystemExit(f"expected one kernel matching {fragment!r}, found {len(hits)}")
+    return hits[0]
+
+
+def record_traffic(prefix: str, workload: str, copy_bytes: int) -> int:
+    """Write the decode call's per-launch HBM bytes into profiles/decode_traffic.json.
+
+    Reads four rocprofv3 --pmc runs: {prefix}_fetch_decode and
+    {prefix}_write_decode (this bench on `workload`, counters FETCH_SIZE and
+    WRITE_SIZE), {prefix}_fetch_copy and {prefix}_write_copy (--probe-copy of
+    `copy_bytes` bytes). Each counter is scaled by what it reads for the copy,
+    which moves exactly `copy_bytes` each way, so the units need not be known.
+    """
+    def means(kind, counter):
+        return _counter_means(f"{prefix}_{kind}/run_counter_collection.csv", counter)
+
+    fetch_copy = _one(means("fetch_copy", "FETCH_SIZE"), "probe_copy")
+    write_copy = _one(means("write_copy", "WRITE_SIZE"), "probe_copy")
+    fd, wd = means("fetch_decode", "FETCH_SIZE"), means("write_decode", "WRITE_SIZE")
+    f_scale, w_scale = copy_bytes / fetch_copy, copy_bytes / write_copy
+    per = {}
+    for frag in ("decode_kernel", "merge_kernel"):
+        per[frag] = {"fetch_bytes": int(_one(fd, frag) * f_scale), "write_bytes": int(_one(wd, frag) * w_scale)}
+    total = sum(v["fetch_bytes"] + v["write_bytes"] for v in per.values())
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        data = {}
+    data[workload] = {
+        "decode_hip_sha256_16": source_digest(),
+        "bytes_per_launch": total,
+        "kernels": per,
+        "calibration": {"copy_bytes": copy_bytes, "fetch_size_per_copy": fetch_copy,
+                        "write_size_per_copy": write_copy},
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(data[workload]))
+    return 0
 
 
 def cpu_baseline(batch, seconds: float):
@@ -130,7 +193,12 @@ def main(argv=None) -> int:
     ap.add_argument("--probe-copy", type=int, default=0, metavar="BYTES",
                     help="instead of the decode step: time a plain 16-byte copy of BYTES bytes "
                          "(the reference kernel that calibrates rocprofv3 byte counters)")
+    ap.add_argument("--record-traffic", metavar="PREFIX",
+                    help="no GPU work: turn the rocprofv3 --pmc runs PREFIX_{fetch,write}_{decode,copy} "
+                         "into the traffic record for --config (copy size from --probe-copy)")
     args = ap.parse_args(argv)
+    if args.record_traffic:
+        return record_traffic(args.record_traffic, args.config, args.probe_copy or (1 << 30))
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -236,7 +304,7 @@ def main(argv=None) -> int:
         "seq_steps_per_s": round(b.num_seqs / (ms * 1e-3), 1),
         "bytes_per_step": int(step_bytes),
         "roofline": {
-            "kernel": "decode",
+            "kernel": "decode call: decode_kernel + merge_kernel",
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": PEAK_HBM_GBS,

@@ -634,8 +634,7 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
 // Grid: (num_wgs, heads_per_wg): block (w, k) merges KV head k of the
 // segment that workgroup w's first piece ended, if any. One wavefront per
 // query head of the group; lane i owns head dims [i*D/64, (i+1)*D/64). The
-// pieces are read in one pass with a running rescale, so their loads are
-// all in flight together.
+// pieces are read in one pass with a running rescale.
 template <int D>
 __global__ __launch_bounds__(1024) void merge_kernel(const DecodeArgs a) {
   constexpr int PL = D / 64;  // dims per lane: 1 or 2
@@ -652,23 +651,45 @@ __global__ __launch_bounds__(1024) void merge_kernel(const DecodeArgs a) {
   const int HG = a.heads_per_wg;
 
   // Pieces: slot d.y & 1 of workgroup w0, then the first slot of every
-  // workgroup up to w1 (whose ranges all lie inside the segment).
+  // workgroup up to w1 (whose ranges all lie inside the segment). Four at a
+  // time: their loads are issued together, then folded in.
+  constexpr int kPieces = 4;
   float M = -INFINITY, Lsum = 0.f;
   float o[PL];
 #pragma unroll
   for (int i = 0; i < PL; ++i) o[i] = 0.f;
-  for (int w = w0; w <= w1; ++w) {
-    const int rec = w == w0 ? d.y : 2 * w;
-    const size_t r = ((size_t)rec * HG + wave) * a.group + c;
-    const f32x2_t ml = *reinterpret_cast<const f32x2_t *>(a.part_ml + r * 2);
-    float po[PL];
+  for (int w = w0; w <= w1; w += kPieces) {
+    float pm[kPieces], pl[kPieces], po[kPieces][PL];
 #pragma unroll
-    for (int i = 0; i < PL; ++i) po[i] = a.part_o[r * D + lane * PL + i];
-    const float Mn = fmaxf(M, ml[0]);
-    const float so = fast_exp2(M - Mn), wt = fast_exp2(ml[0] - Mn);
-    Lsum = Lsum * so + wt * ml[1];
+    for (int k = 0; k < kPieces; ++k) {
+      pm[k] = -INFINITY;
+      pl[k] = 0.f;
 #pragma unroll
-    for (int i = 0; i < PL; ++i) o[i] = o[i] * so + wt * po[i];
+      for (int i = 0; i < PL; ++i) po[k][i] = 0.f;
+      if (w + k <= w1) {
+        const int rec = w + k == w0 ? d.y : 2 * (w + k);
+        const size_t r = ((size_t)rec * HG + wave) * a.group + c;
+        const f32x2_t ml = *reinterpret_cast<const f32x2_t *>(a.part_ml + r * 2);
+        pm[k] = ml[0];
+        pl[k] = ml[1];
+#pragma unroll
+        for (int i = 0; i < PL; ++i) po[k][i] = a.part_o[r * D + lane * PL + i];
+      }
+    }
+    float Mn = M;
+#pragma unroll
+    for (int k = 0; k < kPieces; ++k) Mn = fmaxf(Mn, pm[k]);
+    const float so = fast_exp2(M - Mn);
+    Lsum *= so;
+#pragma unroll
+    for (int i = 0; i < PL; ++i) o[i] *= so;
+#pragma unroll
+    for (int k = 0; k < kPieces; ++k) {
+      const float wt = fast_exp2(pm[k] - Mn);  // 0 for the padding (max -inf)
+      Lsum += wt * pl[k];
+#pragma unroll
+      for (int i = 0; i < PL; ++i) o[i] += wt * po[k][i];
+    }
     M = Mn;
   }
   const float inv = 1.f / Lsum;
