@@ -13,7 +13,9 @@ step (GB/s). ``roofline`` covers the decode call (the decode kernel and the
 merge of cut pieces that follows it on the same stream): its algorithmic
 bytes / its mean time from HIP events around the call on the launch stream,
 against 8 TB/s; ``traffic`` is the call's HBM bytes from rocprofv3 counters
-(profiles/decode_traffic.json) when they were taken on the current kernel. ``cpu_baseline`` times the float64 oracle on a bounded
+(profiles/decode_traffic.json) when they were taken on the current kernel;
+``mean_launch_us_mall_evicted`` repeats the call with the 256 MB memory-side
+cache evicted before each launch (a 2 GiB read scan outside the events). ``cpu_baseline`` times the float64 oracle on a bounded
 sample of the same workload on this host.
 
     python bench.py [--gpus 1] [--steps 500] [--warmup 20] [--config NAME]
@@ -35,6 +37,10 @@ METRIC = "paged decode attention: achieved KV HBM GB/s (% of peak) and seq-steps
 PEAK_HBM_GBS = 8000.0
 DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_433_amd", "csrc", "decode.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+CACHE_NOTES = {
+    "tiny_mha": "warm: the whole cache fits in L2",
+    "beam_cow": "warm in part: the 4 beams of a prompt read its shared blocks, so some logical bytes come from cache",
+}
 
 
 def source_digest(path=DECODE_SRC) -> str:
@@ -116,23 +122,15 @@ def record_traffic(prefix: str, workload: str, copy_bytes: int) -> int:
     return 0
 
 
-def cpu_baseline(batch, seconds: float):
-    """Time the float64 oracle on whole sequences, in a seeded order (cycling
-    through the batch), until `seconds` of work; rate in the metric's unit
-    (algorithmic GB/s)."""
-    import numpy as np
+def _time_oracle(batch, kc, vc, order, seconds: float, threads: int):
+    """Run the oracle on whole sequences of `order` (cycling) for `seconds`
+    with BLAS limited to `threads`; returns (sequences done, seconds)."""
     from threadpoolctl import threadpool_limits
 
     import oracle
-    from paged_kv_cache_433_amd import workloads as W
 
-    kc, vc = batch.k_cache, batch.v_cache  # updated in place; the device copies exist already
-    if len(batch.cow_pairs):
-        oracle.copy_blocks(kc, vc, batch.cow_pairs)
-    oracle.reshape_and_cache(kc, vc, batch.new_k, batch.new_v, batch.slot_mapping)
-    order = np.random.default_rng(0).permutation(batch.num_seqs)
     done = []
-    with threadpool_limits(limits=1):
+    with threadpool_limits(limits=threads):
         t0 = time.perf_counter()
         while time.perf_counter() - t0 < seconds:
             for s in order:
@@ -142,17 +140,47 @@ def cpu_baseline(batch, seconds: float):
                 if time.perf_counter() - t0 >= seconds:
                     break
         dt = time.perf_counter() - t0
-    lens = batch.context_lens[done]
-    nbytes = W.algorithmic_bytes(lens, batch.num_q_heads, batch.num_kv_heads, batch.head_size)
+    return done, dt
+
+
+def cpu_baseline(batch, seconds: float):
+    """Time the float64 oracle on whole sequences, in a seeded order (cycling
+    through the batch), for `seconds` with BLAS on every core this process may
+    use and again on one thread; rate in the metric's unit (algorithmic GB/s).
+    The multi-core run is the reported value."""
+    import numpy as np
+
+    import oracle
+    from paged_kv_cache_433_amd import workloads as W
+
+    kc, vc = batch.k_cache, batch.v_cache  # updated in place; the device copies exist already
+    if len(batch.cow_pairs):
+        oracle.copy_blocks(kc, vc, batch.cow_pairs)
+    oracle.reshape_and_cache(kc, vc, batch.new_k, batch.new_v, batch.slot_mapping)
+    order = np.random.default_rng(0).permutation(batch.num_seqs)
+    # The host share this process may use: its CPU affinity, capped by the
+    # thread count the environment sets for OpenMP/BLAS.
+    cores = len(os.sched_getaffinity(0))
+    if os.environ.get("OMP_NUM_THREADS", "").isdigit():
+        cores = max(1, min(cores, int(os.environ["OMP_NUM_THREADS"])))
+    res = {}
+    for threads in (cores, 1):
+        done, dt = _time_oracle(batch, kc, vc, order, seconds, threads)
+        lens = batch.context_lens[done]
+        nbytes = W.algorithmic_bytes(lens, batch.num_q_heads, batch.num_kv_heads, batch.head_size)
+        res[threads] = (len(done), int(lens.sum()), dt, nbytes / dt / 1e9, len(done) / dt)
+    n, tokens, dt, gbps, sps = res[cores]
     return {
-        "value": round(nbytes / dt / 1e9, 4),
+        "value": round(gbps, 4),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": cores,
         "kind": "oracle",
-        "sample": (f"{len(done)} sequence-steps of the {batch.num_seqs}-sequence batch, taken in a "
-                   f"seeded order ({int(lens.sum())} tokens), float64 numpy oracle, BLAS limited "
-                   f"to 1 thread, {dt:.1f} s"),
-        "seq_steps_per_s": round(len(done) / dt, 3),
+        "sample": (f"{n} sequence-steps of the {batch.num_seqs}-sequence batch, taken in a seeded "
+                   f"order ({tokens} tokens), float64 numpy oracle, BLAS limited to {cores} threads "
+                   f"(the gather and exp are single-threaded numpy), {dt:.1f} s"),
+        "seq_steps_per_s": round(sps, 3),
+        "single_thread": {"value": round(res[1][3], 4), "unit": "GB/s", "seq_steps_per_s": round(res[1][4], 3),
+                          "sample": f"{res[1][0]} sequence-steps, {res[1][2]:.1f} s"},
     }
 
 
@@ -188,8 +216,11 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="llama3_8b_gqa")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="seconds of oracle work per CPU-baseline run (two runs: all cores, one thread)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-launches", type=int, default=100,
+                    help="extra decode calls timed with the MALL evicted before each (0: skip)")
     ap.add_argument("--probe-copy", type=int, default=0, metavar="BYTES",
                     help="instead of the decode step: time a plain 16-byte copy of BYTES bytes "
                          "(the reference kernel that calibrates rocprofv3 byte counters)")
@@ -270,6 +301,25 @@ def main(argv=None) -> int:
           f"(p10 {np.percentile(dec_ms, 10) * 1e3:.1f}, p90 {np.percentile(dec_ms, 90) * 1e3:.1f})",
           file=sys.stderr, flush=True)
 
+    # The same decode call again with the 256 MB MALL (memory-side cache)
+    # evicted before each launch by reading a 2 GiB buffer, outside the
+    # events: shows whether repeated calls on the same cache are served from
+    # it. A read scan leaves no dirty lines behind to be written back later.
+    cold_us = None
+    if args.cold_launches:
+        scratch = torch.ones(2 << 30, dtype=torch.uint8, device=dev)
+        sink = torch.empty(pa.probe_read_sink_bytes(), dtype=torch.uint8, device=dev)
+        cold = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(args.cold_launches)]
+        for a, z in cold:
+            pa.probe_read(scratch, sink)
+            a.record(stream)
+            pa.decode(q, kc, vc, tables, lens, scale, out=out)
+            z.record(stream)
+        torch.cuda.synchronize()
+        cold_us = float(np.mean([a.elapsed_time(z) for a, z in cold])) * 1e3
+        del scratch, sink
+
     value = step_bytes / (ms * 1e-3) / 1e9
     achieved = decode_bytes / (dec_mean * 1e-3) / 1e9
     traffic = measured_traffic(args.config)
@@ -299,6 +349,7 @@ def main(argv=None) -> int:
             "step": ("copy_blocks + " if pairs is not None else "")
                     + "reshape_and_cache + decode",
             "parallelism": "single GPU",
+            "cache": CACHE_NOTES.get(args.config, "cold: the K/V of a call is several times the 256 MB MALL"),
         },
         "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "seq_steps_per_s": round(b.num_seqs / (ms * 1e-3), 1),
@@ -313,11 +364,13 @@ def main(argv=None) -> int:
             "traffic": traffic,
             "algorithmic_bytes_per_launch": int(decode_bytes),
             "mean_launch_us": round(dec_mean * 1e3, 2),
+            "mean_launch_us_mall_evicted": round(cold_us, 2) if cold_us else None,
+            "achieved_mall_evicted": round(decode_bytes / cold_us / 1e3, 2) if cold_us else None,
         },
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        print(f"[bench] cpu baseline (~{args.cpu_seconds:.0f} s)", file=sys.stderr, flush=True)
+        print(f"[bench] cpu baseline (~{2 * args.cpu_seconds:.0f} s)", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(b, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
     return 0

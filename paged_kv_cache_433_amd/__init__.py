@@ -12,5 +12,6 @@ from .ops import (  # noqa: F401
     decode_workspace_bytes,
     probe_copy,
     probe_read,
+    probe_read_sink_bytes,
     reshape_and_cache,
 )

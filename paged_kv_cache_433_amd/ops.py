@@ -134,6 +134,11 @@ def probe_copy(dst: torch.Tensor, src: torch.Tensor) -> None:
     _check(_lib.lib().pa_probe_copy(_ptr(dst), _ptr(src), nbytes, _stream(src.device)))
 
 
+def probe_read_sink_bytes() -> int:
+    """Bytes of the sink buffer pa_probe_read folds its loads into."""
+    return int(_lib.lib().pa_probe_read_sink_bytes())
+
+
 def probe_read(src: torch.Tensor, sink: torch.Tensor = None) -> torch.Tensor:
     """Read all of ``src`` with 16-byte vector loads (measurement helper);
     returns the sink buffer the probe folds its loads into."""
