@@ -318,7 +318,7 @@ def config_lens(name: str, seed: int):
         return np.array([1, 17, 33, 100])
     if name == "llama2_7b":
         return r.integers(128, 2048, size=64, endpoint=True)
-    if name == "llama3_8b_gqa":
+    if name in ("llama3_8b_gqa", "llama3_8b_gqa_tp8"):
         return lognormal_lens(r, 256, 1024, 0.5, 16, 4096)
     if name == "long_splitk":
         return np.tile(np.array([32768, 65536, 98304, 131072]), 2)
@@ -334,6 +334,9 @@ CONFIG_SHAPES = {
     "llama3_8b_gqa": (32, 8, 128, 65536, 256, 3),
     "long_splitk": (64, 8, 128, 65536, 8192, 4),
     "long_splitk_max": (64, 8, 128, 65536, 8192, 4),
+    # One GPU's share of the GQA layer under 8-way tensor parallelism: the
+    # same sequences and lengths, 32/8 query heads on 8/8 KV heads.
+    "llama3_8b_gqa_tp8": (4, 1, 128, 65536, 256, 3),
 }
 
 

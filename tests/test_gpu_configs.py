@@ -16,10 +16,11 @@ from paged_kv_cache_433_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
 
-SAMPLE = {"llama2_7b": 24, "llama3_8b_gqa": 40, "long_splitk": 8}
+SAMPLE = {"llama2_7b": 24, "llama3_8b_gqa": 40, "long_splitk": 8, "long_splitk_max": 2, "llama3_8b_gqa_tp8": 40}
 
 
-@pytest.mark.parametrize("name", ["llama2_7b", "llama3_8b_gqa", "long_splitk"])
+@pytest.mark.parametrize("name", ["llama2_7b", "llama3_8b_gqa", "long_splitk", "long_splitk_max",
+                                  "llama3_8b_gqa_tp8"])
 def test_full_size_config(name):
     note(f"generate {name}")
     b = W.make_config(name)
