@@ -210,6 +210,54 @@ def probe_copy(nbytes: int, steps: int, warmup: int, dev) -> int:
     return 0
 
 
+def swap_probe(num_blocks: int, steps: int, dev) -> int:
+    """Time pa_swap_blocks of `num_blocks` scattered blocks of the GQA layer's
+    shape (8 KV heads of 128: 64 KiB of K and V per block) out to pinned host
+    memory and back in, against a DMA copy of the same bytes (torch's pinned
+    host <-> device copy of one contiguous buffer) as the link's reference."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_433_amd as pa
+
+    shape = (65536, 16, 8, 128)
+    kc = torch.zeros(shape, dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros_like(kc)
+    hk = torch.empty((num_blocks,) + shape[1:], dtype=torch.bfloat16, pin_memory=True)
+    hv = torch.empty_like(hk, pin_memory=True)
+    rng = np.random.default_rng(7)
+    out_pairs = torch.from_numpy(np.stack([rng.permutation(shape[0])[:num_blocks], np.arange(num_blocks)],
+                                          axis=1).astype(np.int64)).to(dev)
+    in_pairs = torch.from_numpy(np.stack([np.arange(num_blocks), rng.permutation(shape[0])[:num_blocks]],
+                                         axis=1).astype(np.int64)).to(dev)
+    nbytes = 2 * hk.numel() * hk.element_size()
+    stream = torch.cuda.current_stream(dev)
+    dbuf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    hbuf = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, z in evs:
+            a.record(stream)
+            fn()
+            z.record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(z) for a, z in evs])) * 1e3
+
+    t_out = timed(lambda: pa.swap_blocks(kc, vc, hk, hv, out_pairs, "out"))
+    t_in = timed(lambda: pa.swap_blocks(kc, vc, hk, hv, in_pairs, "in"))
+    t_d2h = timed(lambda: hbuf.copy_(dbuf, non_blocking=True))
+    t_h2d = timed(lambda: dbuf.copy_(hbuf, non_blocking=True))
+    print(json.dumps({"probe": "swap_blocks", "blocks": num_blocks, "bytes_per_direction": nbytes,
+                      "out_us": round(t_out, 1), "out_GBps": round(nbytes / t_out / 1e3, 2),
+                      "in_us": round(t_in, 1), "in_GBps": round(nbytes / t_in / 1e3, 2),
+                      "dma_d2h_GBps": round(nbytes / t_d2h / 1e3, 2),
+                      "dma_h2d_GBps": round(nbytes / t_h2d / 1e3, 2)}), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -224,6 +272,8 @@ def main(argv=None) -> int:
     ap.add_argument("--probe-copy", type=int, default=0, metavar="BYTES",
                     help="instead of the decode step: time a plain 16-byte copy of BYTES bytes "
                          "(the reference kernel that calibrates rocprofv3 byte counters)")
+    ap.add_argument("--swap-blocks", type=int, default=0, metavar="N",
+                    help="instead of the decode step: time swapping N blocks out to pinned host memory and in")
     ap.add_argument("--record-traffic", metavar="PREFIX",
                     help="no GPU work: turn the rocprofv3 --pmc runs PREFIX_{fetch,write}_{decode,copy} "
                          "into the traffic record for --config (copy size from --probe-copy)")
@@ -245,6 +295,8 @@ def main(argv=None) -> int:
     dev = torch.device("cuda:0")
     if args.probe_copy:
         return probe_copy(args.probe_copy, args.steps, args.warmup, dev)
+    if args.swap_blocks:
+        return swap_probe(args.swap_blocks, min(args.steps, 50), dev)
     print(f"[bench] generating {args.config}", file=sys.stderr, flush=True)
     # The beam-search workload's first step: its copy-on-write pairs, its
     # scatter and its decode are repeated every step (both are idempotent).

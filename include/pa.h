@@ -173,6 +173,40 @@ int pa_reshape_and_cache(const pa_kv_cache *cache, const void *k, const void *v,
 int pa_copy_blocks(const pa_kv_cache *cache, const int64_t *src_dst_pairs, int32_t num_pairs,
                    void *stream);
 
+/* Directions of pa_swap_blocks. */
+enum { PA_SWAP_OUT = 0, PA_SWAP_IN = 1 };
+
+/*
+ * pa_swap_blocks - move whole blocks between the device cache and a host
+ * cache, for preemption by swapping: a preempted request's KV blocks go to
+ * CPU RAM and come back when it resumes ("vLLM: Anatomy and Mechanisms of
+ * High-Throughput LLM Inference", section "Preemption and Recovery";
+ * "vLLM Internals", section "The Block Manager").
+ *
+ *   host_k, host_v   bf16 [host_num_blocks, 16, num_kv_heads, head_size],
+ *                    contiguous, in pinned host memory (hipHostMalloc, or
+ *                    a pinned torch tensor); owned by the caller, who
+ *                    guarantees host_num_blocks blocks of each. The library
+ *                    asks the HIP runtime for their device address and
+ *                    returns PA_ERR_UNSUPPORTED for memory it does not know
+ *                    as pinned host memory.
+ *   src_dst_pairs    int64 [num_pairs][2], device memory. PA_SWAP_OUT: host
+ *                    block dst becomes a bit copy of device block src;
+ *                    PA_SWAP_IN: device block dst becomes a bit copy of host
+ *                    block src. K and V both. Destinations must be distinct;
+ *                    a pair with an index outside its side's pool is
+ *                    skipped.
+ *   direction        PA_SWAP_OUT or PA_SWAP_IN
+ * Asynchronous on `stream`; the host array is complete (swap out) or may be
+ * reused (swap in) once the stream has reached the call. num_pairs == 0 is a
+ * no-op.
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE (num_pairs < 0, host_num_blocks < 0, bad
+ * direction), PA_ERR_UNSUPPORTED (see pa_kv_cache; host memory not pinned),
+ * PA_ERR_HIP.
+ */
+int pa_swap_blocks(const pa_kv_cache *cache, void *host_k, void *host_v, int64_t host_num_blocks,
+                   const int64_t *src_dst_pairs, int32_t num_pairs, int32_t direction, void *stream);
+
 /* Text of the last error on this thread ("" after a successful call). */
 const char *pa_last_error(void);
 

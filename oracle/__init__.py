@@ -1,4 +1,4 @@
-"""Plain, slow CPU oracle for paged decode attention and its two cache kernels.
+"""Plain, slow CPU oracle for paged decode attention and its cache kernels.
 
 TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import, call or run anything in this
@@ -6,19 +6,20 @@ package. The product path (``paged_kv_cache_433_amd``) never imports it and
 shares no code with it: the two meet only at the seeded input arrays.
 
 Every result is computed from its plain definition in float64 (attention) or
-as an exact bit copy (slot scatter, copy-on-write), citing the page passage it
-follows:
+as an exact bit copy (slot scatter, copy-on-write, swapping), citing the page
+passage it follows:
 
 * "vLLM: Anatomy and Mechanisms of High-Throughput LLM Inference", section
   "PagedAttention: The vLLM Innovation" / "Block-Level Management" (block
   tables map logical blocks to physical blocks; 16-token default block) and
   "Memory Sharing via Copy-on-Write (CoW)" (only the diverging block is
-  copied);
+  copied) and "Preemption and Recovery" (evicted KV blocks move to CPU RAM);
 * "Inside vLLM: Anatomy of a High-Throughput LLM Inference System", section
   "Scheduler" (a decode step runs over the most recent token with every
   earlier K/V vector already cached) and section "LLM Engine constructor"
   (per-block size 2 * block_size * num_kv_heads * head_size * dtype bytes);
-* "vLLM Internals", section "The Block Manager" (per-request block tables).
+* "vLLM Internals", section "The Block Manager" (per-request block tables;
+  a preempted request's blocks are swapped to CPU and back).
 
 Pins: every function here is checked in ``tests/test_oracle_pins.py``
 against facts the pages or mathematics fix (a library routine on the dense
@@ -32,4 +33,5 @@ from .paged_attention import (  # noqa: F401
     decode,
     decode_sequence,
     reshape_and_cache,
+    swap_blocks,
 )

@@ -135,3 +135,31 @@ def copy_blocks(k_cache, v_cache, src_dst_pairs) -> None:
     for i, d in enumerate(dst):
         k_cache[d] = k_src[i]
         v_cache[d] = v_src[i]
+
+
+def swap_blocks(dev_k, dev_v, host_k, host_v, src_dst_pairs, direction) -> None:
+    """Move whole blocks, K and V, between the device cache and a host cache.
+
+    A preempted request's KV blocks are moved to CPU RAM and brought back
+    when it is rescheduled ("vLLM: Anatomy and Mechanisms", section
+    "Preemption and Recovery"; "vLLM Internals", section "The Block
+    Manager"). ``direction`` "out": host block ``dst`` becomes a bit copy of
+    device block ``src``; "in": device block ``dst`` becomes a bit copy of
+    host block ``src``. The two sides are different arrays, so only the
+    destinations must be distinct.
+    """
+    pairs = np.asarray(src_dst_pairs, dtype=np.int64).reshape(-1, 2)
+    if len(pairs) == 0:
+        return
+    if direction == "out":
+        (fk, fv), (tk, tv) = (dev_k, dev_v), (host_k, host_v)
+    elif direction == "in":
+        (fk, fv), (tk, tv) = (host_k, host_v), (dev_k, dev_v)
+    else:
+        raise ValueError(direction)
+    src, dst = pairs[:, 0], pairs[:, 1]
+    assert np.all((src >= 0) & (src < fk.shape[0]) & (dst >= 0) & (dst < tk.shape[0]))
+    assert len(np.unique(dst)) == len(dst), "duplicate swap destination"
+    for s_, d_ in zip(src, dst):
+        tk[d_] = fk[s_]
+        tv[d_] = fv[s_]

@@ -1,6 +1,6 @@
 """MI355X (gfx950) paged KV-cache decode: HIP kernels behind a C ABI.
 
-``decode``, ``reshape_and_cache`` and ``copy_blocks`` call libpa.so (built
+``decode``, ``reshape_and_cache``, ``copy_blocks`` and ``swap_blocks`` call libpa.so (built
 with ``python -m paged_kv_cache_433_amd.build``); the library is loaded on
 first use and a missing build raises. ``workloads`` makes seeded inputs.
 """
@@ -14,4 +14,5 @@ from .ops import (  # noqa: F401
     probe_read,
     probe_read_sink_bytes,
     reshape_and_cache,
+    swap_blocks,
 )

@@ -16,10 +16,12 @@ PA_ERR_UNSUPPORTED = -3
 PA_ERR_WORKSPACE = -4
 PA_ERR_HIP = -5
 PA_DTYPE_BF16 = 0
+PA_SWAP_OUT = 0
+PA_SWAP_IN = 1
 
 # Every function include/pa.h declares.
 EXPORTS = ("pa_decode", "pa_decode_workspace_bytes", "pa_reshape_and_cache", "pa_copy_blocks",
-           "pa_last_error", "pa_probe_copy", "pa_probe_read", "pa_probe_read_sink_bytes")
+           "pa_swap_blocks", "pa_last_error", "pa_probe_copy", "pa_probe_read", "pa_probe_read_sink_bytes")
 
 
 class KVCacheDesc(ctypes.Structure):
@@ -52,6 +54,8 @@ def _declare(lib):
     lib.pa_reshape_and_cache.restype = ctypes.c_int
     lib.pa_copy_blocks.argtypes = [D, P, I32, P]
     lib.pa_copy_blocks.restype = ctypes.c_int
+    lib.pa_swap_blocks.argtypes = [D, P, P, I64, P, I32, I32, P]
+    lib.pa_swap_blocks.restype = ctypes.c_int
     lib.pa_last_error.argtypes = []
     lib.pa_last_error.restype = ctypes.c_char_p
     lib.pa_probe_copy.argtypes = [P, P, SZ, P]
@@ -60,7 +64,6 @@ def _declare(lib):
     lib.pa_probe_read.restype = ctypes.c_int
     lib.pa_probe_read_sink_bytes.argtypes = []
     lib.pa_probe_read_sink_bytes.restype = SZ
-    _ = I64
     return lib
 
 

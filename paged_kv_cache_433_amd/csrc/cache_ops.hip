@@ -61,6 +61,31 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(uint16_t *__restrict__
   for (int64_t i = lo + threadIdx.x; i < hi; i += blockDim.x) to[i] = from[i];
 }
 
+// Moves whole blocks between the device cache and a host cache in pinned
+// memory (swapping a preempted request's blocks out to host RAM and back:
+// "vLLM: Anatomy and Mechanisms of High-Throughput LLM Inference", section
+// "Preemption and Recovery"; "vLLM Internals", section "The Block Manager").
+// `from_*` and `to_*` are the two sides (device addresses of the host
+// arrays); grid = (pair, K/V, 32 KiB chunk of a block). A pair with an index
+// outside its side's pool is skipped. Over PCIe every workgroup keeps its
+// chunk's 16-byte loads in flight together.
+__global__ __launch_bounds__(256) void swap_blocks_kernel(const uint16_t *__restrict__ from_k,
+                                                          const uint16_t *__restrict__ from_v,
+                                                          int64_t from_blocks, uint16_t *__restrict__ to_k,
+                                                          uint16_t *__restrict__ to_v, int64_t to_blocks,
+                                                          const int64_t *__restrict__ pairs, int64_t block_elems,
+                                                          int32_t chunk_vecs) {
+  const int64_t src = pairs[2 * (size_t)blockIdx.x];
+  const int64_t dst = pairs[2 * (size_t)blockIdx.x + 1];
+  if (src < 0 || src >= from_blocks || dst < 0 || dst >= to_blocks) return;
+  const u32x4_t *from = reinterpret_cast<const u32x4_t *>((blockIdx.y ? from_v : from_k) + (size_t)src * block_elems);
+  u32x4_t *to = reinterpret_cast<u32x4_t *>((blockIdx.y ? to_v : to_k) + (size_t)dst * block_elems);
+  const int64_t vecs = block_elems / 8;
+  const int64_t lo = (int64_t)blockIdx.z * chunk_vecs;
+  const int64_t hi = lo + chunk_vecs < vecs ? lo + chunk_vecs : vecs;
+  for (int64_t i = lo + threadIdx.x; i < hi; i += blockDim.x) to[i] = from[i];
+}
+
 // Grid-stride 16-byte copy (measurement helper).
 __global__ __launch_bounds__(256) void probe_copy_kernel(u32x4_t *__restrict__ dst,
                                                          const u32x4_t *__restrict__ src,
@@ -100,6 +125,17 @@ hipError_t launch_copy_blocks(uint16_t *k_cache, uint16_t *v_cache, const int64_
   const unsigned chunks = (unsigned)((vecs + chunk - 1) / chunk);
   hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)num_pairs, 2, chunks), dim3(256), 0, stream,
                      k_cache, v_cache, pairs, block_elems, num_blocks, chunk);
+  return hipGetLastError();
+}
+
+hipError_t launch_swap_blocks(const uint16_t *from_k, const uint16_t *from_v, int64_t from_blocks, uint16_t *to_k,
+                              uint16_t *to_v, int64_t to_blocks, const int64_t *pairs, int32_t num_pairs,
+                              int64_t block_elems, hipStream_t stream) {
+  const int64_t vecs = block_elems / 8;
+  const int32_t chunk = 2048;  // 32 KiB of a block per workgroup
+  const unsigned chunks = (unsigned)((vecs + chunk - 1) / chunk);
+  hipLaunchKernelGGL(swap_blocks_kernel, dim3((unsigned)num_pairs, 2, chunks), dim3(256), 0, stream, from_k, from_v,
+                     from_blocks, to_k, to_v, to_blocks, pairs, block_elems, chunk);
   return hipGetLastError();
 }
 

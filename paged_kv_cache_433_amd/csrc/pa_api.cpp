@@ -223,6 +223,50 @@ int pa_copy_blocks(const pa_kv_cache *cache, const int64_t *src_dst_pairs, int32
   return ok();
 }
 
+// The device address of a host array, if the HIP runtime knows it as pinned
+// host memory that kernels may access; nullptr otherwise (so a pageable
+// pointer is an error here, never a fault in the kernel).
+static void *pinned_device_address(void *host) {
+  hipPointerAttribute_t attr{};
+  if (hipPointerGetAttributes(&attr, host) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (attr.type != hipMemoryTypeHost) return nullptr;
+  void *dev = nullptr;
+  if (hipHostGetDevicePointer(&dev, host, 0) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  return dev;
+}
+
+int pa_swap_blocks(const pa_kv_cache *cache, void *host_k, void *host_v, int64_t host_num_blocks,
+                   const int64_t *src_dst_pairs, int32_t num_pairs, int32_t direction, void *stream) {
+  int rc = check_cache(cache, num_pairs > 0);
+  if (rc != PA_OK) return rc;
+  if (num_pairs < 0) return fail(PA_ERR_SHAPE, "num_pairs < 0");
+  if (direction != PA_SWAP_OUT && direction != PA_SWAP_IN)
+    return fail(PA_ERR_SHAPE, "direction must be PA_SWAP_OUT or PA_SWAP_IN");
+  if (host_num_blocks < 0) return fail(PA_ERR_SHAPE, "host_num_blocks < 0");
+  if (num_pairs == 0) return ok();
+  if (!host_k || !host_v || !src_dst_pairs) return fail(PA_ERR_NULL, "host_k, host_v or src_dst_pairs is NULL");
+  uint16_t *hk = static_cast<uint16_t *>(pinned_device_address(host_k));
+  uint16_t *hv = static_cast<uint16_t *>(pinned_device_address(host_v));
+  if (!hk || !hv)
+    return fail(PA_ERR_UNSUPPORTED, "host_k and host_v must be pinned host memory (hipHostMalloc)");
+  const int64_t block_elems = (int64_t)cache->block_size * cache->num_kv_heads * cache->head_size;
+  uint16_t *dk = static_cast<uint16_t *>(cache->k_cache);
+  uint16_t *dv = static_cast<uint16_t *>(cache->v_cache);
+  hipError_t e = direction == PA_SWAP_OUT
+                     ? pa::launch_swap_blocks(dk, dv, cache->num_blocks, hk, hv, host_num_blocks, src_dst_pairs,
+                                              num_pairs, block_elems, static_cast<hipStream_t>(stream))
+                     : pa::launch_swap_blocks(hk, hv, host_num_blocks, dk, dv, cache->num_blocks, src_dst_pairs,
+                                              num_pairs, block_elems, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "swap_blocks launch");
+  return ok();
+}
+
 int pa_probe_copy(void *dst, const void *src, size_t bytes, void *stream) {
   if (bytes == 0) return ok();
   if (!dst || !src) return fail(PA_ERR_NULL, "dst or src is NULL");

@@ -55,6 +55,10 @@ hipError_t launch_copy_blocks(uint16_t *k_cache, uint16_t *v_cache, const int64_
                               int32_t num_pairs, int64_t block_elems, int64_t num_blocks,
                               hipStream_t stream);
 
+hipError_t launch_swap_blocks(const uint16_t *from_k, const uint16_t *from_v, int64_t from_blocks, uint16_t *to_k,
+                              uint16_t *to_v, int64_t to_blocks, const int64_t *pairs, int32_t num_pairs,
+                              int64_t block_elems, hipStream_t stream);
+
 hipError_t launch_probe_copy(void *dst, const void *src, size_t bytes, hipStream_t stream);
 
 // Workgroups of the read probe (256 threads each); its sink holds one

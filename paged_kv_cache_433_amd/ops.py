@@ -126,6 +126,28 @@ def copy_blocks(k_cache, v_cache, src_dst_pairs) -> None:
     _check(_lib.lib().pa_copy_blocks(ctypes.byref(desc), _ptr(src_dst_pairs), P, _stream(dev)))
 
 
+def swap_blocks(k_cache, v_cache, host_k, host_v, src_dst_pairs, direction: str) -> None:
+    """Move whole blocks between the device cache and a host cache.
+
+    ``host_k``/``host_v``: pinned CPU bf16 tensors ``[host_blocks, 16,
+    num_kv_heads, head_size]``. ``src_dst_pairs``: int64 ``[P, 2]`` on the
+    cache's device. ``direction`` "out": host block dst <- device block src;
+    "in": device block dst <- host block src. Asynchronous on the current
+    stream (synchronize before reading swapped-out blocks on the host).
+    """
+    desc = _cache_desc(k_cache, v_cache)
+    dev = k_cache.device
+    shape = (host_k.shape[0],) + tuple(k_cache.shape[1:])
+    for name, t in (("host_k", host_k), ("host_v", host_v)):
+        if t.dtype != _BF16 or tuple(t.shape) != shape or not t.is_contiguous() or t.is_cuda or not t.is_pinned():
+            raise ValueError(f"{name}: expected a contiguous pinned CPU bf16 tensor {shape}")
+    P = src_dst_pairs.shape[0]
+    _need(src_dst_pairs, "src_dst_pairs", torch.int64, (P, 2), dev)
+    d = {"out": _lib.PA_SWAP_OUT, "in": _lib.PA_SWAP_IN}[direction]
+    _check(_lib.lib().pa_swap_blocks(ctypes.byref(desc), _ptr(host_k), _ptr(host_v), shape[0],
+                                     _ptr(src_dst_pairs), P, d, _stream(dev)))
+
+
 def probe_copy(dst: torch.Tensor, src: torch.Tensor) -> None:
     """Plain 16-byte-vector copy of ``src`` into ``dst`` (measurement helper)."""
     nbytes = src.numel() * src.element_size()

@@ -281,6 +281,35 @@ def pin_copy_blocks(orc):
     assert np.array_equal(k3, kc) and np.array_equal(v3, vc)
 
 
+def pin_swap_blocks(orc):
+    """Swapping moves whole blocks, K into K and V into V, between the two
+    caches in the direction asked; a block swapped out and back in to
+    another slot comes back bit for bit; nothing else changes."""
+    rng = np.random.default_rng(31)
+    nd, nh = 20, 12
+    dk = rng.integers(0, 2**16, size=(nd, 16, 2, 8), dtype=np.uint16)
+    dv = rng.integers(0, 2**16, size=(nd, 16, 2, 8), dtype=np.uint16)
+    hk = rng.integers(0, 2**16, size=(nh, 16, 2, 8), dtype=np.uint16)
+    hv = rng.integers(0, 2**16, size=(nh, 16, 2, 8), dtype=np.uint16)
+    dk0, dv0, hk0, hv0 = dk.copy(), dv.copy(), hk.copy(), hv.copy()
+    out_pairs = np.array([[4, 0], [19, 11], [4, 5]], dtype=np.int64)   # device src -> host dst
+    orc.swap_blocks(dk, dv, hk, hv, out_pairs, "out")
+    assert np.array_equal(dk, dk0) and np.array_equal(dv, dv0)
+    for src, dst in out_pairs:
+        assert np.array_equal(hk[dst], dk0[src]) and np.array_equal(hv[dst], dv0[src])
+    rest = sorted(set(range(nh)) - set(out_pairs[:, 1].tolist()))
+    assert np.array_equal(hk[rest], hk0[rest]) and np.array_equal(hv[rest], hv0[rest])
+    in_pairs = np.array([[11, 2], [0, 7]], dtype=np.int64)              # host src -> device dst
+    hk1, hv1 = hk.copy(), hv.copy()
+    orc.swap_blocks(dk, dv, hk, hv, in_pairs, "in")
+    assert np.array_equal(hk, hk1) and np.array_equal(hv, hv1)
+    assert np.array_equal(dk[2], dk0[19]) and np.array_equal(dv[7], dv0[4])
+    rest = sorted(set(range(nd)) - {2, 7})
+    assert np.array_equal(dk[rest], dk0[rest]) and np.array_equal(dv[rest], dv0[rest])
+    orc.swap_blocks(dk, dv, hk, hv, np.zeros((0, 2), dtype=np.int64), "in")
+    assert np.array_equal(hk, hk1)
+
+
 def pin_widening(orc):
     """bfloat16 patterns widen to the float32 of the same bits: checks a few
     patterns with known values (1, -2, 0.5, smallest normal, largest)."""
@@ -305,5 +334,6 @@ ALL_PINS = [
     pin_zero_length,
     pin_scatter_places_tokens,
     pin_copy_blocks,
+    pin_swap_blocks,
     pin_widening,
 ]

@@ -112,6 +112,20 @@ def test_cache_op_argument_errors(L):
     assert L.pa_copy_blocks(ctypes.byref(d), None, 1, None) == _lib.PA_ERR_NULL
     assert L.pa_copy_blocks(ctypes.byref(d), P, -2, None) == _lib.PA_ERR_SHAPE
     assert L.pa_copy_blocks(ctypes.byref(d), None, 0, None) == _lib.PA_OK
+    S = lambda *a: L.pa_swap_blocks(*a)  # noqa: E731
+    assert S(None, P, P, 4, P, 1, _lib.PA_SWAP_OUT, None) == _lib.PA_ERR_NULL
+    assert S(ctypes.byref(d), P, P, 4, P, -1, _lib.PA_SWAP_OUT, None) == _lib.PA_ERR_SHAPE
+    assert S(ctypes.byref(d), P, P, 4, P, 1, 7, None) == _lib.PA_ERR_SHAPE
+    assert S(ctypes.byref(d), P, P, -4, P, 1, _lib.PA_SWAP_IN, None) == _lib.PA_ERR_SHAPE
+    assert S(ctypes.byref(d), None, P, 4, P, 1, _lib.PA_SWAP_IN, None) == _lib.PA_ERR_NULL
+    assert S(ctypes.byref(d), P, P, 4, None, 1, _lib.PA_SWAP_IN, None) == _lib.PA_ERR_NULL
+    assert S(ctypes.byref(d), None, None, 0, None, 0, _lib.PA_SWAP_OUT, None) == _lib.PA_OK
+    # memory the HIP runtime does not know as pinned host memory is refused
+    # before anything is launched
+    plain = (ctypes.c_uint16 * (16 * 8 * 128 * 4))()
+    addr = ctypes.cast(plain, ctypes.c_void_p)
+    assert S(ctypes.byref(d), addr, addr, 4, P, 1, _lib.PA_SWAP_OUT, None) == _lib.PA_ERR_UNSUPPORTED
+    assert "pinned" in L.pa_last_error().decode()
     assert L.pa_probe_copy(P, P, 24, None) == _lib.PA_ERR_SHAPE
     assert L.pa_probe_copy(None, P, 32, None) == _lib.PA_ERR_NULL
     assert L.pa_probe_copy(None, None, 0, None) == _lib.PA_OK

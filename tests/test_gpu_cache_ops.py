@@ -44,3 +44,44 @@ def test_reshape_and_cache_bit_exact(hkv, d, T):
     pa.reshape_and_cache(to_dev_bf16(k), to_dev_bf16(v), kd, vd, to_dev(slots))
     oracle.reshape_and_cache(kc, vc, k, v, slots)
     assert np.array_equal(bits_of(kd), kc) and np.array_equal(bits_of(vd), vc)
+
+
+@pytest.mark.parametrize("hkv,d", [(8, 128), (1, 64)])
+def test_swap_blocks_bit_exact(hkv, d):
+    """Blocks swapped out to pinned host memory and back in, bit for bit,
+    with out-of-pool pairs skipped and untouched blocks left alone."""
+    import torch
+
+    import paged_kv_cache_433_amd as pa
+    rng = np.random.default_rng(hkv * 7 + d)
+    nd, nh = 200, 90
+    kc = rng.integers(0, 2 ** 16, size=(nd, 16, hkv, d), dtype=np.uint16)
+    vc = rng.integers(0, 2 ** 16, size=(nd, 16, hkv, d), dtype=np.uint16)
+    hk0 = rng.integers(0, 2 ** 16, size=(nh, 16, hkv, d), dtype=np.uint16)
+    hv0 = rng.integers(0, 2 ** 16, size=(nh, 16, hkv, d), dtype=np.uint16)
+
+    def pinned(bits):
+        t = torch.empty(bits.shape, dtype=torch.bfloat16, pin_memory=True)
+        t.view(torch.int16).copy_(torch.from_numpy(bits.view(np.int16)))
+        return t
+
+    hk, hv = pinned(hk0), pinned(hv0)
+    kd, vd = to_dev_bf16(kc), to_dev_bf16(vc)
+    out_pairs = np.stack([rng.permutation(nd)[:60], rng.permutation(nh)[:60]], axis=1).astype(np.int64)
+    bad = np.array([[nd, 0], [0, nh + 5], [-1, 1]], dtype=np.int64)
+    note(f"swap out hkv={hkv} d={d}")
+    pa.swap_blocks(kd, vd, hk, hv, to_dev(np.concatenate([out_pairs, bad])), "out")
+    torch.cuda.synchronize()
+    ok, ov = kc.copy(), vc.copy()
+    xk, xv = hk0.copy(), hv0.copy()
+    oracle.swap_blocks(ok, ov, xk, xv, out_pairs, "out")
+    assert np.array_equal(hk.view(torch.int16).numpy().view(np.uint16), xk)
+    assert np.array_equal(hv.view(torch.int16).numpy().view(np.uint16), xv)
+    assert np.array_equal(bits_of(kd), kc) and np.array_equal(bits_of(vd), vc)
+
+    in_pairs = np.stack([rng.permutation(nh)[:50], rng.permutation(nd)[:50]], axis=1).astype(np.int64)
+    note(f"swap in hkv={hkv} d={d}")
+    pa.swap_blocks(kd, vd, hk, hv, to_dev(np.concatenate([in_pairs, bad[:, ::-1].copy()])), "in")
+    oracle.swap_blocks(ok, ov, xk, xv, in_pairs, "in")
+    assert np.array_equal(bits_of(kd), ok) and np.array_equal(bits_of(vd), ov)
+    assert np.array_equal(hk.view(torch.int16).numpy().view(np.uint16), xk)
