@@ -31,6 +31,7 @@ from .paged_attention import (  # noqa: F401
     bf16_bits_to_f64,
     copy_blocks,
     decode,
+    decode_multi,
     decode_sequence,
     reshape_and_cache,
     swap_blocks,

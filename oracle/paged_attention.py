@@ -88,6 +88,32 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale) -> np.ndarray
     return out
 
 
+def decode_multi(q, k_cache, v_cache, block_tables, context_lens, scale) -> np.ndarray:
+    """Attention of several new tokens per sequence over the paged cache.
+
+    A step that runs ``q_len`` new tokens of a sequence at once (verifying
+    speculative tokens in one forward pass: "vLLM: Anatomy and Mechanisms",
+    section "Speculative Decoding"; a chunk of a prefill: section "Chunked
+    Prefill") has all of them in the cache already, at positions
+    ``n - q_len .. n - 1``. Attention is causal: new token ``j`` attends over
+    positions ``0 .. n - q_len + j``, itself included, which is the decode
+    step of a context of ``n - q_len + j + 1`` tokens. ``q``:
+    ``[num_seqs, q_len, num_q_heads, head_size]`` bfloat16 bits; returns
+    float64 of that shape. ``n == 0`` gives zeros; otherwise ``n >= q_len``.
+    """
+    q = np.asarray(q)
+    num_seqs, q_len = q.shape[:2]
+    out = np.zeros(q.shape, dtype=np.float64)
+    for s in range(num_seqs):
+        n = int(context_lens[s])
+        if n == 0:
+            continue
+        assert n >= q_len, "the new tokens must be in the cache"
+        for j in range(q_len):
+            out[s, j] = decode_sequence(q[s, j], k_cache, v_cache, block_tables[s], n - q_len + j + 1, scale)
+    return out
+
+
 def reshape_and_cache(k_cache, v_cache, k, v, slot_mapping) -> None:
     """Scatter each new token's K and V into its physical slot, in place.
 

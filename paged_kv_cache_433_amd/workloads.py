@@ -196,6 +196,11 @@ class DecodeBatch:
     decode over ``context_lens``. Slots no table references, including the
     newest token's slot before the scatter, hold bfloat16 NaN. Table entries
     past a sequence's last block hold ``num_blocks + 12345``.
+
+    With ``q_len`` > 1 (several new tokens per sequence: speculative-decode
+    verification, a prefill chunk) the newest ``q_len`` tokens of every
+    sequence are new: ``new_k``/``new_v``/``slot_mapping`` hold them sequence
+    by sequence (``T = S * q_len``) and ``q`` is ``[S, q_len, Hq, D]``.
     """
 
     name: str
@@ -215,6 +220,7 @@ class DecodeBatch:
     new_v: np.ndarray
     slot_mapping: np.ndarray   # int64 [T]
     cow_pairs: np.ndarray      # int64 [P, 2]
+    q_len: int = 1
 
     @property
     def num_seqs(self) -> int:
@@ -235,12 +241,12 @@ def _fill_sequence(k_cache, v_cache, table, k_bits, v_bits, block_size):
 
 
 def make_batch(name, seed, lens, num_q_heads, num_kv_heads, head_size, num_blocks,
-               max_blocks_per_seq=None, scale=None, block_size=BLOCK_SIZE) -> DecodeBatch:
-    """A decode batch with the given context lengths (newest token included).
+               max_blocks_per_seq=None, scale=None, block_size=BLOCK_SIZE, q_len=1) -> DecodeBatch:
+    """A decode batch with the given context lengths (new tokens included).
 
     Draw order for ``seed``:
     * stream (seed, 0) shuffles the free pool;
-    * stream (seed, 2) draws q;
+    * stream (seed, 2) draws q (``[S, Hq, D]``, or ``[S, q_len, Hq, D]``);
     * stream (seed, 1, s) draws sequence s's K then V, per logical position.
 
     Blocks are popped from the shuffled pool in (sequence, logical block)
@@ -248,7 +254,7 @@ def make_batch(name, seed, lens, num_q_heads, num_kv_heads, head_size, num_block
     block lands.
     """
     lens = np.asarray(lens, dtype=np.int64)
-    assert np.all(lens >= 1)
+    assert np.all(lens >= q_len) and q_len >= 1
     S = len(lens)
     nblk = (lens + block_size - 1) // block_size
     MB = int(max_blocks_per_seq or nblk.max())
@@ -261,28 +267,32 @@ def make_batch(name, seed, lens, num_q_heads, num_kv_heads, head_size, num_block
     shape = (num_blocks, block_size, num_kv_heads, head_size)
     k_cache = np.full(shape, BF16_QNAN, dtype=np.uint16)
     v_cache = np.full(shape, BF16_QNAN, dtype=np.uint16)
-    new_k = np.empty((S, num_kv_heads, head_size), dtype=np.uint16)
+    new_k = np.empty((S * q_len, num_kv_heads, head_size), dtype=np.uint16)
     new_v = np.empty_like(new_k)
-    slots = np.empty(S, dtype=np.int64)
+    slots = np.empty(S * q_len, dtype=np.int64)
 
     def one(s):
         n = int(lens[s])
         r = _rng(seed, 1, s)
         kb = normal_bf16(r, (n, num_kv_heads, head_size))
         vb = normal_bf16(r, (n, num_kv_heads, head_size))
-        _fill_sequence(k_cache, v_cache, seqs[s].table, kb[: n - 1], vb[: n - 1], block_size)
-        new_k[s], new_v[s] = kb[n - 1], vb[n - 1]
-        slots[s] = seqs[s].table[(n - 1) // block_size] * block_size + (n - 1) % block_size
+        old = n - q_len
+        _fill_sequence(k_cache, v_cache, seqs[s].table, kb[:old], vb[:old], block_size)
+        for j in range(q_len):
+            pos = old + j
+            new_k[s * q_len + j], new_v[s * q_len + j] = kb[pos], vb[pos]
+            slots[s * q_len + j] = seqs[s].table[pos // block_size] * block_size + pos % block_size
 
     with ThreadPoolExecutor(_workers()) as ex:
         list(ex.map(one, range(S)))
-    q = normal_bf16(_rng(seed, 2), (S, num_q_heads, head_size))
+    q_shape = (S, num_q_heads, head_size) if q_len == 1 else (S, q_len, num_q_heads, head_size)
+    q = normal_bf16(_rng(seed, 2), q_shape)
     if scale is None:
         scale = 1.0 / math.sqrt(head_size)
     return DecodeBatch(name, seed, num_blocks, block_size, num_q_heads, num_kv_heads,
                        head_size, np.float32(scale), tables, lens.astype(np.int32), q,
                        k_cache, v_cache, new_k, new_v, slots,
-                       np.zeros((0, 2), dtype=np.int64))
+                       np.zeros((0, 2), dtype=np.int64), q_len)
 
 
 def sequence_kv(batch: DecodeBatch, s: int):

@@ -310,6 +310,53 @@ def pin_swap_blocks(orc):
     assert np.array_equal(hk, hk1)
 
 
+MULTI_CASES = [
+    # seed, lens, q_len, Hq, Hkv, D
+    (41, [3, 16, 17, 40], 3, 8, 2, 16),
+    (42, [2, 33, 64], 2, 4, 4, 32),
+    (43, [5, 9, 31, 48], 5, 16, 1, 8),
+]
+
+
+def pin_multi_token_causal_sdpa(orc):
+    """Several new tokens per sequence = torch's dense attention (fp64, CPU)
+    with an explicit causal mask (new token j sees positions up to
+    n - q_len + j), over K/V regenerated in logical order."""
+    for seed, lens, ql, hq, hkv, d in MULTI_CASES:
+        nb = int(sum((n + 15) // 16 for n in lens)) + 5
+        b = W.make_batch("pin", seed, lens, hq, hkv, d, nb, q_len=ql)
+        kc, vc = scattered(orc, b)
+        out = orc.decode_multi(b.q, kc, vc, b.block_tables, b.context_lens, b.scale)
+        assert out.shape == b.q.shape
+        for s, n in enumerate(lens):
+            kb, vb = W.sequence_kv(b, s)
+            k = torch.from_numpy(widen(kb)).permute(1, 0, 2).repeat_interleave(hq // hkv, 0)
+            v = torch.from_numpy(widen(vb)).permute(1, 0, 2).repeat_interleave(hq // hkv, 0)
+            q = torch.from_numpy(widen(b.q[s])).permute(1, 0, 2)                    # [Hq, q_len, D]
+            mask = torch.arange(n)[None, :] <= (n - ql + torch.arange(ql))[:, None]  # [q_len, n]
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                q[None], k[None].contiguous(), v[None].contiguous(), attn_mask=mask[None, None],
+                scale=float(b.scale))[0].permute(1, 0, 2)
+            err = np.abs(out[s] - ref.numpy()).max()
+            assert err <= 1e-12, (seed, s, err)
+
+
+def pin_multi_token_prefill_start(orc):
+    """When every token of a sequence is new (a prefill chunk from position
+    0), the first one sees only itself: its output is its own V. An empty
+    sequence gives zeros."""
+    lens = [4, 17, 20]
+    b = W.make_batch("pin", 44, lens, 8, 2, 16, 12, q_len=4)
+    kc, vc = scattered(orc, b)
+    out = orc.decode_multi(b.q, kc, vc, b.block_tables, b.context_lens, b.scale)
+    new_v = b.new_v.reshape(len(lens), 4, 2, 16)
+    for h in range(8):
+        assert np.array_equal(out[0, 0, h], widen(new_v[0, 0, h // 4])), h
+    zero = W.make_batch("pin", 45, [3], 4, 1, 8, 3, q_len=3)
+    zl = np.zeros(1, dtype=np.int32)
+    assert np.all(orc.decode_multi(zero.q, zero.k_cache, zero.v_cache, zero.block_tables, zl, zero.scale) == 0)
+
+
 def pin_widening(orc):
     """bfloat16 patterns widen to the float32 of the same bits: checks a few
     patterns with known values (1, -2, 0.5, smallest normal, largest)."""
@@ -335,5 +382,7 @@ ALL_PINS = [
     pin_scatter_places_tokens,
     pin_copy_blocks,
     pin_swap_blocks,
+    pin_multi_token_causal_sdpa,
+    pin_multi_token_prefill_start,
     pin_widening,
 ]

@@ -28,6 +28,8 @@ MUTANTS = {
     "copy reads V into K": ("k_cache[d] = k_src[i]", "k_cache[d] = v_src[i]"),
     "copy direction reversed": ("k_src = k_cache[src].copy()", "k_src = k_cache[dst].copy()"),
     "widening shift wrong": ("<< np.uint32(16)", "<< np.uint32(15)"),
+    "causal limit off by one": ("n - q_len + j + 1, scale)", "n - q_len + j, scale)"),
+    "new tokens in reverse order": ("decode_sequence(q[s, j], k_cache", "decode_sequence(q[s, q_len - 1 - j], k_cache"),
     "swap direction ignored": ('if direction == "out":', 'if direction != "out":'),
     "swap copies K into V": ("tv[d_] = fv[s_]", "tv[d_] = fk[s_]"),
     "query heads transposed": ("qf = bf16_bits_to_f64(q_s)", "qf = bf16_bits_to_f64(q_s)[::-1]"),
