@@ -134,8 +134,12 @@ def _time_oracle(batch, kc, vc, order, seconds: float, threads: int):
         t0 = time.perf_counter()
         while time.perf_counter() - t0 < seconds:
             for s in order:
-                oracle.decode_sequence(batch.q[s], kc, vc, batch.block_tables[s],
-                                       batch.context_lens[s], batch.scale)
+                if batch.q_len > 1:
+                    oracle.decode_multi(batch.q[s:s + 1], kc, vc, batch.block_tables[s:s + 1],
+                                        batch.context_lens[s:s + 1], batch.scale)
+                else:
+                    oracle.decode_sequence(batch.q[s], kc, vc, batch.block_tables[s],
+                                           batch.context_lens[s], batch.scale)
                 done.append(int(s))
                 if time.perf_counter() - t0 >= seconds:
                     break
@@ -167,7 +171,8 @@ def cpu_baseline(batch, seconds: float):
     for threads in (cores, 1):
         done, dt = _time_oracle(batch, kc, vc, order, seconds, threads)
         lens = batch.context_lens[done]
-        nbytes = W.algorithmic_bytes(lens, batch.num_q_heads, batch.num_kv_heads, batch.head_size)
+        nbytes = W.algorithmic_bytes(lens, batch.num_q_heads, batch.num_kv_heads, batch.head_size,
+                                     q_len=batch.q_len)
         res[threads] = (len(done), int(lens.sum()), dt, nbytes / dt / 1e9, len(done) / dt)
     n, tokens, dt, gbps, sps = res[cores]
     return {
@@ -264,6 +269,9 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="llama3_8b_gqa")
+    ap.add_argument("--q-len", type=int, default=1,
+                    help="new tokens per sequence (speculative-decode verification): the step scatters them "
+                         "and runs pa_decode_multi")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="seconds of oracle work per CPU-baseline run (two runs: all cores, one thread)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -300,7 +308,13 @@ def main(argv=None) -> int:
     print(f"[bench] generating {args.config}", file=sys.stderr, flush=True)
     # The beam-search workload's first step: its copy-on-write pairs, its
     # scatter and its decode are repeated every step (both are idempotent).
-    b = W.BeamSearchWorkload().step() if args.config == "beam_cow" else W.make_config(args.config)
+    if args.config == "beam_cow":
+        if args.q_len != 1:
+            raise SystemExit("--q-len applies to the named single-step configs")
+        b = W.BeamSearchWorkload().step()
+    else:
+        b = W.make_config(args.config, q_len=args.q_len)
+    multi = args.q_len > 1
 
     def bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -315,10 +329,17 @@ def main(argv=None) -> int:
     out = torch.empty_like(q)
     scale = float(b.scale)
 
-    decode_bytes = W.algorithmic_bytes(b.context_lens, b.num_q_heads, b.num_kv_heads, b.head_size)
-    step_bytes = decode_bytes + W.scatter_bytes(b.num_seqs, b.num_kv_heads, b.head_size)
+    decode_bytes = W.algorithmic_bytes(b.context_lens, b.num_q_heads, b.num_kv_heads, b.head_size,
+                                       q_len=args.q_len)
+    step_bytes = decode_bytes + W.scatter_bytes(len(b.slot_mapping), b.num_kv_heads, b.head_size)
     if pairs is not None:
         step_bytes += W.copy_bytes(len(b.cow_pairs), b.block_size, b.num_kv_heads, b.head_size)
+
+    def run_decode():
+        if multi:
+            pa.decode_multi(q, kc, vc, tables, lens, scale, out=out)
+        else:
+            pa.decode(q, kc, vc, tables, lens, scale, out=out)
 
     stream = torch.cuda.current_stream(dev)
     n_ev = args.steps
@@ -331,7 +352,7 @@ def main(argv=None) -> int:
         pa.reshape_and_cache(new_k, new_v, kc, vc, slots)
         if i is not None:
             ev_a[i].record(stream)
-        pa.decode(q, kc, vc, tables, lens, scale, out=out)
+        run_decode()
         if i is not None:
             ev_b[i].record(stream)
 
@@ -366,7 +387,7 @@ def main(argv=None) -> int:
         for a, z in cold:
             pa.probe_read(scratch, sink)
             a.record(stream)
-            pa.decode(q, kc, vc, tables, lens, scale, out=out)
+            run_decode()
             z.record(stream)
         torch.cuda.synchronize()
         cold_us = float(np.mean([a.elapsed_time(z) for a, z in cold])) * 1e3
@@ -374,7 +395,7 @@ def main(argv=None) -> int:
 
     value = step_bytes / (ms * 1e-3) / 1e9
     achieved = decode_bytes / (dec_mean * 1e-3) / 1e9
-    traffic = measured_traffic(args.config)
+    traffic = measured_traffic(args.config) if not multi else None
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -398,8 +419,9 @@ def main(argv=None) -> int:
             "kv_pool_blocks": b.num_blocks,
             "sum_context_tokens": int(b.context_lens.sum()),
             "seed": b.seed,
+            "q_len": args.q_len,
             "step": ("copy_blocks + " if pairs is not None else "")
-                    + "reshape_and_cache + decode",
+                    + ("reshape_and_cache + decode_multi" if multi else "reshape_and_cache + decode"),
             "parallelism": "single GPU",
             "cache": CACHE_NOTES.get(args.config, "cold: the K/V of a call is several times the 256 MB MALL"),
         },

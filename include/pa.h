@@ -138,6 +138,33 @@ size_t pa_decode_workspace_bytes(const pa_kv_cache *cache, int32_t num_seqs,
                                  int32_t num_q_heads, int32_t max_blocks_per_seq);
 
 /*
+ * pa_decode_multi - attention of q_len new tokens per sequence over the paged
+ * cache, causal: new token j of a sequence with context length n (its new
+ * tokens included, already written by pa_reshape_and_cache at positions
+ * n-q_len .. n-1) attends over positions 0 .. n-q_len+j. This is what a
+ * step that verifies speculative tokens in one forward pass, or runs a
+ * chunk of a prefill, needs ("vLLM: Anatomy and Mechanisms of
+ * High-Throughput LLM Inference", sections "Speculative Decoding" and
+ * "Chunked Prefill"; "Inside vLLM", section "Scheduler": the new tokens of a
+ * step are not always 1).
+ *
+ *   q, out   bf16 [num_seqs, q_len, num_q_heads, head_size]
+ *   q_len    >= 1, with q_len * (num_q_heads / num_kv_heads) <= 32
+ * Other arguments, the workspace (size from pa_decode_multi_workspace_bytes)
+ * and the errors are those of pa_decode; q_len == 1 is pa_decode. Every
+ * context length must be 0 or >= q_len; a new token that would see no
+ * position gets a zero output.
+ */
+int pa_decode_multi(const pa_kv_cache *cache, const void *q, const int32_t *block_tables,
+                    const int32_t *context_lens, int32_t num_seqs, int32_t q_len, int32_t num_q_heads,
+                    int32_t max_blocks_per_seq, float scale, void *out, void *workspace,
+                    size_t workspace_bytes, void *stream);
+
+/* Workspace bytes of pa_decode_multi (as pa_decode_workspace_bytes). */
+size_t pa_decode_multi_workspace_bytes(const pa_kv_cache *cache, int32_t num_seqs, int32_t q_len,
+                                       int32_t num_q_heads, int32_t max_blocks_per_seq);
+
+/*
  * pa_reshape_and_cache - write each new token's K and V into its physical
  * slot before attention runs (the slot the block manager assigned on demand:
  * "vLLM: Anatomy and Mechanisms", section "Block-Level Management"; the

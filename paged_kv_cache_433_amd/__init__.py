@@ -9,6 +9,7 @@ from .ops import (  # noqa: F401
     PagedAttentionError,
     copy_blocks,
     decode,
+    decode_multi,
     decode_workspace_bytes,
     probe_copy,
     probe_read,

@@ -222,59 +222,96 @@ __device__ __forceinline__ bool next_piece(Walker &wk, Piece &p) {
   return true;
 }
 
-// Per-thread constants of the decode kernel.
+// Per-thread constants of the decode kernel. A wavefront serves one KV head;
+// its MFMA columns are (new token, query head) pairs of that head, token-
+// major (column = token * group + head), 16 per tile. Lane (c, grp) holds
+// column 16*t + c of tile t.
+template <int NT>
 struct Lane {
   int tid, wave, lane, c, grp, w;
   int HG, NG;
-  bool head_ok;       // lane column c is a query head of the group
-  int crow;           // query head the lane loads (c, or the group's last head)
-  size_t blk_stride;  // elements per block of one cache array
-  int row_bytes;      // bytes per token row of one cache array (all KV heads)
-  uint32_t lane_off;  // byte offset of the lane's 16 bytes in (block, head): token c, dims 8*grp..
-  uint32_t q_off;     // byte offset of the lane's 16 bytes in a group's q rows: row crow, dims 8*grp..
+  bool col_ok[NT];       // the lane's column of tile t exists (column < q_len * group)
+  int col[NT];           // that column, or the last one when it does not exist
+  int qshift[NT];        // q_len - 1 - new token of the column: its causal limit is n - qshift
+  uint32_t q_off[NT];    // byte offset of the lane's 16 bytes of its column's q row (in the
+                         // sequence's q rows from the KV head's first query head on)
+  uint32_t out_off[NT];  // element offset of the lane's 8 outputs, same origin
+  size_t blk_stride;     // elements per block of one cache array
+  int row_bytes;         // bytes per token row of one cache array (all KV heads)
+  uint32_t lane_off;     // byte offset of the lane's 16 bytes in (block, head): token c, dims 8*grp..
   long long U, E;
-  uint32_t pool32;    // min(num_blocks, INT32_MAX)
+  uint32_t pool32;       // min(num_blocks, INT32_MAX)
   u32x2_t sel;
 };
 
 // One wavefront's pass over its workgroup's stream of blocks.
-template <int NJ>
+template <int NJ, int NT>
 struct Stream {
-  Piece P, Q;         // the piece being computed and the next one
+  Piece P, Q;            // the piece being computed and the next one
   bool has_q;
-  int i;              // block of P being computed
-  int ord;            // P's position among the workgroup's pieces
+  int i;                 // block of P being computed
+  int ord;               // P's position among the workgroup's pieces
   size_t hoff, hoff_q;
-  u32x4_t qv[NJ];     // q of P, in the MFMA operand layout
-  float m_run;        // running max of base-2 logits, query head c
-  float l_part;       // this lane's share of the running sum
-  f32x4_t acc[2 * NJ];
+  u32x4_t qv[NT][NJ];    // q of P, in the MFMA operand layout (one column tile only)
+  float m_run[NT];       // running max of base-2 logits, per column
+  float l_part[NT];      // this lane's share of the running sum
+  f32x4_t acc[NT][2 * NJ];
 };
 
 // Buffer-resource word 3 for gfx9-family raw (untyped) buffer loads.
 constexpr int kRawBufferWord3 = 0x00020000;
 
-// q rows of the piece's query-head group for this wavefront, in the MFMA
-// operand layout. Read through a buffer resource (scalar base, fixed lane
-// offset) so that no vector address is computed here.
-template <int NJ>
-__device__ __forceinline__ void load_q(const DecodeArgs &a, const Lane &ln, const Piece &p, u32x4_t (&qv)[NJ]) {
+// q rows of the piece's columns for this wavefront, in the MFMA operand
+// layout. Read through a buffer resource (scalar base at the KV head's first
+// query head of the sequence's first new token, fixed lane offsets) so that
+// no vector address is computed here.
+template <int NJ, int NT>
+__device__ __forceinline__ void load_q(const DecodeArgs &a, const Lane<NT> &ln, const Piece &p,
+                                       u32x4_t (&qv)[NT][NJ]) {
   constexpr int D = NJ * 32;
-  const size_t base =
-      ((size_t)p.s * a.num_q_heads + (size_t)(p.hg * ln.HG + ln.wave) * a.group) * D * sizeof(uint16_t);
+  const size_t base = ((size_t)p.s * a.q_len * a.num_q_heads + (size_t)(p.hg * ln.HG + ln.wave) * a.group) * D *
+                      sizeof(uint16_t);
+  const int span = ((a.q_len - 1) * a.num_q_heads + a.group) * D * (int)sizeof(uint16_t);
   const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<char *>(reinterpret_cast<const char *>(a.q) + base), 0, a.group * D * (int)sizeof(uint16_t),
-      kRawBufferWord3);
+      const_cast<char *>(reinterpret_cast<const char *>(a.q) + base), 0, span, kRawBufferWord3);
 #pragma unroll
-  for (int j = 0; j < NJ; ++j)
-    qv[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, ln.q_off + 64 * j, 0, 0));
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      qv[t][j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, ln.q_off[t] + 64 * j, 0, 0));
 }
 
-// q of the next piece travels through LDS: two slots per wavefront, each
-// holding the group's rows [group][D] as bf16; slot = piece position & 1.
+// q of the next piece travels through LDS (one column tile only): two slots
+// per wavefront, each holding the KV head's column rows [num_cols][D] as
+// bf16; slot = piece position & 1.
 template <int NJ>
-__device__ __forceinline__ uint16_t *q_slot(uint16_t *lds, const DecodeArgs &a, const Lane &ln, int ord) {
-  return lds + ((size_t)ln.wave * 2 + (ord & 1)) * a.group * (NJ * 32);
+__device__ __forceinline__ uint16_t *q_slot(uint16_t *lds, const DecodeArgs &a, int wave, int ord) {
+  return lds + ((size_t)wave * 2 + (ord & 1)) * a.num_cols * (NJ * 32);
+}
+
+// With two column tiles the current piece's q lives in LDS (one slot per
+// wavefront, [num_cols][D]) and is read per block: the registers to keep it
+// are not there. Each lane writes and reads only its own columns' rows (or,
+// for a missing column, the last row, written by the same wavefront), so no
+// barrier is needed.
+template <int NJ, int NT>
+__device__ __forceinline__ void park_q(uint16_t *lds, const DecodeArgs &a, const Lane<NT> &ln,
+                                       const u32x4_t (&qv)[NT][NJ]) {
+  uint16_t *qs = lds + (size_t)ln.wave * a.num_cols * (NJ * 32) + ln.grp * 8;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+    if (ln.col_ok[t]) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) *reinterpret_cast<u32x4_t *>(qs + ln.col[t] * (NJ * 32) + 32 * j) = qv[t][j];
+    }
+}
+
+template <int NJ, int NT>
+__device__ __forceinline__ void parked_q(const uint16_t *lds, const DecodeArgs &a, const Lane<NT> &ln, int t,
+                                         u32x4_t (&qv)[NJ]) {
+  const uint16_t *qs = lds + (size_t)ln.wave * a.num_cols * (NJ * 32) + ln.col[t] * (NJ * 32) + ln.grp * 8;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) qv[j] = *reinterpret_cast<const u32x4_t *>(qs + 32 * j);
 }
 
 // Physical block of logical block b of sequence s, clamped to the pool. The
@@ -289,8 +326,8 @@ __device__ __forceinline__ int block_id(const int32_t *__restrict__ tables, cons
 }
 
 // Element offset of the wavefront's KV head inside a token row (uniform).
-template <int NJ>
-__device__ __forceinline__ size_t head_off(const Lane &ln, const Piece &p) {
+template <int NJ, int NT>
+__device__ __forceinline__ size_t head_off(const Lane<NT> &ln, const Piece &p) {
   return (size_t)(p.hg * ln.HG + ln.wave) * (NJ * 32);
 }
 
@@ -300,8 +337,8 @@ __device__ __forceinline__ size_t head_off(const Lane &ln, const Piece &p) {
 // `nrows` token rows; the lane adds its fixed offset. So no vector address
 // arithmetic happens per block, and the rows past the context length in a
 // sequence's last block are never fetched: they read as zeros.
-template <int NJ>
-__device__ __forceinline__ void issue(const DecodeArgs &a, const Lane &ln, int blk, size_t hoff, int nrows,
+template <int NJ, int NT>
+__device__ __forceinline__ void issue(const DecodeArgs &a, const Lane<NT> &ln, int blk, size_t hoff, int nrows,
                                       u32x4_t (&K)[NJ], u32x4_t (&V)[NJ]) {
   const size_t base = ((size_t)blk * ln.blk_stride + hoff) * sizeof(uint16_t);
   const int span = nrows * ln.row_bytes;
@@ -328,25 +365,33 @@ __device__ __forceinline__ int rows_in(int n, int b) {
 // segment begun in an earlier workgroup, so each workgroup writes one merge
 // record, when its first piece ends: that segment and where its pieces are,
 // or none.
-template <int NJ>
-__device__ __forceinline__ void finish_piece(const DecodeArgs &a, const Lane &ln, Stream<NJ> &st) {
+template <int NJ, int NT, bool kMulti>
+__device__ __forceinline__ void finish_piece(const DecodeArgs &a, const Lane<NT> &ln, Stream<NJ, NT> &st) {
   constexpr int D = NJ * 32;
   const Piece &P = st.P;
-  float l = st.l_part + __shfl_xor(st.l_part, 16);
-  l += __shfl_xor(l, 32);
-  const int head = (P.hg * ln.HG + ln.wave) * a.group + ln.c;
   const bool whole = P.off == 0 && P.cnt == P.L;
-  if (whole) {
-    if (ln.head_ok)
-      store_out<NJ>(a.out + ((size_t)P.s * a.num_q_heads + head) * D + ln.grp * 8, st.acc, 1.f / l);
-  } else {
-    const int slot = P.first ? 0 : 1;
-    const size_t row = (((size_t)ln.w * 2 + slot) * ln.HG + ln.wave) * a.group + ln.c;
-    if (ln.head_ok) {
-      float *po = a.part_o + row * D + ln.grp * 8;
+  const int g = P.hg * ln.HG + ln.wave;
 #pragma unroll
-      for (int t = 0; t < 2 * NJ; ++t) *reinterpret_cast<f32x4_t *>(po + 32 * (t >> 1) + 4 * (t & 1)) = st.acc[t];
-      if (ln.grp == 0) *reinterpret_cast<f32x2_t *>(a.part_ml + row * 2) = f32x2_t{st.m_run, l};
+  for (int t = 0; t < NT; ++t) {
+    float l = st.l_part[t] + __shfl_xor(st.l_part[t], 16);
+    l += __shfl_xor(l, 32);
+    if (whole) {
+      // With several new tokens a column can see no position at all (only
+      // if a context is shorter than q_len); it is written as zeros.
+      const float inv = kMulti ? (l > 0.f ? 1.f / l : 0.f) : 1.f / l;
+      if (ln.col_ok[t])
+        store_out<NJ>(a.out + ((size_t)P.s * a.q_len * a.num_q_heads + (size_t)g * a.group) * D + ln.out_off[t],
+                      st.acc[t], inv);
+    } else {
+      const int slot = P.first ? 0 : 1;
+      const size_t row = (((size_t)ln.w * 2 + slot) * ln.HG + ln.wave) * a.num_cols + ln.col[t];
+      if (ln.col_ok[t]) {
+        float *po = a.part_o + row * D + ln.grp * 8;
+#pragma unroll
+        for (int k = 0; k < 2 * NJ; ++k)
+          *reinterpret_cast<f32x4_t *>(po + 32 * (k >> 1) + 4 * (k & 1)) = st.acc[t][k];
+        if (ln.grp == 0) *reinterpret_cast<f32x2_t *>(a.part_ml + row * 2) = f32x2_t{st.m_run[t], l};
+      }
     }
   }
   if (P.first && ln.tid == 0 && a.merge_desc) {
@@ -360,22 +405,32 @@ __device__ __forceinline__ void finish_piece(const DecodeArgs &a, const Lane &ln
   }
 }
 
-// Makes Q the current piece (its first block is already loading, its q is
-// in LDS) and looks one piece further ahead.
-template <int NJ>
-__device__ __forceinline__ void advance(const DecodeArgs &a, const Lane &ln, Walker &wk, Stream<NJ> &st,
+// Makes Q the current piece (its first block is already loading) and looks
+// one piece further ahead. With one column tile Q's q is in LDS already;
+// with two it is loaded here and parked in LDS.
+template <int NJ, int NT>
+__device__ __forceinline__ void advance(const DecodeArgs &a, const Lane<NT> &ln, Walker &wk, Stream<NJ, NT> &st,
                                         uint16_t *lds) {
   st.P = st.Q;
   ++st.ord;
-  const uint16_t *qs = q_slot<NJ>(lds, a, ln, st.ord) + ln.crow * (NJ * 32) + ln.grp * 8;
+  if constexpr (NT == 1) {
+    const uint16_t *qs = q_slot<NJ>(lds, a, ln.wave, st.ord) + ln.grp * 8;
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) st.qv[j] = *reinterpret_cast<const u32x4_t *>(qs + 32 * j);
+    for (int j = 0; j < NJ; ++j) st.qv[0][j] = *reinterpret_cast<const u32x4_t *>(qs + ln.col[0] * (NJ * 32) + 32 * j);
+  } else {
+    u32x4_t qv[NT][NJ];
+    load_q<NJ>(a, ln, st.P, qv);
+    park_q<NJ>(lds, a, ln, qv);
+  }
   st.hoff = st.hoff_q;
   st.i = 0;
-  st.m_run = -INFINITY;
-  st.l_part = 0.f;
 #pragma unroll
-  for (int t = 0; t < 2 * NJ; ++t) st.acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < NT; ++t) {
+    st.m_run[t] = -INFINITY;
+    st.l_part[t] = 0.f;
+#pragma unroll
+    for (int k = 0; k < 2 * NJ; ++k) st.acc[t][k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
   st.has_q = next_piece(wk, st.Q);
   if (!st.has_q) st.Q = st.P;
   st.hoff_q = head_off<NJ>(ln, st.Q);
@@ -384,17 +439,17 @@ __device__ __forceinline__ void advance(const DecodeArgs &a, const Lane &ln, Wal
 // Computes block i of P from (K, V) after starting the next block of the
 // stream loading into (Kn, Vn); finishes P at its end and moves to Q.
 // Returns false once the stream is done.
-template <int NJ>
-__device__ __forceinline__ bool step(const int32_t *__restrict__ tables, const DecodeArgs &a, const Lane &ln,
-                                     Walker &wk, Stream<NJ> &st, u32x4_t (&K)[NJ], u32x4_t (&V)[NJ],
+template <int NJ, int NT, bool kMulti>
+__device__ __forceinline__ bool step(const int32_t *__restrict__ tables, const DecodeArgs &a, const Lane<NT> &ln,
+                                     Walker &wk, Stream<NJ, NT> &st, u32x4_t (&K)[NJ], u32x4_t (&V)[NJ],
                                      u32x4_t (&Kn)[NJ], u32x4_t (&Vn)[NJ], uint16_t *lds) {
   const Piece &P = st.P;
   // In P's first step, q of the next piece is loaded (before this step's K/V
   // loads) and parked in LDS at the end of the step: the registers never
   // cross a loop iteration, and the wait for them covers only the K/V loads
   // issued after them.
-  const bool stage_q = st.i == 0 && st.has_q;
-  u32x4_t qt[NJ];
+  const bool stage_q = NT == 1 && st.i == 0 && st.has_q;
+  u32x4_t qt[NT][NJ];
   if (stage_q) load_q<NJ>(a, ln, st.Q, qt);
   // The next block of the stream: P's next, else Q's first. The loads are
   // issued on every path (past the end of the stream they reload the
@@ -413,30 +468,46 @@ __device__ __forceinline__ bool step(const int32_t *__restrict__ tables, const D
 
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
   const int b = P.off + st.i;
-  f32x4_t sc = zero4;
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) sc = mfma32(K[j], st.qv[j], sc);
   const int pos0 = b * kBlock + ln.grp * 4;
-  float z[4];
+  u32x2_t pb_hi[NT], pb_lo[NT];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) z[r] = (pos0 + r < P.n) ? sc[r] * a.scale_log2 : -INFINITY;
-  float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m_new = fmaxf(st.m_run, mx);  // finite: token b*16 is always < n
-  const float alpha = fast_exp2(st.m_run - m_new);
-  st.m_run = m_new;
+  for (int t = 0; t < NT; ++t) {
+    f32x4_t sc = zero4;
+    if constexpr (NT == 1) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) sc = mfma32(K[j], st.qv[t][j], sc);
+    } else {
+      u32x4_t qv[NJ];
+      parked_q<NJ>(lds, a, ln, t, qv);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) sc = mfma32(K[j], qv[j], sc);
+    }
+    // Positions past the column's causal limit (the context length for a
+    // single new token) are masked.
+    const int lim = kMulti ? P.n - ln.qshift[t] : P.n;
+    float z[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) z[r] = (pos0 + r < lim) ? sc[r] * a.scale_log2 : -INFINITY;
+    float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    // With one new token, position b*16 is always visible, so the max is
+    // finite. With several, a column may see nothing in this block yet.
+    const float m_new = fmaxf(st.m_run[t], mx);
+    const float m_use = kMulti ? (m_new == -INFINITY ? 0.f : m_new) : m_new;
+    const float alpha = fast_exp2(st.m_run[t] - m_use);
+    st.m_run[t] = m_new;
 
-  // P = P_hi + P_lo, both bf16.
-  const float p0 = fast_exp2(z[0] - m_new), p1 = fast_exp2(z[1] - m_new);
-  const float p2 = fast_exp2(z[2] - m_new), p3 = fast_exp2(z[3] - m_new);
-  const uint32_t h01 = to_bf16x2(p0, p1), h23 = to_bf16x2(p2, p3);
-  const u32x2_t pb_hi = {h01, h23};
-  const u32x2_t pb_lo = {to_bf16x2(p0 - bf16_lo(h01), p1 - bf16_hi(h01)),
-                         to_bf16x2(p2 - bf16_lo(h23), p3 - bf16_hi(h23))};
-  st.l_part = st.l_part * alpha + ((p0 + p1) + (p2 + p3));
+    // P = P_hi + P_lo, both bf16.
+    const float p0 = fast_exp2(z[0] - m_use), p1 = fast_exp2(z[1] - m_use);
+    const float p2 = fast_exp2(z[2] - m_use), p3 = fast_exp2(z[3] - m_use);
+    const uint32_t h01 = to_bf16x2(p0, p1), h23 = to_bf16x2(p2, p3);
+    pb_hi[t] = u32x2_t{h01, h23};
+    pb_lo[t] = u32x2_t{to_bf16x2(p0 - bf16_lo(h01), p1 - bf16_hi(h01)), to_bf16x2(p2 - bf16_lo(h23), p3 - bf16_hi(h23))};
+    st.l_part[t] = st.l_part[t] * alpha + ((p0 + p1) + (p2 + p3));
 #pragma unroll
-  for (int t = 0; t < 2 * NJ; ++t) st.acc[t] *= alpha;
+    for (int k = 0; k < 2 * NJ; ++k) st.acc[t][k] *= alpha;
+  }
 
   // V rows of tokens at or past n must not reach the sum, even as NaN * 0.
   const bool v_live = b * kBlock + ln.c < P.n;
@@ -445,22 +516,29 @@ __device__ __forceinline__ bool step(const int32_t *__restrict__ tables, const D
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const u32x2_t vin = v_live ? u32x2_t{V[j][2 * h], V[j][2 * h + 1]} : u32x2_t{0u, 0u};
-      const f32x4_t t = mfma16(vin, ln.sel, zero4);
-      const u32x2_t av = {pack_hi(t[0], t[1]), pack_hi(t[2], t[3])};
-      st.acc[2 * j + h] = mfma16(av, pb_hi, st.acc[2 * j + h]);
-      st.acc[2 * j + h] = mfma16(av, pb_lo, st.acc[2 * j + h]);
+      const f32x4_t tv = mfma16(vin, ln.sel, zero4);
+      const u32x2_t av = {pack_hi(tv[0], tv[1]), pack_hi(tv[2], tv[3])};
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        st.acc[t][2 * j + h] = mfma16(av, pb_hi[t], st.acc[t][2 * j + h]);
+        st.acc[t][2 * j + h] = mfma16(av, pb_lo[t], st.acc[t][2 * j + h]);
+      }
     }
   }
 
-  if (stage_q && ln.head_ok) {
-    uint16_t *qs = q_slot<NJ>(lds, a, ln, st.ord + 1) + ln.c * (NJ * 32) + ln.grp * 8;
+  if (stage_q) {
+    uint16_t *qs = q_slot<NJ>(lds, a, ln.wave, st.ord + 1) + ln.grp * 8;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) *reinterpret_cast<u32x4_t *>(qs + 32 * j) = qt[j];
+    for (int t = 0; t < NT; ++t)
+      if (ln.col_ok[t]) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) *reinterpret_cast<u32x4_t *>(qs + ln.col[t] * (NJ * 32) + 32 * j) = qt[t][j];
+      }
   }
 
   st.i = nx;
   if (in_p) return true;
-  finish_piece<NJ>(a, ln, st);
+  finish_piece<NJ, NT, kMulti>(a, ln, st);
   if (!st.has_q) return false;
   advance<NJ>(a, ln, wk, st, lds);
   return true;
@@ -471,8 +549,9 @@ __device__ __forceinline__ bool step(const int32_t *__restrict__ tables, const D
 template <int D>
 __device__ __forceinline__ void zero_empty(const DecodeArgs &a, int s, int w) {
   if (s % a.num_wgs != w) return;
-  u32x4_t *row = reinterpret_cast<u32x4_t *>(a.out + (size_t)s * a.num_q_heads * D);
-  for (int i = 0; i < a.num_q_heads * D / 8; ++i) row[i] = u32x4_t{0, 0, 0, 0};
+  const int rows = a.q_len * a.num_q_heads;
+  u32x4_t *row = reinterpret_cast<u32x4_t *>(a.out + (size_t)s * rows * D);
+  for (int i = 0; i < rows * D / 8; ++i) row[i] = u32x4_t{0, 0, 0, 0};
 }
 
 // Workgroups past the ones that get units have no merge record to write.
@@ -480,12 +559,16 @@ __device__ __forceinline__ void no_merge(const DecodeArgs &a, int w, int tid) {
   if (tid == 0 && a.merge_desc) a.merge_desc[w] = int2{-1, -1};
 }
 
-template <int D>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+// NT: 16-column MFMA tiles per KV head (columns = q_len * group). kMulti:
+// several new tokens per sequence, each with its own causal limit. The
+// launch puts one wavefront on each SIMD; with two tiles the wavefront may
+// take the whole register file (arch and accumulation registers).
+template <int D, int NT, bool kMulti>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2 : 1)))
 void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const int32_t *__restrict__ lens) {
   constexpr int NJ = D / 32;  // MFMA steps over head_size; 16-byte loads per lane per row
   static_assert(NJ >= 1 && D % 32 == 0, "head_size must be a multiple of 32");
-  extern __shared__ __align__(16) uint16_t q_lds[];  // heads_per_wg * 2 * group * D
+  extern __shared__ __align__(16) uint16_t q_lds[];  // heads_per_wg * (NT == 1 ? 2 : 1) * num_cols * D
   __shared__ long long red[8];
   __shared__ int found_seq, found_n;
   __shared__ long long found_prefix;
@@ -578,10 +661,11 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
   wk.off = (int)((lo - wk.seg_base) % wk.L);
   wk.first = true;
 
-  // The wavefront serves KV head hg*HG + wave of every piece: its query heads
-  // are that head's group, one per lane column c. Lanes with c >= group
-  // repeat the group's last head; their results are never stored.
-  Lane ln;
+  // The wavefront serves KV head hg*HG + wave of every piece. Its columns are
+  // (new token, query head of that KV head's group) pairs; lanes whose column
+  // does not exist repeat the last column, and their results are never
+  // stored.
+  Lane<NT> ln;
   ln.tid = tid;
   ln.wave = wave;
   ln.lane = lane;
@@ -590,12 +674,20 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
   ln.w = w;
   ln.HG = a.heads_per_wg;
   ln.NG = NG;
-  ln.head_ok = ln.c < a.group;
-  ln.crow = ln.head_ok ? ln.c : a.group - 1;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int col = 16 * t + ln.c;
+    ln.col_ok[t] = col < a.num_cols;
+    ln.col[t] = ln.col_ok[t] ? col : a.num_cols - 1;
+    const int tok = ln.col[t] / a.group;
+    const int qh = ln.col[t] - tok * a.group;
+    ln.qshift[t] = a.q_len - 1 - tok;
+    ln.out_off[t] = (uint32_t)((tok * a.num_q_heads + qh) * D + ln.grp * 8);
+    ln.q_off[t] = ln.out_off[t] * (uint32_t)sizeof(uint16_t);
+  }
   ln.blk_stride = (size_t)a.num_kv_heads * D * kBlock;
   ln.row_bytes = a.num_kv_heads * D * (int)sizeof(uint16_t);
   ln.lane_off = (uint32_t)(((size_t)ln.c * a.num_kv_heads * D + ln.grp * 8) * sizeof(uint16_t));
-  ln.q_off = (uint32_t)((ln.crow * D + ln.grp * 8) * sizeof(uint16_t));
   ln.U = U;
   ln.E = E;
   ln.pool32 = (uint32_t)(a.num_blocks < 0x7fffffffLL ? a.num_blocks : 0x7fffffffLL);
@@ -610,31 +702,41 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
   // buffers take turns: while one block is computed, the next block of the
   // stream (possibly the first block of the next piece) loads into the
   // other. The next piece's q goes through LDS one piece ahead.
-  Stream<NJ> st;
+  Stream<NJ, NT> st;
   next_piece(wk, st.P);
-  load_q<NJ>(a, ln, st.P, st.qv);
+  if constexpr (NT == 1) {
+    load_q<NJ>(a, ln, st.P, st.qv);
+  } else {
+    u32x4_t qv[NT][NJ];
+    load_q<NJ>(a, ln, st.P, qv);
+    park_q<NJ>(q_lds, a, ln, qv);
+  }
   st.hoff = head_off<NJ>(ln, st.P);
   st.has_q = next_piece(wk, st.Q);
   if (!st.has_q) st.Q = st.P;
   st.hoff_q = head_off<NJ>(ln, st.Q);
   st.i = 0;
   st.ord = 0;
-  st.m_run = -INFINITY;
-  st.l_part = 0.f;
 #pragma unroll
-  for (int t = 0; t < 2 * NJ; ++t) st.acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < NT; ++t) {
+    st.m_run[t] = -INFINITY;
+    st.l_part[t] = 0.f;
+#pragma unroll
+    for (int k = 0; k < 2 * NJ; ++k) st.acc[t][k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
   u32x4_t KA[NJ], VA[NJ], KB[NJ], VB[NJ];
   issue<NJ>(a, ln, block_id(tables, a, ln.pool32, st.P.s, st.P.off), st.hoff, rows_in(st.P.n, st.P.off), KA, VA);
-  while (step<NJ>(tables, a, ln, wk, st, KA, VA, KB, VB, q_lds) &&
-         step<NJ>(tables, a, ln, wk, st, KB, VB, KA, VA, q_lds)) {
+  while (step<NJ, NT, kMulti>(tables, a, ln, wk, st, KA, VA, KB, VB, q_lds) &&
+         step<NJ, NT, kMulti>(tables, a, ln, wk, st, KB, VB, KA, VA, q_lds)) {
   }
 }
 
 // Log-sum-exp merge of the pieces of segments cut by workgroup boundaries.
-// Grid: (num_wgs, heads_per_wg): block (w, k) merges KV head k of the
-// segment that workgroup w's first piece ended, if any. One wavefront per
-// query head of the group; lane i owns head dims [i*D/64, (i+1)*D/64). The
-// pieces are read in one pass with a running rescale.
+// Grid: (num_wgs, heads_per_wg, column tiles of 16): block (w, k, t) merges
+// KV head k's columns 16t.. of the segment that workgroup w's first piece
+// ended, if any. One wavefront per column; lane i owns head dims
+// [i*D/64, (i+1)*D/64). The pieces are read in one pass with a running
+// rescale.
 template <int D>
 __global__ __launch_bounds__(1024) void merge_kernel(const DecodeArgs a) {
   constexpr int PL = D / 64;  // dims per lane: 1 or 2
@@ -642,11 +744,14 @@ __global__ __launch_bounds__(1024) void merge_kernel(const DecodeArgs a) {
   const int2 d = a.merge_desc[w1];
   if (d.x < 0) return;
   const int lane = threadIdx.x & 63;
-  const int c = threadIdx.x >> 6;            // query head within the KV head's group
-  const int wave = blockIdx.y;               // KV head within the head group
+  const int c = (threadIdx.x >> 6) + 16 * blockIdx.z;  // column: new token * group + query head
+  if (c >= a.num_cols) return;
+  const int wave = blockIdx.y;                        // KV head within the head group
   const int s = d.x / a.num_head_groups;
   const int hg = d.x - s * a.num_head_groups;
   const int g = hg * a.heads_per_wg + wave;
+  const int tok = c / a.group;
+  const int qh = c - tok * a.group;
   const int w0 = d.y >> 1;
   const int HG = a.heads_per_wg;
 
@@ -668,7 +773,7 @@ __global__ __launch_bounds__(1024) void merge_kernel(const DecodeArgs a) {
       for (int i = 0; i < PL; ++i) po[k][i] = 0.f;
       if (w + k <= w1) {
         const int rec = w + k == w0 ? d.y : 2 * (w + k);
-        const size_t r = ((size_t)rec * HG + wave) * a.group + c;
+        const size_t r = ((size_t)rec * HG + wave) * a.num_cols + c;
         const f32x2_t ml = *reinterpret_cast<const f32x2_t *>(a.part_ml + r * 2);
         pm[k] = ml[0];
         pl[k] = ml[1];
@@ -679,21 +784,24 @@ __global__ __launch_bounds__(1024) void merge_kernel(const DecodeArgs a) {
     float Mn = M;
 #pragma unroll
     for (int k = 0; k < kPieces; ++k) Mn = fmaxf(Mn, pm[k]);
-    const float so = fast_exp2(M - Mn);
+    // A piece may see no position of a column (several new tokens): its max
+    // is -inf and its weight 0; so is the running max before the first piece.
+    const float Mu = Mn == -INFINITY ? 0.f : Mn;
+    const float so = fast_exp2(M - Mu);
     Lsum *= so;
 #pragma unroll
     for (int i = 0; i < PL; ++i) o[i] *= so;
 #pragma unroll
     for (int k = 0; k < kPieces; ++k) {
-      const float wt = fast_exp2(pm[k] - Mn);  // 0 for the padding (max -inf)
+      const float wt = fast_exp2(pm[k] - Mu);  // 0 for the padding (max -inf)
       Lsum += wt * pl[k];
 #pragma unroll
       for (int i = 0; i < PL; ++i) o[i] += wt * po[k][i];
     }
     M = Mn;
   }
-  const float inv = 1.f / Lsum;
-  uint16_t *dst = a.out + ((size_t)s * a.num_q_heads + (size_t)g * a.group + c) * D + lane * PL;
+  const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
+  uint16_t *dst = a.out + (((size_t)s * a.q_len + tok) * a.num_q_heads + (size_t)g * a.group + qh) * D + lane * PL;
   if constexpr (PL == 2) {
     *reinterpret_cast<uint32_t *>(dst) = to_bf16x2(o[0] * inv, o[1] * inv);
   } else {
@@ -701,23 +809,52 @@ __global__ __launch_bounds__(1024) void merge_kernel(const DecodeArgs a) {
   }
 }
 
+// Lets a kernel use more than 64 KiB of dynamic LDS (gfx950 has 160 KiB per
+// compute unit).
+template <typename Kernel>
+hipError_t allow_lds(Kernel kernel, size_t bytes) {
+  if (bytes <= 48 * 1024) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)bytes);
+}
+
+template <int D, int NT, bool kMulti>
+hipError_t launch_decode_kernel(const DecodeArgs &args, size_t lds, hipStream_t stream) {
+  hipError_t e = allow_lds(decode_kernel<D, NT, kMulti>, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_kernel<D, NT, kMulti>), dim3((unsigned)args.num_wgs),
+                     dim3(64 * (unsigned)args.heads_per_wg), lds, stream, args, args.block_tables,
+                     args.context_lens);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_decode_d(const DecodeArgs &args, size_t lds, hipStream_t stream) {
+  if (args.q_len == 1) return launch_decode_kernel<D, 1, false>(args, lds, stream);
+  if (args.num_cols <= 16) return launch_decode_kernel<D, 1, true>(args, lds, stream);
+  return launch_decode_kernel<D, 2, true>(args, lds, stream);
+}
+
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs &args, int32_t head_size, hipStream_t stream) {
-  const dim3 grid((unsigned)args.num_wgs);
-  const dim3 block(64 * (unsigned)args.heads_per_wg);
-  const size_t lds = (size_t)args.heads_per_wg * 2 * args.group * head_size * sizeof(uint16_t);
+  if (args.q_len < 1 || args.num_cols > 32 || (args.q_len == 1 && args.num_cols > 16)) return hipErrorInvalidValue;
+  // LDS holds q: a two-slot ring per wavefront for the next piece (one column
+  // tile), or the current piece's (two tiles).
+  const size_t lds = (size_t)args.heads_per_wg * (args.num_cols <= 16 ? 2 : 1) * args.num_cols * head_size *
+                     sizeof(uint16_t);
+  hipError_t err;
   if (head_size == 128) {
-    hipLaunchKernelGGL(decode_kernel<128>, grid, block, lds, stream, args, args.block_tables, args.context_lens);
+    err = launch_decode_d<128>(args, lds, stream);
   } else if (head_size == 64) {
-    hipLaunchKernelGGL(decode_kernel<64>, grid, block, lds, stream, args, args.block_tables, args.context_lens);
+    err = launch_decode_d<64>(args, lds, stream);
   } else {
     return hipErrorInvalidValue;
   }
-  hipError_t err = hipGetLastError();
   if (err != hipSuccess || args.num_wgs <= 1) return err;
-  const dim3 mgrid((unsigned)args.num_wgs, (unsigned)args.heads_per_wg);
-  const dim3 mblock(64 * (unsigned)args.group);
+  const unsigned tiles = (unsigned)((args.num_cols + 15) / 16);
+  const dim3 mgrid((unsigned)args.num_wgs, (unsigned)args.heads_per_wg, tiles);
+  const dim3 mblock(64 * (unsigned)(args.num_cols < 16 ? args.num_cols : 16));
   if (head_size == 128) {
     hipLaunchKernelGGL(merge_kernel<128>, mgrid, mblock, 0, stream, args);
   } else {

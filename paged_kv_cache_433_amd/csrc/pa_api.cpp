@@ -94,19 +94,28 @@ int check_decode_shape(const pa_kv_cache *c, int32_t num_seqs, int32_t num_q_hea
   return PA_OK;
 }
 
+// Several new tokens per sequence: their (token, query head) pairs of one KV
+// head must fit two 16-column MFMA tiles.
+int check_q_len(const pa_kv_cache *c, int32_t num_q_heads, int32_t q_len) {
+  if (q_len < 1) return fail(PA_ERR_SHAPE, "q_len must be >= 1");
+  if ((int64_t)q_len * (num_q_heads / c->num_kv_heads) > 32)
+    return fail(PA_ERR_UNSUPPORTED, "q_len * (num_q_heads / num_kv_heads) must be <= 32");
+  return PA_OK;
+}
+
 }  // namespace
 
 namespace pa {
 
 DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                       int32_t head_size, int32_t max_blocks_per_seq) {
+                       int32_t head_size, int32_t max_blocks_per_seq, int32_t q_len) {
   DecodePlan p{};
   p.heads_per_wg = heads_per_workgroup(num_kv_heads);
   p.num_head_groups = num_kv_heads / p.heads_per_wg;
   p.num_wgs = decode_wgs(num_seqs, p.num_head_groups, p.heads_per_wg, max_blocks_per_seq);
   if (p.num_wgs <= 1) return p;
-  const size_t group = (size_t)(num_q_heads / num_kv_heads);
-  const size_t rows = (size_t)p.num_wgs * 2 * p.heads_per_wg * group;
+  const size_t cols = (size_t)q_len * (num_q_heads / num_kv_heads);
+  const size_t rows = (size_t)p.num_wgs * 2 * p.heads_per_wg * cols;
   p.desc_bytes = round_up((size_t)p.num_wgs * sizeof(int2), 256);
   p.ml_bytes = round_up(rows * 2 * sizeof(float), 256);
   p.o_bytes = round_up(rows * head_size * sizeof(float), 256);
@@ -122,10 +131,16 @@ const char *pa_last_error(void) { return g_error.c_str(); }
 
 size_t pa_decode_workspace_bytes(const pa_kv_cache *cache, int32_t num_seqs, int32_t num_q_heads,
                                  int32_t max_blocks_per_seq) {
+  return pa_decode_multi_workspace_bytes(cache, num_seqs, 1, num_q_heads, max_blocks_per_seq);
+}
+
+size_t pa_decode_multi_workspace_bytes(const pa_kv_cache *cache, int32_t num_seqs, int32_t q_len,
+                                       int32_t num_q_heads, int32_t max_blocks_per_seq) {
   if (check_cache(cache, false) != PA_OK) return 0;
   if (check_decode_shape(cache, num_seqs, num_q_heads, max_blocks_per_seq) != PA_OK) return 0;
+  if (check_q_len(cache, num_q_heads, q_len) != PA_OK) return 0;
   return pa::plan_decode(num_seqs, num_q_heads, cache->num_kv_heads, cache->head_size,
-                         max_blocks_per_seq)
+                         max_blocks_per_seq, q_len)
       .total_bytes;
 }
 
@@ -133,16 +148,26 @@ int pa_decode(const pa_kv_cache *cache, const void *q, const int32_t *block_tabl
               const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
               int32_t max_blocks_per_seq, float scale, void *out, void *workspace,
               size_t workspace_bytes, void *stream) {
+  return pa_decode_multi(cache, q, block_tables, context_lens, num_seqs, 1, num_q_heads, max_blocks_per_seq,
+                         scale, out, workspace, workspace_bytes, stream);
+}
+
+int pa_decode_multi(const pa_kv_cache *cache, const void *q, const int32_t *block_tables,
+                    const int32_t *context_lens, int32_t num_seqs, int32_t q_len, int32_t num_q_heads,
+                    int32_t max_blocks_per_seq, float scale, void *out, void *workspace,
+                    size_t workspace_bytes, void *stream) {
   int rc = check_cache(cache, num_seqs > 0);
   if (rc != PA_OK) return rc;
   rc = check_decode_shape(cache, num_seqs, num_q_heads, max_blocks_per_seq);
+  if (rc != PA_OK) return rc;
+  rc = check_q_len(cache, num_q_heads, q_len);
   if (rc != PA_OK) return rc;
   if (num_seqs == 0) return ok();
   if (!q || !block_tables || !context_lens || !out)
     return fail(PA_ERR_NULL, "q, block_tables, context_lens or out is NULL");
 
   const pa::DecodePlan plan = pa::plan_decode(num_seqs, num_q_heads, cache->num_kv_heads,
-                                              cache->head_size, max_blocks_per_seq);
+                                              cache->head_size, max_blocks_per_seq, q_len);
   if (workspace && workspace_bytes < plan.total_bytes)
     return fail(PA_ERR_WORKSPACE, "workspace smaller than pa_decode_workspace_bytes()");
   if (workspace && reinterpret_cast<uintptr_t>(workspace) % 16)
@@ -175,6 +200,8 @@ int pa_decode(const pa_kv_cache *cache, const void *q, const int32_t *block_tabl
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = cache->num_kv_heads;
   a.group = num_q_heads / cache->num_kv_heads;
+  a.q_len = q_len;
+  a.num_cols = q_len * a.group;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.heads_per_wg = plan.heads_per_wg;
   a.num_head_groups = plan.num_head_groups;

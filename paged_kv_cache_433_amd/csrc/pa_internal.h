@@ -10,20 +10,22 @@ namespace pa {
 
 // Arguments of one decode launch, passed by value as the kernel argument.
 struct DecodeArgs {
-  const uint16_t *q;             // bf16 [S, Hq, D]
+  const uint16_t *q;             // bf16 [S, q_len, Hq, D]
   const uint16_t *k_cache;       // bf16 [NB, 16, Hkv, D]
   const uint16_t *v_cache;
   const int32_t *block_tables;   // [S, MB]
   const int32_t *context_lens;   // [S]
-  uint16_t *out;                 // bf16 [S, Hq, D]
+  uint16_t *out;                 // bf16 [S, q_len, Hq, D]
   int2 *merge_desc;              // [num_wgs]: segment ended by the workgroup's first piece, or -1
-  float *part_ml;                // [2 * num_wgs, heads_per_wg, group, 2]: max (base 2), sum
-  float *part_o;                 // [2 * num_wgs, heads_per_wg, group, D]: unnormalised output
+  float *part_ml;                // [2 * num_wgs, heads_per_wg, num_cols, 2]: max (base 2), sum
+  float *part_o;                 // [2 * num_wgs, heads_per_wg, num_cols, D]: unnormalised output
   int64_t num_blocks;
   int32_t num_seqs;
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t group;                 // Hq / Hkv, <= 16
+  int32_t q_len;                 // new tokens per sequence (1: decode)
+  int32_t num_cols;              // q_len * group, <= 32 (<= 16 when q_len == 1)
   int32_t max_blocks_per_seq;
   int32_t heads_per_wg;          // KV heads per workgroup (one wavefront each), <= 8
   int32_t num_head_groups;       // Hkv / heads_per_wg
@@ -43,7 +45,7 @@ struct DecodePlan {
 };
 
 DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                       int32_t head_size, int32_t max_blocks_per_seq);
+                       int32_t head_size, int32_t max_blocks_per_seq, int32_t q_len);
 
 hipError_t launch_decode(const DecodeArgs &args, int32_t head_size, hipStream_t stream);
 

@@ -103,6 +103,33 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=None, wor
     return out
 
 
+def decode_multi(q, k_cache, v_cache, block_tables, context_lens, scale, out=None, workspace=None):
+    """Causal attention of several new tokens per sequence; returns ``out``.
+
+    ``q``: bf16 ``[num_seqs, q_len, num_q_heads, head_size]``; new token j of
+    a sequence with context length n attends over positions 0..n-q_len+j.
+    The new tokens must be in the cache already (``reshape_and_cache``).
+    """
+    desc = _cache_desc(k_cache, v_cache)
+    dev = k_cache.device
+    S, ql, hq, d = q.shape
+    _need(q, "q", _BF16, (S, ql, hq, k_cache.shape[3]), dev)
+    mb = block_tables.shape[1] if block_tables.dim() == 2 else -1
+    _need(block_tables, "block_tables", torch.int32, (S, mb), dev)
+    _need(context_lens, "context_lens", torch.int32, (S,), dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", _BF16, (S, ql, hq, d), dev)
+    lib = _lib.lib()
+    nbytes = int(lib.pa_decode_multi_workspace_bytes(ctypes.byref(desc), S, ql, hq, mb))
+    if workspace is None and nbytes:
+        workspace = _workspace(dev, nbytes)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.pa_decode_multi(ctypes.byref(desc), _ptr(q), _ptr(block_tables), _ptr(context_lens), S, ql, hq,
+                               mb, float(scale), _ptr(out), _ptr(workspace), ws_bytes, _stream(dev)))
+    return out
+
+
 def reshape_and_cache(k, v, k_cache, v_cache, slot_mapping) -> None:
     """Scatter new tokens' K/V (bf16 ``[T, num_kv_heads, head_size]``) into
     their slots (int64 ``[T]``; negative = skip), in place, on the current stream."""

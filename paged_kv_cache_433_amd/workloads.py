@@ -350,20 +350,22 @@ CONFIG_SHAPES = {
 }
 
 
-def make_config(name: str, seed: int | None = None) -> DecodeBatch:
-    """Build one of the named decode configs (the CoW config has its own class)."""
+def make_config(name: str, seed: int | None = None, q_len: int = 1) -> DecodeBatch:
+    """Build one of the named decode configs (the CoW config has its own
+    class); ``q_len`` > 1 makes the newest q_len tokens of each sequence new."""
     hq, hkv, d, nb, mb, default_seed = CONFIG_SHAPES[name]
     seed = default_seed if seed is None else seed
-    return make_batch(name, seed, config_lens(name, seed), hq, hkv, d, nb, mb)
+    return make_batch(name, seed, config_lens(name, seed), hq, hkv, d, nb, mb, q_len=q_len)
 
 
 def algorithmic_bytes(context_lens, num_q_heads, num_kv_heads, head_size,
-                      block_size=BLOCK_SIZE, dtype_bytes=2) -> int:
+                      block_size=BLOCK_SIZE, dtype_bytes=2, q_len=1) -> int:
     """Bytes a decode step must move: K and V of every cached token, q in,
-    out back, the used block-table entries and the context lengths."""
+    out back (q_len rows of each per sequence), the used block-table entries
+    and the context lengths."""
     n = np.asarray(context_lens, dtype=np.int64)
     kv = int(n.sum()) * 2 * num_kv_heads * head_size * dtype_bytes
-    qo = len(n) * 2 * num_q_heads * head_size * dtype_bytes
+    qo = len(n) * q_len * 2 * num_q_heads * head_size * dtype_bytes
     tables = int(((n + block_size - 1) // block_size).sum()) * 4
     return kv + qo + tables + 4 * len(n)
 

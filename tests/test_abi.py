@@ -101,6 +101,21 @@ def test_workspace_size_and_check(L, monkeypatch):
     assert L.pa_decode_workspace_bytes(ctypes.byref(d), 256, 32, 256) >= 3 * 2 * hg * grp * 130 * 4
 
 
+def test_decode_multi_limits(L):
+    d = desc()                                     # 8 KV heads of 128
+    M = L.pa_decode_multi
+    # 4 new tokens x 8 query heads per KV head = 32 columns: supported
+    assert L.pa_decode_multi_workspace_bytes(ctypes.byref(d), 256, 4, 64, 256) > 0
+    # 5 x 8 = 40 columns: refused before anything runs
+    assert L.pa_decode_multi_workspace_bytes(ctypes.byref(d), 256, 5, 64, 256) == 0
+    assert M(ctypes.byref(d), P, P, P, 4, 5, 64, 16, 1.0, P, None, 0, None) == _lib.PA_ERR_UNSUPPORTED
+    assert M(ctypes.byref(d), P, P, P, 4, 0, 64, 16, 1.0, P, None, 0, None) == _lib.PA_ERR_SHAPE
+    assert M(ctypes.byref(d), None, P, P, 4, 2, 64, 16, 1.0, P, None, 0, None) == _lib.PA_ERR_NULL
+    # q_len = 1 needs the same workspace as pa_decode
+    assert (L.pa_decode_multi_workspace_bytes(ctypes.byref(d), 256, 1, 32, 256)
+            == L.pa_decode_workspace_bytes(ctypes.byref(d), 256, 32, 256))
+
+
 def test_cache_op_argument_errors(L):
     d = desc()
     assert L.pa_reshape_and_cache(None, P, P, P, 1, None) == _lib.PA_ERR_NULL

@@ -1,0 +1,85 @@
+"""GPU parity of pa_decode_multi: several new tokens per sequence, causal
+(speculative-decode verification, prefill chunks), against the float64
+oracle's decode_multi, across head shapes, column-tile counts and work
+splits, including contexts made only of new tokens and empty sequences."""
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import assert_attention_close, bits_of, note, to_dev, to_dev_bf16
+from paged_kv_cache_433_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+LENS = [4, 5, 16, 17, 31, 33, 64, 100, 129, 300, 1000]
+
+
+def run_multi(b, what):
+    import paged_kv_cache_433_amd as pa
+    note(what)
+    kd, vd = to_dev_bf16(b.k_cache), to_dev_bf16(b.v_cache)
+    pa.reshape_and_cache(to_dev_bf16(b.new_k), to_dev_bf16(b.new_v), kd, vd, to_dev(b.slot_mapping))
+    out = bits_of(pa.decode_multi(to_dev_bf16(b.q), kd, vd, to_dev(b.block_tables), to_dev(b.context_lens),
+                                  float(b.scale)))
+    kc, vc = b.k_cache.copy(), b.v_cache.copy()
+    oracle.reshape_and_cache(kc, vc, b.new_k, b.new_v, b.slot_mapping)
+    ref = oracle.decode_multi(b.q, kc, vc, b.block_tables, b.context_lens, b.scale)
+    return assert_attention_close(out, ref, what), out
+
+
+@pytest.mark.parametrize("ql,hq,hkv,d", [(2, 32, 8, 128), (4, 32, 8, 128), (3, 8, 8, 64), (5, 16, 4, 64),
+                                         (8, 8, 2, 128), (4, 4, 4, 128), (32, 1, 1, 64)])
+def test_multi_token_across_work_splits(ql, hq, hkv, d, monkeypatch):
+    lens = [max(n, ql) for n in LENS]
+    nb = int(sum((n + 15) // 16 for n in lens)) + 9
+    b = W.make_batch("multi", 500 + ql * 10 + hq + d, lens, hq, hkv, d, nb, q_len=ql)
+    for wgs in ("1", "5", "default"):
+        if wgs == "default":
+            monkeypatch.delenv("PA_DECODE_WGS", raising=False)
+        else:
+            monkeypatch.setenv("PA_DECODE_WGS", wgs)
+        run_multi(b, f"multi ql={ql} hq={hq} hkv={hkv} d={d} wgs={wgs}")
+
+
+def test_multi_token_prefill_chunk_and_empty_sequences():
+    """Every token of the first sequence is new (a prefill chunk from
+    position 0): its first token sees only itself. An empty sequence gives
+    a zero output."""
+    b = W.make_batch("multi", 777, [6, 40, 6], 8, 2, 64, 8, q_len=6)
+    b.context_lens[2] = 0
+    r, out = run_multi(b, "multi prefill chunk + empty sequence")
+    assert np.all(out[2] == 0)
+
+
+def test_single_new_token_equals_decode():
+    """q_len = 1 through pa_decode_multi is pa_decode, bit for bit."""
+    import paged_kv_cache_433_amd as pa
+    b = W.make_batch("multi", 778, LENS, 32, 8, 128, 200)
+    note("multi q_len=1 vs decode")
+    kd, vd = to_dev_bf16(b.k_cache), to_dev_bf16(b.v_cache)
+    pa.reshape_and_cache(to_dev_bf16(b.new_k), to_dev_bf16(b.new_v), kd, vd, to_dev(b.slot_mapping))
+    q = to_dev_bf16(b.q)
+    tabs, lens = to_dev(b.block_tables), to_dev(b.context_lens)
+    one = pa.decode(q, kd, vd, tabs, lens, float(b.scale))
+    multi = pa.decode_multi(q[:, None], kd, vd, tabs, lens, float(b.scale))
+    assert np.array_equal(bits_of(one), bits_of(multi[:, 0]))
+
+
+def test_multi_token_gqa_layer_full_size():
+    """The Llama-3-8B-shaped GQA layer verifying 3 speculative tokens (4 new
+    tokens per sequence, 32 columns per KV head), default split, on a
+    sample of sequences."""
+    b = W.make_batch("llama3_8b_gqa_q4", 3, W.config_lens("llama3_8b_gqa", 3), 32, 8, 128, 65536,
+                     max_blocks_per_seq=256, q_len=4)
+    import paged_kv_cache_433_amd as pa
+    note("multi gqa full size q_len=4")
+    kd, vd = to_dev_bf16(b.k_cache), to_dev_bf16(b.v_cache)
+    pa.reshape_and_cache(to_dev_bf16(b.new_k), to_dev_bf16(b.new_v), kd, vd, to_dev(b.slot_mapping))
+    out = bits_of(pa.decode_multi(to_dev_bf16(b.q), kd, vd, to_dev(b.block_tables), to_dev(b.context_lens),
+                                  float(b.scale)))
+    oracle.reshape_and_cache(b.k_cache, b.v_cache, b.new_k, b.new_v, b.slot_mapping)
+    rng = np.random.default_rng(4321)
+    idx = np.sort(rng.choice(b.num_seqs, 24, replace=False))
+    ref = oracle.decode_multi(b.q[idx], b.k_cache, b.v_cache, b.block_tables[idx], b.context_lens[idx], b.scale)
+    assert_attention_close(out[idx], ref, "multi gqa full size")
