@@ -19,7 +19,10 @@ passage it follows:
   earlier K/V vector already cached) and section "LLM Engine constructor"
   (per-block size 2 * block_size * num_kv_heads * head_size * dtype bytes);
 * "vLLM Internals", section "The Block Manager" (per-request block tables;
-  a preempted request's blocks are swapped to CPU and back).
+  a preempted request's blocks are swapped to CPU and back);
+* "vLLM: Anatomy and Mechanisms", section "Prefix Caching" (prompts with a
+  common beginning reuse the cached blocks), read with the CoW section for
+  ``decode_shared``.
 
 Pins: every function here is checked in ``tests/test_oracle_pins.py``
 against facts the pages or mathematics fix (a library routine on the dense
@@ -32,6 +35,7 @@ from .paged_attention import (  # noqa: F401
     copy_blocks,
     decode,
     decode_multi,
+    decode_shared,
     decode_sequence,
     reshape_and_cache,
     swap_blocks,

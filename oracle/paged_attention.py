@@ -114,6 +114,48 @@ def decode_multi(q, k_cache, v_cache, block_tables, context_lens, scale) -> np.n
     return out
 
 
+def decode_shared(q, k_cache, v_cache, block_tables, context_lens, group_starts, shared_blocks,
+                  scale) -> np.ndarray:
+    """Decode attention of a batch whose sequences share leading blocks.
+
+    Several sequences can hold the same physical blocks at the start of their
+    tables: the outputs of parallel sampling share the prompt's blocks, beams
+    share their common history ("vLLM: Anatomy and Mechanisms", section
+    "Memory Sharing via Copy-on-Write (CoW)"), and prompts with a common
+    beginning reuse cached blocks (section "Prefix Caching"). A caller that
+    knows this declares it: group ``g`` is the sequences
+    ``group_starts[g] <= i < group_starts[g + 1]``, and their tables agree on
+    the first ``shared_blocks[g]`` entries. ``group_starts`` has one entry
+    more than ``shared_blocks``, never decreases, and stays within
+    ``0..num_seqs``; a sequence in no group is on its own.
+
+    Reading (the pages define the sharing, not a call that uses it): the
+    declared prefix of group ``g`` counts only whole blocks that every member
+    fills, ``e = min(shared_blocks[g], n_j // block_size for each member j)``
+    (clamped to ``0..max_blocks_per_seq``), and every member reads those
+    ``e`` blocks through the table of the group's first member, the rest
+    through its own. When the declaration is true the tables agree there and
+    the result is ``decode``'s. Returns float64 ``[num_seqs, num_q_heads,
+    head_size]``.
+    """
+    block_size = k_cache.shape[1]
+    starts = np.asarray(group_starts, dtype=np.int64)
+    shared = np.asarray(shared_blocks, dtype=np.int64)
+    num_seqs = np.asarray(q).shape[0]
+    assert starts.ndim == 1 and len(starts) == len(shared) + 1
+    assert np.all(np.diff(starts) >= 0) and starts[0] >= 0 and starts[-1] <= num_seqs
+    tables = np.array(block_tables, copy=True)
+    for g in range(len(shared)):
+        lo, hi = int(starts[g]), int(starts[g + 1])
+        if hi <= lo:
+            continue
+        full = min(int(context_lens[j]) // block_size for j in range(lo, hi))
+        e = max(0, min(int(shared[g]), full, tables.shape[1]))
+        for j in range(lo + 1, hi):
+            tables[j, :e] = block_tables[lo, :e]
+    return decode(q, k_cache, v_cache, tables, context_lens, scale)
+
+
 def reshape_and_cache(k_cache, v_cache, k, v, slot_mapping) -> None:
     """Scatter each new token's K and V into its physical slot, in place.
 

@@ -309,6 +309,96 @@ def sequence_kv(batch: DecodeBatch, s: int):
 
 
 # ----------------------------------------------------------------------------
+# groups of sequences that share leading blocks
+# ----------------------------------------------------------------------------
+
+
+def consecutive_groups(num_seqs: int, group_size: int) -> np.ndarray:
+    """``group_starts`` for groups of ``group_size`` consecutive sequences (the
+    last one may be shorter): int32 ``[ceil(num_seqs / group_size) + 1]``."""
+    return np.array(list(range(0, num_seqs, group_size)) + [num_seqs], dtype=np.int32)
+
+
+def declared_sharing(block_tables, context_lens, group_starts, block_size=BLOCK_SIZE) -> np.ndarray:
+    """Leading blocks each group's members hold in common: int32 ``[G]``.
+
+    A block manager knows this from its reference counts; here it is read
+    back from the tables: the run of equal leading entries, counting only
+    blocks every member of the group fills.
+    """
+    out = []
+    for lo, hi in zip(group_starts[:-1], group_starts[1:]):
+        lo, hi = int(lo), int(hi)
+        if hi <= lo:
+            out.append(0)
+            continue
+        full = min(int(context_lens[j]) // block_size for j in range(lo, hi))
+        rows = np.asarray(block_tables)[lo:hi, :full]
+        same = np.all(rows == rows[0], axis=0)
+        out.append(full if same.all() else int(np.argmin(same)))
+    return np.array(out, dtype=np.int32)
+
+
+def make_shared_batch(name, seed, group_sizes, prefix_lens, private_lens, num_q_heads, num_kv_heads,
+                      head_size, num_blocks, block_size=BLOCK_SIZE):
+    """A decode batch whose sequences come in groups that share a prompt.
+
+    Group g's ``group_sizes[g]`` members fork one prompt of ``prefix_lens[g]``
+    tokens; then member i (counted over the whole batch) appends its own
+    ``private_lens[i]`` tokens, and a shared partial last block is copied
+    before the first append into it (copy-on-write). Every token is cached
+    already: ``new_k``/``new_v``/``slot_mapping`` are empty.
+
+    Draw order for ``seed``: stream (seed, 0) shuffles the pool, (seed, 1, g)
+    draws group g's prompt K then V, (seed, 4, i) member i's private K then
+    V, (seed, 2) q. Returns ``(batch, group_starts, shared_blocks)``, the
+    sharing read back from the tables by ``declared_sharing``.
+    """
+    S = int(sum(group_sizes))
+    assert len(prefix_lens) == len(group_sizes) and len(private_lens) == S
+    pool = BlockPool(num_blocks, _rng(seed, 0).permutation(num_blocks))
+    shape = (num_blocks, block_size, num_kv_heads, head_size)
+    k_cache = np.full(shape, BF16_QNAN, dtype=np.uint16)
+    v_cache = np.full(shape, BF16_QNAN, dtype=np.uint16)
+    seqs = []
+    for g, (m, plen) in enumerate(zip(group_sizes, prefix_lens)):
+        prompt = allocate_prefix(pool, int(plen), block_size)
+        r = _rng(seed, 1, g)
+        kb = normal_bf16(r, (int(plen), num_kv_heads, head_size))
+        vb = normal_bf16(r, (int(plen), num_kv_heads, head_size))
+        _fill_sequence(k_cache, v_cache, prompt.table, kb, vb, block_size)
+        for b in range(int(m)):
+            seqs.append(prompt.fork(pool) if b < m - 1 else prompt)
+        if m == 0:
+            prompt.release(pool)
+    for i, sq in enumerate(seqs):
+        m = int(private_lens[i])
+        r = _rng(seed, 4, i)
+        kb = normal_bf16(r, (m, num_kv_heads, head_size))
+        vb = normal_bf16(r, (m, num_kv_heads, head_size))
+        for t in range(m):
+            slot, cow = append_token(pool, sq, block_size)
+            if cow is not None:
+                k_cache[cow[1]] = k_cache[cow[0]]
+                v_cache[cow[1]] = v_cache[cow[0]]
+            blk, off = divmod(slot, block_size)
+            k_cache[blk, off] = kb[t]
+            v_cache[blk, off] = vb[t]
+    lens = np.array([sq.length for sq in seqs], dtype=np.int32)
+    MB = max(1, max(len(sq.table) for sq in seqs))
+    tables = np.full((S, MB), num_blocks + TABLE_PAD_OFFSET, dtype=np.int32)
+    for s, sq in enumerate(seqs):
+        tables[s, : len(sq.table)] = sq.table
+    q = normal_bf16(_rng(seed, 2), (S, num_q_heads, head_size))
+    empty = np.zeros((0, num_kv_heads, head_size), dtype=np.uint16)
+    batch = DecodeBatch(name, seed, num_blocks, block_size, num_q_heads, num_kv_heads, head_size,
+                        np.float32(1.0 / math.sqrt(head_size)), tables, lens, q, k_cache, v_cache,
+                        empty, empty.copy(), np.zeros(0, dtype=np.int64), np.zeros((0, 2), dtype=np.int64))
+    starts = np.cumsum([0] + list(group_sizes)).astype(np.int32)
+    return batch, starts, declared_sharing(tables, lens, starts, block_size)
+
+
+# ----------------------------------------------------------------------------
 # the five named workloads
 # ----------------------------------------------------------------------------
 

@@ -357,6 +357,79 @@ def pin_multi_token_prefill_start(orc):
     assert np.all(orc.decode_multi(zero.q, zero.k_cache, zero.v_cache, zero.block_tables, zl, zero.scale) == 0)
 
 
+SHARED_CASES = [
+    # seed, group sizes, prompt lengths, private lengths, Hq, Hkv, D
+    (51, [3, 1, 2, 0, 4], [40, 16, 0, 5, 35], [5, 0, 17, 9, 3, 20, 0, 1, 2, 3], 8, 2, 16),
+    (52, [5], [33], [1, 2, 0, 16, 31], 4, 4, 8),
+]
+
+
+def pin_shared_equals_dense(orc):
+    """Where the declared blocks really are shared, sharing-aware decode is
+    torch's dense attention (fp64, CPU) over each sequence's K/V gathered by
+    hand through its own table; declaring less sharing changes nothing."""
+    for seed, sizes, plens, privs, hq, hkv, d in SHARED_CASES:
+        nb = sum((p + 15) // 16 for p in plens) + sum((x + 16) // 16 for x in privs) + 9
+        b, starts, shared = W.make_shared_batch("pin", seed, sizes, plens, privs, hq, hkv, d, nb)
+        assert shared.max() > 0
+        got = orc.decode_shared(b.q, b.k_cache, b.v_cache, b.block_tables, b.context_lens, starts, shared, b.scale)
+        assert got.shape == b.q.shape and got.dtype == np.float64
+        for s, n in enumerate(b.context_lens):
+            if n == 0:
+                assert np.all(got[s] == 0)
+                continue
+            slots = table_slots(b.block_tables[s], int(n))
+            kb = np.stack([b.k_cache[blk, off] for blk, off in slots])   # [n, Hkv, D]
+            vb = np.stack([b.v_cache[blk, off] for blk, off in slots])
+            k = torch.from_numpy(widen(kb)).permute(1, 0, 2).repeat_interleave(hq // hkv, 0)
+            v = torch.from_numpy(widen(vb)).permute(1, 0, 2).repeat_interleave(hq // hkv, 0)
+            q = torch.from_numpy(widen(b.q[s]))[:, None, :]
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                q[None], k[None].contiguous(), v[None].contiguous(), scale=float(b.scale))[0, :, 0]
+            err = np.abs(got[s] - ref.numpy()).max()
+            assert err <= 1e-12, (seed, s, err)
+        less = orc.decode_shared(b.q, b.k_cache, b.v_cache, b.block_tables, b.context_lens, starts,
+                                 np.maximum(shared - 1, 0), b.scale)
+        assert np.array_equal(less, got)
+
+
+def _constant_v_cache(num_blocks, d=8):
+    """K all zero (every logit 0, so attention is the plain mean of the
+    visible V rows); every element of block b's V is b + 1."""
+    kc = np.zeros((num_blocks, 16, 1, d), dtype=np.uint16)
+    vc = np.stack([np.full((16, 1, d), bf16(b + 1.0)[()], dtype=np.uint16) for b in range(num_blocks)])
+    return kc, vc
+
+
+def pin_shared_reads_leader_prefix(orc):
+    """A member reads the declared prefix through the table of its group's
+    first member, even where its own table differs; a sequence outside
+    the group reads its own. Closed form: means of constant V blocks."""
+    kc, vc = _constant_v_cache(6)
+    tables = np.array([[0], [1], [2]], dtype=np.int32)
+    lens = np.array([16, 16, 16], dtype=np.int32)
+    q = bf16(np.random.default_rng(3).normal(size=(3, 1, 8)))
+    out = orc.decode_shared(q, kc, vc, tables, lens, np.array([0, 2]), np.array([1]), np.float32(1.0))
+    assert np.allclose(out[:, 0, :], np.array([1.0, 1.0, 3.0])[:, None], rtol=0, atol=1e-12), out[:, 0, 0]
+
+
+def pin_shared_prefix_clamped(orc):
+    """The declared prefix counts only whole blocks every member fills, and
+    never less than none. Group [0, 2) declares 3 blocks, but member 1 fills
+    only 1 (20 tokens): it reads block 0 through the leader (V = 1) and
+    positions 16..19 through its own block 4 (V = 5): (16 + 4*5)/20 = 1.8.
+    The leader reads its own blocks 0, 2, 3: (16*1 + 16*3 + 8*4)/40 = 2.4.
+    Group [2, 4) declares -1 blocks: each member reads its own (6 and 5)."""
+    kc, vc = _constant_v_cache(6)
+    pad = 6 + 12345
+    tables = np.array([[0, 2, 3], [1, 4, pad], [5, pad, pad], [4, pad, pad]], dtype=np.int32)
+    lens = np.array([40, 20, 16, 16], dtype=np.int32)
+    q = bf16(np.random.default_rng(4).normal(size=(4, 1, 8)))
+    out = orc.decode_shared(q, kc, vc, tables, lens, np.array([0, 2, 4]), np.array([3, -1]), np.float32(1.0))
+    want = np.array([2.4, 1.8, 6.0, 5.0])
+    assert np.allclose(out[:, 0, :], want[:, None], rtol=0, atol=1e-12), out[:, 0, 0]
+
+
 def pin_widening(orc):
     """bfloat16 patterns widen to the float32 of the same bits: checks a few
     patterns with known values (1, -2, 0.5, smallest normal, largest)."""
@@ -384,5 +457,8 @@ ALL_PINS = [
     pin_swap_blocks,
     pin_multi_token_causal_sdpa,
     pin_multi_token_prefill_start,
+    pin_shared_equals_dense,
+    pin_shared_reads_leader_prefix,
+    pin_shared_prefix_clamped,
     pin_widening,
 ]

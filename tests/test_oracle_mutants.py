@@ -32,6 +32,15 @@ MUTANTS = {
     "new tokens in reverse order": ("decode_sequence(q[s, j], k_cache", "decode_sequence(q[s, q_len - 1 - j], k_cache"),
     "swap direction ignored": ('if direction == "out":', 'if direction != "out":'),
     "swap copies K into V": ("tv[d_] = fv[s_]", "tv[d_] = fk[s_]"),
+    "shared prefix read through own table": ("tables[j, :e] = block_tables[lo, :e]",
+                                             "tables[j, :e] = block_tables[j, :e]"),
+    "shared prefix not clamped to members": ("e = max(0, min(int(shared[g]), full, tables.shape[1]))",
+                                             "e = max(0, min(int(shared[g]), tables.shape[1]))"),
+    "shared prefix counts partial blocks": ("full = min(int(context_lens[j]) // block_size",
+                                            "full = min(-(-int(context_lens[j]) // block_size)"),
+    "negative shared prefix not clamped": ("e = max(0, min(int(shared[g]), full, tables.shape[1]))",
+                                           "e = min(int(shared[g]), full, tables.shape[1])"),
+    "group end taken inclusive": ("for j in range(lo + 1, hi):", "for j in range(lo + 1, hi + 1):"),
     "query heads transposed": ("qf = bf16_bits_to_f64(q_s)", "qf = bf16_bits_to_f64(q_s)[::-1]"),
 }
 
