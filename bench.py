@@ -40,6 +40,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 CACHE_NOTES = {
     "tiny_mha": "warm: the whole cache fits in L2",
     "beam_cow": "warm in part: the 4 beams of a prompt read its shared blocks, so some logical bytes come from cache",
+    "beam_cow_shared": "cold in part: every distinct K/V byte is read once per call (about 0.37 GB; the MALL is 256 MB)",
 }
 
 
@@ -122,9 +123,11 @@ def record_traffic(prefix: str, workload: str, copy_bytes: int) -> int:
     return 0
 
 
-def _time_oracle(batch, kc, vc, order, seconds: float, threads: int):
+def _time_oracle(batch, kc, vc, order, seconds: float, threads: int, groups=None):
     """Run the oracle on whole sequences of `order` (cycling) for `seconds`
-    with BLAS limited to `threads`; returns (sequences done, seconds)."""
+    with BLAS limited to `threads`; returns (sequences done, seconds). With
+    `groups` = (group_starts, shared_blocks), `order` lists groups and each
+    is decoded whole by the oracle's decode_shared."""
     from threadpoolctl import threadpool_limits
 
     import oracle
@@ -134,6 +137,15 @@ def _time_oracle(batch, kc, vc, order, seconds: float, threads: int):
         t0 = time.perf_counter()
         while time.perf_counter() - t0 < seconds:
             for s in order:
+                if groups is not None:
+                    starts, shared = groups
+                    lo, hi = int(starts[s]), int(starts[s + 1])
+                    oracle.decode_shared(batch.q[lo:hi], kc, vc, batch.block_tables[lo:hi],
+                                         batch.context_lens[lo:hi], [0, hi - lo], [shared[s]], batch.scale)
+                    done.append(int(s))
+                    if time.perf_counter() - t0 >= seconds:
+                        break
+                    continue
                 if batch.q_len > 1:
                     oracle.decode_multi(batch.q[s:s + 1], kc, vc, batch.block_tables[s:s + 1],
                                         batch.context_lens[s:s + 1], batch.scale)
@@ -147,11 +159,12 @@ def _time_oracle(batch, kc, vc, order, seconds: float, threads: int):
     return done, dt
 
 
-def cpu_baseline(batch, seconds: float):
-    """Time the float64 oracle on whole sequences, in a seeded order (cycling
-    through the batch), for `seconds` with BLAS on every core this process may
-    use and again on one thread; rate in the metric's unit (algorithmic GB/s).
-    The multi-core run is the reported value."""
+def cpu_baseline(batch, seconds: float, groups=None):
+    """Time the float64 oracle on whole sequences (whole groups, with
+    `groups`), in a seeded order (cycling through the batch), for `seconds`
+    with BLAS on every core this process may use and again on one thread;
+    rate in the metric's unit (algorithmic GB/s). The multi-core run is the
+    reported value."""
     import numpy as np
 
     import oracle
@@ -161,7 +174,8 @@ def cpu_baseline(batch, seconds: float):
     if len(batch.cow_pairs):
         oracle.copy_blocks(kc, vc, batch.cow_pairs)
     oracle.reshape_and_cache(kc, vc, batch.new_k, batch.new_v, batch.slot_mapping)
-    order = np.random.default_rng(0).permutation(batch.num_seqs)
+    units = batch.num_seqs if groups is None else len(groups[1])
+    order = np.random.default_rng(0).permutation(units)
     # The host share this process may use: its CPU affinity, capped by the
     # thread count the environment sets for OpenMP/BLAS.
     cores = len(os.sched_getaffinity(0))
@@ -169,11 +183,24 @@ def cpu_baseline(batch, seconds: float):
         cores = max(1, min(cores, int(os.environ["OMP_NUM_THREADS"])))
     res = {}
     for threads in (cores, 1):
-        done, dt = _time_oracle(batch, kc, vc, order, seconds, threads)
-        lens = batch.context_lens[done]
-        nbytes = W.algorithmic_bytes(lens, batch.num_q_heads, batch.num_kv_heads, batch.head_size,
-                                     q_len=batch.q_len)
-        res[threads] = (len(done), int(lens.sum()), dt, nbytes / dt / 1e9, len(done) / dt)
+        done, dt = _time_oracle(batch, kc, vc, order, seconds, threads, groups)
+        if groups is None:
+            lens = batch.context_lens[done]
+            nbytes = W.algorithmic_bytes(lens, batch.num_q_heads, batch.num_kv_heads, batch.head_size,
+                                         q_len=batch.q_len)
+            seqs = len(done)
+        else:
+            starts, shared = groups
+            nbytes, seqs, toks = 0, 0, 0
+            for g in done:
+                lo, hi = int(starts[g]), int(starts[g + 1])
+                nbytes += W.shared_algorithmic_bytes(batch.context_lens[lo:hi], [0, hi - lo], [shared[g]],
+                                                     batch.max_blocks_per_seq, batch.num_q_heads,
+                                                     batch.num_kv_heads, batch.head_size)
+                seqs += hi - lo
+                toks += int(batch.context_lens[lo:hi].sum())
+            lens = np.array([toks])
+        res[threads] = (seqs, int(lens.sum()), dt, nbytes / dt / 1e9, seqs / dt)
     n, tokens, dt, gbps, sps = res[cores]
     return {
         "value": round(gbps, 4),
@@ -181,7 +208,8 @@ def cpu_baseline(batch, seconds: float):
         "cores": cores,
         "kind": "oracle",
         "sample": (f"{n} sequence-steps of the {batch.num_seqs}-sequence batch, taken in a seeded "
-                   f"order ({tokens} tokens), float64 numpy oracle, BLAS limited to {cores} threads "
+                   f"order{' of whole groups (decode_shared)' if groups is not None else ''} ({tokens} tokens), "
+                   f"float64 numpy oracle, BLAS limited to {cores} threads "
                    f"(the gather and exp are single-threaded numpy), {dt:.1f} s"),
         "seq_steps_per_s": round(sps, 3),
         "single_thread": {"value": round(res[1][3], 4), "unit": "GB/s", "seq_steps_per_s": round(res[1][4], 3),
@@ -272,6 +300,9 @@ def main(argv=None) -> int:
     ap.add_argument("--q-len", type=int, default=1,
                     help="new tokens per sequence (speculative-decode verification): the step scatters them "
                          "and runs pa_decode_multi")
+    ap.add_argument("--shared", action="store_true",
+                    help="beam_cow only: decode with pa_decode_shared, reading a prompt's shared blocks once "
+                         "for its beams (the sharing is read back from the block tables)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="seconds of oracle work per CPU-baseline run (two runs: all cores, one thread)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -287,7 +318,8 @@ def main(argv=None) -> int:
                          "into the traffic record for --config (copy size from --probe-copy)")
     args = ap.parse_args(argv)
     if args.record_traffic:
-        return record_traffic(args.record_traffic, args.config, args.probe_copy or (1 << 30))
+        return record_traffic(args.record_traffic, args.config + ("_shared" if args.shared else ""),
+                              args.probe_copy or (1 << 30))
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -311,10 +343,14 @@ def main(argv=None) -> int:
     if args.config == "beam_cow":
         if args.q_len != 1:
             raise SystemExit("--q-len applies to the named single-step configs")
-        b = W.BeamSearchWorkload().step()
+        wl = W.BeamSearchWorkload()
+        b = wl.step()
     else:
+        if args.shared:
+            raise SystemExit("--shared applies to the beam_cow workload")
         b = W.make_config(args.config, q_len=args.q_len)
     multi = args.q_len > 1
+    workload = args.config + ("_shared" if args.shared else "")
 
     def bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -329,14 +365,24 @@ def main(argv=None) -> int:
     out = torch.empty_like(q)
     scale = float(b.scale)
 
-    decode_bytes = W.algorithmic_bytes(b.context_lens, b.num_q_heads, b.num_kv_heads, b.head_size,
-                                       q_len=args.q_len)
+    logical_bytes = W.algorithmic_bytes(b.context_lens, b.num_q_heads, b.num_kv_heads, b.head_size,
+                                        q_len=args.q_len)
+    decode_bytes = logical_bytes
+    if args.shared:
+        gstarts = W.consecutive_groups(b.num_seqs, wl.beams)
+        gshared = W.declared_sharing(b.block_tables, b.context_lens, gstarts)
+        gstarts_t = torch.from_numpy(gstarts).to(dev)
+        gshared_t = torch.from_numpy(gshared).to(dev)
+        decode_bytes = W.shared_algorithmic_bytes(b.context_lens, gstarts, gshared, b.max_blocks_per_seq,
+                                                  b.num_q_heads, b.num_kv_heads, b.head_size)
     step_bytes = decode_bytes + W.scatter_bytes(len(b.slot_mapping), b.num_kv_heads, b.head_size)
     if pairs is not None:
         step_bytes += W.copy_bytes(len(b.cow_pairs), b.block_size, b.num_kv_heads, b.head_size)
 
     def run_decode():
-        if multi:
+        if args.shared:
+            pa.decode_shared(q, kc, vc, tables, lens, gstarts_t, gshared_t, scale, out=out)
+        elif multi:
             pa.decode_multi(q, kc, vc, tables, lens, scale, out=out)
         else:
             pa.decode(q, kc, vc, tables, lens, scale, out=out)
@@ -395,7 +441,11 @@ def main(argv=None) -> int:
 
     value = step_bytes / (ms * 1e-3) / 1e9
     achieved = decode_bytes / (dec_mean * 1e-3) / 1e9
-    traffic = measured_traffic(args.config) if not multi else None
+    traffic = measured_traffic(workload) if not multi else None
+    if args.shared:
+        kernel = "decode_shared call: share_plan_kernel + decode_kernel + share_finalize_kernel"
+    else:
+        kernel = "decode call: decode_kernel + merge_kernel"
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -421,15 +471,16 @@ def main(argv=None) -> int:
             "seed": b.seed,
             "q_len": args.q_len,
             "step": ("copy_blocks + " if pairs is not None else "")
-                    + ("reshape_and_cache + decode_multi" if multi else "reshape_and_cache + decode"),
+                    + ("reshape_and_cache + decode_multi" if multi else
+                       "reshape_and_cache + decode_shared" if args.shared else "reshape_and_cache + decode"),
             "parallelism": "single GPU",
-            "cache": CACHE_NOTES.get(args.config, "cold: the K/V of a call is several times the 256 MB MALL"),
+            "cache": CACHE_NOTES.get(workload, "cold: the K/V of a call is several times the 256 MB MALL"),
         },
         "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "seq_steps_per_s": round(b.num_seqs / (ms * 1e-3), 1),
         "bytes_per_step": int(step_bytes),
         "roofline": {
-            "kernel": "decode call: decode_kernel + merge_kernel",
+            "kernel": kernel,
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": PEAK_HBM_GBS,
@@ -437,6 +488,7 @@ def main(argv=None) -> int:
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": traffic,
             "algorithmic_bytes_per_launch": int(decode_bytes),
+            "logical_bytes_per_launch": int(logical_bytes),
             "mean_launch_us": round(dec_mean * 1e3, 2),
             "mean_launch_us_mall_evicted": round(cold_us, 2) if cold_us else None,
             "achieved_mall_evicted": round(decode_bytes / cold_us / 1e3, 2) if cold_us else None,
@@ -445,7 +497,7 @@ def main(argv=None) -> int:
     }
     if not args.no_cpu_baseline:
         print(f"[bench] cpu baseline (~{2 * args.cpu_seconds:.0f} s)", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(b, args.cpu_seconds)
+        rec["cpu_baseline"] = cpu_baseline(b, args.cpu_seconds, (gstarts, gshared) if args.shared else None)
     print(json.dumps(rec), flush=True)
     return 0
 

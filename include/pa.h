@@ -165,6 +165,52 @@ size_t pa_decode_multi_workspace_bytes(const pa_kv_cache *cache, int32_t num_seq
                                        int32_t num_q_heads, int32_t max_blocks_per_seq);
 
 /*
+ * pa_decode_shared - pa_decode for a batch in which groups of sequences share
+ * the leading blocks of their block tables. The outputs of parallel sampling
+ * share the prompt's blocks, and beams share their history ("vLLM: Anatomy
+ * and Mechanisms of High-Throughput LLM Inference", section "Memory Sharing
+ * via Copy-on-Write (CoW)"). Prompts with a common beginning reuse cached
+ * blocks (same page, section "Prefix Caching"). Here the shared blocks are
+ * read from HBM once for up to 32 / (num_q_heads / num_kv_heads) members of a
+ * group, instead of once for each member.
+ *
+ *   group_starts   int32 [num_groups + 1], device memory. Group g is the
+ *                  sequences group_starts[g] .. group_starts[g+1]-1. The
+ *                  array must not decrease and must stay within 0..num_seqs.
+ *                  Sequences in no group are on their own. If the array
+ *                  breaks these rules, no group is formed: every sequence
+ *                  reads its own table, as in pa_decode.
+ *   shared_blocks  int32 [num_groups], device memory: the number of leading
+ *                  table entries the members of group g have in common.
+ *   num_groups     0 .. num_seqs. With 0 there is no sharing, and the two
+ *                  arrays may be NULL.
+ * Which blocks are read:
+ *   - Group g's prefix counts only whole blocks that every member fills:
+ *     e = min(shared_blocks[g], context_lens[j] / 16 for each member j),
+ *     clamped to 0..max_blocks_per_seq.
+ *   - Every member reads those e blocks through the table of the group's
+ *     first member, and the rest through its own table.
+ * When the declaration is true, the result is pa_decode's up to rounding
+ * (the sums run in a different order). A false declaration reads the first
+ * member's blocks, which is defined and stays in bounds.
+ * Limits: num_seqs <= 4096. The other arguments, layouts and errors are those
+ * of pa_decode. The workspace (owned by the caller, or allocated
+ * stream-ordered by the call when NULL) has the size that
+ * pa_decode_shared_workspace_bytes returns, which is never 0 for
+ * num_seqs > 0. Errors: as pa_decode, plus PA_ERR_SHAPE (num_groups outside
+ * 0..num_seqs) and PA_ERR_UNSUPPORTED (num_seqs > 4096).
+ */
+int pa_decode_shared(const pa_kv_cache *cache, const void *q, const int32_t *block_tables,
+                     const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                     int32_t max_blocks_per_seq, const int32_t *group_starts, const int32_t *shared_blocks,
+                     int32_t num_groups, float scale, void *out, void *workspace, size_t workspace_bytes,
+                     void *stream);
+
+/* Workspace bytes of pa_decode_shared (0 on invalid arguments or num_seqs == 0). */
+size_t pa_decode_shared_workspace_bytes(const pa_kv_cache *cache, int32_t num_seqs, int32_t num_q_heads,
+                                        int32_t max_blocks_per_seq, int32_t num_groups);
+
+/*
  * pa_reshape_and_cache - write each new token's K and V into its physical
  * slot before attention runs (the slot the block manager assigned on demand:
  * "vLLM: Anatomy and Mechanisms", section "Block-Level Management"; the

@@ -1,6 +1,7 @@
 """MI355X (gfx950) paged KV-cache decode: HIP kernels behind a C ABI.
 
-``decode``, ``reshape_and_cache``, ``copy_blocks`` and ``swap_blocks`` call libpa.so (built
+``decode``, ``decode_multi``, ``decode_shared``, ``reshape_and_cache``, ``copy_blocks`` and
+``swap_blocks`` call libpa.so (built
 with ``python -m paged_kv_cache_433_amd.build``); the library is loaded on
 first use and a missing build raises. ``workloads`` makes seeded inputs.
 """
@@ -10,6 +11,7 @@ from .ops import (  # noqa: F401
     copy_blocks,
     decode,
     decode_multi,
+    decode_shared,
     decode_workspace_bytes,
     probe_copy,
     probe_read,

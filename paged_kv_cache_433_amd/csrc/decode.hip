@@ -73,6 +73,11 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 constexpr int kBlock = 16;
 constexpr uint32_t kBf16One = 0x3F80u;
 
+// What a decode launch computes: one new token per sequence (kSingle);
+// several, each with its own causal limit (kCausal); or a list of items,
+// each read once for the one or more sequences it serves (kShared).
+constexpr int kSingle = 0, kCausal = 1, kShared = 2;
+
 __device__ __forceinline__ f32x4_t mfma32(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
@@ -173,13 +178,16 @@ __device__ __forceinline__ long long wg_scan(long long v, long long *red, int wa
 // this workgroup's range of units.
 struct Piece {
   long long seg_start;  // first unit of the segment the piece belongs to
-  int s;                // sequence
+  int s;                // sequence (an item, in kShared)
   int hg;               // head group
-  int off;              // first logical block of the piece
+  int off;              // first block of the piece, counted from the segment's first
   int cnt;              // blocks in the piece (>= 1)
-  int n;                // context length of s (clamped)
-  int L;                // blocks of s
+  int n;                // positions < n are visible (the clamped context length)
+  int L;                // blocks of the segment
   bool first;           // the workgroup's first piece
+  // kShared only: the item's table row, first q row, q rows, and first
+  // logical block (otherwise row s is read from block 0 with q_len q rows).
+  int row, qrow, ntok, b0;
 };
 
 // Produces the workgroup's pieces in order. Every thread of the workgroup
@@ -187,14 +195,32 @@ struct Piece {
 // context lengths it reads (scalar loads).
 struct Walker {
   const int32_t *lens;
-  int S, NG, cap;
+  const ShareItem *items;
+  int S, NG, cap;  // S: sequences, or items in kShared
   long long u, hi, seg_base;
   int s, hg, off, L, n;
+  int row, qrow, ntok, b0;
   bool first;
 };
 
+__device__ __forceinline__ void take_item(Walker &wk, const ShareItem &x) {
+  wk.L = x.L;
+  wk.n = x.n;
+  wk.row = x.row;
+  wk.qrow = x.qrow;
+  wk.ntok = x.ntok;
+  wk.b0 = x.b0;
+}
+
+template <int M>
 __device__ __forceinline__ bool next_piece(Walker &wk, Piece &p) {
   if (wk.u >= wk.hi) return false;
+  if constexpr (M == kShared) {
+    p.row = wk.row;
+    p.qrow = wk.qrow;
+    p.ntok = wk.ntok;
+    p.b0 = wk.b0;
+  }
   p.s = wk.s;
   p.hg = wk.hg;
   p.off = wk.off;
@@ -211,10 +237,14 @@ __device__ __forceinline__ bool next_piece(Walker &wk, Piece &p) {
     if (++wk.hg == wk.NG && wk.u < wk.hi) {
       wk.hg = 0;
       wk.seg_base += (long long)wk.NG * wk.L;
-      do {  // units remain, so a non-empty sequence follows
+      do {  // units remain, so a non-empty sequence (item) follows
         ++wk.s;
-        wk.n = wk.s < wk.S ? clamp_len(wk.lens[wk.s], wk.cap) : 0;
-        wk.L = (wk.n + kBlock - 1) / kBlock;
+        if constexpr (M == kShared) {
+          if (wk.s < wk.S) take_item(wk, wk.items[wk.s]); else wk.L = 0;
+        } else {
+          wk.n = wk.s < wk.S ? clamp_len(wk.lens[wk.s], wk.cap) : 0;
+          wk.L = (wk.n + kBlock - 1) / kBlock;
+        }
       } while (wk.L == 0 && wk.s < wk.S);
       if (wk.s >= wk.S) wk.u = wk.hi;  // only if the lengths changed during the call
     }
@@ -265,13 +295,16 @@ constexpr int kRawBufferWord3 = 0x00020000;
 // layout. Read through a buffer resource (scalar base at the KV head's first
 // query head of the sequence's first new token, fixed lane offsets) so that
 // no vector address is computed here.
-template <int NJ, int NT>
+template <int NJ, int NT, int M>
 __device__ __forceinline__ void load_q(const DecodeArgs &a, const Lane<NT> &ln, const Piece &p,
                                        u32x4_t (&qv)[NT][NJ]) {
   constexpr int D = NJ * 32;
-  const size_t base = ((size_t)p.s * a.q_len * a.num_q_heads + (size_t)(p.hg * ln.HG + ln.wave) * a.group) * D *
-                      sizeof(uint16_t);
-  const int span = ((a.q_len - 1) * a.num_q_heads + a.group) * D * (int)sizeof(uint16_t);
+  // q rows of the piece: its sequence's q_len rows, or an item's ntok rows
+  // (columns past them read as zeros and are never stored).
+  const size_t row0 = M == kShared ? (size_t)p.qrow : (size_t)p.s * a.q_len;
+  const int rows = M == kShared ? p.ntok : a.q_len;
+  const size_t base = (row0 * a.num_q_heads + (size_t)(p.hg * ln.HG + ln.wave) * a.group) * D * sizeof(uint16_t);
+  const int span = ((rows - 1) * a.num_q_heads + a.group) * D * (int)sizeof(uint16_t);
   const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<char *>(reinterpret_cast<const char *>(a.q) + base), 0, span, kRawBufferWord3);
 #pragma unroll
@@ -325,6 +358,16 @@ __device__ __forceinline__ int block_id(const int32_t *__restrict__ tables, cons
   return (uint32_t)id < pool32 ? id : 0;
 }
 
+// Table row and first logical block of a piece's segment.
+template <int M>
+__device__ __forceinline__ int table_row(const Piece &p) {
+  if constexpr (M == kShared) return p.row; else return p.s;
+}
+template <int M>
+__device__ __forceinline__ int first_block(const Piece &p) {
+  if constexpr (M == kShared) return p.b0; else return 0;
+}
+
 // Element offset of the wavefront's KV head inside a token row (uniform).
 template <int NJ, int NT>
 __device__ __forceinline__ size_t head_off(const Lane<NT> &ln, const Piece &p) {
@@ -365,12 +408,34 @@ __device__ __forceinline__ int rows_in(int n, int b) {
 // segment begun in an earlier workgroup, so each workgroup writes one merge
 // record, when its first piece ends: that segment and where its pieces are,
 // or none.
-template <int NJ, int NT, bool kMulti>
+template <int NJ, int NT, int M>
 __device__ __forceinline__ void finish_piece(const DecodeArgs &a, const Lane<NT> &ln, Stream<NJ, NT> &st) {
   constexpr int D = NJ * 32;
+  constexpr bool kMulti = M == kCausal;
   const Piece &P = st.P;
   const bool whole = P.off == 0 && P.cnt == P.L;
   const int g = P.hg * ln.HG + ln.wave;
+  if constexpr (M == kShared) {
+    // Every piece leaves a record: the item's own when the piece is the
+    // whole segment, else the workgroup's slot. The finalize kernel merges
+    // each sequence's records (its prefix item's column and its tail).
+    const size_t rec = whole ? (size_t)2 * a.num_wgs + (size_t)P.s * ln.NG + P.hg : (size_t)2 * ln.w + (P.first ? 0 : 1);
+    const int live = P.ntok * a.group;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      float l = st.l_part[t] + __shfl_xor(st.l_part[t], 16);
+      l += __shfl_xor(l, 32);
+      if (ln.col_ok[t] && ln.col[t] < live) {
+        const size_t row = (rec * ln.HG + ln.wave) * a.num_cols + ln.col[t];
+        float *po = a.part_o + row * D + ln.grp * 8;
+#pragma unroll
+        for (int k = 0; k < 2 * NJ; ++k)
+          *reinterpret_cast<f32x4_t *>(po + 32 * (k >> 1) + 4 * (k & 1)) = st.acc[t][k];
+        if (ln.grp == 0) *reinterpret_cast<f32x2_t *>(a.part_ml + row * 2) = f32x2_t{st.m_run[t], l};
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     float l = st.l_part[t] + __shfl_xor(st.l_part[t], 16);
@@ -408,7 +473,7 @@ __device__ __forceinline__ void finish_piece(const DecodeArgs &a, const Lane<NT>
 // Makes Q the current piece (its first block is already loading) and looks
 // one piece further ahead. With one column tile Q's q is in LDS already;
 // with two it is loaded here and parked in LDS.
-template <int NJ, int NT>
+template <int NJ, int NT, int M>
 __device__ __forceinline__ void advance(const DecodeArgs &a, const Lane<NT> &ln, Walker &wk, Stream<NJ, NT> &st,
                                         uint16_t *lds) {
   st.P = st.Q;
@@ -419,7 +484,7 @@ __device__ __forceinline__ void advance(const DecodeArgs &a, const Lane<NT> &ln,
     for (int j = 0; j < NJ; ++j) st.qv[0][j] = *reinterpret_cast<const u32x4_t *>(qs + ln.col[0] * (NJ * 32) + 32 * j);
   } else {
     u32x4_t qv[NT][NJ];
-    load_q<NJ>(a, ln, st.P, qv);
+    load_q<NJ, NT, M>(a, ln, st.P, qv);
     park_q<NJ>(lds, a, ln, qv);
   }
   st.hoff = st.hoff_q;
@@ -431,7 +496,7 @@ __device__ __forceinline__ void advance(const DecodeArgs &a, const Lane<NT> &ln,
 #pragma unroll
     for (int k = 0; k < 2 * NJ; ++k) st.acc[t][k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  st.has_q = next_piece(wk, st.Q);
+  st.has_q = next_piece<M>(wk, st.Q);
   if (!st.has_q) st.Q = st.P;
   st.hoff_q = head_off<NJ>(ln, st.Q);
 }
@@ -439,10 +504,11 @@ __device__ __forceinline__ void advance(const DecodeArgs &a, const Lane<NT> &ln,
 // Computes block i of P from (K, V) after starting the next block of the
 // stream loading into (Kn, Vn); finishes P at its end and moves to Q.
 // Returns false once the stream is done.
-template <int NJ, int NT, bool kMulti>
+template <int NJ, int NT, int M>
 __device__ __forceinline__ bool step(const int32_t *__restrict__ tables, const DecodeArgs &a, const Lane<NT> &ln,
                                      Walker &wk, Stream<NJ, NT> &st, u32x4_t (&K)[NJ], u32x4_t (&V)[NJ],
                                      u32x4_t (&Kn)[NJ], u32x4_t (&Vn)[NJ], uint16_t *lds) {
+  constexpr bool kMulti = M == kCausal;
   const Piece &P = st.P;
   // In P's first step, q of the next piece is loaded (before this step's K/V
   // loads) and parked in LDS at the end of the step: the registers never
@@ -450,7 +516,7 @@ __device__ __forceinline__ bool step(const int32_t *__restrict__ tables, const D
   // issued after them.
   const bool stage_q = NT == 1 && st.i == 0 && st.has_q;
   u32x4_t qt[NT][NJ];
-  if (stage_q) load_q<NJ>(a, ln, st.Q, qt);
+  if (stage_q) load_q<NJ, NT, M>(a, ln, st.Q, qt);
   // The next block of the stream: P's next, else Q's first. The loads are
   // issued on every path (past the end of the stream they reload the
   // current block, which is still in the cache), so the compiler can count
@@ -459,19 +525,23 @@ __device__ __forceinline__ bool step(const int32_t *__restrict__ tables, const D
   const int nx = st.i + 1;
   const bool in_p = nx < P.cnt;
   const bool to_q = !in_p && st.has_q;
-  const int next_s = to_q ? st.Q.s : P.s;
-  const int next_b = in_p ? P.off + nx : (to_q ? st.Q.off : P.off + st.i);
-  issue<NJ>(a, ln, block_id(tables, a, ln.pool32, next_s, next_b), to_q ? st.hoff_q : st.hoff,
+  const int next_row = to_q ? table_row<M>(st.Q) : table_row<M>(P);
+  const int next_b = (in_p ? P.off + nx : (to_q ? st.Q.off : P.off + st.i)) +
+                     (to_q ? first_block<M>(st.Q) : first_block<M>(P));
+  issue<NJ>(a, ln, block_id(tables, a, ln.pool32, next_row, next_b), to_q ? st.hoff_q : st.hoff,
             rows_in(to_q ? st.Q.n : P.n, next_b), Kn, Vn);
   // Keep the scheduler from sinking those loads below the compute.
   __builtin_amdgcn_sched_barrier(0);
 
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
-  const int b = P.off + st.i;
+  const int b = first_block<M>(P) + P.off + st.i;
   const int pos0 = b * kBlock + ln.grp * 4;
+  // kShared: an item of one sequence fills only the first tile.
+  const int live = M == kShared ? P.ntok * a.group : a.num_cols;
   u32x2_t pb_hi[NT], pb_lo[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
+    if (M == kShared && t > 0 && live <= 16 * t) continue;
     f32x4_t sc = zero4;
     if constexpr (NT == 1) {
 #pragma unroll
@@ -520,6 +590,7 @@ __device__ __forceinline__ bool step(const int32_t *__restrict__ tables, const D
       const u32x2_t av = {pack_hi(tv[0], tv[1]), pack_hi(tv[2], tv[3])};
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
+        if (M == kShared && t > 0 && live <= 16 * t) continue;
         st.acc[t][2 * j + h] = mfma16(av, pb_hi[t], st.acc[t][2 * j + h]);
         st.acc[t][2 * j + h] = mfma16(av, pb_lo[t], st.acc[t][2 * j + h]);
       }
@@ -538,9 +609,9 @@ __device__ __forceinline__ bool step(const int32_t *__restrict__ tables, const D
 
   st.i = nx;
   if (in_p) return true;
-  finish_piece<NJ, NT, kMulti>(a, ln, st);
+  finish_piece<NJ, NT, M>(a, ln, st);
   if (!st.has_q) return false;
-  advance<NJ>(a, ln, wk, st, lds);
+  advance<NJ, NT, M>(a, ln, wk, st, lds);
   return true;
 }
 
@@ -559,11 +630,11 @@ __device__ __forceinline__ void no_merge(const DecodeArgs &a, int w, int tid) {
   if (tid == 0 && a.merge_desc) a.merge_desc[w] = int2{-1, -1};
 }
 
-// NT: 16-column MFMA tiles per KV head (columns = q_len * group). kMulti:
-// several new tokens per sequence, each with its own causal limit. The
-// launch puts one wavefront on each SIMD; with two tiles the wavefront may
-// take the whole register file (arch and accumulation registers).
-template <int D, int NT, bool kMulti>
+// NT: 16-column MFMA tiles per KV head (columns = q_len * group, or the
+// item width in kShared). M: kSingle, kCausal or kShared. The launch puts
+// one wavefront on each SIMD; with two tiles the wavefront may take the
+// whole register file (arch and accumulation registers).
+template <int D, int NT, int M>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2 : 1)))
 void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const int32_t *__restrict__ lens) {
   constexpr int NJ = D / 32;  // MFMA steps over head_size; 16-byte loads per lane per row
@@ -584,7 +655,29 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
   const long long W = a.num_wgs;
 
   long long U, lo, hi, E;
-  if (S <= nthr) {
+  Walker wk;
+  if constexpr (M == kShared) {
+    // The plan kernel wrote the items and their first units; one parallel
+    // search finds the item that holds `lo` (empty items never match).
+    const ShareHeader h = *a.share;
+    U = h.units;
+    E = U < W ? U : W;
+    if (w >= E) return;
+    lo = range_lo(w, U, E);
+    hi = range_lo(w + 1, U, E);
+    if (tid == 0) found_seq = -1;
+    __syncthreads();
+    for (int v = tid; v < h.items; v += nthr)
+      if (a.items[v].ustart <= lo && lo < a.items[v + 1].ustart) found_seq = v;
+    __syncthreads();
+    if (found_seq < 0) return;  // only if the plan is inconsistent
+    const int v = __builtin_amdgcn_readfirstlane(found_seq);
+    wk.items = a.items;
+    wk.S = h.items;
+    take_item(wk, a.items[v]);
+    wk.s = v;
+    wk.seg_base = a.items[v].ustart;
+  } else if (S <= nthr) {
     // One pass: every thread holds one sequence's block count; a block scan
     // gives the total and every sequence's first unit at once.
     const int n = tid < S ? clamp_len(lens[tid], cap) : 0;
@@ -646,17 +739,18 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
     if (found_seq < 0) return;  // only if the lengths changed during the call
   }
 
-  Walker wk;
-  wk.lens = lens;
-  wk.S = S;
+  if constexpr (M != kShared) {
+    wk.lens = lens;
+    wk.S = S;
+    wk.cap = cap;
+    wk.seg_base = found_prefix * NG;
+    wk.s = __builtin_amdgcn_readfirstlane(found_seq);
+    wk.n = __builtin_amdgcn_readfirstlane(found_n);
+    wk.L = (wk.n + kBlock - 1) / kBlock;
+  }
   wk.NG = NG;
-  wk.cap = cap;
   wk.u = lo;
   wk.hi = hi;
-  wk.seg_base = found_prefix * NG;
-  wk.s = __builtin_amdgcn_readfirstlane(found_seq);
-  wk.n = __builtin_amdgcn_readfirstlane(found_n);
-  wk.L = (wk.n + kBlock - 1) / kBlock;
   wk.hg = (int)((lo - wk.seg_base) / wk.L);
   wk.off = (int)((lo - wk.seg_base) % wk.L);
   wk.first = true;
@@ -703,16 +797,16 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
   // stream (possibly the first block of the next piece) loads into the
   // other. The next piece's q goes through LDS one piece ahead.
   Stream<NJ, NT> st;
-  next_piece(wk, st.P);
+  next_piece<M>(wk, st.P);
   if constexpr (NT == 1) {
-    load_q<NJ>(a, ln, st.P, st.qv);
+    load_q<NJ, NT, M>(a, ln, st.P, st.qv);
   } else {
     u32x4_t qv[NT][NJ];
-    load_q<NJ>(a, ln, st.P, qv);
+    load_q<NJ, NT, M>(a, ln, st.P, qv);
     park_q<NJ>(q_lds, a, ln, qv);
   }
   st.hoff = head_off<NJ>(ln, st.P);
-  st.has_q = next_piece(wk, st.Q);
+  st.has_q = next_piece<M>(wk, st.Q);
   if (!st.has_q) st.Q = st.P;
   st.hoff_q = head_off<NJ>(ln, st.Q);
   st.i = 0;
@@ -725,9 +819,11 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
     for (int k = 0; k < 2 * NJ; ++k) st.acc[t][k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
   u32x4_t KA[NJ], VA[NJ], KB[NJ], VB[NJ];
-  issue<NJ>(a, ln, block_id(tables, a, ln.pool32, st.P.s, st.P.off), st.hoff, rows_in(st.P.n, st.P.off), KA, VA);
-  while (step<NJ, NT, kMulti>(tables, a, ln, wk, st, KA, VA, KB, VB, q_lds) &&
-         step<NJ, NT, kMulti>(tables, a, ln, wk, st, KB, VB, KA, VA, q_lds)) {
+  const int b_first = first_block<M>(st.P) + st.P.off;
+  issue<NJ>(a, ln, block_id(tables, a, ln.pool32, table_row<M>(st.P), b_first), st.hoff, rows_in(st.P.n, b_first),
+            KA, VA);
+  while (step<NJ, NT, M>(tables, a, ln, wk, st, KA, VA, KB, VB, q_lds) &&
+         step<NJ, NT, M>(tables, a, ln, wk, st, KB, VB, KA, VA, q_lds)) {
   }
 }
 
@@ -809,6 +905,234 @@ __global__ __launch_bounds__(1024) void merge_kernel(const DecodeArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Sharing-aware decode: sequences in a group share the leading blocks of
+// their tables (parallel samples share the prompt, beams their history:
+// "vLLM: Anatomy and Mechanisms", section "Memory Sharing via Copy-on-Write
+// (CoW)"; prompts with a common beginning reuse cached blocks: section
+// "Prefix Caching"). Those blocks are read once for up to 32 / group members
+// (their query heads become MFMA columns of one item), each member's private
+// blocks once for it alone; a finalize pass merges the two per sequence.
+// ---------------------------------------------------------------------------
+
+// Inclusive max-scan over the workgroup (plan kernel only).
+__device__ __forceinline__ int wg_max_scan(int v, int *red, int wave, int lane, int nwaves, int &total) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(v, d);
+    if (lane >= d) v = max(v, u);
+  }
+  __syncthreads();
+  if (lane == 63) red[wave] = v;
+  __syncthreads();
+  int pre = -1;
+  total = -1;
+  for (int i = 0; i < nwaves; ++i) {
+    if (i < wave) pre = max(pre, red[i]);
+    total = max(total, red[i]);
+  }
+  return max(v, pre);
+}
+
+// Builds the call's items in one workgroup.
+//   * group_starts must not decrease and must stay within 0..S; otherwise no
+//     group is formed and every sequence reads its own table.
+//   * A sequence's group is the last one that starts at or before it (a
+//     max-scan of start marks), if the sequence lies before its end.
+//   * A group's shared blocks are clamped to 0..max_blocks_per_seq and to the
+//     whole blocks each member fills.
+//   * Items: one prefix item per run of members_per_item consecutive members
+//     of every group with shared blocks (read through the first member's
+//     table), then one tail item per sequence (its blocks past the shared
+//     ones). Units follow item order, head group major within an item.
+template <int kThreads>
+__global__ __launch_bounds__(kThreads) void share_plan_kernel(const SharePlanArgs p) {
+  extern __shared__ __align__(16) int plan_lds[];  // grp[S], shb[G], ibase[G], then pblk[G] (64-bit)
+  __shared__ long long red[kThreads / 64];
+  __shared__ int redi[kThreads / 64];
+  __shared__ int bad;
+  constexpr int nwaves = kThreads / 64;
+  const int S = p.num_seqs, NGr = p.num_groups, C = p.members_per_item;
+  int *grp = plan_lds;
+  int *shb = grp + S;
+  int *ibase = shb + NGr;
+  long long *pblk = reinterpret_cast<long long *>(plan_lds + ((S + 2 * NGr + 1) & ~1));
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cap = p.max_blocks_per_seq * kBlock;
+
+  if (tid == 0) bad = 0;
+  for (int i = tid; i < S; i += kThreads) grp[i] = -1;
+  __syncthreads();
+  for (int g = tid; g < NGr; g += kThreads) {
+    const int lo = p.group_starts[g], hi = p.group_starts[g + 1];
+    if (lo > hi || (g == 0 && lo < 0) || (g == NGr - 1 && hi > S)) bad = 1;
+  }
+  __syncthreads();
+  const bool valid = bad == 0;
+  for (int g = tid; g < NGr; g += kThreads) {
+    shb[g] = min(max(p.shared_blocks[g], 0), p.max_blocks_per_seq);
+    const int lo = p.group_starts[g], hi = p.group_starts[g + 1];
+    if (valid && hi > lo) grp[lo] = g;  // distinct starts: groups are nonempty and ordered
+  }
+  __syncthreads();
+  int carry = -1;
+  for (int base = 0; base < S; base += kThreads) {
+    const int i = base + tid;
+    int total;
+    const int v = max(wg_max_scan(i < S ? grp[i] : -1, redi, wave, lane, nwaves, total), carry);
+    if (i < S) grp[i] = v;
+    carry = max(carry, total);
+  }
+  __syncthreads();
+  for (int i = tid; i < S; i += kThreads) {
+    const int g = grp[i];
+    if (g < 0) continue;
+    if (i >= p.group_starts[g + 1]) {
+      grp[i] = -1;
+      continue;
+    }
+    atomicMin(&shb[g], clamp_len(p.lens[i], cap) / kBlock);  // LDS atomic
+  }
+  __syncthreads();
+
+  // Prefix items and blocks per group, scanned.
+  int items_before = 0;
+  long long blocks_before = 0;
+  for (int base = 0; base < NGr; base += kThreads) {
+    const int g = base + tid;
+    int nsub = 0;
+    long long blocks = 0;
+    if (g < NGr && valid) {
+      const int m = p.group_starts[g + 1] - p.group_starts[g];
+      if (m > 0 && shb[g] > 0) {
+        nsub = (m + C - 1) / C;
+        blocks = (long long)nsub * shb[g];
+      }
+    }
+    long long pre, tot, preb, totb;
+    const long long incl = wg_scan((long long)nsub, red, wave, lane, nwaves, pre, tot);
+    const long long inclb = wg_scan(blocks, red, wave, lane, nwaves, preb, totb);
+    if (g < NGr) {
+      ibase[g] = items_before + (int)(pre + incl - nsub);
+      pblk[g] = blocks_before + preb + inclb - blocks;
+    }
+    items_before += (int)tot;
+    blocks_before += totb;
+  }
+  __syncthreads();
+  const int Vp = items_before;
+  const long long NG = p.num_head_groups;
+
+  long long tail_before = 0;
+  for (int base = 0; base < S; base += kThreads) {
+    const int i = base + tid;
+    int b0 = 0, n = 0;
+    int2 map = {-1, 0};
+    if (i < S) {
+      n = clamp_len(p.lens[i], cap);
+      const int g = grp[i];
+      if (g >= 0 && shb[g] > 0) {
+        const int lo = p.group_starts[g], hi = p.group_starts[g + 1];
+        const int k = i - lo, sub = k / C;
+        b0 = shb[g];
+        map = int2{ibase[g] + sub, (k - sub * C) * p.group};
+        if (k == sub * C) {
+          ShareItem x;
+          x.row = lo;
+          x.qrow = i;
+          x.ntok = min(C, hi - i);
+          x.b0 = 0;
+          x.n = shb[g] * kBlock;
+          x.L = shb[g];
+          x.ustart = NG * (pblk[g] + (long long)sub * shb[g]);
+          p.items[ibase[g] + sub] = x;
+        }
+      }
+    }
+    const long long Lt = i < S ? (long long)((n + kBlock - 1) / kBlock - b0) : 0;
+    long long pre, tot;
+    const long long incl = wg_scan(Lt, red, wave, lane, nwaves, pre, tot);
+    if (i < S) {
+      ShareItem x;
+      x.row = i;
+      x.qrow = i;
+      x.ntok = 1;
+      x.b0 = b0;
+      x.n = n;
+      x.L = (int)Lt;
+      x.ustart = NG * (blocks_before + tail_before + pre + incl - Lt);
+      p.items[Vp + i] = x;
+      p.seq_map[i] = map;
+    }
+    tail_before += tot;
+  }
+  if (tid == 0) {
+    const long long units = NG * (blocks_before + tail_before);
+    ShareItem x = {0, 0, 0, 0, 0, 0, units};
+    p.items[Vp + S] = x;  // sentinel: the end of the last item
+    ShareHeader h;
+    h.units = units;
+    h.items = Vp + S;
+    h.prefix_items = Vp;
+    *p.share = h;
+  }
+}
+
+// For every sequence and query head: merges the records of its column in
+// its prefix item and of its tail item with log-sum-exp weights, and writes
+// the bf16 output. Grid (S, Hkv, ceil(group / 16)), one wavefront per query
+// head; lane i owns head dims [i*D/64, (i+1)*D/64).
+template <int D>
+__global__ __launch_bounds__(1024) void share_finalize_kernel(const DecodeArgs a) {
+  constexpr int PL = D / 64;
+  const int s = blockIdx.x, g = blockIdx.y;
+  const int qh = (threadIdx.x >> 6) + 16 * blockIdx.z;
+  if (qh >= a.group) return;
+  const int lane = threadIdx.x & 63;
+  const int HG = a.heads_per_wg, NG = a.num_head_groups;
+  const int hg = g / HG, k = g - hg * HG;
+  const ShareHeader h = *a.share;
+  const long long U = h.units, W = a.num_wgs, E = U < W ? U : W;
+  float M = -INFINITY, Lsum = 0.f, o[PL];
+#pragma unroll
+  for (int i = 0; i < PL; ++i) o[i] = 0.f;
+  auto fold = [&](size_t rec, int col) {
+    const size_t r = (rec * HG + k) * a.num_cols + col;
+    const f32x2_t ml = *reinterpret_cast<const f32x2_t *>(a.part_ml + r * 2);
+    const float Mn = fmaxf(M, ml[0]);
+    const float Mu = Mn == -INFINITY ? 0.f : Mn;
+    const float so = fast_exp2(M - Mu), wt = fast_exp2(ml[0] - Mu);
+    Lsum = Lsum * so + wt * ml[1];
+#pragma unroll
+    for (int i = 0; i < PL; ++i) o[i] = o[i] * so + wt * a.part_o[r * D + lane * PL + i];
+    M = Mn;
+  };
+  // The records of item v's segment for head group hg: the item's own when
+  // one workgroup holds the whole segment, else one per workgroup it spans.
+  auto fold_item = [&](int v, int col) {
+    const ShareItem x = a.items[v];
+    if (x.L <= 0) return;
+    const long long seg0 = x.ustart + (long long)hg * x.L, seg1 = seg0 + x.L;
+    const int w0 = owner_of(seg0, U, E), w1 = owner_of(seg1 - 1, U, E);
+    if (w0 == w1) {
+      fold((size_t)2 * a.num_wgs + (size_t)v * NG + hg, col);
+      return;
+    }
+    fold((size_t)2 * w0 + (range_lo(w0, U, E) < seg0 ? 1 : 0), col);
+    for (int w = w0 + 1; w <= w1; ++w) fold((size_t)2 * w, col);
+  };
+  fold_item(h.prefix_items + s, qh);
+  const int2 m = a.seq_map[s];
+  if (m.x >= 0) fold_item(m.x, m.y + qh);
+  const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
+  uint16_t *dst = a.out + ((size_t)s * a.num_q_heads + (size_t)g * a.group + qh) * D + lane * PL;
+  if constexpr (PL == 2) {
+    *reinterpret_cast<uint32_t *>(dst) = to_bf16x2(o[0] * inv, o[1] * inv);
+  } else {
+    dst[0] = (uint16_t)(to_bf16x2(o[0] * inv, 0.f) & 0xFFFFu);
+  }
+}
+
 // Lets a kernel use more than 64 KiB of dynamic LDS (gfx950 has 160 KiB per
 // compute unit).
 template <typename Kernel>
@@ -818,11 +1142,11 @@ hipError_t allow_lds(Kernel kernel, size_t bytes) {
                              (int)bytes);
 }
 
-template <int D, int NT, bool kMulti>
+template <int D, int NT, int M>
 hipError_t launch_decode_kernel(const DecodeArgs &args, size_t lds, hipStream_t stream) {
-  hipError_t e = allow_lds(decode_kernel<D, NT, kMulti>, lds);
+  hipError_t e = allow_lds(decode_kernel<D, NT, M>, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_kernel<D, NT, kMulti>), dim3((unsigned)args.num_wgs),
+  hipLaunchKernelGGL((decode_kernel<D, NT, M>), dim3((unsigned)args.num_wgs),
                      dim3(64 * (unsigned)args.heads_per_wg), lds, stream, args, args.block_tables,
                      args.context_lens);
   return hipGetLastError();
@@ -830,9 +1154,9 @@ hipError_t launch_decode_kernel(const DecodeArgs &args, size_t lds, hipStream_t 
 
 template <int D>
 hipError_t launch_decode_d(const DecodeArgs &args, size_t lds, hipStream_t stream) {
-  if (args.q_len == 1) return launch_decode_kernel<D, 1, false>(args, lds, stream);
-  if (args.num_cols <= 16) return launch_decode_kernel<D, 1, true>(args, lds, stream);
-  return launch_decode_kernel<D, 2, true>(args, lds, stream);
+  if (args.q_len == 1) return launch_decode_kernel<D, 1, kSingle>(args, lds, stream);
+  if (args.num_cols <= 16) return launch_decode_kernel<D, 1, kCausal>(args, lds, stream);
+  return launch_decode_kernel<D, 2, kCausal>(args, lds, stream);
 }
 
 }  // namespace
@@ -859,6 +1183,36 @@ hipError_t launch_decode(const DecodeArgs &args, int32_t head_size, hipStream_t 
     hipLaunchKernelGGL(merge_kernel<128>, mgrid, mblock, 0, stream, args);
   } else {
     hipLaunchKernelGGL(merge_kernel<64>, mgrid, mblock, 0, stream, args);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_shared(const SharePlanArgs &plan, const DecodeArgs &args, int32_t head_size,
+                                hipStream_t stream) {
+  if (args.q_len != 1 || args.num_cols <= 16 || args.num_cols > 32 || !args.items || !args.share ||
+      !args.seq_map || plan.num_seqs < 1 || plan.num_seqs > kMaxSharedSeqs || plan.num_groups < 0 ||
+      plan.num_groups > plan.num_seqs || plan.members_per_item < 1)
+    return hipErrorInvalidValue;
+  if (head_size != 128 && head_size != 64) return hipErrorInvalidValue;
+  constexpr int kPlanThreads = 512;
+  const size_t plan_lds = (((size_t)plan.num_seqs + 2 * (size_t)plan.num_groups + 1) & ~(size_t)1) * sizeof(int) +
+                          (size_t)plan.num_groups * sizeof(long long);
+  hipError_t e = allow_lds(share_plan_kernel<kPlanThreads>, plan_lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(share_plan_kernel<kPlanThreads>, dim3(1), dim3(kPlanThreads), plan_lds, stream, plan);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // q of the current piece is parked in LDS: one [num_cols][D] slot per wavefront.
+  const size_t lds = (size_t)args.heads_per_wg * args.num_cols * head_size * sizeof(uint16_t);
+  e = head_size == 128 ? launch_decode_kernel<128, 2, kShared>(args, lds, stream)
+                       : launch_decode_kernel<64, 2, kShared>(args, lds, stream);
+  if (e != hipSuccess) return e;
+  const dim3 fgrid((unsigned)args.num_seqs, (unsigned)args.num_kv_heads, (unsigned)((args.group + 15) / 16));
+  const dim3 fblock(64 * (unsigned)(args.group < 16 ? args.group : 16));
+  if (head_size == 128) {
+    hipLaunchKernelGGL(share_finalize_kernel<128>, fgrid, fblock, 0, stream, args);
+  } else {
+    hipLaunchKernelGGL(share_finalize_kernel<64>, fgrid, fblock, 0, stream, args);
   }
   return hipGetLastError();
 }

@@ -103,6 +103,44 @@ int check_q_len(const pa_kv_cache *c, int32_t num_q_heads, int32_t q_len) {
   return PA_OK;
 }
 
+// Sharing-aware decode: an item serves up to 32 / group sequences (its
+// columns are their query heads of one KV head: at most two MFMA tiles).
+int32_t members_per_item(int32_t group) { return 32 / group; }
+
+// Workspace of pa_decode_shared: header, items (+ sentinel), sequence map,
+// then piece records: 2 per workgroup, then one per (item, head group).
+struct SharedLayout {
+  pa::DecodePlan plan;
+  int32_t cols;
+  size_t items_off, map_off, ml_off, o_off, total;
+};
+
+SharedLayout layout_shared(const pa_kv_cache *c, int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq) {
+  SharedLayout l{};
+  const int32_t group = num_q_heads / c->num_kv_heads;
+  l.plan.heads_per_wg = heads_per_workgroup(c->num_kv_heads);
+  l.plan.num_head_groups = c->num_kv_heads / l.plan.heads_per_wg;
+  // Up to one prefix item and one tail item per sequence, each at most
+  // max_blocks_per_seq blocks.
+  l.plan.num_wgs = decode_wgs(2 * (int64_t)num_seqs, l.plan.num_head_groups, l.plan.heads_per_wg, max_blocks_per_seq);
+  l.cols = members_per_item(group) * group;
+  const size_t recs = 2 * (size_t)l.plan.num_wgs + 2 * (size_t)num_seqs * l.plan.num_head_groups;
+  const size_t rows = recs * l.plan.heads_per_wg * l.cols;
+  l.items_off = 256;  // ShareHeader
+  l.map_off = l.items_off + round_up((2 * (size_t)num_seqs + 1) * sizeof(pa::ShareItem), 256);
+  l.ml_off = l.map_off + round_up((size_t)num_seqs * sizeof(int2), 256);
+  l.o_off = l.ml_off + round_up(rows * 2 * sizeof(float), 256);
+  l.total = l.o_off + round_up(rows * c->head_size * sizeof(float), 256);
+  return l;
+}
+
+int check_shared(int32_t num_seqs, int32_t num_groups) {
+  if (num_seqs > pa::kMaxSharedSeqs)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode_shared takes at most 4096 sequences");
+  if (num_groups < 0 || num_groups > num_seqs) return fail(PA_ERR_SHAPE, "num_groups must be in 0..num_seqs");
+  return PA_OK;
+}
+
 }  // namespace
 
 namespace pa {
@@ -214,6 +252,98 @@ int pa_decode_multi(const pa_kv_cache *cache, const void *q, const int32_t *bloc
     if (e == hipSuccess) e = fe;
   }
   if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return ok();
+}
+
+size_t pa_decode_shared_workspace_bytes(const pa_kv_cache *cache, int32_t num_seqs, int32_t num_q_heads,
+                                        int32_t max_blocks_per_seq, int32_t num_groups) {
+  if (check_cache(cache, false) != PA_OK) return 0;
+  if (check_decode_shape(cache, num_seqs, num_q_heads, max_blocks_per_seq) != PA_OK) return 0;
+  if (check_shared(num_seqs, num_groups) != PA_OK || num_seqs == 0) return 0;
+  return layout_shared(cache, num_seqs, num_q_heads, max_blocks_per_seq).total;
+}
+
+int pa_decode_shared(const pa_kv_cache *cache, const void *q, const int32_t *block_tables,
+                     const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                     int32_t max_blocks_per_seq, const int32_t *group_starts, const int32_t *shared_blocks,
+                     int32_t num_groups, float scale, void *out, void *workspace, size_t workspace_bytes,
+                     void *stream) {
+  int rc = check_cache(cache, num_seqs > 0);
+  if (rc != PA_OK) return rc;
+  rc = check_decode_shape(cache, num_seqs, num_q_heads, max_blocks_per_seq);
+  if (rc != PA_OK) return rc;
+  rc = check_shared(num_seqs, num_groups);
+  if (rc != PA_OK) return rc;
+  if (num_seqs == 0) return ok();
+  if (!q || !block_tables || !context_lens || !out)
+    return fail(PA_ERR_NULL, "q, block_tables, context_lens or out is NULL");
+  if (num_groups > 0 && (!group_starts || !shared_blocks))
+    return fail(PA_ERR_NULL, "group_starts or shared_blocks is NULL");
+
+  const SharedLayout l = layout_shared(cache, num_seqs, num_q_heads, max_blocks_per_seq);
+  if (workspace && workspace_bytes < l.total)
+    return fail(PA_ERR_WORKSPACE, "workspace smaller than pa_decode_shared_workspace_bytes()");
+  if (workspace && reinterpret_cast<uintptr_t>(workspace) % 16)
+    return fail(PA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  void *ws = workspace;
+  bool owned = false;
+  if (!ws) {
+    hipError_t e = hipMallocAsync(&ws, l.total, hs);
+    if (e != hipSuccess) return hip_fail(e, "hipMallocAsync(workspace)");
+    owned = true;
+  }
+  char *base = static_cast<char *>(ws);
+  pa::ShareHeader *hdr = reinterpret_cast<pa::ShareHeader *>(base);
+  pa::ShareItem *items = reinterpret_cast<pa::ShareItem *>(base + l.items_off);
+  int2 *seq_map = reinterpret_cast<int2 *>(base + l.map_off);
+
+  pa::DecodeArgs a{};
+  a.q = static_cast<const uint16_t *>(q);
+  a.k_cache = static_cast<const uint16_t *>(cache->k_cache);
+  a.v_cache = static_cast<const uint16_t *>(cache->v_cache);
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.out = static_cast<uint16_t *>(out);
+  a.part_ml = reinterpret_cast<float *>(base + l.ml_off);
+  a.part_o = reinterpret_cast<float *>(base + l.o_off);
+  a.num_blocks = cache->num_blocks;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.group = num_q_heads / cache->num_kv_heads;
+  a.q_len = 1;
+  a.num_cols = l.cols;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.heads_per_wg = l.plan.heads_per_wg;
+  a.num_head_groups = l.plan.num_head_groups;
+  a.num_wgs = l.plan.num_wgs;
+  a.scale_log2 = scale * 1.44269504088896340736f;
+  a.items = items;
+  a.share = hdr;
+  a.seq_map = seq_map;
+
+  pa::SharePlanArgs p{};
+  p.lens = context_lens;
+  p.group_starts = group_starts;
+  p.shared_blocks = shared_blocks;
+  p.items = items;
+  p.seq_map = seq_map;
+  p.share = hdr;
+  p.num_seqs = num_seqs;
+  p.num_groups = num_groups;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.members_per_item = members_per_item(a.group);
+  p.group = a.group;
+  p.num_head_groups = a.num_head_groups;
+
+  hipError_t e = pa::launch_decode_shared(p, a, cache->head_size, hs);
+  if (owned) {
+    hipError_t fe = hipFreeAsync(ws, hs);
+    if (e == hipSuccess) e = fe;
+  }
+  if (e != hipSuccess) return hip_fail(e, "decode_shared launch");
   return ok();
 }
 

@@ -8,6 +8,27 @@
 
 namespace pa {
 
+// Sharing-aware decode: the call's work as a list of items. An item is a
+// run of one table row's blocks read once for one or more sequences: a
+// group's shared prefix for up to 32 / group of its members (its q rows are
+// consecutive), or one sequence's private tail.
+struct ShareItem {
+  int32_t row;     // table row read (a sequence index)
+  int32_t qrow;    // q rows qrow .. qrow + ntok - 1 are the item's columns
+  int32_t ntok;    // sequences served (1 for a tail)
+  int32_t b0;      // first logical block
+  int32_t n;       // positions < n are visible
+  int32_t L;       // blocks: ceil(n / 16) - b0 (>= 0)
+  int64_t ustart;  // first unit: head groups times the blocks of all earlier items
+};
+
+// Written by the plan kernel: totals of the call.
+struct ShareHeader {
+  int64_t units;
+  int32_t items;         // prefix items, then one tail item per sequence
+  int32_t prefix_items;
+};
+
 // Arguments of one decode launch, passed by value as the kernel argument.
 struct DecodeArgs {
   const uint16_t *q;             // bf16 [S, q_len, Hq, D]
@@ -31,6 +52,28 @@ struct DecodeArgs {
   int32_t num_head_groups;       // Hkv / heads_per_wg
   int32_t num_wgs;               // workgroups sharing the units evenly
   float scale_log2;              // softmax scale times log2(e)
+  // Sharing-aware decode only (null otherwise). Records of pieces: the
+  // 2 * num_wgs per-workgroup slots first, then one per (item, head group)
+  // for items that no workgroup boundary cuts.
+  const ShareItem *items;        // [2 * num_seqs + 1]: items, then a sentinel holding the total units
+  const ShareHeader *share;
+  const int2 *seq_map;           // [num_seqs]: (prefix item or -1, first column of the sequence in it)
+};
+
+// Arguments of the sharing-aware plan kernel.
+struct SharePlanArgs {
+  const int32_t *lens;           // [S]
+  const int32_t *group_starts;   // [num_groups + 1]
+  const int32_t *shared_blocks;  // [num_groups]
+  ShareItem *items;
+  int2 *seq_map;
+  ShareHeader *share;
+  int32_t num_seqs;
+  int32_t num_groups;
+  int32_t max_blocks_per_seq;
+  int32_t members_per_item;      // 32 / group
+  int32_t group;
+  int32_t num_head_groups;
 };
 
 // How a decode call is split and what scratch it needs (host only).
@@ -48,6 +91,15 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
                        int32_t head_size, int32_t max_blocks_per_seq, int32_t q_len);
 
 hipError_t launch_decode(const DecodeArgs &args, int32_t head_size, hipStream_t stream);
+
+// Largest batch the sharing-aware plan kernel takes (it keeps per-sequence
+// and per-group state in LDS).
+constexpr int32_t kMaxSharedSeqs = 4096;
+
+// Plan, decode and finalize of a sharing-aware call. args.num_cols is the
+// item width (members_per_item * group), args.q_len is 1.
+hipError_t launch_decode_shared(const SharePlanArgs &plan, const DecodeArgs &args, int32_t head_size,
+                                hipStream_t stream);
 
 hipError_t launch_reshape_and_cache(const uint16_t *k, const uint16_t *v, const int64_t *slots,
                                     uint16_t *k_cache, uint16_t *v_cache, int32_t num_tokens,

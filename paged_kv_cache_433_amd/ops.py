@@ -130,6 +130,39 @@ def decode_multi(q, k_cache, v_cache, block_tables, context_lens, scale, out=Non
     return out
 
 
+def decode_shared(q, k_cache, v_cache, block_tables, context_lens, group_starts, shared_blocks, scale,
+                  out=None, workspace=None):
+    """Decode attention for groups of sequences that share leading blocks.
+
+    ``group_starts`` int32 ``[G + 1]`` and ``shared_blocks`` int32 ``[G]`` on
+    the cache's device: group g is sequences ``group_starts[g]`` ..
+    ``group_starts[g+1]-1`` and their tables agree on the first
+    ``shared_blocks[g]`` entries. Other arguments as ``decode``.
+    """
+    desc = _cache_desc(k_cache, v_cache)
+    dev = k_cache.device
+    S, hq, d = q.shape
+    _need(q, "q", _BF16, (S, hq, k_cache.shape[3]), dev)
+    mb = block_tables.shape[1] if block_tables.dim() == 2 else -1
+    _need(block_tables, "block_tables", torch.int32, (S, mb), dev)
+    _need(context_lens, "context_lens", torch.int32, (S,), dev)
+    G = shared_blocks.shape[0] if shared_blocks.dim() == 1 else -1
+    _need(shared_blocks, "shared_blocks", torch.int32, (G,), dev)
+    _need(group_starts, "group_starts", torch.int32, (G + 1,), dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", _BF16, (S, hq, d), dev)
+    lib = _lib.lib()
+    nbytes = int(lib.pa_decode_shared_workspace_bytes(ctypes.byref(desc), S, hq, mb, G))
+    if workspace is None and nbytes:
+        workspace = _workspace(dev, nbytes)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.pa_decode_shared(ctypes.byref(desc), _ptr(q), _ptr(block_tables), _ptr(context_lens), S, hq, mb,
+                                _ptr(group_starts), _ptr(shared_blocks), G, float(scale), _ptr(out),
+                                _ptr(workspace), ws_bytes, _stream(dev)))
+    return out
+
+
 def reshape_and_cache(k, v, k_cache, v_cache, slot_mapping) -> None:
     """Scatter new tokens' K/V (bf16 ``[T, num_kv_heads, head_size]``) into
     their slots (int64 ``[T]``; negative = skip), in place, on the current stream."""

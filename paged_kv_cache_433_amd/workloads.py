@@ -460,6 +460,40 @@ def algorithmic_bytes(context_lens, num_q_heads, num_kv_heads, head_size,
     return kv + qo + tables + 4 * len(n)
 
 
+def effective_sharing(context_lens, group_starts, shared_blocks, max_blocks_per_seq,
+                      block_size=BLOCK_SIZE) -> np.ndarray:
+    """Shared blocks each group really gets: the declaration clamped to
+    ``0..max_blocks_per_seq`` and to the whole blocks every member fills
+    (int64 ``[G]``; nondecreasing ``group_starts`` within ``0..S`` assumed)."""
+    out = []
+    for g in range(len(shared_blocks)):
+        lo, hi = int(group_starts[g]), int(group_starts[g + 1])
+        if hi <= lo:
+            out.append(0)
+            continue
+        full = min(int(context_lens[j]) // block_size for j in range(lo, hi))
+        out.append(max(0, min(int(shared_blocks[g]), full, max_blocks_per_seq)))
+    return np.array(out, dtype=np.int64)
+
+
+def shared_algorithmic_bytes(context_lens, group_starts, shared_blocks, max_blocks_per_seq, num_q_heads,
+                             num_kv_heads, head_size, block_size=BLOCK_SIZE, dtype_bytes=2) -> int:
+    """Bytes a sharing-aware decode step must move: K and V of a group's
+    shared blocks once and of each member's tokens past them once, q in and
+    out back, the block-table entries read (shared ones once), the context
+    lengths and the group description."""
+    n = np.asarray(context_lens, dtype=np.int64)
+    e = effective_sharing(n, group_starts, shared_blocks, max_blocks_per_seq, block_size)
+    shared_of = np.zeros(len(n), dtype=np.int64)
+    for g in range(len(e)):
+        shared_of[int(group_starts[g]):int(group_starts[g + 1])] = e[g]
+    tokens = int(e.sum()) * block_size + int((n - shared_of * block_size).sum())
+    row = 2 * num_kv_heads * head_size * dtype_bytes
+    entries = int(e.sum()) + int(((n + block_size - 1) // block_size - shared_of).sum())
+    qo = len(n) * 2 * num_q_heads * head_size * dtype_bytes
+    return tokens * row + qo + entries * 4 + 4 * len(n) + 4 * (2 * len(e) + 1)
+
+
 def scatter_bytes(num_tokens, num_kv_heads, head_size, dtype_bytes=2) -> int:
     """Bytes of the slot scatter: read new K/V, write them, read the slots."""
     return num_tokens * (2 * num_kv_heads * head_size * dtype_bytes * 2 + 8)

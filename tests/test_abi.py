@@ -116,6 +116,33 @@ def test_decode_multi_limits(L):
             == L.pa_decode_workspace_bytes(ctypes.byref(d), 256, 32, 256))
 
 
+def test_decode_shared_limits(L):
+    d = desc()                                     # 8 KV heads of 128, groups of 4 heads
+    Sh = L.pa_decode_shared
+    W = L.pa_decode_shared_workspace_bytes
+
+    def call(S=8, mb=16, gs=P, sb=P, ng=2, q=P, ws=None, wsb=0):
+        return Sh(ctypes.byref(d), q, P, P, S, 32, mb, gs, sb, ng, 1.0, P, ws, wsb, None)
+
+    # the plan kernel holds per-sequence state in LDS: at most 4096 sequences
+    assert W(ctypes.byref(d), 4096, 32, 64, 1024) > 0
+    assert W(ctypes.byref(d), 4097, 32, 64, 1024) == 0
+    assert call(S=4097) == _lib.PA_ERR_UNSUPPORTED
+    assert call(ng=9) == _lib.PA_ERR_SHAPE and call(ng=-1) == _lib.PA_ERR_SHAPE
+    assert call(gs=None) == _lib.PA_ERR_NULL and call(sb=None) == _lib.PA_ERR_NULL
+    assert call(q=None) == _lib.PA_ERR_NULL
+    assert Sh(ctypes.byref(desc(k_cache=0, v_cache=0)), None, None, None, 0, 32, 16, None, None, 0, 1.0,
+              None, None, 0, None) == _lib.PA_OK   # empty batch
+    # items are 4 sequences x 8 query heads = 32 columns wide; records: 2 per
+    # workgroup and 1 per (item, head group), each with max, sum and 128 floats
+    S, mb, hg, ng = 256, 256, 4, 2
+    wgs = 256
+    rows = (2 * wgs + 2 * S * ng) * hg * 32
+    need = W(ctypes.byref(d), S, 32, mb, 64)
+    assert need >= (2 * S + 1) * 32 + S * 8 + rows * (128 + 2) * 4
+    assert call(S=S, mb=mb, ng=64, ws=P, wsb=need - 1) == _lib.PA_ERR_WORKSPACE
+
+
 def test_cache_op_argument_errors(L):
     d = desc()
     assert L.pa_reshape_and_cache(None, P, P, P, 1, None) == _lib.PA_ERR_NULL
