@@ -203,13 +203,15 @@ struct Walker {
   bool first;
 };
 
+// The item's fields are uniform; readfirstlane keeps them in scalar
+// registers (the buffer ranges and table reads built from them must be).
 __device__ __forceinline__ void take_item(Walker &wk, const ShareItem &x) {
-  wk.L = x.L;
-  wk.n = x.n;
-  wk.row = x.row;
-  wk.qrow = x.qrow;
-  wk.ntok = x.ntok;
-  wk.b0 = x.b0;
+  wk.L = __builtin_amdgcn_readfirstlane(x.L);
+  wk.n = __builtin_amdgcn_readfirstlane(x.n);
+  wk.row = __builtin_amdgcn_readfirstlane(x.row);
+  wk.qrow = __builtin_amdgcn_readfirstlane(x.qrow);
+  wk.ntok = __builtin_amdgcn_readfirstlane(x.ntok);
+  wk.b0 = __builtin_amdgcn_readfirstlane(x.b0);
 }
 
 template <int M>
@@ -263,6 +265,7 @@ struct Lane {
   bool col_ok[NT];       // the lane's column of tile t exists (column < q_len * group)
   int col[NT];           // that column, or the last one when it does not exist
   int qshift[NT];        // q_len - 1 - new token of the column: its causal limit is n - qshift
+  int tok[NT];           // the column's new token (kShared: its member of the segment)
   uint32_t q_off[NT];    // byte offset of the lane's 16 bytes of its column's q row (in the
                          // sequence's q rows from the KV head's first query head on)
   uint32_t out_off[NT];  // element offset of the lane's 8 outputs, same origin
@@ -272,6 +275,17 @@ struct Lane {
   long long U, E;
   uint32_t pool32;       // min(num_blocks, INT32_MAX)
   u32x2_t sel;
+};
+
+// kShared: where a block of a segment comes from. A segment is one or more
+// members of a group: first the group's shared blocks (read through the
+// first member's table, every column live), then each member's own blocks
+// past them (its own table, only its columns live).
+struct Cursor {
+  int j;    // -1: the shared blocks; else the member whose own blocks these are
+  int b;    // logical block
+  int n;    // positions < n are visible
+  int row;  // table row read
 };
 
 // One wavefront's pass over its workgroup's stream of blocks.
@@ -286,6 +300,10 @@ struct Stream {
   float m_run[NT];       // running max of base-2 logits, per column
   float l_part[NT];      // this lane's share of the running sum
   f32x4_t acc[NT][2 * NJ];
+  // kShared: cursor of block i of P, and the members' context lengths of
+  // P's and Q's segments (lane j: member j; 0 past the last member).
+  Cursor cc;
+  int lv_p, lv_q;
 };
 
 // Buffer-resource word 3 for gfx9-family raw (untyped) buffer loads.
@@ -322,15 +340,21 @@ __device__ __forceinline__ uint16_t *q_slot(uint16_t *lds, const DecodeArgs &a, 
   return lds + ((size_t)wave * 2 + (ord & 1)) * a.num_cols * (NJ * 32);
 }
 
+// The one slot per wavefront that holds the current piece's q (two tiles).
+template <int NJ>
+__device__ __forceinline__ uint16_t *q_park(uint16_t *lds, const DecodeArgs &a, int wave) {
+  return lds + (size_t)wave * a.num_cols * (NJ * 32);
+}
+
 // With two column tiles the current piece's q lives in LDS (one slot per
-// wavefront, [num_cols][D]) and is read per block: the registers to keep it
-// are not there. Each lane writes and reads only its own columns' rows (or,
-// for a missing column, the last row, written by the same wavefront), so no
-// barrier is needed.
+// wavefront, [num_cols][D]), loaded at the piece switch and read per block:
+// the registers to keep it, or to stage the next piece's, are not there.
+// Each lane writes and reads only its own columns' rows (or, for a missing
+// column, the last row, written by the same wavefront), so no barrier is
+// needed.
 template <int NJ, int NT>
-__device__ __forceinline__ void park_q(uint16_t *lds, const DecodeArgs &a, const Lane<NT> &ln,
-                                       const u32x4_t (&qv)[NT][NJ]) {
-  uint16_t *qs = lds + (size_t)ln.wave * a.num_cols * (NJ * 32) + ln.grp * 8;
+__device__ __forceinline__ void park_q(uint16_t *slot, const Lane<NT> &ln, const u32x4_t (&qv)[NT][NJ]) {
+  uint16_t *qs = slot + ln.grp * 8;
 #pragma unroll
   for (int t = 0; t < NT; ++t)
     if (ln.col_ok[t]) {
@@ -340,9 +364,8 @@ __device__ __forceinline__ void park_q(uint16_t *lds, const DecodeArgs &a, const
 }
 
 template <int NJ, int NT>
-__device__ __forceinline__ void parked_q(const uint16_t *lds, const DecodeArgs &a, const Lane<NT> &ln, int t,
-                                         u32x4_t (&qv)[NJ]) {
-  const uint16_t *qs = lds + (size_t)ln.wave * a.num_cols * (NJ * 32) + ln.col[t] * (NJ * 32) + ln.grp * 8;
+__device__ __forceinline__ void parked_q(const uint16_t *slot, const Lane<NT> &ln, int t, u32x4_t (&qv)[NJ]) {
+  const uint16_t *qs = slot + ln.col[t] * (NJ * 32) + ln.grp * 8;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) qv[j] = *reinterpret_cast<const u32x4_t *>(qs + 32 * j);
 }
@@ -358,14 +381,42 @@ __device__ __forceinline__ int block_id(const int32_t *__restrict__ tables, cons
   return (uint32_t)id < pool32 ? id : 0;
 }
 
-// Table row and first logical block of a piece's segment.
-template <int M>
-__device__ __forceinline__ int table_row(const Piece &p) {
-  if constexpr (M == kShared) return p.row; else return p.s;
+// kShared: the context lengths of a segment's members (clamped), lane j
+// holding member j's; lanes past the last member read 0.
+__device__ __forceinline__ int member_lens(const int32_t *__restrict__ lens, const Piece &p, int cap, int lane) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int32_t *>(lens + p.qrow), 0, p.ntok * (int)sizeof(int32_t), kRawBufferWord3);
+  return clamp_len((int)__builtin_amdgcn_raw_buffer_load_b32(r, lane * (int)sizeof(int32_t), 0, 0), cap);
 }
-template <int M>
-__device__ __forceinline__ int first_block(const Piece &p) {
-  if constexpr (M == kShared) return p.b0; else return 0;
+
+// kShared: cursor of the segment's block at unit offset p.off (the piece's
+// first block). Every member fills the b0 shared blocks, so each member owns
+// ceil(n_j / 16) - b0 >= 0 blocks after them.
+__device__ __forceinline__ Cursor seg_first(const Piece &p, int lv) {
+  int r = p.off;
+  if (r < p.b0) return Cursor{-1, r, p.b0 * kBlock, p.row};
+  r -= p.b0;
+  Cursor c{-1, 0, 0, p.row};
+  for (int j = 0; j < p.ntok; ++j) {
+    const int nj = __builtin_amdgcn_readlane(lv, j);
+    const int lj = ((nj + kBlock - 1) >> 4) - p.b0;
+    c = Cursor{j, p.b0 + r, nj, p.qrow + j};
+    if (r < lj) break;
+    r -= lj;
+  }
+  return c;
+}
+
+// kShared: cursor of the segment's block after c (the same member's next
+// block, else the next member with blocks of its own).
+__device__ __forceinline__ Cursor seg_next(const Piece &p, const Cursor &c, int lv) {
+  const int end = c.j < 0 ? p.b0 : (c.n + kBlock - 1) >> 4;
+  if (c.b + 1 < end) return Cursor{c.j, c.b + 1, c.n, c.row};
+  for (int j = c.j + 1; j < p.ntok; ++j) {
+    const int nj = __builtin_amdgcn_readlane(lv, j);
+    if (((nj + kBlock - 1) >> 4) > p.b0) return Cursor{j, p.b0, nj, p.qrow + j};
+  }
+  return c;  // past the segment's end: not reached inside a piece
 }
 
 // Element offset of the wavefront's KV head inside a token row (uniform).
@@ -415,47 +466,39 @@ __device__ __forceinline__ void finish_piece(const DecodeArgs &a, const Lane<NT>
   const Piece &P = st.P;
   const bool whole = P.off == 0 && P.cnt == P.L;
   const int g = P.hg * ln.HG + ln.wave;
-  if constexpr (M == kShared) {
-    // Every piece leaves a record: the item's own when the piece is the
-    // whole segment, else the workgroup's slot. The finalize kernel merges
-    // each sequence's records (its prefix item's column and its tail).
-    const size_t rec = whole ? (size_t)2 * a.num_wgs + (size_t)P.s * ln.NG + P.hg : (size_t)2 * ln.w + (P.first ? 0 : 1);
-    const int live = P.ntok * a.group;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      float l = st.l_part[t] + __shfl_xor(st.l_part[t], 16);
-      l += __shfl_xor(l, 32);
-      if (ln.col_ok[t] && ln.col[t] < live) {
-        const size_t row = (rec * ln.HG + ln.wave) * a.num_cols + ln.col[t];
-        float *po = a.part_o + row * D + ln.grp * 8;
-#pragma unroll
-        for (int k = 0; k < 2 * NJ; ++k)
-          *reinterpret_cast<f32x4_t *>(po + 32 * (k >> 1) + 4 * (k & 1)) = st.acc[t][k];
-        if (ln.grp == 0) *reinterpret_cast<f32x2_t *>(a.part_ml + row * 2) = f32x2_t{st.m_run[t], l};
-      }
-    }
-    return;
-  }
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     float l = st.l_part[t] + __shfl_xor(st.l_part[t], 16);
     l += __shfl_xor(l, 32);
+    // kShared: a segment serves ntok members (their q rows from qrow on).
+    const bool keep = M == kShared ? ln.col_ok[t] && ln.col[t] < P.ntok * a.group : ln.col_ok[t];
     if (whole) {
       // With several new tokens a column can see no position at all (only
-      // if a context is shorter than q_len); it is written as zeros.
-      const float inv = kMulti ? (l > 0.f ? 1.f / l : 0.f) : 1.f / l;
-      if (ln.col_ok[t])
-        store_out<NJ>(a.out + ((size_t)P.s * a.q_len * a.num_q_heads + (size_t)g * a.group) * D + ln.out_off[t],
-                      st.acc[t], inv);
+      // if a context is shorter than q_len), and so can an empty member of a
+      // segment; it is written as zeros.
+      const float inv = (kMulti || M == kShared) ? (l > 0.f ? 1.f / l : 0.f) : 1.f / l;
+      const size_t row0 = M == kShared ? (size_t)P.qrow : (size_t)P.s * a.q_len;
+      if (keep)
+        store_out<NJ>(a.out + (row0 * a.num_q_heads + (size_t)g * a.group) * D + ln.out_off[t], st.acc[t], inv);
     } else {
       const int slot = P.first ? 0 : 1;
       const size_t row = (((size_t)ln.w * 2 + slot) * ln.HG + ln.wave) * a.num_cols + ln.col[t];
-      if (ln.col_ok[t]) {
+      if (keep) {
         float *po = a.part_o + row * D + ln.grp * 8;
 #pragma unroll
         for (int k = 0; k < 2 * NJ; ++k)
           *reinterpret_cast<f32x4_t *>(po + 32 * (k >> 1) + 4 * (k & 1)) = st.acc[t][k];
-        if (ln.grp == 0) *reinterpret_cast<f32x2_t *>(a.part_ml + row * 2) = f32x2_t{st.m_run[t], l};
+        // With two tiles, two scalar stores: building a float2 from m_run[t]
+        // lets the compiler widen that read over m_run[t + 1], which pins the
+        // array to scratch, and every reload then waits for all loads in flight.
+        if (ln.grp == 0) {
+          if constexpr (NT == 1) {
+            *reinterpret_cast<f32x2_t *>(a.part_ml + row * 2) = f32x2_t{st.m_run[t], l};
+          } else {
+            a.part_ml[row * 2] = st.m_run[t];
+            a.part_ml[row * 2 + 1] = l;
+          }
+        }
       }
     }
   }
@@ -485,7 +528,7 @@ __device__ __forceinline__ void advance(const DecodeArgs &a, const Lane<NT> &ln,
   } else {
     u32x4_t qv[NT][NJ];
     load_q<NJ, NT, M>(a, ln, st.P, qv);
-    park_q<NJ>(lds, a, ln, qv);
+    park_q<NJ>(q_park<NJ>(lds, a, ln.wave), ln, qv);
   }
   st.hoff = st.hoff_q;
   st.i = 0;
@@ -499,6 +542,10 @@ __device__ __forceinline__ void advance(const DecodeArgs &a, const Lane<NT> &ln,
   st.has_q = next_piece<M>(wk, st.Q);
   if (!st.has_q) st.Q = st.P;
   st.hoff_q = head_off<NJ>(ln, st.Q);
+  if constexpr (M == kShared) {
+    st.lv_p = st.lv_q;
+    st.lv_q = member_lens(wk.lens, st.Q, wk.cap, ln.lane);
+  }
 }
 
 // Computes block i of P from (K, V) after starting the next block of the
@@ -525,36 +572,49 @@ __device__ __forceinline__ bool step(const int32_t *__restrict__ tables, const D
   const int nx = st.i + 1;
   const bool in_p = nx < P.cnt;
   const bool to_q = !in_p && st.has_q;
-  const int next_row = to_q ? table_row<M>(st.Q) : table_row<M>(P);
-  const int next_b = (in_p ? P.off + nx : (to_q ? st.Q.off : P.off + st.i)) +
-                     (to_q ? first_block<M>(st.Q) : first_block<M>(P));
-  issue<NJ>(a, ln, block_id(tables, a, ln.pool32, next_row, next_b), to_q ? st.hoff_q : st.hoff,
-            rows_in(to_q ? st.Q.n : P.n, next_b), Kn, Vn);
+  Cursor cn;
+  if constexpr (M == kShared) {
+    cn = in_p ? seg_next(P, st.cc, st.lv_p) : (to_q ? seg_first(st.Q, st.lv_q) : st.cc);
+    issue<NJ>(a, ln, block_id(tables, a, ln.pool32, cn.row, cn.b), to_q ? st.hoff_q : st.hoff,
+              rows_in(cn.n, cn.b), Kn, Vn);
+  } else {
+    const int next_s = to_q ? st.Q.s : P.s;
+    const int next_b = in_p ? P.off + nx : (to_q ? st.Q.off : P.off + st.i);
+    issue<NJ>(a, ln, block_id(tables, a, ln.pool32, next_s, next_b), to_q ? st.hoff_q : st.hoff,
+              rows_in(to_q ? st.Q.n : P.n, next_b), Kn, Vn);
+  }
   // Keep the scheduler from sinking those loads below the compute.
   __builtin_amdgcn_sched_barrier(0);
 
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
-  const int b = first_block<M>(P) + P.off + st.i;
+  const int b = M == kShared ? st.cc.b : P.off + st.i;
   const int pos0 = b * kBlock + ln.grp * 4;
-  // kShared: an item of one sequence fills only the first tile.
-  const int live = M == kShared ? P.ntok * a.group : a.num_cols;
+  // kShared: in a member's own blocks only that member's columns are live,
+  // and a tile holding none of them is skipped (a uniform branch).
+  const int cj = M == kShared ? st.cc.j : -1;
+  auto tile_live = [&](int t) {
+    return M != kShared || cj < 0 || (cj * a.group < 16 * (t + 1) && (cj + 1) * a.group > 16 * t);
+  };
   u32x2_t pb_hi[NT], pb_lo[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    if (M == kShared && t > 0 && live <= 16 * t) continue;
+    if (!tile_live(t)) continue;
     f32x4_t sc = zero4;
     if constexpr (NT == 1) {
 #pragma unroll
       for (int j = 0; j < NJ; ++j) sc = mfma32(K[j], st.qv[t][j], sc);
     } else {
       u32x4_t qv[NJ];
-      parked_q<NJ>(lds, a, ln, t, qv);
+      parked_q<NJ>(q_park<NJ>(lds, a, ln.wave), ln, t, qv);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) sc = mfma32(K[j], qv[j], sc);
     }
     // Positions past the column's causal limit (the context length for a
-    // single new token) are masked.
-    const int lim = kMulti ? P.n - ln.qshift[t] : P.n;
+    // single new token) are masked, and so are a dead column's.
+    int lim;
+    if constexpr (kMulti) lim = P.n - ln.qshift[t];
+    else if constexpr (M == kShared) lim = (cj < 0 || ln.tok[t] == cj) ? st.cc.n : 0;
+    else lim = P.n;
     float z[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) z[r] = (pos0 + r < lim) ? sc[r] * a.scale_log2 : -INFINITY;
@@ -564,7 +624,7 @@ __device__ __forceinline__ bool step(const int32_t *__restrict__ tables, const D
     // With one new token, position b*16 is always visible, so the max is
     // finite. With several, a column may see nothing in this block yet.
     const float m_new = fmaxf(st.m_run[t], mx);
-    const float m_use = kMulti ? (m_new == -INFINITY ? 0.f : m_new) : m_new;
+    const float m_use = (kMulti || M == kShared) ? (m_new == -INFINITY ? 0.f : m_new) : m_new;
     const float alpha = fast_exp2(st.m_run[t] - m_use);
     st.m_run[t] = m_new;
 
@@ -580,7 +640,7 @@ __device__ __forceinline__ bool step(const int32_t *__restrict__ tables, const D
   }
 
   // V rows of tokens at or past n must not reach the sum, even as NaN * 0.
-  const bool v_live = b * kBlock + ln.c < P.n;
+  const bool v_live = b * kBlock + ln.c < (M == kShared ? st.cc.n : P.n);
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
 #pragma unroll
@@ -590,24 +650,17 @@ __device__ __forceinline__ bool step(const int32_t *__restrict__ tables, const D
       const u32x2_t av = {pack_hi(tv[0], tv[1]), pack_hi(tv[2], tv[3])};
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        if (M == kShared && t > 0 && live <= 16 * t) continue;
+        if (!tile_live(t)) continue;
         st.acc[t][2 * j + h] = mfma16(av, pb_hi[t], st.acc[t][2 * j + h]);
         st.acc[t][2 * j + h] = mfma16(av, pb_lo[t], st.acc[t][2 * j + h]);
       }
     }
   }
 
-  if (stage_q) {
-    uint16_t *qs = q_slot<NJ>(lds, a, ln.wave, st.ord + 1) + ln.grp * 8;
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-      if (ln.col_ok[t]) {
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) *reinterpret_cast<u32x4_t *>(qs + ln.col[t] * (NJ * 32) + 32 * j) = qt[t][j];
-      }
-  }
+  if (stage_q) park_q<NJ>(q_slot<NJ>(lds, a, ln.wave, st.ord + 1), ln, qt);
 
   st.i = nx;
+  if constexpr (M == kShared) st.cc = cn;
   if (in_p) return true;
   finish_piece<NJ, NT, M>(a, ln, st);
   if (!st.has_q) return false;
@@ -636,7 +689,8 @@ __device__ __forceinline__ void no_merge(const DecodeArgs &a, int w, int tid) {
 // whole register file (arch and accumulation registers).
 template <int D, int NT, int M>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2 : 1)))
-void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const int32_t *__restrict__ lens) {
+void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const int32_t *__restrict__ lens,
+                   const ShareItem *__restrict__ items) {
   constexpr int NJ = D / 32;  // MFMA steps over head_size; 16-byte loads per lane per row
   static_assert(NJ >= 1 && D % 32 == 0, "head_size must be a multiple of 32");
   extern __shared__ __align__(16) uint16_t q_lds[];  // heads_per_wg * (NT == 1 ? 2 : 1) * num_cols * D
@@ -662,21 +716,31 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
     const ShareHeader h = *a.share;
     U = h.units;
     E = U < W ? U : W;
-    if (w >= E) return;
+    if (w >= E) {  // every workgroup writes its merge record, this one "none"
+      no_merge(a, w, tid);
+      return;
+    }
     lo = range_lo(w, U, E);
     hi = range_lo(w + 1, U, E);
     if (tid == 0) found_seq = -1;
     __syncthreads();
     for (int v = tid; v < h.items; v += nthr)
-      if (a.items[v].ustart <= lo && lo < a.items[v + 1].ustart) found_seq = v;
+      if (items[v].ustart <= lo && lo < items[v + 1].ustart) found_seq = v;
     __syncthreads();
-    if (found_seq < 0) return;  // only if the plan is inconsistent
+    if (found_seq < 0) {  // only if the plan is inconsistent
+      no_merge(a, w, tid);
+      return;
+    }
     const int v = __builtin_amdgcn_readfirstlane(found_seq);
-    wk.items = a.items;
+    wk.items = items;
+    wk.lens = lens;
+    wk.cap = cap;
     wk.S = h.items;
-    take_item(wk, a.items[v]);
+    take_item(wk, items[v]);
     wk.s = v;
-    wk.seg_base = a.items[v].ustart;
+    const long long us = items[v].ustart;
+    wk.seg_base = (long long)(((unsigned long long)(unsigned)__builtin_amdgcn_readfirstlane((int)(us >> 32)) << 32) |
+                              (unsigned)__builtin_amdgcn_readfirstlane((int)us));
   } else if (S <= nthr) {
     // One pass: every thread holds one sequence's block count; a block scan
     // gives the total and every sequence's first unit at once.
@@ -736,7 +800,10 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
       if (found_seq >= 0) break;
       before += chunk_total;
     }
-    if (found_seq < 0) return;  // only if the lengths changed during the call
+    if (found_seq < 0) {  // only if the lengths changed during the call
+      no_merge(a, w, tid);
+      return;
+    }
   }
 
   if constexpr (M != kShared) {
@@ -776,6 +843,7 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
     const int tok = ln.col[t] / a.group;
     const int qh = ln.col[t] - tok * a.group;
     ln.qshift[t] = a.q_len - 1 - tok;
+    ln.tok[t] = tok;
     ln.out_off[t] = (uint32_t)((tok * a.num_q_heads + qh) * D + ln.grp * 8);
     ln.q_off[t] = ln.out_off[t] * (uint32_t)sizeof(uint16_t);
   }
@@ -803,12 +871,17 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
   } else {
     u32x4_t qv[NT][NJ];
     load_q<NJ, NT, M>(a, ln, st.P, qv);
-    park_q<NJ>(q_lds, a, ln, qv);
+    park_q<NJ>(q_park<NJ>(q_lds, a, wave), ln, qv);
   }
   st.hoff = head_off<NJ>(ln, st.P);
   st.has_q = next_piece<M>(wk, st.Q);
   if (!st.has_q) st.Q = st.P;
   st.hoff_q = head_off<NJ>(ln, st.Q);
+  if constexpr (M == kShared) {
+    st.lv_p = member_lens(lens, st.P, cap, lane);
+    st.lv_q = member_lens(lens, st.Q, cap, lane);
+    st.cc = seg_first(st.P, st.lv_p);
+  }
   st.i = 0;
   st.ord = 0;
 #pragma unroll
@@ -819,9 +892,11 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
     for (int k = 0; k < 2 * NJ; ++k) st.acc[t][k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
   u32x4_t KA[NJ], VA[NJ], KB[NJ], VB[NJ];
-  const int b_first = first_block<M>(st.P) + st.P.off;
-  issue<NJ>(a, ln, block_id(tables, a, ln.pool32, table_row<M>(st.P), b_first), st.hoff, rows_in(st.P.n, b_first),
-            KA, VA);
+  if constexpr (M == kShared) {
+    issue<NJ>(a, ln, block_id(tables, a, ln.pool32, st.cc.row, st.cc.b), st.hoff, rows_in(st.cc.n, st.cc.b), KA, VA);
+  } else {
+    issue<NJ>(a, ln, block_id(tables, a, ln.pool32, st.P.s, st.P.off), st.hoff, rows_in(st.P.n, st.P.off), KA, VA);
+  }
   while (step<NJ, NT, M>(tables, a, ln, wk, st, KA, VA, KB, VB, q_lds) &&
          step<NJ, NT, M>(tables, a, ln, wk, st, KB, VB, KA, VA, q_lds)) {
   }
@@ -833,7 +908,7 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
 // ended, if any. One wavefront per column; lane i owns head dims
 // [i*D/64, (i+1)*D/64). The pieces are read in one pass with a running
 // rescale.
-template <int D>
+template <int D, bool kSegments>
 __global__ __launch_bounds__(1024) void merge_kernel(const DecodeArgs a) {
   constexpr int PL = D / 64;  // dims per lane: 1 or 2
   const int w1 = blockIdx.x;
@@ -850,6 +925,13 @@ __global__ __launch_bounds__(1024) void merge_kernel(const DecodeArgs a) {
   const int qh = c - tok * a.group;
   const int w0 = d.y >> 1;
   const int HG = a.heads_per_wg;
+  // Output rows: the sequence's q_len rows, or a segment's members (kShared).
+  size_t row0 = (size_t)s * a.q_len;
+  if constexpr (kSegments) {
+    const ShareItem x = a.items[s];
+    if (c >= x.ntok * a.group) return;
+    row0 = (size_t)x.qrow;
+  }
 
   // Pieces: slot d.y & 1 of workgroup w0, then the first slot of every
   // workgroup up to w1 (whose ranges all lie inside the segment). Four at a
@@ -897,7 +979,7 @@ __global__ __launch_bounds__(1024) void merge_kernel(const DecodeArgs a) {
     M = Mn;
   }
   const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
-  uint16_t *dst = a.out + (((size_t)s * a.q_len + tok) * a.num_q_heads + (size_t)g * a.group + qh) * D + lane * PL;
+  uint16_t *dst = a.out + ((row0 + tok) * a.num_q_heads + (size_t)g * a.group + qh) * D + lane * PL;
   if constexpr (PL == 2) {
     *reinterpret_cast<uint32_t *>(dst) = to_bf16x2(o[0] * inv, o[1] * inv);
   } else {
@@ -934,29 +1016,31 @@ __device__ __forceinline__ int wg_max_scan(int v, int *red, int wave, int lane, 
   return max(v, pre);
 }
 
-// Builds the call's items in one workgroup.
+// Builds the call's segments in one workgroup.
 //   * group_starts must not decrease and must stay within 0..S; otherwise no
 //     group is formed and every sequence reads its own table.
 //   * A sequence's group is the last one that starts at or before it (a
 //     max-scan of start marks), if the sequence lies before its end.
-//   * A group's shared blocks are clamped to 0..max_blocks_per_seq and to the
-//     whole blocks each member fills.
-//   * Items: one prefix item per run of members_per_item consecutive members
-//     of every group with shared blocks (read through the first member's
-//     table), then one tail item per sequence (its blocks past the shared
-//     ones). Units follow item order, head group major within an item.
+//   * A group's shared blocks e are clamped to 0..max_blocks_per_seq and to
+//     the whole blocks each member fills.
+//   * Segments: each run of members_per_item consecutive members of a group,
+//     and each sequence in no group, is one segment: the e shared blocks
+//     (through the first member's table), then every member's own blocks past
+//     them. Units follow segment order, head group major within a segment.
+//   * A segment with no block at all (every member's context empty) is not
+//     decoded: its members' outputs are zeroed here.
 template <int kThreads>
 __global__ __launch_bounds__(kThreads) void share_plan_kernel(const SharePlanArgs p) {
-  extern __shared__ __align__(16) int plan_lds[];  // grp[S], shb[G], ibase[G], then pblk[G] (64-bit)
+  extern __shared__ __align__(16) int plan_lds[];  // grp[S], sid[S], shb[G], then csum[S] (64-bit)
   __shared__ long long red[kThreads / 64];
   __shared__ int redi[kThreads / 64];
   __shared__ int bad;
   constexpr int nwaves = kThreads / 64;
   const int S = p.num_seqs, NGr = p.num_groups, C = p.members_per_item;
   int *grp = plan_lds;
-  int *shb = grp + S;
-  int *ibase = shb + NGr;
-  long long *pblk = reinterpret_cast<long long *>(plan_lds + ((S + 2 * NGr + 1) & ~1));
+  int *sid = grp + S;
+  int *shb = sid + S;
+  long long *csum = reinterpret_cast<long long *>(plan_lds + ((2 * S + NGr + 1) & ~1));
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int cap = p.max_blocks_per_seq * kBlock;
 
@@ -995,141 +1079,62 @@ __global__ __launch_bounds__(kThreads) void share_plan_kernel(const SharePlanArg
   }
   __syncthreads();
 
-  // Prefix items and blocks per group, scanned.
-  int items_before = 0;
-  long long blocks_before = 0;
-  for (int base = 0; base < NGr; base += kThreads) {
-    const int g = base + tid;
-    int nsub = 0;
-    long long blocks = 0;
-    if (g < NGr && valid) {
-      const int m = p.group_starts[g + 1] - p.group_starts[g];
-      if (m > 0 && shb[g] > 0) {
-        nsub = (m + C - 1) / C;
-        blocks = (long long)nsub * shb[g];
-      }
+  // Per sequence: does it open a segment, and the blocks it adds (its own
+  // past the shared ones, and the shared ones too if it opens the segment).
+  long long segs_before = 0, blocks_before = 0;
+  for (int base = 0; base < S; base += kThreads) {
+    const int i = base + tid;
+    long long opens = 0, adds = 0;
+    if (i < S) {
+      const int n = clamp_len(p.lens[i], cap);
+      const int g = grp[i];
+      const int e = g >= 0 ? shb[g] : 0;
+      opens = (g < 0 || (i - p.group_starts[g]) % C == 0) ? 1 : 0;
+      adds = (n + kBlock - 1) / kBlock - e + (opens ? e : 0);
     }
     long long pre, tot, preb, totb;
-    const long long incl = wg_scan((long long)nsub, red, wave, lane, nwaves, pre, tot);
-    const long long inclb = wg_scan(blocks, red, wave, lane, nwaves, preb, totb);
-    if (g < NGr) {
-      ibase[g] = items_before + (int)(pre + incl - nsub);
-      pblk[g] = blocks_before + preb + inclb - blocks;
+    const long long incl = wg_scan(opens, red, wave, lane, nwaves, pre, tot);
+    const long long inclb = wg_scan(adds, red, wave, lane, nwaves, preb, totb);
+    if (i < S) {
+      sid[i] = (int)(segs_before + pre + incl - 1);
+      csum[i] = blocks_before + preb + inclb;
     }
-    items_before += (int)tot;
+    segs_before += tot;
     blocks_before += totb;
   }
   __syncthreads();
-  const int Vp = items_before;
   const long long NG = p.num_head_groups;
-
-  long long tail_before = 0;
-  for (int base = 0; base < S; base += kThreads) {
-    const int i = base + tid;
-    int b0 = 0, n = 0;
-    int2 map = {-1, 0};
-    if (i < S) {
-      n = clamp_len(p.lens[i], cap);
-      const int g = grp[i];
-      if (g >= 0 && shb[g] > 0) {
-        const int lo = p.group_starts[g], hi = p.group_starts[g + 1];
-        const int k = i - lo, sub = k / C;
-        b0 = shb[g];
-        map = int2{ibase[g] + sub, (k - sub * C) * p.group};
-        if (k == sub * C) {
-          ShareItem x;
-          x.row = lo;
-          x.qrow = i;
-          x.ntok = min(C, hi - i);
-          x.b0 = 0;
-          x.n = shb[g] * kBlock;
-          x.L = shb[g];
-          x.ustart = NG * (pblk[g] + (long long)sub * shb[g]);
-          p.items[ibase[g] + sub] = x;
-        }
-      }
+  for (int i = tid; i < S; i += kThreads) {
+    const int g = grp[i];
+    if (g >= 0 && (i - p.group_starts[g]) % C != 0) continue;  // not the first member of its segment
+    const int lo = g >= 0 ? p.group_starts[g] : i;
+    const int hi = g >= 0 ? p.group_starts[g + 1] : i + 1;
+    const int ntok = min(C, hi - i);
+    const long long start = i > 0 ? csum[i - 1] : 0;
+    const long long blocks = csum[i + ntok - 1] - start;
+    const int e = g >= 0 ? shb[g] : 0;
+    ShareItem x;
+    x.row = lo;
+    x.qrow = i;
+    x.ntok = ntok;
+    x.b0 = e;
+    x.n = e * kBlock;
+    x.L = (int)blocks;
+    x.ustart = NG * start;
+    p.items[sid[i]] = x;
+    if (blocks == 0) {  // every member's context is empty
+      u32x4_t *row = reinterpret_cast<u32x4_t *>(p.out + (size_t)i * p.row_elems);
+      for (size_t k = 0; k < (size_t)ntok * p.row_elems / 8; ++k) row[k] = u32x4_t{0, 0, 0, 0};
     }
-    const long long Lt = i < S ? (long long)((n + kBlock - 1) / kBlock - b0) : 0;
-    long long pre, tot;
-    const long long incl = wg_scan(Lt, red, wave, lane, nwaves, pre, tot);
-    if (i < S) {
-      ShareItem x;
-      x.row = i;
-      x.qrow = i;
-      x.ntok = 1;
-      x.b0 = b0;
-      x.n = n;
-      x.L = (int)Lt;
-      x.ustart = NG * (blocks_before + tail_before + pre + incl - Lt);
-      p.items[Vp + i] = x;
-      p.seq_map[i] = map;
-    }
-    tail_before += tot;
   }
   if (tid == 0) {
-    const long long units = NG * (blocks_before + tail_before);
+    const long long units = NG * blocks_before;
     ShareItem x = {0, 0, 0, 0, 0, 0, units};
-    p.items[Vp + S] = x;  // sentinel: the end of the last item
+    p.items[segs_before] = x;  // sentinel: the end of the last segment
     ShareHeader h;
     h.units = units;
-    h.items = Vp + S;
-    h.prefix_items = Vp;
+    h.items = (int)segs_before;
     *p.share = h;
-  }
-}
-
-// For every sequence and query head: merges the records of its column in
-// its prefix item and of its tail item with log-sum-exp weights, and writes
-// the bf16 output. Grid (S, Hkv, ceil(group / 16)), one wavefront per query
-// head; lane i owns head dims [i*D/64, (i+1)*D/64).
-template <int D>
-__global__ __launch_bounds__(1024) void share_finalize_kernel(const DecodeArgs a) {
-  constexpr int PL = D / 64;
-  const int s = blockIdx.x, g = blockIdx.y;
-  const int qh = (threadIdx.x >> 6) + 16 * blockIdx.z;
-  if (qh >= a.group) return;
-  const int lane = threadIdx.x & 63;
-  const int HG = a.heads_per_wg, NG = a.num_head_groups;
-  const int hg = g / HG, k = g - hg * HG;
-  const ShareHeader h = *a.share;
-  const long long U = h.units, W = a.num_wgs, E = U < W ? U : W;
-  float M = -INFINITY, Lsum = 0.f, o[PL];
-#pragma unroll
-  for (int i = 0; i < PL; ++i) o[i] = 0.f;
-  auto fold = [&](size_t rec, int col) {
-    const size_t r = (rec * HG + k) * a.num_cols + col;
-    const f32x2_t ml = *reinterpret_cast<const f32x2_t *>(a.part_ml + r * 2);
-    const float Mn = fmaxf(M, ml[0]);
-    const float Mu = Mn == -INFINITY ? 0.f : Mn;
-    const float so = fast_exp2(M - Mu), wt = fast_exp2(ml[0] - Mu);
-    Lsum = Lsum * so + wt * ml[1];
-#pragma unroll
-    for (int i = 0; i < PL; ++i) o[i] = o[i] * so + wt * a.part_o[r * D + lane * PL + i];
-    M = Mn;
-  };
-  // The records of item v's segment for head group hg: the item's own when
-  // one workgroup holds the whole segment, else one per workgroup it spans.
-  auto fold_item = [&](int v, int col) {
-    const ShareItem x = a.items[v];
-    if (x.L <= 0) return;
-    const long long seg0 = x.ustart + (long long)hg * x.L, seg1 = seg0 + x.L;
-    const int w0 = owner_of(seg0, U, E), w1 = owner_of(seg1 - 1, U, E);
-    if (w0 == w1) {
-      fold((size_t)2 * a.num_wgs + (size_t)v * NG + hg, col);
-      return;
-    }
-    fold((size_t)2 * w0 + (range_lo(w0, U, E) < seg0 ? 1 : 0), col);
-    for (int w = w0 + 1; w <= w1; ++w) fold((size_t)2 * w, col);
-  };
-  fold_item(h.prefix_items + s, qh);
-  const int2 m = a.seq_map[s];
-  if (m.x >= 0) fold_item(m.x, m.y + qh);
-  const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
-  uint16_t *dst = a.out + ((size_t)s * a.num_q_heads + (size_t)g * a.group + qh) * D + lane * PL;
-  if constexpr (PL == 2) {
-    *reinterpret_cast<uint32_t *>(dst) = to_bf16x2(o[0] * inv, o[1] * inv);
-  } else {
-    dst[0] = (uint16_t)(to_bf16x2(o[0] * inv, 0.f) & 0xFFFFu);
   }
 }
 
@@ -1148,7 +1153,7 @@ hipError_t launch_decode_kernel(const DecodeArgs &args, size_t lds, hipStream_t 
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_kernel<D, NT, M>), dim3((unsigned)args.num_wgs),
                      dim3(64 * (unsigned)args.heads_per_wg), lds, stream, args, args.block_tables,
-                     args.context_lens);
+                     args.context_lens, args.items);
   return hipGetLastError();
 }
 
@@ -1180,9 +1185,9 @@ hipError_t launch_decode(const DecodeArgs &args, int32_t head_size, hipStream_t 
   const dim3 mgrid((unsigned)args.num_wgs, (unsigned)args.heads_per_wg, tiles);
   const dim3 mblock(64 * (unsigned)(args.num_cols < 16 ? args.num_cols : 16));
   if (head_size == 128) {
-    hipLaunchKernelGGL(merge_kernel<128>, mgrid, mblock, 0, stream, args);
+    hipLaunchKernelGGL((merge_kernel<128, false>), mgrid, mblock, 0, stream, args);
   } else {
-    hipLaunchKernelGGL(merge_kernel<64>, mgrid, mblock, 0, stream, args);
+    hipLaunchKernelGGL((merge_kernel<64, false>), mgrid, mblock, 0, stream, args);
   }
   return hipGetLastError();
 }
@@ -1190,29 +1195,29 @@ hipError_t launch_decode(const DecodeArgs &args, int32_t head_size, hipStream_t 
 hipError_t launch_decode_shared(const SharePlanArgs &plan, const DecodeArgs &args, int32_t head_size,
                                 hipStream_t stream) {
   if (args.q_len != 1 || args.num_cols <= 16 || args.num_cols > 32 || !args.items || !args.share ||
-      !args.seq_map || plan.num_seqs < 1 || plan.num_seqs > kMaxSharedSeqs || plan.num_groups < 0 ||
-      plan.num_groups > plan.num_seqs || plan.members_per_item < 1)
+      plan.num_seqs < 1 || plan.num_seqs > kMaxSharedSeqs || plan.num_groups < 0 ||
+      plan.num_groups > plan.num_seqs || plan.members_per_item < 1 || !plan.out || plan.row_elems % 8)
     return hipErrorInvalidValue;
   if (head_size != 128 && head_size != 64) return hipErrorInvalidValue;
   constexpr int kPlanThreads = 512;
-  const size_t plan_lds = (((size_t)plan.num_seqs + 2 * (size_t)plan.num_groups + 1) & ~(size_t)1) * sizeof(int) +
-                          (size_t)plan.num_groups * sizeof(long long);
+  const size_t plan_lds = ((2 * (size_t)plan.num_seqs + plan.num_groups + 1) & ~(size_t)1) * sizeof(int) +
+                          (size_t)plan.num_seqs * sizeof(long long);
   hipError_t e = allow_lds(share_plan_kernel<kPlanThreads>, plan_lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(share_plan_kernel<kPlanThreads>, dim3(1), dim3(kPlanThreads), plan_lds, stream, plan);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // q of the current piece is parked in LDS: one [num_cols][D] slot per wavefront.
+  // q of the current piece in LDS: one [num_cols][D] slot per wavefront.
   const size_t lds = (size_t)args.heads_per_wg * args.num_cols * head_size * sizeof(uint16_t);
   e = head_size == 128 ? launch_decode_kernel<128, 2, kShared>(args, lds, stream)
                        : launch_decode_kernel<64, 2, kShared>(args, lds, stream);
-  if (e != hipSuccess) return e;
-  const dim3 fgrid((unsigned)args.num_seqs, (unsigned)args.num_kv_heads, (unsigned)((args.group + 15) / 16));
-  const dim3 fblock(64 * (unsigned)(args.group < 16 ? args.group : 16));
+  if (e != hipSuccess || args.num_wgs <= 1) return e;
+  const dim3 mgrid((unsigned)args.num_wgs, (unsigned)args.heads_per_wg, (unsigned)((args.num_cols + 15) / 16));
+  const dim3 mblock(64 * 16);
   if (head_size == 128) {
-    hipLaunchKernelGGL(share_finalize_kernel<128>, fgrid, fblock, 0, stream, args);
+    hipLaunchKernelGGL((merge_kernel<128, true>), mgrid, mblock, 0, stream, args);
   } else {
-    hipLaunchKernelGGL(share_finalize_kernel<64>, fgrid, fblock, 0, stream, args);
+    hipLaunchKernelGGL((merge_kernel<64, true>), mgrid, mblock, 0, stream, args);
   }
   return hipGetLastError();
 }

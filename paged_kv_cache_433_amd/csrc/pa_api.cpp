@@ -107,12 +107,13 @@ int check_q_len(const pa_kv_cache *c, int32_t num_q_heads, int32_t q_len) {
 // columns are their query heads of one KV head: at most two MFMA tiles).
 int32_t members_per_item(int32_t group) { return 32 / group; }
 
-// Workspace of pa_decode_shared: header, items (+ sentinel), sequence map,
-// then piece records: 2 per workgroup, then one per (item, head group).
+// Workspace of pa_decode_shared: header, segments (+ sentinel), merge
+// records (one per workgroup), then the partial records of cut segments
+// (2 per workgroup).
 struct SharedLayout {
   pa::DecodePlan plan;
   int32_t cols;
-  size_t items_off, map_off, ml_off, o_off, total;
+  size_t items_off, desc_off, ml_off, o_off, total;
 };
 
 SharedLayout layout_shared(const pa_kv_cache *c, int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq) {
@@ -120,15 +121,13 @@ SharedLayout layout_shared(const pa_kv_cache *c, int32_t num_seqs, int32_t num_q
   const int32_t group = num_q_heads / c->num_kv_heads;
   l.plan.heads_per_wg = heads_per_workgroup(c->num_kv_heads);
   l.plan.num_head_groups = c->num_kv_heads / l.plan.heads_per_wg;
-  // Up to one prefix item and one tail item per sequence, each at most
-  // max_blocks_per_seq blocks.
-  l.plan.num_wgs = decode_wgs(2 * (int64_t)num_seqs, l.plan.num_head_groups, l.plan.heads_per_wg, max_blocks_per_seq);
+  // A segment holds at most max_blocks_per_seq blocks per member.
+  l.plan.num_wgs = decode_wgs(num_seqs, l.plan.num_head_groups, l.plan.heads_per_wg, max_blocks_per_seq);
   l.cols = members_per_item(group) * group;
-  const size_t recs = 2 * (size_t)l.plan.num_wgs + 2 * (size_t)num_seqs * l.plan.num_head_groups;
-  const size_t rows = recs * l.plan.heads_per_wg * l.cols;
+  const size_t rows = 2 * (size_t)l.plan.num_wgs * l.plan.heads_per_wg * l.cols;
   l.items_off = 256;  // ShareHeader
-  l.map_off = l.items_off + round_up((2 * (size_t)num_seqs + 1) * sizeof(pa::ShareItem), 256);
-  l.ml_off = l.map_off + round_up((size_t)num_seqs * sizeof(int2), 256);
+  l.desc_off = l.items_off + round_up(((size_t)num_seqs + 1) * sizeof(pa::ShareItem), 256);
+  l.ml_off = l.desc_off + round_up((size_t)l.plan.num_wgs * sizeof(int2), 256);
   l.o_off = l.ml_off + round_up(rows * 2 * sizeof(float), 256);
   l.total = l.o_off + round_up(rows * c->head_size * sizeof(float), 256);
   return l;
@@ -297,7 +296,6 @@ int pa_decode_shared(const pa_kv_cache *cache, const void *q, const int32_t *blo
   char *base = static_cast<char *>(ws);
   pa::ShareHeader *hdr = reinterpret_cast<pa::ShareHeader *>(base);
   pa::ShareItem *items = reinterpret_cast<pa::ShareItem *>(base + l.items_off);
-  int2 *seq_map = reinterpret_cast<int2 *>(base + l.map_off);
 
   pa::DecodeArgs a{};
   a.q = static_cast<const uint16_t *>(q);
@@ -306,6 +304,7 @@ int pa_decode_shared(const pa_kv_cache *cache, const void *q, const int32_t *blo
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.out = static_cast<uint16_t *>(out);
+  a.merge_desc = reinterpret_cast<int2 *>(base + l.desc_off);
   a.part_ml = reinterpret_cast<float *>(base + l.ml_off);
   a.part_o = reinterpret_cast<float *>(base + l.o_off);
   a.num_blocks = cache->num_blocks;
@@ -322,15 +321,15 @@ int pa_decode_shared(const pa_kv_cache *cache, const void *q, const int32_t *blo
   a.scale_log2 = scale * 1.44269504088896340736f;
   a.items = items;
   a.share = hdr;
-  a.seq_map = seq_map;
 
   pa::SharePlanArgs p{};
   p.lens = context_lens;
   p.group_starts = group_starts;
   p.shared_blocks = shared_blocks;
   p.items = items;
-  p.seq_map = seq_map;
   p.share = hdr;
+  p.out = static_cast<uint16_t *>(out);
+  p.row_elems = num_q_heads * cache->head_size;
   p.num_seqs = num_seqs;
   p.num_groups = num_groups;
   p.max_blocks_per_seq = max_blocks_per_seq;

@@ -8,25 +8,26 @@
 
 namespace pa {
 
-// Sharing-aware decode: the call's work as a list of items. An item is a
-// run of one table row's blocks read once for one or more sequences: a
-// group's shared prefix for up to 32 / group of its members (its q rows are
-// consecutive), or one sequence's private tail.
+// Sharing-aware decode: the call's work as a list of segments. A segment is
+// up to 32 / group consecutive members of a group (one sequence outside
+// groups): the group's shared blocks, read once through the first member's
+// table with every member's query heads as MFMA columns, then each member's
+// own blocks past them, read for that member alone.
 struct ShareItem {
-  int32_t row;     // table row read (a sequence index)
-  int32_t qrow;    // q rows qrow .. qrow + ntok - 1 are the item's columns
-  int32_t ntok;    // sequences served (1 for a tail)
-  int32_t b0;      // first logical block
-  int32_t n;       // positions < n are visible
-  int32_t L;       // blocks: ceil(n / 16) - b0 (>= 0)
-  int64_t ustart;  // first unit: head groups times the blocks of all earlier items
+  int32_t row;     // table row of the shared blocks (the group's first member)
+  int32_t qrow;    // first member: q and output rows qrow .. qrow + ntok - 1
+  int32_t ntok;    // members
+  int32_t b0;      // shared blocks
+  int32_t n;       // b0 * 16
+  int32_t L;       // blocks in all: b0 + the members' own blocks
+  int64_t ustart;  // first unit: head groups times the blocks of all earlier segments
 };
 
 // Written by the plan kernel: totals of the call.
 struct ShareHeader {
   int64_t units;
-  int32_t items;         // prefix items, then one tail item per sequence
-  int32_t prefix_items;
+  int32_t items;   // segments
+  int32_t pad;
 };
 
 // Arguments of one decode launch, passed by value as the kernel argument.
@@ -48,16 +49,13 @@ struct DecodeArgs {
   int32_t q_len;                 // new tokens per sequence (1: decode)
   int32_t num_cols;              // q_len * group, <= 32 (<= 16 when q_len == 1)
   int32_t max_blocks_per_seq;
-  int32_t heads_per_wg;          // KV heads per workgroup (one wavefront each), <= 8
+  int32_t heads_per_wg;          // KV heads per workgroup (one wavefront each), <= 4
   int32_t num_head_groups;       // Hkv / heads_per_wg
   int32_t num_wgs;               // workgroups sharing the units evenly
   float scale_log2;              // softmax scale times log2(e)
-  // Sharing-aware decode only (null otherwise). Records of pieces: the
-  // 2 * num_wgs per-workgroup slots first, then one per (item, head group)
-  // for items that no workgroup boundary cuts.
-  const ShareItem *items;        // [2 * num_seqs + 1]: items, then a sentinel holding the total units
+  // Sharing-aware decode only (null otherwise).
+  const ShareItem *items;        // [num_seqs + 1]: segments, then a sentinel holding the total units
   const ShareHeader *share;
-  const int2 *seq_map;           // [num_seqs]: (prefix item or -1, first column of the sequence in it)
 };
 
 // Arguments of the sharing-aware plan kernel.
@@ -66,8 +64,9 @@ struct SharePlanArgs {
   const int32_t *group_starts;   // [num_groups + 1]
   const int32_t *shared_blocks;  // [num_groups]
   ShareItem *items;
-  int2 *seq_map;
   ShareHeader *share;
+  uint16_t *out;                 // zeroed for segments whose members are all empty
+  int32_t row_elems;             // num_q_heads * head_size
   int32_t num_seqs;
   int32_t num_groups;
   int32_t max_blocks_per_seq;
@@ -96,8 +95,8 @@ hipError_t launch_decode(const DecodeArgs &args, int32_t head_size, hipStream_t 
 // and per-group state in LDS).
 constexpr int32_t kMaxSharedSeqs = 4096;
 
-// Plan, decode and finalize of a sharing-aware call. args.num_cols is the
-// item width (members_per_item * group), args.q_len is 1.
+// Plan, decode and merge of a sharing-aware call. args.num_cols is the
+// segment width (members_per_item * group), args.q_len is 1.
 hipError_t launch_decode_shared(const SharePlanArgs &plan, const DecodeArgs &args, int32_t head_size,
                                 hipStream_t stream);
 

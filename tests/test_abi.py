@@ -133,13 +133,14 @@ def test_decode_shared_limits(L):
     assert call(q=None) == _lib.PA_ERR_NULL
     assert Sh(ctypes.byref(desc(k_cache=0, v_cache=0)), None, None, None, 0, 32, 16, None, None, 0, 1.0,
               None, None, 0, None) == _lib.PA_OK   # empty batch
-    # items are 4 sequences x 8 query heads = 32 columns wide; records: 2 per
-    # workgroup and 1 per (item, head group), each with max, sum and 128 floats
-    S, mb, hg, ng = 256, 256, 4, 2
+    # segments are 4 sequences x 8 query heads = 32 columns wide; partial
+    # records: 2 per workgroup, KV head of the group and column, each with
+    # max, sum and 128 floats; a merge record per workgroup
+    S, mb, hg = 256, 256, 4
     wgs = 256
-    rows = (2 * wgs + 2 * S * ng) * hg * 32
+    rows = 2 * wgs * hg * 32
     need = W(ctypes.byref(d), S, 32, mb, 64)
-    assert need >= (2 * S + 1) * 32 + S * 8 + rows * (128 + 2) * 4
+    assert need >= (S + 1) * 32 + wgs * 8 + rows * (128 + 2) * 4
     assert call(S=S, mb=mb, ng=64, ws=P, wsb=need - 1) == _lib.PA_ERR_WORKSPACE
 
 
