@@ -90,7 +90,8 @@ def record_traffic(prefix: str, workload: str, copy_bytes: int) -> int:
     Reads four rocprofv3 --pmc runs: {prefix}_fetch_decode and
     {prefix}_write_decode (this bench on `workload`, counters FETCH_SIZE and
     WRITE_SIZE), {prefix}_fetch_copy and {prefix}_write_copy (--probe-copy of
-    `copy_bytes` bytes). Each counter is scaled by what it reads for the copy,
+    `copy_bytes` bytes). The call's kernels are the decode and merge kernels,
+    and the plan kernel when the call is sharing-aware. Each counter is scaled by what it reads for the copy,
     which moves exactly `copy_bytes` each way, so the units need not be known.
     """
     def means(kind, counter):
@@ -101,7 +102,10 @@ def record_traffic(prefix: str, workload: str, copy_bytes: int) -> int:
     fd, wd = means("fetch_decode", "FETCH_SIZE"), means("write_decode", "WRITE_SIZE")
     f_scale, w_scale = copy_bytes / fetch_copy, copy_bytes / write_copy
     per = {}
-    for frag in ("decode_kernel", "merge_kernel"):
+    frags = ["decode_kernel", "merge_kernel"]
+    if any("share_plan_kernel" in k for k in fd):  # the sharing-aware call's plan
+        frags.insert(0, "share_plan_kernel")
+    for frag in frags:
         per[frag] = {"fetch_bytes": int(_one(fd, frag) * f_scale), "write_bytes": int(_one(wd, frag) * w_scale)}
     total = sum(v["fetch_bytes"] + v["write_bytes"] for v in per.values())
     try:
@@ -443,7 +447,7 @@ def main(argv=None) -> int:
     achieved = decode_bytes / (dec_mean * 1e-3) / 1e9
     traffic = measured_traffic(workload) if not multi else None
     if args.shared:
-        kernel = "decode_shared call: share_plan_kernel + decode_kernel + share_finalize_kernel"
+        kernel = "decode_shared call: share_plan_kernel + decode_kernel + merge_kernel"
     else:
         kernel = "decode call: decode_kernel + merge_kernel"
     rec = {
