@@ -304,6 +304,9 @@ def main(argv=None) -> int:
     ap.add_argument("--q-len", type=int, default=1,
                     help="new tokens per sequence (speculative-decode verification): the step scatters them "
                          "and runs pa_decode_multi")
+    ap.add_argument("--block-size", type=int, default=16, choices=(8, 16, 32),
+                    help="tokens per cache block for the named single-step configs (same pool capacity in "
+                         "tokens); with 8 or 32 one new token per sequence")
     ap.add_argument("--shared", action="store_true",
                     help="beam_cow only: decode with pa_decode_shared, reading a prompt's shared blocks once "
                          "for its beams (the sharing is read back from the block tables)")
@@ -352,9 +355,13 @@ def main(argv=None) -> int:
     else:
         if args.shared:
             raise SystemExit("--shared applies to the beam_cow workload")
-        b = W.make_config(args.config, q_len=args.q_len)
+        if args.block_size != 16 and args.q_len != 1:
+            raise SystemExit("--block-size 8 or 32 takes one new token per sequence")
+        b = W.make_config(args.config, q_len=args.q_len, block_size=args.block_size)
     multi = args.q_len > 1
-    workload = args.config + ("_shared" if args.shared else "")
+    if args.config == "beam_cow" and args.block_size != 16:
+        raise SystemExit("--block-size applies to the named single-step configs")
+    workload = args.config + ("_shared" if args.shared else "") + (f"_bs{args.block_size}" if args.block_size != 16 else "")
 
     def bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -370,7 +377,7 @@ def main(argv=None) -> int:
     scale = float(b.scale)
 
     logical_bytes = W.algorithmic_bytes(b.context_lens, b.num_q_heads, b.num_kv_heads, b.head_size,
-                                        q_len=args.q_len)
+                                        block_size=b.block_size, q_len=args.q_len)
     decode_bytes = logical_bytes
     if args.shared:
         gstarts = W.consecutive_groups(b.num_seqs, wl.beams)
@@ -471,6 +478,7 @@ def main(argv=None) -> int:
             "head_size": b.head_size,
             "block_size": b.block_size,
             "kv_pool_blocks": b.num_blocks,
+            "kv_memory_utilization": round(W.memory_utilization(b.context_lens, b.block_size), 5),
             "sum_context_tokens": int(b.context_lens.sum()),
             "seed": b.seed,
             "q_len": args.q_len,

@@ -70,7 +70,13 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
+// The unit of work is a chunk of tokens, at most 16 (one MFMA tile of rows):
+// with 16-token cache blocks a chunk is a block, a 32-token block holds two
+// chunks, and an 8-token block is a chunk that fills half a tile.
 constexpr int kBlock = 16;
+
+template <int BS>
+constexpr int chunk_of() { return BS < kBlock ? BS : kBlock; }
 constexpr uint32_t kBf16One = 0x3F80u;
 
 // What a decode launch computes: one new token per sequence (kSingle);
@@ -214,7 +220,7 @@ __device__ __forceinline__ void take_item(Walker &wk, const ShareItem &x) {
   wk.b0 = __builtin_amdgcn_readfirstlane(x.b0);
 }
 
-template <int M>
+template <int M, int CH = kBlock>
 __device__ __forceinline__ bool next_piece(Walker &wk, Piece &p) {
   if (wk.u >= wk.hi) return false;
   if constexpr (M == kShared) {
@@ -245,7 +251,7 @@ __device__ __forceinline__ bool next_piece(Walker &wk, Piece &p) {
           if (wk.s < wk.S) take_item(wk, wk.items[wk.s]); else wk.L = 0;
         } else {
           wk.n = wk.s < wk.S ? clamp_len(wk.lens[wk.s], wk.cap) : 0;
-          wk.L = (wk.n + kBlock - 1) / kBlock;
+          wk.L = (wk.n + CH - 1) / CH;
         }
       } while (wk.L == 0 && wk.s < wk.S);
       if (wk.s >= wk.S) wk.u = wk.hi;  // only if the lengths changed during the call
@@ -448,10 +454,28 @@ __device__ __forceinline__ void issue(const DecodeArgs &a, const Lane<NT> &ln, i
     V[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, ln.lane_off + 64 * j, 0, 0));
 }
 
-// Token rows of logical block b that lie before the context length n.
+// Starts the loads of chunk c of table row `row` for this wavefront's head,
+// in a cache of BS-token blocks: block c (BS = 16, or BS = 8 with the
+// tile's rows 8-15 past the block's range, read as zeros), or half of block
+// c/2 (BS = 32).
+template <int NJ, int NT, int BS>
+__device__ __forceinline__ void issue_chunk(const int32_t *__restrict__ tables, const DecodeArgs &a,
+                                            const Lane<NT> &ln, int row, int c, size_t hoff, int nrows,
+                                            u32x4_t (&K)[NJ], u32x4_t (&V)[NJ]) {
+  static_assert(BS == 8 || BS == 16 || BS == 32, "block size 8, 16 or 32");
+  if constexpr (BS <= kBlock) {
+    issue<NJ>(a, ln, block_id(tables, a, ln.pool32, row, c), hoff, nrows, K, V);
+  } else {
+    issue<NJ>(a, ln, block_id(tables, a, ln.pool32, row, c >> 1),
+              hoff + (size_t)(c & 1) * kBlock * (ln.row_bytes / sizeof(uint16_t)), nrows, K, V);
+  }
+}
+
+// Token rows of chunk b (CH tokens) that lie before the context length n.
+template <int CH = kBlock>
 __device__ __forceinline__ int rows_in(int n, int b) {
-  const int r = n - b * kBlock;
-  return r < kBlock ? r : kBlock;
+  const int r = n - b * CH;
+  return r < CH ? r : CH;
 }
 
 // Writes P's result: bf16 output when P is a whole segment, otherwise its
@@ -516,7 +540,7 @@ __device__ __forceinline__ void finish_piece(const DecodeArgs &a, const Lane<NT>
 // Makes Q the current piece (its first block is already loading) and looks
 // one piece further ahead. With one column tile Q's q is in LDS already;
 // with two it is loaded here and parked in LDS.
-template <int NJ, int NT, int M>
+template <int NJ, int NT, int M, int CH>
 __device__ __forceinline__ void advance(const DecodeArgs &a, const Lane<NT> &ln, Walker &wk, Stream<NJ, NT> &st,
                                         uint16_t *lds) {
   st.P = st.Q;
@@ -539,7 +563,7 @@ __device__ __forceinline__ void advance(const DecodeArgs &a, const Lane<NT> &ln,
 #pragma unroll
     for (int k = 0; k < 2 * NJ; ++k) st.acc[t][k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  st.has_q = next_piece<M>(wk, st.Q);
+  st.has_q = next_piece<M, CH>(wk, st.Q);
   if (!st.has_q) st.Q = st.P;
   st.hoff_q = head_off<NJ>(ln, st.Q);
   if constexpr (M == kShared) {
@@ -551,11 +575,12 @@ __device__ __forceinline__ void advance(const DecodeArgs &a, const Lane<NT> &ln,
 // Computes block i of P from (K, V) after starting the next block of the
 // stream loading into (Kn, Vn); finishes P at its end and moves to Q.
 // Returns false once the stream is done.
-template <int NJ, int NT, int M>
+template <int NJ, int NT, int M, int BS>
 __device__ __forceinline__ bool step(const int32_t *__restrict__ tables, const DecodeArgs &a, const Lane<NT> &ln,
                                      Walker &wk, Stream<NJ, NT> &st, u32x4_t (&K)[NJ], u32x4_t (&V)[NJ],
                                      u32x4_t (&Kn)[NJ], u32x4_t (&Vn)[NJ], uint16_t *lds) {
   constexpr bool kMulti = M == kCausal;
+  constexpr int CH = chunk_of<BS>();
   const Piece &P = st.P;
   // In P's first step, q of the next piece is loaded (before this step's K/V
   // loads) and parked in LDS at the end of the step: the registers never
@@ -580,15 +605,15 @@ __device__ __forceinline__ bool step(const int32_t *__restrict__ tables, const D
   } else {
     const int next_s = to_q ? st.Q.s : P.s;
     const int next_b = in_p ? P.off + nx : (to_q ? st.Q.off : P.off + st.i);
-    issue<NJ>(a, ln, block_id(tables, a, ln.pool32, next_s, next_b), to_q ? st.hoff_q : st.hoff,
-              rows_in(to_q ? st.Q.n : P.n, next_b), Kn, Vn);
+    issue_chunk<NJ, NT, BS>(tables, a, ln, next_s, next_b, to_q ? st.hoff_q : st.hoff,
+                            rows_in<CH>(to_q ? st.Q.n : P.n, next_b), Kn, Vn);
   }
   // Keep the scheduler from sinking those loads below the compute.
   __builtin_amdgcn_sched_barrier(0);
 
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
   const int b = M == kShared ? st.cc.b : P.off + st.i;
-  const int pos0 = b * kBlock + ln.grp * 4;
+  const int pos0 = b * CH + ln.grp * 4;
   // kShared: in a member's own blocks only that member's columns are live,
   // and a tile holding none of them is skipped (a uniform branch).
   const int cj = M == kShared ? st.cc.j : -1;
@@ -617,7 +642,9 @@ __device__ __forceinline__ bool step(const int32_t *__restrict__ tables, const D
     else lim = P.n;
     float z[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) z[r] = (pos0 + r < lim) ? sc[r] * a.scale_log2 : -INFINITY;
+    // With 8-token chunks the tile's rows 8-15 hold no token of the chunk.
+    for (int r = 0; r < 4; ++r)
+      z[r] = (ln.grp * 4 + r < CH && pos0 + r < lim) ? sc[r] * a.scale_log2 : -INFINITY;
     float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -640,7 +667,7 @@ __device__ __forceinline__ bool step(const int32_t *__restrict__ tables, const D
   }
 
   // V rows of tokens at or past n must not reach the sum, even as NaN * 0.
-  const bool v_live = b * kBlock + ln.c < (M == kShared ? st.cc.n : P.n);
+  const bool v_live = ln.c < CH && b * CH + ln.c < (M == kShared ? st.cc.n : P.n);
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
 #pragma unroll
@@ -664,7 +691,7 @@ __device__ __forceinline__ bool step(const int32_t *__restrict__ tables, const D
   if (in_p) return true;
   finish_piece<NJ, NT, M>(a, ln, st);
   if (!st.has_q) return false;
-  advance<NJ, NT, M>(a, ln, wk, st, lds);
+  advance<NJ, NT, M, CH>(a, ln, wk, st, lds);
   return true;
 }
 
@@ -687,7 +714,7 @@ __device__ __forceinline__ void no_merge(const DecodeArgs &a, int w, int tid) {
 // item width in kShared). M: kSingle, kCausal or kShared. The launch puts
 // one wavefront on each SIMD; with two tiles the wavefront may take the
 // whole register file (arch and accumulation registers).
-template <int D, int NT, int M>
+template <int D, int NT, int M, int BS>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2 : 1)))
 void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const int32_t *__restrict__ lens,
                    const ShareItem *__restrict__ items) {
@@ -705,7 +732,8 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
   const int w = blockIdx.x;
   const int S = a.num_seqs;
   const int NG = a.num_head_groups;
-  const int cap = a.max_blocks_per_seq * kBlock;
+  const int cap = a.max_blocks_per_seq * BS;  // tokens a table row can address
+  constexpr int CH = chunk_of<BS>();          // tokens per chunk (unit of work)
   const long long W = a.num_wgs;
 
   long long U, lo, hi, E;
@@ -746,7 +774,7 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
     // gives the total and every sequence's first unit at once.
     const int n = tid < S ? clamp_len(lens[tid], cap) : 0;
     if (tid < S && n == 0) zero_empty<D>(a, tid, w);
-    const long long L = (n + kBlock - 1) / kBlock;
+    const long long L = (n + CH - 1) / CH;
     long long pre, total;
     const long long incl = wg_scan(L, red, wave, lane, nthr >> 6, pre, total);
     U = total * NG;
@@ -769,7 +797,7 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
     long long mine = 0;
     for (int s = tid; s < S; s += nthr) {
       const int n = clamp_len(lens[s], cap);
-      mine += (n + kBlock - 1) / kBlock;
+      mine += (n + CH - 1) / CH;
       if (n == 0) zero_empty<D>(a, s, w);
     }
     U = wg_sum(mine, red, wave, lane, nthr >> 6) * NG;
@@ -787,7 +815,7 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
     for (int base = 0; base < S; base += nthr) {
       const int s = base + tid;
       const int n = s < S ? clamp_len(lens[s], cap) : 0;
-      const long long L = (n + kBlock - 1) / kBlock;
+      const long long L = (n + CH - 1) / CH;
       long long pre, chunk_total;
       const long long incl = wg_scan(L, red, wave, lane, nthr >> 6, pre, chunk_total);
       const long long excl = before + pre + incl - L;
@@ -813,7 +841,7 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
     wk.seg_base = found_prefix * NG;
     wk.s = __builtin_amdgcn_readfirstlane(found_seq);
     wk.n = __builtin_amdgcn_readfirstlane(found_n);
-    wk.L = (wk.n + kBlock - 1) / kBlock;
+    wk.L = (wk.n + CH - 1) / CH;
   }
   wk.NG = NG;
   wk.u = lo;
@@ -847,7 +875,7 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
     ln.out_off[t] = (uint32_t)((tok * a.num_q_heads + qh) * D + ln.grp * 8);
     ln.q_off[t] = ln.out_off[t] * (uint32_t)sizeof(uint16_t);
   }
-  ln.blk_stride = (size_t)a.num_kv_heads * D * kBlock;
+  ln.blk_stride = (size_t)a.num_kv_heads * D * BS;
   ln.row_bytes = a.num_kv_heads * D * (int)sizeof(uint16_t);
   ln.lane_off = (uint32_t)(((size_t)ln.c * a.num_kv_heads * D + ln.grp * 8) * sizeof(uint16_t));
   ln.U = U;
@@ -865,7 +893,7 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
   // stream (possibly the first block of the next piece) loads into the
   // other. The next piece's q goes through LDS one piece ahead.
   Stream<NJ, NT> st;
-  next_piece<M>(wk, st.P);
+  next_piece<M, CH>(wk, st.P);
   if constexpr (NT == 1) {
     load_q<NJ, NT, M>(a, ln, st.P, st.qv);
   } else {
@@ -874,7 +902,7 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
     park_q<NJ>(q_park<NJ>(q_lds, a, wave), ln, qv);
   }
   st.hoff = head_off<NJ>(ln, st.P);
-  st.has_q = next_piece<M>(wk, st.Q);
+  st.has_q = next_piece<M, CH>(wk, st.Q);
   if (!st.has_q) st.Q = st.P;
   st.hoff_q = head_off<NJ>(ln, st.Q);
   if constexpr (M == kShared) {
@@ -895,10 +923,10 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
   if constexpr (M == kShared) {
     issue<NJ>(a, ln, block_id(tables, a, ln.pool32, st.cc.row, st.cc.b), st.hoff, rows_in(st.cc.n, st.cc.b), KA, VA);
   } else {
-    issue<NJ>(a, ln, block_id(tables, a, ln.pool32, st.P.s, st.P.off), st.hoff, rows_in(st.P.n, st.P.off), KA, VA);
+    issue_chunk<NJ, NT, BS>(tables, a, ln, st.P.s, st.P.off, st.hoff, rows_in<CH>(st.P.n, st.P.off), KA, VA);
   }
-  while (step<NJ, NT, M>(tables, a, ln, wk, st, KA, VA, KB, VB, q_lds) &&
-         step<NJ, NT, M>(tables, a, ln, wk, st, KB, VB, KA, VA, q_lds)) {
+  while (step<NJ, NT, M, BS>(tables, a, ln, wk, st, KA, VA, KB, VB, q_lds) &&
+         step<NJ, NT, M, BS>(tables, a, ln, wk, st, KB, VB, KA, VA, q_lds)) {
   }
 }
 
@@ -1147,11 +1175,11 @@ hipError_t allow_lds(Kernel kernel, size_t bytes) {
                              (int)bytes);
 }
 
-template <int D, int NT, int M>
+template <int D, int NT, int M, int BS = 16>
 hipError_t launch_decode_kernel(const DecodeArgs &args, size_t lds, hipStream_t stream) {
-  hipError_t e = allow_lds(decode_kernel<D, NT, M>, lds);
+  hipError_t e = allow_lds(decode_kernel<D, NT, M, BS>, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_kernel<D, NT, M>), dim3((unsigned)args.num_wgs),
+  hipLaunchKernelGGL((decode_kernel<D, NT, M, BS>), dim3((unsigned)args.num_wgs),
                      dim3(64 * (unsigned)args.heads_per_wg), lds, stream, args, args.block_tables,
                      args.context_lens, args.items);
   return hipGetLastError();
@@ -1159,7 +1187,12 @@ hipError_t launch_decode_kernel(const DecodeArgs &args, size_t lds, hipStream_t 
 
 template <int D>
 hipError_t launch_decode_d(const DecodeArgs &args, size_t lds, hipStream_t stream) {
-  if (args.q_len == 1) return launch_decode_kernel<D, 1, kSingle>(args, lds, stream);
+  if (args.q_len == 1) {
+    // One new token: every block size; the other modes take 16-token blocks.
+    if (args.block_size == 8) return launch_decode_kernel<D, 1, kSingle, 8>(args, lds, stream);
+    if (args.block_size == 32) return launch_decode_kernel<D, 1, kSingle, 32>(args, lds, stream);
+    return launch_decode_kernel<D, 1, kSingle>(args, lds, stream);
+  }
   if (args.num_cols <= 16) return launch_decode_kernel<D, 1, kCausal>(args, lds, stream);
   return launch_decode_kernel<D, 2, kCausal>(args, lds, stream);
 }
@@ -1168,6 +1201,8 @@ hipError_t launch_decode_d(const DecodeArgs &args, size_t lds, hipStream_t strea
 
 hipError_t launch_decode(const DecodeArgs &args, int32_t head_size, hipStream_t stream) {
   if (args.q_len < 1 || args.num_cols > 32 || (args.q_len == 1 && args.num_cols > 16)) return hipErrorInvalidValue;
+  if (args.block_size != 16 && (args.q_len != 1 || (args.block_size != 8 && args.block_size != 32)))
+    return hipErrorInvalidValue;
   // LDS holds q: a two-slot ring per wavefront for the next piece (one column
   // tile), or the current piece's (two tiles).
   const size_t lds = (size_t)args.heads_per_wg * (args.num_cols <= 16 ? 2 : 1) * args.num_cols * head_size *
@@ -1194,7 +1229,7 @@ hipError_t launch_decode(const DecodeArgs &args, int32_t head_size, hipStream_t 
 
 hipError_t launch_decode_shared(const SharePlanArgs &plan, const DecodeArgs &args, int32_t head_size,
                                 hipStream_t stream) {
-  if (args.q_len != 1 || args.num_cols <= 16 || args.num_cols > 32 || !args.items || !args.share ||
+  if (args.q_len != 1 || args.block_size != 16 || args.num_cols <= 16 || args.num_cols > 32 || !args.items || !args.share ||
       plan.num_seqs < 1 || plan.num_seqs > kMaxSharedSeqs || plan.num_groups < 0 ||
       plan.num_groups > plan.num_seqs || plan.members_per_item < 1 || !plan.out || plan.row_elems % 8)
     return hipErrorInvalidValue;

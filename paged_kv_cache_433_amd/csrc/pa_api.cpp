@@ -35,7 +35,7 @@ int hip_fail(hipError_t e, const char *what) {
 // and the older one runs ahead while the younger one finishes alone with
 // half the loads in flight. So floor(4 / heads_per_wg) workgroups per CU,
 // all resident at once (a second round of workgroups would undo the
-// balance). Fewer when every sequence at max_blocks_per_seq would still give
+// balance). Fewer when every sequence at max_blocks_per_seq (as chunks) would still give
 // a workgroup fewer than 4 units. The count depends on the sizes only (not on
 // the device or the data), so workspace sizes are a host function and
 // results are reproducible. PA_DECODE_WGS overrides it (tests, tuning).
@@ -43,9 +43,9 @@ constexpr int64_t kTargetCUs = 256;
 constexpr int64_t kWavesPerCU = 4;
 
 int32_t decode_wgs(int64_t num_seqs, int32_t num_head_groups, int32_t heads_per_wg,
-                   int32_t max_blocks_per_seq) {
+                   int32_t max_chunks_per_seq) {
   int64_t w = kTargetCUs * (kWavesPerCU / heads_per_wg > 0 ? kWavesPerCU / heads_per_wg : 1);
-  const int64_t units_bound = num_seqs * num_head_groups * (int64_t)max_blocks_per_seq;
+  const int64_t units_bound = num_seqs * num_head_groups * (int64_t)max_chunks_per_seq;
   const int64_t by_work = (units_bound + 3) / 4;
   if (by_work < w) w = by_work;
   if (const char *env = getenv("PA_DECODE_WGS")) {
@@ -71,11 +71,15 @@ int check_cache(const pa_kv_cache *c, bool need_data) {
   if (!c) return fail(PA_ERR_NULL, "cache descriptor is NULL");
   if (need_data && (!c->k_cache || !c->v_cache)) return fail(PA_ERR_NULL, "k_cache or v_cache is NULL");
   if (c->dtype != PA_DTYPE_BF16) return fail(PA_ERR_UNSUPPORTED, "only bf16 caches are supported");
-  if (c->block_size != 16) return fail(PA_ERR_UNSUPPORTED, "only block_size 16 is supported");
+  if (c->block_size != 8 && c->block_size != 16 && c->block_size != 32)
+    return fail(PA_ERR_UNSUPPORTED, "block_size must be 8, 16 or 32");
   if (c->head_size != 64 && c->head_size != 128)
     return fail(PA_ERR_UNSUPPORTED, "head_size must be 64 or 128");
   if (c->num_blocks < 1) return fail(PA_ERR_SHAPE, "num_blocks must be >= 1");
   if (c->num_kv_heads < 1) return fail(PA_ERR_SHAPE, "num_kv_heads must be >= 1");
+  // Kernels address a block with 32-bit byte offsets.
+  if ((int64_t)c->num_kv_heads * c->head_size * c->block_size * 2 > (int64_t)1 << 30)
+    return fail(PA_ERR_SHAPE, "a cache block (block_size * num_kv_heads * head_size * 2 bytes) exceeds 1 GiB");
   return PA_OK;
 }
 
@@ -87,7 +91,7 @@ int check_decode_shape(const pa_kv_cache *c, int32_t num_seqs, int32_t num_q_hea
     return fail(PA_ERR_SHAPE, "num_q_heads must be a positive multiple of num_kv_heads");
   if (num_q_heads / c->num_kv_heads > 16)
     return fail(PA_ERR_UNSUPPORTED, "more than 16 query heads per KV head");
-  if ((int64_t)max_blocks_per_seq * 16 > 0x7fffffffLL)
+  if ((int64_t)max_blocks_per_seq * c->block_size > 0x7fffffffLL)
     return fail(PA_ERR_SHAPE, "max_blocks_per_seq too large");
   if ((int64_t)num_seqs * c->num_kv_heads > 0x7fffffffLL)
     return fail(PA_ERR_SHAPE, "num_seqs * num_kv_heads too large");
@@ -95,9 +99,12 @@ int check_decode_shape(const pa_kv_cache *c, int32_t num_seqs, int32_t num_q_hea
 }
 
 // Several new tokens per sequence: their (token, query head) pairs of one KV
-// head must fit two 16-column MFMA tiles.
+// head must fit two 16-column MFMA tiles, and the cache must use 16-token
+// blocks (8- and 32-token blocks are taken with one new token).
 int check_q_len(const pa_kv_cache *c, int32_t num_q_heads, int32_t q_len) {
   if (q_len < 1) return fail(PA_ERR_SHAPE, "q_len must be >= 1");
+  if (q_len > 1 && c->block_size != 16)
+    return fail(PA_ERR_UNSUPPORTED, "several new tokens per sequence need block_size 16");
   if ((int64_t)q_len * (num_q_heads / c->num_kv_heads) > 32)
     return fail(PA_ERR_UNSUPPORTED, "q_len * (num_q_heads / num_kv_heads) must be <= 32");
   return PA_OK;
@@ -133,7 +140,15 @@ SharedLayout layout_shared(const pa_kv_cache *c, int32_t num_seqs, int32_t num_q
   return l;
 }
 
-int check_shared(int32_t num_seqs, int32_t num_groups) {
+// The decode kernel works in chunks of min(block_size, 16) tokens: a table
+// row of max_blocks_per_seq blocks holds at most this many.
+int32_t chunks_per_row(const pa_kv_cache *c, int32_t max_blocks_per_seq) {
+  const int64_t chunk = c->block_size < 16 ? c->block_size : 16;
+  return (int32_t)((int64_t)max_blocks_per_seq * c->block_size / chunk);
+}
+
+int check_shared(const pa_kv_cache *c, int32_t num_seqs, int32_t num_groups) {
+  if (c->block_size != 16) return fail(PA_ERR_UNSUPPORTED, "pa_decode_shared needs block_size 16");
   if (num_seqs > pa::kMaxSharedSeqs)
     return fail(PA_ERR_UNSUPPORTED, "pa_decode_shared takes at most 4096 sequences");
   if (num_groups < 0 || num_groups > num_seqs) return fail(PA_ERR_SHAPE, "num_groups must be in 0..num_seqs");
@@ -145,11 +160,11 @@ int check_shared(int32_t num_seqs, int32_t num_groups) {
 namespace pa {
 
 DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                       int32_t head_size, int32_t max_blocks_per_seq, int32_t q_len) {
+                       int32_t head_size, int32_t max_chunks_per_seq, int32_t q_len) {
   DecodePlan p{};
   p.heads_per_wg = heads_per_workgroup(num_kv_heads);
   p.num_head_groups = num_kv_heads / p.heads_per_wg;
-  p.num_wgs = decode_wgs(num_seqs, p.num_head_groups, p.heads_per_wg, max_blocks_per_seq);
+  p.num_wgs = decode_wgs(num_seqs, p.num_head_groups, p.heads_per_wg, max_chunks_per_seq);
   if (p.num_wgs <= 1) return p;
   const size_t cols = (size_t)q_len * (num_q_heads / num_kv_heads);
   const size_t rows = (size_t)p.num_wgs * 2 * p.heads_per_wg * cols;
@@ -177,7 +192,7 @@ size_t pa_decode_multi_workspace_bytes(const pa_kv_cache *cache, int32_t num_seq
   if (check_decode_shape(cache, num_seqs, num_q_heads, max_blocks_per_seq) != PA_OK) return 0;
   if (check_q_len(cache, num_q_heads, q_len) != PA_OK) return 0;
   return pa::plan_decode(num_seqs, num_q_heads, cache->num_kv_heads, cache->head_size,
-                         max_blocks_per_seq, q_len)
+                         chunks_per_row(cache, max_blocks_per_seq), q_len)
       .total_bytes;
 }
 
@@ -203,8 +218,8 @@ int pa_decode_multi(const pa_kv_cache *cache, const void *q, const int32_t *bloc
   if (!q || !block_tables || !context_lens || !out)
     return fail(PA_ERR_NULL, "q, block_tables, context_lens or out is NULL");
 
-  const pa::DecodePlan plan = pa::plan_decode(num_seqs, num_q_heads, cache->num_kv_heads,
-                                              cache->head_size, max_blocks_per_seq, q_len);
+  const pa::DecodePlan plan = pa::plan_decode(num_seqs, num_q_heads, cache->num_kv_heads, cache->head_size,
+                                              chunks_per_row(cache, max_blocks_per_seq), q_len);
   if (workspace && workspace_bytes < plan.total_bytes)
     return fail(PA_ERR_WORKSPACE, "workspace smaller than pa_decode_workspace_bytes()");
   if (workspace && reinterpret_cast<uintptr_t>(workspace) % 16)
@@ -240,6 +255,7 @@ int pa_decode_multi(const pa_kv_cache *cache, const void *q, const int32_t *bloc
   a.q_len = q_len;
   a.num_cols = q_len * a.group;
   a.max_blocks_per_seq = max_blocks_per_seq;
+  a.block_size = cache->block_size;
   a.heads_per_wg = plan.heads_per_wg;
   a.num_head_groups = plan.num_head_groups;
   a.num_wgs = plan.num_wgs;
@@ -258,7 +274,7 @@ size_t pa_decode_shared_workspace_bytes(const pa_kv_cache *cache, int32_t num_se
                                         int32_t max_blocks_per_seq, int32_t num_groups) {
   if (check_cache(cache, false) != PA_OK) return 0;
   if (check_decode_shape(cache, num_seqs, num_q_heads, max_blocks_per_seq) != PA_OK) return 0;
-  if (check_shared(num_seqs, num_groups) != PA_OK || num_seqs == 0) return 0;
+  if (check_shared(cache, num_seqs, num_groups) != PA_OK || num_seqs == 0) return 0;
   return layout_shared(cache, num_seqs, num_q_heads, max_blocks_per_seq).total;
 }
 
@@ -271,7 +287,7 @@ int pa_decode_shared(const pa_kv_cache *cache, const void *q, const int32_t *blo
   if (rc != PA_OK) return rc;
   rc = check_decode_shape(cache, num_seqs, num_q_heads, max_blocks_per_seq);
   if (rc != PA_OK) return rc;
-  rc = check_shared(num_seqs, num_groups);
+  rc = check_shared(cache, num_seqs, num_groups);
   if (rc != PA_OK) return rc;
   if (num_seqs == 0) return ok();
   if (!q || !block_tables || !context_lens || !out)
@@ -315,6 +331,7 @@ int pa_decode_shared(const pa_kv_cache *cache, const void *q, const int32_t *blo
   a.q_len = 1;
   a.num_cols = l.cols;
   a.max_blocks_per_seq = max_blocks_per_seq;
+  a.block_size = cache->block_size;
   a.heads_per_wg = l.plan.heads_per_wg;
   a.num_head_groups = l.plan.num_head_groups;
   a.num_wgs = l.plan.num_wgs;

@@ -56,6 +56,7 @@ struct DecodeArgs {
   // Sharing-aware decode only (null otherwise).
   const ShareItem *items;        // [num_seqs + 1]: segments, then a sentinel holding the total units
   const ShareHeader *share;
+  int32_t block_size;            // tokens per cache block: 8, 16 or 32 (16 unless q_len == 1 and no sharing)
 };
 
 // Arguments of the sharing-aware plan kernel.
@@ -87,7 +88,7 @@ struct DecodePlan {
 };
 
 DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                       int32_t head_size, int32_t max_blocks_per_seq, int32_t q_len);
+                       int32_t head_size, int32_t max_chunks_per_seq, int32_t q_len);
 
 hipError_t launch_decode(const DecodeArgs &args, int32_t head_size, hipStream_t stream);
 

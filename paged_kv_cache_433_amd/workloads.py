@@ -440,12 +440,25 @@ CONFIG_SHAPES = {
 }
 
 
-def make_config(name: str, seed: int | None = None, q_len: int = 1) -> DecodeBatch:
+def make_config(name: str, seed: int | None = None, q_len: int = 1, block_size: int = BLOCK_SIZE) -> DecodeBatch:
     """Build one of the named decode configs (the CoW config has its own
-    class); ``q_len`` > 1 makes the newest q_len tokens of each sequence new."""
+    class); ``q_len`` > 1 makes the newest q_len tokens of each sequence new.
+    Another ``block_size`` keeps the pool's token capacity and the tables'
+    token reach (blocks and table width scaled by 16 / block_size)."""
     hq, hkv, d, nb, mb, default_seed = CONFIG_SHAPES[name]
     seed = default_seed if seed is None else seed
-    return make_batch(name, seed, config_lens(name, seed), hq, hkv, d, nb, mb, q_len=q_len)
+    nb = nb * BLOCK_SIZE // block_size
+    mb = (mb * BLOCK_SIZE + block_size - 1) // block_size
+    return make_batch(name, seed, config_lens(name, seed), hq, hkv, d, nb, mb, q_len=q_len, block_size=block_size)
+
+
+def memory_utilization(context_lens, block_size=BLOCK_SIZE) -> float:
+    """Share of the allocated slots that hold a token: each sequence owns
+    ceil(n / block_size) whole blocks, so its last block is partly empty
+    (internal fragmentation)."""
+    n = np.asarray(context_lens, dtype=np.int64)
+    slots = int(((n + block_size - 1) // block_size).sum()) * block_size
+    return float(n.sum()) / slots if slots else 1.0
 
 
 def algorithmic_bytes(context_lens, num_q_heads, num_kv_heads, head_size,

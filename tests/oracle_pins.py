@@ -74,6 +74,32 @@ def pin_dense_sdpa(orc):
             assert err <= 1e-12, (seed, s, err)
 
 
+def pin_block_sizes(orc):
+    """The cache block size is only a layout: with 8- and 32-token blocks the
+    paged output is still torch's dense attention over the logical K/V, and
+    the slot scatter still places token t at offset t % block_size of block
+    t // block_size of its table."""
+    for bs in (8, 32):
+        lens = [1, 7, 8, 9, 31, 32, 33, 70]
+        nb = int(sum((n + bs - 1) // bs for n in lens)) + 5
+        b = W.make_batch("pin", 60 + bs, lens, 8, 2, 16, nb, block_size=bs)
+        assert b.k_cache.shape[1] == bs
+        kc, vc = scattered(orc, b)
+        for s, n in enumerate(lens):           # the newest token lands where the table says
+            blk, off = table_slots(b.block_tables[s], n, bs)[n - 1]
+            assert np.array_equal(kc[blk, off], b.new_k[s]) and np.array_equal(vc[blk, off], b.new_v[s])
+        out = orc.decode(b.q, kc, vc, b.block_tables, b.context_lens, b.scale)
+        for s, n in enumerate(lens):
+            kb, vb = W.sequence_kv(b, s)
+            k = torch.from_numpy(widen(kb)).permute(1, 0, 2).repeat_interleave(4, 0)
+            v = torch.from_numpy(widen(vb)).permute(1, 0, 2).repeat_interleave(4, 0)
+            q = torch.from_numpy(widen(b.q[s]))[:, None, :]
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                q[None], k[None].contiguous(), v[None].contiguous(), scale=float(b.scale))[0, :, 0]
+            err = np.abs(out[s] - ref.numpy()).max()
+            assert err <= 1e-12, (bs, s, err)
+
+
 def pin_single_token(orc):
     """context_len = 1: softmax over one token is 1, so out = that token's V."""
     b = small_batch(21, [1, 1, 1], 8, 2, 16)
@@ -444,6 +470,7 @@ def pin_widening(orc):
 ALL_PINS = [
     pin_dense_sdpa,
     pin_single_token,
+    pin_block_sizes,
     pin_identical_keys,
     pin_zero_scale,
     pin_two_tokens_closed_form,

@@ -57,7 +57,7 @@ def test_decode_argument_errors(L):
     assert decode(L, desc(), q=None) == _lib.PA_ERR_NULL
     assert decode(L, desc(), out=None) == _lib.PA_ERR_NULL
     assert decode(L, desc(dtype=1)) == _lib.PA_ERR_UNSUPPORTED
-    assert decode(L, desc(block_size=32)) == _lib.PA_ERR_UNSUPPORTED
+    assert decode(L, desc(block_size=12)) == _lib.PA_ERR_UNSUPPORTED
     assert decode(L, desc(head_size=96)) == _lib.PA_ERR_UNSUPPORTED
     assert decode(L, desc(), hq=31) == _lib.PA_ERR_SHAPE
     assert decode(L, desc(num_kv_heads=1), hq=32) == _lib.PA_ERR_UNSUPPORTED   # group 32
@@ -142,6 +142,27 @@ def test_decode_shared_limits(L):
     need = W(ctypes.byref(d), S, 32, mb, 64)
     assert need >= (S + 1) * 32 + wgs * 8 + rows * (128 + 2) * 4
     assert call(S=S, mb=mb, ng=64, ws=P, wsb=need - 1) == _lib.PA_ERR_WORKSPACE
+
+
+def test_block_sizes(L):
+    """8-, 16- and 32-token blocks for one new token per sequence and the
+    cache ops; several new tokens and sharing-aware decode need 16."""
+    for bs in (8, 16, 32):
+        d = desc(block_size=bs)
+        assert L.pa_decode_workspace_bytes(ctypes.byref(d), 256, 32, 4096 // bs) > 0
+        assert L.pa_decode_multi_workspace_bytes(ctypes.byref(d), 256, 4, 32, 4096 // bs) == (0 if bs != 16 else
+            L.pa_decode_multi_workspace_bytes(ctypes.byref(d), 256, 4, 32, 4096 // bs))
+        assert (L.pa_decode_shared_workspace_bytes(ctypes.byref(d), 256, 32, 4096 // bs, 64) > 0) == (bs == 16)
+    d8 = desc(block_size=8)
+    assert L.pa_decode_multi(ctypes.byref(d8), P, P, P, 4, 2, 32, 16, 1.0, P, None, 0, None) == \
+        _lib.PA_ERR_UNSUPPORTED
+    assert L.pa_decode_shared(ctypes.byref(d8), P, P, P, 4, 32, 16, P, P, 1, 1.0, P, None, 0, None) == \
+        _lib.PA_ERR_UNSUPPORTED
+    # the kernels address a block with 32-bit offsets: blocks over 1 GiB are refused
+    assert decode(L, desc(block_size=32, num_kv_heads=8192 * 32, head_size=128), hq=8192 * 32) == _lib.PA_ERR_SHAPE
+    # the same token reach in fewer, larger blocks plans the same work split
+    assert (L.pa_decode_workspace_bytes(ctypes.byref(desc(block_size=32)), 256, 32, 128)
+            == L.pa_decode_workspace_bytes(ctypes.byref(desc(block_size=16)), 256, 32, 256))
 
 
 def test_cache_op_argument_errors(L):
