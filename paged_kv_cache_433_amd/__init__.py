@@ -11,7 +11,9 @@ from .ops import (  # noqa: F401
     copy_blocks,
     decode,
     decode_multi,
+    decode_multi_workspace_bytes,
     decode_shared,
+    decode_shared_workspace_bytes,
     decode_workspace_bytes,
     probe_copy,
     probe_read,

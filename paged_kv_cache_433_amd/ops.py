@@ -77,6 +77,18 @@ def decode_workspace_bytes(k_cache, num_seqs, num_q_heads, max_blocks_per_seq) -
                                                    max_blocks_per_seq))
 
 
+def decode_multi_workspace_bytes(k_cache, num_seqs, q_len, num_q_heads, max_blocks_per_seq) -> int:
+    desc = _cache_desc(k_cache, k_cache)
+    return int(_lib.lib().pa_decode_multi_workspace_bytes(ctypes.byref(desc), num_seqs, q_len, num_q_heads,
+                                                         max_blocks_per_seq))
+
+
+def decode_shared_workspace_bytes(k_cache, num_seqs, num_q_heads, max_blocks_per_seq, num_groups) -> int:
+    desc = _cache_desc(k_cache, k_cache)
+    return int(_lib.lib().pa_decode_shared_workspace_bytes(ctypes.byref(desc), num_seqs, num_q_heads,
+                                                          max_blocks_per_seq, num_groups))
+
+
 def decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=None, workspace=None):
     """Paged decode attention; returns ``out`` (bf16 ``[num_seqs, num_q_heads, head_size]``).
 
