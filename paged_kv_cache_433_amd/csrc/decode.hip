@@ -931,87 +931,98 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
 }
 
 // Log-sum-exp merge of the pieces of segments cut by workgroup boundaries.
-// Grid: (num_wgs, heads_per_wg, column tiles of 16): block (w, k, t) merges
-// KV head k's columns 16t.. of the segment that workgroup w's first piece
-// ended, if any. One wavefront per column; lane i owns head dims
-// [i*D/64, (i+1)*D/64). The pieces are read in one pass with a running
-// rescale.
+// Grid: one block per decode workgroup w, one wavefront per KV head of a
+// head group. Block w merges the segment that workgroup w's first piece
+// ended, if any (the others exit at once). Lanes take 8 head dims of a column
+// each (D/8 lanes per column) and two columns per pass, 64 / (D/8) columns
+// apart. The pieces are slot d.y & 1 of workgroup d.y >> 1, then the first
+// slot of every workgroup up to w; the records of four pieces of both columns
+// are loaded together, then folded in with a running rescale.
 template <int D, bool kSegments>
-__global__ __launch_bounds__(1024) void merge_kernel(const DecodeArgs a) {
-  constexpr int PL = D / 64;  // dims per lane: 1 or 2
+__global__ __launch_bounds__(256) void merge_kernel(const DecodeArgs a) {
+  constexpr int LPC = D / 8;     // lanes per column
+  constexpr int CPP = 64 / LPC;  // columns per half pass
+  constexpr int kPieces = 4;
   const int w1 = blockIdx.x;
   const int2 d = a.merge_desc[w1];
   if (d.x < 0) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // KV head within the head group
   const int lane = threadIdx.x & 63;
-  const int c = (threadIdx.x >> 6) + 16 * blockIdx.z;  // column: new token * group + query head
-  if (c >= a.num_cols) return;
-  const int wave = blockIdx.y;                        // KV head within the head group
-  const int s = d.x / a.num_head_groups;
-  const int hg = d.x - s * a.num_head_groups;
-  const int g = hg * a.heads_per_wg + wave;
-  const int tok = c / a.group;
-  const int qh = c - tok * a.group;
-  const int w0 = d.y >> 1;
   const int HG = a.heads_per_wg;
-  // Output rows: the sequence's q_len rows, or a segment's members (kShared).
+  const int s = d.x / a.num_head_groups;
+  const int g = (d.x - s * a.num_head_groups) * HG + wave;
+  // Output rows: the sequence's q_len rows, or a segment's members (kSegments).
   size_t row0 = (size_t)s * a.q_len;
+  int cols = a.num_cols;
   if constexpr (kSegments) {
     const ShareItem x = a.items[s];
-    if (c >= x.ntok * a.group) return;
     row0 = (size_t)x.qrow;
+    cols = x.ntok * a.group;
   }
-
-  // Pieces: slot d.y & 1 of workgroup w0, then the first slot of every
-  // workgroup up to w1 (whose ranges all lie inside the segment). Four at a
-  // time: their loads are issued together, then folded in.
-  constexpr int kPieces = 4;
-  float M = -INFINITY, Lsum = 0.f;
-  float o[PL];
+  const float *__restrict__ pml = a.part_ml;
+  const float *__restrict__ pob = a.part_o;
+  const int w0 = d.y >> 1;
+  const int sub = lane / LPC, dd = (lane - sub * LPC) * 8;
+  for (int c0 = 0; c0 < cols; c0 += 2 * CPP) {
+    float Mx[2] = {-INFINITY, -INFINITY}, Ls[2] = {0.f, 0.f};
+    f32x4_t o[2][2];
 #pragma unroll
-  for (int i = 0; i < PL; ++i) o[i] = 0.f;
-  for (int w = w0; w <= w1; w += kPieces) {
-    float pm[kPieces], pl[kPieces], po[kPieces][PL];
+    for (int u = 0; u < 2; ++u) o[u][0] = o[u][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int w = w0; w <= w1; w += kPieces) {
+      float pm[2][kPieces], pl[2][kPieces];
+      f32x4_t po[2][kPieces][2];
 #pragma unroll
-    for (int k = 0; k < kPieces; ++k) {
-      pm[k] = -INFINITY;
-      pl[k] = 0.f;
+      for (int k = 0; k < kPieces; ++k) {
+        const size_t rec = w + k == w0 ? (size_t)d.y : (size_t)2 * (w + k);
 #pragma unroll
-      for (int i = 0; i < PL; ++i) po[k][i] = 0.f;
-      if (w + k <= w1) {
-        const int rec = w + k == w0 ? d.y : 2 * (w + k);
-        const size_t r = ((size_t)rec * HG + wave) * a.num_cols + c;
-        const f32x2_t ml = *reinterpret_cast<const f32x2_t *>(a.part_ml + r * 2);
-        pm[k] = ml[0];
-        pl[k] = ml[1];
+        for (int u = 0; u < 2; ++u) {
+          const int c = c0 + u * CPP + sub;
+          pm[u][k] = -INFINITY;  // padding: weight 0
+          pl[u][k] = 0.f;
+          po[u][k][0] = po[u][k][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          if (w + k <= w1 && c < cols) {
+            const size_t r = (rec * HG + wave) * a.num_cols + c;
+            const f32x2_t ml = *reinterpret_cast<const f32x2_t *>(pml + r * 2);
+            pm[u][k] = ml[0];
+            pl[u][k] = ml[1];
+            po[u][k][0] = *reinterpret_cast<const f32x4_t *>(pob + r * D + dd);
+            po[u][k][1] = *reinterpret_cast<const f32x4_t *>(pob + r * D + dd + 4);
+          }
+        }
+      }
 #pragma unroll
-        for (int i = 0; i < PL; ++i) po[k][i] = a.part_o[r * D + lane * PL + i];
+      for (int u = 0; u < 2; ++u) {
+        float Mn = Mx[u];
+#pragma unroll
+        for (int k = 0; k < kPieces; ++k) Mn = fmaxf(Mn, pm[u][k]);
+        // A piece may see no position of a column (several new tokens, an
+        // empty member): its max is -inf and its weight 0; so is the running
+        // max before the first piece.
+        const float Mu = Mn == -INFINITY ? 0.f : Mn;
+        const float so = fast_exp2(Mx[u] - Mu);
+        Ls[u] *= so;
+        o[u][0] = o[u][0] * so;
+        o[u][1] = o[u][1] * so;
+#pragma unroll
+        for (int k = 0; k < kPieces; ++k) {
+          const float wt = fast_exp2(pm[u][k] - Mu);
+          Ls[u] += wt * pl[u][k];
+          o[u][0] += po[u][k][0] * wt;
+          o[u][1] += po[u][k][1] * wt;
+        }
+        Mx[u] = Mn;
       }
     }
-    float Mn = M;
 #pragma unroll
-    for (int k = 0; k < kPieces; ++k) Mn = fmaxf(Mn, pm[k]);
-    // A piece may see no position of a column (several new tokens): its max
-    // is -inf and its weight 0; so is the running max before the first piece.
-    const float Mu = Mn == -INFINITY ? 0.f : Mn;
-    const float so = fast_exp2(M - Mu);
-    Lsum *= so;
-#pragma unroll
-    for (int i = 0; i < PL; ++i) o[i] *= so;
-#pragma unroll
-    for (int k = 0; k < kPieces; ++k) {
-      const float wt = fast_exp2(pm[k] - Mu);  // 0 for the padding (max -inf)
-      Lsum += wt * pl[k];
-#pragma unroll
-      for (int i = 0; i < PL; ++i) o[i] += wt * po[k][i];
+    for (int u = 0; u < 2; ++u) {
+      const int c = c0 + u * CPP + sub;
+      if (c >= cols) continue;
+      const float inv = Ls[u] > 0.f ? 1.f / Ls[u] : 0.f;
+      const int tok = c / a.group, qh = c - tok * a.group;
+      const f32x4_t x = o[u][0] * inv, y = o[u][1] * inv;
+      const u32x4_t v = {to_bf16x2(x[0], x[1]), to_bf16x2(x[2], x[3]), to_bf16x2(y[0], y[1]), to_bf16x2(y[2], y[3])};
+      *reinterpret_cast<u32x4_t *>(a.out + ((row0 + tok) * a.num_q_heads + (size_t)g * a.group + qh) * D + dd) = v;
     }
-    M = Mn;
-  }
-  const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
-  uint16_t *dst = a.out + ((row0 + tok) * a.num_q_heads + (size_t)g * a.group + qh) * D + lane * PL;
-  if constexpr (PL == 2) {
-    *reinterpret_cast<uint32_t *>(dst) = to_bf16x2(o[0] * inv, o[1] * inv);
-  } else {
-    dst[0] = (uint16_t)(to_bf16x2(o[0] * inv, 0.f) & 0xFFFFu);
   }
 }
 
@@ -1059,7 +1070,8 @@ __device__ __forceinline__ int wg_max_scan(int v, int *red, int wave, int lane, 
 //     decoded: its members' outputs are zeroed here.
 template <int kThreads>
 __global__ __launch_bounds__(kThreads) void share_plan_kernel(const SharePlanArgs p) {
-  extern __shared__ __align__(16) int plan_lds[];  // grp[S], sid[S], shb[G], then csum[S] (64-bit)
+  // grp[S], sid[S], shb[G], gs[G + 1], len[S], then csum[S] (64-bit)
+  extern __shared__ __align__(16) int plan_lds[];
   __shared__ long long red[kThreads / 64];
   __shared__ int redi[kThreads / 64];
   __shared__ int bad;
@@ -1068,22 +1080,31 @@ __global__ __launch_bounds__(kThreads) void share_plan_kernel(const SharePlanArg
   int *grp = plan_lds;
   int *sid = grp + S;
   int *shb = sid + S;
-  long long *csum = reinterpret_cast<long long *>(plan_lds + ((2 * S + NGr + 1) & ~1));
+  int *gs = shb + NGr;
+  int *len = gs + NGr + 1;
+  long long *csum = reinterpret_cast<long long *>(plan_lds + ((3 * S + 2 * NGr + 1 + 1) & ~1));
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int cap = p.max_blocks_per_seq * kBlock;
 
+  // Every input into LDS first: their loads are independent, so the plan
+  // waits for memory once.
   if (tid == 0) bad = 0;
-  for (int i = tid; i < S; i += kThreads) grp[i] = -1;
+  for (int i = tid; i < S; i += kThreads) {
+    grp[i] = -1;
+    len[i] = clamp_len(p.lens[i], cap);
+  }
+  if (NGr > 0)  // with no groups the arrays may be null
+    for (int g = tid; g <= NGr; g += kThreads) gs[g] = p.group_starts[g];
+  for (int g = tid; g < NGr; g += kThreads) shb[g] = min(max(p.shared_blocks[g], 0), p.max_blocks_per_seq);
   __syncthreads();
   for (int g = tid; g < NGr; g += kThreads) {
-    const int lo = p.group_starts[g], hi = p.group_starts[g + 1];
+    const int lo = gs[g], hi = gs[g + 1];
     if (lo > hi || (g == 0 && lo < 0) || (g == NGr - 1 && hi > S)) bad = 1;
   }
   __syncthreads();
   const bool valid = bad == 0;
   for (int g = tid; g < NGr; g += kThreads) {
-    shb[g] = min(max(p.shared_blocks[g], 0), p.max_blocks_per_seq);
-    const int lo = p.group_starts[g], hi = p.group_starts[g + 1];
+    const int lo = gs[g], hi = gs[g + 1];
     if (valid && hi > lo) grp[lo] = g;  // distinct starts: groups are nonempty and ordered
   }
   __syncthreads();
@@ -1099,11 +1120,11 @@ __global__ __launch_bounds__(kThreads) void share_plan_kernel(const SharePlanArg
   for (int i = tid; i < S; i += kThreads) {
     const int g = grp[i];
     if (g < 0) continue;
-    if (i >= p.group_starts[g + 1]) {
+    if (i >= gs[g + 1]) {
       grp[i] = -1;
       continue;
     }
-    atomicMin(&shb[g], clamp_len(p.lens[i], cap) / kBlock);  // LDS atomic
+    atomicMin(&shb[g], len[i] / kBlock);  // LDS atomic
   }
   __syncthreads();
 
@@ -1114,10 +1135,10 @@ __global__ __launch_bounds__(kThreads) void share_plan_kernel(const SharePlanArg
     const int i = base + tid;
     long long opens = 0, adds = 0;
     if (i < S) {
-      const int n = clamp_len(p.lens[i], cap);
+      const int n = len[i];
       const int g = grp[i];
       const int e = g >= 0 ? shb[g] : 0;
-      opens = (g < 0 || (i - p.group_starts[g]) % C == 0) ? 1 : 0;
+      opens = (g < 0 || (i - gs[g]) % C == 0) ? 1 : 0;
       adds = (n + kBlock - 1) / kBlock - e + (opens ? e : 0);
     }
     long long pre, tot, preb, totb;
@@ -1134,9 +1155,9 @@ __global__ __launch_bounds__(kThreads) void share_plan_kernel(const SharePlanArg
   const long long NG = p.num_head_groups;
   for (int i = tid; i < S; i += kThreads) {
     const int g = grp[i];
-    if (g >= 0 && (i - p.group_starts[g]) % C != 0) continue;  // not the first member of its segment
-    const int lo = g >= 0 ? p.group_starts[g] : i;
-    const int hi = g >= 0 ? p.group_starts[g + 1] : i + 1;
+    if (g >= 0 && (i - gs[g]) % C != 0) continue;  // not the first member of its segment
+    const int lo = g >= 0 ? gs[g] : i;
+    const int hi = g >= 0 ? gs[g + 1] : i + 1;
     const int ntok = min(C, hi - i);
     const long long start = i > 0 ? csum[i - 1] : 0;
     const long long blocks = csum[i + ntok - 1] - start;
@@ -1216,9 +1237,8 @@ hipError_t launch_decode(const DecodeArgs &args, int32_t head_size, hipStream_t 
     return hipErrorInvalidValue;
   }
   if (err != hipSuccess || args.num_wgs <= 1) return err;
-  const unsigned tiles = (unsigned)((args.num_cols + 15) / 16);
-  const dim3 mgrid((unsigned)args.num_wgs, (unsigned)args.heads_per_wg, tiles);
-  const dim3 mblock(64 * (unsigned)(args.num_cols < 16 ? args.num_cols : 16));
+  const dim3 mgrid((unsigned)args.num_wgs);
+  const dim3 mblock(64 * (unsigned)args.heads_per_wg);
   if (head_size == 128) {
     hipLaunchKernelGGL((merge_kernel<128, false>), mgrid, mblock, 0, stream, args);
   } else {
@@ -1235,8 +1255,9 @@ hipError_t launch_decode_shared(const SharePlanArgs &plan, const DecodeArgs &arg
     return hipErrorInvalidValue;
   if (head_size != 128 && head_size != 64) return hipErrorInvalidValue;
   constexpr int kPlanThreads = 512;
-  const size_t plan_lds = ((2 * (size_t)plan.num_seqs + plan.num_groups + 1) & ~(size_t)1) * sizeof(int) +
-                          (size_t)plan.num_seqs * sizeof(long long);
+  const size_t plan_lds =
+      ((3 * (size_t)plan.num_seqs + 2 * (size_t)plan.num_groups + 2) & ~(size_t)1) * sizeof(int) +
+      (size_t)plan.num_seqs * sizeof(long long);
   hipError_t e = allow_lds(share_plan_kernel<kPlanThreads>, plan_lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(share_plan_kernel<kPlanThreads>, dim3(1), dim3(kPlanThreads), plan_lds, stream, plan);
@@ -1247,8 +1268,8 @@ hipError_t launch_decode_shared(const SharePlanArgs &plan, const DecodeArgs &arg
   e = head_size == 128 ? launch_decode_kernel<128, 2, kShared>(args, lds, stream)
                        : launch_decode_kernel<64, 2, kShared>(args, lds, stream);
   if (e != hipSuccess || args.num_wgs <= 1) return e;
-  const dim3 mgrid((unsigned)args.num_wgs, (unsigned)args.heads_per_wg, (unsigned)((args.num_cols + 15) / 16));
-  const dim3 mblock(64 * 16);
+  const dim3 mgrid((unsigned)args.num_wgs);
+  const dim3 mblock(64 * (unsigned)args.heads_per_wg);
   if (head_size == 128) {
     hipLaunchKernelGGL((merge_kernel<128, true>), mgrid, mblock, 0, stream, args);
   } else {
