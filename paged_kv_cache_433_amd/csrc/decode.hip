@@ -614,11 +614,13 @@ __device__ __forceinline__ bool step(const int32_t *__restrict__ tables, const D
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
   const int b = M == kShared ? st.cc.b : P.off + st.i;
   const int pos0 = b * CH + ln.grp * 4;
-  // kShared: in a member's own blocks only that member's columns are live,
-  // and a tile holding none of them is skipped (a uniform branch).
+  // kShared: in the shared blocks the segment's members' columns are live,
+  // in a member's own blocks only that member's; a tile holding none of them
+  // is skipped (a uniform branch).
   const int cj = M == kShared ? st.cc.j : -1;
   auto tile_live = [&](int t) {
-    return M != kShared || cj < 0 || (cj * a.group < 16 * (t + 1) && (cj + 1) * a.group > 16 * t);
+    if constexpr (M != kShared) return true;
+    return cj < 0 ? 16 * t < P.ntok * a.group : (cj * a.group < 16 * (t + 1) && (cj + 1) * a.group > 16 * t);
   };
   u32x2_t pb_hi[NT], pb_lo[NT];
 #pragma unroll
