@@ -26,7 +26,9 @@
  *   - bfloat16 tensors are passed as raw 16-bit storage.
  *   - Errors that can be seen on the host are reported before anything is
  *     enqueued: a NULL pointer, a negative count, an unsupported dtype, head
- *     size, block size or head grouping, or a workspace that is too small.
+ *     size, block size or head grouping, a data pointer that is not 16-byte
+ *     aligned (the kernels move data in 16-byte vectors), or a workspace that
+ *     is too small.
  *     PA_ERR_HIP reports a failed HIP call; its text is in pa_last_error().
  *   - Device-side indices are clamped or skipped, never trusted: a block id
  *     outside [0, num_blocks), a slot outside the pool or a CoW pair outside
@@ -63,8 +65,10 @@ enum { PA_DTYPE_BF16 = 0 };
  * KV head, so a block's K plus V is 2*block_size*num_kv_heads*head_size*2
  * bytes, the per-block size the page gives.
  *
- * Supported: dtype PA_DTYPE_BF16, block_size 16, head_size 64 or 128,
- * num_blocks >= 1, num_kv_heads >= 1. The descriptor is read on every call
+ * Supported: dtype PA_DTYPE_BF16; block_size 8, 16 or 32 (several new tokens
+ * per sequence and sharing-aware decode need 16); head_size 64 or 128;
+ * num_blocks >= 1; num_kv_heads >= 1; one block of one array at most 1 GiB;
+ * k_cache and v_cache 16-byte aligned. The descriptor is read on every call
  * and not kept.
  */
 typedef struct pa_kv_cache {
@@ -85,21 +89,23 @@ typedef struct pa_kv_cache {
  *
  * For sequence s with n = context_lens[s] cached tokens (the newest one
  * included, so pa_reshape_and_cache of this step runs first), logical token
- * i lives in physical block block_tables[s*max_blocks_per_seq + i/16] at
- * offset i%16. Query head h uses KV head h / (num_q_heads/num_kv_heads).
+ * i lives in physical block block_tables[s*max_blocks_per_seq + i/B] at
+ * offset i%B, B = cache->block_size. Query head h uses KV head
+ * h / (num_q_heads/num_kv_heads).
  *   out[s,h,:] = sum_i softmax_i(scale * q[s,h,:].k_i) * v_i
  * computed with fp32 accumulation and stored as bfloat16 (round to nearest
  * even). n == 0 gives a zero row.
  *
- *   q             bf16 [num_seqs, num_q_heads, head_size], contiguous
+ *   q             bf16 [num_seqs, num_q_heads, head_size], contiguous,
+ *                 16-byte aligned
  *   block_tables  int32 [num_seqs, max_blocks_per_seq]; entries at index
- *                 >= ceil(n/16) are never read
- *   context_lens  int32 [num_seqs]; 0 <= n <= max_blocks_per_seq*16
- *                 (larger values are treated as max_blocks_per_seq*16)
+ *                 >= ceil(n/B) are never read
+ *   context_lens  int32 [num_seqs]; 0 <= n <= max_blocks_per_seq*B
+ *                 (larger values are treated as max_blocks_per_seq*B)
  *   num_q_heads   multiple of num_kv_heads, with at most 16 query heads per
  *                 KV head
- *   out           bf16 [num_seqs, num_q_heads, head_size]; must not alias
- *                 any input
+ *   out           bf16 [num_seqs, num_q_heads, head_size], 16-byte aligned;
+ *                 must not alias any input
  *   workspace     device scratch of at least pa_decode_workspace_bytes(...)
  *                 bytes, 16-byte aligned, or NULL. The call shares the K/V
  *                 blocks of the whole batch evenly among its workgroups, so a
@@ -121,7 +127,8 @@ typedef struct pa_kv_cache {
  * Errors: PA_ERR_NULL (cache, cache->k_cache/v_cache, q, block_tables,
  * context_lens or out NULL while num_seqs > 0), PA_ERR_SHAPE (negative
  * counts, max_blocks_per_seq < 1, num_q_heads % num_kv_heads != 0),
- * PA_ERR_UNSUPPORTED (see pa_kv_cache; group size > 16), PA_ERR_WORKSPACE
+ * PA_ERR_UNSUPPORTED (see pa_kv_cache; group size > 16; q or out not
+ * 16-byte aligned), PA_ERR_WORKSPACE
  * (too small or misaligned), PA_ERR_HIP. num_seqs == 0 is a no-op.
  */
 int pa_decode(const pa_kv_cache *cache, const void *q, const int32_t *block_tables,
@@ -148,8 +155,9 @@ size_t pa_decode_workspace_bytes(const pa_kv_cache *cache, int32_t num_seqs,
  * "Chunked Prefill"; "Inside vLLM", section "Scheduler": the new tokens of a
  * step are not always 1).
  *
- *   q, out   bf16 [num_seqs, q_len, num_q_heads, head_size]
- *   q_len    >= 1, with q_len * (num_q_heads / num_kv_heads) <= 32
+ *   q, out   bf16 [num_seqs, q_len, num_q_heads, head_size], 16-byte aligned
+ *   q_len    >= 1, with q_len * (num_q_heads / num_kv_heads) <= 32; q_len > 1
+ *            needs block_size 16 (PA_ERR_UNSUPPORTED otherwise)
  * Other arguments, the workspace (size from pa_decode_multi_workspace_bytes)
  * and the errors are those of pa_decode; q_len == 1 is pa_decode. Every
  * context length must be 0 or >= q_len; a new token that would see no
@@ -193,12 +201,12 @@ size_t pa_decode_multi_workspace_bytes(const pa_kv_cache *cache, int32_t num_seq
  * When the declaration is true, the result is pa_decode's up to rounding
  * (the sums run in a different order). A false declaration reads the first
  * member's blocks, which is defined and stays in bounds.
- * Limits: num_seqs <= 4096. The other arguments, layouts and errors are those
- * of pa_decode. The workspace (owned by the caller, or allocated
+ * Limits: num_seqs <= 4096; block_size 16. The other arguments, layouts and
+ * errors are those of pa_decode. The workspace (owned by the caller, or allocated
  * stream-ordered by the call when NULL) has the size that
  * pa_decode_shared_workspace_bytes returns, which is never 0 for
  * num_seqs > 0. Errors: as pa_decode, plus PA_ERR_SHAPE (num_groups outside
- * 0..num_seqs) and PA_ERR_UNSUPPORTED (num_seqs > 4096).
+ * 0..num_seqs) and PA_ERR_UNSUPPORTED (num_seqs > 4096, block_size not 16).
  */
 int pa_decode_shared(const pa_kv_cache *cache, const void *q, const int32_t *block_tables,
                      const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
@@ -217,9 +225,11 @@ size_t pa_decode_shared_workspace_bytes(const pa_kv_cache *cache, int32_t num_se
  * decode step that follows sees every earlier token cached: "Inside vLLM",
  * section "Scheduler").
  *
- *   k, v          bf16 [num_tokens, num_kv_heads, head_size], contiguous
- *   slot_mapping  int64 [num_tokens]; slot = block*16 + offset. A negative
- *                 slot (padding) or a slot >= num_blocks*16 is skipped.
+ *   k, v          bf16 [num_tokens, num_kv_heads, head_size], contiguous,
+ *                 16-byte aligned
+ *   slot_mapping  int64 [num_tokens]; slot = block*block_size + offset. A
+ *                 negative slot (padding) or a slot >= num_blocks*block_size
+ *                 is skipped.
  *                 Slots must be distinct (otherwise which token wins is
  *                 unspecified).
  * The copy is bit-exact. num_tokens == 0 is a no-op.

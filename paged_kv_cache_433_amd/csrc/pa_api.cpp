@@ -67,9 +67,17 @@ int32_t heads_per_workgroup(int32_t num_kv_heads) {
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// The kernels move data in 16-byte vectors.
+int check_aligned(const void *p, const char *what) {
+  if (reinterpret_cast<uintptr_t>(p) % 16) return fail(PA_ERR_UNSUPPORTED, std::string(what) + " must be 16-byte aligned");
+  return PA_OK;
+}
+
 int check_cache(const pa_kv_cache *c, bool need_data) {
   if (!c) return fail(PA_ERR_NULL, "cache descriptor is NULL");
   if (need_data && (!c->k_cache || !c->v_cache)) return fail(PA_ERR_NULL, "k_cache or v_cache is NULL");
+  if (need_data && (check_aligned(c->k_cache, "k_cache") != PA_OK || check_aligned(c->v_cache, "v_cache") != PA_OK))
+    return PA_ERR_UNSUPPORTED;
   if (c->dtype != PA_DTYPE_BF16) return fail(PA_ERR_UNSUPPORTED, "only bf16 caches are supported");
   if (c->block_size != 8 && c->block_size != 16 && c->block_size != 32)
     return fail(PA_ERR_UNSUPPORTED, "block_size must be 8, 16 or 32");
@@ -217,6 +225,7 @@ int pa_decode_multi(const pa_kv_cache *cache, const void *q, const int32_t *bloc
   if (num_seqs == 0) return ok();
   if (!q || !block_tables || !context_lens || !out)
     return fail(PA_ERR_NULL, "q, block_tables, context_lens or out is NULL");
+  if (check_aligned(q, "q") != PA_OK || check_aligned(out, "out") != PA_OK) return PA_ERR_UNSUPPORTED;
 
   const pa::DecodePlan plan = pa::plan_decode(num_seqs, num_q_heads, cache->num_kv_heads, cache->head_size,
                                               chunks_per_row(cache, max_blocks_per_seq), q_len);
@@ -292,6 +301,7 @@ int pa_decode_shared(const pa_kv_cache *cache, const void *q, const int32_t *blo
   if (num_seqs == 0) return ok();
   if (!q || !block_tables || !context_lens || !out)
     return fail(PA_ERR_NULL, "q, block_tables, context_lens or out is NULL");
+  if (check_aligned(q, "q") != PA_OK || check_aligned(out, "out") != PA_OK) return PA_ERR_UNSUPPORTED;
   if (num_groups > 0 && (!group_starts || !shared_blocks))
     return fail(PA_ERR_NULL, "group_starts or shared_blocks is NULL");
 
@@ -370,6 +380,7 @@ int pa_reshape_and_cache(const pa_kv_cache *cache, const void *k, const void *v,
   if (num_tokens < 0) return fail(PA_ERR_SHAPE, "num_tokens < 0");
   if (num_tokens == 0) return ok();
   if (!k || !v || !slot_mapping) return fail(PA_ERR_NULL, "k, v or slot_mapping is NULL");
+  if (check_aligned(k, "k") != PA_OK || check_aligned(v, "v") != PA_OK) return PA_ERR_UNSUPPORTED;
   const int64_t row = (int64_t)cache->num_kv_heads * cache->head_size;
   if (row > 0x7fffffffLL) return fail(PA_ERR_SHAPE, "num_kv_heads * head_size too large");
   hipError_t e = pa::launch_reshape_and_cache(

@@ -193,3 +193,24 @@ def test_cache_op_argument_errors(L):
     assert L.pa_probe_copy(P, P, 24, None) == _lib.PA_ERR_SHAPE
     assert L.pa_probe_copy(None, P, 32, None) == _lib.PA_ERR_NULL
     assert L.pa_probe_copy(None, None, 0, None) == _lib.PA_OK
+
+
+def test_misaligned_pointers_are_refused(L):
+    """The kernels move data in 16-byte vectors: a misaligned data pointer is
+    refused on the host, naming the argument."""
+    odd = ctypes.c_void_p(0x3008)
+    d = desc()
+    assert decode(L, d, q=odd) == _lib.PA_ERR_UNSUPPORTED
+    assert "q must be 16-byte aligned" in L.pa_last_error().decode()
+    assert decode(L, d, out=odd) == _lib.PA_ERR_UNSUPPORTED
+    assert decode(L, desc(k_cache=0x1002)) == _lib.PA_ERR_UNSUPPORTED
+    assert "k_cache" in L.pa_last_error().decode()
+    assert decode(L, desc(v_cache=0x2004)) == _lib.PA_ERR_UNSUPPORTED
+    assert L.pa_decode_multi(ctypes.byref(d), P, P, P, 4, 2, 32, 16, 1.0, odd, None, 0, None) == _lib.PA_ERR_UNSUPPORTED
+    assert L.pa_decode_shared(ctypes.byref(d), odd, P, P, 8, 32, 16, P, P, 2, 1.0, P, None, 0,
+                              None) == _lib.PA_ERR_UNSUPPORTED
+    assert L.pa_reshape_and_cache(ctypes.byref(d), odd, P, P, 4, None) == _lib.PA_ERR_UNSUPPORTED
+    assert L.pa_reshape_and_cache(ctypes.byref(d), P, odd, P, 4, None) == _lib.PA_ERR_UNSUPPORTED
+    assert L.pa_copy_blocks(ctypes.byref(desc(k_cache=0x1008)), P, 2, None) == _lib.PA_ERR_UNSUPPORTED
+    # sizes alone need no data pointers, aligned or not
+    assert L.pa_decode_workspace_bytes(ctypes.byref(desc(k_cache=0x1002)), 256, 32, 256) > 0
