@@ -314,6 +314,8 @@ struct Stream {
 
 // Buffer-resource word 3 for gfx9-family raw (untyped) buffer loads.
 constexpr int kRawBufferWord3 = 0x00020000;
+// Cache-policy operand of a buffer load: the nt (non-temporal) bit.
+constexpr int kNonTemporal = 2;
 
 // q rows of the piece's columns for this wavefront, in the MFMA operand
 // layout. Read through a buffer resource (scalar base at the KV head's first
@@ -436,7 +438,10 @@ __device__ __forceinline__ size_t head_off(const Lane<NT> &ln, const Piece &p) {
 // head) start (scalar registers) and whose size covers the block's first
 // `nrows` token rows; the lane adds its fixed offset. So no vector address
 // arithmetic happens per block, and the rows past the context length in a
-// sequence's last block are never fetched: they read as zeros.
+// sequence's last block are never fetched: they read as zeros. The loads
+// carry the non-temporal hint: K/V bytes are read once per call, and on the
+// GQA layer the hint measured about 1 us (0.4%) faster per call than plain
+// loads, with a lower p90.
 template <int NJ, int NT>
 __device__ __forceinline__ void issue(const DecodeArgs &a, const Lane<NT> &ln, int blk, size_t hoff, int nrows,
                                       u32x4_t (&K)[NJ], u32x4_t (&V)[NJ]) {
@@ -448,10 +453,10 @@ __device__ __forceinline__ void issue(const DecodeArgs &a, const Lane<NT> &ln, i
       const_cast<char *>(reinterpret_cast<const char *>(a.v_cache) + base), 0, span, kRawBufferWord3);
 #pragma unroll
   for (int j = 0; j < NJ; ++j)
-    K[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, ln.lane_off + 64 * j, 0, 0));
+    K[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, ln.lane_off + 64 * j, 0, kNonTemporal));
 #pragma unroll
   for (int j = 0; j < NJ; ++j)
-    V[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, ln.lane_off + 64 * j, 0, 0));
+    V[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, ln.lane_off + 64 * j, 0, kNonTemporal));
 }
 
 // Starts the loads of chunk c of table row `row` for this wavefront's head,
