@@ -15,8 +15,11 @@ bytes / its mean time from HIP events around the call on the launch stream,
 against 8 TB/s; ``traffic`` is the call's HBM bytes from rocprofv3 counters
 (profiles/decode_traffic.json) when they were taken on the current kernel;
 ``mean_launch_us_mall_evicted`` repeats the call with the 256 MB memory-side
-cache evicted before each launch (a 2 GiB read scan outside the events). ``cpu_baseline`` times the float64 oracle on a bounded
-sample of the same workload on this host.
+cache evicted before each launch (a 2 GiB read scan outside the events), and
+``stream_read_same_bytes`` is a streaming read of as many contiguous bytes
+timed the same way (``frac_of_stream_read`` = achieved / that).
+``cpu_baseline`` times the float64 oracle on a bounded sample of the same
+workload on this host.
 
     python bench.py [--gpus 1] [--steps 500] [--warmup 20] [--config NAME]
 """
@@ -435,7 +438,7 @@ def main(argv=None) -> int:
     # evicted before each launch by reading a 2 GiB buffer, outside the
     # events: shows whether repeated calls on the same cache are served from
     # it. A read scan leaves no dirty lines behind to be written back later.
-    cold_us = None
+    cold_us = stream_read_gbps = None
     if args.cold_launches:
         scratch = torch.ones(2 << 30, dtype=torch.uint8, device=dev)
         sink = torch.empty(pa.probe_read_sink_bytes(), dtype=torch.uint8, device=dev)
@@ -448,7 +451,21 @@ def main(argv=None) -> int:
             z.record(stream)
         torch.cuda.synchronize()
         cold_us = float(np.mean([a.elapsed_time(z) for a, z in cold])) * 1e3
-        del scratch, sink
+        # A streaming read (pa_probe_read) of as many bytes as the call's
+        # algorithmic bytes, with the MALL evicted the same way: what one pass
+        # over contiguous memory achieves at this size.
+        span = torch.ones(int(decode_bytes) // 16 * 16, dtype=torch.uint8, device=dev)
+        reads = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+        pa.probe_read(span, sink)
+        for a, z in reads:
+            pa.probe_read(scratch, sink)
+            a.record(stream)
+            pa.probe_read(span, sink)
+            z.record(stream)
+        torch.cuda.synchronize()
+        read_us = float(np.median([a.elapsed_time(z) for a, z in reads])) * 1e3
+        stream_read_gbps = span.numel() / read_us / 1e3
+        del scratch, sink, span
 
     value = step_bytes / (ms * 1e-3) / 1e9
     achieved = decode_bytes / (dec_mean * 1e-3) / 1e9
@@ -504,6 +521,8 @@ def main(argv=None) -> int:
             "mean_launch_us": round(dec_mean * 1e3, 2),
             "mean_launch_us_mall_evicted": round(cold_us, 2) if cold_us else None,
             "achieved_mall_evicted": round(decode_bytes / cold_us / 1e3, 2) if cold_us else None,
+            "stream_read_same_bytes": round(stream_read_gbps, 1) if stream_read_gbps else None,
+            "frac_of_stream_read": round(achieved / stream_read_gbps, 4) if stream_read_gbps else None,
         },
         "cpu_baseline": None,
     }
