@@ -310,6 +310,14 @@ struct Stream {
   // P's and Q's segments (lane j: member j; 0 past the last member).
   Cursor cc;
   int lv_p, lv_q;
+  // One column tile: the first piece's partial record when that piece is
+  // cut, and the workgroup's merge record. Both are stored after the stream
+  // ends, not when the first piece ends: the wait for every later block's
+  // loads would otherwise also wait for those stores to complete.
+  f32x4_t first_acc[2 * NJ];
+  float first_m, first_l;
+  bool first_cut;
+  int2 desc;
 };
 
 // Buffer-resource word 3 for gfx9-family raw (untyped) buffer loads.
@@ -492,11 +500,33 @@ __device__ __forceinline__ int rows_in(int n, int b) {
   return r < CH ? r : CH;
 }
 
+// Stores the partial record of column tile t of this wavefront in slot
+// `slot` (0: the workgroup's first piece, 1: its last): unnormalised output,
+// running max (base 2) and sum.
+template <int NJ, int NT>
+__device__ __forceinline__ void store_record(const DecodeArgs &a, const Lane<NT> &ln, int t, int slot,
+                                             const f32x4_t (&acc)[2 * NJ], float m, float l) {
+  constexpr int D = NJ * 32;
+  const size_t row = (((size_t)ln.w * 2 + slot) * ln.HG + ln.wave) * a.num_cols + ln.col[t];
+  float *po = a.part_o + row * D + ln.grp * 8;
+#pragma unroll
+  for (int k = 0; k < 2 * NJ; ++k) *reinterpret_cast<f32x4_t *>(po + 32 * (k >> 1) + 4 * (k & 1)) = acc[k];
+  if (ln.grp == 0) {
+    if constexpr (NT == 1) {
+      *reinterpret_cast<f32x2_t *>(a.part_ml + row * 2) = f32x2_t{m, l};
+    } else {
+      a.part_ml[row * 2] = m;
+      a.part_ml[row * 2 + 1] = l;
+    }
+  }
+}
+
 // Writes P's result: bf16 output when P is a whole segment, otherwise its
 // partial record. A workgroup's first piece is the only one that can end a
 // segment begun in an earlier workgroup, so each workgroup writes one merge
-// record, when its first piece ends: that segment and where its pieces are,
-// or none.
+// record, decided when its first piece ends: that segment and where its
+// pieces are, or none. With one column tile the first piece's partial record
+// and the merge record are stored after the stream (finish_stream).
 template <int NJ, int NT, int M>
 __device__ __forceinline__ void finish_piece(const DecodeArgs &a, const Lane<NT> &ln, Stream<NJ, NT> &st) {
   constexpr int D = NJ * 32;
@@ -520,34 +550,40 @@ __device__ __forceinline__ void finish_piece(const DecodeArgs &a, const Lane<NT>
         store_out<NJ>(a.out + (row0 * a.num_q_heads + (size_t)g * a.group) * D + ln.out_off[t], st.acc[t], inv);
     } else {
       const int slot = P.first ? 0 : 1;
-      const size_t row = (((size_t)ln.w * 2 + slot) * ln.HG + ln.wave) * a.num_cols + ln.col[t];
-      if (keep) {
-        float *po = a.part_o + row * D + ln.grp * 8;
+      if (NT == 1 && P.first) {  // kept in registers until the stream ends
+        st.first_cut = keep;
 #pragma unroll
-        for (int k = 0; k < 2 * NJ; ++k)
-          *reinterpret_cast<f32x4_t *>(po + 32 * (k >> 1) + 4 * (k & 1)) = st.acc[t][k];
-        // With two tiles, two scalar stores: building a float2 from m_run[t]
-        // lets the compiler widen that read over m_run[t + 1], which pins the
-        // array to scratch, and every reload then waits for all loads in flight.
-        if (ln.grp == 0) {
-          if constexpr (NT == 1) {
-            *reinterpret_cast<f32x2_t *>(a.part_ml + row * 2) = f32x2_t{st.m_run[t], l};
-          } else {
-            a.part_ml[row * 2] = st.m_run[t];
-            a.part_ml[row * 2 + 1] = l;
-          }
-        }
+        for (int k = 0; k < 2 * NJ; ++k) st.first_acc[k] = st.acc[t][k];
+        st.first_m = st.m_run[t];
+        st.first_l = l;
+      } else if (keep) {
+        // With two tiles, two scalar stores for max and sum: building a float2
+        // from m_run[t] lets the compiler widen that read over m_run[t + 1],
+        // which pins the array to scratch, and every reload then waits for all
+        // loads in flight.
+        store_record<NJ, NT>(a, ln, t, slot, st.acc[t], st.m_run[t], l);
       }
     }
   }
-  if (P.first && ln.tid == 0 && a.merge_desc) {
+  if (P.first) {
     int2 d = {-1, -1};
     if (!whole && P.off + P.cnt == P.L) {  // ends a segment begun in an earlier workgroup
       const int w0 = owner_of(P.seg_start, ln.U, ln.E);
       const int slot0 = range_lo(w0, ln.U, ln.E) < P.seg_start ? 1 : 0;
       d = int2{P.s * ln.NG + P.hg, w0 * 2 + slot0};
     }
-    a.merge_desc[ln.w] = d;
+    if constexpr (NT == 1) st.desc = d;
+    else if (ln.tid == 0 && a.merge_desc) a.merge_desc[ln.w] = d;
+  }
+}
+
+// After the stream: the first piece's partial record (one column tile, if
+// that piece was cut) and the merge record.
+template <int NJ, int NT>
+__device__ __forceinline__ void finish_stream(const DecodeArgs &a, const Lane<NT> &ln, const Stream<NJ, NT> &st) {
+  if constexpr (NT == 1) {
+    if (st.first_cut) store_record<NJ, NT>(a, ln, 0, 0, st.first_acc, st.first_m, st.first_l);
+    if (ln.tid == 0 && a.merge_desc) a.merge_desc[ln.w] = st.desc;
   }
 }
 
@@ -928,6 +964,8 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
   }
   st.i = 0;
   st.ord = 0;
+  st.first_cut = false;
+  st.desc = int2{-1, -1};
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     st.m_run[t] = -INFINITY;
@@ -944,6 +982,7 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
   while (step<NJ, NT, M, BS>(tables, a, ln, wk, st, KA, VA, KB, VB, q_lds) &&
          step<NJ, NT, M, BS>(tables, a, ln, wk, st, KB, VB, KA, VA, q_lds)) {
   }
+  finish_stream<NJ, NT>(a, ln, st);
 }
 
 // Log-sum-exp merge of the pieces of segments cut by workgroup boundaries.
