@@ -70,13 +70,13 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-// The unit of work is a chunk of tokens, at most 16 (one MFMA tile of rows):
-// with 16-token cache blocks a chunk is a block, a 32-token block holds two
-// chunks, and an 8-token block is a chunk that fills half a tile.
+// The unit of work is a chunk of 16 tokens (one MFMA tile of rows): with
+// 16-token cache blocks a chunk is a block, a 32-token block holds two
+// chunks, and a chunk holds two 8-token blocks.
 constexpr int kBlock = 16;
 
 template <int BS>
-constexpr int chunk_of() { return BS < kBlock ? BS : kBlock; }
+constexpr int chunk_of() { return kBlock; }
 constexpr uint32_t kBf16One = 0x3F80u;
 
 // What a decode launch computes: one new token per sequence (kSingle);
@@ -509,16 +509,58 @@ __device__ __forceinline__ void issue(const DecodeArgs &a, const Lane<NT> &ln, i
     V[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, ln.lane_off + 64 * j, 0, 0));
 }
 
+// Two 8-token blocks as one chunk: rows 0-7 of the tile from block `ida`
+// (its first `na` rows), rows 8-15 from block `idb` (its first `nb`). Each
+// row is loaded from both blocks' resources at the lane's offset and at that
+// offset less 8 rows; for every lane one of the two is outside its range
+// (the second one is negative, so wraps past any range) and reads as zero,
+// so OR-ing them gives the row without a per-lane choice of resource.
+template <int NJ, int NT>
+__device__ __forceinline__ void issue_pair(const DecodeArgs &a, const Lane<NT> &ln, int ida, int idb, size_t hoff,
+                                           int na, int nb, u32x4_t (&K)[NJ], u32x4_t (&V)[NJ]) {
+  constexpr int kHalf = kBlock / 2;
+  const size_t base_a = ((size_t)ida * ln.blk_stride + hoff) * sizeof(uint16_t);
+  const size_t base_b = ((size_t)idb * ln.blk_stride + hoff) * sizeof(uint16_t);
+  const char *kc = reinterpret_cast<const char *>(a.k_cache), *vc = reinterpret_cast<const char *>(a.v_cache);
+  const __amdgpu_buffer_rsrc_t rka =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(kc + base_a), 0, na * ln.row_bytes, kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t rkb =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(kc + base_b), 0, nb * ln.row_bytes, kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t rva =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(vc + base_a), 0, na * ln.row_bytes, kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t rvb =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(vc + base_b), 0, nb * ln.row_bytes, kRawBufferWord3);
+  const uint32_t off_b = ln.lane_off - (uint32_t)(kHalf * ln.row_bytes);
+#pragma unroll
+  for (int j = 0; j < NJ / 2; ++j)
+    K[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rka, ln.lane_off + 64 * j, 0, kNonTemporal)) |
+           __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rkb, off_b + 64 * j, 0, kNonTemporal));
+#pragma unroll
+  for (int j = NJ / 2; j < NJ; ++j)
+    K[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rka, ln.lane_off + 64 * j, 0, 0)) |
+           __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rkb, off_b + 64 * j, 0, 0));
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+    V[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rva, ln.lane_off + 64 * j, 0, 0)) |
+           __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rvb, off_b + 64 * j, 0, 0));
+}
+
 // Starts the loads of chunk c of table row `row` for this wavefront's head,
-// in a cache of BS-token blocks: block c (BS = 16, or BS = 8 with the
-// tile's rows 8-15 past the block's range, read as zeros), or half of block
-// c/2 (BS = 32).
+// in a cache of BS-token blocks: block c (BS = 16), half of block c/2
+// (BS = 32), or blocks 2c and 2c+1 (BS = 8; the second only if the chunk
+// reaches into it).
 template <int NJ, int NT, int BS>
 __device__ __forceinline__ void issue_chunk(const int32_t *__restrict__ tables, const DecodeArgs &a,
                                             const Lane<NT> &ln, int row, int c, size_t hoff, int nrows,
                                             u32x4_t (&K)[NJ], u32x4_t (&V)[NJ]) {
   static_assert(BS == 8 || BS == 16 || BS == 32, "block size 8, 16 or 32");
-  if constexpr (BS <= kBlock) {
+  if constexpr (BS < kBlock) {
+    const int na = nrows < BS ? nrows : BS;
+    const int nb = nrows - na;
+    const int ida = block_id(tables, a, ln.pool32, row, 2 * c);
+    const int idb = nb > 0 ? block_id(tables, a, ln.pool32, row, 2 * c + 1) : 0;
+    issue_pair<NJ>(a, ln, ida, idb, hoff, na, nb, K, V);
+  } else if constexpr (BS == kBlock) {
     issue<NJ>(a, ln, block_id(tables, a, ln.pool32, row, c), hoff, nrows, K, V);
   } else {
     issue<NJ>(a, ln, block_id(tables, a, ln.pool32, row, c >> 1),

@@ -148,11 +148,10 @@ SharedLayout layout_shared(const pa_kv_cache *c, int32_t num_seqs, int32_t num_q
   return l;
 }
 
-// The decode kernel works in chunks of min(block_size, 16) tokens: a table
-// row of max_blocks_per_seq blocks holds at most this many.
+// The decode kernel works in chunks of 16 tokens: a table row of
+// max_blocks_per_seq blocks holds at most this many.
 int32_t chunks_per_row(const pa_kv_cache *c, int32_t max_blocks_per_seq) {
-  const int64_t chunk = c->block_size < 16 ? c->block_size : 16;
-  return (int32_t)((int64_t)max_blocks_per_seq * c->block_size / chunk);
+  return (int32_t)(((int64_t)max_blocks_per_seq * c->block_size + 15) / 16);
 }
 
 int check_shared(const pa_kv_cache *c, int32_t num_seqs, int32_t num_groups) {
