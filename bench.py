@@ -309,7 +309,7 @@ def main(argv=None) -> int:
                          "and runs pa_decode_multi")
     ap.add_argument("--block-size", type=int, default=16, choices=(8, 16, 32),
                     help="tokens per cache block for the named single-step configs (same pool capacity in "
-                         "tokens); with 8 or 32 one new token per sequence")
+                         "tokens)")
     ap.add_argument("--shared", action="store_true",
                     help="beam_cow only: decode with pa_decode_shared, reading a prompt's shared blocks once "
                          "for its beams (the sharing is read back from the block tables)")
@@ -358,8 +358,6 @@ def main(argv=None) -> int:
     else:
         if args.shared:
             raise SystemExit("--shared applies to the beam_cow workload")
-        if args.block_size != 16 and args.q_len != 1:
-            raise SystemExit("--block-size 8 or 32 takes one new token per sequence")
         b = W.make_config(args.config, q_len=args.q_len, block_size=args.block_size)
     multi = args.q_len > 1
     if args.config == "beam_cow" and args.block_size != 16:

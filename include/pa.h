@@ -156,8 +156,8 @@ size_t pa_decode_workspace_bytes(const pa_kv_cache *cache, int32_t num_seqs,
  * step are not always 1).
  *
  *   q, out   bf16 [num_seqs, q_len, num_q_heads, head_size], 16-byte aligned
- *   q_len    >= 1, with q_len * (num_q_heads / num_kv_heads) <= 32; q_len > 1
- *            needs block_size 16 (PA_ERR_UNSUPPORTED otherwise)
+ *   q_len    >= 1, with q_len * (num_q_heads / num_kv_heads) <= 32 (any of
+ *            the cache's block sizes, 8, 16 or 32)
  * Other arguments, the workspace (size from pa_decode_multi_workspace_bytes)
  * and the errors are those of pa_decode; q_len == 1 is pa_decode. Every
  * context length must be 0 or >= q_len; a new token that would see no

@@ -1373,12 +1373,17 @@ hipError_t launch_decode_kernel(const DecodeArgs &args, size_t lds, hipStream_t 
 template <int D>
 hipError_t launch_decode_d(const DecodeArgs &args, size_t lds, hipStream_t stream) {
   if (args.q_len == 1) {
-    // One new token: every block size; the other modes take 16-token blocks.
     if (args.block_size == 8) return launch_decode_kernel<D, 1, kSingle, 8>(args, lds, stream);
     if (args.block_size == 32) return launch_decode_kernel<D, 1, kSingle, 32>(args, lds, stream);
     return launch_decode_kernel<D, 1, kSingle>(args, lds, stream);
   }
-  if (args.num_cols <= 16) return launch_decode_kernel<D, 1, kCausal>(args, lds, stream);
+  if (args.num_cols <= 16) {
+    if (args.block_size == 8) return launch_decode_kernel<D, 1, kCausal, 8>(args, lds, stream);
+    if (args.block_size == 32) return launch_decode_kernel<D, 1, kCausal, 32>(args, lds, stream);
+    return launch_decode_kernel<D, 1, kCausal>(args, lds, stream);
+  }
+  if (args.block_size == 8) return launch_decode_kernel<D, 2, kCausal, 8>(args, lds, stream);
+  if (args.block_size == 32) return launch_decode_kernel<D, 2, kCausal, 32>(args, lds, stream);
   return launch_decode_kernel<D, 2, kCausal>(args, lds, stream);
 }
 
@@ -1386,8 +1391,7 @@ hipError_t launch_decode_d(const DecodeArgs &args, size_t lds, hipStream_t strea
 
 hipError_t launch_decode(const DecodeArgs &args, int32_t head_size, hipStream_t stream) {
   if (args.q_len < 1 || args.num_cols > 32 || (args.q_len == 1 && args.num_cols > 16)) return hipErrorInvalidValue;
-  if (args.block_size != 16 && (args.q_len != 1 || (args.block_size != 8 && args.block_size != 32)))
-    return hipErrorInvalidValue;
+  if (args.block_size != 8 && args.block_size != 16 && args.block_size != 32) return hipErrorInvalidValue;
   // LDS holds q: a two-slot ring per wavefront for the next piece (one column
   // tile), or the current piece's (two tiles).
   // With one column tile, each wavefront also has an output staging area.

@@ -107,12 +107,9 @@ int check_decode_shape(const pa_kv_cache *c, int32_t num_seqs, int32_t num_q_hea
 }
 
 // Several new tokens per sequence: their (token, query head) pairs of one KV
-// head must fit two 16-column MFMA tiles, and the cache must use 16-token
-// blocks (8- and 32-token blocks are taken with one new token).
+// head must fit two 16-column MFMA tiles.
 int check_q_len(const pa_kv_cache *c, int32_t num_q_heads, int32_t q_len) {
   if (q_len < 1) return fail(PA_ERR_SHAPE, "q_len must be >= 1");
-  if (q_len > 1 && c->block_size != 16)
-    return fail(PA_ERR_UNSUPPORTED, "several new tokens per sequence need block_size 16");
   if ((int64_t)q_len * (num_q_heads / c->num_kv_heads) > 32)
     return fail(PA_ERR_UNSUPPORTED, "q_len * (num_q_heads / num_kv_heads) must be <= 32");
   return PA_OK;

@@ -83,3 +83,21 @@ def test_multi_token_gqa_layer_full_size():
     idx = np.sort(rng.choice(b.num_seqs, 24, replace=False))
     ref = oracle.decode_multi(b.q[idx], b.k_cache, b.v_cache, b.block_tables[idx], b.context_lens[idx], b.scale)
     assert_attention_close(out[idx], ref, "multi gqa full size")
+
+
+@pytest.mark.parametrize("bs", [8, 32])
+@pytest.mark.parametrize("ql,hq,hkv,d", [(4, 32, 8, 128), (8, 8, 2, 128), (3, 8, 8, 64)])
+def test_multi_token_block_sizes(bs, ql, hq, hkv, d, monkeypatch):
+    """Several new tokens per sequence in 8- and 32-token blocks (one and two
+    column tiles), across work splits; lengths sit on block and chunk
+    boundaries."""
+    lens = [max(n, ql) for n in [4, 7, 8, 9, 15, 16, 17, 31, 32, 33, 100, 255, 1000]]
+    nb = int(sum((n + bs - 1) // bs for n in lens)) + 9
+    b = W.make_batch("multi", 800 + bs + ql * 10 + hq + d, lens, hq, hkv, d, nb, q_len=ql, block_size=bs)
+    assert b.block_size == bs
+    for wgs in ("1", "5", "default"):
+        if wgs == "default":
+            monkeypatch.delenv("PA_DECODE_WGS", raising=False)
+        else:
+            monkeypatch.setenv("PA_DECODE_WGS", wgs)
+        run_multi(b, f"multi bs={bs} ql={ql} hq={hq} hkv={hkv} d={d} wgs={wgs}")
