@@ -194,19 +194,19 @@ size_t pa_decode_multi_workspace_bytes(const pa_kv_cache *cache, int32_t num_seq
  *                  arrays may be NULL.
  * Which blocks are read:
  *   - Group g's prefix counts only whole blocks that every member fills:
- *     e = min(shared_blocks[g], context_lens[j] / 16 for each member j),
- *     clamped to 0..max_blocks_per_seq.
+ *     e = min(shared_blocks[g], context_lens[j] / block_size for each
+ *     member j), clamped to 0..max_blocks_per_seq.
  *   - Every member reads those e blocks through the table of the group's
  *     first member, and the rest through its own table.
  * When the declaration is true, the result is pa_decode's up to rounding
  * (the sums run in a different order). A false declaration reads the first
  * member's blocks, which is defined and stays in bounds.
- * Limits: num_seqs <= 4096; block_size 16. The other arguments, layouts and
+ * Limits: num_seqs <= 4096; block_size 8, 16 or 32. The other arguments, layouts and
  * errors are those of pa_decode. The workspace (owned by the caller, or allocated
  * stream-ordered by the call when NULL) has the size that
  * pa_decode_shared_workspace_bytes returns, which is never 0 for
  * num_seqs > 0. Errors: as pa_decode, plus PA_ERR_SHAPE (num_groups outside
- * 0..num_seqs) and PA_ERR_UNSUPPORTED (num_seqs > 4096, block_size not 16).
+ * 0..num_seqs) and PA_ERR_UNSUPPORTED (num_seqs > 4096).
  */
 int pa_decode_shared(const pa_kv_cache *cache, const void *q, const int32_t *block_tables,
                      const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,

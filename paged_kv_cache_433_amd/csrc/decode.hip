@@ -191,9 +191,10 @@ struct Piece {
   int n;                // positions < n are visible (the clamped context length)
   int L;                // blocks of the segment
   bool first;           // the workgroup's first piece
-  // kShared only: the item's table row, first q row, q rows, and first
-  // logical block (otherwise row s is read from block 0 with q_len q rows).
-  int row, qrow, ntok, b0;
+  // kShared only: the item's table row, first q row, q rows, first own
+  // chunk and shared cache blocks (otherwise row s is read from block 0
+  // with q_len q rows).
+  int row, qrow, ntok, b0, eb;
 };
 
 // Produces the workgroup's pieces in order. Every thread of the workgroup
@@ -205,13 +206,14 @@ struct Walker {
   int S, NG, cap;  // S: sequences, or items in kShared
   long long u, hi, seg_base;
   int s, hg, off, L, n;
-  int row, qrow, ntok, b0;
+  int row, qrow, ntok, b0, eb;
   bool first;
 };
 
 // The item's fields are uniform; readfirstlane keeps them in scalar
 // registers (the buffer ranges and table reads built from them must be).
 __device__ __forceinline__ void take_item(Walker &wk, const ShareItem &x) {
+  wk.eb = __builtin_amdgcn_readfirstlane(x.eb);
   wk.L = __builtin_amdgcn_readfirstlane(x.L);
   wk.n = __builtin_amdgcn_readfirstlane(x.n);
   wk.row = __builtin_amdgcn_readfirstlane(x.row);
@@ -228,6 +230,7 @@ __device__ __forceinline__ bool next_piece(Walker &wk, Piece &p) {
     p.qrow = wk.qrow;
     p.ntok = wk.ntok;
     p.b0 = wk.b0;
+    p.eb = wk.eb;
   }
   p.s = wk.s;
   p.hg = wk.hg;
@@ -568,6 +571,26 @@ __device__ __forceinline__ void issue_chunk(const int32_t *__restrict__ tables, 
   }
 }
 
+// kShared: starts the loads of the segment's chunk at cursor c of piece p.
+// The shared chunks come through the first member's table row, a member's
+// own chunks through its own row, except that with 8-token blocks a chunk
+// can begin with the group's last shared block (an odd count of shared
+// blocks): that block comes through the first member's row too.
+template <int NJ, int NT, int BS>
+__device__ __forceinline__ void issue_shared(const int32_t *__restrict__ tables, const DecodeArgs &a,
+                                             const Lane<NT> &ln, const Piece &p, const Cursor &c, size_t hoff,
+                                             int nrows, u32x4_t (&K)[NJ], u32x4_t (&V)[NJ]) {
+  if constexpr (BS < kBlock) {
+    const int na = nrows < BS ? nrows : BS;
+    const int nb = nrows - na;
+    const int ida = block_id(tables, a, ln.pool32, 2 * c.b < p.eb ? p.row : c.row, 2 * c.b);
+    const int idb = nb > 0 ? block_id(tables, a, ln.pool32, c.row, 2 * c.b + 1) : 0;
+    issue_pair<NJ>(a, ln, ida, idb, hoff, na, nb, K, V);
+  } else {
+    issue_chunk<NJ, NT, BS>(tables, a, ln, c.row, c.b, hoff, nrows, K, V);
+  }
+}
+
 // Token rows of chunk b (CH tokens) that lie before the context length n.
 template <int CH = kBlock>
 __device__ __forceinline__ int rows_in(int n, int b) {
@@ -758,8 +781,8 @@ __device__ __forceinline__ bool step(const int32_t *__restrict__ tables, const D
   Cursor cn;
   if constexpr (M == kShared) {
     cn = in_p ? seg_next(P, st.cc, st.lv_p) : (to_q ? seg_first(st.Q, st.lv_q) : st.cc);
-    issue<NJ>(a, ln, block_id(tables, a, ln.pool32, cn.row, cn.b), to_q ? st.hoff_q : st.hoff,
-              rows_in(cn.n, cn.b), Kn, Vn);
+    issue_shared<NJ, NT, BS>(tables, a, ln, to_q ? st.Q : P, cn, to_q ? st.hoff_q : st.hoff, rows_in(cn.n, cn.b),
+                             Kn, Vn);
   } else {
     const int next_s = to_q ? st.Q.s : P.s;
     const int next_b = in_p ? P.off + nx : (to_q ? st.Q.off : P.off + st.i);
@@ -1084,7 +1107,7 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
   }
   u32x4_t KA[NJ], VA[NJ], KB[NJ], VB[NJ];
   if constexpr (M == kShared) {
-    issue<NJ>(a, ln, block_id(tables, a, ln.pool32, st.cc.row, st.cc.b), st.hoff, rows_in(st.cc.n, st.cc.b), KA, VA);
+    issue_shared<NJ, NT, BS>(tables, a, ln, st.P, st.cc, st.hoff, rows_in(st.cc.n, st.cc.b), KA, VA);
   } else {
     issue_chunk<NJ, NT, BS>(tables, a, ln, st.P.s, st.P.off, st.hoff, rows_in<CH>(st.P.n, st.P.off), KA, VA);
   }
@@ -1248,7 +1271,8 @@ __global__ __launch_bounds__(kThreads) void share_plan_kernel(const SharePlanArg
   int *len = gs + NGr + 1;
   long long *csum = reinterpret_cast<long long *>(plan_lds + ((3 * S + 2 * NGr + 1 + 1) & ~1));
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int cap = p.max_blocks_per_seq * kBlock;
+  const int bs = p.block_size;
+  const int cap = p.max_blocks_per_seq * bs;
 
   // Every input into LDS first: their loads are independent, so the plan
   // waits for memory once.
@@ -1288,7 +1312,7 @@ __global__ __launch_bounds__(kThreads) void share_plan_kernel(const SharePlanArg
       grp[i] = -1;
       continue;
     }
-    atomicMin(&shb[g], len[i] / kBlock);  // LDS atomic
+    atomicMin(&shb[g], len[i] / bs);  // LDS atomic: shared cache blocks
   }
   __syncthreads();
 
@@ -1301,7 +1325,7 @@ __global__ __launch_bounds__(kThreads) void share_plan_kernel(const SharePlanArg
     if (i < S) {
       const int n = len[i];
       const int g = grp[i];
-      const int e = g >= 0 ? shb[g] : 0;
+      const int e = g >= 0 ? shb[g] * bs / kBlock : 0;  // shared chunks
       opens = (g < 0 || (i - gs[g]) % C == 0) ? 1 : 0;
       adds = (n + kBlock - 1) / kBlock - e + (opens ? e : 0);
     }
@@ -1325,13 +1349,15 @@ __global__ __launch_bounds__(kThreads) void share_plan_kernel(const SharePlanArg
     const int ntok = min(C, hi - i);
     const long long start = i > 0 ? csum[i - 1] : 0;
     const long long blocks = csum[i + ntok - 1] - start;
-    const int e = g >= 0 ? shb[g] : 0;
+    const int eb = g >= 0 ? shb[g] : 0;
+    const int e = eb * bs / kBlock;
     ShareItem x;
     x.row = lo;
     x.qrow = i;
     x.ntok = ntok;
     x.b0 = e;
     x.n = e * kBlock;
+    x.eb = eb;
     x.L = (int)blocks;
     x.ustart = NG * start;
     p.items[sid[i]] = x;
@@ -1342,7 +1368,7 @@ __global__ __launch_bounds__(kThreads) void share_plan_kernel(const SharePlanArg
   }
   if (tid == 0) {
     const long long units = NG * blocks_before;
-    ShareItem x = {0, 0, 0, 0, 0, 0, units};
+    ShareItem x = {0, 0, 0, 0, 0, 0, units, 0};
     p.items[segs_before] = x;  // sentinel: the end of the last segment
     ShareHeader h;
     h.units = units;
@@ -1421,7 +1447,8 @@ hipError_t launch_decode(const DecodeArgs &args, int32_t head_size, hipStream_t 
 
 hipError_t launch_decode_shared(const SharePlanArgs &plan, const DecodeArgs &args, int32_t head_size,
                                 hipStream_t stream) {
-  if (args.q_len != 1 || args.block_size != 16 || args.num_cols <= 16 || args.num_cols > 32 || !args.items || !args.share ||
+  if (args.q_len != 1 || (args.block_size != 8 && args.block_size != 16 && args.block_size != 32) ||
+      plan.block_size != args.block_size || args.num_cols <= 16 || args.num_cols > 32 || !args.items || !args.share ||
       plan.num_seqs < 1 || plan.num_seqs > kMaxSharedSeqs || plan.num_groups < 0 ||
       plan.num_groups > plan.num_seqs || plan.members_per_item < 1 || !plan.out || plan.row_elems % 8)
     return hipErrorInvalidValue;
@@ -1437,8 +1464,14 @@ hipError_t launch_decode_shared(const SharePlanArgs &plan, const DecodeArgs &arg
   if (e != hipSuccess) return e;
   // q of the current piece in LDS: one [num_cols][D] slot per wavefront.
   const size_t lds = (size_t)args.heads_per_wg * args.num_cols * head_size * sizeof(uint16_t);
-  e = head_size == 128 ? launch_decode_kernel<128, 2, kShared>(args, lds, stream)
-                       : launch_decode_kernel<64, 2, kShared>(args, lds, stream);
+  if (head_size == 128)
+    e = args.block_size == 8    ? launch_decode_kernel<128, 2, kShared, 8>(args, lds, stream)
+        : args.block_size == 32 ? launch_decode_kernel<128, 2, kShared, 32>(args, lds, stream)
+                                : launch_decode_kernel<128, 2, kShared>(args, lds, stream);
+  else
+    e = args.block_size == 8    ? launch_decode_kernel<64, 2, kShared, 8>(args, lds, stream)
+        : args.block_size == 32 ? launch_decode_kernel<64, 2, kShared, 32>(args, lds, stream)
+                                : launch_decode_kernel<64, 2, kShared>(args, lds, stream);
   if (e != hipSuccess || args.num_wgs <= 1) return e;
   const dim3 mgrid((unsigned)args.num_wgs);
   const dim3 mblock(64 * (unsigned)args.heads_per_wg);

@@ -115,6 +115,12 @@ int check_q_len(const pa_kv_cache *c, int32_t num_q_heads, int32_t q_len) {
   return PA_OK;
 }
 
+// The decode kernel works in chunks of 16 tokens: a table row of
+// max_blocks_per_seq blocks holds at most this many.
+int32_t chunks_per_row(const pa_kv_cache *c, int32_t max_blocks_per_seq) {
+  return (int32_t)(((int64_t)max_blocks_per_seq * c->block_size + 15) / 16);
+}
+
 // Sharing-aware decode: an item serves up to 32 / group sequences (its
 // columns are their query heads of one KV head: at most two MFMA tiles).
 int32_t members_per_item(int32_t group) { return 32 / group; }
@@ -133,8 +139,8 @@ SharedLayout layout_shared(const pa_kv_cache *c, int32_t num_seqs, int32_t num_q
   const int32_t group = num_q_heads / c->num_kv_heads;
   l.plan.heads_per_wg = heads_per_workgroup(c->num_kv_heads);
   l.plan.num_head_groups = c->num_kv_heads / l.plan.heads_per_wg;
-  // A segment holds at most max_blocks_per_seq blocks per member.
-  l.plan.num_wgs = decode_wgs(num_seqs, l.plan.num_head_groups, l.plan.heads_per_wg, max_blocks_per_seq);
+  // A segment holds at most a table row's chunks per member.
+  l.plan.num_wgs = decode_wgs(num_seqs, l.plan.num_head_groups, l.plan.heads_per_wg, chunks_per_row(c, max_blocks_per_seq));
   l.cols = members_per_item(group) * group;
   const size_t rows = 2 * (size_t)l.plan.num_wgs * l.plan.heads_per_wg * l.cols;
   l.items_off = 256;  // ShareHeader
@@ -145,14 +151,7 @@ SharedLayout layout_shared(const pa_kv_cache *c, int32_t num_seqs, int32_t num_q
   return l;
 }
 
-// The decode kernel works in chunks of 16 tokens: a table row of
-// max_blocks_per_seq blocks holds at most this many.
-int32_t chunks_per_row(const pa_kv_cache *c, int32_t max_blocks_per_seq) {
-  return (int32_t)(((int64_t)max_blocks_per_seq * c->block_size + 15) / 16);
-}
-
 int check_shared(const pa_kv_cache *c, int32_t num_seqs, int32_t num_groups) {
-  if (c->block_size != 16) return fail(PA_ERR_UNSUPPORTED, "pa_decode_shared needs block_size 16");
   if (num_seqs > pa::kMaxSharedSeqs)
     return fail(PA_ERR_UNSUPPORTED, "pa_decode_shared takes at most 4096 sequences");
   if (num_groups < 0 || num_groups > num_seqs) return fail(PA_ERR_SHAPE, "num_groups must be in 0..num_seqs");
@@ -359,6 +358,7 @@ int pa_decode_shared(const pa_kv_cache *cache, const void *q, const int32_t *blo
   p.members_per_item = members_per_item(a.group);
   p.group = a.group;
   p.num_head_groups = a.num_head_groups;
+  p.block_size = cache->block_size;
 
   hipError_t e = pa::launch_decode_shared(p, a, cache->head_size, hs);
   if (owned) {

@@ -17,10 +17,11 @@ struct ShareItem {
   int32_t row;     // table row of the shared blocks (the group's first member)
   int32_t qrow;    // first member: q and output rows qrow .. qrow + ntok - 1
   int32_t ntok;    // members
-  int32_t b0;      // shared blocks
+  int32_t b0;      // shared 16-token chunks
   int32_t n;       // b0 * 16
-  int32_t L;       // blocks in all: b0 + the members' own blocks
-  int64_t ustart;  // first unit: head groups times the blocks of all earlier segments
+  int32_t L;       // chunks in all: b0 + the members' own chunks
+  int64_t ustart;  // first unit: head groups times the chunks of all earlier segments
+  int32_t eb;      // shared cache blocks (b0 = eb * block_size / 16, rounded down)
 };
 
 // Written by the plan kernel: totals of the call.
@@ -74,6 +75,7 @@ struct SharePlanArgs {
   int32_t members_per_item;      // 32 / group
   int32_t group;
   int32_t num_head_groups;
+  int32_t block_size;            // tokens per cache block: 8, 16 or 32
 };
 
 // How a decode call is split and what scratch it needs (host only).

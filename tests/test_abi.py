@@ -145,19 +145,22 @@ def test_decode_shared_limits(L):
 
 
 def test_block_sizes(L):
-    """8-, 16- and 32-token blocks for single- and multi-token decode and
-    the cache ops; sharing-aware decode needs 16. The kernels work in
-    16-token chunks, so a table row of 4096 tokens gives the same workspace
-    at every block size."""
-    sizes = set()
+    """8-, 16- and 32-token blocks for single-token, multi-token and
+    sharing-aware decode and the cache ops. The kernels work in 16-token
+    chunks, so a table row of 4096 tokens gives the same workspace at every
+    block size; other block sizes are refused."""
+    sizes, shared = set(), set()
     for bs in (8, 16, 32):
         d = desc(block_size=bs)
         assert L.pa_decode_workspace_bytes(ctypes.byref(d), 256, 32, 4096 // bs) > 0
         sizes.add(L.pa_decode_multi_workspace_bytes(ctypes.byref(d), 256, 4, 32, 4096 // bs))
-        assert (L.pa_decode_shared_workspace_bytes(ctypes.byref(d), 256, 32, 4096 // bs, 64) > 0) == (bs == 16)
+        shared.add(L.pa_decode_shared_workspace_bytes(ctypes.byref(d), 256, 32, 4096 // bs, 64))
     assert len(sizes) == 1 and sizes.pop() > 0
-    d8 = desc(block_size=8)
-    assert L.pa_decode_shared(ctypes.byref(d8), P, P, P, 4, 32, 16, P, P, 1, 1.0, P, None, 0, None) == \
+    assert len(shared) == 1 and shared.pop() > 0
+    for bs in (4, 24, 64):
+        assert L.pa_decode_workspace_bytes(ctypes.byref(desc(block_size=bs)), 256, 32, 64) == 0
+    d24 = desc(block_size=24)
+    assert L.pa_decode_shared(ctypes.byref(d24), P, P, P, 4, 32, 16, P, P, 1, 1.0, P, None, 0, None) == \
         _lib.PA_ERR_UNSUPPORTED
     # the kernels address a block with 32-bit offsets: blocks over 1 GiB are refused
     assert decode(L, desc(block_size=32, num_kv_heads=8192 * 32, head_size=128), hq=8192 * 32) == _lib.PA_ERR_SHAPE

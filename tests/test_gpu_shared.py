@@ -133,3 +133,29 @@ def test_shared_beam_search_full_size():
         # the declaration is true, so the oracle's plain decode is the reference
         ref = oracle.decode(b.q[idx], kc, vc, b.block_tables[idx], b.context_lens[idx], b.scale)
         assert_attention_close(out[idx], ref, f"beam shared step {step}")
+
+
+@pytest.mark.parametrize("bs", [8, 32])
+@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (8, 8, 64), (16, 1, 128)])
+def test_shared_block_sizes(bs, hq, hkv, d, monkeypatch):
+    """Sharing-aware decode with 8- and 32-token blocks across work splits.
+    Prompt lengths give odd and even counts of shared 8-token blocks (with
+    an odd count a 16-token chunk begins with the last shared block and ends
+    in a member's own block), partial last blocks and none; false and
+    clamped declarations read the first member's blocks, as the oracle does."""
+    rng = np.random.default_rng(900 + bs + hq + d)
+    sizes, plens = [4, 9, 1, 3, 5], [24, 100, 8, 40, 64]
+    privs = rng.integers(0, 50, size=int(sum(sizes)), endpoint=True)
+    privs[::5] = 0
+    nb = sum((p + bs - 1) // bs for p in plens) + int(sum((x + bs) // bs for x in privs)) + 9
+    b, starts, shared = W.make_shared_batch("shared", 900 + bs + hq + d, sizes, plens, privs, hq, hkv, d, nb,
+                                            block_size=bs)
+    assert b.block_size == bs and np.all(shared >= np.array(plens) // bs)
+    for wgs in ("1", "3", "default"):
+        if wgs == "default":
+            monkeypatch.delenv("PA_DECODE_WGS", raising=False)
+        else:
+            monkeypatch.setenv("PA_DECODE_WGS", wgs)
+        check_shared(b, starts, shared, f"shared bs={bs} hq={hq} hkv={hkv} d={d} wgs={wgs}")
+    check_shared(b, starts, shared + 3, f"shared bs={bs} declared +3 (false, clamped)")
+    check_shared(b, starts, np.array([1, -1, 100, 3, 0]), f"shared bs={bs} declared 1/-1/100/3/0")
