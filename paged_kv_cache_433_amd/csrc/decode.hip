@@ -281,6 +281,8 @@ struct Lane {
   size_t blk_stride;     // elements per block of one cache array
   int row_bytes;         // bytes per token row of one cache array (all KV heads)
   uint32_t lane_off;     // byte offset of the lane's 16 bytes in (block, head): token c, dims 8*grp..
+  uint32_t lane_off_b;   // 8-token blocks: the same in the chunk's second block (rows 8-15), or 2 GiB
+                         // (past any block's range) for rows 0-7
   long long U, E;
   uint32_t pool32;       // min(num_blocks, INT32_MAX)
   u32x2_t sel;
@@ -514,14 +516,14 @@ __device__ __forceinline__ void issue(const DecodeArgs &a, const Lane<NT> &ln, i
 
 // Two 8-token blocks as one chunk: rows 0-7 of the tile from block `ida`
 // (its first `na` rows), rows 8-15 from block `idb` (its first `nb`). Each
-// row is loaded from both blocks' resources at the lane's offset and at that
-// offset less 8 rows; for every lane one of the two is outside its range
-// (the second one is negative, so wraps past any range) and reads as zero,
-// so OR-ing them gives the row without a per-lane choice of resource.
+// lane loads from both blocks' resources: at its offset in the first block
+// (past that block's range for rows 8-15) and at lane_off_b in the second
+// (its row less 8, or 2 GiB for rows 0-7, past any range). The load outside
+// its range reads as zero, so OR-ing the two gives the row without a
+// per-lane choice of resource.
 template <int NJ, int NT>
 __device__ __forceinline__ void issue_pair(const DecodeArgs &a, const Lane<NT> &ln, int ida, int idb, size_t hoff,
                                            int na, int nb, u32x4_t (&K)[NJ], u32x4_t (&V)[NJ]) {
-  constexpr int kHalf = kBlock / 2;
   const size_t base_a = ((size_t)ida * ln.blk_stride + hoff) * sizeof(uint16_t);
   const size_t base_b = ((size_t)idb * ln.blk_stride + hoff) * sizeof(uint16_t);
   const char *kc = reinterpret_cast<const char *>(a.k_cache), *vc = reinterpret_cast<const char *>(a.v_cache);
@@ -533,7 +535,7 @@ __device__ __forceinline__ void issue_pair(const DecodeArgs &a, const Lane<NT> &
       __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(vc + base_a), 0, na * ln.row_bytes, kRawBufferWord3);
   const __amdgpu_buffer_rsrc_t rvb =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(vc + base_b), 0, nb * ln.row_bytes, kRawBufferWord3);
-  const uint32_t off_b = ln.lane_off - (uint32_t)(kHalf * ln.row_bytes);
+  const uint32_t off_b = ln.lane_off_b;
 #pragma unroll
   for (int j = 0; j < NJ / 2; ++j)
     K[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rka, ln.lane_off + 64 * j, 0, kNonTemporal)) |
@@ -1061,6 +1063,7 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
   ln.blk_stride = (size_t)a.num_kv_heads * D * BS;
   ln.row_bytes = a.num_kv_heads * D * (int)sizeof(uint16_t);
   ln.lane_off = (uint32_t)(((size_t)ln.c * a.num_kv_heads * D + ln.grp * 8) * sizeof(uint16_t));
+  ln.lane_off_b = ln.c >= kBlock / 2 ? ln.lane_off - (uint32_t)(kBlock / 2 * ln.row_bytes) : 0x80000000u;
   ln.U = U;
   ln.E = E;
   ln.pool32 = (uint32_t)(a.num_blocks < 0x7fffffffLL ? a.num_blocks : 0x7fffffffLL);
