@@ -57,6 +57,10 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <map>
+#include <mutex>
+#include <utility>
+
 #include "pa_internal.h"
 
 namespace pa {
@@ -1382,11 +1386,25 @@ __global__ __launch_bounds__(kThreads) void share_plan_kernel(const SharePlanArg
 
 // Lets a kernel use more than 64 KiB of dynamic LDS (gfx950 has 160 KiB per
 // compute unit).
+// Raises a kernel's dynamic LDS limit when a launch needs more than 48 KiB.
+// The largest limit set so far is remembered per (device, kernel), so a
+// repeated launch makes no runtime call besides the launch itself (which
+// keeps it capturable in a graph once an eager call has run).
 template <typename Kernel>
 hipError_t allow_lds(Kernel kernel, size_t bytes) {
   if (bytes <= 48 * 1024) return hipSuccess;
-  return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                             (int)bytes);
+  static std::mutex mu;
+  static std::map<std::pair<int, const void *>, size_t> allowed;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const auto key = std::make_pair(dev, reinterpret_cast<const void *>(kernel));
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = allowed.find(key);
+  if (it != allowed.end() && it->second >= bytes) return hipSuccess;
+  e = hipFuncSetAttribute(key.second, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) allowed[key] = bytes;
+  return e;
 }
 
 template <int D, int NT, int M, int BS = 16>

@@ -1,0 +1,78 @@
+"""A decode step (slot scatter, then paged decode and its merge) captured in
+a HIP graph and replayed: every replay gives the eager call's output bit for
+bit, with eager work and synchronisation between replays. The library's
+calls enqueue only kernels when the caller brings the workspace (no
+allocation, no memset), which is what makes them capturable."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import DevBatch, assert_attention_close, bits_of, note, oracle_step
+from oracle_pins import small_batch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("hq,hkv,d,q_len", [(32, 8, 128, 1), (8, 8, 64, 1), (16, 4, 128, 3)])
+def test_graph_replay_matches_eager(hq, hkv, d, q_len):
+    import paged_kv_cache_433_amd as pa
+    from paged_kv_cache_433_amd import workloads as W
+
+    lens = [q_len, 17, 100, 513, 1000, 2049, 40]
+    if q_len == 1:
+        b = small_batch(950 + hq + d, lens, hq, hkv, d, spare=7)
+    else:
+        nb = int(sum((n + 15) // 16 for n in lens)) + 7
+        b = W.make_batch("graph", 950 + hq + d, lens, hq, hkv, d, nb, q_len=q_len)
+    db = DevBatch(b)
+    S, mb = b.num_seqs, b.block_tables.shape[1]
+    if q_len == 1:
+        ws_bytes = pa.decode_workspace_bytes(db.k_cache, S, hq, mb)
+    else:
+        ws_bytes = pa.decode_multi_workspace_bytes(db.k_cache, S, q_len, hq, mb)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=db.k_cache.device)
+    out = torch.empty_like(db.q)
+
+    def step():
+        db.scatter()
+        if q_len == 1:
+            pa.decode(db.q, db.k_cache, db.v_cache, db.block_tables, db.context_lens, float(b.scale),
+                      out=out, workspace=ws)
+        else:
+            pa.decode_multi(db.q, db.k_cache, db.v_cache, db.block_tables, db.context_lens, float(b.scale),
+                            out=out, workspace=ws)
+
+    note(f"graph eager hq={hq} hkv={hkv} d={d} q_len={q_len}")
+    step()
+    torch.cuda.synchronize()
+    eager = bits_of(out)
+    if q_len == 1:
+        assert_attention_close(eager, oracle_step(b)[2], "graph eager")
+    else:
+        hk, hv = b.k_cache.copy(), b.v_cache.copy()
+        oracle.reshape_and_cache(hk, hv, b.new_k, b.new_v, b.slot_mapping)
+        assert_attention_close(eager, oracle.decode_multi(b.q, hk, hv, b.block_tables, b.context_lens, b.scale),
+                               "graph eager multi")
+
+    note(f"graph capture hq={hq} hkv={hkv} d={d} q_len={q_len}")
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        step()  # warm up on the capture stream
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    scratch = torch.zeros(1 << 20, device=out.device)
+    for r in range(3):
+        out.zero_()                     # the replay must rewrite every output
+        scratch.add_(1.0)               # eager work between replays
+        torch.cuda.synchronize()
+        note(f"graph replay {r}")
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits_of(out), eager), f"replay {r} differs from the eager call"
