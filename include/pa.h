@@ -65,8 +65,8 @@ enum { PA_DTYPE_BF16 = 0 };
  * KV head, so a block's K plus V is 2*block_size*num_kv_heads*head_size*2
  * bytes, the per-block size the page gives.
  *
- * Supported: dtype PA_DTYPE_BF16; block_size 8, 16 or 32 (several new tokens
- * per sequence and sharing-aware decode need 16); head_size 64 or 128;
+ * Supported: dtype PA_DTYPE_BF16; block_size 8, 16 or 32 (every call);
+ * head_size 64 or 128;
  * num_blocks >= 1; num_kv_heads >= 1; one block of one array at most 1 GiB;
  * k_cache and v_cache 16-byte aligned. The descriptor is read on every call
  * and not kept.
