@@ -524,6 +524,14 @@ def main(argv=None) -> int:
         },
         "cpu_baseline": None,
     }
+    if args.config == "beam_cow":
+        # Copy-on-write pairs of the step, and the K/V bytes of the distinct
+        # blocks the step's tables use (every block read by the step, once).
+        used = np.unique(np.concatenate([b.block_tables[s, :(int(n) + b.block_size - 1) // b.block_size]
+                                         for s, n in enumerate(b.context_lens)]))
+        rec["config"]["cow_pairs"] = int(len(b.cow_pairs))
+        rec["config"]["distinct_blocks"] = int(len(used))
+        rec["config"]["distinct_block_kv_bytes"] = int(len(used)) * 2 * b.block_size * b.num_kv_heads * b.head_size * 2
     if not args.no_cpu_baseline:
         print(f"[bench] cpu baseline (~{2 * args.cpu_seconds:.0f} s)", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(b, args.cpu_seconds, (gstarts, gshared) if args.shared else None)
