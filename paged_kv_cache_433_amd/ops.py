@@ -201,8 +201,8 @@ def copy_blocks(k_cache, v_cache, src_dst_pairs) -> None:
 def swap_blocks(k_cache, v_cache, host_k, host_v, src_dst_pairs, direction: str) -> None:
     """Move whole blocks between the device cache and a host cache.
 
-    ``host_k``/``host_v``: pinned CPU bf16 tensors ``[host_blocks, 16,
-    num_kv_heads, head_size]``. ``src_dst_pairs``: int64 ``[P, 2]`` on the
+    ``host_k``/``host_v``: pinned CPU bf16 tensors ``[host_blocks, block_size,
+    num_kv_heads, head_size]`` (the device cache's block shape). ``src_dst_pairs``: int64 ``[P, 2]`` on the
     cache's device. ``direction`` "out": host block dst <- device block src;
     "in": device block dst <- host block src. Asynchronous on the current
     stream (synchronize before reading swapped-out blocks on the host).
