@@ -266,7 +266,7 @@ enum { PA_SWAP_OUT = 0, PA_SWAP_IN = 1 };
  * High-Throughput LLM Inference", section "Preemption and Recovery";
  * "vLLM Internals", section "The Block Manager").
  *
- *   host_k, host_v   bf16 [host_num_blocks, 16, num_kv_heads, head_size],
+ *   host_k, host_v   bf16 [host_num_blocks, block_size, num_kv_heads, head_size],
  *                    contiguous, in pinned host memory (hipHostMalloc, or
  *                    a pinned torch tensor); owned by the caller, who
  *                    guarantees host_num_blocks blocks of each. The library
