@@ -8,18 +8,20 @@ and 8 KV heads, head size 128, 16-token blocks, context lengths lognormal
 (median 1024, sigma 0.5, clipped to [16, 4096]), a shuffled pool of 65536
 blocks.
 
-Prints one JSON line. ``value`` is algorithmic bytes per step / time per
-step (GB/s). ``roofline`` covers the decode call (the decode kernel and the
-merge of cut pieces that follows it on the same stream): its algorithmic
-bytes / its mean time from HIP events around the call on the launch stream,
-against 8 TB/s; ``traffic`` is the call's HBM bytes from rocprofv3 counters
+Prints one JSON line. After ``--warmup`` untimed steps and at least 200 ms
+more of untimed steps, exactly ``--steps`` steps are timed: ``value`` is
+algorithmic bytes per step / time per step (GB/s). ``roofline`` covers the
+decode call (the decode kernel and the merge of cut pieces that follows it
+on the same stream), timed over at least 100 more steps and 200 ms with HIP
+events around the call on the launch stream: its algorithmic bytes / its
+mean time, against 8 TB/s, with the median, p10 and p90 beside the mean; ``traffic`` is the call's HBM bytes from rocprofv3 counters
 (profiles/decode_traffic.json) when they were taken on the current kernel;
 ``mean_launch_us_mall_evicted`` repeats the call with the 256 MB memory-side
 cache evicted before each launch (a 2 GiB read scan outside the events), and
 ``stream_read_same_bytes`` is a streaming read of as many contiguous bytes
 timed the same way (``frac_of_stream_read`` = achieved / that).
 ``cpu_baseline`` times the float64 oracle on a bounded sample of the same
-workload on this host.
+workload on this host, on one worker process per core and on one thread.
 
     python bench.py [--gpus 1] [--steps 500] [--warmup 20] [--config NAME]
 """
@@ -38,6 +40,12 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attention: achieved KV HBM GB/s (% of peak) and seq-steps/sec"
 PEAK_HBM_GBS = 8000.0
+# Timing protocol: an untimed warm-up of at least WARMUP_S seconds of steps
+# before anything is timed; the decode call's roofline time over at least
+# ROOF_MIN_LAUNCHES launches and ROOF_MIN_S seconds (mean, median, p10, p90).
+WARMUP_S = 0.2
+ROOF_MIN_LAUNCHES = 100
+ROOF_MIN_S = 0.2
 DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_433_amd", "csrc", "decode.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 CACHE_NOTES = {
@@ -130,35 +138,35 @@ def record_traffic(prefix: str, workload: str, copy_bytes: int) -> int:
     return 0
 
 
-def _time_oracle(batch, kc, vc, order, seconds: float, threads: int, groups=None):
-    """Run the oracle on whole sequences of `order` (cycling) for `seconds`
-    with BLAS limited to `threads`; returns (sequences done, seconds). With
-    `groups` = (group_starts, shared_blocks), `order` lists groups and each
-    is decoded whole by the oracle's decode_shared."""
+def _oracle_worker(task):
+    """One process of the CPU baseline: run the oracle on whole sequences
+    (whole groups, for sharing-aware decode) of its share of the seeded
+    order, cycling, for `seconds` with BLAS on one thread. The cache arrays
+    are memory-mapped read-only from files the parent wrote, so the workers
+    share one copy. Returns (units done, seconds)."""
     from threadpoolctl import threadpool_limits
+
+    import numpy as np
 
     import oracle
 
+    (paths, shape, q, tables, lens, scale, q_len, groups, order, seconds) = task
+    kc = np.memmap(paths[0], dtype=np.uint16, mode="r", shape=shape)
+    vc = np.memmap(paths[1], dtype=np.uint16, mode="r", shape=shape)
     done = []
-    with threadpool_limits(limits=threads):
+    with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         while time.perf_counter() - t0 < seconds:
             for s in order:
                 if groups is not None:
                     starts, shared = groups
                     lo, hi = int(starts[s]), int(starts[s + 1])
-                    oracle.decode_shared(batch.q[lo:hi], kc, vc, batch.block_tables[lo:hi],
-                                         batch.context_lens[lo:hi], [0, hi - lo], [shared[s]], batch.scale)
-                    done.append(int(s))
-                    if time.perf_counter() - t0 >= seconds:
-                        break
-                    continue
-                if batch.q_len > 1:
-                    oracle.decode_multi(batch.q[s:s + 1], kc, vc, batch.block_tables[s:s + 1],
-                                        batch.context_lens[s:s + 1], batch.scale)
+                    oracle.decode_shared(q[lo:hi], kc, vc, tables[lo:hi], lens[lo:hi], [0, hi - lo], [shared[s]],
+                                         scale)
+                elif q_len > 1:
+                    oracle.decode_multi(q[s:s + 1], kc, vc, tables[s:s + 1], lens[s:s + 1], scale)
                 else:
-                    oracle.decode_sequence(batch.q[s], kc, vc, batch.block_tables[s],
-                                           batch.context_lens[s], batch.scale)
+                    oracle.decode_sequence(q[s], kc, vc, tables[s], lens[s], scale)
                 done.append(int(s))
                 if time.perf_counter() - t0 >= seconds:
                     break
@@ -166,12 +174,39 @@ def _time_oracle(batch, kc, vc, order, seconds: float, threads: int, groups=None
     return done, dt
 
 
+def _time_oracle(batch, paths, order, seconds: float, procs: int, groups=None):
+    """The oracle on `procs` worker processes (each a slice of `order`), or
+    in this process when procs == 1; returns (units done, seconds)."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+
+    shape = batch.k_cache.shape
+    tasks = [(paths, shape, batch.q, batch.block_tables, batch.context_lens, batch.scale, batch.q_len, groups,
+              order[i::procs], seconds) for i in range(procs)]
+    if procs == 1:
+        res = [_oracle_worker(tasks[0])]
+    else:
+        # Fresh interpreters (spawn), not forks of this process: they never
+        # touch the GPU and hold no copy of its state.
+        ex = ProcessPoolExecutor(procs, mp_context=mp.get_context("spawn"))
+        try:
+            res = list(ex.map(_oracle_worker, tasks, timeout=seconds + 300))
+        finally:
+            ex.shutdown(wait=False, cancel_futures=True)
+    done = [s for r in res for s in r[0]]
+    return done, max(r[1] for r in res)
+
+
 def cpu_baseline(batch, seconds: float, groups=None):
     """Time the float64 oracle on whole sequences (whole groups, with
-    `groups`), in a seeded order (cycling through the batch), for `seconds`
-    with BLAS on every core this process may use and again on one thread;
-    rate in the metric's unit (algorithmic GB/s). The multi-core run is the
-    reported value."""
+    `groups`), in a seeded order (cycling through the batch), for `seconds`:
+    once on one worker process per core this process may use (the oracle is
+    serial numpy, so the host's cores work through separate sequences), and
+    once on a single thread; rate in the metric's unit (algorithmic GB/s).
+    The all-cores run is the reported value."""
+    import shutil
+    import tempfile
+
     import numpy as np
 
     import oracle
@@ -188,26 +223,33 @@ def cpu_baseline(batch, seconds: float, groups=None):
     cores = len(os.sched_getaffinity(0))
     if os.environ.get("OMP_NUM_THREADS", "").isdigit():
         cores = max(1, min(cores, int(os.environ["OMP_NUM_THREADS"])))
+    tmp = tempfile.mkdtemp(prefix="pa_oracle_", dir="/dev/shm" if os.path.isdir("/dev/shm") else None)
+    paths = (os.path.join(tmp, "k_cache"), os.path.join(tmp, "v_cache"))
     res = {}
-    for threads in (cores, 1):
-        done, dt = _time_oracle(batch, kc, vc, order, seconds, threads, groups)
-        if groups is None:
-            lens = batch.context_lens[done]
-            nbytes = W.algorithmic_bytes(lens, batch.num_q_heads, batch.num_kv_heads, batch.head_size,
-                                         q_len=batch.q_len)
-            seqs = len(done)
-        else:
-            starts, shared = groups
-            nbytes, seqs, toks = 0, 0, 0
-            for g in done:
-                lo, hi = int(starts[g]), int(starts[g + 1])
-                nbytes += W.shared_algorithmic_bytes(batch.context_lens[lo:hi], [0, hi - lo], [shared[g]],
-                                                     batch.max_blocks_per_seq, batch.num_q_heads,
-                                                     batch.num_kv_heads, batch.head_size)
-                seqs += hi - lo
-                toks += int(batch.context_lens[lo:hi].sum())
-            lens = np.array([toks])
-        res[threads] = (seqs, int(lens.sum()), dt, nbytes / dt / 1e9, seqs / dt)
+    try:
+        kc.tofile(paths[0])
+        vc.tofile(paths[1])
+        for procs in (cores, 1):
+            done, dt = _time_oracle(batch, paths, order, seconds, procs, groups)
+            if groups is None:
+                lens = batch.context_lens[done]
+                nbytes = W.algorithmic_bytes(lens, batch.num_q_heads, batch.num_kv_heads, batch.head_size,
+                                             q_len=batch.q_len)
+                seqs = len(done)
+            else:
+                starts, shared = groups
+                nbytes, seqs, toks = 0, 0, 0
+                for g in done:
+                    lo, hi = int(starts[g]), int(starts[g + 1])
+                    nbytes += W.shared_algorithmic_bytes(batch.context_lens[lo:hi], [0, hi - lo], [shared[g]],
+                                                         batch.max_blocks_per_seq, batch.num_q_heads,
+                                                         batch.num_kv_heads, batch.head_size)
+                    seqs += hi - lo
+                    toks += int(batch.context_lens[lo:hi].sum())
+                lens = np.array([toks])
+            res[procs] = (seqs, int(lens.sum()), dt, nbytes / dt / 1e9, seqs / dt)
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
     n, tokens, dt, gbps, sps = res[cores]
     return {
         "value": round(gbps, 4),
@@ -216,11 +258,11 @@ def cpu_baseline(batch, seconds: float, groups=None):
         "kind": "oracle",
         "sample": (f"{n} sequence-steps of the {batch.num_seqs}-sequence batch, taken in a seeded "
                    f"order{' of whole groups (decode_shared)' if groups is not None else ''} ({tokens} tokens), "
-                   f"float64 numpy oracle, BLAS limited to {cores} threads "
-                   f"(the gather and exp are single-threaded numpy), {dt:.1f} s"),
+                   f"float64 numpy oracle on {cores} worker processes (one per core, BLAS on one thread "
+                   f"each, cache arrays shared read-only), {dt:.1f} s"),
         "seq_steps_per_s": round(sps, 3),
         "single_thread": {"value": round(res[1][3], 4), "unit": "GB/s", "seq_steps_per_s": round(res[1][4], 3),
-                          "sample": f"{res[1][0]} sequence-steps, {res[1][2]:.1f} s"},
+                          "sample": f"{res[1][0]} sequence-steps on one thread, {res[1][2]:.1f} s"},
     }
 
 
@@ -400,37 +442,59 @@ def main(argv=None) -> int:
             pa.decode(q, kc, vc, tables, lens, scale, out=out)
 
     stream = torch.cuda.current_stream(dev)
-    n_ev = args.steps
-    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
-    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
 
-    def step(i=None):
+    def step(ev=None):
         if pairs is not None:
             pa.copy_blocks(kc, vc, pairs)
         pa.reshape_and_cache(new_k, new_v, kc, vc, slots)
-        if i is not None:
-            ev_a[i].record(stream)
+        if ev is not None:
+            ev[0].record(stream)
         run_decode()
-        if i is not None:
-            ev_b[i].record(stream)
+        if ev is not None:
+            ev[1].record(stream)
 
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    def events(n):
+        return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+
+    print(f"[bench] warmup {args.warmup} steps + at least {WARMUP_S * 1e3:.0f} ms", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # Untimed warm-up of at least WARMUP_S of steps, whatever --warmup says,
+    # so that clocks and caches have settled before any event is recorded.
+    t_warm = time.perf_counter()
+    while time.perf_counter() - t_warm < WARMUP_S:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+
+    # Exactly `steps` timed steps (the step time), with the decode call's
+    # own events inside each.
+    ev_steps = events(args.steps)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     start.record(stream)
     for i in range(args.steps):
-        step(i)
+        step(ev_steps[i])
     end.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms = total_ms / args.steps
-    dec_ms = [a.elapsed_time(z) for a, z in zip(ev_a, ev_b)]
-    dec_mean = float(np.mean(dec_ms))
-    print(f"[bench] {args.steps} steps: {ms * 1e3:.1f} us/step, decode {dec_mean * 1e3:.1f} us "
-          f"(p10 {np.percentile(dec_ms, 10) * 1e3:.1f}, p90 {np.percentile(dec_ms, 90) * 1e3:.1f})",
-          file=sys.stderr, flush=True)
+    step_dec_us = np.array([a.elapsed_time(z) for a, z in ev_steps]) * 1e3
+
+    # The decode call's time for the roofline: at least ROOF_MIN_LAUNCHES
+    # launches and ROOF_MIN_S of them, each inside a whole step as above.
+    n_roof = max(ROOF_MIN_LAUNCHES, args.steps, int(np.ceil(ROOF_MIN_S / (np.mean(step_dec_us) * 1e-6))))
+    ev_roof = events(n_roof)
+    for i in range(n_roof):
+        step(ev_roof[i])
+    torch.cuda.synchronize()
+    dec_us = np.array([a.elapsed_time(z) for a, z in ev_roof]) * 1e3
+    dec_mean_us = float(np.mean(dec_us))
+    dec_pct = {p: float(np.percentile(dec_us, p)) for p in (10, 50, 90)}
+    print(f"[bench] {args.steps} steps: {ms * 1e3:.1f} us/step (decode call {np.mean(step_dec_us):.1f} us); "
+          f"{n_roof} decode calls: mean {dec_mean_us:.1f} us, median {dec_pct[50]:.1f}, p10 {dec_pct[10]:.1f}, "
+          f"p90 {dec_pct[90]:.1f}", file=sys.stderr, flush=True)
 
     # The same decode call again with the 256 MB MALL (memory-side cache)
     # evicted before each launch by reading a 2 GiB buffer, outside the
@@ -466,7 +530,7 @@ def main(argv=None) -> int:
         del scratch, sink, span
 
     value = step_bytes / (ms * 1e-3) / 1e9
-    achieved = decode_bytes / (dec_mean * 1e-3) / 1e9
+    achieved = decode_bytes / (dec_mean_us * 1e-6) / 1e9
     traffic = measured_traffic(workload) if not multi else None
     if args.shared:
         kernel = "decode_shared call: share_plan_kernel + decode_kernel + merge_kernel"
@@ -516,7 +580,12 @@ def main(argv=None) -> int:
             "traffic": traffic,
             "algorithmic_bytes_per_launch": int(decode_bytes),
             "logical_bytes_per_launch": int(logical_bytes),
-            "mean_launch_us": round(dec_mean * 1e3, 2),
+            "mean_launch_us": round(dec_mean_us, 2),
+            "median_launch_us": round(dec_pct[50], 2),
+            "p10_launch_us": round(dec_pct[10], 2),
+            "p90_launch_us": round(dec_pct[90], 2),
+            "launches_timed": int(n_roof),
+            "timed_steps_mean_launch_us": round(float(np.mean(step_dec_us)), 2),
             "mean_launch_us_mall_evicted": round(cold_us, 2) if cold_us else None,
             "achieved_mall_evicted": round(decode_bytes / cold_us / 1e3, 2) if cold_us else None,
             "stream_read_same_bytes": round(stream_read_gbps, 1) if stream_read_gbps else None,

@@ -17,10 +17,10 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // One workgroup per new token. The token's K row and V row (num_kv_heads *
 // head_size elements each) go to physical slot slot_mapping[t]: offset
-// slot % 16 of block slot / 16 ("vLLM: Anatomy and Mechanisms of
+// slot % block_size of block slot / block_size ("vLLM: Anatomy and Mechanisms of
 // High-Throughput LLM Inference", section "Block-Level Management": a block
 // from the free pool receives the tokens of its logical block as they come).
-// In the [num_blocks, 16, Hkv, D] layout a slot's row is contiguous and
+// In the [num_blocks, block_size, Hkv, D] layout a slot's row is contiguous and
 // starts at element slot * row_elems.
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     const uint16_t *__restrict__ k, const uint16_t *__restrict__ v, const int64_t *__restrict__ slots,

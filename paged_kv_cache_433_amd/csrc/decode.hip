@@ -1,15 +1,17 @@
 // Paged decode attention for CDNA4 (gfx950).
 //
 // What is computed: for each sequence, one new query token per query head
-// attends over the sequence's cached K/V. The cache sits in 16-token physical
-// blocks that the sequence's block table maps from logical blocks ("vLLM:
+// attends over the sequence's cached K/V. The cache sits in physical blocks
+// of 8, 16 or 32 tokens that the sequence's block table maps from logical
+// blocks ("vLLM:
 // Anatomy and Mechanisms of High-Throughput LLM Inference", section
 // "Block-Level Management"; decode semantics from "Inside vLLM: Anatomy of a
 // High-Throughput LLM Inference System", section "Scheduler").
 //
 // Work split (balanced). KV heads form groups of HG heads (HG = largest
-// divisor of num_kv_heads that is <= 4). A "unit" is one physical block of
-// one sequence for one head group; a "segment" is all units of one
+// divisor of num_kv_heads that is <= 4). A "unit" is one 16-token chunk of
+// one sequence for one head group (a block with 16-token blocks, half a
+// 32-token block, two 8-token blocks); a "segment" is all units of one
 // (sequence, head group), in logical order. Segments are laid end to end in
 // (sequence, head group) order, and workgroup w takes units
 // [w*U/E, (w+1)*U/E) of the U in total, E = min(W, U) of the W workgroups
@@ -26,7 +28,7 @@
 // that holds its last unit records which pieces exist, and merge_kernel
 // combines them with log-sum-exp weights after the decode kernel.
 //
-// Inner loop, per block (16 tokens), on matrix cores:
+// Inner loop, per chunk (16 tokens), on matrix cores:
 //   * QK^T on v_mfma_f32_16x16x32_bf16: rows are the 16 tokens of the block,
 //     columns the 16 query-head slots, the reduction runs over head_size.
 //     Lane (c, grp) (c = lane % 16, grp = lane / 16) loads, for MFMA step j,
@@ -940,7 +942,8 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
   if constexpr (M == kShared) {
     // The plan kernel wrote the items and their first units; one parallel
     // search finds the item that holds `lo` (empty items never match).
-    const ShareHeader h = *a.share;
+    ShareHeader h = *a.share;
+    h.items = min(max(h.items, 0), S);  // the plan writes at most one segment per sequence
     U = h.units;
     E = U < W ? U : W;
     if (w >= E) {  // every workgroup writes its merge record, this one "none"
@@ -1150,6 +1153,12 @@ __global__ __launch_bounds__(256) void merge_kernel(const DecodeArgs a) {
   const int w1 = blockIdx.x;
   const int2 d = a.merge_desc[w1];
   if (d.x < 0) return;
+  // Every index below comes from the workspace. Each is checked before it
+  // is used, so a bookkeeping slip gives a wrong result, never an access
+  // outside the call's arrays: the segment must be one of the call's, and
+  // its first piece must belong to this workgroup or an earlier one.
+  const int nseg = kSegments ? min(max(a.share->items, 0), a.num_seqs) : a.num_seqs;
+  if (d.x >= nseg * a.num_head_groups || d.y < 0 || (d.y >> 1) > w1) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // KV head within the head group
   const int lane = threadIdx.x & 63;
   const int HG = a.heads_per_wg;
@@ -1160,6 +1169,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const DecodeArgs a) {
   int cols = a.num_cols;
   if constexpr (kSegments) {
     const ShareItem x = a.items[s];
+    if (x.qrow < 0 || x.ntok < 1 || x.ntok > a.num_seqs - x.qrow || x.ntok * a.group > a.num_cols) return;
     row0 = (size_t)x.qrow;
     cols = x.ntok * a.group;
   }
@@ -1236,8 +1246,9 @@ __global__ __launch_bounds__(256) void merge_kernel(const DecodeArgs a) {
 // "vLLM: Anatomy and Mechanisms", section "Memory Sharing via Copy-on-Write
 // (CoW)"; prompts with a common beginning reuse cached blocks: section
 // "Prefix Caching"). Those blocks are read once for up to 32 / group members
-// (their query heads become MFMA columns of one item), each member's private
-// blocks once for it alone; a finalize pass merges the two per sequence.
+// (their query heads become MFMA columns of one segment), then each member's
+// own blocks for it alone, in one stream: the softmax state runs across the
+// whole segment, so no extra pass combines the shared and the own parts.
 // ---------------------------------------------------------------------------
 
 // Inclusive max-scan over the workgroup (plan kernel only).

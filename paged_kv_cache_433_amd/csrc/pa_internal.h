@@ -34,7 +34,7 @@ struct ShareHeader {
 // Arguments of one decode launch, passed by value as the kernel argument.
 struct DecodeArgs {
   const uint16_t *q;             // bf16 [S, q_len, Hq, D]
-  const uint16_t *k_cache;       // bf16 [NB, 16, Hkv, D]
+  const uint16_t *k_cache;       // bf16 [NB, block_size, Hkv, D]
   const uint16_t *v_cache;
   const int32_t *block_tables;   // [S, MB]
   const int32_t *context_lens;   // [S]

@@ -1,0 +1,269 @@
+"""CPU model of the decode launches' bookkeeping: the balanced work split,
+the walk of each workgroup's range into pieces, the partial and merge
+records the decode kernel writes, the sharing-aware plan, and the records
+the merge kernel reads back.
+
+It models the HIP kernels' integer logic (csrc/decode.hip: the prologue,
+``next_piece``, ``finish_piece``, ``share_plan_kernel``, ``merge_kernel``)
+and the host-side sizes (csrc/pa_api.cpp: ``decode_wgs``,
+``heads_per_workgroup``), not attention: no arithmetic of the method is
+here. The tests use it to show, without a GPU, that every workgroup writes
+its merge record, that every record index the merge dereferences is in
+range and was written for the same segment by this call, and that every
+output row is written exactly once.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+CHUNK = 16  # tokens per unit of work (one MFMA tile of rows)
+
+
+def heads_per_workgroup(num_kv_heads: int) -> int:
+    for h in (4, 3, 2):
+        if num_kv_heads % h == 0:
+            return h
+    return 1
+
+
+def decode_wgs(num_seqs: int, num_head_groups: int, heads_per_wg: int, max_chunks_per_seq: int,
+               override: int | None = None) -> int:
+    w = 256 * max(4 // heads_per_wg, 1)
+    by_work = (num_seqs * num_head_groups * max_chunks_per_seq + 3) // 4
+    w = min(w, by_work)
+    if override is not None and override > 0:
+        w = override
+    return max(1, min(w, 1 << 20))
+
+
+def chunks_per_row(max_blocks_per_seq: int, block_size: int) -> int:
+    return (max_blocks_per_seq * block_size + CHUNK - 1) // CHUNK
+
+
+@dataclass
+class Segment:
+    """What a segment stands for: kernel-side (item or sequence, head group),
+    its unit count and the output rows it covers."""
+    key: tuple
+    L: int
+    rows: tuple  # output row keys the segment produces (one per (q row, KV head))
+
+
+@dataclass
+class Split:
+    W: int
+    U: int
+    E: int
+    desc: list = field(default_factory=list)      # per workgroup: (x, y) as the kernel writes it
+    records: dict = field(default_factory=dict)   # (w, slot) -> (segment key, offset, count)
+    written: dict = field(default_factory=dict)   # output row key -> times written
+    pieces: list = field(default_factory=list)    # per workgroup: [(key, off, cnt)]
+
+
+def range_lo(w: int, U: int, E: int) -> int:
+    return w * U // E
+
+
+def owner_of(u: int, U: int, E: int) -> int:
+    return ((u + 1) * E - 1) // U
+
+
+def walk(segments: list, NG: int, W: int) -> Split:
+    """The balanced split and the decode kernel's walk.
+
+    ``segments`` lists (key, L, rows) in kernel order, one entry per
+    sequence or item (head groups expand inside, head-group major). Returns
+    the records each workgroup writes, as decode_kernel does.
+    """
+    U = sum(seg.L for seg in segments) * NG
+    E = min(W, U)
+    sp = Split(W=W, U=U, E=E)
+    # unit -> (segment index, head group, offset)
+    starts, acc = [], 0
+    for seg in segments:
+        starts.append(acc)
+        acc += seg.L * NG
+    for w in range(W):
+        sp.pieces.append([])
+        if w >= E:
+            sp.desc.append((-1, -1))
+            continue
+        lo, hi = range_lo(w, U, E), range_lo(w + 1, U, E)
+        # the segment holding `lo`: the one whose units contain it (empty ones never do)
+        si = max(i for i, st in enumerate(starts) if st <= lo and segments[i].L > 0 and lo < st + segments[i].L * NG)
+        seg_base = starts[si]
+        L = segments[si].L
+        hg, off = (lo - seg_base) // L, (lo - seg_base) % L
+        u, first, desc = lo, True, (-1, -1)
+        while u < hi:
+            seg = segments[si]
+            cnt = min(seg.L - off, hi - u)
+            seg_start = seg_base + hg * seg.L
+            key = (seg.key, hg)
+            sp.pieces[w].append((key, off, cnt))
+            whole = off == 0 and cnt == seg.L
+            if whole:
+                for r in seg.rows:
+                    rk = (r, hg)
+                    sp.written[rk] = sp.written.get(rk, 0) + 1
+            else:
+                slot = 0 if first else 1
+                assert (w, slot) not in sp.records, f"workgroup {w} writes slot {slot} twice"
+                sp.records[(w, slot)] = (key, off, cnt)
+            if first:
+                if not whole and off + cnt == seg.L:
+                    w0 = owner_of(seg_start, U, E)
+                    slot0 = 1 if range_lo(w0, U, E) < seg_start else 0
+                    desc = (si * NG + hg, w0 * 2 + slot0)
+                first = False
+            u += cnt
+            off += cnt
+            if off == seg.L:
+                off = 0
+                hg += 1
+                if hg == NG and u < hi:
+                    hg = 0
+                    seg_base += seg.L * NG
+                    si += 1
+                    while segments[si].L == 0:
+                        si += 1
+        sp.desc.append(desc)
+    return sp
+
+
+def merge(sp: Split, segments: list, NG: int, S_items: int) -> None:
+    """The merge kernel's reads: checks every index before use the way the
+    kernel does, and that what it reads is this segment's pieces, in order,
+    covering the segment exactly."""
+    for w1, (x, y) in enumerate(sp.desc):
+        if x < 0:
+            continue
+        assert 0 <= x < S_items * NG, f"merge record of workgroup {w1}: segment {x} out of range"
+        assert 0 <= y and (y >> 1) <= w1, f"merge record of workgroup {w1}: first piece {y} out of range"
+        si, hg = divmod(x, NG)
+        seg = segments[si]
+        key = (seg.key, hg)
+        w0 = y >> 1
+        got = []
+        for w in range(w0, w1 + 1):
+            rec = (w0, y & 1) if w == w0 else (w, 0)
+            assert rec in sp.records, f"merge of workgroup {w1} reads record {rec}, never written"
+            k, off, cnt = sp.records[rec]
+            assert k == key, f"merge of workgroup {w1} reads record {rec} of another segment"
+            got.append((off, cnt))
+        pos = 0
+        for off, cnt in got:
+            assert off == pos, f"merge of workgroup {w1}: pieces not contiguous"
+            pos += cnt
+        assert pos == seg.L, f"merge of workgroup {w1}: pieces cover {pos} of {seg.L} units"
+        for r in seg.rows:
+            rk = (r, hg)
+            sp.written[rk] = sp.written.get(rk, 0) + 1
+
+
+def plain_segments(lens, cap: int) -> list:
+    """Sequences as segments (pa_decode, pa_decode_multi): clamped lengths."""
+    segs = []
+    for s, n in enumerate(lens):
+        n = min(max(int(n), 0), cap)
+        segs.append(Segment(key=s, L=(n + CHUNK - 1) // CHUNK, rows=(s,)))
+    return segs
+
+
+def check_plain(lens, num_q_heads, num_kv_heads, max_blocks_per_seq, block_size=16, override=None) -> Split:
+    hg = heads_per_workgroup(num_kv_heads)
+    NG = num_kv_heads // hg
+    cap = max_blocks_per_seq * block_size
+    W = decode_wgs(len(lens), NG, hg, chunks_per_row(max_blocks_per_seq, block_size), override)
+    segs = plain_segments(lens, cap)
+    sp = walk(segs, NG, W)
+    if W > 1:
+        merge(sp, segs, NG, len(lens))
+    # every sequence row: once per head group, or zeroed when empty
+    for s, seg in enumerate(segs):
+        for g in range(NG):
+            times = sp.written.get((s, g), 0)
+            want = 0 if seg.L == 0 else 1
+            assert times == want, f"output of sequence {s}, head group {g} written {times} times"
+    return sp
+
+
+def share_plan(lens, group_starts, shared_blocks, max_blocks_per_seq, block_size, members_per_item):
+    """share_plan_kernel: items (segments) of a sharing-aware call. Returns
+    (items, zeroed rows) with each item as a dict of its fields."""
+    S = len(lens)
+    cap = max_blocks_per_seq * block_size
+    n = [min(max(int(x), 0), cap) for x in lens]
+    gs = [int(x) for x in group_starts] if len(shared_blocks) else []
+    G = len(shared_blocks)
+    shb = [min(max(int(x), 0), max_blocks_per_seq) for x in shared_blocks]
+    valid = True
+    for g in range(G):
+        lo, hi = gs[g], gs[g + 1]
+        if lo > hi or (g == 0 and lo < 0) or (g == G - 1 and hi > S):
+            valid = False
+    grp = [-1] * S
+    if valid:
+        marks = [-1] * S
+        for g in range(G):
+            if gs[g + 1] > gs[g]:
+                marks[gs[g]] = g
+        run = -1
+        for i in range(S):
+            run = max(run, marks[i])
+            grp[i] = run
+    for i in range(S):
+        g = grp[i]
+        if g >= 0 and i >= gs[g + 1]:
+            grp[i] = -1
+    for i in range(S):
+        g = grp[i]
+        if g >= 0:
+            shb[g] = min(shb[g], n[i] // block_size)
+    items, zeroed, start = [], [], 0
+    csum, acc = [], 0
+    opens = []
+    for i in range(S):
+        g = grp[i]
+        e = shb[g] * block_size // CHUNK if g >= 0 else 0
+        op = g < 0 or (i - gs[g]) % members_per_item == 0
+        opens.append(op)
+        acc += (n[i] + CHUNK - 1) // CHUNK - e + (e if op else 0)
+        csum.append(acc)
+    for i in range(S):
+        if not opens[i]:
+            continue
+        g = grp[i]
+        hi = gs[g + 1] if g >= 0 else i + 1
+        ntok = min(members_per_item, hi - i)
+        start = csum[i - 1] if i > 0 else 0
+        blocks = csum[i + ntok - 1] - start
+        eb = shb[g] if g >= 0 else 0
+        items.append(dict(row=gs[g] if g >= 0 else i, qrow=i, ntok=ntok, b0=eb * block_size // CHUNK, L=blocks))
+        if blocks == 0:
+            zeroed.extend(range(i, i + ntok))
+    return items, zeroed
+
+
+def check_shared(lens, group_starts, shared_blocks, num_q_heads, num_kv_heads, max_blocks_per_seq,
+                 block_size=16, override=None) -> Split:
+    group = num_q_heads // num_kv_heads
+    C = 32 // group
+    hg = heads_per_workgroup(num_kv_heads)
+    NG = num_kv_heads // hg
+    W = decode_wgs(len(lens), NG, hg, chunks_per_row(max_blocks_per_seq, block_size), override)
+    items, zeroed = share_plan(lens, group_starts, shared_blocks, max_blocks_per_seq, block_size, C)
+    assert len(items) <= len(lens)
+    segs = [Segment(key=v, L=it["L"], rows=tuple(range(it["qrow"], it["qrow"] + it["ntok"])))
+            for v, it in enumerate(items)]
+    for it in items:
+        assert 0 <= it["qrow"] and it["qrow"] + it["ntok"] <= len(lens) and it["ntok"] * group <= 32
+    sp = walk(segs, NG, W)
+    if W > 1:
+        merge(sp, segs, NG, len(items))
+    for s in range(len(lens)):
+        for g in range(NG):
+            times = sp.written.get((s, g), 0) + (1 if s in zeroed else 0)
+            assert times == 1, f"output of sequence {s}, head group {g} written {times} times"
+    return sp
