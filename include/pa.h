@@ -20,7 +20,8 @@
  * Conventions shared by every call:
  *   - Every data pointer is a DEVICE pointer owned by the caller. The library
  *     never frees caller memory and keeps no state between calls, except a
- *     thread-local error string (pa_last_error).
+ *     thread-local error string (pa_last_error), per-device launch settings,
+ *     and the static scratch of pa_decode_noalloc.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the null
  *     stream). A return of PA_OK means the work was enqueued.
  *   - bfloat16 tensors are passed as raw 16-bit storage.
@@ -143,6 +144,31 @@ int pa_decode(const pa_kv_cache *cache, const void *q, const int32_t *block_tabl
  */
 size_t pa_decode_workspace_bytes(const pa_kv_cache *cache, int32_t num_seqs,
                                  int32_t num_q_heads, int32_t max_blocks_per_seq);
+
+/*
+ * pa_decode_noalloc - pa_decode for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation. Same arguments, computation, kernels and result (bit
+ * for bit) as pa_decode, without the workspace arguments: the partial
+ * results go to a static device array of the library (PA_NOALLOC_SCRATCH_BYTES,
+ * 16.5 MiB), which each GPU the library runs on holds until the process
+ * ends. The call allocates nothing: no hipMalloc, no hipMallocAsync, no
+ * free. The caller still owns q, block_tables, context_lens and out.
+ *
+ * The scratch is one array per GPU, shared by every call on that GPU: two
+ * calls on one GPU that overlap in time (different streams, unordered) race
+ * on it and their results are undefined. Order them (one stream, or events).
+ * It needs no initialisation: every call rewrites what it reads.
+ *
+ * Errors: those of pa_decode, and PA_ERR_WORKSPACE when the sizes need more
+ * scratch than the static array holds (pa_decode_workspace_bytes() >
+ * PA_NOALLOC_SCRATCH_BYTES; with the default work split no single-token
+ * call of a supported shape does).
+ */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)17301504)
+int pa_decode_noalloc(const pa_kv_cache *cache, const void *q, const int32_t *block_tables,
+                      const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                      int32_t max_blocks_per_seq, float scale, void *out, void *stream);
 
 /*
  * pa_decode_multi - attention of q_len new tokens per sequence over the paged

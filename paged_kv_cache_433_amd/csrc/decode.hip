@@ -1525,4 +1525,31 @@ hipError_t launch_decode_shared(const SharePlanArgs &plan, const DecodeArgs &arg
   return hipGetLastError();
 }
 
+// Scratch of the decode entry point that allocates nothing: a file-scope
+// device array. Every GPU the library runs on holds its own copy, at its own
+// address, until the process ends. Host code never passes the array's name
+// to a kernel (in host code it stands for a host-side shadow, not for device
+// memory): it asks the runtime for the device address once per device, with
+// that device current, and keeps it.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void **ptr) {
+  static std::mutex mu;
+  static std::map<int, void *> addr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = addr.find(dev);
+  if (it == addr.end()) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    it = addr.emplace(dev, p).first;
+  }
+  *ptr = it->second;
+  return hipSuccess;
+}
+
 }  // namespace pa

@@ -180,37 +180,16 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
 
 }  // namespace pa
 
-extern "C" {
+namespace {
 
-const char *pa_last_error(void) { return g_error.c_str(); }
-
-size_t pa_decode_workspace_bytes(const pa_kv_cache *cache, int32_t num_seqs, int32_t num_q_heads,
-                                 int32_t max_blocks_per_seq) {
-  return pa_decode_multi_workspace_bytes(cache, num_seqs, 1, num_q_heads, max_blocks_per_seq);
-}
-
-size_t pa_decode_multi_workspace_bytes(const pa_kv_cache *cache, int32_t num_seqs, int32_t q_len,
-                                       int32_t num_q_heads, int32_t max_blocks_per_seq) {
-  if (check_cache(cache, false) != PA_OK) return 0;
-  if (check_decode_shape(cache, num_seqs, num_q_heads, max_blocks_per_seq) != PA_OK) return 0;
-  if (check_q_len(cache, num_q_heads, q_len) != PA_OK) return 0;
-  return pa::plan_decode(num_seqs, num_q_heads, cache->num_kv_heads, cache->head_size,
-                         chunks_per_row(cache, max_blocks_per_seq), q_len)
-      .total_bytes;
-}
-
-int pa_decode(const pa_kv_cache *cache, const void *q, const int32_t *block_tables,
-              const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
-              int32_t max_blocks_per_seq, float scale, void *out, void *workspace,
-              size_t workspace_bytes, void *stream) {
-  return pa_decode_multi(cache, q, block_tables, context_lens, num_seqs, 1, num_q_heads, max_blocks_per_seq,
-                         scale, out, workspace, workspace_bytes, stream);
-}
-
-int pa_decode_multi(const pa_kv_cache *cache, const void *q, const int32_t *block_tables,
-                    const int32_t *context_lens, int32_t num_seqs, int32_t q_len, int32_t num_q_heads,
-                    int32_t max_blocks_per_seq, float scale, void *out, void *workspace,
-                    size_t workspace_bytes, void *stream) {
+// Checks, plans and launches a decode call. The partial records go to the
+// caller's workspace, to stream-ordered scratch allocated here when that is
+// NULL, or (static_scratch) to the library's static device scratch, with no
+// allocation at all.
+int decode_impl(const pa_kv_cache *cache, const void *q, const int32_t *block_tables,
+                const int32_t *context_lens, int32_t num_seqs, int32_t q_len, int32_t num_q_heads,
+                int32_t max_blocks_per_seq, float scale, void *out, void *workspace,
+                size_t workspace_bytes, void *stream, bool static_scratch) {
   int rc = check_cache(cache, num_seqs > 0);
   if (rc != PA_OK) return rc;
   rc = check_decode_shape(cache, num_seqs, num_q_heads, max_blocks_per_seq);
@@ -228,11 +207,20 @@ int pa_decode_multi(const pa_kv_cache *cache, const void *q, const int32_t *bloc
     return fail(PA_ERR_WORKSPACE, "workspace smaller than pa_decode_workspace_bytes()");
   if (workspace && reinterpret_cast<uintptr_t>(workspace) % 16)
     return fail(PA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  if (static_scratch && plan.total_bytes > pa::kNoAllocScratchBytes)
+    return fail(PA_ERR_WORKSPACE, "this call needs " + std::to_string(plan.total_bytes) +
+                                      " bytes of scratch, more than the library's static " +
+                                      std::to_string(pa::kNoAllocScratchBytes) + "-byte scratch");
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
   void *ws = workspace;
   bool owned = false;
-  if (plan.total_bytes && !ws) {
+  if (static_scratch) {
+    if (plan.total_bytes) {
+      hipError_t e = pa::noalloc_scratch(&ws);
+      if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    }
+  } else if (plan.total_bytes && !ws) {
     hipError_t e = hipMallocAsync(&ws, plan.total_bytes, hs);
     if (e != hipSuccess) return hip_fail(e, "hipMallocAsync(workspace)");
     owned = true;
@@ -272,6 +260,50 @@ int pa_decode_multi(const pa_kv_cache *cache, const void *q, const int32_t *bloc
   }
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *pa_last_error(void) { return g_error.c_str(); }
+
+size_t pa_decode_workspace_bytes(const pa_kv_cache *cache, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t max_blocks_per_seq) {
+  return pa_decode_multi_workspace_bytes(cache, num_seqs, 1, num_q_heads, max_blocks_per_seq);
+}
+
+size_t pa_decode_multi_workspace_bytes(const pa_kv_cache *cache, int32_t num_seqs, int32_t q_len,
+                                       int32_t num_q_heads, int32_t max_blocks_per_seq) {
+  if (check_cache(cache, false) != PA_OK) return 0;
+  if (check_decode_shape(cache, num_seqs, num_q_heads, max_blocks_per_seq) != PA_OK) return 0;
+  if (check_q_len(cache, num_q_heads, q_len) != PA_OK) return 0;
+  return pa::plan_decode(num_seqs, num_q_heads, cache->num_kv_heads, cache->head_size,
+                         chunks_per_row(cache, max_blocks_per_seq), q_len)
+      .total_bytes;
+}
+
+int pa_decode(const pa_kv_cache *cache, const void *q, const int32_t *block_tables,
+              const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+              int32_t max_blocks_per_seq, float scale, void *out, void *workspace,
+              size_t workspace_bytes, void *stream) {
+  return pa_decode_multi(cache, q, block_tables, context_lens, num_seqs, 1, num_q_heads, max_blocks_per_seq,
+                         scale, out, workspace, workspace_bytes, stream);
+}
+
+int pa_decode_multi(const pa_kv_cache *cache, const void *q, const int32_t *block_tables,
+                    const int32_t *context_lens, int32_t num_seqs, int32_t q_len, int32_t num_q_heads,
+                    int32_t max_blocks_per_seq, float scale, void *out, void *workspace,
+                    size_t workspace_bytes, void *stream) {
+  return decode_impl(cache, q, block_tables, context_lens, num_seqs, q_len, num_q_heads, max_blocks_per_seq, scale,
+                     out, workspace, workspace_bytes, stream, false);
+}
+
+int pa_decode_noalloc(const pa_kv_cache *cache, const void *q, const int32_t *block_tables,
+                      const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                      int32_t max_blocks_per_seq, float scale, void *out, void *stream) {
+  return decode_impl(cache, q, block_tables, context_lens, num_seqs, 1, num_q_heads, max_blocks_per_seq, scale,
+                     out, nullptr, 0, stream, true);
 }
 
 size_t pa_decode_shared_workspace_bytes(const pa_kv_cache *cache, int32_t num_seqs, int32_t num_q_heads,

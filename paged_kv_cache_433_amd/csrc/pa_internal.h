@@ -3,6 +3,8 @@
 #pragma once
 
 #include <hip/hip_runtime_api.h>
+
+#include "../../include/pa.h"
 #include <stddef.h>
 #include <stdint.h>
 
@@ -93,6 +95,18 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
                        int32_t head_size, int32_t max_chunks_per_seq, int32_t q_len);
 
 hipError_t launch_decode(const DecodeArgs &args, int32_t head_size, hipStream_t stream);
+
+// Bytes of the static device scratch of pa_decode_noalloc. It covers every
+// single-token decode the default split can produce: at most 1024
+// workgroups x KV heads per workgroup, 16 columns each, head size 128, two
+// partial records per (workgroup, head, column): merge records 8 KiB,
+// max/sum 256 KiB, outputs 16 MiB.
+constexpr size_t kNoAllocScratchBytes = ((size_t)16 << 20) + ((size_t)512 << 10);
+static_assert(kNoAllocScratchBytes == PA_NOALLOC_SCRATCH_BYTES, "the header states the scratch size");
+
+// Device address of that scratch on the current device (looked up once per
+// device and kept).
+hipError_t noalloc_scratch(void **ptr);
 
 // Largest batch the sharing-aware plan kernel takes (it keeps per-sequence
 // and per-group state in LDS).

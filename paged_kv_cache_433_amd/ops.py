@@ -115,6 +115,24 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=None, wor
     return out
 
 
+def decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, scale, out):
+    """``decode`` through the entry point that allocates nothing
+    (``pa_decode_noalloc``): the partial results go to the library's static
+    device scratch, so ``out`` must be given. Calls on one GPU that overlap
+    in time race on that scratch; keep them on one stream."""
+    desc = _cache_desc(k_cache, v_cache)
+    dev = k_cache.device
+    S, hq, d = q.shape
+    _need(q, "q", _BF16, (S, hq, k_cache.shape[3]), dev)
+    mb = block_tables.shape[1] if block_tables.dim() == 2 else -1
+    _need(block_tables, "block_tables", torch.int32, (S, mb), dev)
+    _need(context_lens, "context_lens", torch.int32, (S,), dev)
+    _need(out, "out", _BF16, (S, hq, d), dev)
+    _check(_lib.lib().pa_decode_noalloc(ctypes.byref(desc), _ptr(q), _ptr(block_tables), _ptr(context_lens), S,
+                                        hq, mb, float(scale), _ptr(out), _stream(dev)))
+    return out
+
+
 def decode_multi(q, k_cache, v_cache, block_tables, context_lens, scale, out=None, workspace=None):
     """Causal attention of several new tokens per sequence; returns ``out``.
 

@@ -218,3 +218,23 @@ def test_misaligned_pointers_are_refused(L):
     assert L.pa_copy_blocks(ctypes.byref(desc(k_cache=0x1008)), P, 2, None) == _lib.PA_ERR_UNSUPPORTED
     # sizes alone need no data pointers, aligned or not
     assert L.pa_decode_workspace_bytes(ctypes.byref(desc(k_cache=0x1002)), 256, 32, 256) > 0
+
+
+def test_noalloc_argument_errors(L, monkeypatch):
+    """pa_decode_noalloc checks what pa_decode checks, and refuses sizes past
+    its static scratch, all on the host."""
+    def call(d, S=2, hq=32, mb=8, q=P, out=P):
+        return L.pa_decode_noalloc(ctypes.byref(d) if d is not None else None, q, P, P, S, hq, mb, 1.0, out, None)
+
+    assert call(None) == _lib.PA_ERR_NULL
+    assert call(desc(), q=None) == _lib.PA_ERR_NULL
+    assert call(desc(dtype=1)) == _lib.PA_ERR_UNSUPPORTED
+    assert call(desc(), hq=12) == _lib.PA_ERR_SHAPE
+    assert call(desc(), out=ctypes.c_void_p(0x3008)) == _lib.PA_ERR_UNSUPPORTED
+    assert call(desc(), S=0) == _lib.PA_OK
+    monkeypatch.setenv("PA_DECODE_WGS", "20000")
+    d = desc()
+    need = L.pa_decode_workspace_bytes(ctypes.byref(d), 64, 32, 256)
+    assert need > _lib.PA_NOALLOC_SCRATCH_BYTES
+    assert call(d, S=64, mb=256) == _lib.PA_ERR_WORKSPACE
+    assert "static" in _lib.last_error()
