@@ -40,6 +40,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attention: achieved KV HBM GB/s (% of peak) and seq-steps/sec"
 PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0  # dense bf16 matrix-core peak
 # Timing protocol: an untimed warm-up of at least WARMUP_S seconds of steps
 # before anything is timed; the decode call's roofline time over at least
 # ROOF_MIN_LAUNCHES launches and ROOF_MIN_S seconds (mean, median, p10, p90).
@@ -531,6 +532,11 @@ def main(argv=None) -> int:
 
     value = step_bytes / (ms * 1e-3) / 1e9
     achieved = decode_bytes / (dec_mean_us * 1e-6) / 1e9
+    # Which peak binds the call: the time its bytes need at peak HBM
+    # bandwidth against the time its flops need at the bf16 matrix-core peak.
+    flops = W.algorithmic_flops(b.context_lens, b.num_q_heads, b.head_size, q_len=args.q_len)
+    achieved_tflops = flops / (dec_mean_us * 1e-6) / 1e12
+    mfma_bound = flops / (PEAK_BF16_TFLOPS * 1e12) > decode_bytes / (PEAK_HBM_GBS * 1e9)
     traffic = measured_traffic(workload) if not multi else None
     if args.shared:
         kernel = "decode_shared call: share_plan_kernel + decode_kernel + merge_kernel"
@@ -572,11 +578,16 @@ def main(argv=None) -> int:
         "bytes_per_step": int(step_bytes),
         "roofline": {
             "kernel": kernel,
-            "bound": "hbm",
-            "achieved": round(achieved, 2),
-            "peak": PEAK_HBM_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "bound": "mfma" if mfma_bound else "hbm",
+            "achieved": round(achieved_tflops, 2) if mfma_bound else round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS if mfma_bound else PEAK_HBM_GBS,
+            "unit": "TFLOP/s" if mfma_bound else "GB/s",
+            "frac": round((achieved_tflops / PEAK_BF16_TFLOPS) if mfma_bound else (achieved / PEAK_HBM_GBS), 4),
+            "hbm_achieved_GBps": round(achieved, 2),
+            "hbm_frac": round(achieved / PEAK_HBM_GBS, 4),
+            "flops_per_launch": int(flops),
+            "mfma_achieved_TFLOPs": round(achieved_tflops, 2),
+            "mfma_frac": round(achieved_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
             "algorithmic_bytes_per_launch": int(decode_bytes),
             "logical_bytes_per_launch": int(logical_bytes),

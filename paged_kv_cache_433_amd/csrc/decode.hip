@@ -86,9 +86,15 @@ constexpr int chunk_of() { return kBlock; }
 constexpr uint32_t kBf16One = 0x3F80u;
 
 // What a decode launch computes: one new token per sequence (kSingle);
-// several, each with its own causal limit (kCausal); or a list of items,
-// each read once for the one or more sequences it serves (kShared).
-constexpr int kSingle = 0, kCausal = 1, kShared = 2;
+// several, each with its own causal limit (kCausal); the same with more than
+// 32 (new token, query head) columns per KV head (kWide: a workgroup's
+// wavefronts are the column groups of one KV head, 32 columns each); or a
+// list of items, each read once for the one or more sequences it serves
+// (kShared).
+constexpr int kSingle = 0, kCausal = 1, kShared = 2, kWide = 3;
+
+// Several new tokens per sequence, each with its own causal limit.
+constexpr bool causal(int M) { return M == kCausal || M == kWide; }
 
 __device__ __forceinline__ f32x4_t mfma32(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -279,6 +285,7 @@ struct Lane {
   int HG, NG;
   bool col_ok[NT];       // the lane's column of tile t exists (column < q_len * group)
   int col[NT];           // that column, or the last one when it does not exist
+  int lcol[NT];          // the same counted within the wavefront's column group (kWide; else = col)
   int qshift[NT];        // q_len - 1 - new token of the column: its causal limit is n - qshift
   int tok[NT];           // the column's new token (kShared: its member of the segment)
   uint32_t q_off[NT];    // byte offset of the lane's 16 bytes of its column's q row (in the
@@ -293,6 +300,13 @@ struct Lane {
   uint32_t pool32;       // min(num_blocks, INT32_MAX)
   u32x2_t sel;
 };
+
+// The KV head a wavefront serves in head group hg: one head per wavefront,
+// or (kWide) the group's one head for every wavefront.
+template <int M, int NT>
+__device__ __forceinline__ int kv_head(const Lane<NT> &ln, int hg) {
+  return M == kWide ? hg : hg * ln.HG + ln.wave;
+}
 
 // kShared: where a block of a segment comes from. A segment is one or more
 // members of a group: first the group's shared blocks (read through the
@@ -370,7 +384,7 @@ __device__ __forceinline__ void load_q(const DecodeArgs &a, const Lane<NT> &ln, 
   // (columns past them read as zeros and are never stored).
   const size_t row0 = M == kShared ? (size_t)p.qrow : (size_t)p.s * a.q_len;
   const int rows = M == kShared ? p.ntok : a.q_len;
-  const size_t base = (row0 * a.num_q_heads + (size_t)(p.hg * ln.HG + ln.wave) * a.group) * D * sizeof(uint16_t);
+  const size_t base = (row0 * a.num_q_heads + (size_t)kv_head<M>(ln, p.hg) * a.group) * D * sizeof(uint16_t);
   const int span = ((rows - 1) * a.num_q_heads + a.group) * D * (int)sizeof(uint16_t);
   const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<char *>(reinterpret_cast<const char *>(a.q) + base), 0, span, kRawBufferWord3);
@@ -407,10 +421,11 @@ __device__ __forceinline__ int stage_slots(const DecodeArgs &a) {
   return n < kStageSlots ? n : kStageSlots;
 }
 
-// The one slot per wavefront that holds the current piece's q (two tiles).
+// The one slot per wavefront that holds the current piece's q (two tiles):
+// [rec_cols][D], the wavefront's own columns.
 template <int NJ>
 __device__ __forceinline__ uint16_t *q_park(uint16_t *lds, const DecodeArgs &a, int wave) {
-  return lds + (size_t)wave * a.num_cols * (NJ * 32);
+  return lds + (size_t)wave * a.rec_cols * (NJ * 32);
 }
 
 // With two column tiles the current piece's q lives in LDS (one slot per
@@ -426,13 +441,13 @@ __device__ __forceinline__ void park_q(uint16_t *slot, const Lane<NT> &ln, const
   for (int t = 0; t < NT; ++t)
     if (ln.col_ok[t]) {
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) *reinterpret_cast<u32x4_t *>(qs + ln.col[t] * (NJ * 32) + 32 * j) = qv[t][j];
+      for (int j = 0; j < NJ; ++j) *reinterpret_cast<u32x4_t *>(qs + ln.lcol[t] * (NJ * 32) + 32 * j) = qv[t][j];
     }
 }
 
 template <int NJ, int NT>
 __device__ __forceinline__ void parked_q(const uint16_t *slot, const Lane<NT> &ln, int t, u32x4_t (&qv)[NJ]) {
-  const uint16_t *qs = slot + ln.col[t] * (NJ * 32) + ln.grp * 8;
+  const uint16_t *qs = slot + ln.lcol[t] * (NJ * 32) + ln.grp * 8;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) qv[j] = *reinterpret_cast<const u32x4_t *>(qs + 32 * j);
 }
@@ -487,9 +502,9 @@ __device__ __forceinline__ Cursor seg_next(const Piece &p, const Cursor &c, int 
 }
 
 // Element offset of the wavefront's KV head inside a token row (uniform).
-template <int NJ, int NT>
+template <int NJ, int M, int NT>
 __device__ __forceinline__ size_t head_off(const Lane<NT> &ln, const Piece &p) {
-  return (size_t)(p.hg * ln.HG + ln.wave) * (NJ * 32);
+  return (size_t)kv_head<M>(ln, p.hg) * (NJ * 32);
 }
 
 // Starts the loads of one block's K and V rows for this wavefront's head.
@@ -620,7 +635,7 @@ template <int NJ, int NT>
 __device__ __forceinline__ void store_record(const DecodeArgs &a, const Lane<NT> &ln, int t, int slot,
                                              const f32x4_t (&acc)[2 * NJ], float m, float l) {
   constexpr int D = NJ * 32;
-  const size_t row = (((size_t)ln.w * 2 + slot) * ln.HG + ln.wave) * a.num_cols + ln.col[t];
+  const size_t row = (((size_t)ln.w * 2 + slot) * ln.HG + ln.wave) * a.rec_cols + ln.lcol[t];
   float *po = a.part_o + row * D + ln.grp * 8;
 #pragma unroll
   for (int k = 0; k < 2 * NJ; ++k) *reinterpret_cast<f32x4_t *>(po + 32 * (k >> 1) + 4 * (k & 1)) = acc[k];
@@ -646,10 +661,10 @@ template <int NJ, int NT, int M, bool DF>
 __device__ __forceinline__ void finish_piece(const DecodeArgs &a, const Lane<NT> &ln, Stream<NJ, NT> &st,
                                              uint16_t *lds) {
   constexpr int D = NJ * 32;
-  constexpr bool kMulti = M == kCausal;
+  constexpr bool kMulti = causal(M);
   const Piece &P = st.P;
   const bool whole = P.off == 0 && P.cnt == P.L;
-  const int g = P.hg * ln.HG + ln.wave;
+  const int g = kv_head<M>(ln, P.hg);
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     float l = st.l_part[t] + __shfl_xor(st.l_part[t], 16);
@@ -764,7 +779,7 @@ __device__ __forceinline__ void advance(const DecodeArgs &a, const Lane<NT> &ln,
   }
   st.has_q = next_piece<M, CH>(wk, st.Q);
   if (!st.has_q) st.Q = st.P;
-  st.hoff_q = head_off<NJ>(ln, st.Q);
+  st.hoff_q = head_off<NJ, M>(ln, st.Q);
   if constexpr (M == kShared) {
     st.lv_p = st.lv_q;
     st.lv_q = member_lens(wk.lens, st.Q, wk.cap, ln.lane);
@@ -778,7 +793,7 @@ template <int NJ, int NT, int M, int BS>
 __device__ __forceinline__ bool step(const int32_t *__restrict__ tables, const DecodeArgs &a, const Lane<NT> &ln,
                                      Walker &wk, Stream<NJ, NT> &st, u32x4_t (&K)[NJ], u32x4_t (&V)[NJ],
                                      u32x4_t (&Kn)[NJ], u32x4_t (&Vn)[NJ], uint16_t *lds) {
-  constexpr bool kMulti = M == kCausal;
+  constexpr bool kMulti = causal(M);
   constexpr int CH = chunk_of<BS>();
   const Piece &P = st.P;
   // In P's first step, q of the next piece is loaded (before this step's K/V
@@ -911,17 +926,19 @@ __device__ __forceinline__ void no_merge(const DecodeArgs &a, int w, int tid) {
   if (tid == 0 && a.merge_desc) a.merge_desc[w] = int2{-1, -1};
 }
 
-// NT: 16-column MFMA tiles per KV head (columns = q_len * group, or the
-// item width in kShared). M: kSingle, kCausal or kShared. The launch puts
-// one wavefront on each SIMD; with two tiles the wavefront may take the
-// whole register file (arch and accumulation registers).
+// NT: 16-column MFMA tiles per wavefront (columns = q_len * group, or the
+// item width in kShared, or 32 per column group in kWide). M: kSingle,
+// kCausal, kWide or kShared. The narrow launches put one wavefront on each
+// SIMD; with two tiles the wavefront may take the whole register file (arch
+// and accumulation registers). kWide runs two wavefronts per SIMD (a
+// workgroup of up to 8 column groups of one KV head), 256 registers each.
 template <int D, int NT, int M, int BS>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2 : 1)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NT == 1 || M == kWide ? 2 : 1)))
 void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const int32_t *__restrict__ lens,
                    const ShareItem *__restrict__ items) {
   constexpr int NJ = D / 32;  // MFMA steps over head_size; 16-byte loads per lane per row
   static_assert(NJ >= 1 && D % 32 == 0, "head_size must be a multiple of 32");
-  extern __shared__ __align__(16) uint16_t q_lds[];  // heads_per_wg * (NT == 1 ? 2 : 1) * num_cols * D
+  extern __shared__ __align__(16) uint16_t q_lds[];  // heads_per_wg * (NT == 1 ? 2 : 1) * rec_cols * D
   __shared__ long long red[8];
   __shared__ int found_seq, found_n;
   __shared__ long long found_prefix;
@@ -1065,11 +1082,14 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
   ln.w = w;
   ln.HG = a.heads_per_wg;
   ln.NG = NG;
+  // kWide: wavefront w holds columns 32*w .. 32*w + 31 of its KV head.
+  const int col0 = M == kWide ? 32 * wave : 0;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    const int col = 16 * t + ln.c;
+    const int col = col0 + 16 * t + ln.c;
     ln.col_ok[t] = col < a.num_cols;
     ln.col[t] = ln.col_ok[t] ? col : a.num_cols - 1;
+    ln.lcol[t] = ln.col[t] - col0;
     const int tok = ln.col[t] / a.group;
     const int qh = ln.col[t] - tok * a.group;
     ln.qshift[t] = a.q_len - 1 - tok;
@@ -1104,10 +1124,10 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
     load_q<NJ, NT, M>(a, ln, st.P, qv);
     park_q<NJ>(q_park<NJ>(q_lds, a, wave), ln, qv);
   }
-  st.hoff = head_off<NJ>(ln, st.P);
+  st.hoff = head_off<NJ, M>(ln, st.P);
   st.has_q = next_piece<M, CH>(wk, st.Q);
   if (!st.has_q) st.Q = st.P;
-  st.hoff_q = head_off<NJ>(ln, st.Q);
+  st.hoff_q = head_off<NJ, M>(ln, st.Q);
   if constexpr (M == kShared) {
     st.lv_p = member_lens(lens, st.P, cap, lane);
     st.lv_q = member_lens(lens, st.Q, cap, lane);
@@ -1138,15 +1158,15 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
 }
 
 // Log-sum-exp merge of the pieces of segments cut by workgroup boundaries.
-// Grid: one block per decode workgroup w, one wavefront per KV head of a
-// head group. Block w merges the segment that workgroup w's first piece
+// Grid: one block per decode workgroup w, one wavefront per wavefront of the
+// decode workgroup (a KV head of a head group, or a column group). Block w merges the segment that workgroup w's first piece
 // ended, if any (the others exit at once). Lanes take 8 head dims of a column
 // each (D/8 lanes per column) and two columns per pass, 64 / (D/8) columns
 // apart. The pieces are slot d.y & 1 of workgroup d.y >> 1, then the first
 // slot of every workgroup up to w; the records of four pieces of both columns
 // are loaded together, then folded in with a running rescale.
 template <int D, bool kSegments>
-__global__ __launch_bounds__(256) void merge_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(512) void merge_kernel(const DecodeArgs a) {
   constexpr int LPC = D / 8;     // lanes per column
   constexpr int CPP = 64 / LPC;  // columns per half pass
   constexpr int kPieces = 4;
@@ -1163,10 +1183,15 @@ __global__ __launch_bounds__(256) void merge_kernel(const DecodeArgs a) {
   const int lane = threadIdx.x & 63;
   const int HG = a.heads_per_wg;
   const int s = d.x / a.num_head_groups;
-  const int g = (d.x - s * a.num_head_groups) * HG + wave;
+  // The wavefront's KV head and column group: one head per wavefront, or
+  // (more than 32 columns) the head group's one head with the wavefront's
+  // 32 columns.
+  const int vh = (d.x - s * a.num_head_groups) * HG + wave;
+  const int g = vh / a.col_groups;
+  const int col0 = (vh - g * a.col_groups) * a.rec_cols;
   // Output rows: the sequence's q_len rows, or a segment's members (kSegments).
   size_t row0 = (size_t)s * a.q_len;
-  int cols = a.num_cols;
+  int cols = min(a.rec_cols, a.num_cols - col0);
   if constexpr (kSegments) {
     const ShareItem x = a.items[s];
     if (x.qrow < 0 || x.ntok < 1 || x.ntok > a.num_seqs - x.qrow || x.ntok * a.group > a.num_cols) return;
@@ -1195,7 +1220,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const DecodeArgs a) {
           pl[u][k] = 0.f;
           po[u][k][0] = po[u][k][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
           if (w + k <= w1 && c < cols) {
-            const size_t r = (rec * HG + wave) * a.num_cols + c;
+            const size_t r = (rec * HG + wave) * a.rec_cols + c;
             const f32x2_t ml = *reinterpret_cast<const f32x2_t *>(pml + r * 2);
             pm[u][k] = ml[0];
             pl[u][k] = ml[1];
@@ -1232,7 +1257,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const DecodeArgs a) {
       const int c = c0 + u * CPP + sub;
       if (c >= cols) continue;
       const float inv = Ls[u] > 0.f ? 1.f / Ls[u] : 0.f;
-      const int tok = c / a.group, qh = c - tok * a.group;
+      const int tok = (col0 + c) / a.group, qh = col0 + c - tok * a.group;
       const f32x4_t x = o[u][0] * inv, y = o[u][1] * inv;
       const u32x4_t v = {to_bf16x2(x[0], x[1]), to_bf16x2(x[2], x[3]), to_bf16x2(y[0], y[1]), to_bf16x2(y[2], y[3])};
       *reinterpret_cast<u32x4_t *>(a.out + ((row0 + tok) * a.num_q_heads + (size_t)g * a.group + qh) * D + dd) = v;
@@ -1450,20 +1475,32 @@ hipError_t launch_decode_d(const DecodeArgs &args, size_t lds, hipStream_t strea
     if (args.block_size == 32) return launch_decode_kernel<D, 1, kCausal, 32>(args, lds, stream);
     return launch_decode_kernel<D, 1, kCausal>(args, lds, stream);
   }
-  if (args.block_size == 8) return launch_decode_kernel<D, 2, kCausal, 8>(args, lds, stream);
-  if (args.block_size == 32) return launch_decode_kernel<D, 2, kCausal, 32>(args, lds, stream);
-  return launch_decode_kernel<D, 2, kCausal>(args, lds, stream);
+  if (args.num_cols <= 32) {
+    if (args.block_size == 8) return launch_decode_kernel<D, 2, kCausal, 8>(args, lds, stream);
+    if (args.block_size == 32) return launch_decode_kernel<D, 2, kCausal, 32>(args, lds, stream);
+    return launch_decode_kernel<D, 2, kCausal>(args, lds, stream);
+  }
+  if (args.block_size == 8) return launch_decode_kernel<D, 2, kWide, 8>(args, lds, stream);
+  if (args.block_size == 32) return launch_decode_kernel<D, 2, kWide, 32>(args, lds, stream);
+  return launch_decode_kernel<D, 2, kWide>(args, lds, stream);
 }
 
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs &args, int32_t head_size, hipStream_t stream) {
-  if (args.q_len < 1 || args.num_cols > 32 || (args.q_len == 1 && args.num_cols > 16)) return hipErrorInvalidValue;
+  const bool wide = args.num_cols > 32;
+  if (args.q_len < 1 || args.num_cols > kMaxDecodeCols || (args.q_len == 1 && args.num_cols > 16)) return hipErrorInvalidValue;
+  // Columns per wavefront: all of them, or (wide) 32 per column group with
+  // one wavefront per column group of the head group's one KV head.
+  if (wide ? (args.rec_cols != 32 || args.col_groups != (args.num_cols + 31) / 32 ||
+              args.heads_per_wg != args.col_groups || args.num_head_groups != args.num_kv_heads)
+           : (args.rec_cols != args.num_cols || args.col_groups != 1))
+    return hipErrorInvalidValue;
   if (args.block_size != 8 && args.block_size != 16 && args.block_size != 32) return hipErrorInvalidValue;
   // LDS holds q: a two-slot ring per wavefront for the next piece (one column
   // tile), or the current piece's (two tiles).
   // With one column tile, each wavefront also has an output staging area.
-  const size_t lds = (size_t)args.heads_per_wg * (args.num_cols <= 16 ? 2 : 1) * args.num_cols * head_size *
+  const size_t lds = (size_t)args.heads_per_wg * (args.num_cols <= 16 ? 2 : 1) * args.rec_cols * head_size *
                          sizeof(uint16_t) +
                      (args.num_cols <= 16 && args.block_size != 8
                           ? (size_t)args.heads_per_wg * (kStageBytes + kStageSlots * sizeof(size_t))

@@ -39,12 +39,16 @@ int hip_fail(hipError_t e, const char *what) {
 // a workgroup fewer than 4 units. The count depends on the sizes only (not on
 // the device or the data), so workspace sizes are a host function and
 // results are reproducible. PA_DECODE_WGS overrides it (tests, tuning).
+// Launches with more than 32 columns per KV head (a workgroup per head group
+// of column groups) are heavier on the matrix cores and run two wavefronts
+// per SIMD, 8 per compute unit.
 constexpr int64_t kTargetCUs = 256;
 constexpr int64_t kWavesPerCU = 4;
+constexpr int64_t kWideWavesPerCU = 8;
 
 int32_t decode_wgs(int64_t num_seqs, int32_t num_head_groups, int32_t heads_per_wg,
-                   int32_t max_chunks_per_seq) {
-  int64_t w = kTargetCUs * (kWavesPerCU / heads_per_wg > 0 ? kWavesPerCU / heads_per_wg : 1);
+                   int32_t max_chunks_per_seq, int64_t waves_per_cu = kWavesPerCU) {
+  int64_t w = kTargetCUs * (waves_per_cu / heads_per_wg > 0 ? waves_per_cu / heads_per_wg : 1);
   const int64_t units_bound = num_seqs * num_head_groups * (int64_t)max_chunks_per_seq;
   const int64_t by_work = (units_bound + 3) / 4;
   if (by_work < w) w = by_work;
@@ -107,11 +111,11 @@ int check_decode_shape(const pa_kv_cache *c, int32_t num_seqs, int32_t num_q_hea
 }
 
 // Several new tokens per sequence: their (token, query head) pairs of one KV
-// head must fit two 16-column MFMA tiles.
+// head are the columns of the launch, at most 8 column groups of 32.
 int check_q_len(const pa_kv_cache *c, int32_t num_q_heads, int32_t q_len) {
   if (q_len < 1) return fail(PA_ERR_SHAPE, "q_len must be >= 1");
-  if ((int64_t)q_len * (num_q_heads / c->num_kv_heads) > 32)
-    return fail(PA_ERR_UNSUPPORTED, "q_len * (num_q_heads / num_kv_heads) must be <= 32");
+  if ((int64_t)q_len * (num_q_heads / c->num_kv_heads) > pa::kMaxDecodeCols)
+    return fail(PA_ERR_UNSUPPORTED, "q_len * (num_q_heads / num_kv_heads) must be <= 256");
   return PA_OK;
 }
 
@@ -139,9 +143,11 @@ SharedLayout layout_shared(const pa_kv_cache *c, int32_t num_seqs, int32_t num_q
   const int32_t group = num_q_heads / c->num_kv_heads;
   l.plan.heads_per_wg = heads_per_workgroup(c->num_kv_heads);
   l.plan.num_head_groups = c->num_kv_heads / l.plan.heads_per_wg;
+  l.plan.col_groups = 1;
   // A segment holds at most a table row's chunks per member.
   l.plan.num_wgs = decode_wgs(num_seqs, l.plan.num_head_groups, l.plan.heads_per_wg, chunks_per_row(c, max_blocks_per_seq));
   l.cols = members_per_item(group) * group;
+  l.plan.rec_cols = l.cols;
   const size_t rows = 2 * (size_t)l.plan.num_wgs * l.plan.heads_per_wg * l.cols;
   l.items_off = 256;  // ShareHeader
   l.desc_off = l.items_off + round_up(((size_t)num_seqs + 1) * sizeof(pa::ShareItem), 256);
@@ -165,12 +171,23 @@ namespace pa {
 DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                        int32_t head_size, int32_t max_chunks_per_seq, int32_t q_len) {
   DecodePlan p{};
-  p.heads_per_wg = heads_per_workgroup(num_kv_heads);
-  p.num_head_groups = num_kv_heads / p.heads_per_wg;
-  p.num_wgs = decode_wgs(num_seqs, p.num_head_groups, p.heads_per_wg, max_chunks_per_seq);
+  const int32_t cols = q_len * (num_q_heads / num_kv_heads);
+  if (cols > 32) {
+    // One workgroup per KV head of a piece, one wavefront per 32 columns.
+    p.col_groups = (cols + 31) / 32;
+    p.rec_cols = 32;
+    p.heads_per_wg = p.col_groups;
+    p.num_head_groups = num_kv_heads;
+    p.num_wgs = decode_wgs(num_seqs, p.num_head_groups, p.heads_per_wg, max_chunks_per_seq, kWideWavesPerCU);
+  } else {
+    p.col_groups = 1;
+    p.rec_cols = cols;
+    p.heads_per_wg = heads_per_workgroup(num_kv_heads);
+    p.num_head_groups = num_kv_heads / p.heads_per_wg;
+    p.num_wgs = decode_wgs(num_seqs, p.num_head_groups, p.heads_per_wg, max_chunks_per_seq);
+  }
   if (p.num_wgs <= 1) return p;
-  const size_t cols = (size_t)q_len * (num_q_heads / num_kv_heads);
-  const size_t rows = (size_t)p.num_wgs * 2 * p.heads_per_wg * cols;
+  const size_t rows = (size_t)p.num_wgs * 2 * p.heads_per_wg * p.rec_cols;
   p.desc_bytes = round_up((size_t)p.num_wgs * sizeof(int2), 256);
   p.ml_bytes = round_up(rows * 2 * sizeof(float), 256);
   p.o_bytes = round_up(rows * head_size * sizeof(float), 256);
@@ -250,6 +267,8 @@ int decode_impl(const pa_kv_cache *cache, const void *q, const int32_t *block_ta
   a.block_size = cache->block_size;
   a.heads_per_wg = plan.heads_per_wg;
   a.num_head_groups = plan.num_head_groups;
+  a.col_groups = plan.col_groups;
+  a.rec_cols = plan.rec_cols;
   a.num_wgs = plan.num_wgs;
   a.scale_log2 = scale * 1.44269504088896340736f;
 
@@ -371,6 +390,8 @@ int pa_decode_shared(const pa_kv_cache *cache, const void *q, const int32_t *blo
   a.block_size = cache->block_size;
   a.heads_per_wg = l.plan.heads_per_wg;
   a.num_head_groups = l.plan.num_head_groups;
+  a.col_groups = 1;
+  a.rec_cols = l.cols;
   a.num_wgs = l.plan.num_wgs;
   a.scale_log2 = scale * 1.44269504088896340736f;
   a.items = items;

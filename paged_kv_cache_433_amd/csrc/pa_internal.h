@@ -42,18 +42,20 @@ struct DecodeArgs {
   const int32_t *context_lens;   // [S]
   uint16_t *out;                 // bf16 [S, q_len, Hq, D]
   int2 *merge_desc;              // [num_wgs]: segment ended by the workgroup's first piece, or -1
-  float *part_ml;                // [2 * num_wgs, heads_per_wg, num_cols, 2]: max (base 2), sum
-  float *part_o;                 // [2 * num_wgs, heads_per_wg, num_cols, D]: unnormalised output
+  float *part_ml;                // [2 * num_wgs, heads_per_wg, rec_cols, 2]: max (base 2), sum
+  float *part_o;                 // [2 * num_wgs, heads_per_wg, rec_cols, D]: unnormalised output
   int64_t num_blocks;
   int32_t num_seqs;
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t group;                 // Hq / Hkv, <= 16
   int32_t q_len;                 // new tokens per sequence (1: decode)
-  int32_t num_cols;              // q_len * group, <= 32 (<= 16 when q_len == 1)
+  int32_t num_cols;              // q_len * group, <= kMaxDecodeCols (<= 16 when q_len == 1)
+  int32_t col_groups;            // 1, or ceil(num_cols / 32) when num_cols > 32
+  int32_t rec_cols;              // columns per wavefront: num_cols, or 32 when num_cols > 32
   int32_t max_blocks_per_seq;
-  int32_t heads_per_wg;          // KV heads per workgroup (one wavefront each), <= 4
-  int32_t num_head_groups;       // Hkv / heads_per_wg
+  int32_t heads_per_wg;          // wavefronts per workgroup: KV heads (<= 4), or column groups (<= 8)
+  int32_t num_head_groups;       // Hkv / heads_per_wg, or Hkv with column groups
   int32_t num_wgs;               // workgroups sharing the units evenly
   float scale_log2;              // softmax scale times log2(e)
   // Sharing-aware decode only (null otherwise).
@@ -80,10 +82,16 @@ struct SharePlanArgs {
   int32_t block_size;            // tokens per cache block: 8, 16 or 32
 };
 
+// Most (new token, query head) columns per KV head a decode launch takes:
+// 8 column groups of 32, one wavefront each.
+constexpr int32_t kMaxDecodeCols = 256;
+
 // How a decode call is split and what scratch it needs (host only).
 struct DecodePlan {
-  int32_t heads_per_wg;
+  int32_t heads_per_wg;          // wavefronts per workgroup
   int32_t num_head_groups;
+  int32_t col_groups;
+  int32_t rec_cols;
   int32_t num_wgs;
   size_t desc_bytes;             // offset of part_ml
   size_t ml_bytes;

@@ -473,6 +473,17 @@ def algorithmic_bytes(context_lens, num_q_heads, num_kv_heads, head_size,
     return kv + qo + tables + 4 * len(n)
 
 
+def algorithmic_flops(context_lens, num_q_heads, head_size, q_len=1) -> int:
+    """Floating-point operations a step's attention must do: for every new
+    token j of a sequence of n cached tokens, every query head, and every
+    position it sees (n - q_len + j + 1 of them), a dot product with the key
+    and a scaled add of the value, 2 * head_size flops each."""
+    n = np.asarray(context_lens, dtype=np.int64)
+    live = n > 0
+    seen = q_len * n[live] - q_len * (q_len - 1) // 2  # sum over j of n - q_len + j + 1
+    return int(seen.sum()) * num_q_heads * 4 * head_size
+
+
 def effective_sharing(context_lens, group_starts, shared_blocks, max_blocks_per_seq,
                       block_size=BLOCK_SIZE) -> np.ndarray:
     """Shared blocks each group really gets: the declaration clamped to

@@ -28,8 +28,8 @@ def heads_per_workgroup(num_kv_heads: int) -> int:
 
 
 def decode_wgs(num_seqs: int, num_head_groups: int, heads_per_wg: int, max_chunks_per_seq: int,
-               override: int | None = None) -> int:
-    w = 256 * max(4 // heads_per_wg, 1)
+               override: int | None = None, waves_per_cu: int = 4) -> int:
+    w = 256 * max(waves_per_cu // heads_per_wg, 1)
     by_work = (num_seqs * num_head_groups * max_chunks_per_seq + 3) // 4
     w = min(w, by_work)
     if override is not None and override > 0:
@@ -171,11 +171,16 @@ def plain_segments(lens, cap: int) -> list:
     return segs
 
 
-def check_plain(lens, num_q_heads, num_kv_heads, max_blocks_per_seq, block_size=16, override=None) -> Split:
-    hg = heads_per_workgroup(num_kv_heads)
-    NG = num_kv_heads // hg
+def check_plain(lens, num_q_heads, num_kv_heads, max_blocks_per_seq, block_size=16, override=None,
+                q_len=1) -> Split:
+    cols = q_len * (num_q_heads // num_kv_heads)
+    if cols > 32:  # a workgroup per KV head, a wavefront per 32 columns, 8 wavefronts per CU
+        hg, NG, wpc = (cols + 31) // 32, num_kv_heads, 8
+    else:
+        hg = heads_per_workgroup(num_kv_heads)
+        NG, wpc = num_kv_heads // hg, 4
     cap = max_blocks_per_seq * block_size
-    W = decode_wgs(len(lens), NG, hg, chunks_per_row(max_blocks_per_seq, block_size), override)
+    W = decode_wgs(len(lens), NG, hg, chunks_per_row(max_blocks_per_seq, block_size), override, wpc)
     segs = plain_segments(lens, cap)
     sp = walk(segs, NG, W)
     if W > 1:

@@ -104,11 +104,14 @@ def test_workspace_size_and_check(L, monkeypatch):
 def test_decode_multi_limits(L):
     d = desc()                                     # 8 KV heads of 128
     M = L.pa_decode_multi
-    # 4 new tokens x 8 query heads per KV head = 32 columns: supported
+    # 4 new tokens x 8 query heads per KV head = 32 columns: one wavefront per KV head
     assert L.pa_decode_multi_workspace_bytes(ctypes.byref(d), 256, 4, 64, 256) > 0
-    # 5 x 8 = 40 columns: refused before anything runs
-    assert L.pa_decode_multi_workspace_bytes(ctypes.byref(d), 256, 5, 64, 256) == 0
-    assert M(ctypes.byref(d), P, P, P, 4, 5, 64, 16, 1.0, P, None, 0, None) == _lib.PA_ERR_UNSUPPORTED
+    # 5 x 8 = 40 and 32 x 8 = 256 columns: column groups of 32, one wavefront each
+    assert L.pa_decode_multi_workspace_bytes(ctypes.byref(d), 256, 5, 64, 256) > 0
+    assert L.pa_decode_multi_workspace_bytes(ctypes.byref(d), 256, 32, 64, 256) > 0
+    # 33 x 8 = 264 columns: refused before anything runs
+    assert L.pa_decode_multi_workspace_bytes(ctypes.byref(d), 256, 33, 64, 256) == 0
+    assert M(ctypes.byref(d), P, P, P, 4, 33, 64, 16, 1.0, P, None, 0, None) == _lib.PA_ERR_UNSUPPORTED
     assert M(ctypes.byref(d), P, P, P, 4, 0, 64, 16, 1.0, P, None, 0, None) == _lib.PA_ERR_SHAPE
     assert M(ctypes.byref(d), None, P, P, 4, 2, 64, 16, 1.0, P, None, 0, None) == _lib.PA_ERR_NULL
     # q_len = 1 needs the same workspace as pa_decode

@@ -99,3 +99,74 @@ def test_multi_token_block_sizes(bs, ql, hq, hkv, d, monkeypatch):
         else:
             monkeypatch.setenv("PA_DECODE_WGS", wgs)
         run_multi(b, f"multi bs={bs} ql={ql} hq={hq} hkv={hkv} d={d} wgs={wgs}")
+
+
+# More than 32 (new token, query head) columns per KV head: a workgroup's
+# wavefronts are the column groups of one KV head (32 columns each, the last
+# one possibly partial).
+WIDE = [(9, 32, 8, 128), (16, 32, 8, 128), (64, 32, 8, 128), (8, 64, 8, 128), (40, 4, 4, 64),
+        (100, 2, 1, 128), (20, 12, 4, 128), (32, 64, 8, 64)]
+
+
+@pytest.mark.parametrize("ql,hq,hkv,d", WIDE)
+def test_wide_multi_token_across_work_splits(ql, hq, hkv, d, monkeypatch):
+    lens = [max(n, ql) for n in LENS + [ql, ql + 1, 2 * ql + 15]]
+    nb = int(sum((n + 15) // 16 for n in lens)) + 9
+    b = W.make_batch("wide", 1500 + ql * 10 + hq + d, lens, hq, hkv, d, nb, q_len=ql)
+    b.context_lens[-3] = 0  # an empty sequence among them
+    for wgs in ("1", "5", "default", "3000"):
+        if wgs == "default":
+            monkeypatch.delenv("PA_DECODE_WGS", raising=False)
+        else:
+            monkeypatch.setenv("PA_DECODE_WGS", wgs)
+        _, out = run_multi(b, f"wide ql={ql} hq={hq} hkv={hkv} d={d} wgs={wgs}")
+        assert np.all(out[-3] == 0)
+
+
+@pytest.mark.parametrize("bs", [8, 32])
+@pytest.mark.parametrize("ql,hq,hkv,d", [(16, 32, 8, 128), (64, 32, 8, 128), (33, 8, 8, 64)])
+def test_wide_multi_token_block_sizes(bs, ql, hq, hkv, d, monkeypatch):
+    lens = [max(n, ql) for n in [4, 7, 8, 9, 15, 16, 17, 31, 32, 33, 100, 255, 1000]]
+    nb = int(sum((n + bs - 1) // bs for n in lens)) + 9
+    b = W.make_batch("wide", 1800 + bs + ql * 10 + hq + d, lens, hq, hkv, d, nb, q_len=ql, block_size=bs)
+    assert b.block_size == bs
+    for wgs in ("1", "5", "default"):
+        if wgs == "default":
+            monkeypatch.delenv("PA_DECODE_WGS", raising=False)
+        else:
+            monkeypatch.setenv("PA_DECODE_WGS", wgs)
+        run_multi(b, f"wide bs={bs} ql={ql} hq={hq} hkv={hkv} d={d} wgs={wgs}")
+
+
+def test_wide_prefill_chunk_from_the_start():
+    """A whole 64-token prompt as one chunk (every token new, from position 0)
+    and a 200-token one: token j attends over positions 0..j only."""
+    b = W.make_batch("wide", 1900, [64, 200, 64], 32, 8, 128, 40, q_len=64)
+    run_multi(b, "wide prefill chunk from position 0")
+
+
+def test_wide_columns_past_the_limit_are_refused():
+    import paged_kv_cache_433_amd as pa
+    b = W.make_batch("wide", 1901, [40, 50], 8, 1, 64, 8, q_len=33)   # 264 columns per KV head
+    kd, vd = to_dev_bf16(b.k_cache), to_dev_bf16(b.v_cache)
+    with pytest.raises(pa.PagedAttentionError) as e:
+        pa.decode_multi(to_dev_bf16(b.q), kd, vd, to_dev(b.block_tables), to_dev(b.context_lens), float(b.scale))
+    assert e.value.code == -3
+
+
+def test_wide_prefill_chunk_gqa_layer_full_size():
+    """The Llama-3-8B-shaped GQA layer with a 64-token chunk per sequence (256
+    columns per KV head), default split, every output against the oracle."""
+    from oracle_pool import oracle_batch
+    import paged_kv_cache_433_amd as pa
+    b = W.make_batch("llama3_8b_gqa_q64", 3, np.maximum(W.config_lens("llama3_8b_gqa", 3), 64), 32, 8, 128, 65536,
+                     max_blocks_per_seq=256, q_len=64)
+    note("wide gqa full size q_len=64")
+    kd, vd = to_dev_bf16(b.k_cache), to_dev_bf16(b.v_cache)
+    pa.reshape_and_cache(to_dev_bf16(b.new_k), to_dev_bf16(b.new_v), kd, vd, to_dev(b.slot_mapping))
+    out = bits_of(pa.decode_multi(to_dev_bf16(b.q), kd, vd, to_dev(b.block_tables), to_dev(b.context_lens),
+                                  float(b.scale)))
+    oracle.reshape_and_cache(b.k_cache, b.v_cache, b.new_k, b.new_v, b.slot_mapping)
+    note("wide gqa full size q_len=64: oracle over worker processes")
+    ref = oracle_batch("decode_multi", b.q, b.k_cache, b.v_cache, b.block_tables, b.context_lens, b.scale)
+    assert_attention_close(out, ref, "wide gqa full size")

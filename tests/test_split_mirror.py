@@ -55,6 +55,17 @@ def test_full_size_workloads(name):
     assert sp.E == sp.W
 
 
+@pytest.mark.parametrize("q_len,hq,hkv", [(4, 32, 8), (9, 32, 8), (64, 32, 8), (8, 64, 8), (100, 2, 1),
+                                          (20, 12, 4)])
+def test_multi_token_splits(q_len, hq, hkv):
+    lens = [max(n, q_len) for n in EDGE_LENS]
+    mb = max((n + 15) // 16 for n in lens)
+    for wgs in SPLITS:
+        M.check_plain(lens, hq, hkv, mb, override=wgs, q_len=q_len)
+    hq_, hkv_, _, _, mb, seed = W.CONFIG_SHAPES["llama3_8b_gqa"]
+    M.check_plain(np.maximum(W.config_lens("llama3_8b_gqa", seed), q_len), hq_, hkv_, mb, q_len=q_len)
+
+
 def test_seeded_random_plain_cases():
     rng = np.random.default_rng(2024)
     for case in range(300):

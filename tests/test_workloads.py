@@ -158,3 +158,15 @@ def test_beam_workload_invariants():
         assert np.array_equal(cnt, wl.pool.ref)
     assert total_pairs > 0
     assert refs.sum() > 0
+
+
+def test_algorithmic_flops_counts_every_visible_position():
+    """4 * head_size flops per (new token, query head, visible position),
+    counted here by walking the causal limits one by one."""
+    lens, q_len, hq, d = [0, 5, 64, 100, 7], 5, 12, 64
+    want = 0
+    for n in lens:
+        for j in range(q_len if n else 0):
+            want += (n - q_len + j + 1) * hq * 4 * d
+    assert W.algorithmic_flops(lens, hq, d, q_len=q_len) == want
+    assert W.algorithmic_flops([10, 3], 8, 128) == 13 * 8 * 4 * 128
