@@ -353,6 +353,10 @@ def main(argv=None) -> int:
     ap.add_argument("--block-size", type=int, default=16, choices=(8, 16, 32),
                     help="tokens per cache block for the named single-step configs (same pool capacity in "
                          "tokens)")
+    ap.add_argument("--unfused", action="store_true",
+                    help="single new token: scatter with pa_reshape_and_cache, then pa_decode (two launches), "
+                         "instead of the fused step (pa_decode_step: the new token is attended from its K/V "
+                         "row and written to its slot in the decode launch)")
     ap.add_argument("--shared", action="store_true",
                     help="beam_cow only: decode with pa_decode_shared, reading a prompt's shared blocks once "
                          "for its beams (the sharing is read back from the block tables)")
@@ -403,9 +407,18 @@ def main(argv=None) -> int:
             raise SystemExit("--shared applies to the beam_cow workload")
         b = W.make_config(args.config, q_len=args.q_len, block_size=args.block_size)
     multi = args.q_len > 1
+    fused = not (multi or args.shared or args.unfused)
+    if fused:
+        # The fused step derives each new token's slot from its table: the
+        # batch's slots must be position n - 1 of each sequence.
+        pos = b.context_lens.astype(np.int64) - 1
+        want = b.block_tables[np.arange(b.num_seqs), pos // b.block_size].astype(np.int64) * b.block_size + \
+            pos % b.block_size
+        assert np.array_equal(want, b.slot_mapping), "new tokens are not at position n - 1 of their sequences"
     if args.config == "beam_cow" and args.block_size != 16:
         raise SystemExit("--block-size applies to the named single-step configs")
-    workload = args.config + ("_shared" if args.shared else "") + (f"_bs{args.block_size}" if args.block_size != 16 else "")
+    workload = args.config + ("_shared" if args.shared else "") + ("_unfused" if args.unfused else "") + \
+        (f"_bs{args.block_size}" if args.block_size != 16 else "")
 
     def bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -430,12 +443,18 @@ def main(argv=None) -> int:
         gshared_t = torch.from_numpy(gshared).to(dev)
         decode_bytes = W.shared_algorithmic_bytes(b.context_lens, gstarts, gshared, b.max_blocks_per_seq,
                                                   b.num_q_heads, b.num_kv_heads, b.head_size)
-    step_bytes = decode_bytes + W.scatter_bytes(len(b.slot_mapping), b.num_kv_heads, b.head_size)
+    if fused:
+        decode_bytes += W.step_write_bytes(b.context_lens, b.num_kv_heads, b.head_size)
+        step_bytes = decode_bytes
+    else:
+        step_bytes = decode_bytes + W.scatter_bytes(len(b.slot_mapping), b.num_kv_heads, b.head_size)
     if pairs is not None:
         step_bytes += W.copy_bytes(len(b.cow_pairs), b.block_size, b.num_kv_heads, b.head_size)
 
     def run_decode():
-        if args.shared:
+        if fused:
+            pa.decode_step(q, new_k, new_v, kc, vc, tables, lens, scale, out=out)
+        elif args.shared:
             pa.decode_shared(q, kc, vc, tables, lens, gstarts_t, gshared_t, scale, out=out)
         elif multi:
             pa.decode_multi(q, kc, vc, tables, lens, scale, out=out)
@@ -447,7 +466,8 @@ def main(argv=None) -> int:
     def step(ev=None):
         if pairs is not None:
             pa.copy_blocks(kc, vc, pairs)
-        pa.reshape_and_cache(new_k, new_v, kc, vc, slots)
+        if not fused:
+            pa.reshape_and_cache(new_k, new_v, kc, vc, slots)
         if ev is not None:
             ev[0].record(stream)
         run_decode()
@@ -469,23 +489,22 @@ def main(argv=None) -> int:
             step()
         torch.cuda.synchronize()
 
-    # Exactly `steps` timed steps (the step time), with the decode call's
-    # own events inside each.
-    ev_steps = events(args.steps)
+    # Exactly `steps` timed steps (the step time), back to back between two
+    # events: no marker inside the timed region.
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
-    for i in range(args.steps):
-        step(ev_steps[i])
+    for _ in range(args.steps):
+        step()
     end.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms = total_ms / args.steps
-    step_dec_us = np.array([a.elapsed_time(z) for a, z in ev_steps]) * 1e3
 
     # The decode call's time for the roofline: at least ROOF_MIN_LAUNCHES
-    # launches and ROOF_MIN_S of them, each inside a whole step as above.
-    n_roof = max(ROOF_MIN_LAUNCHES, args.steps, int(np.ceil(ROOF_MIN_S / (np.mean(step_dec_us) * 1e-6))))
+    # launches and ROOF_MIN_S of them, each inside a whole step as above,
+    # with events around the call.
+    n_roof = max(ROOF_MIN_LAUNCHES, args.steps, int(np.ceil(ROOF_MIN_S / (ms * 1e-3))))
     ev_roof = events(n_roof)
     for i in range(n_roof):
         step(ev_roof[i])
@@ -493,7 +512,7 @@ def main(argv=None) -> int:
     dec_us = np.array([a.elapsed_time(z) for a, z in ev_roof]) * 1e3
     dec_mean_us = float(np.mean(dec_us))
     dec_pct = {p: float(np.percentile(dec_us, p)) for p in (10, 50, 90)}
-    print(f"[bench] {args.steps} steps: {ms * 1e3:.1f} us/step (decode call {np.mean(step_dec_us):.1f} us); "
+    print(f"[bench] {args.steps} steps: {ms * 1e3:.1f} us/step; "
           f"{n_roof} decode calls: mean {dec_mean_us:.1f} us, median {dec_pct[50]:.1f}, p10 {dec_pct[10]:.1f}, "
           f"p90 {dec_pct[90]:.1f}", file=sys.stderr, flush=True)
 
@@ -540,6 +559,8 @@ def main(argv=None) -> int:
     traffic = measured_traffic(workload) if not multi else None
     if args.shared:
         kernel = "decode_shared call: share_plan_kernel + decode_kernel + merge_kernel"
+    elif fused:
+        kernel = "decode_step call (new tokens attended and written in the launch): decode_kernel + merge_kernel"
     else:
         kernel = "decode call: decode_kernel + merge_kernel"
     rec = {
@@ -569,7 +590,8 @@ def main(argv=None) -> int:
             "q_len": args.q_len,
             "step": ("copy_blocks + " if pairs is not None else "")
                     + ("reshape_and_cache + decode_multi" if multi else
-                       "reshape_and_cache + decode_shared" if args.shared else "reshape_and_cache + decode"),
+                       "reshape_and_cache + decode_shared" if args.shared else
+                       "decode_step (fused scatter and decode)" if fused else "reshape_and_cache + decode"),
             "parallelism": "single GPU",
             "cache": CACHE_NOTES.get(workload, "cold: the K/V of a call is several times the 256 MB MALL"),
         },
@@ -596,7 +618,6 @@ def main(argv=None) -> int:
             "p10_launch_us": round(dec_pct[10], 2),
             "p90_launch_us": round(dec_pct[90], 2),
             "launches_timed": int(n_roof),
-            "timed_steps_mean_launch_us": round(float(np.mean(step_dec_us)), 2),
             "mean_launch_us_mall_evicted": round(cold_us, 2) if cold_us else None,
             "achieved_mall_evicted": round(decode_bytes / cold_us / 1e3, 2) if cold_us else None,
             "stream_read_same_bytes": round(stream_read_gbps, 1) if stream_read_gbps else None,

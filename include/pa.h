@@ -146,6 +146,42 @@ size_t pa_decode_workspace_bytes(const pa_kv_cache *cache, int32_t num_seqs,
                                  int32_t num_q_heads, int32_t max_blocks_per_seq);
 
 /*
+ * pa_decode_step - one decode step in one call: pa_reshape_and_cache of
+ * each sequence's new token, then pa_decode, with the same result
+ * ("Inside vLLM", section "Scheduler": a decode step attends from the most
+ * recent token over every cached K/V vector, its own included, and stores
+ * its K/V for later steps; "vLLM: Anatomy and Mechanisms", section
+ * "Block-Level Management": the token's slot lies in the block its table
+ * names).
+ *
+ * Sequence s has one new token, at position n - 1 (n = context_lens[s], the
+ * new token included). Its K and V are k[s] and v[s]; its slot is row
+ * (n - 1) % B of physical block block_tables[s*max_blocks_per_seq +
+ * (n - 1)/B], B = cache->block_size (the slot pa_reshape_and_cache would be
+ * given). The call attends over positions 0 .. n - 2 from the cache and
+ * over position n - 1 from k[s], v[s], and writes k[s], v[s] into that
+ * slot. The output is pa_decode's after that scatter, and the cache after
+ * the call is the cache after it, bit for bit. n == 0: nothing is written
+ * and the output row is zero. A table entry for position n - 1 outside
+ * [0, num_blocks) skips the write (the output still uses k[s], v[s]).
+ *
+ *   k, v   bf16 [num_seqs, num_kv_heads, head_size], 16-byte aligned
+ * Other arguments, the workspace (pa_decode_step_workspace_bytes) and the
+ * errors are those of pa_decode. Preconditions: the slot's block is not read
+ * at that row by another sequence of the call (a copy-on-write block is
+ * private before a token is appended to it), and no two sequences share a
+ * slot.
+ */
+int pa_decode_step(const pa_kv_cache *cache, const void *q, const void *k, const void *v,
+                   const int32_t *block_tables, const int32_t *context_lens, int32_t num_seqs,
+                   int32_t num_q_heads, int32_t max_blocks_per_seq, float scale, void *out,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes of pa_decode_step (as pa_decode_workspace_bytes). */
+size_t pa_decode_step_workspace_bytes(const pa_kv_cache *cache, int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t max_blocks_per_seq);
+
+/*
  * pa_decode_noalloc - pa_decode for callers that cannot allocate device
  * memory: code under HIP graph capture, tight serving loops, harnesses that
  * forbid allocation. Same arguments, computation, kernels and result (bit

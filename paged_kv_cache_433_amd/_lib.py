@@ -22,6 +22,7 @@ PA_NOALLOC_SCRATCH_BYTES = 17301504
 
 # Every function include/pa.h declares.
 EXPORTS = ("pa_decode", "pa_decode_workspace_bytes", "pa_decode_noalloc",
+           "pa_decode_step", "pa_decode_step_workspace_bytes",
            "pa_decode_multi", "pa_decode_multi_workspace_bytes",
            "pa_decode_shared", "pa_decode_shared_workspace_bytes",
            "pa_reshape_and_cache", "pa_copy_blocks",
@@ -52,6 +53,10 @@ def _declare(lib):
     D = ctypes.POINTER(KVCacheDesc)
     lib.pa_decode.argtypes = [D, P, P, P, I32, I32, I32, ctypes.c_float, P, P, SZ, P]
     lib.pa_decode.restype = ctypes.c_int
+    lib.pa_decode_step.argtypes = [D, P, P, P, P, P, I32, I32, I32, ctypes.c_float, P, P, SZ, P]
+    lib.pa_decode_step.restype = ctypes.c_int
+    lib.pa_decode_step_workspace_bytes.argtypes = [D, I32, I32, I32]
+    lib.pa_decode_step_workspace_bytes.restype = SZ
     lib.pa_decode_noalloc.argtypes = [D, P, P, P, I32, I32, I32, ctypes.c_float, P, P]
     lib.pa_decode_noalloc.restype = ctypes.c_int
     lib.pa_decode_workspace_bytes.argtypes = [D, I32, I32, I32]

@@ -90,8 +90,18 @@ constexpr uint32_t kBf16One = 0x3F80u;
 // 32 (new token, query head) columns per KV head (kWide: a workgroup's
 // wavefronts are the column groups of one KV head, 32 columns each); or a
 // list of items, each read once for the one or more sequences it serves
-// (kShared).
-constexpr int kSingle = 0, kCausal = 1, kShared = 2, kWide = 3;
+// (kShared); or one new token per sequence that is not in the cache yet
+// (kStep): it is read from the step's new K/V rows as one more chunk at the
+// end of its sequence, and written to its slot in the same launch.
+constexpr int kSingle = 0, kCausal = 1, kShared = 2, kWide = 3, kStep = 4;
+
+// Chunks of a segment of n positions: the cached ones in CH-token chunks,
+// and (kStep) the newest position on its own as the last chunk.
+template <int M, int CH>
+__device__ __forceinline__ int seg_chunks(int n) {
+  if constexpr (M == kStep) return n > 0 ? (n - 1 + CH - 1) / CH + 1 : 0;
+  return (n + CH - 1) / CH;
+}
 
 // Several new tokens per sequence, each with its own causal limit.
 constexpr bool causal(int M) { return M == kCausal || M == kWide; }
@@ -266,7 +276,7 @@ __device__ __forceinline__ bool next_piece(Walker &wk, Piece &p) {
           if (wk.s < wk.S) take_item(wk, wk.items[wk.s]); else wk.L = 0;
         } else {
           wk.n = wk.s < wk.S ? clamp_len(wk.lens[wk.s], wk.cap) : 0;
-          wk.L = (wk.n + CH - 1) / CH;
+          wk.L = seg_chunks<M, CH>(wk.n);
         }
       } while (wk.L == 0 && wk.s < wk.S);
       if (wk.s >= wk.S) wk.u = wk.hi;  // only if the lengths changed during the call
@@ -344,6 +354,7 @@ struct Stream {
   bool first_cut;
   int2 desc;
   int staged;  // whole-segment outputs staged in LDS
+  int nnew;    // kStep: new K/V rows staged in LDS for their slots
 };
 
 // Buffer-resource word 3 for gfx9-family raw (untyped) buffer loads.
@@ -412,6 +423,22 @@ __device__ __forceinline__ uint16_t *stage_area(uint16_t *lds, const DecodeArgs 
   constexpr int D = NJ * 32;
   return lds + (size_t)a.heads_per_wg * 2 * a.num_cols * D +
          (size_t)wave * (kStageBytes + kStageSlots * sizeof(size_t)) / sizeof(uint16_t);
+}
+
+// kStep: the new K/V rows a wavefront writes to their slots are staged here
+// and stored after the stream, up to kNewSlots per wavefront (more are
+// stored at once). A slot holds the K row, the V row (head_size bf16 each)
+// and the destination element offset, padded to 16 bytes.
+constexpr int kNewSlots = 8;
+template <int D>
+constexpr int new_slot_elems() { return 2 * D + 8; }
+
+template <int NJ>
+__device__ __forceinline__ uint16_t *new_area(uint16_t *lds, const DecodeArgs &a, int wave) {
+  constexpr int D = NJ * 32;
+  return lds + (size_t)a.heads_per_wg * 2 * a.num_cols * D +
+         (size_t)a.heads_per_wg * (kStageBytes + kStageSlots * sizeof(size_t)) / sizeof(uint16_t) +
+         (size_t)wave * kNewSlots * new_slot_elems<D>();
 }
 
 template <int NJ>
@@ -523,14 +550,11 @@ __device__ __forceinline__ size_t head_off(const Lane<NT> &ln, const Piece &p) {
 // (beams sharing a prompt) it is also faster than all-plain (179 against
 // 186 us).
 template <int NJ, int NT>
-__device__ __forceinline__ void issue(const DecodeArgs &a, const Lane<NT> &ln, int blk, size_t hoff, int nrows,
-                                      u32x4_t (&K)[NJ], u32x4_t (&V)[NJ]) {
-  const size_t base = ((size_t)blk * ln.blk_stride + hoff) * sizeof(uint16_t);
+__device__ __forceinline__ void issue_rows(const char *kb, const char *vb, const Lane<NT> &ln, int nrows,
+                                           u32x4_t (&K)[NJ], u32x4_t (&V)[NJ]) {
   const int span = nrows * ln.row_bytes;
-  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<char *>(reinterpret_cast<const char *>(a.k_cache) + base), 0, span, kRawBufferWord3);
-  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<char *>(reinterpret_cast<const char *>(a.v_cache) + base), 0, span, kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(kb), 0, span, kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(vb), 0, span, kRawBufferWord3);
 #pragma unroll
   for (int j = 0; j < NJ / 2; ++j)
     K[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, ln.lane_off + 64 * j, 0, kNonTemporal));
@@ -542,6 +566,16 @@ __device__ __forceinline__ void issue(const DecodeArgs &a, const Lane<NT> &ln, i
     V[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, ln.lane_off + 64 * j, 0, 0));
 }
 
+// The same for the first `nrows` token rows of block `blk` of the cache, at
+// the wavefront's KV head (element offset hoff in a token row).
+template <int NJ, int NT>
+__device__ __forceinline__ void issue(const DecodeArgs &a, const Lane<NT> &ln, int blk, size_t hoff, int nrows,
+                                      u32x4_t (&K)[NJ], u32x4_t (&V)[NJ]) {
+  const size_t base = ((size_t)blk * ln.blk_stride + hoff) * sizeof(uint16_t);
+  issue_rows<NJ>(reinterpret_cast<const char *>(a.k_cache) + base, reinterpret_cast<const char *>(a.v_cache) + base,
+                 ln, nrows, K, V);
+}
+
 // Two 8-token blocks as one chunk: rows 0-7 of the tile from block `ida`
 // (its first `na` rows), rows 8-15 from block `idb` (its first `nb`). Each
 // lane loads from both blocks' resources: at its offset in the first block
@@ -550,19 +584,17 @@ __device__ __forceinline__ void issue(const DecodeArgs &a, const Lane<NT> &ln, i
 // its range reads as zero, so OR-ing the two gives the row without a
 // per-lane choice of resource.
 template <int NJ, int NT>
-__device__ __forceinline__ void issue_pair(const DecodeArgs &a, const Lane<NT> &ln, int ida, int idb, size_t hoff,
-                                           int na, int nb, u32x4_t (&K)[NJ], u32x4_t (&V)[NJ]) {
-  const size_t base_a = ((size_t)ida * ln.blk_stride + hoff) * sizeof(uint16_t);
-  const size_t base_b = ((size_t)idb * ln.blk_stride + hoff) * sizeof(uint16_t);
-  const char *kc = reinterpret_cast<const char *>(a.k_cache), *vc = reinterpret_cast<const char *>(a.v_cache);
+__device__ __forceinline__ void issue_pair_rows(const char *kba, const char *vba, int na, const char *kbb,
+                                                const char *vbb, int nb, const Lane<NT> &ln, u32x4_t (&K)[NJ],
+                                                u32x4_t (&V)[NJ]) {
   const __amdgpu_buffer_rsrc_t rka =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(kc + base_a), 0, na * ln.row_bytes, kRawBufferWord3);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(kba), 0, na * ln.row_bytes, kRawBufferWord3);
   const __amdgpu_buffer_rsrc_t rkb =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(kc + base_b), 0, nb * ln.row_bytes, kRawBufferWord3);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(kbb), 0, nb * ln.row_bytes, kRawBufferWord3);
   const __amdgpu_buffer_rsrc_t rva =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(vc + base_a), 0, na * ln.row_bytes, kRawBufferWord3);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(vba), 0, na * ln.row_bytes, kRawBufferWord3);
   const __amdgpu_buffer_rsrc_t rvb =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(vc + base_b), 0, nb * ln.row_bytes, kRawBufferWord3);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(vbb), 0, nb * ln.row_bytes, kRawBufferWord3);
   const uint32_t off_b = ln.lane_off_b;
 #pragma unroll
   for (int j = 0; j < NJ / 2; ++j)
@@ -576,6 +608,33 @@ __device__ __forceinline__ void issue_pair(const DecodeArgs &a, const Lane<NT> &
   for (int j = 0; j < NJ; ++j)
     V[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rva, ln.lane_off + 64 * j, 0, 0)) |
            __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rvb, off_b + 64 * j, 0, 0));
+}
+
+template <int NJ, int NT>
+__device__ __forceinline__ void issue_pair(const DecodeArgs &a, const Lane<NT> &ln, int ida, int idb, size_t hoff,
+                                           int na, int nb, u32x4_t (&K)[NJ], u32x4_t (&V)[NJ]) {
+  const size_t base_a = ((size_t)ida * ln.blk_stride + hoff) * sizeof(uint16_t);
+  const size_t base_b = ((size_t)idb * ln.blk_stride + hoff) * sizeof(uint16_t);
+  const char *kc = reinterpret_cast<const char *>(a.k_cache), *vc = reinterpret_cast<const char *>(a.v_cache);
+  issue_pair_rows<NJ>(kc + base_a, vc + base_a, na, kc + base_b, vc + base_b, nb, ln, K, V);
+}
+
+// kStep: the newest position of sequence s as a chunk of its own, read from
+// the step's new K/V rows ([num_seqs, num_kv_heads, head_size]): it is row 0
+// of the tile; rows 1-15 lie past the one-row range and read as zeros. With
+// 8-token blocks the loads take the two-block form (the second set reads
+// nothing), so every path has the same loads in flight.
+template <int NJ, int NT, int BS>
+__device__ __forceinline__ void issue_new(const DecodeArgs &a, const Lane<NT> &ln, int s, size_t hoff,
+                                          u32x4_t (&K)[NJ], u32x4_t (&V)[NJ]) {
+  const size_t base = ((size_t)s * a.num_kv_heads * (NJ * 32) + hoff) * sizeof(uint16_t);
+  const char *kb = reinterpret_cast<const char *>(a.k_new) + base;
+  const char *vb = reinterpret_cast<const char *>(a.v_new) + base;
+  if constexpr (BS < kBlock) {
+    issue_pair_rows<NJ>(kb, vb, 1, kb, vb, 0, ln, K, V);
+  } else {
+    issue_rows<NJ>(kb, vb, ln, 1, K, V);
+  }
 }
 
 // Starts the loads of chunk c of table row `row` for this wavefront's head,
@@ -626,6 +685,24 @@ template <int CH = kBlock>
 __device__ __forceinline__ int rows_in(int n, int b) {
   const int r = n - b * CH;
   return r < CH ? r : CH;
+}
+
+// Starts the loads of chunk b of sequence s (n positions, L chunks): from
+// the cache, or (kStep) for the last chunk the step's new K/V row; the
+// cached chunks of kStep end before the newest position.
+template <int NJ, int NT, int M, int BS>
+__device__ __forceinline__ void issue_seq(const int32_t *__restrict__ tables, const DecodeArgs &a, const Lane<NT> &ln,
+                                          int s, int b, int n, int L, size_t hoff, u32x4_t (&K)[NJ],
+                                          u32x4_t (&V)[NJ]) {
+  constexpr int CH = chunk_of<BS>();
+  if constexpr (M == kStep) {
+    if (b == L - 1)
+      issue_new<NJ, NT, BS>(a, ln, s, hoff, K, V);
+    else
+      issue_chunk<NJ, NT, BS>(tables, a, ln, s, b, hoff, rows_in<CH>(n - 1, b), K, V);
+  } else {
+    issue_chunk<NJ, NT, BS>(tables, a, ln, s, b, hoff, rows_in<CH>(n, b), K, V);
+  }
 }
 
 // Stores the partial record of column tile t of this wavefront in slot
@@ -726,10 +803,24 @@ __device__ __forceinline__ void finish_piece(const DecodeArgs &a, const Lane<NT>
 // After the stream (launches that defer): the staged whole-segment outputs,
 // the first piece's partial record (if that piece was cut) and the merge
 // record.
-template <int NJ, int NT, bool DF>
+template <int NJ, int NT, int M, bool DF>
 __device__ __forceinline__ void finish_stream(const DecodeArgs &a, const Lane<NT> &ln, const Stream<NJ, NT> &st,
                                               uint16_t *lds) {
   constexpr int D = NJ * 32;
+  if constexpr (M == kStep) {
+    // The staged new rows: lanes 0 .. D/8 - 1 store the K row, the next D/8
+    // lanes the V row, 16 bytes each.
+    const uint16_t *area = new_area<NJ>(lds, a, ln.wave);
+    for (int i = 0; i < st.nnew; ++i) {
+      const uint16_t *slot = area + (size_t)i * new_slot_elems<D>();
+      const size_t dst = *reinterpret_cast<const size_t *>(slot + 2 * D);
+      if (ln.lane < D / 4) {
+        const int half = ln.lane / (D / 8), piece = ln.lane - half * (D / 8);
+        const u32x4_t v = *reinterpret_cast<const u32x4_t *>(slot + half * D + piece * 8);
+        *reinterpret_cast<u32x4_t *>(const_cast<uint16_t *>(half ? a.v_cache : a.k_cache) + dst + piece * 8) = v;
+      }
+    }
+  }
   if constexpr (DF) {
     const uint16_t *area = stage_area<NJ>(lds, a, ln.wave);
     const size_t *dsts = reinterpret_cast<const size_t *>(area + kStageBytes / sizeof(uint16_t));
@@ -745,6 +836,43 @@ __device__ __forceinline__ void finish_stream(const DecodeArgs &a, const Lane<NT
     }
     if (st.first_cut) store_record<NJ, NT>(a, ln, 0, 0, st.first_acc, st.first_m, st.first_l);
     if (ln.tid == 0 && a.merge_desc) a.merge_desc[ln.w] = st.desc;
+  }
+}
+
+// kStep: the newest position's K/V row of this wavefront's KV head goes to
+// its slot in the cache: row (n - 1) % block_size of the physical block the
+// table names for position n - 1. Lanes of tile row 0 hold it (dims 32j +
+// 8*grp .. +7). It is staged in LDS and stored after the stream (a store
+// issued mid-stream would make the waits for later loads wait for it too);
+// past the staging capacity it is stored at once. A table entry outside the
+// pool skips the write.
+template <int NJ, int NT, int M, int BS>
+__device__ __forceinline__ void stage_new(const int32_t *__restrict__ tables, const DecodeArgs &a, const Lane<NT> &ln,
+                                          Stream<NJ, NT> &st, uint16_t *lds, const u32x4_t (&K)[NJ],
+                                          const u32x4_t (&V)[NJ]) {
+  constexpr int D = NJ * 32;
+  const Piece &P = st.P;
+  const int pos = P.n - 1;
+  const int id = tables[(size_t)P.s * a.max_blocks_per_seq + pos / BS];
+  if ((uint32_t)id >= ln.pool32) return;
+  const size_t dst = (size_t)id * ln.blk_stride + (size_t)(pos % BS) * a.num_kv_heads * D + head_off<NJ, M>(ln, P);
+  if (st.nnew < kNewSlots) {
+    uint16_t *slot = new_area<NJ>(lds, a, ln.wave) + (size_t)st.nnew * new_slot_elems<D>();
+    if (ln.c == 0) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        *reinterpret_cast<u32x4_t *>(slot + 32 * j + 8 * ln.grp) = K[j];
+        *reinterpret_cast<u32x4_t *>(slot + D + 32 * j + 8 * ln.grp) = V[j];
+      }
+    }
+    if (ln.lane == 0) *reinterpret_cast<size_t *>(slot + 2 * D) = dst;
+    ++st.nnew;
+  } else if (ln.c == 0) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      *reinterpret_cast<u32x4_t *>(const_cast<uint16_t *>(a.k_cache) + dst + 32 * j + 8 * ln.grp) = K[j];
+      *reinterpret_cast<u32x4_t *>(const_cast<uint16_t *>(a.v_cache) + dst + 32 * j + 8 * ln.grp) = V[j];
+    }
   }
 }
 
@@ -819,15 +947,20 @@ __device__ __forceinline__ bool step(const int32_t *__restrict__ tables, const D
   } else {
     const int next_s = to_q ? st.Q.s : P.s;
     const int next_b = in_p ? P.off + nx : (to_q ? st.Q.off : P.off + st.i);
-    issue_chunk<NJ, NT, BS>(tables, a, ln, next_s, next_b, to_q ? st.hoff_q : st.hoff,
-                            rows_in<CH>(to_q ? st.Q.n : P.n, next_b), Kn, Vn);
+    issue_seq<NJ, NT, M, BS>(tables, a, ln, next_s, next_b, to_q ? st.Q.n : P.n, to_q ? st.Q.L : P.L,
+                             to_q ? st.hoff_q : st.hoff, Kn, Vn);
   }
   // Keep the scheduler from sinking those loads below the compute.
   __builtin_amdgcn_sched_barrier(0);
 
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
   const int b = M == kShared ? st.cc.b : P.off + st.i;
-  const int pos0 = b * CH + ln.grp * 4;
+  // kStep: the last chunk of a segment is the newest position alone (row 0),
+  // and the cached chunks before it end at position n - 2.
+  const bool fresh = M == kStep && b == P.L - 1;
+  const int pos_base = fresh ? P.n - 1 : b * CH;
+  const int vis = M == kStep ? (fresh ? P.n : P.n - 1) : P.n;  // positions < vis are in this chunk's rows
+  const int pos0 = pos_base + ln.grp * 4;
   // kShared: in the shared blocks the segment's members' columns are live,
   // in a member's own blocks only that member's; a tile holding none of them
   // is skipped (a uniform branch).
@@ -855,7 +988,7 @@ __device__ __forceinline__ bool step(const int32_t *__restrict__ tables, const D
     int lim;
     if constexpr (kMulti) lim = P.n - ln.qshift[t];
     else if constexpr (M == kShared) lim = (cj < 0 || ln.tok[t] == cj) ? st.cc.n : 0;
-    else lim = P.n;
+    else lim = vis;
     float z[4];
 #pragma unroll
     // With 8-token chunks the tile's rows 8-15 hold no token of the chunk.
@@ -883,7 +1016,7 @@ __device__ __forceinline__ bool step(const int32_t *__restrict__ tables, const D
   }
 
   // V rows of tokens at or past n must not reach the sum, even as NaN * 0.
-  const bool v_live = ln.c < CH && b * CH + ln.c < (M == kShared ? st.cc.n : P.n);
+  const bool v_live = ln.c < CH && pos_base + ln.c < (M == kShared ? st.cc.n : vis);
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
 #pragma unroll
@@ -900,6 +1033,9 @@ __device__ __forceinline__ bool step(const int32_t *__restrict__ tables, const D
     }
   }
 
+  if constexpr (M == kStep) {
+    if (fresh) stage_new<NJ, NT, M, BS>(tables, a, ln, st, lds, K, V);
+  }
   if (stage_q) park_q<NJ>(q_slot<NJ>(lds, a, ln.wave, st.ord + 1), ln, qt);
 
   st.i = nx;
@@ -993,7 +1129,7 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
     // gives the total and every sequence's first unit at once.
     const int n = tid < S ? clamp_len(lens[tid], cap) : 0;
     if (tid < S && n == 0) zero_empty<D>(a, tid, w);
-    const long long L = (n + CH - 1) / CH;
+    const long long L = seg_chunks<M, CH>(n);
     long long pre, total;
     const long long incl = wg_scan(L, red, wave, lane, nthr >> 6, pre, total);
     U = total * NG;
@@ -1016,7 +1152,7 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
     long long mine = 0;
     for (int s = tid; s < S; s += nthr) {
       const int n = clamp_len(lens[s], cap);
-      mine += (n + CH - 1) / CH;
+      mine += seg_chunks<M, CH>(n);
       if (n == 0) zero_empty<D>(a, s, w);
     }
     U = wg_sum(mine, red, wave, lane, nthr >> 6) * NG;
@@ -1034,7 +1170,7 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
     for (int base = 0; base < S; base += nthr) {
       const int s = base + tid;
       const int n = s < S ? clamp_len(lens[s], cap) : 0;
-      const long long L = (n + CH - 1) / CH;
+      const long long L = seg_chunks<M, CH>(n);
       long long pre, chunk_total;
       const long long incl = wg_scan(L, red, wave, lane, nthr >> 6, pre, chunk_total);
       const long long excl = before + pre + incl - L;
@@ -1060,7 +1196,7 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
     wk.seg_base = found_prefix * NG;
     wk.s = __builtin_amdgcn_readfirstlane(found_seq);
     wk.n = __builtin_amdgcn_readfirstlane(found_n);
-    wk.L = (wk.n + CH - 1) / CH;
+    wk.L = seg_chunks<M, CH>(wk.n);
   }
   wk.NG = NG;
   wk.u = lo;
@@ -1138,6 +1274,7 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
   st.first_cut = false;
   st.desc = int2{-1, -1};
   st.staged = 0;
+  st.nnew = 0;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     st.m_run[t] = -INFINITY;
@@ -1149,12 +1286,12 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
   if constexpr (M == kShared) {
     issue_shared<NJ, NT, BS>(tables, a, ln, st.P, st.cc, st.hoff, rows_in(st.cc.n, st.cc.b), KA, VA);
   } else {
-    issue_chunk<NJ, NT, BS>(tables, a, ln, st.P.s, st.P.off, st.hoff, rows_in<CH>(st.P.n, st.P.off), KA, VA);
+    issue_seq<NJ, NT, M, BS>(tables, a, ln, st.P.s, st.P.off, st.P.n, st.P.L, st.hoff, KA, VA);
   }
   while (step<NJ, NT, M, BS>(tables, a, ln, wk, st, KA, VA, KB, VB, q_lds) &&
          step<NJ, NT, M, BS>(tables, a, ln, wk, st, KB, VB, KA, VA, q_lds)) {
   }
-  finish_stream<NJ, NT, defers<NT, BS>()>(a, ln, st, q_lds);
+  finish_stream<NJ, NT, M, defers<NT, BS>()>(a, ln, st, q_lds);
 }
 
 // Log-sum-exp merge of the pieces of segments cut by workgroup boundaries.
@@ -1465,6 +1602,11 @@ hipError_t launch_decode_kernel(const DecodeArgs &args, size_t lds, hipStream_t 
 
 template <int D>
 hipError_t launch_decode_d(const DecodeArgs &args, size_t lds, hipStream_t stream) {
+  if (args.k_new) {
+    if (args.block_size == 8) return launch_decode_kernel<D, 1, kStep, 8>(args, lds, stream);
+    if (args.block_size == 32) return launch_decode_kernel<D, 1, kStep, 32>(args, lds, stream);
+    return launch_decode_kernel<D, 1, kStep>(args, lds, stream);
+  }
   if (args.q_len == 1) {
     if (args.block_size == 8) return launch_decode_kernel<D, 1, kSingle, 8>(args, lds, stream);
     if (args.block_size == 32) return launch_decode_kernel<D, 1, kSingle, 32>(args, lds, stream);
@@ -1489,7 +1631,9 @@ hipError_t launch_decode_d(const DecodeArgs &args, size_t lds, hipStream_t strea
 
 hipError_t launch_decode(const DecodeArgs &args, int32_t head_size, hipStream_t stream) {
   const bool wide = args.num_cols > 32;
+  const bool fused = args.k_new != nullptr;
   if (args.q_len < 1 || args.num_cols > kMaxDecodeCols || (args.q_len == 1 && args.num_cols > 16)) return hipErrorInvalidValue;
+  if (fused && (args.q_len != 1 || !args.v_new)) return hipErrorInvalidValue;
   // Columns per wavefront: all of them, or (wide) 32 per column group with
   // one wavefront per column group of the head group's one KV head.
   if (wide ? (args.rec_cols != 32 || args.col_groups != (args.num_cols + 31) / 32 ||
@@ -1502,9 +1646,11 @@ hipError_t launch_decode(const DecodeArgs &args, int32_t head_size, hipStream_t 
   // With one column tile, each wavefront also has an output staging area.
   const size_t lds = (size_t)args.heads_per_wg * (args.num_cols <= 16 ? 2 : 1) * args.rec_cols * head_size *
                          sizeof(uint16_t) +
-                     (args.num_cols <= 16 && args.block_size != 8
+                     (args.num_cols <= 16 && (args.block_size != 8 || fused)
                           ? (size_t)args.heads_per_wg * (kStageBytes + kStageSlots * sizeof(size_t))
-                          : 0);
+                          : 0) +
+                     // kStep: the new K/V rows staged for their slots
+                     (fused ? (size_t)args.heads_per_wg * kNewSlots * (4 * (size_t)head_size + 16) : 0);
   hipError_t err;
   if (head_size == 128) {
     err = launch_decode_d<128>(args, lds, stream);

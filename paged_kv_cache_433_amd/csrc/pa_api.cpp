@@ -125,6 +125,11 @@ int32_t chunks_per_row(const pa_kv_cache *c, int32_t max_blocks_per_seq) {
   return (int32_t)(((int64_t)max_blocks_per_seq * c->block_size + 15) / 16);
 }
 
+// The fused step reads each sequence's newest position as one more chunk.
+int32_t step_chunks_per_row(const pa_kv_cache *c, int32_t max_blocks_per_seq, bool fused) {
+  return chunks_per_row(c, max_blocks_per_seq) + (fused ? 1 : 0);
+}
+
 // Sharing-aware decode: an item serves up to 32 / group sequences (its
 // columns are their query heads of one KV head: at most two MFMA tiles).
 int32_t members_per_item(int32_t group) { return 32 / group; }
@@ -206,7 +211,8 @@ namespace {
 int decode_impl(const pa_kv_cache *cache, const void *q, const int32_t *block_tables,
                 const int32_t *context_lens, int32_t num_seqs, int32_t q_len, int32_t num_q_heads,
                 int32_t max_blocks_per_seq, float scale, void *out, void *workspace,
-                size_t workspace_bytes, void *stream, bool static_scratch) {
+                size_t workspace_bytes, void *stream, bool static_scratch, const void *k_new = nullptr,
+                const void *v_new = nullptr) {
   int rc = check_cache(cache, num_seqs > 0);
   if (rc != PA_OK) return rc;
   rc = check_decode_shape(cache, num_seqs, num_q_heads, max_blocks_per_seq);
@@ -217,9 +223,12 @@ int decode_impl(const pa_kv_cache *cache, const void *q, const int32_t *block_ta
   if (!q || !block_tables || !context_lens || !out)
     return fail(PA_ERR_NULL, "q, block_tables, context_lens or out is NULL");
   if (check_aligned(q, "q") != PA_OK || check_aligned(out, "out") != PA_OK) return PA_ERR_UNSUPPORTED;
+  const bool fused = k_new || v_new;
+  if (fused && (!k_new || !v_new)) return fail(PA_ERR_NULL, "k or v is NULL");
+  if (fused && (check_aligned(k_new, "k") != PA_OK || check_aligned(v_new, "v") != PA_OK)) return PA_ERR_UNSUPPORTED;
 
   const pa::DecodePlan plan = pa::plan_decode(num_seqs, num_q_heads, cache->num_kv_heads, cache->head_size,
-                                              chunks_per_row(cache, max_blocks_per_seq), q_len);
+                                              step_chunks_per_row(cache, max_blocks_per_seq, fused), q_len);
   if (workspace && workspace_bytes < plan.total_bytes)
     return fail(PA_ERR_WORKSPACE, "workspace smaller than pa_decode_workspace_bytes()");
   if (workspace && reinterpret_cast<uintptr_t>(workspace) % 16)
@@ -256,6 +265,8 @@ int decode_impl(const pa_kv_cache *cache, const void *q, const int32_t *block_ta
     a.part_ml = reinterpret_cast<float *>(base + plan.desc_bytes);
     a.part_o = reinterpret_cast<float *>(base + plan.desc_bytes + plan.ml_bytes);
   }
+  a.k_new = static_cast<const uint16_t *>(k_new);
+  a.v_new = static_cast<const uint16_t *>(v_new);
   a.num_blocks = cache->num_blocks;
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
@@ -316,6 +327,25 @@ int pa_decode_multi(const pa_kv_cache *cache, const void *q, const int32_t *bloc
                     size_t workspace_bytes, void *stream) {
   return decode_impl(cache, q, block_tables, context_lens, num_seqs, q_len, num_q_heads, max_blocks_per_seq, scale,
                      out, workspace, workspace_bytes, stream, false);
+}
+
+int pa_decode_step(const pa_kv_cache *cache, const void *q, const void *k, const void *v,
+                   const int32_t *block_tables, const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                   int32_t max_blocks_per_seq, float scale, void *out, void *workspace, size_t workspace_bytes,
+                   void *stream) {
+  if (num_seqs > 0 && (!k || !v)) return fail(PA_ERR_NULL, "k or v is NULL");
+  return decode_impl(cache, q, block_tables, context_lens, num_seqs, 1, num_q_heads, max_blocks_per_seq, scale, out,
+                     workspace, workspace_bytes, stream, false, num_seqs > 0 ? k : nullptr,
+                     num_seqs > 0 ? v : nullptr);
+}
+
+size_t pa_decode_step_workspace_bytes(const pa_kv_cache *cache, int32_t num_seqs, int32_t num_q_heads,
+                                      int32_t max_blocks_per_seq) {
+  if (check_cache(cache, false) != PA_OK) return 0;
+  if (check_decode_shape(cache, num_seqs, num_q_heads, max_blocks_per_seq) != PA_OK) return 0;
+  return pa::plan_decode(num_seqs, num_q_heads, cache->num_kv_heads, cache->head_size,
+                         step_chunks_per_row(cache, max_blocks_per_seq, true), 1)
+      .total_bytes;
 }
 
 int pa_decode_noalloc(const pa_kv_cache *cache, const void *q, const int32_t *block_tables,

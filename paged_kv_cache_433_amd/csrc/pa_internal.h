@@ -58,6 +58,10 @@ struct DecodeArgs {
   int32_t num_head_groups;       // Hkv / heads_per_wg, or Hkv with column groups
   int32_t num_wgs;               // workgroups sharing the units evenly
   float scale_log2;              // softmax scale times log2(e)
+  // The fused step only (null otherwise): each sequence's new token, bf16
+  // [S, Hkv, D], attended at position n - 1 and written to its slot.
+  const uint16_t *k_new;
+  const uint16_t *v_new;
   // Sharing-aware decode only (null otherwise).
   const ShareItem *items;        // [num_seqs + 1]: segments, then a sentinel holding the total units
   const ShareHeader *share;

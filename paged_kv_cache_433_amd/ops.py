@@ -115,6 +115,35 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=None, wor
     return out
 
 
+def decode_step(q, k, v, k_cache, v_cache, block_tables, context_lens, scale, out=None, workspace=None):
+    """One decode step in one call: each sequence's new token (``k``, ``v``:
+    bf16 ``[num_seqs, num_kv_heads, head_size]``) is attended at position
+    ``context_lens[s] - 1`` and written to the slot its block table names
+    there; returns ``out``. Equal to ``reshape_and_cache`` with those slots
+    followed by ``decode``."""
+    desc = _cache_desc(k_cache, v_cache)
+    dev = k_cache.device
+    S, hq, d = q.shape
+    _need(q, "q", _BF16, (S, hq, k_cache.shape[3]), dev)
+    _need(k, "k", _BF16, (S, k_cache.shape[2], k_cache.shape[3]), dev)
+    _need(v, "v", _BF16, (S, k_cache.shape[2], k_cache.shape[3]), dev)
+    mb = block_tables.shape[1] if block_tables.dim() == 2 else -1
+    _need(block_tables, "block_tables", torch.int32, (S, mb), dev)
+    _need(context_lens, "context_lens", torch.int32, (S,), dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", _BF16, (S, hq, d), dev)
+    lib = _lib.lib()
+    nbytes = int(lib.pa_decode_step_workspace_bytes(ctypes.byref(desc), S, hq, mb))
+    if workspace is None and nbytes:
+        workspace = _workspace(dev, nbytes)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.pa_decode_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(block_tables),
+                              _ptr(context_lens), S, hq, mb, float(scale), _ptr(out), _ptr(workspace), ws_bytes,
+                              _stream(dev)))
+    return out
+
+
 def decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, scale, out):
     """``decode`` through the entry point that allocates nothing
     (``pa_decode_noalloc``): the partial results go to the library's static

@@ -518,6 +518,13 @@ def shared_algorithmic_bytes(context_lens, group_starts, shared_blocks, max_bloc
     return tokens * row + qo + entries * 4 + 4 * len(n) + 4 * (2 * len(e) + 1)
 
 
+def step_write_bytes(context_lens, num_kv_heads, head_size, dtype_bytes=2) -> int:
+    """Bytes the fused step writes besides its output: the new K and V row of
+    every sequence with a non-empty context (read as part of its context)."""
+    live = int(np.count_nonzero(np.asarray(context_lens) > 0))
+    return live * 2 * num_kv_heads * head_size * dtype_bytes
+
+
 def scatter_bytes(num_tokens, num_kv_heads, head_size, dtype_bytes=2) -> int:
     """Bytes of the slot scatter: read new K/V, write them, read the slots."""
     return num_tokens * (2 * num_kv_heads * head_size * dtype_bytes * 2 + 8)

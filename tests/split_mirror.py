@@ -162,17 +162,19 @@ def merge(sp: Split, segments: list, NG: int, S_items: int) -> None:
             sp.written[rk] = sp.written.get(rk, 0) + 1
 
 
-def plain_segments(lens, cap: int) -> list:
-    """Sequences as segments (pa_decode, pa_decode_multi): clamped lengths."""
+def plain_segments(lens, cap: int, step: bool = False) -> list:
+    """Sequences as segments (pa_decode, pa_decode_multi): clamped lengths.
+    With `step` (pa_decode_step) the newest position is a chunk of its own."""
     segs = []
     for s, n in enumerate(lens):
         n = min(max(int(n), 0), cap)
-        segs.append(Segment(key=s, L=(n + CHUNK - 1) // CHUNK, rows=(s,)))
+        L = ((n - 1 + CHUNK - 1) // CHUNK + 1 if n > 0 else 0) if step else (n + CHUNK - 1) // CHUNK
+        segs.append(Segment(key=s, L=L, rows=(s,)))
     return segs
 
 
 def check_plain(lens, num_q_heads, num_kv_heads, max_blocks_per_seq, block_size=16, override=None,
-                q_len=1) -> Split:
+                q_len=1, step=False) -> Split:
     cols = q_len * (num_q_heads // num_kv_heads)
     if cols > 32:  # a workgroup per KV head, a wavefront per 32 columns, 8 wavefronts per CU
         hg, NG, wpc = (cols + 31) // 32, num_kv_heads, 8
@@ -180,8 +182,9 @@ def check_plain(lens, num_q_heads, num_kv_heads, max_blocks_per_seq, block_size=
         hg = heads_per_workgroup(num_kv_heads)
         NG, wpc = num_kv_heads // hg, 4
     cap = max_blocks_per_seq * block_size
-    W = decode_wgs(len(lens), NG, hg, chunks_per_row(max_blocks_per_seq, block_size), override, wpc)
-    segs = plain_segments(lens, cap)
+    W = decode_wgs(len(lens), NG, hg, chunks_per_row(max_blocks_per_seq, block_size) + (1 if step else 0),
+                   override, wpc)
+    segs = plain_segments(lens, cap, step)
     sp = walk(segs, NG, W)
     if W > 1:
         merge(sp, segs, NG, len(lens))

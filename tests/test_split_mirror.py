@@ -66,6 +66,23 @@ def test_multi_token_splits(q_len, hq, hkv):
     M.check_plain(np.maximum(W.config_lens("llama3_8b_gqa", seed), q_len), hq_, hkv_, mb, q_len=q_len)
 
 
+def test_fused_step_splits():
+    """pa_decode_step: every sequence has one more chunk (its newest
+    position), so segments and cuts move."""
+    for hq, hkv in [(8, 8), (32, 8), (16, 1), (96, 12)]:
+        mb = max((n + 15) // 16 for n in EDGE_LENS)
+        for wgs in SPLITS:
+            M.check_plain(EDGE_LENS, hq, hkv, mb, override=wgs, step=True)
+    for name in ("llama3_8b_gqa", "llama2_7b", "long_splitk", "llama3_8b_gqa_tp8"):
+        hq, hkv, _, _, mb, seed = W.CONFIG_SHAPES[name]
+        M.check_plain(np.asarray(W.config_lens(name, seed)), hq, hkv, mb, step=True)
+    rng = np.random.default_rng(99)
+    for case in range(100):
+        lens = rng.integers(0, 300, size=int(rng.integers(1, 40)))
+        M.check_plain(lens, 8, 2, 20, block_size=int(rng.choice([8, 16, 32])),
+                      override=None if case % 2 else int(rng.integers(1, 200)), step=True)
+
+
 def test_seeded_random_plain_cases():
     rng = np.random.default_rng(2024)
     for case in range(300):
