@@ -96,7 +96,7 @@ def _one(means: dict, fragment: str) -> float:
     return hits[0]
 
 
-def record_traffic(prefix: str, workload: str, copy_bytes: int) -> int:
+def record_traffic(prefix: str, workload: str, copy_bytes: int, copy_prefix: str | None = None) -> int:
     """Write the decode call's per-launch HBM bytes into profiles/decode_traffic.json.
 
     Reads four rocprofv3 --pmc runs: {prefix}_fetch_decode and
@@ -106,11 +106,11 @@ def record_traffic(prefix: str, workload: str, copy_bytes: int) -> int:
     and the plan kernel when the call is sharing-aware. Each counter is scaled by what it reads for the copy,
     which moves exactly `copy_bytes` each way, so the units need not be known.
     """
-    def means(kind, counter):
-        return _counter_means(f"{prefix}_{kind}/run_counter_collection.csv", counter)
+    def means(kind, counter, pre=None):
+        return _counter_means(f"{pre or prefix}_{kind}/run_counter_collection.csv", counter)
 
-    fetch_copy = _one(means("fetch_copy", "FETCH_SIZE"), "probe_copy")
-    write_copy = _one(means("write_copy", "WRITE_SIZE"), "probe_copy")
+    fetch_copy = _one(means("fetch_copy", "FETCH_SIZE", copy_prefix), "probe_copy")
+    write_copy = _one(means("write_copy", "WRITE_SIZE", copy_prefix), "probe_copy")
     fd, wd = means("fetch_decode", "FETCH_SIZE"), means("write_decode", "WRITE_SIZE")
     f_scale, w_scale = copy_bytes / fetch_copy, copy_bytes / write_copy
     per = {}
@@ -341,6 +341,12 @@ def swap_probe(num_blocks: int, steps: int, dev) -> int:
     return 0
 
 
+def workload_name(args) -> str:
+    """Key of a workload and call kind in the traffic record."""
+    return (args.config + ("_shared" if args.shared else "") + ("_unfused" if args.unfused else "")
+            + (f"_bs{args.block_size}" if args.block_size != 16 else "") + (f"_q{args.q_len}" if args.q_len > 1 else ""))
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -371,12 +377,15 @@ def main(argv=None) -> int:
     ap.add_argument("--swap-blocks", type=int, default=0, metavar="N",
                     help="instead of the decode step: time swapping N blocks out to pinned host memory and in")
     ap.add_argument("--record-traffic", metavar="PREFIX",
-                    help="no GPU work: turn the rocprofv3 --pmc runs PREFIX_{fetch,write}_{decode,copy} "
-                         "into the traffic record for --config (copy size from --probe-copy)")
+                    help="no GPU work: turn the rocprofv3 --pmc runs PREFIX_{fetch,write}_decode and "
+                         "COPY_{fetch,write}_copy (COPY from --copy-prefix, default PREFIX) into the traffic "
+                         "record for the workload --config and the other flags name (copy size from --probe-copy)")
+    ap.add_argument("--copy-prefix", default=None,
+                    help="with --record-traffic: prefix of the copy probe's counter runs")
     args = ap.parse_args(argv)
     if args.record_traffic:
-        return record_traffic(args.record_traffic, args.config + ("_shared" if args.shared else ""),
-                              args.probe_copy or (1 << 30))
+        return record_traffic(args.record_traffic, workload_name(args), args.probe_copy or (1 << 30),
+                              args.copy_prefix)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -417,8 +426,7 @@ def main(argv=None) -> int:
         assert np.array_equal(want, b.slot_mapping), "new tokens are not at position n - 1 of their sequences"
     if args.config == "beam_cow" and args.block_size != 16:
         raise SystemExit("--block-size applies to the named single-step configs")
-    workload = args.config + ("_shared" if args.shared else "") + ("_unfused" if args.unfused else "") + \
-        (f"_bs{args.block_size}" if args.block_size != 16 else "")
+    workload = workload_name(args)
 
     def bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -556,7 +564,7 @@ def main(argv=None) -> int:
     flops = W.algorithmic_flops(b.context_lens, b.num_q_heads, b.head_size, q_len=args.q_len)
     achieved_tflops = flops / (dec_mean_us * 1e-6) / 1e12
     mfma_bound = flops / (PEAK_BF16_TFLOPS * 1e12) > decode_bytes / (PEAK_HBM_GBS * 1e9)
-    traffic = measured_traffic(workload) if not multi else None
+    traffic = measured_traffic(workload)
     if args.shared:
         kernel = "decode_shared call: share_plan_kernel + decode_kernel + merge_kernel"
     elif fused:
