@@ -839,6 +839,91 @@ __device__ __forceinline__ void finish_stream(const DecodeArgs &a, const Lane<NT
   }
 }
 
+// One query head per KV head, on the vector ALU (the launch's `vector`
+// path). Lane (c, grp) takes token c of the chunk: its score is the dot
+// product of q with the token's key over the lane's 32 head dims (8 at
+// 32j + 8*grp for each j, as loaded), summed over the token's four lanes.
+// Each lane keeps its own running max (base 2), sum and unnormalised output
+// over the tokens it sees (token c of every chunk), in the registers the
+// matrix-core path uses for its column (m_run, l_part, acc: dims 32j +
+// 8*grp + 4h + r in acc[2j + h][r]); vec_fold merges the 16 token lanes when
+// the piece ends. `live`: the lane's token lies before the limit (a stale
+// or NaN row past it is replaced by zeros).
+template <int NJ, int NT>
+__device__ __forceinline__ void vec_chunk(const DecodeArgs &a, const Lane<NT> &ln, Stream<NJ, NT> &st,
+                                          const u32x4_t (&K)[NJ], const u32x4_t (&V)[NJ], bool live) {
+  // The bf16 pairs come out of the 16-byte registers by shuffles of the
+  // 8-element vectors: a bit cast of a single extracted 32-bit element to a
+  // bf16 pair is compiled (hipcc, gfx950) into a read of element 0 for every
+  // element, so that form is not used.
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const bf16x8_t kb = __builtin_bit_cast(bf16x8_t, K[j]);
+    const bf16x8_t qb = __builtin_bit_cast(bf16x8_t, st.qv[0][j]);
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(kb, kb, 0, 1), __builtin_shufflevector(qb, qb, 0, 1), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(kb, kb, 2, 3), __builtin_shufflevector(qb, qb, 2, 3), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(kb, kb, 4, 5), __builtin_shufflevector(qb, qb, 4, 5), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(kb, kb, 6, 7), __builtin_shufflevector(qb, qb, 6, 7), s, false);
+  }
+  s += __shfl_xor(s, 16);
+  s += __shfl_xor(s, 32);
+  const float z = live ? s * a.scale_log2 : -INFINITY;
+  const float m_new = fmaxf(st.m_run[0], z);
+  const float m_use = m_new == -INFINITY ? 0.f : m_new;  // a lane that has seen nothing yet
+  const float alpha = fast_exp2(st.m_run[0] - m_use);
+  const float p = fast_exp2(z - m_use);
+  st.m_run[0] = m_new;
+  st.l_part[0] = st.l_part[0] * alpha + p;
+  if (alpha != 1.f) {
+#pragma unroll
+    for (int k = 0; k < 2 * NJ; ++k) st.acc[0][k] *= alpha;
+  }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t v = live ? V[j][w] : 0u;
+      st.acc[0][2 * j + (w >> 1)][2 * (w & 1)] += p * bf16_lo(v);
+      st.acc[0][2 * j + (w >> 1)][2 * (w & 1) + 1] += p * bf16_hi(v);
+    }
+}
+
+// Lane-to-lane exchange inside rows of 16 lanes (DPP).
+__device__ __forceinline__ float row_dpp(float x, int ctrl) {
+  switch (ctrl) {  // the control must be a constant
+    case 0: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xf, 0xf, true));
+    case 1: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xf, 0xf, true));
+    case 2: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xf, 0xf, true));
+    default: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x140, 0xf, 0xf, true));
+  }
+}
+
+// The vector path at a piece's end: merges the 16 token lanes of each row
+// (log-sum-exp weights, a butterfly over lane^1, lane^2 (quad permutes), the
+// half-row mirror and the row mirror, after which every lane of a row holds
+// the row's result), then leaves the state as the matrix-core path does:
+// running max, the sum counted once per column (grp 0), unnormalised output.
+template <int NJ, int NT>
+__device__ __forceinline__ void vec_fold(const Lane<NT> &ln, Stream<NJ, NT> &st) {
+  float m = st.m_run[0], l = st.l_part[0];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float mo = row_dpp(m, k), lo = row_dpp(l, k);
+    const float M = fmaxf(m, mo);
+    const float Mu = M == -INFINITY ? 0.f : M;
+    const float w1 = fast_exp2(m - Mu), w2 = fast_exp2(mo - Mu);
+    l = l * w1 + lo * w2;
+#pragma unroll
+    for (int i = 0; i < 2 * NJ; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st.acc[0][i][r] = st.acc[0][i][r] * w1 + row_dpp(st.acc[0][i][r], k) * w2;
+    m = M;
+  }
+  st.m_run[0] = m;
+  st.l_part[0] = ln.grp == 0 ? l : 0.f;
+}
+
 // kStep: the newest position's K/V row of this wavefront's KV head goes to
 // its slot in the cache: row (n - 1) % block_size of the physical block the
 // table names for position n - 1. Lanes of tile row 0 hold it (dims 32j +
@@ -917,7 +1002,7 @@ __device__ __forceinline__ void advance(const DecodeArgs &a, const Lane<NT> &ln,
 // Computes block i of P from (K, V) after starting the next block of the
 // stream loading into (Kn, Vn); finishes P at its end and moves to Q.
 // Returns false once the stream is done.
-template <int NJ, int NT, int M, int BS>
+template <int NJ, int NT, int M, int BS, bool VEC>
 __device__ __forceinline__ bool step(const int32_t *__restrict__ tables, const DecodeArgs &a, const Lane<NT> &ln,
                                      Walker &wk, Stream<NJ, NT> &st, u32x4_t (&K)[NJ], u32x4_t (&V)[NJ],
                                      u32x4_t (&Kn)[NJ], u32x4_t (&Vn)[NJ], uint16_t *lds) {
@@ -969,6 +1054,9 @@ __device__ __forceinline__ bool step(const int32_t *__restrict__ tables, const D
     if constexpr (M != kShared) return true;
     return cj < 0 ? 16 * t < P.ntok * a.group : (cj * a.group < 16 * (t + 1) && (cj + 1) * a.group > 16 * t);
   };
+  if constexpr (VEC) {
+    vec_chunk<NJ>(a, ln, st, K, V, pos_base + ln.c < vis);
+  } else {
   u32x2_t pb_hi[NT], pb_lo[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
@@ -1032,6 +1120,7 @@ __device__ __forceinline__ bool step(const int32_t *__restrict__ tables, const D
       }
     }
   }
+  }  // matrix-core path
 
   if constexpr (M == kStep) {
     if (fresh) stage_new<NJ, NT, M, BS>(tables, a, ln, st, lds, K, V);
@@ -1041,6 +1130,7 @@ __device__ __forceinline__ bool step(const int32_t *__restrict__ tables, const D
   st.i = nx;
   if constexpr (M == kShared) st.cc = cn;
   if (in_p) return true;
+  if constexpr (VEC) vec_fold<NJ>(ln, st);
   finish_piece<NJ, NT, M, defers<NT, BS>()>(a, ln, st, lds);
   if (!st.has_q) return false;
   advance<NJ, NT, M, BS>(a, ln, wk, st, lds);
@@ -1068,7 +1158,7 @@ __device__ __forceinline__ void no_merge(const DecodeArgs &a, int w, int tid) {
 // SIMD; with two tiles the wavefront may take the whole register file (arch
 // and accumulation registers). kWide runs two wavefronts per SIMD (a
 // workgroup of up to 8 column groups of one KV head), 256 registers each.
-template <int D, int NT, int M, int BS>
+template <int D, int NT, int M, int BS, bool VEC>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NT == 1 || M == kWide ? 2 : 1)))
 void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const int32_t *__restrict__ lens,
                    const ShareItem *__restrict__ items) {
@@ -1288,8 +1378,8 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
   } else {
     issue_seq<NJ, NT, M, BS>(tables, a, ln, st.P.s, st.P.off, st.P.n, st.P.L, st.hoff, KA, VA);
   }
-  while (step<NJ, NT, M, BS>(tables, a, ln, wk, st, KA, VA, KB, VB, q_lds) &&
-         step<NJ, NT, M, BS>(tables, a, ln, wk, st, KB, VB, KA, VA, q_lds)) {
+  while (step<NJ, NT, M, BS, VEC>(tables, a, ln, wk, st, KA, VA, KB, VB, q_lds) &&
+         step<NJ, NT, M, BS, VEC>(tables, a, ln, wk, st, KB, VB, KA, VA, q_lds)) {
   }
   finish_stream<NJ, NT, M, defers<NT, BS>()>(a, ln, st, q_lds);
 }
@@ -1590,11 +1680,11 @@ hipError_t allow_lds(Kernel kernel, size_t bytes) {
   return e;
 }
 
-template <int D, int NT, int M, int BS = 16>
+template <int D, int NT, int M, int BS = 16, bool VEC = false>
 hipError_t launch_decode_kernel(const DecodeArgs &args, size_t lds, hipStream_t stream) {
-  hipError_t e = allow_lds(decode_kernel<D, NT, M, BS>, lds);
+  hipError_t e = allow_lds(decode_kernel<D, NT, M, BS, VEC>, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_kernel<D, NT, M, BS>), dim3((unsigned)args.num_wgs),
+  hipLaunchKernelGGL((decode_kernel<D, NT, M, BS, VEC>), dim3((unsigned)args.num_wgs),
                      dim3(64 * (unsigned)args.heads_per_wg), lds, stream, args, args.block_tables,
                      args.context_lens, args.items);
   return hipGetLastError();
@@ -1602,12 +1692,24 @@ hipError_t launch_decode_kernel(const DecodeArgs &args, size_t lds, hipStream_t 
 
 template <int D>
 hipError_t launch_decode_d(const DecodeArgs &args, size_t lds, hipStream_t stream) {
+  // One query head per KV head: the vector path when the host chose it.
+  const bool vec = args.vector_path && args.num_cols == 1;
   if (args.k_new) {
+    if (vec) {
+      if (args.block_size == 8) return launch_decode_kernel<D, 1, kStep, 8, true>(args, lds, stream);
+      if (args.block_size == 32) return launch_decode_kernel<D, 1, kStep, 32, true>(args, lds, stream);
+      return launch_decode_kernel<D, 1, kStep, 16, true>(args, lds, stream);
+    }
     if (args.block_size == 8) return launch_decode_kernel<D, 1, kStep, 8>(args, lds, stream);
     if (args.block_size == 32) return launch_decode_kernel<D, 1, kStep, 32>(args, lds, stream);
     return launch_decode_kernel<D, 1, kStep>(args, lds, stream);
   }
   if (args.q_len == 1) {
+    if (vec) {
+      if (args.block_size == 8) return launch_decode_kernel<D, 1, kSingle, 8, true>(args, lds, stream);
+      if (args.block_size == 32) return launch_decode_kernel<D, 1, kSingle, 32, true>(args, lds, stream);
+      return launch_decode_kernel<D, 1, kSingle, 16, true>(args, lds, stream);
+    }
     if (args.block_size == 8) return launch_decode_kernel<D, 1, kSingle, 8>(args, lds, stream);
     if (args.block_size == 32) return launch_decode_kernel<D, 1, kSingle, 32>(args, lds, stream);
     return launch_decode_kernel<D, 1, kSingle>(args, lds, stream);

@@ -61,6 +61,24 @@ int32_t decode_wgs(int64_t num_seqs, int32_t num_head_groups, int32_t heads_per_
   return (int32_t)w;
 }
 
+// Which ALU computes a single-token decode with one query head per KV head.
+// The matrix-core tiles carry 16 query-head columns, of which one is live
+// here; the vector path computes the one column on the vector ALU. Measured
+// on the MHA layer (64 sequences, 32/32 heads), the two run in the same time
+// (decode kernel 216.1 against 216.3 us; the call is bound by memory), so
+// the matrix cores, which do not win, are not used for it.
+// PA_DECODE_PATH=mfma|vector overrides the default (tests, tuning).
+constexpr bool kVectorPathDefault = true;
+
+int32_t use_vector_path(int32_t group, int32_t q_len) {
+  if (group != 1 || q_len != 1) return 0;
+  if (const char *env = getenv("PA_DECODE_PATH")) {
+    if (!strcmp(env, "vector")) return 1;
+    if (!strcmp(env, "mfma")) return 0;
+  }
+  return kVectorPathDefault ? 1 : 0;
+}
+
 // KV heads per workgroup (one wavefront each): the largest divisor of
 // num_kv_heads that is <= 4.
 int32_t heads_per_workgroup(int32_t num_kv_heads) {
@@ -282,6 +300,7 @@ int decode_impl(const pa_kv_cache *cache, const void *q, const int32_t *block_ta
   a.rec_cols = plan.rec_cols;
   a.num_wgs = plan.num_wgs;
   a.scale_log2 = scale * 1.44269504088896340736f;
+  a.vector_path = use_vector_path(a.group, q_len);
 
   hipError_t e = pa::launch_decode(a, cache->head_size, hs);
   if (owned) {

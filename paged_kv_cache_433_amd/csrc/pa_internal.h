@@ -66,6 +66,7 @@ struct DecodeArgs {
   const ShareItem *items;        // [num_seqs + 1]: segments, then a sentinel holding the total units
   const ShareHeader *share;
   int32_t block_size;            // tokens per cache block: 8, 16 or 32 (16 unless q_len == 1 and no sharing)
+  int32_t vector_path;           // one query head per KV head: compute on the vector ALU, not matrix cores
 };
 
 // Arguments of the sharing-aware plan kernel.
