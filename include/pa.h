@@ -125,6 +125,14 @@ typedef struct pa_kv_cache {
  * reproducible bit for bit for the same sizes and context lengths (no
  * atomics; the cut points depend only on those).
  *
+ * K and V rows at positions < n must be finite: the kernels multiply every
+ * value by weights some of which are zero, and an infinity times zero is
+ * NaN, which would spread to other head dims. Rows past a context length
+ * (stale tail slots) may hold anything, NaN included; they are never read
+ * into the sums. With one query head per KV head the arithmetic runs on the
+ * vector ALU, otherwise on matrix cores (PA_DECODE_PATH=mfma|vector in the
+ * environment overrides the first choice, for tests and tuning).
+ *
  * Errors: PA_ERR_NULL (cache, cache->k_cache/v_cache, q, block_tables,
  * context_lens or out NULL while num_seqs > 0), PA_ERR_SHAPE (negative
  * counts, max_blocks_per_seq < 1, num_q_heads % num_kv_heads != 0),
