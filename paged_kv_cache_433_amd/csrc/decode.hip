@@ -139,6 +139,43 @@ __device__ __forceinline__ u32x4_t load16(const uint16_t *p) {
 
 __device__ __forceinline__ int clamp_len(int n, int cap) { return n < 0 ? 0 : (n > cap ? cap : n); }
 
+// The two values of lanes i and i ^ 16 (lane_pair16) or i and i ^ 32
+// (lane_pair32), lower lane first, by the gfx950 lane-swap instructions
+// (vector ALU; no LDS round trip). Both lanes of a pair get the same two
+// values in the same order, so a max or a sum of them is the same in both.
+// The instruction swaps rows between two registers that both hold x; it is
+// written as an asm statement (a register-only ALU instruction, preceded by
+// the two wait states a lane swap needs after a vector write of its
+// sources). Through the compiler builtin, hipcc (gfx950) treated the two
+// results as one value and dropped the max of them.
+__device__ __forceinline__ void lane_pair16(float x, float &lo, float &hi) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  lo = a;
+  hi = b;
+}
+__device__ __forceinline__ void lane_pair32(float x, float &lo, float &hi) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  lo = a;
+  hi = b;
+}
+
+// Max and sum over the four lanes c, c + 16, c + 32, c + 48 (the four
+// lane groups of a 16-wide MFMA column or of a token's head dims).
+__device__ __forceinline__ float max_over_groups(float x) {
+  float a, b;
+  lane_pair16(x, a, b);
+  lane_pair32(fmaxf(a, b), a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float sum_over_groups(float x) {
+  float a, b;
+  lane_pair16(x, a, b);
+  lane_pair32(a + b, a, b);
+  return a + b;
+}
+
 // Workgroup w's first unit, w <= E: floor(w * U / E). With E <= U every
 // range is non-empty.
 __device__ __forceinline__ long long range_lo(long long w, long long U, long long E) {
@@ -744,8 +781,7 @@ __device__ __forceinline__ void finish_piece(const DecodeArgs &a, const Lane<NT>
   const int g = kv_head<M>(ln, P.hg);
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    float l = st.l_part[t] + __shfl_xor(st.l_part[t], 16);
-    l += __shfl_xor(l, 32);
+    const float l = sum_over_groups(st.l_part[t]);
     // kShared: a segment serves ntok members (their q rows from qrow on).
     const bool keep = M == kShared ? ln.col_ok[t] && ln.col[t] < P.ntok * a.group : ln.col_ok[t];
     if (whole) {
@@ -866,8 +902,7 @@ __device__ __forceinline__ void vec_chunk(const DecodeArgs &a, const Lane<NT> &l
     s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(kb, kb, 4, 5), __builtin_shufflevector(qb, qb, 4, 5), s, false);
     s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(kb, kb, 6, 7), __builtin_shufflevector(qb, qb, 6, 7), s, false);
   }
-  s += __shfl_xor(s, 16);
-  s += __shfl_xor(s, 32);
+  s = sum_over_groups(s);
   const float z = live ? s * a.scale_log2 : -INFINITY;
   const float m_new = fmaxf(st.m_run[0], z);
   const float m_use = m_new == -INFINITY ? 0.f : m_new;  // a lane that has seen nothing yet
@@ -1083,8 +1118,7 @@ __device__ __forceinline__ bool step(const int32_t *__restrict__ tables, const D
     for (int r = 0; r < 4; ++r)
       z[r] = (ln.grp * 4 + r < CH && pos0 + r < lim) ? sc[r] * a.scale_log2 : -INFINITY;
     float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_over_groups(mx);
     // With one new token, position b*16 is always visible, so the max is
     // finite. With several, a column may see nothing in this block yet.
     const float m_new = fmaxf(st.m_run[t], mx);
