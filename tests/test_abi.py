@@ -241,3 +241,22 @@ def test_noalloc_argument_errors(L, monkeypatch):
     assert need > _lib.PA_NOALLOC_SCRATCH_BYTES
     assert call(d, S=64, mb=256) == _lib.PA_ERR_WORKSPACE
     assert "static" in _lib.last_error()
+
+
+def test_step_argument_errors(L):
+    """pa_decode_step checks what pa_decode checks, plus its new K/V rows,
+    on the host; its workspace covers the extra chunk of each sequence."""
+    def call(d, k=P, v=P, S=2, hq=32, out=P):
+        return L.pa_decode_step(ctypes.byref(d) if d is not None else None, P, k, v, P, P, S, hq, 8, 1.0, out,
+                                None, 0, None)
+
+    assert call(None) == _lib.PA_ERR_NULL
+    assert call(desc(), k=None) == _lib.PA_ERR_NULL
+    assert call(desc(), v=None) == _lib.PA_ERR_NULL
+    assert call(desc(), k=ctypes.c_void_p(0x3004)) == _lib.PA_ERR_UNSUPPORTED
+    assert call(desc(dtype=1)) == _lib.PA_ERR_UNSUPPORTED
+    assert call(desc(), hq=12) == _lib.PA_ERR_SHAPE
+    assert call(desc(), S=0, k=None, v=None) == _lib.PA_OK
+    d = desc()
+    assert L.pa_decode_step_workspace_bytes(ctypes.byref(d), 256, 32, 256) >= \
+        L.pa_decode_workspace_bytes(ctypes.byref(d), 256, 32, 256)
