@@ -52,7 +52,9 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 CACHE_NOTES = {
     "tiny_mha": "warm: the whole cache fits in L2",
     "beam_cow": "warm in part: the 4 beams of a prompt read its shared blocks, so some logical bytes come from cache",
-    "beam_cow_shared": "cold in part: every distinct K/V byte is read once per call (about 0.37 GB; the MALL is 256 MB)",
+    "beam_cow_shared": "cold in part: a prompt's blocks are read once per group of beams, beams forked from the same "
+                       "parent read its history each (about 0.38 GB; the MALL is 256 MB)",
+    "beam_cow_tree": "cold in part: every distinct block is read once per call (about 0.35 GB; the MALL is 256 MB)",
 }
 
 
@@ -140,10 +142,11 @@ def record_traffic(prefix: str, workload: str, copy_bytes: int, copy_prefix: str
 
 
 def _oracle_worker(task):
-    """One process of the CPU baseline: run the oracle on whole sequences
-    (whole groups, for sharing-aware decode) of its share of the seeded
-    order, cycling, for `seconds` with BLAS on one thread. The cache arrays
-    are memory-mapped read-only from files the parent wrote, so the workers
+    """One process of the CPU baseline: run the oracle on whole units of its
+    share of the seeded order, cycling, for `seconds` with BLAS on one
+    thread. A unit is a sequence, or (sharing-aware decode) a group or a run
+    of sequences that share leading blocks. The cache arrays are
+    memory-mapped read-only from files the parent wrote, so the workers
     share one copy. Returns (units done, seconds)."""
     from threadpoolctl import threadpool_limits
 
@@ -151,38 +154,39 @@ def _oracle_worker(task):
 
     import oracle
 
-    (paths, shape, q, tables, lens, scale, q_len, groups, order, seconds) = task
+    (paths, shape, q, tables, lens, scale, q_len, kind, units, order, seconds) = task
     kc = np.memmap(paths[0], dtype=np.uint16, mode="r", shape=shape)
     vc = np.memmap(paths[1], dtype=np.uint16, mode="r", shape=shape)
     done = []
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         while time.perf_counter() - t0 < seconds:
-            for s in order:
-                if groups is not None:
-                    starts, shared = groups
-                    lo, hi = int(starts[s]), int(starts[s + 1])
-                    oracle.decode_shared(q[lo:hi], kc, vc, tables[lo:hi], lens[lo:hi], [0, hi - lo], [shared[s]],
+            for u in order:
+                lo, hi, shared = units[u]
+                if kind == "groups":
+                    oracle.decode_shared(q[lo:hi], kc, vc, tables[lo:hi], lens[lo:hi], [0, hi - lo], [shared],
                                          scale)
+                elif kind == "tree":  # true declarations: the plain decode of the run
+                    oracle.decode(q[lo:hi], kc, vc, tables[lo:hi], lens[lo:hi], scale)
                 elif q_len > 1:
-                    oracle.decode_multi(q[s:s + 1], kc, vc, tables[s:s + 1], lens[s:s + 1], scale)
+                    oracle.decode_multi(q[lo:hi], kc, vc, tables[lo:hi], lens[lo:hi], scale)
                 else:
-                    oracle.decode_sequence(q[s], kc, vc, tables[s], lens[s], scale)
-                done.append(int(s))
+                    oracle.decode_sequence(q[lo], kc, vc, tables[lo], lens[lo], scale)
+                done.append(int(u))
                 if time.perf_counter() - t0 >= seconds:
                     break
         dt = time.perf_counter() - t0
     return done, dt
 
 
-def _time_oracle(batch, paths, order, seconds: float, procs: int, groups=None):
+def _time_oracle(batch, paths, order, seconds: float, procs: int, kind, units):
     """The oracle on `procs` worker processes (each a slice of `order`), or
     in this process when procs == 1; returns (units done, seconds)."""
     import multiprocessing as mp
     from concurrent.futures import ProcessPoolExecutor
 
     shape = batch.k_cache.shape
-    tasks = [(paths, shape, batch.q, batch.block_tables, batch.context_lens, batch.scale, batch.q_len, groups,
+    tasks = [(paths, shape, batch.q, batch.block_tables, batch.context_lens, batch.scale, batch.q_len, kind, units,
               order[i::procs], seconds) for i in range(procs)]
     if procs == 1:
         res = [_oracle_worker(tasks[0])]
@@ -198,13 +202,15 @@ def _time_oracle(batch, paths, order, seconds: float, procs: int, groups=None):
     return done, max(r[1] for r in res)
 
 
-def cpu_baseline(batch, seconds: float, groups=None):
-    """Time the float64 oracle on whole sequences (whole groups, with
-    `groups`), in a seeded order (cycling through the batch), for `seconds`:
-    once on one worker process per core this process may use (the oracle is
-    serial numpy, so the host's cores work through separate sequences), and
-    once on a single thread; rate in the metric's unit (algorithmic GB/s).
-    The all-cores run is the reported value."""
+def cpu_baseline(batch, seconds: float, sharing=None):
+    """Time the float64 oracle on whole units of the batch in a seeded order
+    (cycling through it), for `seconds`: once on one worker process per
+    core this process may use (the oracle is serial numpy, so the host's
+    cores work through separate units), and once on a single thread; rate
+    in the metric's unit (algorithmic GB/s). A unit is a sequence, or with
+    `sharing` ("groups", starts, shared) a group, or with ("tree", sprev) a
+    run of sequences each sharing leading blocks with the one before. The
+    all-cores run is the reported value."""
     import shutil
     import tempfile
 
@@ -217,8 +223,30 @@ def cpu_baseline(batch, seconds: float, groups=None):
     if len(batch.cow_pairs):
         oracle.copy_blocks(kc, vc, batch.cow_pairs)
     oracle.reshape_and_cache(kc, vc, batch.new_k, batch.new_v, batch.slot_mapping)
-    units = batch.num_seqs if groups is None else len(groups[1])
-    order = np.random.default_rng(0).permutation(units)
+    S, mb = batch.num_seqs, batch.max_blocks_per_seq
+    kind = sharing[0] if sharing else "plain"
+    if kind == "groups":
+        starts, shared = sharing[1], sharing[2]
+        units = [(int(starts[g]), int(starts[g + 1]), int(shared[g])) for g in range(len(shared))]
+    elif kind == "tree":
+        sprev = sharing[1]
+        cuts = list(np.flatnonzero(W.chain_sharing(batch.context_lens, sprev, mb) == 0)) + [S]
+        units = [(int(cuts[i]), int(cuts[i + 1]), 0) for i in range(len(cuts) - 1)]
+    else:
+        units = [(s, s + 1, 0) for s in range(S)]
+
+    def unit_bytes(u):
+        lo, hi, shared = units[u]
+        n = batch.context_lens[lo:hi]
+        if kind == "groups":
+            return W.shared_algorithmic_bytes(n, [0, hi - lo], [shared], mb, batch.num_q_heads,
+                                              batch.num_kv_heads, batch.head_size)
+        if kind == "tree":
+            return W.tree_algorithmic_bytes(n, sprev[lo:hi], mb, batch.num_q_heads, batch.num_kv_heads,
+                                            batch.head_size)
+        return W.algorithmic_bytes(n, batch.num_q_heads, batch.num_kv_heads, batch.head_size, q_len=batch.q_len)
+
+    order = np.random.default_rng(0).permutation(len(units))
     # The host share this process may use: its CPU affinity, capped by the
     # thread count the environment sets for OpenMP/BLAS.
     cores = len(os.sched_getaffinity(0))
@@ -231,34 +259,23 @@ def cpu_baseline(batch, seconds: float, groups=None):
         kc.tofile(paths[0])
         vc.tofile(paths[1])
         for procs in (cores, 1):
-            done, dt = _time_oracle(batch, paths, order, seconds, procs, groups)
-            if groups is None:
-                lens = batch.context_lens[done]
-                nbytes = W.algorithmic_bytes(lens, batch.num_q_heads, batch.num_kv_heads, batch.head_size,
-                                             q_len=batch.q_len)
-                seqs = len(done)
-            else:
-                starts, shared = groups
-                nbytes, seqs, toks = 0, 0, 0
-                for g in done:
-                    lo, hi = int(starts[g]), int(starts[g + 1])
-                    nbytes += W.shared_algorithmic_bytes(batch.context_lens[lo:hi], [0, hi - lo], [shared[g]],
-                                                         batch.max_blocks_per_seq, batch.num_q_heads,
-                                                         batch.num_kv_heads, batch.head_size)
-                    seqs += hi - lo
-                    toks += int(batch.context_lens[lo:hi].sum())
-                lens = np.array([toks])
-            res[procs] = (seqs, int(lens.sum()), dt, nbytes / dt / 1e9, seqs / dt)
+            done, dt = _time_oracle(batch, paths, order, seconds, procs, kind, units)
+            nbytes = sum(unit_bytes(u) for u in done)
+            seqs = sum(units[u][1] - units[u][0] for u in done)
+            tokens = sum(int(batch.context_lens[units[u][0]:units[u][1]].sum()) for u in done)
+            res[procs] = (seqs, tokens, dt, nbytes / dt / 1e9, seqs / dt)
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
     n, tokens, dt, gbps, sps = res[cores]
+    what = {"plain": "", "groups": " of whole groups (decode_shared)",
+            "tree": " of whole runs of sequences sharing prefixes (decode_shared_tree)"}[kind]
     return {
         "value": round(gbps, 4),
         "unit": "GB/s",
         "cores": cores,
         "kind": "oracle",
         "sample": (f"{n} sequence-steps of the {batch.num_seqs}-sequence batch, taken in a seeded "
-                   f"order{' of whole groups (decode_shared)' if groups is not None else ''} ({tokens} tokens), "
+                   f"order{what} ({tokens} tokens), "
                    f"float64 numpy oracle on {cores} worker processes (one per core, BLAS on one thread "
                    f"each, cache arrays shared read-only), {dt:.1f} s"),
         "seq_steps_per_s": round(sps, 3),
@@ -343,7 +360,8 @@ def swap_probe(num_blocks: int, steps: int, dev) -> int:
 
 def workload_name(args) -> str:
     """Key of a workload and call kind in the traffic record."""
-    return (args.config + ("_shared" if args.shared else "") + ("_unfused" if args.unfused else "")
+    return (args.config + {None: "", "groups": "_shared", "tree": "_tree"}[args.shared]
+            + ("_unfused" if args.unfused else "")
             + (f"_bs{args.block_size}" if args.block_size != 16 else "") + (f"_q{args.q_len}" if args.q_len > 1 else ""))
 
 
@@ -363,9 +381,11 @@ def main(argv=None) -> int:
                     help="single new token: scatter with pa_reshape_and_cache, then pa_decode (two launches), "
                          "instead of the fused step (pa_decode_step: the new token is attended from its K/V "
                          "row and written to its slot in the decode launch)")
-    ap.add_argument("--shared", action="store_true",
-                    help="beam_cow only: decode with pa_decode_shared, reading a prompt's shared blocks once "
-                         "for its beams (the sharing is read back from the block tables)")
+    ap.add_argument("--shared", nargs="?", const="groups", choices=("groups", "tree"), default=None,
+                    help="beam_cow only: sharing-aware decode with the sharing read back from the block tables. "
+                         "groups (the default): pa_decode_shared, a prompt's shared blocks read once for its "
+                         "beams; tree: pa_decode_shared_tree over the beams in depth-first order, so beams "
+                         "that forked from the same parent also read its history once")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="seconds of oracle work per CPU-baseline run (two runs: all cores, one thread)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -411,6 +431,9 @@ def main(argv=None) -> int:
             raise SystemExit("--q-len applies to the named single-step configs")
         wl = W.BeamSearchWorkload()
         b = wl.step()
+        if args.shared == "tree":
+            # the scheduler lists the beams depth first in their prefix tree
+            b = W.permuted(b, W.tree_order(b.block_tables, b.context_lens))
     else:
         if args.shared:
             raise SystemExit("--shared applies to the beam_cow workload")
@@ -444,13 +467,21 @@ def main(argv=None) -> int:
     logical_bytes = W.algorithmic_bytes(b.context_lens, b.num_q_heads, b.num_kv_heads, b.head_size,
                                         block_size=b.block_size, q_len=args.q_len)
     decode_bytes = logical_bytes
-    if args.shared:
+    sharing = None
+    if args.shared == "tree":
+        sprev = W.declared_chain(b.block_tables, b.context_lens)
+        sprev_t = torch.from_numpy(sprev).to(dev)
+        decode_bytes = W.tree_algorithmic_bytes(b.context_lens, sprev, b.max_blocks_per_seq, b.num_q_heads,
+                                                b.num_kv_heads, b.head_size)
+        sharing = ("tree", sprev)
+    elif args.shared:
         gstarts = W.consecutive_groups(b.num_seqs, wl.beams)
         gshared = W.declared_sharing(b.block_tables, b.context_lens, gstarts)
         gstarts_t = torch.from_numpy(gstarts).to(dev)
         gshared_t = torch.from_numpy(gshared).to(dev)
         decode_bytes = W.shared_algorithmic_bytes(b.context_lens, gstarts, gshared, b.max_blocks_per_seq,
                                                   b.num_q_heads, b.num_kv_heads, b.head_size)
+        sharing = ("groups", gstarts, gshared)
     if fused:
         decode_bytes += W.step_write_bytes(b.context_lens, b.num_kv_heads, b.head_size)
         step_bytes = decode_bytes
@@ -462,6 +493,8 @@ def main(argv=None) -> int:
     def run_decode():
         if fused:
             pa.decode_step(q, new_k, new_v, kc, vc, tables, lens, scale, out=out)
+        elif args.shared == "tree":
+            pa.decode_shared_tree(q, kc, vc, tables, lens, sprev_t, scale, out=out)
         elif args.shared:
             pa.decode_shared(q, kc, vc, tables, lens, gstarts_t, gshared_t, scale, out=out)
         elif multi:
@@ -565,7 +598,9 @@ def main(argv=None) -> int:
     achieved_tflops = flops / (dec_mean_us * 1e-6) / 1e12
     mfma_bound = flops / (PEAK_BF16_TFLOPS * 1e12) > decode_bytes / (PEAK_HBM_GBS * 1e9)
     traffic = measured_traffic(workload)
-    if args.shared:
+    if args.shared == "tree":
+        kernel = "decode_shared_tree call: share_plan_kernel + decode_kernel + merge_kernel"
+    elif args.shared:
         kernel = "decode_shared call: share_plan_kernel + decode_kernel + merge_kernel"
     elif fused:
         kernel = "decode_step call (new tokens attended and written in the launch): decode_kernel + merge_kernel"
@@ -598,6 +633,7 @@ def main(argv=None) -> int:
             "q_len": args.q_len,
             "step": ("copy_blocks + " if pairs is not None else "")
                     + ("reshape_and_cache + decode_multi" if multi else
+                       "reshape_and_cache + decode_shared_tree" if args.shared == "tree" else
                        "reshape_and_cache + decode_shared" if args.shared else
                        "decode_step (fused scatter and decode)" if fused else "reshape_and_cache + decode"),
             "parallelism": "single GPU",
@@ -643,7 +679,7 @@ def main(argv=None) -> int:
         rec["config"]["distinct_block_kv_bytes"] = int(len(used)) * 2 * b.block_size * b.num_kv_heads * b.head_size * 2
     if not args.no_cpu_baseline:
         print(f"[bench] cpu baseline (~{2 * args.cpu_seconds:.0f} s)", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(b, args.cpu_seconds, (gstarts, gshared) if args.shared else None)
+        rec["cpu_baseline"] = cpu_baseline(b, args.cpu_seconds, sharing)
     print(json.dumps(rec), flush=True)
     return 0
 

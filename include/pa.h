@@ -294,6 +294,52 @@ size_t pa_decode_shared_workspace_bytes(const pa_kv_cache *cache, int32_t num_se
                                         int32_t max_blocks_per_seq, int32_t num_groups);
 
 /*
+ * pa_decode_shared_tree - pa_decode for a batch whose sequences form a tree
+ * of shared prefixes, listed depth first, each declaring the leading table
+ * entries it holds in common with the sequence before it. Beams hold the
+ * prompt in common and, past it, the history of the beam each forked from:
+ * after a step, beams that picked the same parent hold every full block of
+ * that parent ("vLLM: Anatomy and Mechanisms of High-Throughput LLM
+ * Inference", section "Memory Sharing via Copy-on-Write (CoW)"); cached
+ * prompt prefixes form such a tree as well (same page, section "Prefix
+ * Caching"). Listed depth first (for example sorted by their table rows),
+ * the sequences below any node are consecutive, and what sequences i .. k
+ * hold in common is the least of the declarations of i+1 .. k. A block is
+ * then read from HBM once for each run of up to
+ * 32 / (num_q_heads / num_kv_heads) consecutive sequences that hold it,
+ * where pa_decode_shared shares only one prefix per group.
+ *
+ *   shared_prev  int32 [num_seqs], device memory: shared_prev[i] is the
+ *                number of leading table entries that sequence i has in
+ *                common with sequence i - 1. shared_prev[0] is ignored.
+ * Which blocks are read:
+ *   - Sequence i > 0 shares e_i = min(shared_prev[i],
+ *     context_lens[i] / block_size, context_lens[i-1] / block_size) blocks
+ *     with sequence i - 1 (whole blocks both fill), clamped to
+ *     0..max_blocks_per_seq; negative declarations count as 0.
+ *   - Sharing is by 16-token chunks of those blocks: with 8-token blocks an
+ *     odd e_i leaves its last shared block to sequence i's own reads.
+ *   - Each sequence reads the chunks it does not share with the one before
+ *     it through its own table, for itself and for every later sequence
+ *     whose shared chunks reach them without a break.
+ * When every declaration is true, the result is pa_decode's up to rounding
+ * (the sums run in a different order). A false declaration makes the
+ * outputs of the sequences after it unspecified; every read still goes
+ * through a table row of the batch, with the usual clamping of block ids.
+ * Limits, other arguments, layouts and errors are those of pa_decode_shared,
+ * plus PA_ERR_NULL for shared_prev == NULL when num_seqs > 0. The workspace
+ * has the size pa_decode_shared_tree_workspace_bytes returns.
+ */
+int pa_decode_shared_tree(const pa_kv_cache *cache, const void *q, const int32_t *block_tables,
+                          const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                          int32_t max_blocks_per_seq, const int32_t *shared_prev, float scale, void *out,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes of pa_decode_shared_tree (0 on invalid arguments or num_seqs == 0). */
+size_t pa_decode_shared_tree_workspace_bytes(const pa_kv_cache *cache, int32_t num_seqs, int32_t num_q_heads,
+                                             int32_t max_blocks_per_seq);
+
+/*
  * pa_reshape_and_cache - write each new token's K and V into its physical
  * slot before attention runs (the slot the block manager assigned on demand:
  * "vLLM: Anatomy and Mechanisms", section "Block-Level Management"; the

@@ -1,6 +1,7 @@
 """MI355X (gfx950) paged KV-cache decode: HIP kernels behind a C ABI.
 
-``decode``, ``decode_step``, ``decode_noalloc``, ``decode_multi``, ``decode_shared``, ``reshape_and_cache``,
+``decode``, ``decode_step``, ``decode_noalloc``, ``decode_multi``, ``decode_shared``, ``decode_shared_tree``,
+``reshape_and_cache``,
 ``copy_blocks`` and ``swap_blocks`` call libpa.so (built
 with ``python -m paged_kv_cache_433_amd.build``); the library is loaded on
 first use and a missing build raises. ``workloads`` makes seeded inputs.
@@ -14,6 +15,8 @@ from .ops import (  # noqa: F401
     decode_noalloc,
     decode_multi_workspace_bytes,
     decode_shared,
+    decode_shared_tree,
+    decode_shared_tree_workspace_bytes,
     decode_step,
     decode_shared_workspace_bytes,
     decode_workspace_bytes,

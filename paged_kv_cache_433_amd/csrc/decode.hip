@@ -355,14 +355,14 @@ __device__ __forceinline__ int kv_head(const Lane<NT> &ln, int hg) {
   return M == kWide ? hg : hg * ln.HG + ln.wave;
 }
 
-// kShared: where a block of a segment comes from. A segment is one or more
-// members of a group: first the group's shared blocks (read through the
-// first member's table, every column live), then each member's own blocks
-// past them (its own table, only its columns live).
+// kShared: one chunk of a segment's stream: read through member j's table
+// row (or the segment's `row` for the first member's chunks before b0), and
+// seen by members j .. e.
 struct Cursor {
-  int j;    // -1: the shared blocks; else the member whose own blocks these are
-  int b;    // logical block
-  int n;    // positions < n are visible
+  int j;    // member reading the chunk
+  int e;    // last member that sees it
+  int b;    // chunk
+  int n;    // member j's context length
   int row;  // table row read
 };
 
@@ -378,10 +378,10 @@ struct Stream {
   float m_run[NT];       // running max of base-2 logits, per column
   float l_part[NT];      // this lane's share of the running sum
   f32x4_t acc[NT][2 * NJ];
-  // kShared: cursor of block i of P, and the members' context lengths of
-  // P's and Q's segments (lane j: member j; 0 past the last member).
+  // kShared: cursor of block i of P, and the member records of P's and Q's
+  // segments (lane j: member j).
   Cursor cc;
-  int lv_p, lv_q;
+  int2 mv_p, mv_q;
   // Launches that defer (defers()): the first piece's partial record when that piece is
   // cut, and the workgroup's merge record. Both are stored after the stream
   // ends, not when the first piece ends: the wait for every later block's
@@ -527,40 +527,51 @@ __device__ __forceinline__ int block_id(const int32_t *__restrict__ tables, cons
   return (uint32_t)id < pool32 ? id : 0;
 }
 
-// kShared: the context lengths of a segment's members (clamped), lane j
-// holding member j's; lanes past the last member read 0.
-__device__ __forceinline__ int member_lens(const int32_t *__restrict__ lens, const Piece &p, int cap, int lane) {
+// kShared: the plan's records of a segment's members, lane j holding member
+// j's: its context length (x) and the chunks before its own (y), those it
+// holds in common with member j - 1. Lanes past the last member read {0, 0}.
+// y is clamped to the member's chunks, so no count below goes negative.
+__device__ __forceinline__ int2 member_info(const int32_t *__restrict__ members, const Piece &p, int lane) {
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<int32_t *>(lens + p.qrow), 0, p.ntok * (int)sizeof(int32_t), kRawBufferWord3);
-  return clamp_len((int)__builtin_amdgcn_raw_buffer_load_b32(r, lane * (int)sizeof(int32_t), 0, 0), cap);
+      const_cast<int32_t *>(members + 2 * (size_t)p.qrow), 0, p.ntok * 2 * (int)sizeof(int32_t), kRawBufferWord3);
+  const int n = max((int)__builtin_amdgcn_raw_buffer_load_b32(r, lane * 8, 0, 0), 0);
+  const int y = (int)__builtin_amdgcn_raw_buffer_load_b32(r, lane * 8 + 4, 0, 0);
+  return int2{n, min(max(y, 0), (n + kBlock - 1) >> 4)};
 }
 
-// kShared: cursor of the segment's block at unit offset p.off (the piece's
-// first block). Every member fills the b0 shared blocks, so each member owns
-// ceil(n_j / 16) - b0 >= 0 blocks after them.
-__device__ __forceinline__ Cursor seg_first(const Piece &p, int lv) {
+// kShared: the cursor of member j's chunk b. The members after j that hold
+// it are those up to the first whose own chunks begin at or before b (a
+// ballot over the lanes of the members' records).
+__device__ __forceinline__ Cursor seg_at(const Piece &p, int j, int b, int nj, int2 mv, int lane) {
+  const unsigned long long stop = __builtin_amdgcn_ballot_w64(lane > j && lane < p.ntok && mv.y <= b);
+  const int e = stop ? (int)__builtin_ctzll(stop) - 1 : p.ntok - 1;
+  return Cursor{j, e, b, nj, b < p.b0 ? p.row : p.qrow + j};
+}
+
+// kShared: cursor of the segment's chunk at unit offset p.off (the piece's
+// first). Member j contributes its chunks from y_j on.
+__device__ __forceinline__ Cursor seg_first(const Piece &p, int2 mv, int lane) {
   int r = p.off;
-  if (r < p.b0) return Cursor{-1, r, p.b0 * kBlock, p.row};
-  r -= p.b0;
-  Cursor c{-1, 0, 0, p.row};
-  for (int j = 0; j < p.ntok; ++j) {
-    const int nj = __builtin_amdgcn_readlane(lv, j);
-    const int lj = ((nj + kBlock - 1) >> 4) - p.b0;
-    c = Cursor{j, p.b0 + r, nj, p.qrow + j};
+  int j = 0, nj = 0, yj = 0;
+  for (; j < p.ntok; ++j) {
+    nj = __builtin_amdgcn_readlane(mv.x, j);
+    yj = __builtin_amdgcn_readlane(mv.y, j);
+    const int lj = ((nj + kBlock - 1) >> 4) - yj;
     if (r < lj) break;
     r -= lj;
   }
-  return c;
+  if (j == p.ntok) --j;  // past the segment's end: not reached inside a piece
+  return seg_at(p, j, yj + r, nj, mv, lane);
 }
 
-// kShared: cursor of the segment's block after c (the same member's next
-// block, else the next member with blocks of its own).
-__device__ __forceinline__ Cursor seg_next(const Piece &p, const Cursor &c, int lv) {
-  const int end = c.j < 0 ? p.b0 : (c.n + kBlock - 1) >> 4;
-  if (c.b + 1 < end) return Cursor{c.j, c.b + 1, c.n, c.row};
+// kShared: cursor of the segment's chunk after c (the same member's next
+// chunk, else the next member's first own chunk).
+__device__ __forceinline__ Cursor seg_next(const Piece &p, const Cursor &c, int2 mv, int lane) {
+  if (c.b + 1 < ((c.n + kBlock - 1) >> 4)) return seg_at(p, c.j, c.b + 1, c.n, mv, lane);
   for (int j = c.j + 1; j < p.ntok; ++j) {
-    const int nj = __builtin_amdgcn_readlane(lv, j);
-    if (((nj + kBlock - 1) >> 4) > p.b0) return Cursor{j, p.b0, nj, p.qrow + j};
+    const int nj = __builtin_amdgcn_readlane(mv.x, j);
+    const int yj = __builtin_amdgcn_readlane(mv.y, j);
+    if (((nj + kBlock - 1) >> 4) > yj) return seg_at(p, j, yj, nj, mv, lane);
   }
   return c;  // past the segment's end: not reached inside a piece
 }
@@ -697,11 +708,10 @@ __device__ __forceinline__ void issue_chunk(const int32_t *__restrict__ tables, 
   }
 }
 
-// kShared: starts the loads of the segment's chunk at cursor c of piece p.
-// The shared chunks come through the first member's table row, a member's
-// own chunks through its own row, except that with 8-token blocks a chunk
-// can begin with the group's last shared block (an odd count of shared
-// blocks): that block comes through the first member's row too.
+// kShared: starts the loads of the segment's chunk at cursor c of piece p,
+// through the cursor's table row, except that with 8-token blocks a chunk
+// can begin with the last of the eb blocks a group shares (an odd count):
+// that block comes through the segment's `row` too.
 template <int NJ, int NT, int BS>
 __device__ __forceinline__ void issue_shared(const int32_t *__restrict__ tables, const DecodeArgs &a,
                                              const Lane<NT> &ln, const Piece &p, const Cursor &c, size_t hoff,
@@ -1029,8 +1039,8 @@ __device__ __forceinline__ void advance(const DecodeArgs &a, const Lane<NT> &ln,
   if (!st.has_q) st.Q = st.P;
   st.hoff_q = head_off<NJ, M>(ln, st.Q);
   if constexpr (M == kShared) {
-    st.lv_p = st.lv_q;
-    st.lv_q = member_lens(wk.lens, st.Q, wk.cap, ln.lane);
+    st.mv_p = st.mv_q;
+    st.mv_q = member_info(wk.lens, st.Q, ln.lane);
   }
 }
 
@@ -1061,7 +1071,7 @@ __device__ __forceinline__ bool step(const int32_t *__restrict__ tables, const D
   const bool to_q = !in_p && st.has_q;
   Cursor cn;
   if constexpr (M == kShared) {
-    cn = in_p ? seg_next(P, st.cc, st.lv_p) : (to_q ? seg_first(st.Q, st.lv_q) : st.cc);
+    cn = in_p ? seg_next(P, st.cc, st.mv_p, ln.lane) : (to_q ? seg_first(st.Q, st.mv_q, ln.lane) : st.cc);
     issue_shared<NJ, NT, BS>(tables, a, ln, to_q ? st.Q : P, cn, to_q ? st.hoff_q : st.hoff, rows_in(cn.n, cn.b),
                              Kn, Vn);
   } else {
@@ -1081,13 +1091,12 @@ __device__ __forceinline__ bool step(const int32_t *__restrict__ tables, const D
   const int pos_base = fresh ? P.n - 1 : b * CH;
   const int vis = M == kStep ? (fresh ? P.n : P.n - 1) : P.n;  // positions < vis are in this chunk's rows
   const int pos0 = pos_base + ln.grp * 4;
-  // kShared: in the shared blocks the segment's members' columns are live,
-  // in a member's own blocks only that member's; a tile holding none of them
-  // is skipped (a uniform branch).
-  const int cj = M == kShared ? st.cc.j : -1;
+  // kShared: the columns of the members that see the chunk (j .. e) are
+  // live; a tile holding none of them is skipped (a uniform branch).
+  const int cj = M == kShared ? st.cc.j : 0, ce = M == kShared ? st.cc.e : 0;
   auto tile_live = [&](int t) {
     if constexpr (M != kShared) return true;
-    return cj < 0 ? 16 * t < P.ntok * a.group : (cj * a.group < 16 * (t + 1) && (cj + 1) * a.group > 16 * t);
+    return cj * a.group < 16 * (t + 1) && (ce + 1) * a.group > 16 * t;
   };
   if constexpr (VEC) {
     vec_chunk<NJ>(a, ln, st, K, V, pos_base + ln.c < vis);
@@ -1110,7 +1119,7 @@ __device__ __forceinline__ bool step(const int32_t *__restrict__ tables, const D
     // single new token) are masked, and so are a dead column's.
     int lim;
     if constexpr (kMulti) lim = P.n - ln.qshift[t];
-    else if constexpr (M == kShared) lim = (cj < 0 || ln.tok[t] == cj) ? st.cc.n : 0;
+    else if constexpr (M == kShared) lim = (ln.tok[t] >= cj && ln.tok[t] <= ce) ? st.cc.n : 0;
     else lim = vis;
     float z[4];
 #pragma unroll
@@ -1389,9 +1398,9 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
   if (!st.has_q) st.Q = st.P;
   st.hoff_q = head_off<NJ, M>(ln, st.Q);
   if constexpr (M == kShared) {
-    st.lv_p = member_lens(lens, st.P, cap, lane);
-    st.lv_q = member_lens(lens, st.Q, cap, lane);
-    st.cc = seg_first(st.P, st.lv_p);
+    st.mv_p = member_info(lens, st.P, lane);
+    st.mv_q = member_info(lens, st.Q, lane);
+    st.cc = seg_first(st.P, st.mv_p, lane);
   }
   st.i = 0;
   st.ord = 0;
@@ -1557,33 +1566,46 @@ __device__ __forceinline__ int wg_max_scan(int v, int *red, int wave, int lane, 
 }
 
 // Builds the call's segments in one workgroup.
+// Group form (shared_prev null):
 //   * group_starts must not decrease and must stay within 0..S; otherwise no
 //     group is formed and every sequence reads its own table.
 //   * A sequence's group is the last one that starts at or before it (a
 //     max-scan of start marks), if the sequence lies before its end.
-//   * A group's shared blocks e are clamped to 0..max_blocks_per_seq and to
-//     the whole blocks each member fills.
-//   * Segments: each run of members_per_item consecutive members of a group,
-//     and each sequence in no group, is one segment: the e shared blocks
-//     (through the first member's table), then every member's own blocks past
-//     them. Units follow segment order, head group major within a segment.
-//   * A segment with no block at all (every member's context empty) is not
-//     decoded: its members' outputs are zeroed here.
+//   * A group's shared blocks eb are clamped to 0..max_blocks_per_seq and to
+//     the whole blocks each member fills; e = eb * block_size / 16 chunks.
+//   * Each run of members_per_item consecutive members of a group, and each
+//     sequence in no group, is one segment. Its first member reads all its
+//     chunks (those before e through the group's first member's table), the
+//     others their chunks from e on.
+// Chain form (shared_prev given):
+//   * Sequence i > 0 holds c_i chunks in common with sequence i - 1: the
+//     declared blocks clamped to 0..max_blocks_per_seq and to the whole
+//     blocks both fill, times block_size / 16, rounded down.
+//   * A run is a maximal range of sequences each holding c_i > 0 chunks in
+//     common with the one before (its start a max-scan of the breaks); each
+//     members_per_item consecutive members of a run are one segment. Its
+//     first member reads all its chunks, member i the others from c_i on.
+// Both forms: units follow segment order, head group major within a segment.
+// A segment with no chunk at all (every member's context empty) is not
+// decoded: its members' outputs are zeroed here. Each sequence's record
+// (context length, chunks before its own) goes to `members` for the decode.
 template <int kThreads>
 __global__ __launch_bounds__(kThreads) void share_plan_kernel(const SharePlanArgs p) {
-  // grp[S], sid[S], shb[G], gs[G + 1], len[S], then csum[S] (64-bit)
+  // grp[S], sid[S], own[S], len[S], shb[G], gs[G + 1], then csum[S] (64-bit)
   extern __shared__ __align__(16) int plan_lds[];
   __shared__ long long red[kThreads / 64];
   __shared__ int redi[kThreads / 64];
   __shared__ int bad;
   constexpr int nwaves = kThreads / 64;
-  const int S = p.num_seqs, NGr = p.num_groups, C = p.members_per_item;
+  const bool chain = p.shared_prev != nullptr;
+  const int S = p.num_seqs, NGr = chain ? 0 : p.num_groups, C = p.members_per_item;
   int *grp = plan_lds;
   int *sid = grp + S;
-  int *shb = sid + S;
+  int *own = sid + S;
+  int *len = own + S;
+  int *shb = len + S;
   int *gs = shb + NGr;
-  int *len = gs + NGr + 1;
-  long long *csum = reinterpret_cast<long long *>(plan_lds + ((3 * S + 2 * NGr + 1 + 1) & ~1));
+  long long *csum = reinterpret_cast<long long *>(plan_lds + ((4 * S + 2 * NGr + 1 + 1) & ~1));
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bs = p.block_size;
   const int cap = p.max_blocks_per_seq * bs;
@@ -1594,20 +1616,35 @@ __global__ __launch_bounds__(kThreads) void share_plan_kernel(const SharePlanArg
   for (int i = tid; i < S; i += kThreads) {
     grp[i] = -1;
     len[i] = clamp_len(p.lens[i], cap);
+    if (chain) own[i] = p.shared_prev[i];
   }
   if (NGr > 0)  // with no groups the arrays may be null
     for (int g = tid; g <= NGr; g += kThreads) gs[g] = p.group_starts[g];
   for (int g = tid; g < NGr; g += kThreads) shb[g] = min(max(p.shared_blocks[g], 0), p.max_blocks_per_seq);
   __syncthreads();
-  for (int g = tid; g < NGr; g += kThreads) {
-    const int lo = gs[g], hi = gs[g + 1];
-    if (lo > hi || (g == 0 && lo < 0) || (g == NGr - 1 && hi > S)) bad = 1;
-  }
-  __syncthreads();
-  const bool valid = bad == 0;
-  for (int g = tid; g < NGr; g += kThreads) {
-    const int lo = gs[g], hi = gs[g + 1];
-    if (valid && hi > lo) grp[lo] = g;  // distinct starts: groups are nonempty and ordered
+
+  // Per sequence: the chunks it reads through a predecessor (own) and
+  // whether it opens a segment (sid, 0 or 1, until the scan below).
+  if (chain) {
+    // Chunks held in common with the sequence before; a sequence holding
+    // none starts a run (grp: the run's start after the max-scan).
+    for (int i = tid; i < S; i += kThreads) {
+      const int blocks = i > 0 ? min(min(max(own[i], 0), p.max_blocks_per_seq), min(len[i], len[i - 1]) / bs) : 0;
+      const int c = blocks * bs / kBlock;
+      own[i] = c;
+      grp[i] = c > 0 ? -1 : i;
+    }
+  } else {
+    for (int g = tid; g < NGr; g += kThreads) {
+      const int lo = gs[g], hi = gs[g + 1];
+      if (lo > hi || (g == 0 && lo < 0) || (g == NGr - 1 && hi > S)) bad = 1;
+    }
+    __syncthreads();
+    const bool valid = bad == 0;
+    for (int g = tid; g < NGr; g += kThreads) {
+      const int lo = gs[g], hi = gs[g + 1];
+      if (valid && hi > lo) grp[lo] = g;  // distinct starts: groups are nonempty and ordered
+    }
   }
   __syncthreads();
   int carry = -1;
@@ -1619,29 +1656,43 @@ __global__ __launch_bounds__(kThreads) void share_plan_kernel(const SharePlanArg
     carry = max(carry, total);
   }
   __syncthreads();
-  for (int i = tid; i < S; i += kThreads) {
-    const int g = grp[i];
-    if (g < 0) continue;
-    if (i >= gs[g + 1]) {
-      grp[i] = -1;
-      continue;
+  if (chain) {
+    for (int i = tid; i < S; i += kThreads) {
+      const bool opens = (i - grp[i]) % C == 0;
+      sid[i] = opens ? 1 : 0;
+      if (opens) own[i] = 0;
     }
-    atomicMin(&shb[g], len[i] / bs);  // LDS atomic: shared cache blocks
+  } else {
+    for (int i = tid; i < S; i += kThreads) {
+      const int g = grp[i];
+      if (g < 0) continue;
+      if (i >= gs[g + 1]) {
+        grp[i] = -1;
+        continue;
+      }
+      atomicMin(&shb[g], len[i] / bs);  // LDS atomic: shared cache blocks
+    }
+    __syncthreads();
+    for (int i = tid; i < S; i += kThreads) {
+      const int g = grp[i];
+      const bool opens = g < 0 || (i - gs[g]) % C == 0;
+      sid[i] = opens ? 1 : 0;
+      own[i] = opens ? 0 : shb[g] * bs / kBlock;
+    }
   }
   __syncthreads();
 
-  // Per sequence: does it open a segment, and the blocks it adds (its own
-  // past the shared ones, and the shared ones too if it opens the segment).
+  // Segment index of every sequence and the chunks of the stream up to it;
+  // each sequence's record for the decode.
   long long segs_before = 0, blocks_before = 0;
   for (int base = 0; base < S; base += kThreads) {
     const int i = base + tid;
     long long opens = 0, adds = 0;
     if (i < S) {
-      const int n = len[i];
-      const int g = grp[i];
-      const int e = g >= 0 ? shb[g] * bs / kBlock : 0;  // shared chunks
-      opens = (g < 0 || (i - gs[g]) % C == 0) ? 1 : 0;
-      adds = (n + kBlock - 1) / kBlock - e + (opens ? e : 0);
+      opens = sid[i];
+      adds = (len[i] + kBlock - 1) / kBlock - own[i];
+      p.members[2 * i] = len[i];
+      p.members[2 * i + 1] = own[i];
     }
     long long pre, tot, preb, totb;
     const long long incl = wg_scan(opens, red, wave, lane, nwaves, pre, tot);
@@ -1656,17 +1707,16 @@ __global__ __launch_bounds__(kThreads) void share_plan_kernel(const SharePlanArg
   __syncthreads();
   const long long NG = p.num_head_groups;
   for (int i = tid; i < S; i += kThreads) {
-    const int g = grp[i];
-    if (g >= 0 && (i - gs[g]) % C != 0) continue;  // not the first member of its segment
-    const int lo = g >= 0 ? gs[g] : i;
-    const int hi = g >= 0 ? gs[g + 1] : i + 1;
-    const int ntok = min(C, hi - i);
+    if (i > 0 && sid[i] == sid[i - 1]) continue;  // not the first member of its segment
+    int ntok = 1;
+    while (ntok < C && i + ntok < S && sid[i + ntok] == sid[i]) ++ntok;
     const long long start = i > 0 ? csum[i - 1] : 0;
     const long long blocks = csum[i + ntok - 1] - start;
+    const int g = chain ? -1 : grp[i];
     const int eb = g >= 0 ? shb[g] : 0;
     const int e = eb * bs / kBlock;
     ShareItem x;
-    x.row = lo;
+    x.row = g >= 0 ? gs[g] : i;
     x.qrow = i;
     x.ntok = ntok;
     x.b0 = e;
@@ -1806,9 +1856,13 @@ hipError_t launch_decode(const DecodeArgs &args, int32_t head_size, hipStream_t 
   return hipGetLastError();
 }
 
-hipError_t launch_decode_shared(const SharePlanArgs &plan, const DecodeArgs &args, int32_t head_size,
+hipError_t launch_decode_shared(const SharePlanArgs &plan, const DecodeArgs &call, int32_t head_size,
                                 hipStream_t stream) {
-  if (args.q_len != 1 || (args.block_size != 8 && args.block_size != 16 && args.block_size != 32) ||
+  // The decode reads the plan's member records where other launches read
+  // the context lengths.
+  DecodeArgs args = call;
+  args.context_lens = plan.members;
+  if (!plan.members || !plan.lens || args.q_len != 1 || (args.block_size != 8 && args.block_size != 16 && args.block_size != 32) ||
       plan.block_size != args.block_size || args.num_cols <= 16 || args.num_cols > 32 || !args.items || !args.share ||
       plan.num_seqs < 1 || plan.num_seqs > kMaxSharedSeqs || plan.num_groups < 0 ||
       plan.num_groups > plan.num_seqs || plan.members_per_item < 1 || !plan.out || plan.row_elems % 8)
@@ -1816,7 +1870,8 @@ hipError_t launch_decode_shared(const SharePlanArgs &plan, const DecodeArgs &arg
   if (head_size != 128 && head_size != 64) return hipErrorInvalidValue;
   constexpr int kPlanThreads = 512;
   const size_t plan_lds =
-      ((3 * (size_t)plan.num_seqs + 2 * (size_t)plan.num_groups + 2) & ~(size_t)1) * sizeof(int) +
+      ((4 * (size_t)plan.num_seqs + 2 * (size_t)(plan.shared_prev ? 0 : plan.num_groups) + 2) & ~(size_t)1) *
+          sizeof(int) +
       (size_t)plan.num_seqs * sizeof(long long);
   hipError_t e = allow_lds(share_plan_kernel<kPlanThreads>, plan_lds);
   if (e != hipSuccess) return e;

@@ -152,13 +152,13 @@ int32_t step_chunks_per_row(const pa_kv_cache *c, int32_t max_blocks_per_seq, bo
 // columns are their query heads of one KV head: at most two MFMA tiles).
 int32_t members_per_item(int32_t group) { return 32 / group; }
 
-// Workspace of pa_decode_shared: header, segments (+ sentinel), merge
-// records (one per workgroup), then the partial records of cut segments
-// (2 per workgroup).
+// Workspace of the sharing-aware calls: header, segments (+ sentinel),
+// member records (two ints per sequence), merge records (one per
+// workgroup), then the partial records of cut segments (2 per workgroup).
 struct SharedLayout {
   pa::DecodePlan plan;
   int32_t cols;
-  size_t items_off, desc_off, ml_off, o_off, total;
+  size_t items_off, members_off, desc_off, ml_off, o_off, total;
 };
 
 SharedLayout layout_shared(const pa_kv_cache *c, int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq) {
@@ -173,7 +173,8 @@ SharedLayout layout_shared(const pa_kv_cache *c, int32_t num_seqs, int32_t num_q
   l.plan.rec_cols = l.cols;
   const size_t rows = 2 * (size_t)l.plan.num_wgs * l.plan.heads_per_wg * l.cols;
   l.items_off = 256;  // ShareHeader
-  l.desc_off = l.items_off + round_up(((size_t)num_seqs + 1) * sizeof(pa::ShareItem), 256);
+  l.members_off = l.items_off + round_up(((size_t)num_seqs + 1) * sizeof(pa::ShareItem), 256);
+  l.desc_off = l.members_off + round_up((size_t)num_seqs * 2 * sizeof(int32_t), 256);
   l.ml_off = l.desc_off + round_up((size_t)l.plan.num_wgs * sizeof(int2), 256);
   l.o_off = l.ml_off + round_up(rows * 2 * sizeof(float), 256);
   l.total = l.o_off + round_up(rows * c->head_size * sizeof(float), 256);
@@ -182,9 +183,102 @@ SharedLayout layout_shared(const pa_kv_cache *c, int32_t num_seqs, int32_t num_q
 
 int check_shared(const pa_kv_cache *c, int32_t num_seqs, int32_t num_groups) {
   if (num_seqs > pa::kMaxSharedSeqs)
-    return fail(PA_ERR_UNSUPPORTED, "pa_decode_shared takes at most 4096 sequences");
+    return fail(PA_ERR_UNSUPPORTED, "sharing-aware decode takes at most 4096 sequences");
   if (num_groups < 0 || num_groups > num_seqs) return fail(PA_ERR_SHAPE, "num_groups must be in 0..num_seqs");
   return PA_OK;
+}
+
+// Checks, plans and launches a sharing-aware call: the group form, or
+// (shared_prev non-null) the chain form.
+int shared_impl(const pa_kv_cache *cache, const void *q, const int32_t *block_tables, const int32_t *context_lens,
+                int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq, const int32_t *group_starts,
+                const int32_t *shared_blocks, int32_t num_groups, const int32_t *shared_prev, float scale, void *out,
+                void *workspace, size_t workspace_bytes, void *stream) {
+  const char *name = shared_prev ? "pa_decode_shared_tree" : "pa_decode_shared";
+  int rc = check_cache(cache, num_seqs > 0);
+  if (rc != PA_OK) return rc;
+  rc = check_decode_shape(cache, num_seqs, num_q_heads, max_blocks_per_seq);
+  if (rc != PA_OK) return rc;
+  rc = check_shared(cache, num_seqs, num_groups);
+  if (rc != PA_OK) return rc;
+  if (num_seqs == 0) return ok();
+  if (!q || !block_tables || !context_lens || !out)
+    return fail(PA_ERR_NULL, "q, block_tables, context_lens or out is NULL");
+  if (check_aligned(q, "q") != PA_OK || check_aligned(out, "out") != PA_OK) return PA_ERR_UNSUPPORTED;
+  if (num_groups > 0 && (!group_starts || !shared_blocks))
+    return fail(PA_ERR_NULL, "group_starts or shared_blocks is NULL");
+
+  const SharedLayout l = layout_shared(cache, num_seqs, num_q_heads, max_blocks_per_seq);
+  if (workspace && workspace_bytes < l.total)
+    return fail(PA_ERR_WORKSPACE, std::string("workspace smaller than ") + name + "_workspace_bytes()");
+  if (workspace && reinterpret_cast<uintptr_t>(workspace) % 16)
+    return fail(PA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  void *ws = workspace;
+  bool owned = false;
+  if (!ws) {
+    hipError_t e = hipMallocAsync(&ws, l.total, hs);
+    if (e != hipSuccess) return hip_fail(e, "hipMallocAsync(workspace)");
+    owned = true;
+  }
+  char *base = static_cast<char *>(ws);
+  pa::ShareHeader *hdr = reinterpret_cast<pa::ShareHeader *>(base);
+  pa::ShareItem *items = reinterpret_cast<pa::ShareItem *>(base + l.items_off);
+
+  pa::DecodeArgs a{};
+  a.q = static_cast<const uint16_t *>(q);
+  a.k_cache = static_cast<const uint16_t *>(cache->k_cache);
+  a.v_cache = static_cast<const uint16_t *>(cache->v_cache);
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.out = static_cast<uint16_t *>(out);
+  a.merge_desc = reinterpret_cast<int2 *>(base + l.desc_off);
+  a.part_ml = reinterpret_cast<float *>(base + l.ml_off);
+  a.part_o = reinterpret_cast<float *>(base + l.o_off);
+  a.num_blocks = cache->num_blocks;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.group = num_q_heads / cache->num_kv_heads;
+  a.q_len = 1;
+  a.num_cols = l.cols;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.block_size = cache->block_size;
+  a.heads_per_wg = l.plan.heads_per_wg;
+  a.num_head_groups = l.plan.num_head_groups;
+  a.col_groups = 1;
+  a.rec_cols = l.cols;
+  a.num_wgs = l.plan.num_wgs;
+  a.scale_log2 = scale * 1.44269504088896340736f;
+  a.items = items;
+  a.share = hdr;
+
+  pa::SharePlanArgs p{};
+  p.lens = context_lens;
+  p.group_starts = group_starts;
+  p.shared_blocks = shared_blocks;
+  p.shared_prev = shared_prev;
+  p.members = reinterpret_cast<int32_t *>(base + l.members_off);
+  p.items = items;
+  p.share = hdr;
+  p.out = static_cast<uint16_t *>(out);
+  p.row_elems = num_q_heads * cache->head_size;
+  p.num_seqs = num_seqs;
+  p.num_groups = num_groups;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.members_per_item = members_per_item(a.group);
+  p.group = a.group;
+  p.num_head_groups = a.num_head_groups;
+  p.block_size = cache->block_size;
+
+  hipError_t e = pa::launch_decode_shared(p, a, cache->head_size, hs);
+  if (owned) {
+    hipError_t fe = hipFreeAsync(ws, hs);
+    if (e == hipSuccess) e = fe;
+  }
+  if (e != hipSuccess) return hip_fail(e, (std::string(name) + " launch").c_str());
+  return ok();
 }
 
 }  // namespace
@@ -387,88 +481,22 @@ int pa_decode_shared(const pa_kv_cache *cache, const void *q, const int32_t *blo
                      int32_t max_blocks_per_seq, const int32_t *group_starts, const int32_t *shared_blocks,
                      int32_t num_groups, float scale, void *out, void *workspace, size_t workspace_bytes,
                      void *stream) {
-  int rc = check_cache(cache, num_seqs > 0);
-  if (rc != PA_OK) return rc;
-  rc = check_decode_shape(cache, num_seqs, num_q_heads, max_blocks_per_seq);
-  if (rc != PA_OK) return rc;
-  rc = check_shared(cache, num_seqs, num_groups);
-  if (rc != PA_OK) return rc;
-  if (num_seqs == 0) return ok();
-  if (!q || !block_tables || !context_lens || !out)
-    return fail(PA_ERR_NULL, "q, block_tables, context_lens or out is NULL");
-  if (check_aligned(q, "q") != PA_OK || check_aligned(out, "out") != PA_OK) return PA_ERR_UNSUPPORTED;
-  if (num_groups > 0 && (!group_starts || !shared_blocks))
-    return fail(PA_ERR_NULL, "group_starts or shared_blocks is NULL");
+  return shared_impl(cache, q, block_tables, context_lens, num_seqs, num_q_heads, max_blocks_per_seq, group_starts,
+                     shared_blocks, num_groups, nullptr, scale, out, workspace, workspace_bytes, stream);
+}
 
-  const SharedLayout l = layout_shared(cache, num_seqs, num_q_heads, max_blocks_per_seq);
-  if (workspace && workspace_bytes < l.total)
-    return fail(PA_ERR_WORKSPACE, "workspace smaller than pa_decode_shared_workspace_bytes()");
-  if (workspace && reinterpret_cast<uintptr_t>(workspace) % 16)
-    return fail(PA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+size_t pa_decode_shared_tree_workspace_bytes(const pa_kv_cache *cache, int32_t num_seqs, int32_t num_q_heads,
+                                             int32_t max_blocks_per_seq) {
+  return pa_decode_shared_workspace_bytes(cache, num_seqs, num_q_heads, max_blocks_per_seq, 0);
+}
 
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  void *ws = workspace;
-  bool owned = false;
-  if (!ws) {
-    hipError_t e = hipMallocAsync(&ws, l.total, hs);
-    if (e != hipSuccess) return hip_fail(e, "hipMallocAsync(workspace)");
-    owned = true;
-  }
-  char *base = static_cast<char *>(ws);
-  pa::ShareHeader *hdr = reinterpret_cast<pa::ShareHeader *>(base);
-  pa::ShareItem *items = reinterpret_cast<pa::ShareItem *>(base + l.items_off);
-
-  pa::DecodeArgs a{};
-  a.q = static_cast<const uint16_t *>(q);
-  a.k_cache = static_cast<const uint16_t *>(cache->k_cache);
-  a.v_cache = static_cast<const uint16_t *>(cache->v_cache);
-  a.block_tables = block_tables;
-  a.context_lens = context_lens;
-  a.out = static_cast<uint16_t *>(out);
-  a.merge_desc = reinterpret_cast<int2 *>(base + l.desc_off);
-  a.part_ml = reinterpret_cast<float *>(base + l.ml_off);
-  a.part_o = reinterpret_cast<float *>(base + l.o_off);
-  a.num_blocks = cache->num_blocks;
-  a.num_seqs = num_seqs;
-  a.num_q_heads = num_q_heads;
-  a.num_kv_heads = cache->num_kv_heads;
-  a.group = num_q_heads / cache->num_kv_heads;
-  a.q_len = 1;
-  a.num_cols = l.cols;
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.block_size = cache->block_size;
-  a.heads_per_wg = l.plan.heads_per_wg;
-  a.num_head_groups = l.plan.num_head_groups;
-  a.col_groups = 1;
-  a.rec_cols = l.cols;
-  a.num_wgs = l.plan.num_wgs;
-  a.scale_log2 = scale * 1.44269504088896340736f;
-  a.items = items;
-  a.share = hdr;
-
-  pa::SharePlanArgs p{};
-  p.lens = context_lens;
-  p.group_starts = group_starts;
-  p.shared_blocks = shared_blocks;
-  p.items = items;
-  p.share = hdr;
-  p.out = static_cast<uint16_t *>(out);
-  p.row_elems = num_q_heads * cache->head_size;
-  p.num_seqs = num_seqs;
-  p.num_groups = num_groups;
-  p.max_blocks_per_seq = max_blocks_per_seq;
-  p.members_per_item = members_per_item(a.group);
-  p.group = a.group;
-  p.num_head_groups = a.num_head_groups;
-  p.block_size = cache->block_size;
-
-  hipError_t e = pa::launch_decode_shared(p, a, cache->head_size, hs);
-  if (owned) {
-    hipError_t fe = hipFreeAsync(ws, hs);
-    if (e == hipSuccess) e = fe;
-  }
-  if (e != hipSuccess) return hip_fail(e, "decode_shared launch");
-  return ok();
+int pa_decode_shared_tree(const pa_kv_cache *cache, const void *q, const int32_t *block_tables,
+                          const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                          int32_t max_blocks_per_seq, const int32_t *shared_prev, float scale, void *out,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+  if (num_seqs > 0 && !shared_prev) return fail(PA_ERR_NULL, "shared_prev is NULL");
+  return shared_impl(cache, q, block_tables, context_lens, num_seqs, num_q_heads, max_blocks_per_seq, nullptr,
+                     nullptr, 0, shared_prev, scale, out, workspace, workspace_bytes, stream);
 }
 
 int pa_reshape_and_cache(const pa_kv_cache *cache, const void *k, const void *v,

@@ -11,19 +11,25 @@
 namespace pa {
 
 // Sharing-aware decode: the call's work as a list of segments. A segment is
-// up to 32 / group consecutive members of a group (one sequence outside
-// groups): the group's shared blocks, read once through the first member's
-// table with every member's query heads as MFMA columns, then each member's
-// own blocks past them, read for that member alone.
+// up to 32 / group consecutive members (one sequence outside any sharing).
+// Each 16-token chunk is read once, by the first member that holds it, with
+// the query heads of every member that holds it too as live MFMA columns:
+// member j reads its chunks from its first `own` on (the chunks before are
+// those it holds in common with member j - 1, read by an earlier member),
+// and they are seen by members j .. e, e being the last member after j
+// whose leading shared chunks all cover it. Two ways to declare sharing feed
+// this: groups with one common prefix, and a chain in which each sequence
+// shares leading blocks with the one before it (a prefix tree listed depth
+// first).
 struct ShareItem {
-  int32_t row;     // table row of the shared blocks (the group's first member)
+  int32_t row;     // table row read for the first member's chunks < b0 (the group's first member)
   int32_t qrow;    // first member: q and output rows qrow .. qrow + ntok - 1
   int32_t ntok;    // members
-  int32_t b0;      // shared 16-token chunks
+  int32_t b0;      // chunks of the first member read through row `row` (0 in the chain form)
   int32_t n;       // b0 * 16
-  int32_t L;       // chunks in all: b0 + the members' own chunks
+  int32_t L;       // chunks in all: what the members read themselves
   int64_t ustart;  // first unit: head groups times the chunks of all earlier segments
-  int32_t eb;      // shared cache blocks (b0 = eb * block_size / 16, rounded down)
+  int32_t eb;      // cache blocks read through row `row` (b0 = eb * block_size / 16, rounded down)
 };
 
 // Written by the plan kernel: totals of the call.
@@ -39,7 +45,7 @@ struct DecodeArgs {
   const uint16_t *k_cache;       // bf16 [NB, block_size, Hkv, D]
   const uint16_t *v_cache;
   const int32_t *block_tables;   // [S, MB]
-  const int32_t *context_lens;   // [S]
+  const int32_t *context_lens;   // [S]; sharing-aware decode: the plan's member records [S][2]
   uint16_t *out;                 // bf16 [S, q_len, Hq, D]
   int2 *merge_desc;              // [num_wgs]: segment ended by the workgroup's first piece, or -1
   float *part_ml;                // [2 * num_wgs, heads_per_wg, rec_cols, 2]: max (base 2), sum
@@ -74,6 +80,8 @@ struct SharePlanArgs {
   const int32_t *lens;           // [S]
   const int32_t *group_starts;   // [num_groups + 1]
   const int32_t *shared_blocks;  // [num_groups]
+  const int32_t *shared_prev;    // [S] in the chain form (group_starts unused then), else null
+  int32_t *members;              // [S][2] out: clamped context length, chunks read through a predecessor
   ShareItem *items;
   ShareHeader *share;
   uint16_t *out;                 // zeroed for segments whose members are all empty
@@ -126,7 +134,8 @@ hipError_t noalloc_scratch(void **ptr);
 constexpr int32_t kMaxSharedSeqs = 4096;
 
 // Plan, decode and merge of a sharing-aware call. args.num_cols is the
-// segment width (members_per_item * group), args.q_len is 1.
+// segment width (members_per_item * group), args.q_len is 1; the decode
+// reads plan.members in place of args.context_lens.
 hipError_t launch_decode_shared(const SharePlanArgs &plan, const DecodeArgs &args, int32_t head_size,
                                 hipStream_t stream);
 

@@ -89,6 +89,12 @@ def decode_shared_workspace_bytes(k_cache, num_seqs, num_q_heads, max_blocks_per
                                                           max_blocks_per_seq, num_groups))
 
 
+def decode_shared_tree_workspace_bytes(k_cache, num_seqs, num_q_heads, max_blocks_per_seq) -> int:
+    desc = _cache_desc(k_cache, k_cache)
+    return int(_lib.lib().pa_decode_shared_tree_workspace_bytes(ctypes.byref(desc), num_seqs, num_q_heads,
+                                                               max_blocks_per_seq))
+
+
 def decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=None, workspace=None):
     """Paged decode attention; returns ``out`` (bf16 ``[num_seqs, num_q_heads, head_size]``).
 
@@ -219,6 +225,37 @@ def decode_shared(q, k_cache, v_cache, block_tables, context_lens, group_starts,
     _check(lib.pa_decode_shared(ctypes.byref(desc), _ptr(q), _ptr(block_tables), _ptr(context_lens), S, hq, mb,
                                 _ptr(group_starts), _ptr(shared_blocks), G, float(scale), _ptr(out),
                                 _ptr(workspace), ws_bytes, _stream(dev)))
+    return out
+
+
+def decode_shared_tree(q, k_cache, v_cache, block_tables, context_lens, shared_prev, scale, out=None,
+                       workspace=None):
+    """Decode attention for sequences that form a tree of shared prefixes,
+    listed depth first.
+
+    ``shared_prev`` int32 ``[num_seqs]`` on the cache's device: sequence i's
+    table agrees with sequence i-1's on its first ``shared_prev[i]`` entries
+    (entry 0 is ignored). Other arguments as ``decode``.
+    """
+    desc = _cache_desc(k_cache, v_cache)
+    dev = k_cache.device
+    S, hq, d = q.shape
+    _need(q, "q", _BF16, (S, hq, k_cache.shape[3]), dev)
+    mb = block_tables.shape[1] if block_tables.dim() == 2 else -1
+    _need(block_tables, "block_tables", torch.int32, (S, mb), dev)
+    _need(context_lens, "context_lens", torch.int32, (S,), dev)
+    _need(shared_prev, "shared_prev", torch.int32, (S,), dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", _BF16, (S, hq, d), dev)
+    lib = _lib.lib()
+    nbytes = int(lib.pa_decode_shared_tree_workspace_bytes(ctypes.byref(desc), S, hq, mb))
+    if workspace is None and nbytes:
+        workspace = _workspace(dev, nbytes)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.pa_decode_shared_tree(ctypes.byref(desc), _ptr(q), _ptr(block_tables), _ptr(context_lens), S, hq,
+                                     mb, _ptr(shared_prev), float(scale), _ptr(out), _ptr(workspace), ws_bytes,
+                                     _stream(dev)))
     return out
 
 

@@ -405,6 +405,159 @@ def make_shared_batch(name, seed, group_sizes, prefix_lens, private_lens, num_q_
 CONFIG_NAMES = ("tiny_mha", "llama2_7b", "llama3_8b_gqa", "long_splitk", "beam_cow")
 
 
+# ----------------------------------------------------------------------------
+# sequences that form trees of shared prefixes
+# ----------------------------------------------------------------------------
+
+
+def _used_rows(block_tables, context_lens, block_size):
+    t = np.asarray(block_tables)
+    return [tuple(int(x) for x in t[s, :(int(n) + block_size - 1) // block_size])
+            for s, n in enumerate(np.asarray(context_lens))]
+
+
+def tree_order(block_tables, context_lens, block_size=BLOCK_SIZE) -> np.ndarray:
+    """A depth-first order of the prefix tree the tables form: the sequences
+    sorted by their used table entries, compared entry by entry (a row comes
+    before its extensions), ties kept in batch order; int64 ``[S]``. In this
+    order the sequences below any node of the tree are consecutive."""
+    rows = _used_rows(block_tables, context_lens, block_size)
+    return np.array(sorted(range(len(rows)), key=lambda s: rows[s]), dtype=np.int64)
+
+
+def declared_chain(block_tables, context_lens, block_size=BLOCK_SIZE) -> np.ndarray:
+    """``shared_prev`` of a batch: the leading used table entries each
+    sequence has in common with the one before it (0 for the first); int32
+    ``[S]``. A block manager knows this from its tree; here it is read back
+    from the tables."""
+    rows = _used_rows(block_tables, context_lens, block_size)
+    out = np.zeros(len(rows), dtype=np.int32)
+    for i in range(1, len(rows)):
+        a, b = rows[i - 1], rows[i]
+        k = 0
+        while k < min(len(a), len(b)) and a[k] == b[k]:
+            k += 1
+        out[i] = k
+    return out
+
+
+def chain_sharing(context_lens, shared_prev, max_blocks_per_seq, block_size=BLOCK_SIZE) -> np.ndarray:
+    """Blocks each sequence really shares with the one before it: the
+    declaration clamped to ``0..max_blocks_per_seq`` and to the whole blocks
+    both fill (int64 ``[S]``; 0 for the first)."""
+    n = np.asarray(context_lens, dtype=np.int64)
+    d = np.asarray(shared_prev, dtype=np.int64)
+    out = np.zeros(len(n), dtype=np.int64)
+    for i in range(1, len(n)):
+        out[i] = max(0, min(int(d[i]), max_blocks_per_seq, int(n[i]) // block_size, int(n[i - 1]) // block_size))
+    return out
+
+
+def tree_algorithmic_bytes(context_lens, shared_prev, max_blocks_per_seq, num_q_heads, num_kv_heads, head_size,
+                           block_size=BLOCK_SIZE, dtype_bytes=2) -> int:
+    """Bytes a decode over trees of shared prefixes must move: K and V of
+    each sequence's tokens past the blocks it shares with the one before it
+    (so of every distinct block once, in a depth-first order), q in and out
+    back, the table entries read, the context lengths and the
+    declarations."""
+    n = np.asarray(context_lens, dtype=np.int64)
+    e = chain_sharing(n, shared_prev, max_blocks_per_seq, block_size)
+    tokens = int(n.sum()) - int(e.sum()) * block_size
+    row = 2 * num_kv_heads * head_size * dtype_bytes
+    entries = int(((n + block_size - 1) // block_size).sum()) - int(e.sum())
+    qo = len(n) * 2 * num_q_heads * head_size * dtype_bytes
+    return tokens * row + qo + entries * 4 + 4 * len(n) + 4 * len(n)
+
+
+def permuted(batch: DecodeBatch, order) -> DecodeBatch:
+    """The batch with its sequences taken in ``order`` (same caches; new
+    tokens, slots and queries follow their sequences)."""
+    order = np.asarray(order, dtype=np.int64)
+    assert batch.q_len == 1 and sorted(order.tolist()) == list(range(batch.num_seqs))
+    live = len(batch.slot_mapping) == batch.num_seqs
+    return dataclasses.replace(
+        batch, block_tables=np.ascontiguousarray(batch.block_tables[order]),
+        context_lens=np.ascontiguousarray(batch.context_lens[order]), q=np.ascontiguousarray(batch.q[order]),
+        new_k=np.ascontiguousarray(batch.new_k[order]) if live else batch.new_k,
+        new_v=np.ascontiguousarray(batch.new_v[order]) if live else batch.new_v,
+        slot_mapping=np.ascontiguousarray(batch.slot_mapping[order]) if live else batch.slot_mapping)
+
+
+def make_tree_batch(name, seed, root_lens, beams, rounds, max_append, num_q_heads, num_kv_heads, head_size,
+                    num_blocks, block_size=BLOCK_SIZE):
+    """A decode batch whose sequences form trees of shared prefixes, the way
+    beam search leaves them.
+
+    Root r is a prompt of ``root_lens[r]`` tokens held by ``beams[r]``
+    sequences. Then, ``rounds`` times: every sequence appends
+    ``U{0..max_append}`` tokens of its own (a shared partial last block is
+    copied before the first append into it), and each root's sequences are
+    replaced by forks of parents drawn uniformly among them. The batch lists
+    the sequences root by root in the order of the last draw (not depth
+    first). Every token is cached: ``new_k``/``new_v``/``slot_mapping`` are
+    empty.
+
+    Draw order for ``seed``: stream (seed, 0) shuffles the pool, (seed, 1, r)
+    draws root r's K then V, (seed, 3, k) round k's append counts then
+    parents, (seed, 4, k, i) K then V of sequence i's appends in round k,
+    (seed, 2) q.
+    """
+    assert len(root_lens) == len(beams)
+    pool = BlockPool(num_blocks, _rng(seed, 0).permutation(num_blocks))
+    shape = (num_blocks, block_size, num_kv_heads, head_size)
+    k_cache = np.full(shape, BF16_QNAN, dtype=np.uint16)
+    v_cache = np.full(shape, BF16_QNAN, dtype=np.uint16)
+    seqs, root_of = [], []
+    for r, (plen, m) in enumerate(zip(root_lens, beams)):
+        prompt = allocate_prefix(pool, int(plen), block_size)
+        g = _rng(seed, 1, r)
+        kb = normal_bf16(g, (int(plen), num_kv_heads, head_size))
+        vb = normal_bf16(g, (int(plen), num_kv_heads, head_size))
+        _fill_sequence(k_cache, v_cache, prompt.table, kb, vb, block_size)
+        for b in range(int(m)):
+            seqs.append(prompt.fork(pool) if b < m - 1 else prompt)
+            root_of.append(r)
+        if m == 0:
+            prompt.release(pool)
+    S = len(seqs)
+    for k in range(rounds):
+        g = _rng(seed, 3, k)
+        counts = g.integers(0, max_append, size=S, endpoint=True)
+        for i, sq in enumerate(seqs):
+            c = int(counts[i])
+            if c == 0:
+                continue
+            h = _rng(seed, 4, k, i)
+            kb = normal_bf16(h, (c, num_kv_heads, head_size))
+            vb = normal_bf16(h, (c, num_kv_heads, head_size))
+            for t in range(c):
+                slot, cow = append_token(pool, sq, block_size)
+                if cow is not None:
+                    k_cache[cow[1]] = k_cache[cow[0]]
+                    v_cache[cow[1]] = v_cache[cow[0]]
+                blk, off = divmod(slot, block_size)
+                k_cache[blk, off] = kb[t]
+                v_cache[blk, off] = vb[t]
+        new, lo = [], 0
+        for m in beams:
+            parents = g.integers(0, max(int(m), 1), size=int(m))
+            new.extend(seqs[lo + int(p)].fork(pool) for p in parents)
+            lo += int(m)
+        for sq in seqs:
+            sq.release(pool)
+        seqs = new
+    lens = np.array([sq.length for sq in seqs], dtype=np.int32)
+    MB = max(1, max((len(sq.table) for sq in seqs), default=1))
+    tables = np.full((S, MB), num_blocks + TABLE_PAD_OFFSET, dtype=np.int32)
+    for s, sq in enumerate(seqs):
+        tables[s, : len(sq.table)] = sq.table
+    q = normal_bf16(_rng(seed, 2), (S, num_q_heads, head_size))
+    empty = np.zeros((0, num_kv_heads, head_size), dtype=np.uint16)
+    return DecodeBatch(name, seed, num_blocks, block_size, num_q_heads, num_kv_heads, head_size,
+                       np.float32(1.0 / math.sqrt(head_size)), tables, lens, q, k_cache, v_cache,
+                       empty, empty.copy(), np.zeros(0, dtype=np.int64), np.zeros((0, 2), dtype=np.int64))
+
+
 def lognormal_lens(rng, count, median, sigma, lo, hi):
     """``clip(round(exp(N(ln median, sigma))), lo, hi)``."""
     x = np.exp(rng.normal(math.log(median), sigma, size=count))

@@ -17,6 +17,8 @@ from __future__ import annotations
 
 from dataclasses import dataclass, field
 
+import numpy as np
+
 CHUNK = 16  # tokens per unit of work (one MFMA tile of rows)
 
 
@@ -197,76 +199,194 @@ def check_plain(lens, num_q_heads, num_kv_heads, max_blocks_per_seq, block_size=
     return sp
 
 
-def share_plan(lens, group_starts, shared_blocks, max_blocks_per_seq, block_size, members_per_item):
-    """share_plan_kernel: items (segments) of a sharing-aware call. Returns
-    (items, zeroed rows) with each item as a dict of its fields."""
+def share_plan(lens, group_starts, shared_blocks, max_blocks_per_seq, block_size, members_per_item,
+               shared_prev=None):
+    """share_plan_kernel: items (segments) of a sharing-aware call, group
+    form, or chain form when ``shared_prev`` is given. Returns (items, zeroed
+    rows, member records) with each item as a dict of its fields and each
+    member record as (clamped context length, chunks before its own)."""
     S = len(lens)
+    C = members_per_item
     cap = max_blocks_per_seq * block_size
     n = [min(max(int(x), 0), cap) for x in lens]
-    gs = [int(x) for x in group_starts] if len(shared_blocks) else []
-    G = len(shared_blocks)
-    shb = [min(max(int(x), 0), max_blocks_per_seq) for x in shared_blocks]
-    valid = True
-    for g in range(G):
-        lo, hi = gs[g], gs[g + 1]
-        if lo > hi or (g == 0 and lo < 0) or (g == G - 1 and hi > S):
-            valid = False
     grp = [-1] * S
-    if valid:
-        marks = [-1] * S
-        for g in range(G):
-            if gs[g + 1] > gs[g]:
-                marks[gs[g]] = g
-        run = -1
+    if shared_prev is not None:
+        gs, shb = [], []
+        common = [0] * S
+        for i in range(1, S):
+            blocks = min(min(max(int(shared_prev[i]), 0), max_blocks_per_seq), min(n[i], n[i - 1]) // block_size)
+            common[i] = blocks * block_size // CHUNK
+        run = 0
+        opens, own = [], []
         for i in range(S):
-            run = max(run, marks[i])
-            grp[i] = run
-    for i in range(S):
-        g = grp[i]
-        if g >= 0 and i >= gs[g + 1]:
-            grp[i] = -1
-    for i in range(S):
-        g = grp[i]
-        if g >= 0:
-            shb[g] = min(shb[g], n[i] // block_size)
-    items, zeroed, start = [], [], 0
+            if common[i] == 0:
+                run = i
+            op = (i - run) % C == 0
+            opens.append(op)
+            own.append(0 if op else common[i])
+    else:
+        gs = [int(x) for x in group_starts] if len(shared_blocks) else []
+        G = len(shared_blocks)
+        shb = [min(max(int(x), 0), max_blocks_per_seq) for x in shared_blocks]
+        valid = True
+        for g in range(G):
+            lo, hi = gs[g], gs[g + 1]
+            if lo > hi or (g == 0 and lo < 0) or (g == G - 1 and hi > S):
+                valid = False
+        if valid:
+            marks = [-1] * S
+            for g in range(G):
+                if gs[g + 1] > gs[g]:
+                    marks[gs[g]] = g
+            run = -1
+            for i in range(S):
+                run = max(run, marks[i])
+                grp[i] = run
+        for i in range(S):
+            g = grp[i]
+            if g >= 0 and i >= gs[g + 1]:
+                grp[i] = -1
+        for i in range(S):
+            g = grp[i]
+            if g >= 0:
+                shb[g] = min(shb[g], n[i] // block_size)
+        opens = [grp[i] < 0 or (i - gs[grp[i]]) % C == 0 for i in range(S)]
+        own = [0 if opens[i] else shb[grp[i]] * block_size // CHUNK for i in range(S)]
     csum, acc = [], 0
-    opens = []
     for i in range(S):
-        g = grp[i]
-        e = shb[g] * block_size // CHUNK if g >= 0 else 0
-        op = g < 0 or (i - gs[g]) % members_per_item == 0
-        opens.append(op)
-        acc += (n[i] + CHUNK - 1) // CHUNK - e + (e if op else 0)
+        acc += (n[i] + CHUNK - 1) // CHUNK - own[i]
         csum.append(acc)
+    items, zeroed = [], []
     for i in range(S):
         if not opens[i]:
             continue
-        g = grp[i]
-        hi = gs[g + 1] if g >= 0 else i + 1
-        ntok = min(members_per_item, hi - i)
+        ntok = 1
+        while ntok < C and i + ntok < S and not opens[i + ntok]:
+            ntok += 1
         start = csum[i - 1] if i > 0 else 0
         blocks = csum[i + ntok - 1] - start
+        g = grp[i]
         eb = shb[g] if g >= 0 else 0
-        items.append(dict(row=gs[g] if g >= 0 else i, qrow=i, ntok=ntok, b0=eb * block_size // CHUNK, L=blocks))
+        items.append(dict(row=gs[g] if g >= 0 else i, qrow=i, ntok=ntok, b0=eb * block_size // CHUNK, eb=eb,
+                          L=blocks))
         if blocks == 0:
             zeroed.extend(range(i, i + ntok))
-    return items, zeroed
+    return items, zeroed, list(zip(n, own))
+
+
+def _chunks(n: int) -> int:
+    return (n + CHUNK - 1) // CHUNK
+
+
+def member_lanes(item, members):
+    """member_info: lane j's (context length, chunks before its own) for
+    member j of the item, the second clamped to the member's chunks."""
+    out = []
+    for j in range(item["ntok"]):
+        n, y = members[item["qrow"] + j]
+        n = max(n, 0)
+        out.append((n, min(max(y, 0), _chunks(n))))
+    return out
+
+
+def seg_at(item, lanes, j, b, nj):
+    """The kernel's cursor of member j's chunk b: (j, e, b, n, row)."""
+    stop = [k for k in range(j + 1, item["ntok"]) if lanes[k][1] <= b]
+    e = stop[0] - 1 if stop else item["ntok"] - 1
+    return (j, e, b, nj, item["row"] if b < item["b0"] else item["qrow"] + j)
+
+
+def seg_first(item, lanes, off):
+    r, j, nj, yj = off, 0, 0, 0
+    while j < item["ntok"]:
+        nj, yj = lanes[j]
+        lj = _chunks(nj) - yj
+        if r < lj:
+            break
+        r -= lj
+        j += 1
+    if j == item["ntok"]:
+        j -= 1
+    return seg_at(item, lanes, j, yj + r, nj)
+
+
+def seg_next(item, lanes, c):
+    j, _, b, n, _ = c
+    if b + 1 < _chunks(n):
+        return seg_at(item, lanes, j, b + 1, n)
+    for k in range(j + 1, item["ntok"]):
+        nk, yk = lanes[k]
+        if _chunks(nk) > yk:
+            return seg_at(item, lanes, k, yk, nk)
+    return c
+
+
+def check_item_stream(item, members, tables=None, block_size=16):
+    """Walks an item's stream the way the decode kernel does (seg_first at
+    every offset, seg_next between) and checks what each member sees:
+      * the stream has the item's L chunks, and seg_first at any offset
+        agrees with seg_next from the start;
+      * every member sees each chunk of its context exactly once, and with
+        the reader's context length as the limit, it sees exactly its own
+        positions of that chunk;
+      * with ``tables`` (a true declaration), the cache blocks read for a
+        member hold its own tokens: the reader's table row (the segment's
+        row for the blocks of the group prefix) names the same physical
+        blocks as the member's own row for those tokens.
+    Returns the stream as a list of cursors."""
+    lanes = member_lanes(item, members)
+    L = item["L"]
+    stream = []
+    if L > 0:
+        c = seg_first(item, lanes, 0)
+        for off in range(L):
+            assert seg_first(item, lanes, off) == c, f"seg_first({off}) disagrees with the walk"
+            stream.append(c)
+            c = seg_next(item, lanes, c)
+    seen = {}
+    for (j, e, b, nj, row) in stream:
+        assert 0 <= j <= e < item["ntok"]
+        for k in range(j, e + 1):
+            nk = lanes[k][0]
+            key = (k, b)
+            assert key not in seen, f"member {k} sees chunk {b} twice"
+            seen[key] = (j, row, nj)
+            assert min(CHUNK, nj - b * CHUNK) == min(CHUNK, nk - b * CHUNK), \
+                f"member {k}: chunk {b} limit {nj} differs from its own context {nk}"
+    for k in range(item["ntok"]):
+        got = sorted(b for (kk, b) in seen if kk == k)
+        assert got == list(range(_chunks(lanes[k][0]))), f"member {k} sees chunks {got}"
+    if tables is not None:
+        t = np.asarray(tables)
+        bs = block_size
+        for (k, b), (j, row, nj) in seen.items():
+            own_row = item["qrow"] + k
+            for tok in range(b * CHUNK, min((b + 1) * CHUNK, lanes[k][0])):
+                blk = tok // bs
+                if bs < CHUNK:  # the chunk's first block may come through the segment's row
+                    rr = item["row"] if (blk == 2 * b and blk < item["eb"]) else row
+                else:
+                    rr = row
+                assert t[rr, blk] == t[own_row, blk], \
+                    f"member {k} token {tok}: block {t[rr, blk]} read, its table has {t[own_row, blk]}"
+    return stream
 
 
 def check_shared(lens, group_starts, shared_blocks, num_q_heads, num_kv_heads, max_blocks_per_seq,
-                 block_size=16, override=None) -> Split:
+                 block_size=16, override=None, shared_prev=None, tables=None) -> Split:
     group = num_q_heads // num_kv_heads
     C = 32 // group
     hg = heads_per_workgroup(num_kv_heads)
     NG = num_kv_heads // hg
     W = decode_wgs(len(lens), NG, hg, chunks_per_row(max_blocks_per_seq, block_size), override)
-    items, zeroed = share_plan(lens, group_starts, shared_blocks, max_blocks_per_seq, block_size, C)
+    items, zeroed, members = share_plan(lens, group_starts, shared_blocks, max_blocks_per_seq, block_size, C,
+                                        shared_prev)
     assert len(items) <= len(lens)
     segs = [Segment(key=v, L=it["L"], rows=tuple(range(it["qrow"], it["qrow"] + it["ntok"])))
             for v, it in enumerate(items)]
     for it in items:
         assert 0 <= it["qrow"] and it["qrow"] + it["ntok"] <= len(lens) and it["ntok"] * group <= 32
+        check_item_stream(it, members, tables, block_size)
     sp = walk(segs, NG, W)
     if W > 1:
         merge(sp, segs, NG, len(items))

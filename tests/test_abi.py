@@ -147,6 +147,33 @@ def test_decode_shared_limits(L):
     assert call(S=S, mb=mb, ng=64, ws=P, wsb=need - 1) == _lib.PA_ERR_WORKSPACE
 
 
+def test_decode_shared_tree_limits(L):
+    """The chain form: the group form's limits, a NULL declaration refused,
+    the same workspace as the group form (member records included)."""
+    d = desc()
+    T = L.pa_decode_shared_tree
+    W = L.pa_decode_shared_tree_workspace_bytes
+
+    def call(S=8, mb=16, sp=P, q=P, ws=None, wsb=0):
+        return T(ctypes.byref(d), q, P, P, S, 32, mb, sp, 1.0, P, ws, wsb, None)
+
+    assert W(ctypes.byref(d), 4096, 32, 64) > 0
+    assert W(ctypes.byref(d), 4097, 32, 64) == 0
+    assert W(ctypes.byref(d), 0, 32, 64) == 0
+    assert call(S=4097) == _lib.PA_ERR_UNSUPPORTED
+    assert call(sp=None) == _lib.PA_ERR_NULL and call(q=None) == _lib.PA_ERR_NULL
+    assert call(S=-1) == _lib.PA_ERR_SHAPE
+    assert T(ctypes.byref(desc(k_cache=0, v_cache=0)), None, None, None, 0, 32, 16, None, 1.0, None, None, 0,
+             None) == _lib.PA_OK   # empty batch
+    S, mb = 256, 256
+    need = W(ctypes.byref(d), S, 32, mb)
+    assert need == L.pa_decode_shared_workspace_bytes(ctypes.byref(d), S, 32, mb, 64)
+    assert need >= (S + 1) * 32 + S * 8
+    assert call(S=S, mb=mb, ws=P, wsb=need - 1) == _lib.PA_ERR_WORKSPACE
+    odd = ctypes.c_void_p(P.value + 2)
+    assert call(q=odd) == _lib.PA_ERR_UNSUPPORTED
+
+
 def test_block_sizes(L):
     """8-, 16- and 32-token blocks for single-token, multi-token and
     sharing-aware decode and the cache ops. The kernels work in 16-token

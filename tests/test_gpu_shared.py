@@ -1,9 +1,18 @@
-"""GPU parity of pa_decode_shared: groups of sequences that share leading
-blocks (parallel samples, beams, prefix reuse) read the shared blocks once.
-Checked against the float64 oracle's decode_shared across head shapes, group
-sizes (groups wider than one item included), work splits, members whose
-whole context is shared, empty sequences, false and clamped declarations,
-invalid group lists, and the beam-search workload at full size."""
+"""GPU parity of sharing-aware decode.
+
+pa_decode_shared: groups of sequences that share leading blocks (parallel
+samples, beams, prefix reuse) read the shared blocks once. Checked against
+the float64 oracle's decode_shared across head shapes, group sizes (groups
+wider than one item included), work splits, members whose whole context is
+shared, empty sequences, false and clamped declarations, invalid group
+lists, and the beam-search workload at full size.
+
+pa_decode_shared_tree: trees of shared prefixes (beam histories after
+several rounds of forks), each sequence declaring its common prefix with the
+one before it. True declarations give the oracle's plain decode, in batch
+order and in depth-first order, across head shapes, block sizes and work
+splits; the group form's stream bit for bit; clamped, negative and false
+declarations; empty sequences; the beam-search workload at full size."""
 
 import numpy as np
 import pytest
@@ -157,3 +166,150 @@ def test_shared_block_sizes(bs, hq, hkv, d, monkeypatch):
         check_shared(b, starts, shared, f"shared bs={bs} hq={hq} hkv={hkv} d={d} wgs={wgs}")
     check_shared(b, starts, shared + 3, f"shared bs={bs} declared +3 (false, clamped)")
     check_shared(b, starts, np.array([1, -1, 100, 3, 0]), f"shared bs={bs} declared 1/-1/100/3/0")
+
+
+# ---------------------------------------------------------------------------
+# pa_decode_shared_tree: trees of shared prefixes, listed in any order, with
+# each sequence's common prefix with the one before it declared
+# ---------------------------------------------------------------------------
+
+def tree_call(b, sprev, kd=None, vd=None):
+    import paged_kv_cache_433_amd as pa
+    kd = to_dev_bf16(b.k_cache) if kd is None else kd
+    vd = to_dev_bf16(b.v_cache) if vd is None else vd
+    out = pa.decode_shared_tree(to_dev_bf16(b.q), kd, vd, to_dev(b.block_tables), to_dev(b.context_lens),
+                                to_dev(np.asarray(sprev, dtype=np.int32)), float(b.scale))
+    return bits_of(out)
+
+
+def tree_batch(seed, root_lens, beams, rounds, hq, hkv, d, bs=16, max_append=40):
+    nb = sum((p + bs - 1) // bs for p in root_lens) + sum(beams) * rounds * ((max_append + bs - 1) // bs + 2) + 9
+    return W.make_tree_batch("tree", seed, root_lens, beams, rounds, max_append, hq, hkv, d, nb, block_size=bs)
+
+
+def check_tree_orders(b, what, wgs_list=("1", "3", "7", "default"), monkeypatch=None):
+    """Batch order and depth-first order, declarations read back from the
+    tables (true): the oracle's plain decode of the same order is the
+    reference."""
+    ref = oracle.decode(b.q, b.k_cache, b.v_cache, b.block_tables, b.context_lens, b.scale)
+    for name, order in (("batch", np.arange(b.num_seqs)),
+                        ("depth-first", W.tree_order(b.block_tables, b.context_lens, b.block_size))):
+        bp = W.permuted(b, order)
+        sprev = W.declared_chain(bp.block_tables, bp.context_lens, b.block_size)
+        for wgs in wgs_list:
+            if monkeypatch is not None:
+                if wgs == "default":
+                    monkeypatch.delenv("PA_DECODE_WGS", raising=False)
+                else:
+                    monkeypatch.setenv("PA_DECODE_WGS", wgs)
+            note(f"{what} {name} order wgs={wgs}")
+            assert_attention_close(tree_call(bp, sprev), ref[order], f"{what} {name} order wgs={wgs}")
+
+
+@pytest.mark.parametrize("hq,hkv,d", SHAPES)
+def test_tree_across_shapes_orders_and_splits(hq, hkv, d, monkeypatch):
+    # roots held by 4, 9 (several items when G >= 4), 1, 3 and 40 (two items
+    # when G = 1) sequences; three rounds of appends and forks
+    b = tree_batch(700 + hq + d, [100, 512, 16, 37, 64], [4, 9, 1, 3, 40], 3, hq, hkv, d)
+    check_tree_orders(b, f"tree hq={hq} hkv={hkv} d={d}", monkeypatch=monkeypatch)
+
+
+@pytest.mark.parametrize("bs", [8, 32])
+@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (8, 8, 64), (16, 1, 128)])
+def test_tree_block_sizes(bs, hq, hkv, d, monkeypatch):
+    """8- and 32-token blocks: with 8-token blocks an odd count of shared
+    blocks leaves the last to the sequence's own chunk."""
+    b = tree_batch(760 + bs + hq, [24, 100, 8, 40, 63], [4, 9, 1, 3, 5], 4, hq, hkv, d, bs=bs, max_append=30)
+    check_tree_orders(b, f"tree bs={bs} hq={hq} hkv={hkv} d={d}", ("1", "5", "default"), monkeypatch)
+
+
+def test_tree_matches_the_group_form_bit_for_bit():
+    """Groups that share only their prompt, declared as a chain, give the
+    group form's stream, chunk for chunk: the outputs agree bit for bit."""
+    b, starts, shared = batch(781, [4, 9, 1, 3, 40], [100, 512, 16, 37, 64], 32, 8, 128)
+    sprev = W.declared_chain(b.block_tables, b.context_lens)
+    first = np.isin(np.arange(b.num_seqs), starts[:-1])
+    assert np.all(W.chain_sharing(b.context_lens, sprev, b.max_blocks_per_seq)[~first]
+                  == np.repeat(W.effective_sharing(b.context_lens, starts, shared, b.max_blocks_per_seq),
+                               np.diff(starts))[~first])
+    note("tree vs group form")
+    assert np.array_equal(tree_call(b, sprev), shared_call(b, starts, shared))
+
+
+def test_tree_declarations_clamped_negative_and_empty_members():
+    """Declarations past the contexts or the table are clamped (true ones
+    stay exact); negative ones count as none (plain decode); empty
+    sequences inside a run get zeros and break it."""
+    b = tree_batch(790, [64, 130, 20], [5, 6, 3], 2, 32, 8, 128)
+    ref = oracle.decode(b.q, b.k_cache, b.v_cache, b.block_tables, b.context_lens, b.scale)
+    order = W.tree_order(b.block_tables, b.context_lens)
+    bp = W.permuted(b, order)
+    sprev = W.declared_chain(bp.block_tables, bp.context_lens)
+    # where the common prefix covers every whole block both sequences fill,
+    # any larger declaration is clamped back to it
+    n = bp.context_lens.astype(np.int64)
+    full = np.minimum(n, np.r_[0, n[:-1]]) // bp.block_size
+    big = np.where((sprev >= full) & (full > 0), sprev + 1000, sprev)
+    assert np.count_nonzero(big != sprev) >= 3
+    note("tree: declarations + 1000 where clamped")
+    assert_attention_close(tree_call(bp, big), ref[order], "declared + 1000")
+    note("tree: negative declarations")
+    assert_attention_close(tree_call(bp, -np.ones_like(sprev)), ref[order], "declared -1")
+    lens = bp.context_lens.copy()
+    lens[[2, 7]] = 0
+    zb = W.permuted(bp, np.arange(bp.num_seqs))
+    zb.context_lens[:] = lens
+    zref = oracle.decode(zb.q, zb.k_cache, zb.v_cache, zb.block_tables, zb.context_lens, zb.scale)
+    note("tree: empty sequences inside runs")
+    out = tree_call(zb, sprev)
+    assert np.all(out[[2, 7]] == 0)
+    assert_attention_close(out, zref, "empty sequences inside runs")
+
+
+def test_tree_false_declaration_stays_in_its_run():
+    """A false declaration leaves the outputs of the sequences after it in
+    its run unspecified but finite (every read goes through a table row of
+    the batch); runs it does not reach are exact."""
+    b = tree_batch(795, [64, 300, 50], [4, 4, 4], 2, 32, 8, 128)
+    order = W.tree_order(b.block_tables, b.context_lens)
+    bp = W.permuted(b, order)
+    ref = oracle.decode(bp.q, bp.k_cache, bp.v_cache, bp.block_tables, bp.context_lens, bp.scale)
+    sprev = W.declared_chain(bp.block_tables, bp.context_lens)
+    starts = np.flatnonzero(W.chain_sharing(bp.context_lens, sprev, bp.max_blocks_per_seq) == 0)
+    lo = int(starts[1])
+    hi = int(starts[2]) if len(starts) > 2 else bp.num_seqs
+    bad = sprev.copy()
+    bad[lo + 1:hi] += 3                                  # claims 3 blocks more than are shared
+    note("tree: false declaration in one run")
+    out = tree_call(bp, bad)
+    vals = oracle.bf16_bits_to_f64(out)
+    assert np.all(np.isfinite(vals))
+    keep = np.r_[0:lo, hi:bp.num_seqs]
+    assert_attention_close(out[keep], ref[keep], "runs the false declaration does not reach")
+
+
+def test_tree_beam_search_full_size():
+    """The beam-search workload (64 prompts x 4 beams, 1024-token prompts)
+    stepped twice with fork, copy-on-write and scatter; each step decodes in
+    depth-first order with the chain read back from the tables. Every
+    sequence against the oracle."""
+    import paged_kv_cache_433_amd as pa
+    from oracle_pool import oracle_batch
+    note("generate beam_cow for the tree decode")
+    wl = W.BeamSearchWorkload()
+    kd, vd = to_dev_bf16(wl.k_cache), to_dev_bf16(wl.v_cache)
+    kc, vc = wl.k_cache.copy(), wl.v_cache.copy()
+    for step in range(2):
+        b = wl.step()
+        if len(b.cow_pairs):
+            pa.copy_blocks(kd, vd, to_dev(b.cow_pairs))
+        oracle.copy_blocks(kc, vc, b.cow_pairs)
+        pa.reshape_and_cache(to_dev_bf16(b.new_k), to_dev_bf16(b.new_v), kd, vd, to_dev(b.slot_mapping))
+        oracle.reshape_and_cache(kc, vc, b.new_k, b.new_v, b.slot_mapping)
+        bp = W.permuted(b, W.tree_order(b.block_tables, b.context_lens))
+        sprev = W.declared_chain(bp.block_tables, bp.context_lens)
+        e = W.chain_sharing(bp.context_lens, sprev, bp.max_blocks_per_seq)
+        note(f"beam tree step {step}: {int((e > 64).sum())} sequences share past the prompt")
+        out = tree_call(bp, sprev, kd, vd)
+        ref = oracle_batch("decode", bp.q, kc, vc, bp.block_tables, bp.context_lens, bp.scale)
+        assert_attention_close(out, ref, f"beam tree step {step}")

@@ -192,3 +192,103 @@ def test_mirror_catches_a_missing_merge_record():
     bad.desc[-1] = (123456, 999)  # what uninitialised workspace could hold
     with pytest.raises(AssertionError):
         M.merge(bad, M.plain_segments([40, 3], 64), 2, 2)
+
+
+# ---------------------------------------------------------------------------
+# chain form (pa_decode_shared_tree) and the stream each segment walks
+# ---------------------------------------------------------------------------
+
+def tree_case(seed, roots, beams, rounds, bs, max_append=40):
+    from paged_kv_cache_433_amd import workloads as W
+    rng = np.random.default_rng(seed)
+    root_lens = [int(x) for x in rng.integers(0, 120, size=roots)]
+    nb = sum((p + bs - 1) // bs for p in root_lens) + sum(beams) * rounds * ((max_append + bs - 1) // bs + 2) + 9
+    return W.make_tree_batch("tree", seed, root_lens, beams, rounds, max_append, 8, 1, 64, nb, block_size=bs)
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32])
+@pytest.mark.parametrize("hq,hkv", [(32, 8), (8, 8), (16, 4), (48, 4), (16, 1)])
+def test_tree_plans_read_each_members_own_blocks(bs, hq, hkv):
+    """Trees of shared prefixes (beam-search histories), in depth-first and
+    in batch order, with the declarations read back from the tables: every
+    member sees each chunk of its context once, through a table row that
+    names its own blocks, and every output row is written once."""
+    from paged_kv_cache_433_amd import workloads as W
+    for seed, roots, beams, rounds in [(1, 3, [4, 9, 3], 3), (2, 2, [40, 1], 2), (3, 4, [2, 5, 8, 1], 4)]:
+        b = tree_case(seed + bs + hq, roots, beams, rounds, bs)
+        for order in (np.arange(b.num_seqs), W.tree_order(b.block_tables, b.context_lens, bs)):
+            bp = W.permuted(b, order)
+            d = W.declared_chain(bp.block_tables, bp.context_lens, bs)
+            for wgs in (None, 1, 3, 7):
+                M.check_shared(bp.context_lens, [0], [], hq, hkv, bp.max_blocks_per_seq, block_size=bs,
+                               override=wgs, shared_prev=d, tables=bp.block_tables)
+
+
+def test_tree_order_reads_less():
+    """Depth-first order never reads more chunks than batch order, and both
+    read fewer than no sharing when the tree shares anything."""
+    from paged_kv_cache_433_amd import workloads as W
+    b = tree_case(11, 4, [4, 4, 4, 4], 4, 16)
+    chunks = []
+    for order in (np.arange(b.num_seqs), W.tree_order(b.block_tables, b.context_lens)):
+        bp = W.permuted(b, order)
+        d = W.declared_chain(bp.block_tables, bp.context_lens)
+        items, _, _ = M.share_plan(bp.context_lens, [0], [], bp.max_blocks_per_seq, 16, 8, d)
+        chunks.append(sum(it["L"] for it in items))
+    plain = int(((b.context_lens + 15) // 16).sum())
+    assert chunks[1] <= chunks[0] < plain
+
+
+def test_group_form_reads_each_members_own_blocks():
+    """The group form through the same stream model, with tables: true
+    declarations, 8-, 16- and 32-token blocks, groups wider than one item."""
+    from paged_kv_cache_433_amd import workloads as W
+    for bs in (8, 16, 32):
+        for hq, hkv in [(32, 8), (16, 1), (8, 8)]:
+            rng = np.random.default_rng(40 + bs + hq)
+            sizes, plens = [4, 9, 1, 3, 40], [24, 100, 8, 40, 64]
+            privs = rng.integers(0, 50, size=int(sum(sizes)), endpoint=True)
+            privs[::5] = 0
+            nb = sum((p + bs - 1) // bs for p in plens) + int(sum((x + bs) // bs for x in privs)) + 9
+            b, starts, shared = W.make_shared_batch("g", 40 + bs, sizes, plens, privs, 8, 1, 64, nb, block_size=bs)
+            for wgs in (None, 1, 5):
+                M.check_shared(b.context_lens, starts, shared, hq, hkv, b.max_blocks_per_seq, block_size=bs,
+                               override=wgs, tables=b.block_tables)
+
+
+def test_seeded_random_tree_declarations():
+    """Random lengths and arbitrary declarations (negative, past the
+    contexts, past the table): the plan and the streams stay consistent and
+    every output row is written once."""
+    rng = np.random.default_rng(78)
+    for case in range(200):
+        hkv = int(rng.choice([1, 2, 4, 8]))
+        g = int(rng.choice([1, 2, 4, 8, 16]))
+        bs = int(rng.choice([8, 16, 32]))
+        S = int(rng.integers(1, 60))
+        mb = int(rng.integers(1, 30))
+        lens = rng.integers(0, mb * bs + 1, size=S)
+        if case % 4 == 0:
+            lens[rng.integers(0, S)] = 0
+        decl = rng.integers(-3, mb + 4, size=S)
+        wgs = None if case % 3 == 0 else int(rng.integers(1, 300))
+        M.check_shared(lens, [0], [], hkv * g, hkv, mb, block_size=bs, override=wgs, shared_prev=decl)
+
+
+def test_stream_check_catches_a_wrong_visibility_end(monkeypatch):
+    """The stream model fails when a chunk is shown to one member too many
+    (planted on the CPU, in the model's seg_at)."""
+    from paged_kv_cache_433_amd import workloads as W
+    b = tree_case(5, 2, [4, 4], 2, 16)
+    bp = W.permuted(b, W.tree_order(b.block_tables, b.context_lens))
+    d = W.declared_chain(bp.block_tables, bp.context_lens)
+    good = M.seg_at
+
+    def wide(item, lanes, j, b_, nj):
+        c = good(item, lanes, j, b_, nj)
+        return (c[0], min(c[1] + 1, item["ntok"] - 1), *c[2:])
+
+    monkeypatch.setattr(M, "seg_at", wide)
+    with pytest.raises(AssertionError):
+        M.check_shared(bp.context_lens, [0], [], 32, 8, bp.max_blocks_per_seq, shared_prev=d,
+                       tables=bp.block_tables)
