@@ -22,7 +22,7 @@ passage it follows:
   a preempted request's blocks are swapped to CPU and back);
 * "vLLM: Anatomy and Mechanisms", section "Prefix Caching" (prompts with a
   common beginning reuse the cached blocks), read with the CoW section for
-  ``decode_shared``.
+  ``decode_shared``, and for trees of shared prefixes in ``decode_shared_tree``.
 
 Pins: every function here is checked in ``tests/test_oracle_pins.py``
 against facts the pages or mathematics fix (a library routine on the dense
@@ -36,6 +36,7 @@ from .paged_attention import (  # noqa: F401
     decode,
     decode_multi,
     decode_shared,
+    decode_shared_tree,
     decode_sequence,
     reshape_and_cache,
     swap_blocks,

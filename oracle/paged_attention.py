@@ -156,6 +156,39 @@ def decode_shared(q, k_cache, v_cache, block_tables, context_lens, group_starts,
     return decode(q, k_cache, v_cache, tables, context_lens, scale)
 
 
+def decode_shared_tree(q, k_cache, v_cache, block_tables, context_lens, shared_prev, scale) -> np.ndarray:
+    """Decode attention of a batch whose sequences form trees of shared
+    prefixes.
+
+    After a step of beam search the beams that picked the same parent hold
+    all of its full blocks, so the beams of a prompt form a tree of shared
+    prefixes; cached prompt prefixes form one too ("vLLM: Anatomy and
+    Mechanisms", sections "Memory Sharing via Copy-on-Write (CoW)" and
+    "Prefix Caching"). A caller declares, for each sequence ``i > 0``, the
+    leading table entries it has in common with sequence ``i - 1``
+    (``shared_prev[i]``; ``shared_prev[0]`` is ignored).
+
+    Reading (the pages define the sharing, not a call that uses it):
+    sequence ``i`` shares ``e_i = min(shared_prev[i], n_i // block_size,
+    n_{i-1} // block_size)`` blocks with ``i - 1`` (whole blocks both fill,
+    never fewer than none) and reads them as ``i - 1`` reads them: its first
+    ``e_i`` table entries are those of ``i - 1`` after ``i - 1``'s own
+    substitution, so a chain of declarations resolves to the first sequence
+    of the chain. When the declarations are true the tables agree there and
+    the result is ``decode``'s. Returns float64 ``[num_seqs, num_q_heads,
+    head_size]``.
+    """
+    block_size = k_cache.shape[1]
+    n = [int(x) for x in context_lens]
+    declared = np.asarray(shared_prev, dtype=np.int64)
+    assert declared.shape == (len(n),)
+    tables = np.array(block_tables, copy=True)
+    for i in range(1, len(n)):
+        e = max(0, min(int(declared[i]), n[i] // block_size, n[i - 1] // block_size))
+        tables[i, :e] = tables[i - 1, :e]
+    return decode(q, k_cache, v_cache, tables, context_lens, scale)
+
+
 def reshape_and_cache(k_cache, v_cache, k, v, slot_mapping) -> None:
     """Scatter each new token's K and V into its physical slot, in place.
 

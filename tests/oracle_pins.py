@@ -456,6 +456,78 @@ def pin_shared_prefix_clamped(orc):
     assert np.allclose(out[:, 0, :], want[:, None], rtol=0, atol=1e-12), out[:, 0, 0]
 
 
+TREE_CASES = [  # seed, root prompt lengths, sequences per root, rounds, hq, hkv, d
+    (31, [40, 17, 64], [3, 4, 2], 3, 4, 2, 16),
+    (32, [16, 90], [5, 3], 2, 6, 3, 8),
+]
+
+
+def pin_tree_equals_dense(orc):
+    """With the declarations read back from the tables of beam-search trees
+    (batch order and depth-first order), sharing-aware decode is torch's
+    dense attention (fp64, CPU) over each sequence's K/V gathered by hand
+    through its own table; declaring less sharing changes nothing."""
+    for seed, roots, beams, rounds, hq, hkv, d in TREE_CASES:
+        nb = sum((p + 15) // 16 for p in roots) + sum(beams) * rounds * 4 + 9
+        b0 = W.make_tree_batch("pin", seed, roots, beams, rounds, 30, hq, hkv, d, nb)
+        for order in (np.arange(b0.num_seqs), W.tree_order(b0.block_tables, b0.context_lens)):
+            b = W.permuted(b0, order)
+            sprev = W.declared_chain(b.block_tables, b.context_lens)
+            assert W.chain_sharing(b.context_lens, sprev, b.max_blocks_per_seq).max() > 0
+            got = orc.decode_shared_tree(b.q, b.k_cache, b.v_cache, b.block_tables, b.context_lens, sprev, b.scale)
+            assert got.shape == b.q.shape and got.dtype == np.float64
+            for s, n in enumerate(b.context_lens):
+                slots = table_slots(b.block_tables[s], int(n))
+                kb = np.stack([b.k_cache[blk, off] for blk, off in slots])   # [n, Hkv, D]
+                vb = np.stack([b.v_cache[blk, off] for blk, off in slots])
+                k = torch.from_numpy(widen(kb)).permute(1, 0, 2).repeat_interleave(hq // hkv, 0)
+                v = torch.from_numpy(widen(vb)).permute(1, 0, 2).repeat_interleave(hq // hkv, 0)
+                q = torch.from_numpy(widen(b.q[s]))[:, None, :]
+                ref = torch.nn.functional.scaled_dot_product_attention(
+                    q[None], k[None].contiguous(), v[None].contiguous(), scale=float(b.scale))[0, :, 0]
+                err = np.abs(got[s] - ref.numpy()).max()
+                assert err <= 1e-12, (seed, s, err)
+            less = orc.decode_shared_tree(b.q, b.k_cache, b.v_cache, b.block_tables, b.context_lens,
+                                          np.maximum(sprev - 1, 0), b.scale)
+            assert np.array_equal(less, got)
+
+
+def pin_tree_chain_resolves(orc):
+    """A chain of declarations resolves to the first sequence of the chain,
+    even where the tables differ. Sequences 0..2 own blocks (0, 1), (2, 3),
+    (4, 5) and 32 tokens each; 1 shares one block with 0, 2 shares two with
+    1. Constant V blocks, zero K: sequence 0 reads blocks 0, 1 (mean of
+    V = 1, 2: 1.5); 1 reads 0, 3 (2.5); 2 reads what 1 reads, 0 and 3 (2.5).
+    Sequence 3 declares one block in common with 2, so it reads block 0
+    (through the chain) and then its own block 5 (V = 6): 3.5. The first
+    declaration (9) is ignored."""
+    kc, vc = _constant_v_cache(6)
+    tables = np.array([[0, 1], [2, 3], [4, 5], [1, 5]], dtype=np.int32)
+    lens = np.array([32, 32, 32, 32], dtype=np.int32)
+    q = bf16(np.random.default_rng(5).normal(size=(4, 1, 8)))
+    out = orc.decode_shared_tree(q, kc, vc, tables, lens, np.array([9, 1, 2, 1]), np.float32(1.0))
+    want = np.array([1.5, 2.5, 2.5, 3.5])
+    assert np.allclose(out[:, 0, :], want[:, None], rtol=0, atol=1e-12), out[:, 0, 0]
+
+
+def pin_tree_prefix_clamped(orc):
+    """A declaration counts only whole blocks both sequences fill, and never
+    less than none. Sequence 1 (40 tokens, blocks 2, 3, 6) declares 2
+    blocks in common with sequence 0 (20 tokens, blocks 0, 1), which fills
+    only one: it reads block 0 (V = 1), then its own 3 (V = 4) and 8 rows
+    of 6 (V = 7): (16 + 16*4 + 8*7)/40 = 3.4. Sequence 2 declares -1
+    (none): its own blocks 4 and 5, (16*5 + 4*6)/20 = 5.2. Sequence 0 reads
+    its own: (16 + 4*2)/20 = 1.2."""
+    kc, vc = _constant_v_cache(7)
+    pad = 7 + 12345
+    tables = np.array([[0, 1, pad], [2, 3, 6], [4, 5, pad]], dtype=np.int32)
+    lens = np.array([20, 40, 20], dtype=np.int32)
+    q = bf16(np.random.default_rng(6).normal(size=(3, 1, 8)))
+    out = orc.decode_shared_tree(q, kc, vc, tables, lens, np.array([0, 2, -1]), np.float32(1.0))
+    want = np.array([1.2, 3.4, 5.2])
+    assert np.allclose(out[:, 0, :], want[:, None], rtol=0, atol=1e-12), out[:, 0, 0]
+
+
 def pin_widening(orc):
     """bfloat16 patterns widen to the float32 of the same bits: checks a few
     patterns with known values (1, -2, 0.5, smallest normal, largest)."""
@@ -487,5 +559,8 @@ ALL_PINS = [
     pin_shared_equals_dense,
     pin_shared_reads_leader_prefix,
     pin_shared_prefix_clamped,
+    pin_tree_equals_dense,
+    pin_tree_chain_resolves,
+    pin_tree_prefix_clamped,
     pin_widening,
 ]

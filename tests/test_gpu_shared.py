@@ -9,8 +9,8 @@ lists, and the beam-search workload at full size.
 
 pa_decode_shared_tree: trees of shared prefixes (beam histories after
 several rounds of forks), each sequence declaring its common prefix with the
-one before it. True declarations give the oracle's plain decode, in batch
-order and in depth-first order, across head shapes, block sizes and work
+one before it, against the oracle's decode_shared_tree (true declarations:
+the plain decode), in batch order and in depth-first order, across head shapes, block sizes and work
 splits; the group form's stream bit for bit; clamped, negative and false
 declarations; empty sequences; the beam-search workload at full size."""
 
@@ -189,13 +189,14 @@ def tree_batch(seed, root_lens, beams, rounds, hq, hkv, d, bs=16, max_append=40)
 
 def check_tree_orders(b, what, wgs_list=("1", "3", "7", "default"), monkeypatch=None):
     """Batch order and depth-first order, declarations read back from the
-    tables (true): the oracle's plain decode of the same order is the
+    tables (true): the oracle's decode_shared_tree of the same order is the
     reference."""
-    ref = oracle.decode(b.q, b.k_cache, b.v_cache, b.block_tables, b.context_lens, b.scale)
     for name, order in (("batch", np.arange(b.num_seqs)),
                         ("depth-first", W.tree_order(b.block_tables, b.context_lens, b.block_size))):
         bp = W.permuted(b, order)
         sprev = W.declared_chain(bp.block_tables, bp.context_lens, b.block_size)
+        ref = oracle.decode_shared_tree(bp.q, bp.k_cache, bp.v_cache, bp.block_tables, bp.context_lens, sprev,
+                                        bp.scale)
         for wgs in wgs_list:
             if monkeypatch is not None:
                 if wgs == "default":
@@ -203,7 +204,7 @@ def check_tree_orders(b, what, wgs_list=("1", "3", "7", "default"), monkeypatch=
                 else:
                     monkeypatch.setenv("PA_DECODE_WGS", wgs)
             note(f"{what} {name} order wgs={wgs}")
-            assert_attention_close(tree_call(bp, sprev), ref[order], f"{what} {name} order wgs={wgs}")
+            assert_attention_close(tree_call(bp, sprev), ref, f"{what} {name} order wgs={wgs}")
 
 
 @pytest.mark.parametrize("hq,hkv,d", SHAPES)
@@ -253,6 +254,8 @@ def test_tree_declarations_clamped_negative_and_empty_members():
     assert np.count_nonzero(big != sprev) >= 3
     note("tree: declarations + 1000 where clamped")
     assert_attention_close(tree_call(bp, big), ref[order], "declared + 1000")
+    assert np.array_equal(oracle.decode_shared_tree(bp.q, bp.k_cache, bp.v_cache, bp.block_tables,
+                                                    bp.context_lens, big, bp.scale), ref[order])
     note("tree: negative declarations")
     assert_attention_close(tree_call(bp, -np.ones_like(sprev)), ref[order], "declared -1")
     lens = bp.context_lens.copy()
@@ -268,24 +271,34 @@ def test_tree_declarations_clamped_negative_and_empty_members():
 
 def test_tree_false_declaration_stays_in_its_run():
     """A false declaration leaves the outputs of the sequences after it in
-    its run unspecified but finite (every read goes through a table row of
-    the batch); runs it does not reach are exact."""
+    its run unspecified (every read goes through a table row of the batch);
+    runs it does not reach are exact. Where a run is one segment (here 4
+    sequences at 8 query heads per KV head) and blocks hold 16 tokens, the
+    kernel reads the shared chunks through the chain as the oracle's
+    reading does, so the whole output matches it."""
     b = tree_batch(795, [64, 300, 50], [4, 4, 4], 2, 32, 8, 128)
     order = W.tree_order(b.block_tables, b.context_lens)
     bp = W.permuted(b, order)
     ref = oracle.decode(bp.q, bp.k_cache, bp.v_cache, bp.block_tables, bp.context_lens, bp.scale)
     sprev = W.declared_chain(bp.block_tables, bp.context_lens)
-    starts = np.flatnonzero(W.chain_sharing(bp.context_lens, sprev, bp.max_blocks_per_seq) == 0)
-    lo = int(starts[1])
-    hi = int(starts[2]) if len(starts) > 2 else bp.num_seqs
+    e = W.chain_sharing(bp.context_lens, sprev, bp.max_blocks_per_seq)
+    n = bp.context_lens.astype(np.int64)
+    full = np.minimum(n, np.r_[0, n[:-1]]) // bp.block_size   # whole blocks a sequence and the one before fill
+    starts = list(np.flatnonzero(e == 0)) + [bp.num_seqs]
+    # the first run holding a sequence that shares fewer blocks than both fill
+    lo, hi = next((int(a), int(c)) for a, c in zip(starts[:-1], starts[1:]) if np.any(e[a + 1:c] < full[a + 1:c]))
     bad = sprev.copy()
-    bad[lo + 1:hi] += 3                                  # claims 3 blocks more than are shared
+    bad[lo + 1:hi] = full[lo + 1:hi]                     # claims every whole block both fill
     note("tree: false declaration in one run")
     out = tree_call(bp, bad)
     vals = oracle.bf16_bits_to_f64(out)
     assert np.all(np.isfinite(vals))
     keep = np.r_[0:lo, hi:bp.num_seqs]
     assert_attention_close(out[keep], ref[keep], "runs the false declaration does not reach")
+    assert hi - lo <= 4
+    want = oracle.decode_shared_tree(bp.q, bp.k_cache, bp.v_cache, bp.block_tables, bp.context_lens, bad, bp.scale)
+    assert not np.allclose(want[lo:hi], ref[lo:hi])     # the declaration really is false
+    assert_attention_close(out, want, "false declaration, the oracle's reading")
 
 
 def test_tree_beam_search_full_size():

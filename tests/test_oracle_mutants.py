@@ -42,6 +42,14 @@ MUTANTS = {
                                            "e = min(int(shared[g]), full, tables.shape[1])"),
     "group end taken inclusive": ("for j in range(lo + 1, hi):", "for j in range(lo + 1, hi + 1):"),
     "query heads transposed": ("qf = bf16_bits_to_f64(q_s)", "qf = bf16_bits_to_f64(q_s)[::-1]"),
+    "tree prefix read through own table": ("tables[i, :e] = tables[i - 1, :e]", "tables[i, :e] = tables[i, :e]"),
+    "tree chain not followed": ("tables[i, :e] = tables[i - 1, :e]", "tables[i, :e] = block_tables[i - 1, :e]"),
+    "tree prefix clamped to own blocks only": ("n[i] // block_size, n[i - 1] // block_size))",
+                                               "n[i] // block_size))"),
+    "tree negative declaration not clamped": ("e = max(0, min(int(declared[i]), n[i]",
+                                              "e = (min(int(declared[i]), n[i]"),
+    "tree first declaration used": ("for i in range(1, len(n)):\n        e = max(0, min(int(declared[i])",
+                                    "for i in range(0, len(n)):\n        e = max(0, min(int(declared[i])"),
 }
 
 
