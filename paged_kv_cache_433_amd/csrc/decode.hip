@@ -1213,11 +1213,15 @@ __device__ __forceinline__ void no_merge(const DecodeArgs &a, int w, int tid) {
 // NT: 16-column MFMA tiles per wavefront (columns = q_len * group, or the
 // item width in kShared, or 32 per column group in kWide). M: kSingle,
 // kCausal, kWide or kShared. The narrow launches put one wavefront on each
-// SIMD; with two tiles the wavefront may take the whole register file (arch
-// and accumulation registers). kWide runs two wavefronts per SIMD (a
-// workgroup of up to 8 column groups of one KV head), 256 registers each.
+// SIMD. kWide runs two wavefronts per SIMD (a workgroup of up to 8 column
+// groups of one KV head), 256 registers each. Two tiles of several new
+// tokens with 8-token blocks (two loads in flight per row) do not fit in
+// 256 arch registers: that launch bounds its workgroup at 256 threads, so a
+// wavefront may also use accumulation registers (no scratch; 282 against
+// 286 us at 8 new tokens).
 template <int D, int NT, int M, int BS, bool VEC>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NT == 1 || M == kWide ? 2 : 1)))
+__global__ __launch_bounds__(M == kCausal && NT == 2 && BS == 8 ? 256 : 512)
+__attribute__((amdgpu_waves_per_eu(NT == 1 || M == kWide ? 2 : 1)))
 void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const int32_t *__restrict__ lens,
                    const ShareItem *__restrict__ items) {
   constexpr int NJ = D / 32;  // MFMA steps over head_size; 16-byte loads per lane per row
