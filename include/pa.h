@@ -137,7 +137,7 @@ typedef struct pa_kv_cache {
  * context_lens or out NULL while num_seqs > 0), PA_ERR_SHAPE (negative
  * counts, max_blocks_per_seq < 1, num_q_heads % num_kv_heads != 0),
  * PA_ERR_UNSUPPORTED (see pa_kv_cache; group size > 16; q or out not
- * 16-byte aligned), PA_ERR_WORKSPACE
+ * 16-byte aligned; num_seqs > 2^28), PA_ERR_WORKSPACE
  * (too small or misaligned), PA_ERR_HIP. num_seqs == 0 is a no-op.
  */
 int pa_decode(const pa_kv_cache *cache, const void *q, const int32_t *block_tables,

@@ -125,6 +125,9 @@ int check_decode_shape(const pa_kv_cache *c, int32_t num_seqs, int32_t num_q_hea
     return fail(PA_ERR_SHAPE, "max_blocks_per_seq too large");
   if ((int64_t)num_seqs * c->num_kv_heads > 0x7fffffffLL)
     return fail(PA_ERR_SHAPE, "num_seqs * num_kv_heads too large");
+  // The kernels read the context lengths through one buffer resource, whose
+  // range is a 32-bit byte count.
+  if (num_seqs > pa::kMaxDecodeSeqs) return fail(PA_ERR_UNSUPPORTED, "more than 2^28 sequences");
   return PA_OK;
 }
 

@@ -95,6 +95,10 @@ struct SharePlanArgs {
   int32_t block_size;            // tokens per cache block: 8, 16 or 32
 };
 
+// Most sequences one decode call takes: the kernels read the context
+// lengths through one buffer resource, whose range is a 32-bit byte count.
+constexpr int32_t kMaxDecodeSeqs = 1 << 28;
+
 // Most (new token, query head) columns per KV head a decode launch takes:
 // 8 column groups of 32, one wavefront each.
 constexpr int32_t kMaxDecodeCols = 256;

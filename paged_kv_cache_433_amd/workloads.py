@@ -577,6 +577,8 @@ def config_lens(name: str, seed: int):
         return np.tile(np.array([32768, 65536, 98304, 131072]), 2)
     if name == "long_splitk_max":
         return np.full(8, 131072)
+    if name in ("many_short", "many_short_tp8"):
+        return lognormal_lens(r, 4096, 64, 0.5, 16, 256)
     raise KeyError(name)
 
 
@@ -590,6 +592,11 @@ CONFIG_SHAPES = {
     # One GPU's share of the GQA layer under 8-way tensor parallelism: the
     # same sequences and lengths, 32/8 query heads on 8/8 KV heads.
     "llama3_8b_gqa_tp8": (4, 1, 128, 65536, 256, 3),
+    # Many short requests in one batch (serving early in their decode):
+    # 4096 sequences, lognormal lengths with median 64, the GQA layer's heads
+    # and one GPU's share of them at 8-way tensor parallelism.
+    "many_short": (32, 8, 128, 65536, 16, 6),
+    "many_short_tp8": (4, 1, 128, 65536, 16, 6),
 }
 
 

@@ -395,3 +395,49 @@ def check_shared(lens, group_starts, shared_blocks, num_q_heads, num_kv_heads, m
             times = sp.written.get((s, g), 0) + (1 if s in zeroed else 0)
             assert times == 1, f"output of sequence {s}, head group {g} written {times} times"
     return sp
+
+
+def prologue_search(lens, cap: int, nthr: int, NG: int, W: int, w: int, step: bool = False, tile: int = 16):
+    """The decode prologue with more sequences than threads: thread t sums
+    the units of its contiguous range of K = ceil(S / nthr) sequences, read
+    in tiles; an exclusive scan over the threads gives each range's first
+    chunk; the thread whose range holds `lo` walks it again to find the
+    sequence. Returns (total units, lo, hi, found sequence, its first chunk,
+    its length) or None for a workgroup past the last one with units."""
+    S = len(lens)
+    K = (S + nthr - 1) // nthr
+    n_of = [min(max(int(x), 0), cap) for x in lens]
+
+    def chunks(n):
+        return ((n - 1 + CHUNK - 1) // CHUNK + 1 if n > 0 else 0) if step else (n + CHUNK - 1) // CHUNK
+
+    mine = []
+    for t in range(nthr):
+        s0, s1 = min(t * K, S), min(t * K + K, S)
+        acc = 0
+        for s in range(s0, s1, tile):
+            vals = [n_of[s + k] if s + k < S else 0 for k in range(tile)]  # the buffer range reads 0 past S
+            for k in range(tile):
+                if s + k < s1:
+                    acc += chunks(vals[k])
+        mine.append(acc)
+    U = sum(mine) * NG
+    E = min(U, W)
+    if w >= E:
+        return None
+    lo, hi = range_lo(w, U, E), range_lo(w + 1, U, E)
+    found = []
+    excl = 0
+    for t in range(nthr):
+        s0, s1 = min(t * K, S), min(t * K + K, S)
+        if mine[t] > 0 and excl * NG <= lo < (excl + mine[t]) * NG:
+            acc = excl
+            for s in range(s0, s1):
+                L = chunks(n_of[s])
+                if L > 0 and acc * NG <= lo < (acc + L) * NG:
+                    found.append((s, acc, n_of[s]))
+                    break
+                acc += L
+        excl += mine[t]
+    assert len(found) == 1, f"{len(found)} threads found the sequence holding unit {lo}"
+    return (U, lo, hi) + found[0]

@@ -287,3 +287,12 @@ def test_step_argument_errors(L):
     d = desc()
     assert L.pa_decode_step_workspace_bytes(ctypes.byref(d), 256, 32, 256) >= \
         L.pa_decode_workspace_bytes(ctypes.byref(d), 256, 32, 256)
+
+
+def test_num_seqs_limit(L):
+    """The kernels read the context lengths through one buffer resource with
+    a 32-bit byte range: more than 2^28 sequences are refused."""
+    d = desc(num_kv_heads=1)
+    assert L.pa_decode_workspace_bytes(ctypes.byref(d), 1 << 28, 4, 8) > 0
+    assert L.pa_decode_workspace_bytes(ctypes.byref(d), (1 << 28) + 1, 4, 8) == 0
+    assert decode(L, d, S=(1 << 28) + 1, hq=4) == _lib.PA_ERR_UNSUPPORTED

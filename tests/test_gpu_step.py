@@ -112,7 +112,8 @@ def test_step_table_entry_outside_the_pool_skips_the_write():
     assert_attention_close(out, ref, "step: table entry outside the pool")
 
 
-@pytest.mark.parametrize("name", ["llama3_8b_gqa", "llama2_7b", "llama3_8b_gqa_tp8", "long_splitk"])
+@pytest.mark.parametrize("name", ["llama3_8b_gqa", "llama2_7b", "llama3_8b_gqa_tp8", "long_splitk", "many_short",
+                                  "many_short_tp8"])
 def test_step_full_size(name):
     """The full-size workloads with the benchmark's launch configuration:
     every output against the oracle, the whole cache bit for bit."""
@@ -125,3 +126,27 @@ def test_step_full_size(name):
     note(f"step full size {name}: oracle on all {b.num_seqs} sequences")
     ref = oracle_batch("decode", b.q, b.k_cache, b.v_cache, b.block_tables, b.context_lens, b.scale)
     assert_attention_close(out, ref, f"step full size {name}")
+
+
+@pytest.mark.parametrize("hkv", [1, 8])
+def test_step_thousands_of_short_sequences(hkv, monkeypatch):
+    """3000 short sequences, empty ones among them: the prologue's search
+    over ranges of sequences per thread (47 per thread at one wavefront per
+    workgroup, in tiles of 16) across work splits, the whole output and
+    cache against the oracle."""
+    rng = np.random.default_rng(2600 + hkv)
+    lens = rng.integers(1, 70, size=3000)
+    b = small_batch(2600 + hkv, lens, 4 * hkv, hkv, 128, spare=5)
+    ctx = b.context_lens.copy()
+    empty = [0, 1, 15, 16, 17, 63, 64, 1500, 2047, 2048, 2998, 2999]
+    ctx[empty] = 0
+    kc, vc, ref = oracle_step(b, ctx)
+    for wgs in ("default", "1", "333", "5000"):
+        if wgs == "default":
+            monkeypatch.delenv("PA_DECODE_WGS", raising=False)
+        else:
+            monkeypatch.setenv("PA_DECODE_WGS", wgs)
+        out, kd, vd = run_step(b, f"thousands of short sequences hkv={hkv} wgs={wgs}", ctx)
+        assert np.all(out[empty] == 0)
+        assert np.array_equal(kd, kc) and np.array_equal(vd, vc)
+        assert_attention_close(out, ref, f"thousands of short sequences hkv={hkv} wgs={wgs}")

@@ -47,7 +47,7 @@ def test_all_empty_and_lengths_past_the_table():
 
 
 @pytest.mark.parametrize("name", ["llama2_7b", "llama3_8b_gqa", "long_splitk", "long_splitk_max",
-                                  "llama3_8b_gqa_tp8", "tiny_mha"])
+                                  "llama3_8b_gqa_tp8", "tiny_mha", "many_short", "many_short_tp8"])
 def test_full_size_workloads(name):
     hq, hkv, _, _, mb, seed = W.CONFIG_SHAPES[name]
     lens = np.asarray(W.config_lens(name, seed))
@@ -73,7 +73,7 @@ def test_fused_step_splits():
         mb = max((n + 15) // 16 for n in EDGE_LENS)
         for wgs in SPLITS:
             M.check_plain(EDGE_LENS, hq, hkv, mb, override=wgs, step=True)
-    for name in ("llama3_8b_gqa", "llama2_7b", "long_splitk", "llama3_8b_gqa_tp8"):
+    for name in ("llama3_8b_gqa", "llama2_7b", "long_splitk", "llama3_8b_gqa_tp8", "many_short", "many_short_tp8"):
         hq, hkv, _, _, mb, seed = W.CONFIG_SHAPES[name]
         M.check_plain(np.asarray(W.config_lens(name, seed)), hq, hkv, mb, step=True)
     rng = np.random.default_rng(99)
@@ -292,3 +292,39 @@ def test_stream_check_catches_a_wrong_visibility_end(monkeypatch):
     with pytest.raises(AssertionError):
         M.check_shared(bp.context_lens, [0], [], 32, 8, bp.max_blocks_per_seq, shared_prev=d,
                        tables=bp.block_tables)
+
+
+def test_prologue_search_matches_the_definition():
+    """The many-sequence prologue (contiguous ranges per thread, a scan over
+    threads, one thread walking its range) finds, for every workgroup, the
+    sequence whose units hold its first unit, with that sequence's first
+    chunk, as the plain definition does; and every workgroup past the units
+    is told so."""
+    rng = np.random.default_rng(91)
+    for case in range(120):
+        S = int(rng.integers(2, 700))
+        nthr = int(rng.choice([64, 128, 256]))
+        if S <= nthr:
+            S = nthr + int(rng.integers(1, 300))
+        cap = int(rng.choice([64, 512, 4096]))
+        lens = rng.integers(0, cap + 40, size=S)
+        lens[rng.random(S) < 0.2] = 0
+        NG = int(rng.choice([1, 2, 4]))
+        step = bool(case % 2)
+        n = np.minimum(lens, cap)
+        L = np.where(n > 0, (n - 1 + 15) // 16 + 1, 0) if step else (n + 15) // 16
+        starts = np.concatenate([[0], np.cumsum(L)])
+        U = int(starts[-1]) * NG
+        W = int(rng.integers(1, 2 * max(U, 1) + 3))
+        for w in sorted(set(int(x) for x in rng.integers(0, W, size=8)) | {0, W - 1}):
+            got = M.prologue_search(lens, cap, nthr, NG, W, w, step)
+            E = min(U, W)
+            if w >= E:
+                assert got is None
+                continue
+            lo = M.range_lo(w, U, E)
+            s = int(np.searchsorted(starts * NG, lo, side="right")) - 1
+            while L[s] == 0:  # the units of empty sequences are none: the holder is the next non-empty one
+                s += 1
+            assert got[:3] == (U, lo, M.range_lo(w + 1, U, E))
+            assert got[3:] == (s, int(starts[s]), int(n[s])), (case, w, got, s)
