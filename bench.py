@@ -55,6 +55,8 @@ CACHE_NOTES = {
     "beam_cow_shared": "cold in part: a prompt's blocks are read once per group of beams, beams forked from the same "
                        "parent read its history each (about 0.38 GB; the MALL is 256 MB)",
     "beam_cow_tree": "cold in part: every distinct block is read once per call (about 0.35 GB; the MALL is 256 MB)",
+    "beam_cow_shared_planned": "cold in part: as beam_cow_shared, the plan built once before the timed calls",
+    "beam_cow_tree_planned": "cold in part: as beam_cow_tree, the plan built once before the timed calls",
 }
 
 
@@ -361,7 +363,7 @@ def swap_probe(num_blocks: int, steps: int, dev) -> int:
 def workload_name(args) -> str:
     """Key of a workload and call kind in the traffic record."""
     return (args.config + {None: "", "groups": "_shared", "tree": "_tree"}[args.shared]
-            + ("_unfused" if args.unfused else "")
+            + ("_planned" if args.plan_once else "") + ("_unfused" if args.unfused else "")
             + (f"_bs{args.block_size}" if args.block_size != 16 else "") + (f"_q{args.q_len}" if args.q_len > 1 else ""))
 
 
@@ -386,6 +388,9 @@ def main(argv=None) -> int:
                          "groups (the default): pa_decode_shared, a prompt's shared blocks read once for its "
                          "beams; tree: pa_decode_shared_tree over the beams in depth-first order, so beams "
                          "that forked from the same parent also read its history once")
+    ap.add_argument("--plan-once", action="store_true",
+                    help="with --shared: build the sharing plan once (pa_share_plan, as a model does once per step "
+                         "for all its layers) and time the per-layer call pa_decode_shared_planned")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="seconds of oracle work per CPU-baseline run (two runs: all cores, one thread)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -438,6 +443,8 @@ def main(argv=None) -> int:
         if args.shared:
             raise SystemExit("--shared applies to the beam_cow workload")
         b = W.make_config(args.config, q_len=args.q_len, block_size=args.block_size)
+    if args.plan_once and not args.shared:
+        raise SystemExit("--plan-once applies to --shared")
     multi = args.q_len > 1
     fused = not (multi or args.shared or args.unfused)
     if fused:
@@ -490,8 +497,16 @@ def main(argv=None) -> int:
     if pairs is not None:
         step_bytes += W.copy_bytes(len(b.cow_pairs), b.block_size, b.num_kv_heads, b.head_size)
 
+    plan = None
+    if args.plan_once:
+        plan = (pa.share_plan(kc, lens, b.num_q_heads, b.max_blocks_per_seq, shared_prev=sprev_t)
+                if args.shared == "tree" else
+                pa.share_plan(kc, lens, b.num_q_heads, b.max_blocks_per_seq, gstarts_t, gshared_t))
+
     def run_decode():
-        if fused:
+        if plan is not None:
+            pa.decode_shared_planned(q, kc, vc, tables, plan, scale, out=out)
+        elif fused:
             pa.decode_step(q, new_k, new_v, kc, vc, tables, lens, scale, out=out)
         elif args.shared == "tree":
             pa.decode_shared_tree(q, kc, vc, tables, lens, sprev_t, scale, out=out)
@@ -598,7 +613,9 @@ def main(argv=None) -> int:
     achieved_tflops = flops / (dec_mean_us * 1e-6) / 1e12
     mfma_bound = flops / (PEAK_BF16_TFLOPS * 1e12) > decode_bytes / (PEAK_HBM_GBS * 1e9)
     traffic = measured_traffic(workload)
-    if args.shared == "tree":
+    if args.plan_once:
+        kernel = "decode_shared_planned call (plan built once per step): decode_kernel + merge_kernel"
+    elif args.shared == "tree":
         kernel = "decode_shared_tree call: share_plan_kernel + decode_kernel + merge_kernel"
     elif args.shared:
         kernel = "decode_shared call: share_plan_kernel + decode_kernel + merge_kernel"
@@ -633,6 +650,7 @@ def main(argv=None) -> int:
             "q_len": args.q_len,
             "step": ("copy_blocks + " if pairs is not None else "")
                     + ("reshape_and_cache + decode_multi" if multi else
+                       "reshape_and_cache + decode_shared_planned (plan built once)" if args.plan_once else
                        "reshape_and_cache + decode_shared_tree" if args.shared == "tree" else
                        "reshape_and_cache + decode_shared" if args.shared else
                        "decode_step (fused scatter and decode)" if fused else "reshape_and_cache + decode"),

@@ -340,6 +340,51 @@ size_t pa_decode_shared_tree_workspace_bytes(const pa_kv_cache *cache, int32_t n
                                              int32_t max_blocks_per_seq);
 
 /*
+ * pa_share_plan, pa_decode_shared_planned - the two halves of
+ * pa_decode_shared / pa_decode_shared_tree, for a model whose layers all
+ * decode the same batch. The sharing-aware call first builds a plan (which
+ * blocks each segment of sequences reads, from the context lengths and the
+ * declaration alone), then decodes on it. The plan holds nothing of q, the
+ * caches or the output, so within a step it is the same for every layer:
+ * build it once with pa_share_plan, then call pa_decode_shared_planned per
+ * layer. Each planned call gives the result of the one-call form bit for bit.
+ *
+ *   plan          device memory of at least pa_share_plan_bytes(...) bytes,
+ *                 16-byte aligned, owned by the caller. pa_share_plan writes
+ *                 it (stream-ordered); it needs no initialisation.
+ *   pa_share_plan takes the arguments of pa_decode_shared (group form:
+ *                 group_starts, shared_blocks, num_groups) or, when
+ *                 shared_prev is not NULL, of pa_decode_shared_tree (chain
+ *                 form; the group arguments are then ignored), with the same
+ *                 rules and clamps. context_lens is read once, by the plan.
+ *   pa_decode_shared_planned takes q, block_tables, scale, out and a
+ *                 workspace of pa_decode_shared_planned_workspace_bytes(...)
+ *                 (or NULL: allocated stream-ordered by the call), as
+ *                 pa_decode_shared does.
+ * The plan is valid for the cache descriptor's num_kv_heads and block_size,
+ * num_seqs, num_q_heads and max_blocks_per_seq it was made with, and for the
+ * context lengths it read; with other sizes or lengths the output is
+ * unspecified (every access stays inside the arrays the call is given).
+ * Calls that share a plan may overlap; calls that share a workspace may not.
+ * Errors: those of pa_decode_shared, plus PA_ERR_NULL (plan NULL) and
+ * PA_ERR_WORKSPACE (plan smaller than pa_share_plan_bytes or not 16-byte
+ * aligned).
+ */
+size_t pa_share_plan_bytes(const pa_kv_cache *cache, int32_t num_seqs, int32_t num_q_heads,
+                           int32_t max_blocks_per_seq);
+
+int pa_share_plan(const pa_kv_cache *cache, const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                  int32_t max_blocks_per_seq, const int32_t *group_starts, const int32_t *shared_blocks,
+                  int32_t num_groups, const int32_t *shared_prev, void *plan, size_t plan_bytes, void *stream);
+
+size_t pa_decode_shared_planned_workspace_bytes(const pa_kv_cache *cache, int32_t num_seqs, int32_t num_q_heads,
+                                                int32_t max_blocks_per_seq);
+
+int pa_decode_shared_planned(const pa_kv_cache *cache, const void *q, const int32_t *block_tables,
+                             int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq, const void *plan,
+                             float scale, void *out, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * pa_reshape_and_cache - write each new token's K and V into its physical
  * slot before attention runs (the slot the block manager assigned on demand:
  * "vLLM: Anatomy and Mechanisms", section "Block-Level Management"; the

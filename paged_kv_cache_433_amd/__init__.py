@@ -1,7 +1,7 @@
 """MI355X (gfx950) paged KV-cache decode: HIP kernels behind a C ABI.
 
 ``decode``, ``decode_step``, ``decode_noalloc``, ``decode_multi``, ``decode_shared``, ``decode_shared_tree``,
-``reshape_and_cache``,
+``share_plan`` with ``decode_shared_planned``, ``reshape_and_cache``,
 ``copy_blocks`` and ``swap_blocks`` call libpa.so (built
 with ``python -m paged_kv_cache_433_amd.build``); the library is loaded on
 first use and a missing build raises. ``workloads`` makes seeded inputs.
@@ -15,6 +15,7 @@ from .ops import (  # noqa: F401
     decode_noalloc,
     decode_multi_workspace_bytes,
     decode_shared,
+    decode_shared_planned,
     decode_shared_tree,
     decode_shared_tree_workspace_bytes,
     decode_step,
@@ -24,5 +25,6 @@ from .ops import (  # noqa: F401
     probe_read,
     probe_read_sink_bytes,
     reshape_and_cache,
+    share_plan,
     swap_blocks,
 )

@@ -26,6 +26,8 @@ EXPORTS = ("pa_decode", "pa_decode_workspace_bytes", "pa_decode_noalloc",
            "pa_decode_multi", "pa_decode_multi_workspace_bytes",
            "pa_decode_shared", "pa_decode_shared_workspace_bytes",
            "pa_decode_shared_tree", "pa_decode_shared_tree_workspace_bytes",
+           "pa_share_plan", "pa_share_plan_bytes", "pa_decode_shared_planned",
+           "pa_decode_shared_planned_workspace_bytes",
            "pa_reshape_and_cache", "pa_copy_blocks",
            "pa_swap_blocks", "pa_last_error", "pa_probe_copy", "pa_probe_read", "pa_probe_read_sink_bytes")
 
@@ -74,6 +76,14 @@ def _declare(lib):
     lib.pa_decode_shared_tree.restype = ctypes.c_int
     lib.pa_decode_shared_tree_workspace_bytes.argtypes = [D, I32, I32, I32]
     lib.pa_decode_shared_tree_workspace_bytes.restype = SZ
+    lib.pa_share_plan.argtypes = [D, P, I32, I32, I32, P, P, I32, P, P, SZ, P]
+    lib.pa_share_plan.restype = ctypes.c_int
+    lib.pa_share_plan_bytes.argtypes = [D, I32, I32, I32]
+    lib.pa_share_plan_bytes.restype = SZ
+    lib.pa_decode_shared_planned.argtypes = [D, P, P, I32, I32, I32, P, ctypes.c_float, P, P, SZ, P]
+    lib.pa_decode_shared_planned.restype = ctypes.c_int
+    lib.pa_decode_shared_planned_workspace_bytes.argtypes = [D, I32, I32, I32]
+    lib.pa_decode_shared_planned_workspace_bytes.restype = SZ
     lib.pa_reshape_and_cache.argtypes = [D, P, P, P, I32, P]
     lib.pa_reshape_and_cache.restype = ctypes.c_int
     lib.pa_copy_blocks.argtypes = [D, P, I32, P]

@@ -263,6 +263,7 @@ struct Walker {
   const int32_t *lens;
   const ShareItem *items;
   int S, NG, cap;  // S: sequences, or items in kShared
+  int S_rows;      // kShared: the batch's sequences (q and output rows)
   long long u, hi, seg_base;
   int s, hg, off, L, n;
   int row, qrow, ntok, b0, eb;
@@ -271,13 +272,17 @@ struct Walker {
 
 // The item's fields are uniform; readfirstlane keeps them in scalar
 // registers (the buffer ranges and table reads built from them must be).
+// The rows an item names are clamped to the batch (num_seqs = wk.S_rows),
+// so a plan made for other sizes gives wrong results, never an access
+// outside q, the tables or the output.
 __device__ __forceinline__ void take_item(Walker &wk, const ShareItem &x) {
+  const int S = wk.S_rows;
   wk.eb = __builtin_amdgcn_readfirstlane(x.eb);
   wk.L = __builtin_amdgcn_readfirstlane(x.L);
   wk.n = __builtin_amdgcn_readfirstlane(x.n);
-  wk.row = __builtin_amdgcn_readfirstlane(x.row);
-  wk.qrow = __builtin_amdgcn_readfirstlane(x.qrow);
-  wk.ntok = __builtin_amdgcn_readfirstlane(x.ntok);
+  wk.row = min(max(__builtin_amdgcn_readfirstlane(x.row), 0), S - 1);
+  wk.qrow = min(max(__builtin_amdgcn_readfirstlane(x.qrow), 0), S - 1);
+  wk.ntok = min(max(__builtin_amdgcn_readfirstlane(x.ntok), 1), S - wk.qrow);
   wk.b0 = __builtin_amdgcn_readfirstlane(x.b0);
 }
 
@@ -535,10 +540,10 @@ __device__ __forceinline__ int block_id(const int32_t *__restrict__ tables, cons
 // j's: its context length (x) and the chunks before its own (y), those it
 // holds in common with member j - 1. Lanes past the last member read {0, 0}.
 // y is clamped to the member's chunks, so no count below goes negative.
-__device__ __forceinline__ int2 member_info(const int32_t *__restrict__ members, const Piece &p, int lane) {
+__device__ __forceinline__ int2 member_info(const int32_t *__restrict__ members, const Piece &p, int lane, int cap) {
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int32_t *>(members + 2 * (size_t)p.qrow), 0, p.ntok * 2 * (int)sizeof(int32_t), kRawBufferWord3);
-  const int n = max((int)__builtin_amdgcn_raw_buffer_load_b32(r, lane * 8, 0, 0), 0);
+  const int n = clamp_len((int)__builtin_amdgcn_raw_buffer_load_b32(r, lane * 8, 0, 0), cap);
   const int y = (int)__builtin_amdgcn_raw_buffer_load_b32(r, lane * 8 + 4, 0, 0);
   return int2{n, min(max(y, 0), (n + kBlock - 1) >> 4)};
 }
@@ -1059,7 +1064,7 @@ __device__ __forceinline__ void advance(const DecodeArgs &a, const Lane<NT> &ln,
   st.hoff_q = head_off<NJ, M>(ln, st.Q);
   if constexpr (M == kShared) {
     st.mv_p = st.mv_q;
-    st.mv_q = member_info(wk.lens, st.Q, ln.lane);
+    st.mv_q = member_info(wk.lens, st.Q, ln.lane, wk.cap);
   }
 }
 
@@ -1214,6 +1219,22 @@ __device__ __forceinline__ void no_merge(const DecodeArgs &a, int w, int tid) {
   if (tid == 0 && a.merge_desc) a.merge_desc[w] = int2{-1, -1};
 }
 
+// kShared: a segment with no chunk (every member's context empty) is not
+// decoded; its members' output rows are zeroed here, segment v by workgroup
+// v mod num_wgs, all threads of the workgroup together. The plan counts such
+// segments, so calls without them skip this.
+template <int D>
+__device__ __forceinline__ void zero_empty_items(const DecodeArgs &a, const ShareItem *__restrict__ items, int nitems,
+                                                 int w, int tid, int nthr) {
+  const int row_vec = a.num_q_heads * D / 8;  // 16-byte vectors per q row
+  for (int v = w; v < nitems; v += a.num_wgs) {
+    const ShareItem x = items[v];
+    if (x.L != 0 || x.qrow < 0 || x.ntok < 1 || x.ntok > a.num_seqs - x.qrow) continue;
+    u32x4_t *row = reinterpret_cast<u32x4_t *>(a.out) + (size_t)x.qrow * row_vec;
+    for (int k = tid; k < x.ntok * row_vec; k += nthr) row[k] = u32x4_t{0u, 0u, 0u, 0u};
+  }
+}
+
 // NT: 16-column MFMA tiles per wavefront (columns = q_len * group, or the
 // item width in kShared, or 32 per column group in kWide). M: kSingle,
 // kCausal, kWide or kShared. The narrow launches put one wavefront on each
@@ -1248,14 +1269,18 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
 
   long long U, lo, hi, E;
   Walker wk;
+  int sh_items = 0, sh_empty = 0;  // kShared: the plan's segments, and those with no chunk
   if constexpr (M == kShared) {
     // The plan kernel wrote the items and their first units; one parallel
     // search finds the item that holds `lo` (empty items never match).
     ShareHeader h = *a.share;
     h.items = min(max(h.items, 0), S);  // the plan writes at most one segment per sequence
+    sh_items = h.items;
+    sh_empty = h.empty;
     U = h.units;
     E = U < W ? U : W;
     if (w >= E) {  // every workgroup writes its merge record, this one "none"
+      if (sh_empty > 0) zero_empty_items<D>(a, items, sh_items, w, tid, nthr);
       no_merge(a, w, tid);
       return;
     }
@@ -1275,6 +1300,7 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
     wk.lens = lens;
     wk.cap = cap;
     wk.S = h.items;
+    wk.S_rows = S;
     take_item(wk, items[v]);
     wk.s = v;
     const long long us = items[v].ustart;
@@ -1448,8 +1474,8 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
   if (!st.has_q) st.Q = st.P;
   st.hoff_q = head_off<NJ, M>(ln, st.Q);
   if constexpr (M == kShared) {
-    st.mv_p = member_info(lens, st.P, lane);
-    st.mv_q = member_info(lens, st.Q, lane);
+    st.mv_p = member_info(lens, st.P, lane, cap);
+    st.mv_q = member_info(lens, st.Q, lane, cap);
     st.cc = seg_first(st.P, st.mv_p, lane);
   }
   st.i = 0;
@@ -1475,6 +1501,9 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
          step<NJ, NT, M, BS, VEC>(tables, a, ln, wk, st, KB, VB, KA, VA, q_lds)) {
   }
   finish_stream<NJ, NT, M, defers<NT, BS>()>(a, ln, st, q_lds);
+  if constexpr (M == kShared) {
+    if (sh_empty > 0) zero_empty_items<D>(a, items, sh_items, w, tid, nthr);
+  }
 }
 
 // Log-sum-exp merge of the pieces of segments cut by workgroup boundaries.
@@ -1637,15 +1666,17 @@ __device__ __forceinline__ int wg_max_scan(int v, int *red, int wave, int lane, 
 //     first member reads all its chunks, member i the others from c_i on.
 // Both forms: units follow segment order, head group major within a segment.
 // A segment with no chunk at all (every member's context empty) is not
-// decoded: its members' outputs are zeroed here. Each sequence's record
-// (context length, chunks before its own) goes to `members` for the decode.
+// decoded: the header counts them, and the decode kernel zeroes their
+// members' rows. Each sequence's record (context length, chunks before its
+// own) goes to `members` for the decode. Nothing here depends on q, the
+// caches or the output, so one plan serves every layer of a step.
 template <int kThreads>
 __global__ __launch_bounds__(kThreads) void share_plan_kernel(const SharePlanArgs p) {
   // grp[S], sid[S], own[S], len[S], shb[G], gs[G + 1], then csum[S] (64-bit)
   extern __shared__ __align__(16) int plan_lds[];
   __shared__ long long red[kThreads / 64];
   __shared__ int redi[kThreads / 64];
-  __shared__ int bad;
+  __shared__ int bad, empties;
   constexpr int nwaves = kThreads / 64;
   const bool chain = p.shared_prev != nullptr;
   const int S = p.num_seqs, NGr = chain ? 0 : p.num_groups, C = p.members_per_item;
@@ -1662,7 +1693,7 @@ __global__ __launch_bounds__(kThreads) void share_plan_kernel(const SharePlanArg
 
   // Every input into LDS first: their loads are independent, so the plan
   // waits for memory once.
-  if (tid == 0) bad = 0;
+  if (tid == 0) bad = empties = 0;
   for (int i = tid; i < S; i += kThreads) {
     grp[i] = -1;
     len[i] = clamp_len(p.lens[i], cap);
@@ -1775,11 +1806,9 @@ __global__ __launch_bounds__(kThreads) void share_plan_kernel(const SharePlanArg
     x.L = (int)blocks;
     x.ustart = NG * start;
     p.items[sid[i]] = x;
-    if (blocks == 0) {  // every member's context is empty
-      u32x4_t *row = reinterpret_cast<u32x4_t *>(p.out + (size_t)i * p.row_elems);
-      for (size_t k = 0; k < (size_t)ntok * p.row_elems / 8; ++k) row[k] = u32x4_t{0, 0, 0, 0};
-    }
+    if (blocks == 0) atomicAdd(&empties, 1);  // LDS atomic: a segment with no chunk
   }
+  __syncthreads();
   if (tid == 0) {
     const long long units = NG * blocks_before;
     ShareItem x = {0, 0, 0, 0, 0, 0, units, 0};
@@ -1787,6 +1816,7 @@ __global__ __launch_bounds__(kThreads) void share_plan_kernel(const SharePlanArg
     ShareHeader h;
     h.units = units;
     h.items = (int)segs_before;
+    h.empty = empties;
     *p.share = h;
   }
 }
@@ -1906,18 +1936,12 @@ hipError_t launch_decode(const DecodeArgs &args, int32_t head_size, hipStream_t 
   return hipGetLastError();
 }
 
-hipError_t launch_decode_shared(const SharePlanArgs &plan, const DecodeArgs &call, int32_t head_size,
-                                hipStream_t stream) {
-  // The decode reads the plan's member records where other launches read
-  // the context lengths.
-  DecodeArgs args = call;
-  args.context_lens = plan.members;
-  if (!plan.members || !plan.lens || args.q_len != 1 || (args.block_size != 8 && args.block_size != 16 && args.block_size != 32) ||
-      plan.block_size != args.block_size || args.num_cols <= 16 || args.num_cols > 32 || !args.items || !args.share ||
-      plan.num_seqs < 1 || plan.num_seqs > kMaxSharedSeqs || plan.num_groups < 0 ||
-      plan.num_groups > plan.num_seqs || plan.members_per_item < 1 || !plan.out || plan.row_elems % 8)
+hipError_t launch_share_plan(const SharePlanArgs &plan, hipStream_t stream) {
+  if (!plan.members || !plan.lens || !plan.items || !plan.share ||
+      (plan.block_size != 8 && plan.block_size != 16 && plan.block_size != 32) || plan.num_seqs < 1 ||
+      plan.num_seqs > kMaxSharedSeqs || plan.num_groups < 0 || plan.num_groups > plan.num_seqs ||
+      plan.members_per_item < 1 || plan.num_head_groups < 1)
     return hipErrorInvalidValue;
-  if (head_size != 128 && head_size != 64) return hipErrorInvalidValue;
   constexpr int kPlanThreads = 512;
   const size_t plan_lds =
       ((4 * (size_t)plan.num_seqs + 2 * (size_t)(plan.shared_prev ? 0 : plan.num_groups) + 2) & ~(size_t)1) *
@@ -1926,8 +1950,16 @@ hipError_t launch_decode_shared(const SharePlanArgs &plan, const DecodeArgs &cal
   hipError_t e = allow_lds(share_plan_kernel<kPlanThreads>, plan_lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(share_plan_kernel<kPlanThreads>, dim3(1), dim3(kPlanThreads), plan_lds, stream, plan);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_planned(const DecodeArgs &args, int32_t head_size, hipStream_t stream) {
+  if (args.q_len != 1 || (args.block_size != 8 && args.block_size != 16 && args.block_size != 32) ||
+      args.num_cols <= 16 || args.num_cols > 32 || !args.items || !args.share || !args.context_lens ||
+      args.num_seqs < 1 || args.num_seqs > kMaxSharedSeqs)
+    return hipErrorInvalidValue;
+  if (head_size != 128 && head_size != 64) return hipErrorInvalidValue;
+  hipError_t e;
   // q of the current piece in LDS: one [num_cols][D] slot per wavefront.
   const size_t lds = (size_t)args.heads_per_wg * args.num_cols * head_size * sizeof(uint16_t);
   if (head_size == 128)

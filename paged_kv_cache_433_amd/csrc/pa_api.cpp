@@ -191,24 +191,90 @@ int check_shared(const pa_kv_cache *c, int32_t num_seqs, int32_t num_groups) {
   return PA_OK;
 }
 
+// The checks every sharing-aware call makes on its shape.
+int check_shared_shape(const pa_kv_cache *cache, int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
+                       int32_t num_groups, bool data) {
+  int rc = check_cache(cache, data);
+  if (rc != PA_OK) return rc;
+  rc = check_decode_shape(cache, num_seqs, num_q_heads, max_blocks_per_seq);
+  if (rc != PA_OK) return rc;
+  return check_shared(cache, num_seqs, num_groups);
+}
+
+// Launches the plan kernel into a plan buffer laid out as the front of a
+// SharedLayout (header, segments, member records).
+hipError_t launch_plan(const pa_kv_cache *cache, const SharedLayout &l, const int32_t *context_lens, int32_t num_seqs,
+                       int32_t num_q_heads, int32_t max_blocks_per_seq, const int32_t *group_starts,
+                       const int32_t *shared_blocks, int32_t num_groups, const int32_t *shared_prev, char *plan,
+                       hipStream_t hs) {
+  pa::SharePlanArgs p{};
+  p.lens = context_lens;
+  p.group_starts = group_starts;
+  p.shared_blocks = shared_blocks;
+  p.shared_prev = shared_prev;
+  p.members = reinterpret_cast<int32_t *>(plan + l.members_off);
+  p.items = reinterpret_cast<pa::ShareItem *>(plan + l.items_off);
+  p.share = reinterpret_cast<pa::ShareHeader *>(plan);
+  p.num_seqs = num_seqs;
+  p.num_groups = shared_prev ? 0 : num_groups;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.group = num_q_heads / cache->num_kv_heads;
+  p.members_per_item = members_per_item(p.group);
+  p.num_head_groups = l.plan.num_head_groups;
+  p.block_size = cache->block_size;
+  return pa::launch_share_plan(p, hs);
+}
+
+// Launches decode and merge on a plan; `run` is the call's scratch (merge
+// records, then partial records), laid out as the back of a SharedLayout.
+hipError_t launch_planned(const pa_kv_cache *cache, const SharedLayout &l, const void *q, const int32_t *block_tables,
+                          int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq, const char *plan,
+                          float scale, void *out, char *run, hipStream_t hs) {
+  pa::DecodeArgs a{};
+  a.q = static_cast<const uint16_t *>(q);
+  a.k_cache = static_cast<const uint16_t *>(cache->k_cache);
+  a.v_cache = static_cast<const uint16_t *>(cache->v_cache);
+  a.block_tables = block_tables;
+  a.context_lens = reinterpret_cast<const int32_t *>(plan + l.members_off);  // the member records
+  a.out = static_cast<uint16_t *>(out);
+  a.merge_desc = reinterpret_cast<int2 *>(run);
+  a.part_ml = reinterpret_cast<float *>(run + (l.ml_off - l.desc_off));
+  a.part_o = reinterpret_cast<float *>(run + (l.o_off - l.desc_off));
+  a.num_blocks = cache->num_blocks;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.group = num_q_heads / cache->num_kv_heads;
+  a.q_len = 1;
+  a.num_cols = l.cols;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.block_size = cache->block_size;
+  a.heads_per_wg = l.plan.heads_per_wg;
+  a.num_head_groups = l.plan.num_head_groups;
+  a.col_groups = 1;
+  a.rec_cols = l.cols;
+  a.num_wgs = l.plan.num_wgs;
+  a.scale_log2 = scale * 1.44269504088896340736f;
+  a.items = reinterpret_cast<const pa::ShareItem *>(plan + l.items_off);
+  a.share = reinterpret_cast<const pa::ShareHeader *>(plan);
+  return pa::launch_decode_planned(a, cache->head_size, hs);
+}
+
 // Checks, plans and launches a sharing-aware call: the group form, or
-// (shared_prev non-null) the chain form.
+// (shared_prev non-null) the chain form. The workspace holds the plan, then
+// the call's scratch.
 int shared_impl(const pa_kv_cache *cache, const void *q, const int32_t *block_tables, const int32_t *context_lens,
                 int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq, const int32_t *group_starts,
                 const int32_t *shared_blocks, int32_t num_groups, const int32_t *shared_prev, float scale, void *out,
                 void *workspace, size_t workspace_bytes, void *stream) {
   const char *name = shared_prev ? "pa_decode_shared_tree" : "pa_decode_shared";
-  int rc = check_cache(cache, num_seqs > 0);
-  if (rc != PA_OK) return rc;
-  rc = check_decode_shape(cache, num_seqs, num_q_heads, max_blocks_per_seq);
-  if (rc != PA_OK) return rc;
-  rc = check_shared(cache, num_seqs, num_groups);
+  int rc = check_shared_shape(cache, num_seqs, num_q_heads, max_blocks_per_seq, num_groups, num_seqs > 0);
   if (rc != PA_OK) return rc;
   if (num_seqs == 0) return ok();
   if (!q || !block_tables || !context_lens || !out)
     return fail(PA_ERR_NULL, "q, block_tables, context_lens or out is NULL");
   if (check_aligned(q, "q") != PA_OK || check_aligned(out, "out") != PA_OK) return PA_ERR_UNSUPPORTED;
-  if (num_groups > 0 && (!group_starts || !shared_blocks))
+  if (num_groups > 0 && !shared_prev && (!group_starts || !shared_blocks))
     return fail(PA_ERR_NULL, "group_starts or shared_blocks is NULL");
 
   const SharedLayout l = layout_shared(cache, num_seqs, num_q_heads, max_blocks_per_seq);
@@ -226,56 +292,11 @@ int shared_impl(const pa_kv_cache *cache, const void *q, const int32_t *block_ta
     owned = true;
   }
   char *base = static_cast<char *>(ws);
-  pa::ShareHeader *hdr = reinterpret_cast<pa::ShareHeader *>(base);
-  pa::ShareItem *items = reinterpret_cast<pa::ShareItem *>(base + l.items_off);
-
-  pa::DecodeArgs a{};
-  a.q = static_cast<const uint16_t *>(q);
-  a.k_cache = static_cast<const uint16_t *>(cache->k_cache);
-  a.v_cache = static_cast<const uint16_t *>(cache->v_cache);
-  a.block_tables = block_tables;
-  a.context_lens = context_lens;
-  a.out = static_cast<uint16_t *>(out);
-  a.merge_desc = reinterpret_cast<int2 *>(base + l.desc_off);
-  a.part_ml = reinterpret_cast<float *>(base + l.ml_off);
-  a.part_o = reinterpret_cast<float *>(base + l.o_off);
-  a.num_blocks = cache->num_blocks;
-  a.num_seqs = num_seqs;
-  a.num_q_heads = num_q_heads;
-  a.num_kv_heads = cache->num_kv_heads;
-  a.group = num_q_heads / cache->num_kv_heads;
-  a.q_len = 1;
-  a.num_cols = l.cols;
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.block_size = cache->block_size;
-  a.heads_per_wg = l.plan.heads_per_wg;
-  a.num_head_groups = l.plan.num_head_groups;
-  a.col_groups = 1;
-  a.rec_cols = l.cols;
-  a.num_wgs = l.plan.num_wgs;
-  a.scale_log2 = scale * 1.44269504088896340736f;
-  a.items = items;
-  a.share = hdr;
-
-  pa::SharePlanArgs p{};
-  p.lens = context_lens;
-  p.group_starts = group_starts;
-  p.shared_blocks = shared_blocks;
-  p.shared_prev = shared_prev;
-  p.members = reinterpret_cast<int32_t *>(base + l.members_off);
-  p.items = items;
-  p.share = hdr;
-  p.out = static_cast<uint16_t *>(out);
-  p.row_elems = num_q_heads * cache->head_size;
-  p.num_seqs = num_seqs;
-  p.num_groups = num_groups;
-  p.max_blocks_per_seq = max_blocks_per_seq;
-  p.members_per_item = members_per_item(a.group);
-  p.group = a.group;
-  p.num_head_groups = a.num_head_groups;
-  p.block_size = cache->block_size;
-
-  hipError_t e = pa::launch_decode_shared(p, a, cache->head_size, hs);
+  hipError_t e = launch_plan(cache, l, context_lens, num_seqs, num_q_heads, max_blocks_per_seq, group_starts,
+                             shared_blocks, num_groups, shared_prev, base, hs);
+  if (e == hipSuccess)
+    e = launch_planned(cache, l, q, block_tables, num_seqs, num_q_heads, max_blocks_per_seq, base, scale, out,
+                       base + l.desc_off, hs);
   if (owned) {
     hipError_t fe = hipFreeAsync(ws, hs);
     if (e == hipSuccess) e = fe;
@@ -500,6 +521,73 @@ int pa_decode_shared_tree(const pa_kv_cache *cache, const void *q, const int32_t
   if (num_seqs > 0 && !shared_prev) return fail(PA_ERR_NULL, "shared_prev is NULL");
   return shared_impl(cache, q, block_tables, context_lens, num_seqs, num_q_heads, max_blocks_per_seq, nullptr,
                      nullptr, 0, shared_prev, scale, out, workspace, workspace_bytes, stream);
+}
+
+size_t pa_share_plan_bytes(const pa_kv_cache *cache, int32_t num_seqs, int32_t num_q_heads,
+                           int32_t max_blocks_per_seq) {
+  if (check_shared_shape(cache, num_seqs, num_q_heads, max_blocks_per_seq, 0, false) != PA_OK || num_seqs == 0)
+    return 0;
+  return layout_shared(cache, num_seqs, num_q_heads, max_blocks_per_seq).desc_off;
+}
+
+int pa_share_plan(const pa_kv_cache *cache, const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                  int32_t max_blocks_per_seq, const int32_t *group_starts, const int32_t *shared_blocks,
+                  int32_t num_groups, const int32_t *shared_prev, void *plan, size_t plan_bytes, void *stream) {
+  int rc = check_shared_shape(cache, num_seqs, num_q_heads, max_blocks_per_seq, shared_prev ? 0 : num_groups, false);
+  if (rc != PA_OK) return rc;
+  if (num_seqs == 0) return ok();
+  if (!context_lens || !plan) return fail(PA_ERR_NULL, "context_lens or plan is NULL");
+  if (!shared_prev && num_groups > 0 && (!group_starts || !shared_blocks))
+    return fail(PA_ERR_NULL, "group_starts or shared_blocks is NULL");
+  const SharedLayout l = layout_shared(cache, num_seqs, num_q_heads, max_blocks_per_seq);
+  if (plan_bytes < l.desc_off) return fail(PA_ERR_WORKSPACE, "plan smaller than pa_share_plan_bytes()");
+  if (reinterpret_cast<uintptr_t>(plan) % 16) return fail(PA_ERR_WORKSPACE, "plan must be 16-byte aligned");
+  const hipError_t e = launch_plan(cache, l, context_lens, num_seqs, num_q_heads, max_blocks_per_seq, group_starts,
+                                   shared_blocks, num_groups, shared_prev, static_cast<char *>(plan),
+                                   static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "pa_share_plan launch");
+  return ok();
+}
+
+size_t pa_decode_shared_planned_workspace_bytes(const pa_kv_cache *cache, int32_t num_seqs, int32_t num_q_heads,
+                                                int32_t max_blocks_per_seq) {
+  if (check_shared_shape(cache, num_seqs, num_q_heads, max_blocks_per_seq, 0, false) != PA_OK || num_seqs == 0)
+    return 0;
+  const SharedLayout l = layout_shared(cache, num_seqs, num_q_heads, max_blocks_per_seq);
+  return l.total - l.desc_off;
+}
+
+int pa_decode_shared_planned(const pa_kv_cache *cache, const void *q, const int32_t *block_tables,
+                             int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq, const void *plan,
+                             float scale, void *out, void *workspace, size_t workspace_bytes, void *stream) {
+  int rc = check_shared_shape(cache, num_seqs, num_q_heads, max_blocks_per_seq, 0, num_seqs > 0);
+  if (rc != PA_OK) return rc;
+  if (num_seqs == 0) return ok();
+  if (!q || !block_tables || !plan || !out) return fail(PA_ERR_NULL, "q, block_tables, plan or out is NULL");
+  if (check_aligned(q, "q") != PA_OK || check_aligned(out, "out") != PA_OK) return PA_ERR_UNSUPPORTED;
+  if (reinterpret_cast<uintptr_t>(plan) % 16) return fail(PA_ERR_WORKSPACE, "plan must be 16-byte aligned");
+  const SharedLayout l = layout_shared(cache, num_seqs, num_q_heads, max_blocks_per_seq);
+  const size_t need = l.total - l.desc_off;
+  if (workspace && workspace_bytes < need)
+    return fail(PA_ERR_WORKSPACE, "workspace smaller than pa_decode_shared_planned_workspace_bytes()");
+  if (workspace && reinterpret_cast<uintptr_t>(workspace) % 16)
+    return fail(PA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  void *ws = workspace;
+  bool owned = false;
+  if (!ws) {
+    hipError_t e = hipMallocAsync(&ws, need, hs);
+    if (e != hipSuccess) return hip_fail(e, "hipMallocAsync(workspace)");
+    owned = true;
+  }
+  hipError_t e = launch_planned(cache, l, q, block_tables, num_seqs, num_q_heads, max_blocks_per_seq,
+                                static_cast<const char *>(plan), scale, out, static_cast<char *>(ws), hs);
+  if (owned) {
+    hipError_t fe = hipFreeAsync(ws, hs);
+    if (e == hipSuccess) e = fe;
+  }
+  if (e != hipSuccess) return hip_fail(e, "pa_decode_shared_planned launch");
+  return ok();
 }
 
 int pa_reshape_and_cache(const pa_kv_cache *cache, const void *k, const void *v,

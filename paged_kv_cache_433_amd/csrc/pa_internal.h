@@ -36,7 +36,7 @@ struct ShareItem {
 struct ShareHeader {
   int64_t units;
   int32_t items;   // segments
-  int32_t pad;
+  int32_t empty;   // segments with no chunk (every member's context empty): the decode zeroes their rows
 };
 
 // Arguments of one decode launch, passed by value as the kernel argument.
@@ -84,8 +84,6 @@ struct SharePlanArgs {
   int32_t *members;              // [S][2] out: clamped context length, chunks read through a predecessor
   ShareItem *items;
   ShareHeader *share;
-  uint16_t *out;                 // zeroed for segments whose members are all empty
-  int32_t row_elems;             // num_q_heads * head_size
   int32_t num_seqs;
   int32_t num_groups;
   int32_t max_blocks_per_seq;
@@ -137,11 +135,16 @@ hipError_t noalloc_scratch(void **ptr);
 // and per-group state in LDS).
 constexpr int32_t kMaxSharedSeqs = 4096;
 
-// Plan, decode and merge of a sharing-aware call. args.num_cols is the
-// segment width (members_per_item * group), args.q_len is 1; the decode
-// reads plan.members in place of args.context_lens.
-hipError_t launch_decode_shared(const SharePlanArgs &plan, const DecodeArgs &args, int32_t head_size,
-                                hipStream_t stream);
+// The plan of a sharing-aware call: its segments (plan.items, plan.share)
+// and member records (plan.members), from the context lengths and the
+// declaration alone.
+hipError_t launch_share_plan(const SharePlanArgs &plan, hipStream_t stream);
+
+// Decode and merge of a sharing-aware call on a plan: args.items, args.share
+// and, in place of the context lengths, args.context_lens = the plan's
+// member records. args.num_cols is the segment width (members_per_item *
+// group), args.q_len is 1.
+hipError_t launch_decode_planned(const DecodeArgs &args, int32_t head_size, hipStream_t stream);
 
 hipError_t launch_reshape_and_cache(const uint16_t *k, const uint16_t *v, const int64_t *slots,
                                     uint16_t *k_cache, uint16_t *v_cache, int32_t num_tokens,

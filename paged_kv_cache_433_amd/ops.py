@@ -259,6 +259,57 @@ def decode_shared_tree(q, k_cache, v_cache, block_tables, context_lens, shared_p
     return out
 
 
+def share_plan(k_cache, context_lens, num_q_heads, max_blocks_per_seq, group_starts=None, shared_blocks=None,
+               shared_prev=None, plan=None):
+    """The plan of a sharing-aware decode (segments and member records),
+    from the context lengths and the declaration: groups (``group_starts``,
+    ``shared_blocks``) or, with ``shared_prev``, a chain. Returns the plan
+    (a uint8 tensor on the cache's device), reusable by
+    ``decode_shared_planned`` for every layer that decodes the same batch."""
+    desc = _cache_desc(k_cache, k_cache)
+    dev = k_cache.device
+    S = context_lens.shape[0]
+    _need(context_lens, "context_lens", torch.int32, (S,), dev)
+    G = 0
+    if shared_prev is not None:
+        _need(shared_prev, "shared_prev", torch.int32, (S,), dev)
+    elif shared_blocks is not None:
+        G = shared_blocks.shape[0]
+        _need(shared_blocks, "shared_blocks", torch.int32, (G,), dev)
+        _need(group_starts, "group_starts", torch.int32, (G + 1,), dev)
+    lib = _lib.lib()
+    nbytes = int(lib.pa_share_plan_bytes(ctypes.byref(desc), S, num_q_heads, max_blocks_per_seq))
+    if plan is None:
+        plan = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    _check(lib.pa_share_plan(ctypes.byref(desc), _ptr(context_lens), S, num_q_heads, max_blocks_per_seq,
+                             _ptr(group_starts) if shared_prev is None else None,
+                             _ptr(shared_blocks) if shared_prev is None else None, G, _ptr(shared_prev), _ptr(plan),
+                             plan.numel(), _stream(dev)))
+    return plan
+
+
+def decode_shared_planned(q, k_cache, v_cache, block_tables, plan, scale, out=None, workspace=None):
+    """Sharing-aware decode on a plan from ``share_plan`` (made for the same
+    sizes and context lengths). Other arguments as ``decode``."""
+    desc = _cache_desc(k_cache, v_cache)
+    dev = k_cache.device
+    S, hq, d = q.shape
+    _need(q, "q", _BF16, (S, hq, k_cache.shape[3]), dev)
+    mb = block_tables.shape[1] if block_tables.dim() == 2 else -1
+    _need(block_tables, "block_tables", torch.int32, (S, mb), dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", _BF16, (S, hq, d), dev)
+    lib = _lib.lib()
+    nbytes = int(lib.pa_decode_shared_planned_workspace_bytes(ctypes.byref(desc), S, hq, mb))
+    if workspace is None and nbytes:
+        workspace = _workspace(dev, nbytes)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.pa_decode_shared_planned(ctypes.byref(desc), _ptr(q), _ptr(block_tables), S, hq, mb, _ptr(plan),
+                                        float(scale), _ptr(out), _ptr(workspace), ws_bytes, _stream(dev)))
+    return out
+
+
 def reshape_and_cache(k, v, k_cache, v_cache, slot_mapping) -> None:
     """Scatter new tokens' K/V (bf16 ``[T, num_kv_heads, head_size]``) into
     their slots (int64 ``[T]``; negative = skip), in place, on the current stream."""

@@ -296,3 +296,39 @@ def test_num_seqs_limit(L):
     assert L.pa_decode_workspace_bytes(ctypes.byref(d), 1 << 28, 4, 8) > 0
     assert L.pa_decode_workspace_bytes(ctypes.byref(d), (1 << 28) + 1, 4, 8) == 0
     assert decode(L, d, S=(1 << 28) + 1, hq=4) == _lib.PA_ERR_UNSUPPORTED
+
+
+def test_share_plan_and_planned_decode_arguments(L):
+    """The two halves of sharing-aware decode: the plan takes the one-call
+    form's limits and needs a plan buffer of pa_share_plan_bytes; the
+    planned decode needs q, tables, plan and out; plan and workspace must be
+    16-byte aligned and large enough; the two sizes add up to the one-call
+    workspace."""
+    d = desc()
+    S, mb = 256, 256
+    pb = L.pa_share_plan_bytes(ctypes.byref(d), S, 32, mb)
+    wb = L.pa_decode_shared_planned_workspace_bytes(ctypes.byref(d), S, 32, mb)
+    assert pb > 0 and wb > 0
+    assert pb + wb == L.pa_decode_shared_workspace_bytes(ctypes.byref(d), S, 32, mb, 64)
+    assert L.pa_share_plan_bytes(ctypes.byref(d), 4097, 32, mb) == 0
+    assert L.pa_share_plan_bytes(ctypes.byref(d), 0, 32, mb) == 0
+
+    def plan(S=8, lens=P, gs=P, sb=P, ng=2, sp=None, out=P, nbytes=1 << 20):
+        return L.pa_share_plan(ctypes.byref(d), lens, S, 32, 16, gs, sb, ng, sp, out, nbytes, None)
+
+    assert plan(lens=None) == _lib.PA_ERR_NULL and plan(out=None) == _lib.PA_ERR_NULL
+    assert plan(gs=None) == _lib.PA_ERR_NULL          # group form without its arrays
+    assert plan(S=4097) == _lib.PA_ERR_UNSUPPORTED and plan(ng=9) == _lib.PA_ERR_SHAPE
+    assert plan(nbytes=16) == _lib.PA_ERR_WORKSPACE
+    assert plan(out=ctypes.c_void_p(P.value + 8)) == _lib.PA_ERR_WORKSPACE
+    assert plan(S=0, lens=None, out=None, ng=0) == _lib.PA_OK
+
+    def run(S=8, q=P, bt=P, pl=P, out=P, ws=None, wsb=0):
+        return L.pa_decode_shared_planned(ctypes.byref(d), q, bt, S, 32, 16, pl, 1.0, out, ws, wsb, None)
+
+    for kw in ({"q": None}, {"bt": None}, {"pl": None}, {"out": None}):
+        assert run(**kw) == _lib.PA_ERR_NULL, kw
+    assert run(pl=ctypes.c_void_p(P.value + 8)) == _lib.PA_ERR_WORKSPACE
+    assert run(ws=P, wsb=16) == _lib.PA_ERR_WORKSPACE
+    assert run(S=4097) == _lib.PA_ERR_UNSUPPORTED
+    assert run(S=0, q=None, bt=None, pl=None, out=None) == _lib.PA_OK

@@ -326,3 +326,68 @@ def test_tree_beam_search_full_size():
         out = tree_call(bp, sprev, kd, vd)
         ref = oracle_batch("decode", bp.q, kc, vc, bp.block_tables, bp.context_lens, bp.scale)
         assert_attention_close(out, ref, f"beam tree step {step}")
+
+
+# ---------------------------------------------------------------------------
+# pa_share_plan + pa_decode_shared_planned: one plan per step, one decode
+# per layer
+# ---------------------------------------------------------------------------
+
+def test_planned_equals_one_call_and_serves_every_layer():
+    """A plan built once serves several layers (different q and caches,
+    the same tables and lengths): each planned decode equals the one-call
+    form bit for bit, for groups and for a chain."""
+    import torch
+    import paged_kv_cache_433_amd as pa
+    b, starts, shared = batch(830, [4, 9, 1, 3, 40], [100, 512, 16, 37, 64], 32, 8, 128)
+    tables, lens = to_dev(b.block_tables), to_dev(b.context_lens)
+    kd, vd = to_dev_bf16(b.k_cache), to_dev_bf16(b.v_cache)
+    sprev = W.declared_chain(b.block_tables, b.context_lens)
+    plans = {"groups": pa.share_plan(kd, lens, b.num_q_heads, b.max_blocks_per_seq, to_dev(starts), to_dev(shared)),
+             "chain": pa.share_plan(kd, lens, b.num_q_heads, b.max_blocks_per_seq, shared_prev=to_dev(sprev))}
+    rng = np.random.default_rng(831)
+    for layer in range(3):
+        q = to_dev_bf16(W.normal_bf16(rng, b.q.shape))
+        k2 = kd if layer == 0 else to_dev_bf16(W.normal_bf16(rng, b.k_cache.shape))
+        v2 = vd if layer == 0 else to_dev_bf16(W.normal_bf16(rng, b.v_cache.shape))
+        note(f"planned decode, layer {layer}")
+        one = {"groups": pa.decode_shared(q, k2, v2, tables, lens, to_dev(starts), to_dev(shared), float(b.scale)),
+               "chain": pa.decode_shared_tree(q, k2, v2, tables, lens, to_dev(sprev), float(b.scale))}
+        for form, plan in plans.items():
+            out = pa.decode_shared_planned(q, k2, v2, tables, plan, float(b.scale))
+            assert torch.equal(out.view(torch.int16), one[form].view(torch.int16)), (form, layer)
+    # and the first layer against the oracle
+    q0 = W.normal_bf16(np.random.default_rng(831), b.q.shape)
+    ref = oracle.decode(q0, b.k_cache, b.v_cache, b.block_tables, b.context_lens, b.scale)
+    out = pa.decode_shared_planned(to_dev_bf16(q0), kd, vd, tables, plans["chain"], float(b.scale))
+    assert_attention_close(bits_of(out), ref, "planned decode against the oracle")
+
+
+def test_planned_zeroes_empty_segments_in_a_dirty_output():
+    """Segments whose members are all empty are zeroed by the decode, also
+    when the output buffer holds old values (NaN here) and the plan is
+    reused."""
+    import torch
+    import paged_kv_cache_433_amd as pa
+    b = tree_batch(840, [64, 130, 20], [5, 6, 3], 2, 32, 8, 128)
+    ctx = b.context_lens.copy()
+    ctx[[0, 5, 6, 13]] = 0
+    tables, lens = to_dev(b.block_tables), to_dev(ctx)
+    kd, vd = to_dev_bf16(b.k_cache), to_dev_bf16(b.v_cache)
+    sprev = W.declared_chain(b.block_tables, ctx)
+    plan = pa.share_plan(kd, lens, b.num_q_heads, b.max_blocks_per_seq, shared_prev=to_dev(sprev))
+    ref = oracle.decode_shared_tree(b.q, b.k_cache, b.v_cache, b.block_tables, ctx, sprev, b.scale)
+    q = to_dev_bf16(b.q)
+    for rep in range(2):
+        note(f"planned decode with empty segments, call {rep}")
+        out = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device=q.device)
+        pa.decode_shared_planned(q, kd, vd, tables, plan, float(b.scale), out=out)
+        got = bits_of(out)
+        assert np.all(got[[0, 5, 6, 13]] == 0)
+        assert_attention_close(got, ref, f"planned decode with empty segments, call {rep}")
+    note("all sequences empty")
+    zero = to_dev(np.zeros_like(ctx))
+    plan0 = pa.share_plan(kd, zero, b.num_q_heads, b.max_blocks_per_seq, shared_prev=to_dev(np.zeros_like(sprev)))
+    out = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device=q.device)
+    pa.decode_shared_planned(q, kd, vd, tables, plan0, float(b.scale), out=out)
+    assert np.all(bits_of(out) == 0)
