@@ -125,3 +125,74 @@ def test_graph_replay_fused_step():
         torch.cuda.synchronize()
         assert np.array_equal(bits_of(out), eager), f"replay {r} differs from the eager call"
         assert np.array_equal(bits_of(db.k_cache), k_after), f"replay {r}: k_cache differs"
+
+
+def test_graph_replay_sharing_aware_layers():
+    """A step of a model with two layers on one sharing plan, captured in a
+    graph: the plan (pa_share_plan), then a planned decode per layer, plus
+    the one-call tree form. Every replay equals the eager calls bit for bit;
+    the outputs are cleared (to NaN) between replays, so each replay must
+    rewrite them, empty segments included."""
+    import paged_kv_cache_433_amd as pa
+    from gpu_util import to_dev, to_dev_bf16
+    from paged_kv_cache_433_amd import workloads as W
+
+    nb = 3 + 12 * 2 * 5 + 9 + 64
+    b = W.make_tree_batch("graph", 970, [64, 130, 20], [5, 6, 3], 2, 40, 32, 8, 128, nb)
+    b = W.permuted(b, W.tree_order(b.block_tables, b.context_lens))
+    ctx = b.context_lens.copy()
+    ctx[3] = 0                                            # an empty sequence: its rows must be rewritten too
+    sprev = W.declared_chain(b.block_tables, ctx)
+    dev = torch.device("cuda:0")
+    tables, lens, sp = to_dev(b.block_tables), to_dev(ctx), to_dev(sprev)
+    rng = np.random.default_rng(971)
+    layers = [(to_dev_bf16(W.normal_bf16(rng, b.q.shape)), to_dev_bf16(W.normal_bf16(rng, b.k_cache.shape)),
+               to_dev_bf16(W.normal_bf16(rng, b.v_cache.shape))) for _ in range(2)]
+    S, hq, mb = b.num_seqs, b.num_q_heads, b.max_blocks_per_seq
+    kd = layers[0][1]
+    plan = torch.empty(pa.ops._lib.lib().pa_share_plan_bytes(ctypes_desc(pa, kd), S, hq, mb), dtype=torch.uint8,
+                       device=dev)
+    wsp = torch.empty(pa.ops._lib.lib().pa_decode_shared_planned_workspace_bytes(ctypes_desc(pa, kd), S, hq, mb),
+                      dtype=torch.uint8, device=dev)
+    wst = torch.empty(pa.ops._lib.lib().pa_decode_shared_tree_workspace_bytes(ctypes_desc(pa, kd), S, hq, mb),
+                      dtype=torch.uint8, device=dev)
+    outs = [torch.empty_like(layers[0][0]) for _ in range(3)]
+
+    def step():
+        pa.share_plan(kd, lens, hq, mb, shared_prev=sp, plan=plan)
+        for (q, k, v), out in zip(layers, outs):
+            pa.decode_shared_planned(q, k, v, tables, plan, float(b.scale), out=out, workspace=wsp)
+        q, k, v = layers[1]
+        pa.decode_shared_tree(q, k, v, tables, lens, sp, float(b.scale), out=outs[2], workspace=wst)
+
+    note("graph eager sharing-aware layers")
+    step()
+    torch.cuda.synchronize()
+    eager = [bits_of(o) for o in outs]
+    assert np.array_equal(eager[1], eager[2])             # planned layer 2 == the one-call form
+    assert np.all(eager[0][3] == 0)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        step()
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for r in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        plan.fill_(0)                                    # the replay must rebuild the plan too
+        torch.cuda.synchronize()
+        note(f"graph replay sharing-aware layers {r}")
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, o in enumerate(outs):
+            assert np.array_equal(bits_of(o), eager[i]), f"replay {r}, output {i} differs from the eager call"
+
+
+def ctypes_desc(pa, k):
+    import ctypes
+    return ctypes.byref(pa.ops._cache_desc(k, k))
