@@ -599,14 +599,15 @@ __device__ __forceinline__ size_t head_off(const Lane<NT> &ln, const Piece &p) {
 // sequence's last block are never fetched: they read as zeros.
 //
 // Cache policy: the loads of the first half of each K row (at D = 128 its
-// first 128-byte line) carry the non-temporal hint and every other load is
-// plain, so about a quarter of the K/V bytes stream with the hint. Measured on
+// first 128-byte line) carry policy PK, the non-temporal hint unless several
+// wavefronts read the same block, and every other load is plain, so about a
+// quarter of the K/V bytes stream with the hint. Measured on
 // MI355X against all-plain loads, this is 5-10% faster on every cold workload
 // (e.g. the GQA layer 208 us against 226 us), and faster than hinting all of
 // K (213 us) or all of K and V (225 us). Where the calls re-read blocks
 // (beams sharing a prompt) it is also faster than all-plain (179 against
 // 186 us).
-template <int NJ, int NT>
+template <int NJ, int NT, int PK = kNonTemporal>
 __device__ __forceinline__ void issue_rows(const char *kb, const char *vb, const Lane<NT> &ln, int nrows,
                                            u32x4_t (&K)[NJ], u32x4_t (&V)[NJ]) {
   const int span = nrows * ln.row_bytes;
@@ -614,7 +615,7 @@ __device__ __forceinline__ void issue_rows(const char *kb, const char *vb, const
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(vb), 0, span, kRawBufferWord3);
 #pragma unroll
   for (int j = 0; j < NJ / 2; ++j)
-    K[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, ln.lane_off + 64 * j, 0, kNonTemporal));
+    K[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, ln.lane_off + 64 * j, 0, PK));
 #pragma unroll
   for (int j = NJ / 2; j < NJ; ++j)
     K[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, ln.lane_off + 64 * j, 0, 0));
@@ -625,11 +626,11 @@ __device__ __forceinline__ void issue_rows(const char *kb, const char *vb, const
 
 // The same for the first `nrows` token rows of block `blk` of the cache, at
 // the wavefront's KV head (element offset hoff in a token row).
-template <int NJ, int NT>
+template <int NJ, int NT, int PK = kNonTemporal>
 __device__ __forceinline__ void issue(const DecodeArgs &a, const Lane<NT> &ln, int blk, size_t hoff, int nrows,
                                       u32x4_t (&K)[NJ], u32x4_t (&V)[NJ]) {
   const size_t base = ((size_t)blk * ln.blk_stride + hoff) * sizeof(uint16_t);
-  issue_rows<NJ>(reinterpret_cast<const char *>(a.k_cache) + base, reinterpret_cast<const char *>(a.v_cache) + base,
+  issue_rows<NJ, NT, PK>(reinterpret_cast<const char *>(a.k_cache) + base, reinterpret_cast<const char *>(a.v_cache) + base,
                  ln, nrows, K, V);
 }
 
@@ -640,7 +641,7 @@ __device__ __forceinline__ void issue(const DecodeArgs &a, const Lane<NT> &ln, i
 // (its row less 8, or 2 GiB for rows 0-7, past any range). The load outside
 // its range reads as zero, so OR-ing the two gives the row without a
 // per-lane choice of resource.
-template <int NJ, int NT>
+template <int NJ, int NT, int PK = kNonTemporal>
 __device__ __forceinline__ void issue_pair_rows(const char *kba, const char *vba, int na, const char *kbb,
                                                 const char *vbb, int nb, const Lane<NT> &ln, u32x4_t (&K)[NJ],
                                                 u32x4_t (&V)[NJ]) {
@@ -655,8 +656,8 @@ __device__ __forceinline__ void issue_pair_rows(const char *kba, const char *vba
   const uint32_t off_b = ln.lane_off_b;
 #pragma unroll
   for (int j = 0; j < NJ / 2; ++j)
-    K[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rka, ln.lane_off + 64 * j, 0, kNonTemporal)) |
-           __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rkb, off_b + 64 * j, 0, kNonTemporal));
+    K[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rka, ln.lane_off + 64 * j, 0, PK)) |
+           __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rkb, off_b + 64 * j, 0, PK));
 #pragma unroll
   for (int j = NJ / 2; j < NJ; ++j)
     K[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rka, ln.lane_off + 64 * j, 0, 0)) |
@@ -667,13 +668,13 @@ __device__ __forceinline__ void issue_pair_rows(const char *kba, const char *vba
            __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rvb, off_b + 64 * j, 0, 0));
 }
 
-template <int NJ, int NT>
+template <int NJ, int NT, int PK = kNonTemporal>
 __device__ __forceinline__ void issue_pair(const DecodeArgs &a, const Lane<NT> &ln, int ida, int idb, size_t hoff,
                                            int na, int nb, u32x4_t (&K)[NJ], u32x4_t (&V)[NJ]) {
   const size_t base_a = ((size_t)ida * ln.blk_stride + hoff) * sizeof(uint16_t);
   const size_t base_b = ((size_t)idb * ln.blk_stride + hoff) * sizeof(uint16_t);
   const char *kc = reinterpret_cast<const char *>(a.k_cache), *vc = reinterpret_cast<const char *>(a.v_cache);
-  issue_pair_rows<NJ>(kc + base_a, vc + base_a, na, kc + base_b, vc + base_b, nb, ln, K, V);
+  issue_pair_rows<NJ, NT, PK>(kc + base_a, vc + base_a, na, kc + base_b, vc + base_b, nb, ln, K, V);
 }
 
 // kStep with 16- or 32-token blocks: the newest position of sequence s as a
@@ -693,7 +694,7 @@ __device__ __forceinline__ void issue_new(const DecodeArgs &a, const Lane<NT> &l
 // in a cache of BS-token blocks: block c (BS = 16), half of block c/2
 // (BS = 32), or blocks 2c and 2c+1 (BS = 8; the second only if the chunk
 // reaches into it).
-template <int NJ, int NT, int BS>
+template <int NJ, int NT, int BS, int PK = kNonTemporal>
 __device__ __forceinline__ void issue_chunk(const int32_t *__restrict__ tables, const DecodeArgs &a,
                                             const Lane<NT> &ln, int row, int c, size_t hoff, int nrows,
                                             u32x4_t (&K)[NJ], u32x4_t (&V)[NJ]) {
@@ -703,11 +704,11 @@ __device__ __forceinline__ void issue_chunk(const int32_t *__restrict__ tables, 
     const int nb = nrows - na;
     const int ida = block_id(tables, a, ln.pool32, row, 2 * c);
     const int idb = nb > 0 ? block_id(tables, a, ln.pool32, row, 2 * c + 1) : 0;
-    issue_pair<NJ>(a, ln, ida, idb, hoff, na, nb, K, V);
+    issue_pair<NJ, NT, PK>(a, ln, ida, idb, hoff, na, nb, K, V);
   } else if constexpr (BS == kBlock) {
-    issue<NJ>(a, ln, block_id(tables, a, ln.pool32, row, c), hoff, nrows, K, V);
+    issue<NJ, NT, PK>(a, ln, block_id(tables, a, ln.pool32, row, c), hoff, nrows, K, V);
   } else {
-    issue<NJ>(a, ln, block_id(tables, a, ln.pool32, row, c >> 1),
+    issue<NJ, NT, PK>(a, ln, block_id(tables, a, ln.pool32, row, c >> 1),
               hoff + (size_t)(c & 1) * kBlock * (ln.row_bytes / sizeof(uint16_t)), nrows, K, V);
   }
 }
@@ -772,7 +773,11 @@ __device__ __forceinline__ void issue_seq(const int32_t *__restrict__ tables, co
     else
       issue_chunk<NJ, NT, BS>(tables, a, ln, s, b, hoff, rows_in<CH>(n - 1, b), K, V);
   } else {
-    issue_chunk<NJ, NT, BS>(tables, a, ln, s, b, hoff, rows_in<CH>(n, b), K, V);
+    // Past 32 columns the wavefronts of a workgroup read the same blocks:
+    // plain loads keep them in L2 for the others (64 new tokens: 1148
+    // against 1192 us; 16: 430 against 474 us), where a single reader
+    // streams faster with the hint on part of K.
+    issue_chunk<NJ, NT, BS, M == kWide ? 0 : kNonTemporal>(tables, a, ln, s, b, hoff, rows_in<CH>(n, b), K, V);
   }
 }
 
