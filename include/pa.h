@@ -229,8 +229,8 @@ int pa_decode_noalloc(const pa_kv_cache *cache, const void *q, const int32_t *bl
  *   q_len    >= 1, with q_len * (num_q_heads / num_kv_heads) <= 256 (any
  *            of the cache's block sizes, 8, 16 or 32): a 64-token prefill
  *            chunk with 4 query heads per KV head, or 7 speculative tokens
- *            (8 new tokens) with 8 or 16. Up to 32 such columns one
- *            wavefront serves a KV head; past 32, a workgroup serves one KV
+ *            (8 new tokens) with 8 or 16. Up to 64 such columns one
+ *            wavefront serves a KV head; past 64, a workgroup serves one KV
  *            head with one wavefront per 32 columns, and the same
  *            wavefronts share each block the cache reads.
  * Other arguments, the workspace (size from pa_decode_multi_workspace_bytes)

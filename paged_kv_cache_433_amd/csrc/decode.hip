@@ -1244,13 +1244,14 @@ __device__ __forceinline__ void zero_empty_items(const DecodeArgs &a, const Shar
 // item width in kShared, or 32 per column group in kWide). M: kSingle,
 // kCausal, kWide or kShared. The narrow launches put one wavefront on each
 // SIMD. kWide runs two wavefronts per SIMD (a workgroup of up to 8 column
-// groups of one KV head), 256 registers each. Two tiles of several new
-// tokens with 8-token blocks (two loads in flight per row) do not fit in
-// 256 arch registers: that launch bounds its workgroup at 256 threads, so a
-// wavefront may also use accumulation registers (no scratch; 282 against
-// 286 us at 8 new tokens).
+// groups of one KV head), 256 registers each. Four tiles of several new
+// tokens (33-64 columns), and two with 8-token blocks (two loads in flight
+// per row), do not fit in 256 arch registers: those launches bound their
+// workgroup at 256 threads, so a wavefront may also use accumulation
+// registers (no scratch; two tiles with 8-token blocks: 282 against 286 us
+// at 8 new tokens).
 template <int D, int NT, int M, int BS, bool VEC>
-__global__ __launch_bounds__(M == kCausal && NT == 2 && BS == 8 ? 256 : 512)
+__global__ __launch_bounds__(M == kCausal && (NT == 4 || (NT == 2 && BS == 8)) ? 256 : 512)
 __attribute__((amdgpu_waves_per_eu(NT == 1 || M == kWide ? 2 : 1)))
 void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const int32_t *__restrict__ lens,
                    const ShareItem *__restrict__ items) {
@@ -1893,6 +1894,11 @@ hipError_t launch_decode_d(const DecodeArgs &args, size_t lds, hipStream_t strea
     if (args.block_size == 32) return launch_decode_kernel<D, 2, kCausal, 32>(args, lds, stream);
     return launch_decode_kernel<D, 2, kCausal>(args, lds, stream);
   }
+  if (args.num_cols <= kMaxNarrowCols) {
+    if (args.block_size == 8) return launch_decode_kernel<D, 4, kCausal, 8>(args, lds, stream);
+    if (args.block_size == 32) return launch_decode_kernel<D, 4, kCausal, 32>(args, lds, stream);
+    return launch_decode_kernel<D, 4, kCausal>(args, lds, stream);
+  }
   if (args.block_size == 8) return launch_decode_kernel<D, 2, kWide, 8>(args, lds, stream);
   if (args.block_size == 32) return launch_decode_kernel<D, 2, kWide, 32>(args, lds, stream);
   return launch_decode_kernel<D, 2, kWide>(args, lds, stream);
@@ -1901,7 +1907,7 @@ hipError_t launch_decode_d(const DecodeArgs &args, size_t lds, hipStream_t strea
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs &args, int32_t head_size, hipStream_t stream) {
-  const bool wide = args.num_cols > 32;
+  const bool wide = args.num_cols > kMaxNarrowCols;
   const bool fused = args.k_new != nullptr;
   if (args.q_len < 1 || args.num_cols > kMaxDecodeCols || (args.q_len == 1 && args.num_cols > 16)) return hipErrorInvalidValue;
   if (fused && (args.q_len != 1 || !args.v_new)) return hipErrorInvalidValue;

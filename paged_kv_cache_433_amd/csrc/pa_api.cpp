@@ -313,7 +313,7 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
                        int32_t head_size, int32_t max_chunks_per_seq, int32_t q_len) {
   DecodePlan p{};
   const int32_t cols = q_len * (num_q_heads / num_kv_heads);
-  if (cols > 32) {
+  if (cols > pa::kMaxNarrowCols) {
     // One workgroup per KV head of a piece, one wavefront per 32 columns.
     p.col_groups = (cols + 31) / 32;
     p.rec_cols = 32;

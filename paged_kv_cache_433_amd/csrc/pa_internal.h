@@ -97,6 +97,11 @@ struct SharePlanArgs {
 // lengths through one buffer resource, whose range is a 32-bit byte count.
 constexpr int32_t kMaxDecodeSeqs = 1 << 28;
 
+// Most (new token, query head) columns one wavefront takes for a KV head
+// (four MFMA tiles of 16); past them a workgroup serves one KV head with a
+// wavefront per 32 columns.
+constexpr int32_t kMaxNarrowCols = 64;
+
 // Most (new token, query head) columns per KV head a decode launch takes:
 // 8 column groups of 32, one wavefront each.
 constexpr int32_t kMaxDecodeCols = 256;

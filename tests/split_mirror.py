@@ -178,7 +178,7 @@ def plain_segments(lens, cap: int, step: bool = False) -> list:
 def check_plain(lens, num_q_heads, num_kv_heads, max_blocks_per_seq, block_size=16, override=None,
                 q_len=1, step=False) -> Split:
     cols = q_len * (num_q_heads // num_kv_heads)
-    if cols > 32:  # a workgroup per KV head, a wavefront per 32 columns, 8 wavefronts per CU
+    if cols > 64:  # a workgroup per KV head, a wavefront per 32 columns, 8 wavefronts per CU
         hg, NG, wpc = (cols + 31) // 32, num_kv_heads, 8
     else:
         hg = heads_per_workgroup(num_kv_heads)
