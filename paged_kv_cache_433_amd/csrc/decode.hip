@@ -411,8 +411,9 @@ constexpr int kNonTemporal = 2;
 // for them to complete. With many short sequences a wavefront ends dozens of
 // segments: 16 KiB and 32 outputs (instead of 8 KiB and 16) measured 6%
 // faster at 1024 sequences of about 64 tokens, and the same elsewhere. With
-// the new-row slots below a wavefront takes about 31 KiB of LDS, so four
-// wavefronts (or four one-wavefront workgroups) fit in a compute unit.
+// the new-row slots below a wavefront takes about 31 KiB of LDS at head size
+// 128 and 4 columns (37 KiB at 16), so four wavefronts (or four
+// one-wavefront workgroups) fit in a compute unit.
 constexpr int kStageBytes = 16384;
 constexpr int kStageSlots = 32;
 
@@ -452,12 +453,20 @@ __device__ __forceinline__ void load_q(const DecodeArgs &a, const Lane<NT> &ln, 
       qv[t][j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, ln.q_off[t] + 64 * j, 0, 0));
 }
 
+// A q row in LDS: head_size bf16 values and 16 bytes of padding. Lanes
+// c = 0..15 of a 16-byte read take the rows of 16 columns at the same head
+// dims; with rows 256 bytes apart (head_size 128) all 16 would fall in the
+// same banks, and the read would take 16 passes instead of 4 (measured: LDS
+// bank conflicts 41% of the compute units' cycles with 64 new tokens).
+template <int NJ>
+constexpr int q_row() { return NJ * 32 + 8; }
+
 // q of the next piece travels through LDS (one column tile only): two slots
-// per wavefront, each holding the KV head's column rows [num_cols][D] as
-// bf16; slot = piece position & 1.
+// per wavefront, each holding the KV head's column rows [num_cols][q_row]
+// as bf16; slot = piece position & 1.
 template <int NJ>
 __device__ __forceinline__ uint16_t *q_slot(uint16_t *lds, const DecodeArgs &a, int wave, int ord) {
-  return lds + ((size_t)wave * 2 + (ord & 1)) * a.num_cols * (NJ * 32);
+  return lds + ((size_t)wave * 2 + (ord & 1)) * a.num_cols * q_row<NJ>();
 }
 
 // Launches that defer: the wavefront's output staging area (after the q ring of
@@ -467,7 +476,7 @@ __device__ __forceinline__ uint16_t *q_slot(uint16_t *lds, const DecodeArgs &a, 
 template <int NJ>
 __device__ __forceinline__ uint16_t *stage_area(uint16_t *lds, const DecodeArgs &a, int wave) {
   constexpr int D = NJ * 32;
-  return lds + (size_t)a.heads_per_wg * 2 * a.num_cols * D +
+  return lds + (size_t)a.heads_per_wg * 2 * a.num_cols * q_row<NJ>() +
          (size_t)wave * (kStageBytes + kStageSlots * sizeof(size_t)) / sizeof(uint16_t);
 }
 
@@ -482,7 +491,7 @@ constexpr int new_slot_elems() { return 2 * D + 8; }
 template <int NJ>
 __device__ __forceinline__ uint16_t *new_area(uint16_t *lds, const DecodeArgs &a, int wave) {
   constexpr int D = NJ * 32;
-  return lds + (size_t)a.heads_per_wg * 2 * a.num_cols * D +
+  return lds + (size_t)a.heads_per_wg * 2 * a.num_cols * q_row<NJ>() +
          (size_t)a.heads_per_wg * (kStageBytes + kStageSlots * sizeof(size_t)) / sizeof(uint16_t) +
          (size_t)wave * kNewSlots * new_slot_elems<D>();
 }
@@ -495,14 +504,14 @@ __device__ __forceinline__ int stage_slots(const DecodeArgs &a) {
 }
 
 // The one slot per wavefront that holds the current piece's q (two tiles):
-// [rec_cols][D], the wavefront's own columns.
+// [rec_cols][q_row], the wavefront's own columns.
 template <int NJ>
 __device__ __forceinline__ uint16_t *q_park(uint16_t *lds, const DecodeArgs &a, int wave) {
-  return lds + (size_t)wave * a.rec_cols * (NJ * 32);
+  return lds + (size_t)wave * a.rec_cols * q_row<NJ>();
 }
 
 // With two column tiles the current piece's q lives in LDS (one slot per
-// wavefront, [num_cols][D]), loaded at the piece switch and read per block:
+// wavefront, [num_cols][q_row]), loaded at the piece switch and read per block:
 // the registers to keep it, or to stage the next piece's, are not there.
 // Each lane writes and reads only its own columns' rows (or, for a missing
 // column, the last row, written by the same wavefront), so no barrier is
@@ -514,13 +523,13 @@ __device__ __forceinline__ void park_q(uint16_t *slot, const Lane<NT> &ln, const
   for (int t = 0; t < NT; ++t)
     if (ln.col_ok[t]) {
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) *reinterpret_cast<u32x4_t *>(qs + ln.lcol[t] * (NJ * 32) + 32 * j) = qv[t][j];
+      for (int j = 0; j < NJ; ++j) *reinterpret_cast<u32x4_t *>(qs + ln.lcol[t] * q_row<NJ>() + 32 * j) = qv[t][j];
     }
 }
 
 template <int NJ, int NT>
 __device__ __forceinline__ void parked_q(const uint16_t *slot, const Lane<NT> &ln, int t, u32x4_t (&qv)[NJ]) {
-  const uint16_t *qs = slot + ln.lcol[t] * (NJ * 32) + ln.grp * 8;
+  const uint16_t *qs = slot + ln.lcol[t] * q_row<NJ>() + ln.grp * 8;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) qv[j] = *reinterpret_cast<const u32x4_t *>(qs + 32 * j);
 }
@@ -1047,7 +1056,7 @@ __device__ __forceinline__ void advance(const DecodeArgs &a, const Lane<NT> &ln,
   if constexpr (NT == 1) {
     const uint16_t *qs = q_slot<NJ>(lds, a, ln.wave, st.ord) + ln.grp * 8;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) st.qv[0][j] = *reinterpret_cast<const u32x4_t *>(qs + ln.col[0] * (NJ * 32) + 32 * j);
+    for (int j = 0; j < NJ; ++j) st.qv[0][j] = *reinterpret_cast<const u32x4_t *>(qs + ln.col[0] * q_row<NJ>() + 32 * j);
   } else if constexpr (q_in_regs<NT, M, BS>()) {
     load_q<NJ, NT, M>(a, ln, st.P, st.qv);
   } else {
@@ -1257,7 +1266,7 @@ void decode_kernel(const DecodeArgs a, const int32_t *__restrict__ tables, const
                    const ShareItem *__restrict__ items) {
   constexpr int NJ = D / 32;  // MFMA steps over head_size; 16-byte loads per lane per row
   static_assert(NJ >= 1 && D % 32 == 0, "head_size must be a multiple of 32");
-  extern __shared__ __align__(16) uint16_t q_lds[];  // heads_per_wg * (NT == 1 ? 2 : 1) * rec_cols * D
+  extern __shared__ __align__(16) uint16_t q_lds[];  // heads_per_wg * (NT == 1 ? 2 : 1) * rec_cols * (D + 8), ...
   __shared__ long long red[8];
   __shared__ int found_seq, found_n;
   __shared__ long long found_prefix;
@@ -1921,7 +1930,7 @@ hipError_t launch_decode(const DecodeArgs &args, int32_t head_size, hipStream_t 
   // LDS holds q: a two-slot ring per wavefront for the next piece (one column
   // tile), or the current piece's (two tiles).
   // With one column tile, each wavefront also has an output staging area.
-  const size_t lds = (size_t)args.heads_per_wg * (args.num_cols <= 16 ? 2 : 1) * args.rec_cols * head_size *
+  const size_t lds = (size_t)args.heads_per_wg * (args.num_cols <= 16 ? 2 : 1) * args.rec_cols * (head_size + 8) *
                          sizeof(uint16_t) +
                      (args.num_cols <= 16 && (args.block_size != 8 || fused)
                           ? (size_t)args.heads_per_wg * (kStageBytes + kStageSlots * sizeof(size_t))
@@ -1971,8 +1980,8 @@ hipError_t launch_decode_planned(const DecodeArgs &args, int32_t head_size, hipS
     return hipErrorInvalidValue;
   if (head_size != 128 && head_size != 64) return hipErrorInvalidValue;
   hipError_t e;
-  // q of the current piece in LDS: one [num_cols][D] slot per wavefront.
-  const size_t lds = (size_t)args.heads_per_wg * args.num_cols * head_size * sizeof(uint16_t);
+  // q of the current piece in LDS: one [num_cols][head_size + 8] slot per wavefront.
+  const size_t lds = (size_t)args.heads_per_wg * args.num_cols * (head_size + 8) * sizeof(uint16_t);
   if (head_size == 128)
     e = args.block_size == 8    ? launch_decode_kernel<128, 2, kShared, 8>(args, lds, stream)
         : args.block_size == 32 ? launch_decode_kernel<128, 2, kShared, 32>(args, lds, stream)
