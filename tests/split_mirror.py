@@ -182,7 +182,9 @@ def check_plain(lens, num_q_heads, num_kv_heads, max_blocks_per_seq, block_size=
         hg, NG, wpc = (cols + 31) // 32, num_kv_heads, 8
     else:
         hg = heads_per_workgroup(num_kv_heads)
-        NG, wpc = num_kv_heads // hg, 4
+        NG = num_kv_heads // hg
+        # one-wavefront workgroups on one tile with few segments: 3 per unit
+        wpc = 3 if hg == 1 and cols <= 16 and len(lens) * NG <= 512 else 4
     cap = max_blocks_per_seq * block_size
     W = decode_wgs(len(lens), NG, hg, chunks_per_row(max_blocks_per_seq, block_size) + (1 if step else 0),
                    override, wpc)
