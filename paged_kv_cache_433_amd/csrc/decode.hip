@@ -879,8 +879,11 @@ __device__ __forceinline__ void finish_piece(const DecodeArgs &a, const Lane<NT>
       const int slot0 = range_lo(w0, ln.U, ln.E) < P.seg_start ? 1 : 0;
       d = int2{P.s * ln.NG + P.hg, w0 * 2 + slot0};
     }
+    // Sharing-aware decode also records the segment's q rows, so the merge
+    // needs no read of the plan.
     if constexpr (DF) st.desc = d;
-    else if (ln.tid == 0 && a.merge_desc) a.merge_desc[ln.w] = d;
+    else if (ln.tid == 0 && a.merge_desc)
+      a.merge_desc[ln.w] = M == kShared ? int4{d.x, d.y, P.qrow, P.ntok} : int4{d.x, d.y, 0, 0};
   }
 }
 
@@ -919,7 +922,7 @@ __device__ __forceinline__ void finish_stream(const DecodeArgs &a, const Lane<NT
       }
     }
     if (st.first_cut) store_record<NJ, NT>(a, ln, 0, 0, st.first_acc, st.first_m, st.first_l);
-    if (ln.tid == 0 && a.merge_desc) a.merge_desc[ln.w] = st.desc;
+    if (ln.tid == 0 && a.merge_desc) a.merge_desc[ln.w] = int4{st.desc.x, st.desc.y, 0, 0};
   }
 }
 
@@ -1230,7 +1233,7 @@ __device__ __forceinline__ void zero_empty(const DecodeArgs &a, int s, int w) {
 
 // Workgroups past the ones that get units have no merge record to write.
 __device__ __forceinline__ void no_merge(const DecodeArgs &a, int w, int tid) {
-  if (tid == 0 && a.merge_desc) a.merge_desc[w] = int2{-1, -1};
+  if (tid == 0 && a.merge_desc) a.merge_desc[w] = int4{-1, -1, 0, 0};
 }
 
 // kShared: a segment with no chunk (every member's context empty) is not
@@ -1535,14 +1538,14 @@ __global__ __launch_bounds__(512) void merge_kernel(const DecodeArgs a) {
   constexpr int CPP = 64 / LPC;  // columns per half pass
   constexpr int kPieces = 4;
   const int w1 = blockIdx.x;
-  const int2 d = a.merge_desc[w1];
+  const int4 d = a.merge_desc[w1];
   if (d.x < 0) return;
   // Every index below comes from the workspace. Each is checked before it
   // is used, so a bookkeeping slip gives a wrong result, never an access
-  // outside the call's arrays: the segment must be one of the call's, and
-  // its first piece must belong to this workgroup or an earlier one.
-  const int nseg = kSegments ? min(max(a.share->items, 0), a.num_seqs) : a.num_seqs;
-  if (d.x >= nseg * a.num_head_groups || d.y < 0 || (d.y >> 1) > w1) return;
+  // outside the call's arrays: the segment must be one of the call's (in
+  // sharing-aware decode its q rows must lie in the batch), and its first
+  // piece must belong to this workgroup or an earlier one.
+  if (d.x >= a.num_seqs * a.num_head_groups || d.y < 0 || (d.y >> 1) > w1) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // KV head within the head group
   const int lane = threadIdx.x & 63;
   const int HG = a.heads_per_wg;
@@ -1557,10 +1560,10 @@ __global__ __launch_bounds__(512) void merge_kernel(const DecodeArgs a) {
   size_t row0 = (size_t)s * a.q_len;
   int cols = min(a.rec_cols, a.num_cols - col0);
   if constexpr (kSegments) {
-    const ShareItem x = a.items[s];
-    if (x.qrow < 0 || x.ntok < 1 || x.ntok > a.num_seqs - x.qrow || x.ntok * a.group > a.num_cols) return;
-    row0 = (size_t)x.qrow;
-    cols = x.ntok * a.group;
+    const int qrow = d.z, ntok = d.w;
+    if (qrow < 0 || ntok < 1 || ntok > a.num_seqs - qrow || ntok * a.group > a.num_cols) return;
+    row0 = (size_t)qrow;
+    cols = ntok * a.group;
   }
   const float *__restrict__ pml = a.part_ml;
   const float *__restrict__ pob = a.part_o;

@@ -190,7 +190,7 @@ SharedLayout layout_shared(const pa_kv_cache *c, int32_t num_seqs, int32_t num_q
   l.items_off = 256;  // ShareHeader
   l.members_off = l.items_off + round_up(((size_t)num_seqs + 1) * sizeof(pa::ShareItem), 256);
   l.desc_off = l.members_off + round_up((size_t)num_seqs * 2 * sizeof(int32_t), 256);
-  l.ml_off = l.desc_off + round_up((size_t)l.plan.num_wgs * sizeof(int2), 256);
+  l.ml_off = l.desc_off + round_up((size_t)l.plan.num_wgs * sizeof(int4), 256);
   l.o_off = l.ml_off + round_up(rows * 2 * sizeof(float), 256);
   l.total = l.o_off + round_up(rows * c->head_size * sizeof(float), 256);
   return l;
@@ -249,7 +249,7 @@ hipError_t launch_planned(const pa_kv_cache *cache, const SharedLayout &l, const
   a.block_tables = block_tables;
   a.context_lens = reinterpret_cast<const int32_t *>(plan + l.members_off);  // the member records
   a.out = static_cast<uint16_t *>(out);
-  a.merge_desc = reinterpret_cast<int2 *>(run);
+  a.merge_desc = reinterpret_cast<int4 *>(run);
   a.part_ml = reinterpret_cast<float *>(run + (l.ml_off - l.desc_off));
   a.part_o = reinterpret_cast<float *>(run + (l.o_off - l.desc_off));
   a.num_blocks = cache->num_blocks;
@@ -343,7 +343,7 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
   }
   if (p.num_wgs <= 1) return p;
   const size_t rows = (size_t)p.num_wgs * 2 * p.heads_per_wg * p.rec_cols;
-  p.desc_bytes = round_up((size_t)p.num_wgs * sizeof(int2), 256);
+  p.desc_bytes = round_up((size_t)p.num_wgs * sizeof(int4), 256);
   p.ml_bytes = round_up(rows * 2 * sizeof(float), 256);
   p.o_bytes = round_up(rows * head_size * sizeof(float), 256);
   p.total_bytes = p.desc_bytes + p.ml_bytes + p.o_bytes;
@@ -411,7 +411,7 @@ int decode_impl(const pa_kv_cache *cache, const void *q, const int32_t *block_ta
   a.out = static_cast<uint16_t *>(out);
   if (plan.total_bytes) {
     char *base = static_cast<char *>(ws);
-    a.merge_desc = reinterpret_cast<int2 *>(base);
+    a.merge_desc = reinterpret_cast<int4 *>(base);
     a.part_ml = reinterpret_cast<float *>(base + plan.desc_bytes);
     a.part_o = reinterpret_cast<float *>(base + plan.desc_bytes + plan.ml_bytes);
   }

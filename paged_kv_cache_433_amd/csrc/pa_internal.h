@@ -47,7 +47,10 @@ struct DecodeArgs {
   const int32_t *block_tables;   // [S, MB]
   const int32_t *context_lens;   // [S]; sharing-aware decode: the plan's member records [S][2]
   uint16_t *out;                 // bf16 [S, q_len, Hq, D]
-  int2 *merge_desc;              // [num_wgs]: segment ended by the workgroup's first piece, or -1
+  // [num_wgs]: the segment the workgroup's first piece ended (x, or -1), the
+  // slot of its first piece (y) and, in sharing-aware decode, its first q
+  // row and member count (z, w)
+  int4 *merge_desc;
   float *part_ml;                // [2 * num_wgs, heads_per_wg, rec_cols, 2]: max (base 2), sum
   float *part_o;                 // [2 * num_wgs, heads_per_wg, rec_cols, D]: unnormalised output
   int64_t num_blocks;
@@ -127,7 +130,7 @@ hipError_t launch_decode(const DecodeArgs &args, int32_t head_size, hipStream_t 
 // Bytes of the static device scratch of pa_decode_noalloc. It covers every
 // single-token decode the default split can produce: at most 1024
 // workgroups x KV heads per workgroup, 16 columns each, head size 128, two
-// partial records per (workgroup, head, column): merge records 8 KiB,
+// partial records per (workgroup, head, column): merge records 16 KiB,
 // max/sum 256 KiB, outputs 16 MiB.
 constexpr size_t kNoAllocScratchBytes = ((size_t)16 << 20) + ((size_t)512 << 10);
 static_assert(kNoAllocScratchBytes == PA_NOALLOC_SCRATCH_BYTES, "the header states the scratch size");
