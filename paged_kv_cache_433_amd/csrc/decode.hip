@@ -405,17 +405,18 @@ constexpr int kRawBufferWord3 = 0x00020000;
 constexpr int kNonTemporal = 2;
 
 // bf16 outputs of whole segments are staged in LDS and stored after the
-// stream (launches that defer, below), up to kStageBytes per wavefront and kStageSlots
-// outputs (more are stored at once). Stores issued mid-stream are counted
-// with the loads in flight, so the wait for the next blocks would also wait
-// for them to complete. With many short sequences a wavefront ends dozens of
-// segments: 16 KiB and 32 outputs (instead of 8 KiB and 16) measured 6%
-// faster at 1024 sequences of about 64 tokens, and the same elsewhere. With
-// the new-row slots below a wavefront takes about 31 KiB of LDS at head size
-// 128 and 4 columns (37 KiB at 16), so four wavefronts (or four
-// one-wavefront workgroups) fit in a compute unit.
-constexpr int kStageBytes = 16384;
-constexpr int kStageSlots = 32;
+// stream (launches that defer, below), as many per wavefront as the launch
+// leaves room for (stage_slots; more are stored at once). Stores issued
+// mid-stream are counted with the loads in flight, so the wait for the next
+// blocks would also wait for them to complete. With many short sequences a
+// wavefront ends dozens of segments: 4096 sequences of median 64 tokens
+// (32 segments per wavefront) measured 264.0 us with 16 outputs staged,
+// 251.1 with 24 and 240.8 with 32 (two launches).
+// Each wavefront may take this much LDS: a quarter of the compute unit's
+// 160 KiB (four wavefronts, or four one-wavefront workgroups, per unit),
+// less a margin for the kernel's static LDS.
+constexpr int kLdsPerWave = 163840 / 4 - 256;
+constexpr int kMaxStageSlots = 64;
 
 // Whether the current piece's q stays in registers for the whole piece
 // (one column tile; and sharing-aware decode with two tiles, where it fits
@@ -470,14 +471,24 @@ __device__ __forceinline__ uint16_t *q_slot(uint16_t *lds, const DecodeArgs &a, 
 }
 
 // Launches that defer: the wavefront's output staging area (after the q ring of
-// every wavefront): kStageBytes of bf16 outputs, then kStageSlots row
-// offsets. An output occupies num_cols * D bf16 values, lane (c, grp) holding
-// 8 consecutive values for each MFMA step j at ((j * 4 + grp) * num_cols + c) * 8.
+// every wavefront): stage_slots bf16 outputs, then their row offsets padded
+// to 16 bytes (stage_stride bytes in all). An output occupies num_cols * D
+// bf16 values, lane (c, grp) holding 8 consecutive values for each MFMA step
+// j at ((j * 4 + grp) * num_cols + c) * 8.
+__host__ __device__ __forceinline__ int stage_out_bytes(int slots, int num_cols, int D) {
+  return slots * num_cols * D * (int)sizeof(uint16_t);
+}
+__host__ __device__ __forceinline__ int stage_stride(int slots, int num_cols, int D) {
+  return stage_out_bytes(slots, num_cols, D) + (slots * (int)sizeof(size_t) + 15) / 16 * 16;
+}
 template <int NJ>
 __device__ __forceinline__ uint16_t *stage_area(uint16_t *lds, const DecodeArgs &a, int wave) {
-  constexpr int D = NJ * 32;
   return lds + (size_t)a.heads_per_wg * 2 * a.num_cols * q_row<NJ>() +
-         (size_t)wave * (kStageBytes + kStageSlots * sizeof(size_t)) / sizeof(uint16_t);
+         (size_t)wave * stage_stride(a.stage_slots, a.num_cols, NJ * 32) / sizeof(uint16_t);
+}
+template <int NJ>
+__device__ __forceinline__ size_t *stage_dsts(uint16_t *area, const DecodeArgs &a) {
+  return reinterpret_cast<size_t *>(area + stage_out_bytes(a.stage_slots, a.num_cols, NJ * 32) / sizeof(uint16_t));
 }
 
 // kStep: the new K/V rows a wavefront writes to their slots are staged here
@@ -492,15 +503,13 @@ template <int NJ>
 __device__ __forceinline__ uint16_t *new_area(uint16_t *lds, const DecodeArgs &a, int wave) {
   constexpr int D = NJ * 32;
   return lds + (size_t)a.heads_per_wg * 2 * a.num_cols * q_row<NJ>() +
-         (size_t)a.heads_per_wg * (kStageBytes + kStageSlots * sizeof(size_t)) / sizeof(uint16_t) +
+         (size_t)a.heads_per_wg * stage_stride(a.stage_slots, a.num_cols, D) / sizeof(uint16_t) +
          (size_t)wave * kNewSlots * new_slot_elems<D>();
 }
 
 template <int NJ>
 __device__ __forceinline__ int stage_slots(const DecodeArgs &a) {
-  constexpr int D = NJ * 32;
-  const int n = kStageBytes / (a.num_cols * D * (int)sizeof(uint16_t));
-  return n < kStageSlots ? n : kStageSlots;
+  return a.stage_slots;
 }
 
 // The one slot per wavefront that holds the current piece's q (two tiles):
@@ -850,7 +859,7 @@ __device__ __forceinline__ void finish_piece(const DecodeArgs &a, const Lane<NT>
                 u32x4_t{to_bf16x2(x[0], x[1]), to_bf16x2(x[2], x[3]), to_bf16x2(y[0], y[1]), to_bf16x2(y[2], y[3])};
           }
         }
-        if (ln.lane == 0) reinterpret_cast<size_t *>(area + kStageBytes / sizeof(uint16_t))[st.staged] = dst;
+        if (ln.lane == 0) stage_dsts<NJ>(area, a)[st.staged] = dst;
         ++st.staged;
       } else if (keep) {
         store_out<NJ>(a.out + dst + ln.out_off[t], st.acc[t], inv);
@@ -910,7 +919,7 @@ __device__ __forceinline__ void finish_stream(const DecodeArgs &a, const Lane<NT
   }
   if constexpr (DF) {
     const uint16_t *area = stage_area<NJ>(lds, a, ln.wave);
-    const size_t *dsts = reinterpret_cast<const size_t *>(area + kStageBytes / sizeof(uint16_t));
+    const size_t *dsts = stage_dsts<NJ>(const_cast<uint16_t *>(area), a);
     for (int i = 0; i < st.staged; ++i) {
       const uint16_t *slot = area + (size_t)i * a.num_cols * D;
       uint16_t *dst = a.out + dsts[i] + ln.out_off[0];
@@ -1930,24 +1939,25 @@ hipError_t launch_decode(const DecodeArgs &args, int32_t head_size, hipStream_t 
            : (args.rec_cols != args.num_cols || args.col_groups != 1))
     return hipErrorInvalidValue;
   if (args.block_size != 8 && args.block_size != 16 && args.block_size != 32) return hipErrorInvalidValue;
-  // LDS holds q: a two-slot ring per wavefront for the next piece (one column
-  // tile), or the current piece's (two tiles).
-  // With one column tile, each wavefront also has an output staging area.
-  const size_t lds = (size_t)args.heads_per_wg * (args.num_cols <= 16 ? 2 : 1) * args.rec_cols * (head_size + 8) *
-                         sizeof(uint16_t) +
-                     (args.num_cols <= 16 && (args.block_size != 8 || fused)
-                          ? (size_t)args.heads_per_wg * (kStageBytes + kStageSlots * sizeof(size_t))
-                          : 0) +
-                     // kStep: the new K/V rows staged for their slots
-                     (fused ? (size_t)args.heads_per_wg * kNewSlots * (4 * (size_t)head_size + 16) : 0);
-  hipError_t err;
-  if (head_size == 128) {
-    err = launch_decode_d<128>(args, lds, stream);
-  } else if (head_size == 64) {
-    err = launch_decode_d<64>(args, lds, stream);
-  } else {
-    return hipErrorInvalidValue;
+  if (head_size != 128 && head_size != 64) return hipErrorInvalidValue;
+  // LDS per wavefront: q, as a two-slot ring for the next piece (one column
+  // tile) or the current piece's (two tiles); with the fused step the new
+  // K/V rows staged for their slots; with one column tile (not 8-token
+  // blocks) an output staging area in the room left of kLdsPerWave.
+  const int q_ring = (args.num_cols <= 16 ? 2 : 1) * args.rec_cols * (head_size + 8) * (int)sizeof(uint16_t);
+  const int new_rows = fused ? kNewSlots * (4 * head_size + 16) : 0;
+  DecodeArgs a = args;
+  a.stage_slots = 0;
+  if (args.num_cols <= 16 && args.block_size != 8) {
+    const int avail = kLdsPerWave - q_ring - new_rows;
+    int n = avail > 0 ? avail / (stage_out_bytes(1, args.num_cols, head_size) + 8) : 0;
+    if (n > kMaxStageSlots) n = kMaxStageSlots;
+    while (n > 0 && stage_stride(n, args.num_cols, head_size) > avail) --n;
+    a.stage_slots = n;
   }
+  const size_t lds =
+      (size_t)args.heads_per_wg * (q_ring + stage_stride(a.stage_slots, args.num_cols, head_size) + new_rows);
+  hipError_t err = head_size == 128 ? launch_decode_d<128>(a, lds, stream) : launch_decode_d<64>(a, lds, stream);
   if (err != hipSuccess || args.num_wgs <= 1) return err;
   const dim3 mgrid((unsigned)args.num_wgs);
   const dim3 mblock(64 * (unsigned)args.heads_per_wg);

@@ -76,6 +76,9 @@ struct DecodeArgs {
   const ShareHeader *share;
   int32_t block_size;            // tokens per cache block: 8, 16 or 32 (16 unless q_len == 1 and no sharing)
   int32_t vector_path;           // one query head per KV head: compute on the vector ALU, not matrix cores
+  // Launches that stage whole-segment outputs in LDS (one column tile, not
+  // 8-token blocks): outputs per wavefront (set by the launch; 0 otherwise).
+  int32_t stage_slots;
 };
 
 // Arguments of the sharing-aware plan kernel.
