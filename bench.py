@@ -620,7 +620,9 @@ def main(argv=None) -> int:
     elif args.shared:
         kernel = "decode_shared call: share_plan_kernel + decode_kernel + merge_kernel"
     elif fused:
-        kernel = "decode_step call (new tokens attended and written in the launch): decode_kernel + merge_kernel"
+        kernel = ("decode_step call (new tokens attended and written in the decode launch; with more sequences "
+                  "per workgroup than it can stage, a scatter launch first): [step_scatter_kernel +] "
+                  "decode_kernel + merge_kernel")
     else:
         kernel = "decode call: decode_kernel + merge_kernel"
     rec = {
@@ -653,7 +655,8 @@ def main(argv=None) -> int:
                        "reshape_and_cache + decode_shared_planned (plan built once)" if args.plan_once else
                        "reshape_and_cache + decode_shared_tree" if args.shared == "tree" else
                        "reshape_and_cache + decode_shared" if args.shared else
-                       "decode_step (fused scatter and decode)" if fused else "reshape_and_cache + decode"),
+                       "decode_step (scatter and decode in one launch, or two with many sequences per workgroup)" if fused
+                       else "reshape_and_cache + decode"),
             "parallelism": "single GPU",
             "cache": CACHE_NOTES.get(workload, "cold: the K/V of a call is several times the 256 MB MALL"),
         },

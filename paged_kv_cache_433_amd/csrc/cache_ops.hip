@@ -40,6 +40,39 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   }
 }
 
+// The scatter of a decode step's new tokens, each to the slot of its
+// position n - 1 (n = the sequence's context length clamped to 0 ..
+// max_blocks_per_seq * block_size): row (n - 1) % block_size of the block
+// its table names there ("vLLM: Anatomy and Mechanisms", section
+// "Block-Level Management"). Empty sequences and table entries outside the
+// pool write nothing. The same slots, clamps and skips as the fused step's
+// own writes. Workgroups take sequences in turn; threads take 16-byte
+// vectors of the token row (all KV heads).
+__global__ __launch_bounds__(256) void step_scatter_kernel(
+    const uint16_t *__restrict__ k, const uint16_t *__restrict__ v, const int32_t *__restrict__ tables,
+    const int32_t *__restrict__ lens, uint16_t *__restrict__ k_cache, uint16_t *__restrict__ v_cache,
+    int32_t num_seqs, int32_t row_elems, int32_t max_blocks_per_seq, int32_t block_size, int64_t num_blocks) {
+  const int cap = max_blocks_per_seq * block_size;
+  const int vecs = row_elems / 8;
+  for (int s = blockIdx.x; s < num_seqs; s += gridDim.x) {
+    const int len = lens[s];
+    const int n = len < 0 ? 0 : (len > cap ? cap : len);
+    if (n == 0) continue;
+    const int pos = n - 1;
+    const int id = tables[(size_t)s * max_blocks_per_seq + pos / block_size];
+    if (id < 0 || id >= num_blocks) continue;
+    const size_t dst = ((size_t)id * block_size + pos % block_size) * row_elems;
+    const u32x4_t *ks = reinterpret_cast<const u32x4_t *>(k + (size_t)s * row_elems);
+    const u32x4_t *vs = reinterpret_cast<const u32x4_t *>(v + (size_t)s * row_elems);
+    u32x4_t *kd = reinterpret_cast<u32x4_t *>(k_cache + dst);
+    u32x4_t *vd = reinterpret_cast<u32x4_t *>(v_cache + dst);
+    for (int i = threadIdx.x; i < vecs; i += blockDim.x) {
+      kd[i] = ks[i];
+      vd[i] = vs[i];
+    }
+  }
+}
+
 // grid.x = pair, grid.y = 0 for K and 1 for V, grid.z = chunk of the block.
 // Block dst becomes a copy of block src ("vLLM: Anatomy and Mechanisms",
 // section "Memory Sharing via Copy-on-Write (CoW)": only the block where the
@@ -128,6 +161,18 @@ hipError_t launch_reshape_and_cache(const uint16_t *k, const uint16_t *v, const 
   const int threads = vecs >= 256 ? 256 : ((vecs + 63) / 64) * 64;
   hipLaunchKernelGGL(reshape_and_cache_kernel, dim3((unsigned)num_tokens), dim3(threads), 0, stream,
                      k, v, slots, k_cache, v_cache, row_elems, num_slots);
+  return hipGetLastError();
+}
+
+hipError_t launch_step_scatter(const uint16_t *k, const uint16_t *v, const int32_t *tables, const int32_t *lens,
+                               uint16_t *k_cache, uint16_t *v_cache, int32_t num_seqs, int32_t row_elems,
+                               int32_t max_blocks_per_seq, int32_t block_size, int64_t num_blocks,
+                               hipStream_t stream) {
+  if (num_seqs <= 0) return hipSuccess;
+  const int32_t threads = row_elems / 8 < 256 ? ((row_elems / 8 + 63) / 64) * 64 : 256;
+  const unsigned grid = (unsigned)(num_seqs < 4096 ? num_seqs : 4096);
+  hipLaunchKernelGGL(step_scatter_kernel, dim3(grid), dim3(threads), 0, stream, k, v, tables, lens, k_cache,
+                     v_cache, num_seqs, row_elems, max_blocks_per_seq, block_size, num_blocks);
   return hipGetLastError();
 }
 

@@ -1927,6 +1927,16 @@ hipError_t launch_decode_d(const DecodeArgs &args, size_t lds, hipStream_t strea
 
 }  // namespace
 
+int32_t decode_stage_slots(int32_t num_cols, int32_t head_size, int32_t block_size, bool fused) {
+  if (num_cols > 16 || block_size == 8) return 0;
+  const int q_ring = 2 * num_cols * (head_size + 8) * (int)sizeof(uint16_t);
+  const int avail = kLdsPerWave - q_ring - (fused ? kNewSlots * (4 * head_size + 16) : 0);
+  int n = avail > 0 ? avail / (stage_out_bytes(1, num_cols, head_size) + 8) : 0;
+  if (n > kMaxStageSlots) n = kMaxStageSlots;
+  while (n > 0 && stage_stride(n, num_cols, head_size) > avail) --n;
+  return n;
+}
+
 hipError_t launch_decode(const DecodeArgs &args, int32_t head_size, hipStream_t stream) {
   const bool wide = args.num_cols > kMaxNarrowCols;
   const bool fused = args.k_new != nullptr;
@@ -1947,14 +1957,7 @@ hipError_t launch_decode(const DecodeArgs &args, int32_t head_size, hipStream_t 
   const int q_ring = (args.num_cols <= 16 ? 2 : 1) * args.rec_cols * (head_size + 8) * (int)sizeof(uint16_t);
   const int new_rows = fused ? kNewSlots * (4 * head_size + 16) : 0;
   DecodeArgs a = args;
-  a.stage_slots = 0;
-  if (args.num_cols <= 16 && args.block_size != 8) {
-    const int avail = kLdsPerWave - q_ring - new_rows;
-    int n = avail > 0 ? avail / (stage_out_bytes(1, args.num_cols, head_size) + 8) : 0;
-    if (n > kMaxStageSlots) n = kMaxStageSlots;
-    while (n > 0 && stage_stride(n, args.num_cols, head_size) > avail) --n;
-    a.stage_slots = n;
-  }
+  a.stage_slots = decode_stage_slots(args.num_cols, head_size, args.block_size, fused);
   const size_t lds =
       (size_t)args.heads_per_wg * (q_ring + stage_stride(a.stage_slots, args.num_cols, head_size) + new_rows);
   hipError_t err = head_size == 128 ? launch_decode_d<128>(a, lds, stream) : launch_decode_d<64>(a, lds, stream);

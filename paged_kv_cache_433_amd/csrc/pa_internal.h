@@ -130,6 +130,18 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
 
 hipError_t launch_decode(const DecodeArgs &args, int32_t head_size, hipStream_t stream);
 
+// Whole-segment outputs a wavefront of a one-tile decode launch stages in
+// LDS (0 with 8-token blocks or more than 16 columns); `fused`: the decode
+// step in one launch, whose new-row slots take part of the room.
+int32_t decode_stage_slots(int32_t num_cols, int32_t head_size, int32_t block_size, bool fused);
+
+// The new tokens of a decode step to their slots, found from the tables and
+// context lengths as the fused step finds them (cache_ops.hip).
+hipError_t launch_step_scatter(const uint16_t *k, const uint16_t *v, const int32_t *tables, const int32_t *lens,
+                               uint16_t *k_cache, uint16_t *v_cache, int32_t num_seqs, int32_t row_elems,
+                               int32_t max_blocks_per_seq, int32_t block_size, int64_t num_blocks,
+                               hipStream_t stream);
+
 // Bytes of the static device scratch of pa_decode_noalloc. It covers every
 // single-token decode the default split can produce: at most 1024
 // workgroups x KV heads per workgroup, 16 columns each, head size 128, two
