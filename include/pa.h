@@ -172,9 +172,9 @@ size_t pa_decode_workspace_bytes(const pa_kv_cache *cache, int32_t num_seqs,
  * the call is the cache after it, bit for bit. n == 0: nothing is written
  * and the output row is zero. Usually one launch does both; with more
  * sequences per workgroup than that launch can keep in LDS until its stream
- * ends (thousands of short sequences), the scatter runs as a launch of its
- * own before the decode, which is faster there; the cache is the same bit
- * for bit, the output the same up to rounding. A table entry for position n - 1 outside
+ * ends (thousands of short sequences), the new rows are scattered by a
+ * launch of their own first, which is faster there. The output and the
+ * cache are the same bit for bit either way. A table entry for position n - 1 outside
  * [0, num_blocks) skips the write (the output still uses k[s], v[s]).
  *
  *   k, v   bf16 [num_seqs, num_kv_heads, head_size], 16-byte aligned

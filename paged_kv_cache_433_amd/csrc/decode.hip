@@ -1216,7 +1216,7 @@ __device__ __forceinline__ bool step(const int32_t *__restrict__ tables, const D
   }  // matrix-core path
 
   if constexpr (M == kStep) {
-    if (fresh) stage_new<NJ, NT, M, BS>(tables, a, ln, st, lds, K, V);
+    if (fresh && a.write_new) stage_new<NJ, NT, M, BS>(tables, a, ln, st, lds, K, V);
   }
   if (stage_q) park_q<NJ>(q_slot<NJ>(lds, a, ln.wave, st.ord + 1), ln, qt);
 
@@ -1927,10 +1927,10 @@ hipError_t launch_decode_d(const DecodeArgs &args, size_t lds, hipStream_t strea
 
 }  // namespace
 
-int32_t decode_stage_slots(int32_t num_cols, int32_t head_size, int32_t block_size, bool fused) {
+int32_t decode_stage_slots(int32_t num_cols, int32_t head_size, int32_t block_size, bool new_rows) {
   if (num_cols > 16 || block_size == 8) return 0;
   const int q_ring = 2 * num_cols * (head_size + 8) * (int)sizeof(uint16_t);
-  const int avail = kLdsPerWave - q_ring - (fused ? kNewSlots * (4 * head_size + 16) : 0);
+  const int avail = kLdsPerWave - q_ring - (new_rows ? kNewSlots * (4 * head_size + 16) : 0);
   int n = avail > 0 ? avail / (stage_out_bytes(1, num_cols, head_size) + 8) : 0;
   if (n > kMaxStageSlots) n = kMaxStageSlots;
   while (n > 0 && stage_stride(n, num_cols, head_size) > avail) --n;
@@ -1955,9 +1955,10 @@ hipError_t launch_decode(const DecodeArgs &args, int32_t head_size, hipStream_t 
   // K/V rows staged for their slots; with one column tile (not 8-token
   // blocks) an output staging area in the room left of kLdsPerWave.
   const int q_ring = (args.num_cols <= 16 ? 2 : 1) * args.rec_cols * (head_size + 8) * (int)sizeof(uint16_t);
-  const int new_rows = fused ? kNewSlots * (4 * head_size + 16) : 0;
+  const bool writes = fused && args.write_new;
+  const int new_rows = writes ? kNewSlots * (4 * head_size + 16) : 0;
   DecodeArgs a = args;
-  a.stage_slots = decode_stage_slots(args.num_cols, head_size, args.block_size, fused);
+  a.stage_slots = decode_stage_slots(args.num_cols, head_size, args.block_size, writes);
   const size_t lds =
       (size_t)args.heads_per_wg * (q_ring + stage_stride(a.stage_slots, args.num_cols, head_size) + new_rows);
   hipError_t err = head_size == 128 ? launch_decode_d<128>(a, lds, stream) : launch_decode_d<64>(a, lds, stream);

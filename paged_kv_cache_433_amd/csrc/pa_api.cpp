@@ -373,31 +373,24 @@ int decode_impl(const pa_kv_cache *cache, const void *q, const int32_t *block_ta
   if (!q || !block_tables || !context_lens || !out)
     return fail(PA_ERR_NULL, "q, block_tables, context_lens or out is NULL");
   if (check_aligned(q, "q") != PA_OK || check_aligned(out, "out") != PA_OK) return PA_ERR_UNSUPPORTED;
-  bool fused = k_new || v_new;
+  const bool fused = k_new || v_new;
   if (fused && (!k_new || !v_new)) return fail(PA_ERR_NULL, "k or v is NULL");
   if (fused && (check_aligned(k_new, "k") != PA_OK || check_aligned(v_new, "v") != PA_OK)) return PA_ERR_UNSUPPORTED;
 
-  pa::DecodePlan plan = pa::plan_decode(num_seqs, num_q_heads, cache->num_kv_heads, cache->head_size,
-                                        step_chunks_per_row(cache, max_blocks_per_seq, fused), q_len);
+  const pa::DecodePlan plan = pa::plan_decode(num_seqs, num_q_heads, cache->num_kv_heads, cache->head_size,
+                                              step_chunks_per_row(cache, max_blocks_per_seq, fused), q_len);
   // The decode step in one launch stages each finished sequence's output and
   // new K/V row in LDS until its stream ends. With more sequences per
-  // workgroup than it has places for, the rest are stored mid-stream, and
-  // the scatter as its own launch followed by pa_decode (which has more
-  // places) is faster: 4096 sequences of median 64 tokens at 32/8 heads
-  // (32 per workgroup, 25 places) 247.8 against 263.9 us; 2048 of median
-  // 128 (16 per workgroup) stay fused, 226.0 against 229.8 us. Both forms
-  // give the same cache bit for bit; the outputs differ only in rounding
-  // (the newest position is its own chunk in the fused form).
+  // workgroup than it has places for, the rest are stored mid-stream, which
+  // delays the waits for the loads around them. Then the new rows go to
+  // their slots in a scatter launch first, and the decode launch (still
+  // attending over each new token from k and v) stages outputs only, in the
+  // room the new rows took. Both forms give the same output and cache.
   const int32_t places = fused ? pa::decode_stage_slots(num_q_heads / cache->num_kv_heads, cache->head_size,
                                                          cache->block_size, true)
                                : 0;
   const bool split_step = fused && places > 0 &&
                           (int64_t)num_seqs * plan.num_head_groups > (int64_t)plan.num_wgs * places;
-  if (split_step) {
-    fused = false;
-    plan = pa::plan_decode(num_seqs, num_q_heads, cache->num_kv_heads, cache->head_size,
-                           chunks_per_row(cache, max_blocks_per_seq), q_len);
-  }
   if (workspace && workspace_bytes < plan.total_bytes)
     return fail(PA_ERR_WORKSPACE, "workspace smaller than pa_decode_workspace_bytes()");
   if (workspace && reinterpret_cast<uintptr_t>(workspace) % 16)
@@ -434,8 +427,9 @@ int decode_impl(const pa_kv_cache *cache, const void *q, const int32_t *block_ta
     a.part_ml = reinterpret_cast<float *>(base + plan.desc_bytes);
     a.part_o = reinterpret_cast<float *>(base + plan.desc_bytes + plan.ml_bytes);
   }
-  a.k_new = fused ? static_cast<const uint16_t *>(k_new) : nullptr;
-  a.v_new = fused ? static_cast<const uint16_t *>(v_new) : nullptr;
+  a.k_new = static_cast<const uint16_t *>(k_new);
+  a.v_new = static_cast<const uint16_t *>(v_new);
+  a.write_new = split_step ? 0 : 1;
   a.num_blocks = cache->num_blocks;
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;

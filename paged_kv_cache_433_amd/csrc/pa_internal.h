@@ -79,6 +79,9 @@ struct DecodeArgs {
   // Launches that stage whole-segment outputs in LDS (one column tile, not
   // 8-token blocks): outputs per wavefront (set by the launch; 0 otherwise).
   int32_t stage_slots;
+  // The fused step only: 1 to write the new K/V rows to their slots, 0 when
+  // a scatter launch before the decode has written them.
+  int32_t write_new;
 };
 
 // Arguments of the sharing-aware plan kernel.
@@ -131,9 +134,9 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
 hipError_t launch_decode(const DecodeArgs &args, int32_t head_size, hipStream_t stream);
 
 // Whole-segment outputs a wavefront of a one-tile decode launch stages in
-// LDS (0 with 8-token blocks or more than 16 columns); `fused`: the decode
-// step in one launch, whose new-row slots take part of the room.
-int32_t decode_stage_slots(int32_t num_cols, int32_t head_size, int32_t block_size, bool fused);
+// LDS (0 with 8-token blocks or more than 16 columns); `new_rows`: the
+// decode step writing its new rows, whose slots take part of the room.
+int32_t decode_stage_slots(int32_t num_cols, int32_t head_size, int32_t block_size, bool new_rows);
 
 // The new tokens of a decode step to their slots, found from the tables and
 // context lengths as the fused step finds them (cache_ops.hip).

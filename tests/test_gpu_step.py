@@ -112,6 +112,32 @@ def test_step_table_entry_outside_the_pool_skips_the_write():
     assert_attention_close(out, ref, "step: table entry outside the pool")
 
 
+def test_step_two_launch_form_skips_outside_entries(monkeypatch):
+    """With one workgroup for 48 sequences (96 segments, more than the fused
+    launch's 25 staging places at 32/8 heads) the step scatters the new rows
+    in a launch of their own, then decodes without writing them: an empty
+    sequence writes nothing, a table entry outside the pool skips its write
+    (the output still attends over the new token), and the rest match the
+    oracle's scatter and decode (cache bit for bit)."""
+    rng = np.random.default_rng(2502)
+    lens = [int(x) for x in rng.integers(1, 90, size=48)]
+    lens[5] = 33  # its new token opens block 2
+    b = small_batch(2502, lens, 32, 8, 128, spare=6)
+    tables = b.block_tables.copy()
+    good = int(tables[5, 2])
+    tables[5, 2] = -3
+    bad = dataclasses.replace(b, block_tables=tables)
+    ctx = b.context_lens.copy()
+    ctx[7] = 0
+    monkeypatch.setenv("PA_DECODE_WGS", "1")
+    out, kd, vd = run_step(bad, "step in two launches: outside entry, empty sequence", ctx)
+    kc, vc, ref = oracle_step(b, ctx)
+    kc[good, 0], vc[good, 0] = b.k_cache[good, 0], b.v_cache[good, 0]
+    assert np.array_equal(kd, kc) and np.array_equal(vd, vc)
+    assert np.all(out[7] == 0)
+    assert_attention_close(out, ref, "step in two launches")
+
+
 @pytest.mark.parametrize("name", ["llama3_8b_gqa", "llama2_7b", "llama3_8b_gqa_tp8", "long_splitk", "many_short",
                                   "many_short_tp8"])
 def test_step_full_size(name):
