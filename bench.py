@@ -107,7 +107,8 @@ def record_traffic(prefix: str, workload: str, copy_bytes: int, copy_prefix: str
     {prefix}_write_decode (this bench on `workload`, counters FETCH_SIZE and
     WRITE_SIZE), {prefix}_fetch_copy and {prefix}_write_copy (--probe-copy of
     `copy_bytes` bytes). The call's kernels are the decode and merge kernels,
-    and the plan kernel when the call is sharing-aware. Each counter is scaled by what it reads for the copy,
+    the plan kernel when the call is sharing-aware, and the scatter kernel
+    when the decode step runs as two launches. Each counter is scaled by what it reads for the copy,
     which moves exactly `copy_bytes` each way, so the units need not be known.
     """
     def means(kind, counter, pre=None):
@@ -121,6 +122,8 @@ def record_traffic(prefix: str, workload: str, copy_bytes: int, copy_prefix: str
     frags = ["decode_kernel", "merge_kernel"]
     if any("share_plan_kernel" in k for k in fd):  # the sharing-aware call's plan
         frags.insert(0, "share_plan_kernel")
+    if any("step_scatter_kernel" in k for k in fd):  # the decode step in two launches
+        frags.insert(0, "step_scatter_kernel")
     for frag in frags:
         per[frag] = {"fetch_bytes": int(_one(fd, frag) * f_scale), "write_bytes": int(_one(wd, frag) * w_scale)}
     total = sum(v["fetch_bytes"] + v["write_bytes"] for v in per.values())
